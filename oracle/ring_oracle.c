@@ -1,0 +1,326 @@
+/*
+ * ring_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, single-threaded CPU implementation of the ring AllReduce that the
+ * HIP library computes, written to be checked by eye against the pages.  It
+ * shares no code, header, table or helper with the HIP path; only the tests,
+ * the package's smoke check and the benchmark's CPU-baseline leg may load it.
+ *
+ * What it computes (all citations are to the web pages the method comes from):
+ *
+ *  - Channel split.  A collective is cut into one contiguous share per channel
+ *    ["NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程", ch.2 §2.2 "通道 channel",
+ *    walkthrough step 3 "資料切分"].  The pages leave the exact rounding open;
+ *    the share is rounded up to the 16-byte grain the chunk formula uses:
+ *        P = alignUp(divUp(count, nChannels), 16/elemSize)
+ *        channel ch covers [min(ch*P, count), min((ch+1)*P, count)).
+ *
+ *  - Loops and chunks.  Inside a channel the ring walks loops of
+ *    nRanks*chunkElems elements.  When fewer elements than a full loop remain,
+ *    the chunk shrinks to alignUp(divUp(rem, nRanks), 16/elemSize) and chunk k
+ *    covers [k*cur, min((k+1)*cur, rem)), empty once k*cur >= rem
+ *    [same book, ch.2 §2.3 "演算法 algorithm", RingARAlgorithm::getNextSendAddr].
+ *
+ *  - Summation order.  At ring stage s the member at ring index r sends chunk
+ *    (r + nRanks - 1 - s) mod nRanks [same passage, the chunkId formula].  So
+ *    chunk c leaves member c+1 raw, is combined at c+2, c+3, ... and is
+ *    finished at member c after nRanks-1 reduce steps; the all-gather half then
+ *    copies the finished chunk around the ring [same section, the
+ *    reduce-scatter / all-gather walkthrough and nStepsPerLoop = 2(nRanks-1)].
+ *    With the identity ring used for every channel, member index == rank, so
+ *        acc = x[(c+1) mod N][e];  acc = OP(acc, x[(c+k) mod N][e]), k=2..N
+ *    and every rank receives acc.
+ *
+ *  - OP.  Sum on int32 wraps (two's complement).  Sum on float32 is one IEEE
+ *    binary32 add, round-to-nearest-even.  Sum on float16/bfloat16 widens both
+ *    operands exactly to binary32, adds, and rounds back to the 16-bit type with
+ *    round-to-nearest-even, because the partial crosses the ring in its own
+ *    type at every hop.  Max is acc = (x > acc) ? x : acc and Min is
+ *    acc = (x < acc) ? x : acc with acc the incoming partial and x the local
+ *    value.  The pages fix none of these; they are the readings this build
+ *    takes and both sides implement them independently.
+ *
+ *  - A debug-only uint64 "probe" op, acc = acc*16 + x, is not commutative, so a
+ *    folded value spells out the order in which ranks were visited.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math; x86-64 SSE
+ * arithmetic, default MXCSR, so no flush-to-zero).
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+enum { ORC_INT32 = 0, ORC_FLOAT32 = 1, ORC_FLOAT16 = 2, ORC_BFLOAT16 = 3, ORC_UINT64 = 4 };
+enum { ORC_SUM = 0, ORC_MAX = 1, ORC_MIN = 2, ORC_PROBE = 3 };
+
+static size_t elem_size(int dtype) {
+  switch (dtype) {
+    case ORC_INT32: return 4;
+    case ORC_FLOAT32: return 4;
+    case ORC_FLOAT16: return 2;
+    case ORC_BFLOAT16: return 2;
+    case ORC_UINT64: return 8;
+    default: return 0;
+  }
+}
+
+static size_t div_up(size_t x, size_t y) { return (x + y - 1) / y; }
+static size_t align_up(size_t x, size_t a) { return div_up(x, a) * a; }
+static size_t min_sz(size_t a, size_t b) { return a < b ? a : b; }
+
+/* ---------------- 16-bit float conversions (written from IEEE 754) ---------- */
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bfloat16 is the top half of a binary32; widening is exact. */
+static float bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+/* binary32 -> bfloat16, round to nearest, ties to even.  NaN stays a quiet NaN
+ * with its sign; overflow rounds to infinity through the carry. */
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u = f32_to_bits(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+    return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t lower = u & 0xffffu;          /* the 16 bits dropped */
+  uint32_t upper = u >> 16;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+/* binary16 -> binary32, exact (every half value is a float). */
+static float f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h >> 15) & 1u;
+  uint32_t expo = (uint32_t)(h >> 10) & 0x1fu;
+  uint32_t mant = (uint32_t)h & 0x3ffu;
+  float mag;
+  if (expo == 0) {
+    mag = (float)mant * (1.0f / 16777216.0f);          /* mant * 2^-24, exact */
+  } else if (expo == 31) {
+    return bits_to_f32((sign << 31) | 0x7f800000u | (mant << 13));
+  } else {
+    mag = bits_to_f32(((expo - 15u + 127u) << 23) | (mant << 13));
+  }
+  return sign ? -mag : mag;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, with subnormal results
+ * and overflow to infinity.  Done on the exact binary32 significand. */
+static uint16_t f32_to_f16(float f) {
+  uint32_t u = f32_to_bits(f);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t expo = (u >> 23) & 0xffu;
+  uint32_t mant = u & 0x7fffffu;
+  if (expo == 0xffu) {                                  /* inf or NaN */
+    if (mant == 0) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | 0x7e00u | (mant >> 13));
+  }
+  if (expo == 0) return sign;        /* binary32 subnormals are far below half's range */
+  int e = (int)expo - 127;           /* unbiased exponent of the value */
+  uint32_t sig = mant | 0x800000u;   /* 24-bit significand, value = sig * 2^(e-23) */
+  /* The half result is q * 2^(he) with q an integer; find how many low bits of
+   * sig fall below the half's last place. */
+  int shift;                         /* bits to drop from sig */
+  if (e >= -14) shift = 13;          /* normal half: 11-bit significand */
+  else shift = 13 + (-14 - e);       /* subnormal half: fixed scale 2^-24 */
+  if (shift > 25) return sign;       /* below half the smallest subnormal */
+  uint32_t q = sig >> shift;
+  uint32_t rem = sig & ((1u << shift) - 1u);
+  uint32_t halfway = 1u << (shift - 1);
+  if (rem > halfway || (rem == halfway && (q & 1u))) q += 1u;
+  uint32_t bits;
+  if (e >= -14) {
+    /* q is 1.xxx with the implicit bit at 2^10; a carry may bump the exponent */
+    uint32_t he = (uint32_t)(e + 15);
+    if (q >= 0x800u) { q >>= 1; he += 1; }
+    if (he >= 31) return (uint16_t)(sign | 0x7c00u);
+    bits = (he << 10) | (q & 0x3ffu);
+  } else {
+    bits = q;                         /* q == 0x400 becomes the smallest normal */
+  }
+  return (uint16_t)(sign | bits);
+}
+
+/* ---------------- the per-element combine, one dtype at a time -------------- */
+
+static void fold_i32(int op, int32_t* acc, const int32_t* x, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    if (op == ORC_SUM) acc[i] = (int32_t)((uint32_t)acc[i] + (uint32_t)x[i]);
+    else if (op == ORC_MAX) acc[i] = (x[i] > acc[i]) ? x[i] : acc[i];
+    else acc[i] = (x[i] < acc[i]) ? x[i] : acc[i];
+  }
+}
+
+static void fold_f32(int op, float* acc, const float* x, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    if (op == ORC_SUM) acc[i] = acc[i] + x[i];
+    else if (op == ORC_MAX) acc[i] = (x[i] > acc[i]) ? x[i] : acc[i];
+    else acc[i] = (x[i] < acc[i]) ? x[i] : acc[i];
+  }
+}
+
+static void fold_half(int op, int is_bf16, uint16_t* acc, const uint16_t* x, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    float a = is_bf16 ? bf16_to_f32(acc[i]) : f16_to_f32(acc[i]);
+    float b = is_bf16 ? bf16_to_f32(x[i]) : f16_to_f32(x[i]);
+    if (op == ORC_SUM) {
+      float s = a + b;
+      acc[i] = is_bf16 ? f32_to_bf16(s) : f32_to_f16(s);
+    } else if (op == ORC_MAX) {
+      if (b > a) acc[i] = x[i];
+    } else {
+      if (b < a) acc[i] = x[i];
+    }
+  }
+}
+
+static void fold_u64_probe(uint64_t* acc, const uint64_t* x, size_t n) {
+  for (size_t i = 0; i < n; ++i) acc[i] = acc[i] * 16u + x[i];
+}
+
+static int fold(int dtype, int op, void* acc, const void* x, size_t n) {
+  switch (dtype) {
+    case ORC_INT32: fold_i32(op, (int32_t*)acc, (const int32_t*)x, n); return 0;
+    case ORC_FLOAT32: fold_f32(op, (float*)acc, (const float*)x, n); return 0;
+    case ORC_FLOAT16: fold_half(op, 0, (uint16_t*)acc, (const uint16_t*)x, n); return 0;
+    case ORC_BFLOAT16: fold_half(op, 1, (uint16_t*)acc, (const uint16_t*)x, n); return 0;
+    case ORC_UINT64: fold_u64_probe((uint64_t*)acc, (const uint64_t*)x, n); return 0;
+    default: return -1;
+  }
+}
+
+static int check_args(int nranks, int dtype, int op, int nchannels, size_t chunk_elems) {
+  size_t esz = elem_size(dtype);
+  if (nranks < 1 || nchannels < 1 || esz == 0) return -1;
+  if (op < ORC_SUM || op > ORC_PROBE) return -1;
+  if ((op == ORC_PROBE) != (dtype == ORC_UINT64)) return -1;
+  size_t grain = 16 / esz;
+  if (chunk_elems == 0 || chunk_elems % grain != 0) return -1;
+  return 0;
+}
+
+/* Locate element idx: its channel, loop, chunk and the chunk's element range
+ * [first, first+len) in the rank buffer.  Returns -1 if idx >= count. */
+int ar_oracle_locate(int nranks, size_t count, int dtype, int nchannels, size_t chunk_elems,
+                     size_t idx, int* channel, long long* loop, int* chunk,
+                     size_t* first, size_t* len) {
+  size_t esz = elem_size(dtype);
+  if (esz == 0 || nranks < 1 || nchannels < 1 || idx >= count) return -1;
+  size_t grain = 16 / esz;
+  size_t per_ch = align_up(div_up(count, (size_t)nchannels), grain);
+  size_t ch = idx / per_ch;
+  size_t lo = min_sz(ch * per_ch, count);
+  size_t hi = min_sz((ch + 1) * per_ch, count);
+  size_t loop_size = (size_t)nranks * chunk_elems;
+  size_t in_ch = idx - lo;
+  size_t l = in_ch / loop_size;
+  size_t off = l * loop_size;
+  size_t rem = (hi - lo) - off;
+  size_t cur = rem < loop_size ? align_up(div_up(rem, (size_t)nranks), grain) : chunk_elems;
+  size_t c = (in_ch - off) / cur;
+  size_t b = c * cur;
+  size_t e = min_sz(b + cur, rem);
+  if (channel) *channel = (int)ch;
+  if (loop) *loop = (long long)l;
+  if (chunk) *chunk = (int)c;
+  if (first) *first = lo + off + b;
+  if (len) *len = e - b;
+  return 0;
+}
+
+/* Full ring AllReduce: out[r][0..count) for every rank r.  in and out are
+ * arrays of nranks host pointers; out[r] may equal in[r] only if the caller
+ * does not need the inputs afterwards (the fold reads in[] chunk by chunk
+ * before writing that chunk). */
+int ar_oracle_allreduce(int nranks, size_t count, int dtype, int op, int nchannels,
+                        size_t chunk_elems, const void* const* in, void* const* out) {
+  if (check_args(nranks, dtype, op, nchannels, chunk_elems) != 0) return -1;
+  size_t esz = elem_size(dtype);
+  size_t grain = 16 / esz;
+  if (count == 0) return 0;
+  if (nranks == 1) {
+    if (out[0] != in[0]) memcpy(out[0], in[0], count * esz);
+    return 0;
+  }
+  size_t per_ch = align_up(div_up(count, (size_t)nchannels), grain);
+  size_t loop_size = (size_t)nranks * chunk_elems;
+  /* accumulator for one chunk, in the element type */
+  enum { TMP_BYTES = 1 << 16 };
+  unsigned char acc[TMP_BYTES];
+  size_t tmp_elems = TMP_BYTES / esz;
+  for (int ch = 0; ch < nchannels; ++ch) {
+    size_t lo = min_sz((size_t)ch * per_ch, count);
+    size_t hi = min_sz((size_t)(ch + 1) * per_ch, count);
+    size_t len = hi - lo;
+    for (size_t off = 0; off < len; off += loop_size) {
+      size_t rem = len - off;
+      size_t cur = rem < loop_size ? align_up(div_up(rem, (size_t)nranks), grain) : chunk_elems;
+      for (int c = 0; c < nranks; ++c) {
+        size_t b = (size_t)c * cur;
+        if (b >= rem) continue;                       /* empty chunk */
+        size_t e = min_sz(b + cur, rem);
+        size_t first = lo + off + b;
+        /* walk the chunk in pieces that fit the accumulator */
+        for (size_t p = first; p < lo + off + e; p += tmp_elems) {
+          size_t n = min_sz(tmp_elems, lo + off + e - p);
+          int start = (c + 1) % nranks;               /* member c+1 sends it raw */
+          memcpy(acc, (const unsigned char*)in[start] + p * esz, n * esz);
+          for (int k = 2; k <= nranks; ++k) {
+            int r = (c + k) % nranks;                 /* last one is r == c */
+            fold(dtype, op, acc, (const unsigned char*)in[r] + p * esz, n);
+          }
+          for (int r = 0; r < nranks; ++r)
+            memcpy((unsigned char*)out[r] + p * esz, acc, n * esz);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* One output element, computed on its own (for sampled checks at full size). */
+int ar_oracle_element(int nranks, size_t count, int dtype, int op, int nchannels,
+                      size_t chunk_elems, const void* const* in, size_t idx, void* result) {
+  if (check_args(nranks, dtype, op, nchannels, chunk_elems) != 0) return -1;
+  size_t esz = elem_size(dtype);
+  int c = 0;
+  if (ar_oracle_locate(nranks, count, dtype, nchannels, chunk_elems, idx, NULL, NULL, &c, NULL, NULL) != 0)
+    return -1;
+  unsigned char acc[8];
+  int start = nranks == 1 ? 0 : (c + 1) % nranks;
+  memcpy(acc, (const unsigned char*)in[start] + idx * esz, esz);
+  for (int k = 2; k <= nranks; ++k) {
+    int r = (c + k) % nranks;
+    fold(dtype, op, acc, (const unsigned char*)in[r] + idx * esz, 1);
+  }
+  memcpy(result, acc, esz);
+  return 0;
+}
+
+/* Batched form of ar_oracle_element over an index list. */
+int ar_oracle_elements(int nranks, size_t count, int dtype, int op, int nchannels,
+                       size_t chunk_elems, const void* const* in, const int64_t* idx,
+                       size_t nidx, void* results) {
+  size_t esz = elem_size(dtype);
+  for (size_t i = 0; i < nidx; ++i) {
+    if (idx[i] < 0) return -1;
+    int rc = ar_oracle_element(nranks, count, dtype, op, nchannels, chunk_elems, in,
+                               (size_t)idx[i], (unsigned char*)results + i * esz);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
+/* Conversions exposed so tests can pin them against numpy / torch. */
+void ar_oracle_f32_to_bf16(const float* x, uint16_t* y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = f32_to_bf16(x[i]);
+}
+void ar_oracle_f32_to_f16(const float* x, uint16_t* y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = f32_to_f16(x[i]);
+}
+void ar_oracle_f16_to_f32(const uint16_t* x, float* y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = f16_to_f32(x[i]);
+}
+void ar_oracle_bf16_to_f32(const uint16_t* x, float* y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = bf16_to_f32(x[i]);
+}
