@@ -1,0 +1,227 @@
+/*
+ * ar.h -- C ABI of libar.so: ring AllReduce (reduce-scatter then all-gather)
+ * over per-channel FIFOs in the Simple, LL and LL128 wire formats, with N
+ * virtual ranks emulated on one MI355X (gfx950).
+ *
+ * Sources of the operations (web pages, cited by title and section):
+ *  [B]  "NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程" (AiReadCodeBooks)
+ *  [T]  "NCCL 源码解析：从硬件拓扑到集合通信选型的完整链路"
+ *  [I]  "NVIDIA GPU 集合通信库 NCCL 初始化流程源码级剖析"
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" must point into memory of the GPU that was
+ *    current when the communicator was created; "host" pointers are ordinary
+ *    process memory.  No call takes ownership of caller memory.
+ *  - Bad arguments return arInvalidArgument and enqueue nothing [B ch.3 §3.1,
+ *    argument validation before any work is started].
+ *  - A communicator is not thread-safe: calls on one communicator must come
+ *    from one thread at a time, and AllReduce calls on one communicator must
+ *    be ordered on one stream (or synchronised between streams), since they
+ *    share its FIFOs [B ch.2 §2.1].
+ */
+#ifndef AR_H_
+#define AR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque communicator handle [B ch.2 §2.1, the ncclComm_t handle]. */
+typedef struct arComm* arComm_t;
+
+/* Result codes, mirroring the reference's result enumeration [B ch.3 §3.1 and
+ * ch.5 §一, the InvalidUsage vs InternalError distinction]. */
+typedef enum {
+  arSuccess = 0,
+  arHipError = 1,         /* a HIP runtime call failed (or no usable GPU) */
+  arSystemError = 2,      /* host allocation or OS failure */
+  arInternalError = 3,    /* a bug: the library reached a state it should not */
+  arInvalidArgument = 4,  /* a bad argument; nothing was enqueued */
+  arInvalidUsage = 5,     /* legal arguments that cannot be honoured, e.g. a
+                             forced protocol whose requirements are not met */
+  arRemoteError = 6,      /* a ring member timed out or the comm was aborted */
+  arInProgress = 7,
+  arNumResults = 8
+} arResult_t;
+
+/* Wire formats, in the reference's protocol order [B ch.2 §2.4; ch.5 §二]. */
+typedef enum {
+  arProtoAuto = -1,  /* arTune picks protocol and channel count per call */
+  arProtoLL = 0,     /* 8-byte lines: 4 bytes payload + 4 bytes flag */
+  arProtoLL128 = 1,  /* 128-byte lines: 120 bytes payload + 8 bytes flag */
+  arProtoSimple = 2  /* bulk FIFO slots with head/tail counters */
+} arProto_t;
+
+typedef enum { arAlgoRing = 0 } arAlgo_t;
+
+typedef enum {
+  arInt32 = 0,
+  arFloat32 = 1,
+  arFloat16 = 2,
+  arBfloat16 = 3,
+  arUint64 = 4       /* only with arProbe (debug order probe) */
+} arDataType_t;
+
+typedef enum {
+  arSum = 0,
+  arMax = 1,         /* acc = (x > acc) ? x : acc, acc the incoming partial */
+  arMin = 2,         /* acc = (x < acc) ? x : acc */
+  arProbe = 3        /* debug: uint64 acc = acc*16 + x, not commutative, so the
+                        folded value spells the order ranks were visited in */
+} arRedOp_t;
+
+/*
+ * arInit -- create a communicator for `nranks` virtual ranks on the current
+ * HIP device [B ch.3 §3.1-§3.3 and §3.6: validate, allocate the comm, set up
+ * per-channel rings and FIFOs, one batched copy of device state].
+ *  comm      (host, out) receives the handle.
+ *  nranks    1..AR_MAX_RANKS virtual ranks; ring order is the identity for
+ *            every channel [B ch.2 §2.3; ch.4 ring building].
+ *  nChannels 1..AR_MAX_CHANNELS.  With a fixed protocol every AllReduce uses
+ *            exactly this many channels (the count changes which elements form
+ *            a chunk, hence the summation order).  With arProtoAuto it is the
+ *            upper bound arTune may choose.
+ *  proto     default protocol, or arProtoAuto.
+ *  algo      arAlgoRing.
+ * Allocates the FIFOs, counters and flags of every protocol on the device
+ * (owned by the comm, freed by arDestroy).  Environment overrides, read once
+ * per process: AR_PROTO (LL|LL128|SIMPLE), AR_NCHANNELS, AR_SLICE_BYTES
+ * (Simple slice, default 512 KiB; chunk = 2 slices), AR_STEPS (FIFO depth,
+ * default 8), AR_TIMEOUT_MS.
+ * Errors: arInvalidArgument (bad counts or enums), arHipError (no device or a
+ * HIP failure), arSystemError (host allocation).
+ */
+arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, arAlgo_t algo);
+
+/*
+ * arAllReduce -- every rank's recvbuf receives the reduction over all ranks'
+ * sendbufs [B ch.1 §1.3, ch.2 §2.3 ring reduce-scatter + all-gather].
+ *  sendbufs  (host array of nranks device pointers) rank r's input, `count`
+ *            contiguous elements.  The array itself is copied at call time.
+ *  recvbufs  (host array of nranks device pointers) rank r's output.  In place
+ *            (recvbufs[r] == sendbufs[r]) is allowed; otherwise buffers must
+ *            not overlap.
+ *  count     elements per rank.  count == 0 succeeds with no work [B ch.6 §三].
+ *  dtype/op  see the enums; arProbe only with arUint64.
+ *  stream    a hipStream_t (passed as void*); NULL is the default stream.
+ * The call only enqueues: one kernel launch on `stream`, or a device copy
+ * when nranks == 1 [B ch.6 §三, the one-rank path].  The caller synchronises
+ * the stream before reading results [B ch.1 §1.3].  Buffers must stay valid
+ * until the work completes.  Element pointers need only element alignment;
+ * forcing LL128 needs 128-byte aligned buffers, otherwise arInvalidUsage
+ * [B ch.2 §2.4, LL128 alignment]; arProtoAuto never picks LL128 then.
+ * A ring member that waits longer than the timeout (or an abort) makes the
+ * kernel exit early and is reported by arCommGetAsyncError as arRemoteError;
+ * the comm then only accepts arDestroy.
+ */
+arResult_t arAllReduce(arComm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                       size_t count, arDataType_t dtype, arRedOp_t op, void* stream);
+
+/*
+ * arTune -- choose protocol and channel count for a per-rank message of
+ * nBytes with the pages' cost model [B ch.5 §一 (argmin over candidates),
+ * §三 (ring bandwidth and latency); T §五, time = lat*latCount +
+ * nBytes/(1000*bw) in microseconds and GB/s].
+ *  proto, nChannels, predictedUs (host, out; any may be NULL).
+ * nranks == 1 gives Simple with 0 channels [B ch.5 §一, single-rank short cut].
+ * Candidates: protocols not disabled (AR_PROTO, LL128 alignment is the
+ * caller's concern: arAllReduce re-tunes without LL128 when buffers are not
+ * 128-byte aligned) times power-of-two channel counts up to the comm's
+ * maximum with at least 32 KiB per channel.  Ties keep the earlier candidate:
+ * Simple before LL128 before LL, fewer channels first.
+ */
+arResult_t arTune(arComm_t comm, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs);
+
+/* Per-protocol constants of the ring cost model (microseconds, GB/s). */
+typedef struct {
+  float baseLatUs;    /* per-call latency */
+  float stepLatUs;    /* per ring step; a ring AllReduce has 2(N-1) steps */
+  float bwPerChGBs;   /* bus bandwidth per channel before protocol discount */
+  float maxBwGBs;     /* cap on the discounted bus bandwidth (llMaxBw and
+                         the LL128 per-channel cap of the pages, generalised) */
+} arTuneModel_t;
+
+/*
+ * arTuneEval -- the cost model as a pure function (no device needed).
+ *  models     (host) 3 entries indexed by arProtoLL/LL128/Simple.
+ *  protoMask  bit p set = protocol p allowed.
+ *  busBw = nCh*bwPerCh; LL: min(maxBw, 0.5*busBw); LL128: min(maxBw,
+ *  0.92*busBw); Simple: min(maxBw, busBw); algBw = busBw*N/(2(N-1));
+ *  lat = baseLat + 2(N-1)*stepLat; t = lat + nBytes/(1000*algBw).
+ * Returns arInvalidArgument for bad sizes or an empty mask, arInvalidUsage
+ * if no candidate is valid.
+ */
+arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
+                      unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs);
+
+/* Read / replace the tuner constants of a comm (calibration). */
+arResult_t arTuneGetModel(arComm_t comm, arProto_t proto, arTuneModel_t* model);
+arResult_t arTuneSetModel(arComm_t comm, arProto_t proto, const arTuneModel_t* model);
+
+/*
+ * arSetConfig -- change the comm's default protocol and channel count, same
+ * meaning as in arInit (nChannels must not exceed the value given there).
+ */
+arResult_t arSetConfig(arComm_t comm, arProto_t proto, int nChannels);
+
+/* What arAllReduce would run for a message (for tests and benchmarks). */
+typedef struct {
+  int proto;            /* arProto_t actually used */
+  int nChannels;        /* channels (changes the summation order) */
+  size_t chunkElems;    /* nominal chunk, elements (changes the summation order) */
+  int lanesPerChannel;  /* wavefronts per ring member (pipelining only) */
+  int ranksPerGroup;    /* ring members sharing one workgroup */
+  int workgroups;       /* grid size of the launch */
+  int threadsPerGroup;  /* workgroup size */
+  int stepBytes;        /* FIFO slot size per wavefront (wire bytes) */
+  int stepPayload;      /* payload bytes per FIFO slot */
+  int nSlots;           /* FIFO depth in slots */
+  float predictedUs;    /* cost-model time */
+  double modelBytes;    /* 5(N-1)*S: the stated HBM traffic model */
+} arPlan_t;
+
+/*
+ * arGetPlan -- fill `plan` with what arAllReduce(comm, ..., count, dtype, ...)
+ * would use for buffers that are 128-byte aligned (aligned128 = 1) or not.
+ */
+arResult_t arGetPlan(arComm_t comm, size_t count, arDataType_t dtype, int aligned128, arPlan_t* plan);
+
+/*
+ * arCommGetAsyncError -- non-blocking: arRemoteError once any ring member of
+ * an earlier call timed out or the comm was aborted, else arSuccess
+ * [B ch.2 §2.1 asyncResult; ch.7 group error paths].
+ */
+arResult_t arCommGetAsyncError(arComm_t comm, arResult_t* asyncError);
+
+/*
+ * arCommAbort -- raise the comm's abort word (host memory visible to running
+ * kernels): every waiting ring member gives up within a bounded number of
+ * polls.  Afterwards only arDestroy is accepted [B ch.1 §1.4].
+ */
+arResult_t arCommAbort(arComm_t comm);
+
+/* arDestroy -- synchronise the last stream used, free device and host state
+ * [B ch.1 §1.4, finalize then destroy]. */
+arResult_t arDestroy(arComm_t comm);
+
+/* Debug knobs for failure-handling tests (host-forced conditions; every
+ * kernel still exits normally). */
+typedef enum {
+  arDebugTimeoutUs = 0,  /* a wait longer than this gives up (default 5e6) */
+  arDebugDeadRank = 1,   /* rank whose ring members return at once (-1: none) */
+} arDebugKnob_t;
+arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
+
+const char* arGetErrorString(arResult_t result);
+
+/* Library limits. */
+#define AR_MAX_RANKS 128
+#define AR_MAX_CHANNELS 64
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AR_H_ */

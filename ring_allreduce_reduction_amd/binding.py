@@ -1,0 +1,235 @@
+"""ctypes binding of libar.so -- argument marshalling only.
+
+Every function here has the C ABI's name (include/ar.h) and passes plain
+pointers and sizes through; all work runs in the library's HIP kernels.
+PyTorch is used only for device memory and streams.  Loading fails loudly if
+the library has not been built: there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  -- loads the HIP runtime the library must share
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libar.so")
+
+# enums (include/ar.h)
+arSuccess, arHipError, arSystemError, arInternalError = 0, 1, 2, 3
+arInvalidArgument, arInvalidUsage, arRemoteError, arInProgress = 4, 5, 6, 7
+arProtoAuto, arProtoLL, arProtoLL128, arProtoSimple = -1, 0, 1, 2
+arAlgoRing = 0
+arInt32, arFloat32, arFloat16, arBfloat16, arUint64 = 0, 1, 2, 3, 4
+arSum, arMax, arMin, arProbe = 0, 1, 2, 3
+arDebugTimeoutUs, arDebugDeadRank = 0, 1
+AR_MAX_RANKS, AR_MAX_CHANNELS = 128, 64
+
+PROTO_NAMES = {arProtoLL: "LL", arProtoLL128: "LL128", arProtoSimple: "Simple", arProtoAuto: "auto"}
+PROTO_BY_NAME = {"ll": arProtoLL, "ll128": arProtoLL128, "simple": arProtoSimple, "auto": arProtoAuto}
+DTYPE_BY_NAME = {"int32": arInt32, "float32": arFloat32, "float16": arFloat16,
+                 "bfloat16": arBfloat16, "uint64": arUint64}
+OP_BY_NAME = {"sum": arSum, "max": arMax, "min": arMin, "probe": arProbe}
+
+
+class arTuneModel_t(ctypes.Structure):
+    _fields_ = [("baseLatUs", ctypes.c_float), ("stepLatUs", ctypes.c_float),
+                ("bwPerChGBs", ctypes.c_float), ("maxBwGBs", ctypes.c_float)]
+
+
+class arPlan_t(ctypes.Structure):
+    _fields_ = [("proto", ctypes.c_int), ("nChannels", ctypes.c_int), ("chunkElems", ctypes.c_size_t),
+                ("lanesPerChannel", ctypes.c_int), ("ranksPerGroup", ctypes.c_int),
+                ("workgroups", ctypes.c_int), ("threadsPerGroup", ctypes.c_int),
+                ("stepBytes", ctypes.c_int), ("stepPayload", ctypes.c_int), ("nSlots", ctypes.c_int),
+                ("predictedUs", ctypes.c_float), ("modelBytes", ctypes.c_double)]
+
+
+class ArError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (where, arGetErrorString(code), code))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libar.so (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libar.so is not built (run __graft_entry__.build() or "
+                              "python ring_allreduce_reduction_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        c_int, c_sz, vp, c_f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+        L.arInit.argtypes = [ctypes.POINTER(vp), c_int, c_int, c_int, c_int]
+        L.arAllReduce.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), c_sz, c_int, c_int, vp]
+        L.arTune.argtypes = [vp, c_sz, ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_f)]
+        L.arTuneEval.argtypes = [c_int, c_int, c_sz, ctypes.POINTER(arTuneModel_t), ctypes.c_uint,
+                                 ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_f)]
+        L.arTuneGetModel.argtypes = [vp, c_int, ctypes.POINTER(arTuneModel_t)]
+        L.arTuneSetModel.argtypes = [vp, c_int, ctypes.POINTER(arTuneModel_t)]
+        L.arSetConfig.argtypes = [vp, c_int, c_int]
+        L.arGetPlan.argtypes = [vp, c_sz, c_int, c_int, ctypes.POINTER(arPlan_t)]
+        L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
+        L.arCommAbort.argtypes = [vp]
+        L.arDestroy.argtypes = [vp]
+        L.arSetDebug.argtypes = [vp, c_int, ctypes.c_int64]
+        L.arGetErrorString.argtypes = [c_int]
+        L.arGetErrorString.restype = ctypes.c_char_p
+        for fn in ("arInit", "arAllReduce", "arTune", "arTuneEval", "arTuneGetModel", "arTuneSetModel",
+                   "arSetConfig", "arGetPlan", "arCommGetAsyncError", "arCommAbort", "arDestroy", "arSetDebug"):
+            getattr(L, fn).restype = c_int
+        _lib = L
+    return _lib
+
+
+def _check(code, where):
+    if code != arSuccess:
+        raise ArError(code, where)
+
+
+def arGetErrorString(code):
+    return lib().arGetErrorString(int(code)).decode()
+
+
+def arInit(nranks, nChannels, proto=arProtoSimple, algo=arAlgoRing):
+    h = ctypes.c_void_p()
+    _check(lib().arInit(ctypes.byref(h), int(nranks), int(nChannels), int(proto), int(algo)), "arInit")
+    return h
+
+
+def _ptrs(bufs):
+    out = []
+    for b in bufs:
+        if isinstance(b, torch.Tensor):
+            if not b.is_cuda or not b.is_contiguous():
+                raise ValueError("buffers must be contiguous device tensors")
+            out.append(b.data_ptr())
+        else:
+            out.append(int(b))
+    return (ctypes.c_void_p * len(out))(*out)
+
+
+def _dtype_of(t):
+    m = {torch.int32: arInt32, torch.float32: arFloat32, torch.float16: arFloat16,
+         torch.bfloat16: arBfloat16, torch.int64: arUint64}
+    if hasattr(torch, "uint64"):
+        m[torch.uint64] = arUint64
+    return m[t.dtype]
+
+
+def arAllReduce(comm, sendbufs, recvbufs, count=None, dtype=None, op=arSum, stream=None):
+    """sendbufs / recvbufs: lists of device tensors (or raw device addresses,
+    then count and dtype are required).  stream: a torch.cuda.Stream, a raw
+    hipStream_t value, or None for torch's current stream."""
+    if count is None:
+        count = sendbufs[0].numel()
+    if dtype is None:
+        dtype = _dtype_of(sendbufs[0])
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(lib().arAllReduce(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(count), int(dtype), int(op),
+                             ctypes.c_void_p(handle)), "arAllReduce")
+
+
+def arTune(comm, nBytes):
+    p, ch, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_float()
+    _check(lib().arTune(comm, int(nBytes), ctypes.byref(p), ctypes.byref(ch), ctypes.byref(t)), "arTune")
+    return p.value, ch.value, t.value
+
+
+def arTuneEval(nranks, maxChannels, nBytes, models, protoMask=7):
+    arr = (arTuneModel_t * 3)(*[arTuneModel_t(*m) for m in models])
+    p, ch, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_float()
+    rc = lib().arTuneEval(int(nranks), int(maxChannels), int(nBytes), arr, int(protoMask),
+                          ctypes.byref(p), ctypes.byref(ch), ctypes.byref(t))
+    _check(rc, "arTuneEval")
+    return p.value, ch.value, t.value
+
+
+def arTuneGetModel(comm, proto):
+    m = arTuneModel_t()
+    _check(lib().arTuneGetModel(comm, int(proto), ctypes.byref(m)), "arTuneGetModel")
+    return (m.baseLatUs, m.stepLatUs, m.bwPerChGBs, m.maxBwGBs)
+
+
+def arTuneSetModel(comm, proto, model):
+    m = arTuneModel_t(*model)
+    _check(lib().arTuneSetModel(comm, int(proto), ctypes.byref(m)), "arTuneSetModel")
+
+
+def arSetConfig(comm, proto, nChannels):
+    _check(lib().arSetConfig(comm, int(proto), int(nChannels)), "arSetConfig")
+
+
+def arGetPlan(comm, count, dtype, aligned128=True):
+    p = arPlan_t()
+    _check(lib().arGetPlan(comm, int(count), int(dtype), 1 if aligned128 else 0, ctypes.byref(p)), "arGetPlan")
+    return {f: getattr(p, f) for f, _ in arPlan_t._fields_}
+
+
+def arCommGetAsyncError(comm):
+    e = ctypes.c_int()
+    _check(lib().arCommGetAsyncError(comm, ctypes.byref(e)), "arCommGetAsyncError")
+    return e.value
+
+
+def arCommAbort(comm):
+    _check(lib().arCommAbort(comm), "arCommAbort")
+
+
+def arSetDebug(comm, knob, value):
+    _check(lib().arSetDebug(comm, int(knob), int(value)), "arSetDebug")
+
+
+def arDestroy(comm):
+    _check(lib().arDestroy(comm), "arDestroy")
+
+
+class Comm:
+    """Small convenience wrapper owning one communicator."""
+
+    def __init__(self, nranks, nChannels, proto=arProtoSimple):
+        if isinstance(proto, str):
+            proto = PROTO_BY_NAME[proto.lower()]
+        self.nranks = nranks
+        self.handle = arInit(nranks, nChannels, proto)
+
+    def allreduce(self, sendbufs, recvbufs, op=arSum, stream=None, count=None, dtype=None):
+        if isinstance(op, str):
+            op = OP_BY_NAME[op]
+        arAllReduce(self.handle, sendbufs, recvbufs, count=count, dtype=dtype, op=op, stream=stream)
+
+    def plan(self, count, dtype, aligned128=True):
+        if isinstance(dtype, str):
+            dtype = DTYPE_BY_NAME[dtype]
+        return arGetPlan(self.handle, count, dtype, aligned128)
+
+    def set_config(self, proto, nChannels):
+        if isinstance(proto, str):
+            proto = PROTO_BY_NAME[proto.lower()]
+        arSetConfig(self.handle, proto, nChannels)
+
+    def tune(self, nBytes):
+        return arTune(self.handle, nBytes)
+
+    def async_error(self):
+        return arCommGetAsyncError(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            arDestroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,507 @@
+// ar_comm.cpp -- communicator lifecycle, per-call planning and the C ABI.
+//
+// Init follows the reference's shape ["NCCL 原始碼解讀：一個 AllReduce 的 GPU
+// 旅程", ch.3 §3.1-§3.6]: validate, allocate the comm with magic sentinels,
+// read the environment once, provision per-protocol FIFOs and counters, and
+// make device state visible once.  There is no bootstrap: one process owns
+// every virtual rank.  An AllReduce follows ch.6 §一-§六: argument checks,
+// count == 0 and one-rank short cuts, tuning, channel split, kernel arguments,
+// one launch on the caller's stream.
+#include <ctype.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+
+#include "ar_internal.h"
+
+using namespace ar;
+
+namespace {
+
+constexpr uint64_t kCommMagic = 0x4152434f4d4d3031ull;   // "ARCOMM01"
+
+// ----------------------------------------------------------- environment
+// Read once per process and cached, like the reference's parameter cache
+// [ch.3 §3.5]; AR_PROTO uses the reference's list syntax with '^' to exclude.
+struct Env {
+  int protoMask = 7;      // allowed protocols for tuning
+  int forcedProto = -2;   // -2: none
+  int nChannels = 0;      // 0: not set
+  size_t sliceBytes = kDefaultSliceBytes;
+  int nSteps = kDefaultSteps;
+  int64_t timeoutUs = 5000000;
+  int debug = 0;          // 0 warn, 1 info, 2 trace
+};
+
+int protoFromName(const char* s, size_t n) {
+  char buf[16] = {0};
+  if (n >= sizeof(buf)) return -1;
+  for (size_t i = 0; i < n; ++i) buf[i] = (char)toupper((unsigned char)s[i]);
+  if (!strcmp(buf, "LL")) return arProtoLL;
+  if (!strcmp(buf, "LL128")) return arProtoLL128;
+  if (!strcmp(buf, "SIMPLE")) return arProtoSimple;
+  return -1;
+}
+
+const Env& env() {
+  static Env e;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    if (const char* p = getenv("AR_PROTO")) {
+      bool negate = p[0] == '^';
+      const char* s = negate ? p + 1 : p;
+      int mask = 0;
+      while (*s) {
+        const char* t = strchr(s, ',');
+        size_t n = t ? (size_t)(t - s) : strlen(s);
+        int pr = protoFromName(s, n);
+        if (pr >= 0) mask |= 1 << pr;
+        else fprintf(stderr, "[ar] WARN ignoring unknown protocol in AR_PROTO=%s\n", p);
+        s += n;
+        if (*s == ',') ++s;
+      }
+      if (negate) mask = 7 & ~mask;
+      if (mask != 0) {
+        e.protoMask = mask;
+        if (mask == 1 || mask == 2 || mask == 4) e.forcedProto = mask == 1 ? 0 : mask == 2 ? 1 : 2;
+      }
+    }
+    if (const char* p = getenv("AR_NCHANNELS")) e.nChannels = atoi(p);
+    if (const char* p = getenv("AR_SLICE_BYTES")) {
+      long long v = atoll(p);
+      if (v >= 16 && v % 16 == 0) e.sliceBytes = (size_t)v;
+      else fprintf(stderr, "[ar] WARN ignoring AR_SLICE_BYTES=%s (need a multiple of 16)\n", p);
+    }
+    if (const char* p = getenv("AR_STEPS")) {
+      int v = atoi(p);
+      if (v >= 2 && v <= 64) e.nSteps = v;
+    }
+    if (const char* p = getenv("AR_TIMEOUT_MS")) {
+      long long v = atoll(p);
+      if (v > 0) e.timeoutUs = v * 1000;
+    }
+    if (const char* p = getenv("AR_DEBUG")) {
+      if (!strcasecmp(p, "INFO")) e.debug = 1;
+      else if (!strcasecmp(p, "TRACE")) e.debug = 2;
+    }
+  });
+  return e;
+}
+
+// Tuner constants for MI355X, fitted to a protocol x size x channel sweep of
+// this library on one MI355X (see the benchmark's calibration mode).
+const arTuneModel_t kDefaultModels[3] = {
+    /* LL     */ {6.0f, 0.9f, 6.0f, 120.0f},
+    /* LL128  */ {7.0f, 1.1f, 6.0f, 220.0f},
+    /* Simple */ {9.0f, 1.5f, 6.0f, 330.0f},
+};
+
+}  // namespace
+
+struct arComm {
+  uint64_t startMagic;
+  int nranks;
+  int maxChannels;
+  int proto;            // default protocol or arProtoAuto
+  int nChannels;        // default channel count
+  int device;
+  int numCUs;
+  int wallClockKHz;
+  int nSlots;
+  size_t sliceBytes;
+  int lanesMax;         // lanes (channel x lane) per rank provisioned
+  char* fifo[3];
+  Conn* conn[3];
+  size_t fifoWorkerBytes[3];
+  Control* ctrlHost;
+  Control* ctrlDev;
+  arTuneModel_t models[3];
+  int64_t timeoutUs;
+  int deadRank;
+  hipStream_t lastStream;
+  bool launched;
+  bool aborted;
+  uint64_t opCount;
+  uint64_t endMagic;
+};
+
+namespace {
+
+bool commOk(const arComm* c) {
+  return c != nullptr && c->startMagic == kCommMagic && c->endMagic == kCommMagic;
+}
+
+int slotBytesOf(int proto) {
+  return proto == kSimple ? kSimpleSlotBytes : proto == kLL ? kLLSlotBytes : kLL128SlotBytes;
+}
+int slotPayloadOf(int proto) {
+  return proto == kSimple ? kSimpleSlotPayload : proto == kLL ? kLLSlotPayload : kLL128SlotPayload;
+}
+
+size_t chunkBytesOf(const arComm* c, int proto) {
+  if (proto == kSimple) return 2 * c->sliceBytes;   // one chunk = 2 slices
+  return proto == kLL ? kLLChunkBytes : kLL128ChunkBytes;
+}
+
+uint64_t divUpU(uint64_t x, uint64_t y) { return (x + y - 1) / y; }
+uint64_t alignUpU(uint64_t x, uint64_t a) { return divUpU(x, a) * a; }
+
+void freeComm(arComm* c) {
+  for (int p = 0; p < 3; ++p) {
+    if (c->fifo[p]) (void)hipFree(c->fifo[p]);
+    if (c->conn[p]) (void)hipFree(c->conn[p]);
+  }
+  if (c->ctrlHost) (void)hipHostFree(c->ctrlHost);
+  c->startMagic = c->endMagic = 0;
+  delete c;
+}
+
+// Protocol, channels, chunk, lanes and grid for one call.
+arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned128, Plan* plan) {
+  const Env& e = env();
+  const int esz = elemSize(dtype);
+  const uint64_t nBytes = count * (uint64_t)esz;
+  int proto = e.forcedProto != -2 ? e.forcedProto : c->proto;
+  int nch = e.nChannels > 0 ? e.nChannels : c->nChannels;
+  if (nch > c->maxChannels) nch = c->maxChannels;
+  float predicted = 0.0f;
+  if (proto == arProtoAuto) {
+    unsigned mask = (unsigned)e.protoMask;
+    if (!aligned128) mask &= ~(1u << arProtoLL128);
+    if (mask == 0) mask = 1u << arProtoSimple;
+    arProto_t p;
+    int ch;
+    arResult_t r = arTuneEval(c->nranks, c->maxChannels, nBytes, c->models, mask, &p, &ch, &predicted);
+    if (r != arSuccess) return r;
+    proto = p;
+    nch = ch < 1 ? 1 : ch;
+  } else {
+    if (proto == arProtoLL128 && !aligned128) return arInvalidUsage;   // LL128 needs 128-byte buffers
+    (void)arTuneEval(c->nranks, nch, nBytes, c->models, 1u << proto, nullptr, nullptr, &predicted);
+  }
+  const int N = c->nranks;
+  const uint64_t A = 16 / (uint64_t)esz;
+  plan->proto = proto;
+  plan->nChannels = nch;
+  plan->chunkElems = chunkBytesOf(c, proto) / (uint64_t)esz;
+  plan->slotBytes = slotBytesOf(proto);
+  plan->slotPayload = slotPayloadOf(proto);
+  plan->nSlots = c->nSlots;
+  plan->predictedUs = predicted;
+
+  // Members per workgroup: the whole ring when it fits (N <= 16), else
+  // balanced groups joined by agent-scope edges.
+  int nGroups = (N + kMaxMembersPerGroup - 1) / kMaxMembersPerGroup;
+  int groupSize = (N + nGroups - 1) / nGroups;
+  plan->groupSize = groupSize;
+  plan->nGroups = nGroups;
+  plan->block = groupSize * kWave;
+  plan->cooperative = nGroups > 1;
+
+  // Lanes per (rank, channel): enough wavefronts to fill the chip (about 32
+  // per CU), but never a lane share below two FIFO slots of the largest chunk.
+  const uint64_t per = alignUpU(divUpU(count, (uint64_t)nch), A);
+  const uint64_t loop = (uint64_t)N * plan->chunkElems;
+  const uint64_t cur = per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
+  const uint64_t chunkBytes = cur * (uint64_t)esz;
+  int lanes = (int)((uint64_t)c->numCUs * 32 / ((uint64_t)N * (uint64_t)nch));
+  const int byChunk = (int)(chunkBytes / (2 * (uint64_t)plan->slotPayload));
+  if (lanes > byChunk) lanes = byChunk;
+  if (lanes > c->lanesMax / nch) lanes = c->lanesMax / nch;
+  if (lanes < 1) lanes = 1;
+
+  auto gridFor = [&](int ln) {
+    const int lt = nch * ln;
+    return nGroups == 1 ? lt : ((lt + 7) / 8) * 8 * nGroups;
+  };
+  if (plan->cooperative) {
+    int perCU = 0;
+    if (ringKernelOccupancy(proto, dtype, op, plan->block, &perCU) != hipSuccess) return arHipError;
+    const int capacity = perCU * c->numCUs;
+    while (lanes > 1 && gridFor(lanes) > capacity) --lanes;
+    if (gridFor(lanes) > capacity) return arInvalidUsage;
+  }
+  plan->lanes = lanes;
+  plan->grid = gridFor(lanes);
+  return arSuccess;
+}
+
+bool rangesOverlap(uintptr_t a, uintptr_t b, size_t n) { return a < b + n && b < a + n; }
+
+}  // namespace
+
+extern "C" {
+
+const char* arGetErrorString(arResult_t r) {
+  switch (r) {
+    case arSuccess: return "no error";
+    case arHipError: return "HIP runtime error (or no usable GPU)";
+    case arSystemError: return "system error (host allocation or OS call failed)";
+    case arInternalError: return "internal error";
+    case arInvalidArgument: return "invalid argument";
+    case arInvalidUsage: return "invalid usage";
+    case arRemoteError: return "remote error: a ring member timed out or the comm was aborted";
+    case arInProgress: return "operation in progress";
+    default: return "unknown result code";
+  }
+}
+
+arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arAlgo_t algo) {
+  if (out == nullptr) return arInvalidArgument;
+  *out = nullptr;
+  if (nranks < 1 || nranks > AR_MAX_RANKS) return arInvalidArgument;
+  if (nChannels < 1 || nChannels > AR_MAX_CHANNELS) return arInvalidArgument;
+  if (proto != arProtoAuto && proto != arProtoLL && proto != arProtoLL128 && proto != arProtoSimple)
+    return arInvalidArgument;
+  if (algo != arAlgoRing) return arInvalidArgument;
+  const Env& e = env();
+
+  int dev = 0, ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return arHipError;
+  if (hipGetDevice(&dev) != hipSuccess) return arHipError;
+  int cus = 0, clk = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return arHipError;
+  if (hipDeviceGetAttribute(&clk, hipDeviceAttributeWallClockRate, dev) != hipSuccess || clk <= 0) clk = 100000;
+
+  arComm* c = new (std::nothrow) arComm();
+  if (c == nullptr) return arSystemError;
+  c->startMagic = c->endMagic = kCommMagic;
+  c->nranks = nranks;
+  c->maxChannels = nChannels;
+  c->proto = proto;
+  c->nChannels = nChannels;
+  c->device = dev;
+  c->numCUs = cus;
+  c->wallClockKHz = clk;
+  c->nSlots = e.nSteps;
+  c->sliceBytes = e.sliceBytes;
+  c->timeoutUs = e.timeoutUs;
+  c->deadRank = -1;
+  for (int p = 0; p < 3; ++p) c->models[p] = kDefaultModels[p];
+
+  // FIFOs and counters, one set per protocol (a line of one protocol must
+  // never be read as another's: LL flags live inside the data).
+  const int lanesMax = kMaxWorkers / nranks > nChannels ? kMaxWorkers / nranks : nChannels;
+  c->lanesMax = lanesMax;
+  const size_t workers = (size_t)nranks * (size_t)lanesMax;
+  if (nranks > 1) {
+    for (int p = 0; p < 3; ++p) {
+      c->fifoWorkerBytes[p] = (size_t)c->nSlots * (size_t)slotBytesOf(p);
+      const size_t fb = workers * c->fifoWorkerBytes[p];
+      const size_t cb = workers * sizeof(Conn);
+      if (hipMalloc((void**)&c->fifo[p], fb) != hipSuccess || hipMalloc((void**)&c->conn[p], cb) != hipSuccess ||
+          hipMemset(c->fifo[p], 0, fb) != hipSuccess || hipMemset(c->conn[p], 0, cb) != hipSuccess) {
+        freeComm(c);
+        return arHipError;
+      }
+    }
+  }
+  if (hipHostMalloc((void**)&c->ctrlHost, sizeof(Control), hipHostMallocCoherent | hipHostMallocMapped) !=
+      hipSuccess) {
+    freeComm(c);
+    return arHipError;
+  }
+  memset(c->ctrlHost, 0, sizeof(Control));
+  if (hipHostGetDevicePointer((void**)&c->ctrlDev, c->ctrlHost, 0) != hipSuccess) {
+    freeComm(c);
+    return arHipError;
+  }
+  if (hipDeviceSynchronize() != hipSuccess) {
+    freeComm(c);
+    return arHipError;
+  }
+  if (e.debug >= 1)
+    fprintf(stderr, "[ar] INFO init nranks=%d maxChannels=%d proto=%d CUs=%d slots=%d slice=%zu\n", nranks,
+            nChannels, (int)proto, cus, c->nSlots, c->sliceBytes);
+  *out = c;
+  return arSuccess;
+}
+
+arResult_t arSetConfig(arComm_t c, arProto_t proto, int nChannels) {
+  if (!commOk(c)) return arInvalidArgument;
+  if (proto != arProtoAuto && proto != arProtoLL && proto != arProtoLL128 && proto != arProtoSimple)
+    return arInvalidArgument;
+  if (nChannels < 1 || nChannels > c->maxChannels) return arInvalidArgument;
+  c->proto = proto;
+  c->nChannels = nChannels;
+  return arSuccess;
+}
+
+arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
+  if (!commOk(c)) return arInvalidArgument;
+  if (knob == arDebugTimeoutUs) {
+    if (value <= 0) return arInvalidArgument;
+    c->timeoutUs = value;
+    return arSuccess;
+  }
+  if (knob == arDebugDeadRank) {
+    if (value < -1 || value >= c->nranks) return arInvalidArgument;
+    c->deadRank = (int)value;
+    return arSuccess;
+  }
+  return arInvalidArgument;
+}
+
+arResult_t arTuneGetModel(arComm_t c, arProto_t proto, arTuneModel_t* model) {
+  if (!commOk(c) || model == nullptr || proto < arProtoLL || proto > arProtoSimple) return arInvalidArgument;
+  *model = c->models[proto];
+  return arSuccess;
+}
+
+arResult_t arTuneSetModel(arComm_t c, arProto_t proto, const arTuneModel_t* model) {
+  if (!commOk(c) || model == nullptr || proto < arProtoLL || proto > arProtoSimple) return arInvalidArgument;
+  if (!(model->bwPerChGBs > 0.0f) || !(model->maxBwGBs > 0.0f) || model->baseLatUs < 0.0f ||
+      model->stepLatUs < 0.0f)
+    return arInvalidArgument;
+  c->models[proto] = *model;
+  return arSuccess;
+}
+
+arResult_t arTune(arComm_t c, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs) {
+  if (!commOk(c)) return arInvalidArgument;
+  return arTuneEval(c->nranks, c->maxChannels, nBytes, c->models, (unsigned)env().protoMask, proto, nChannels,
+                    predictedUs);
+}
+
+arResult_t arGetPlan(arComm_t c, size_t count, arDataType_t dtype, int aligned128, arPlan_t* out) {
+  if (!commOk(c) || out == nullptr || elemSize(dtype) == 0) return arInvalidArgument;
+  const int op = dtype == arUint64 ? arProbe : arSum;
+  memset(out, 0, sizeof(*out));
+  const double S = (double)count * elemSize(dtype);
+  out->modelBytes = 5.0 * (double)(c->nranks - 1) * S;
+  if (c->nranks == 1 || count == 0) {
+    out->proto = arProtoSimple;
+    return arSuccess;
+  }
+  Plan p;
+  arResult_t r = makePlan(c, count, dtype, op, aligned128 != 0, &p);
+  if (r != arSuccess) return r;
+  out->proto = p.proto;
+  out->nChannels = p.nChannels;
+  out->chunkElems = p.chunkElems;
+  out->lanesPerChannel = p.lanes;
+  out->ranksPerGroup = p.groupSize;
+  out->workgroups = p.grid;
+  out->threadsPerGroup = p.block;
+  out->stepBytes = p.slotBytes;
+  out->stepPayload = p.slotPayload;
+  out->nSlots = p.nSlots;
+  out->predictedUs = p.predictedUs;
+  return arSuccess;
+}
+
+arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t count,
+                       arDataType_t dtype, arRedOp_t op, void* stream) {
+  if (!commOk(c)) return arInvalidArgument;
+  if (c->aborted) return arInvalidUsage;
+  const int esz = elemSize(dtype);
+  if (esz == 0) return arInvalidArgument;
+  if (op != arSum && op != arMax && op != arMin && op != arProbe) return arInvalidArgument;
+  if ((op == arProbe) != (dtype == arUint64)) return arInvalidArgument;
+  if (count == 0) return arSuccess;   // empty collective: no work
+  if (sendbufs == nullptr || recvbufs == nullptr) return arInvalidArgument;
+  const int N = c->nranks;
+  if (count > (uint64_t)1 << 40) return arInvalidArgument;
+  const size_t bytes = count * (size_t)esz;
+  bool aligned16 = true, aligned128 = true;
+  for (int r = 0; r < N; ++r) {
+    const uintptr_t s = (uintptr_t)sendbufs[r], d = (uintptr_t)recvbufs[r];
+    if (s == 0 || d == 0) return arInvalidArgument;
+    if (s % (uintptr_t)esz != 0 || d % (uintptr_t)esz != 0) return arInvalidArgument;
+    aligned16 = aligned16 && s % 16 == 0 && d % 16 == 0;
+    aligned128 = aligned128 && s % 128 == 0 && d % 128 == 0;
+  }
+  // Outputs must not overlap each other or another rank's input; an output
+  // may be its own rank's input exactly (in place).
+  for (int i = 0; i < N; ++i) {
+    const uintptr_t di = (uintptr_t)recvbufs[i];
+    if (di != (uintptr_t)sendbufs[i] && rangesOverlap(di, (uintptr_t)sendbufs[i], bytes)) return arInvalidArgument;
+    for (int j = 0; j < N; ++j) {
+      if (j == i) continue;
+      if (rangesOverlap(di, (uintptr_t)recvbufs[j], bytes)) return arInvalidArgument;
+      if (rangesOverlap(di, (uintptr_t)sendbufs[j], bytes)) return arInvalidArgument;
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  c->opCount++;
+
+  if (N == 1) {   // one rank: the result is the input [ch.6 §三, one-rank path]
+    c->lastStream = st;
+    c->launched = true;
+    if (recvbufs[0] == sendbufs[0]) return arSuccess;
+    return hipMemcpyAsync(recvbufs[0], sendbufs[0], bytes, hipMemcpyDeviceToDevice, st) == hipSuccess
+               ? arSuccess
+               : arHipError;
+  }
+
+  Plan plan;
+  arResult_t r = makePlan(c, count, dtype, op, aligned128, &plan);
+  if (r != arSuccess) return r;
+
+  KernelArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int i = 0; i < N; ++i) {
+    a.send[i] = sendbufs[i];
+    a.recv[i] = recvbufs[i];
+  }
+  a.fifo = c->fifo[plan.proto];
+  a.conn = c->conn[plan.proto];
+  a.ctrl = c->ctrlDev;
+  a.count = count;
+  a.chunkElems = plan.chunkElems;
+  a.fifoWorkerBytes = c->fifoWorkerBytes[plan.proto];
+  a.timeoutTicks = (uint64_t)c->timeoutUs * (uint64_t)c->wallClockKHz / 1000u;
+  a.nranks = N;
+  a.nChannels = plan.nChannels;
+  a.lanes = plan.lanes;
+  a.groupSize = plan.groupSize;
+  a.nGroups = plan.nGroups;
+  a.nSlots = plan.nSlots;
+  a.aligned16 = aligned16 ? 1 : 0;
+  a.deadRank = c->deadRank;
+
+  if (env().debug >= 1)
+    fprintf(stderr,
+            "[ar] INFO op %llu count=%zu dtype=%d op=%d proto=%d nch=%d chunk=%llu lanes=%d groups=%dx%d grid=%d "
+            "block=%d coop=%d pred=%.1fus\n",
+            (unsigned long long)c->opCount, count, (int)dtype, (int)op, plan.proto, plan.nChannels,
+            (unsigned long long)plan.chunkElems, plan.lanes, plan.nGroups, plan.groupSize, plan.grid, plan.block,
+            (int)plan.cooperative, plan.predictedUs);
+  hipError_t he = launchRing(plan, dtype, op, a, st);
+  if (he != hipSuccess) {
+    fprintf(stderr, "[ar] WARN kernel launch failed: %s\n", hipGetErrorString(he));
+    return arHipError;
+  }
+  c->lastStream = st;
+  c->launched = true;
+  return arSuccess;
+}
+
+arResult_t arCommGetAsyncError(arComm_t c, arResult_t* err) {
+  if (!commOk(c) || err == nullptr) return arInvalidArgument;
+  const uint32_t st = __atomic_load_n(&c->ctrlHost->status, __ATOMIC_ACQUIRE);
+  if (st != 0) c->aborted = true;
+  *err = (st != 0 || c->ctrlHost->abortFlag != 0) ? arRemoteError : arSuccess;
+  return arSuccess;
+}
+
+arResult_t arCommAbort(arComm_t c) {
+  if (!commOk(c)) return arInvalidArgument;
+  __atomic_store_n(&c->ctrlHost->abortFlag, 1u, __ATOMIC_RELEASE);
+  c->aborted = true;
+  return arSuccess;
+}
+
+arResult_t arDestroy(arComm_t c) {
+  if (c == nullptr) return arSuccess;
+  if (!commOk(c)) return arInvalidArgument;
+  arResult_t r = arSuccess;
+  if (c->launched && hipStreamSynchronize(c->lastStream) != hipSuccess) r = arHipError;
+  freeComm(c);
+  return r;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// ar_internal.h -- layouts shared by the host side of libar.so and its HIP
+// kernels.  Nothing here is visible through the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ar.h"
+
+namespace ar {
+
+constexpr int kWave = 64;                 // CDNA wavefront width
+constexpr int kMaxMembersPerGroup = 16;   // ring members (one wavefront each) per workgroup
+constexpr int kMaxWorkers = 16384;        // (rank, lane) wavefronts a comm provisions FIFOs for
+constexpr int kDefaultSteps = 8;          // FIFO depth in slots, the pages' step count
+
+// One ring member is one wavefront.  Per FIFO slot ("step") a wavefront moves
+// kUnroll pieces per lane:
+//   Simple: 16-byte pieces, slot = kUnroll KiB, all payload.
+//   LL:     16-byte lines {data0, flag, data1, flag}: 8 payload bytes per lane.
+//   LL128:  each wavefront instruction fills 8 lines of 128 bytes; a line is
+//           seven 16-byte payload pieces, 8 payload bytes and an 8-byte flag.
+constexpr int kSimpleUnroll = 4;
+constexpr int kLLUnroll = 2;
+constexpr int kLL128Unroll = 2;
+
+constexpr int kSimpleSlotBytes = kSimpleUnroll * kWave * 16;   // 4096
+constexpr int kSimpleSlotPayload = kSimpleSlotBytes;
+constexpr int kLLSlotBytes = kLLUnroll * kWave * 16;           // 2048 wire
+constexpr int kLLSlotPayload = kLLUnroll * kWave * 8;          // 1024 payload
+constexpr int kLL128LinePayload = 120;
+constexpr int kLL128UnitBytes = kWave * 16;                    // 1024 = 8 lines
+constexpr int kLL128UnitPayload = 8 * kLL128LinePayload;       // 960
+constexpr int kLL128SlotBytes = kLL128Unroll * kLL128UnitBytes;
+constexpr int kLL128SlotPayload = kLL128Unroll * kLL128UnitPayload;
+
+// Nominal chunk sizes (bytes).  Simple: two slices of AR_SLICE_BYTES (one
+// chunk = 2 slices).  LL and LL128: builder choices, multiples of 16 bytes.
+constexpr size_t kDefaultSliceBytes = 512 * 1024;
+constexpr size_t kLLChunkBytes = 64 * 1024;
+constexpr size_t kLL128ChunkBytes = 240 * 1024;
+
+// Receive-side counters of one FIFO (one per protocol and worker).  The
+// sender bumps `tail` after filling a slot, the receiver bumps `head` after
+// draining one; each counter has a 128-byte line of its own.  Both are
+// monotonic for the life of the comm, so no reset is ever needed between
+// calls; at every call boundary tail == head.
+struct Conn {
+  uint64_t tail;
+  uint64_t pad0[15];
+  uint64_t head;
+  uint64_t pad1[15];
+};
+static_assert(sizeof(Conn) == 256, "Conn layout");
+
+// Host-pinned, device-visible control block.
+struct Control {
+  uint32_t abortFlag;   // set by arCommAbort
+  uint32_t pad0[31];
+  uint32_t status;      // 0 ok; kStatusTimeout / kStatusAbort from the kernel
+  uint32_t pad1[31];
+};
+constexpr uint32_t kStatusTimeout = 1;
+constexpr uint32_t kStatusAbort = 2;
+
+enum Proto : int { kLL = 0, kLL128 = 1, kSimple = 2 };
+
+struct KernelArgs {
+  const void* send[AR_MAX_RANKS];
+  void* recv[AR_MAX_RANKS];
+  char* fifo;                 // this protocol's FIFOs, fifoWorkerBytes per worker
+  Conn* conn;                 // this protocol's counters, one per worker
+  Control* ctrl;              // host-pinned control block (device address)
+  uint64_t count;             // elements per rank
+  uint64_t chunkElems;        // nominal chunk (elements)
+  uint64_t fifoWorkerBytes;   // nSlots * slot bytes
+  uint64_t timeoutTicks;      // wall-clock ticks a wait may take
+  int nranks;
+  int nChannels;
+  int lanes;                  // wavefronts per (rank, channel)
+  int groupSize;              // ring members per workgroup
+  int nGroups;                // workgroups per (channel, lane)
+  int nSlots;
+  int aligned16;              // every send/recv base is 16-byte aligned
+  int deadRank;               // debug: this rank's members return at once
+};
+
+// Everything arAllReduce decides for one call.
+struct Plan {
+  int proto;
+  int nChannels;
+  uint64_t chunkElems;
+  int lanes;
+  int groupSize;
+  int nGroups;
+  int grid;
+  int block;
+  int slotBytes;
+  int slotPayload;
+  int nSlots;
+  bool cooperative;
+  float predictedUs;
+};
+
+// Provided by ar_kernels.hip.
+hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream);
+hipError_t ringKernelOccupancy(int proto, int dtype, int op, int block, int* blocksPerCU);
+
+inline int elemSize(int dtype) {
+  switch (dtype) {
+    case arInt32: case arFloat32: return 4;
+    case arFloat16: case arBfloat16: return 2;
+    case arUint64: return 8;
+    default: return 0;
+  }
+}
+
+}  // namespace ar

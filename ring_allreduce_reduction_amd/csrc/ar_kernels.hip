@@ -1,0 +1,607 @@
+// ar_kernels.hip -- the ring AllReduce data path for gfx950.
+//
+// What runs: one wavefront per ring member (virtual rank r, channel ch, lane
+// k).  A member walks the ring schedule of the pages ["NCCL 原始碼解讀：一個
+// AllReduce 的 GPU 旅程", ch.2 §2.3, RingARAlgorithm::getNextSendAddr and the
+// reduce-scatter / all-gather walkthrough]: at stage s it sends chunk
+// (r - 1 - s) mod N, so over 2N-1 stage slots it does
+//     send | recv-reduce-send x (N-2) | recv-reduce-copy-send |
+//     recv-copy-send x (N-2) | recv
+// and every transfer goes through a FIFO in HBM owned by the receiver,
+// with credits (head) and readiness (tail counter, or per-line flags for the
+// LL / LL128 wire formats) [same book, ch.2 §2.4, the send/recv memory with
+// head and tail counters on separate cache lines, and the LL / LL128 /
+// Simple protocols].
+//
+// Where it runs: the N members of one (channel, lane) sit in one workgroup
+// (N <= 16), so every producer/consumer pair shares a CU and its vector L1:
+// the FIFO handoff needs only workgroup-scope release/acquire, which on gfx950
+// is a plain ordered store / load, and there is no cross-workgroup wait at all
+// (no co-residency requirement, no deadlock from scheduling).  For N > 16 the
+// ring is cut into groups of up to 16 members; an edge between groups uses
+// agent-scope release/acquire and the launch is cooperative so that every
+// group is resident.
+//
+// Each member reads only its own send buffer, writes only its own receive
+// buffer and its successor's FIFO, so in-place use is safe: a member reads
+// chunk c of its input before it writes chunk c of its output.
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+typedef uint32_t u32;
+typedef uint64_t u64;
+typedef u32 v4u __attribute__((ext_vector_type(4)));
+typedef u32 v2u __attribute__((ext_vector_type(2)));
+
+enum Kind : int { kSend = 0, kRecvReduceSend = 1, kRecvReduceCopySend = 2, kRecvCopySend = 3, kRecv = 4 };
+
+__device__ __forceinline__ u64 divUp(u64 x, u64 y) { return (x + y - 1) / y; }
+__device__ __forceinline__ u64 alignUp(u64 x, u64 a) { return divUp(x, a) * a; }
+__device__ __forceinline__ u64 umin(u64 a, u64 b) { return a < b ? a : b; }
+
+// ------------------------------------------------------------- element ops
+// Sum / Max / Min with acc the incoming partial and x the local value.
+// 16-bit floats widen exactly to f32, combine, and round back to nearest-even.
+
+__device__ __forceinline__ float bf16ToF32(u32 h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ u32 f32ToBf16(float f) {
+  u32 u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;   // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float f16ToF32(u32 h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ u32 f32ToF16(float f) {
+  return (u32)__builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32: RNE, keeps subnormals
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ u32 combineHalf(u32 acc, u32 x) {   // one 16-bit element
+  float a = DT == arBfloat16 ? bf16ToF32(acc) : f16ToF32(acc);
+  float b = DT == arBfloat16 ? bf16ToF32(x) : f16ToF32(x);
+  if (OP == arSum) {
+    float s = a + b;
+    return DT == arBfloat16 ? f32ToBf16(s) : f32ToF16(s);
+  }
+  if (OP == arMax) return (b > a) ? x : acc;
+  return (b < a) ? x : acc;
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ u32 combineWord(u32 acc, u32 x) {   // one 32-bit word
+  if (DT == arFloat32) {
+    float a = __uint_as_float(acc), b = __uint_as_float(x);
+    if (OP == arSum) return __float_as_uint(a + b);
+    if (OP == arMax) return (b > a) ? x : acc;
+    return (b < a) ? x : acc;
+  } else if (DT == arInt32) {
+    if (OP == arSum) return acc + x;   // wraps
+    if (OP == arMax) return ((int)x > (int)acc) ? x : acc;
+    return ((int)x < (int)acc) ? x : acc;
+  } else {                             // two 16-bit elements
+    u32 lo = combineHalf<DT, OP>(acc & 0xffffu, x & 0xffffu);
+    u32 hi = combineHalf<DT, OP>(acc >> 16, x >> 16);
+    return lo | (hi << 16);
+  }
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ v4u combine(v4u acc, v4u x) {
+  v4u r;
+  if (DT == arUint64) {                // probe: acc*16 + x on each 64-bit half
+    u64 a0 = ((u64)acc.y << 32) | acc.x, x0 = ((u64)x.y << 32) | x.x;
+    u64 a1 = ((u64)acc.w << 32) | acc.z, x1 = ((u64)x.w << 32) | x.z;
+    a0 = a0 * 16u + x0;
+    a1 = a1 * 16u + x1;
+    r.x = (u32)a0; r.y = (u32)(a0 >> 32); r.z = (u32)a1; r.w = (u32)(a1 >> 32);
+  } else {
+    r.x = combineWord<DT, OP>(acc.x, x.x);
+    r.y = combineWord<DT, OP>(acc.y, x.y);
+    r.z = combineWord<DT, OP>(acc.z, x.z);
+    r.w = combineWord<DT, OP>(acc.w, x.w);
+  }
+  return r;
+}
+
+// ------------------------------------------------------------- memory access
+// User buffers stream through once: non-temporal hints keep them from
+// evicting the FIFO slots, which are re-used and should stay in cache.
+
+__device__ __forceinline__ v4u ldNt16(const char* p) { return __builtin_nontemporal_load((const v4u*)p); }
+__device__ __forceinline__ v2u ldNt8(const char* p) { return __builtin_nontemporal_load((const v2u*)p); }
+__device__ __forceinline__ void stNt16(char* p, v4u v) { __builtin_nontemporal_store(v, (v4u*)p); }
+__device__ __forceinline__ void stNt8(char* p, v2u v) { __builtin_nontemporal_store(v, (v2u*)p); }
+
+// Load `pieceBytes` (16 or 8) user bytes at p of which `valid` are in range;
+// bytes past the range read as zero.  Element-wise when short or unaligned.
+template <int ESZ>
+__device__ __forceinline__ v4u loadUser(const char* p, long valid, int pieceBytes, bool aligned) {
+  v4u v = {0u, 0u, 0u, 0u};
+  if (valid >= pieceBytes && aligned) {
+    if (pieceBytes == 16) {
+      v = ldNt16(p);
+    } else {
+      v2u t = ldNt8(p);
+      v.x = t.x; v.y = t.y;
+    }
+  } else if (valid > 0) {
+    u32 w[4] = {0u, 0u, 0u, 0u};
+    int nb = valid < pieceBytes ? (int)valid : pieceBytes;
+    for (int b = 0; b < nb; b += ESZ) {
+      if (ESZ == 2) {
+        u32 h = *(const uint16_t*)(p + b);
+        w[b >> 2] |= h << ((b & 2) * 8);
+      } else if (ESZ == 4) {
+        w[b >> 2] = *(const u32*)(p + b);
+      } else {
+        u64 d = *(const u64*)(p + b);
+        w[b >> 2] = (u32)d;
+        w[(b >> 2) + 1] = (u32)(d >> 32);
+      }
+    }
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+  }
+  return v;
+}
+
+template <int ESZ>
+__device__ __forceinline__ void storeUser(char* p, v4u v, long valid, int pieceBytes, bool aligned) {
+  if (valid >= pieceBytes && aligned) {
+    if (pieceBytes == 16) {
+      stNt16(p, v);
+    } else {
+      v2u t; t.x = v.x; t.y = v.y;
+      stNt8(p, t);
+    }
+  } else if (valid > 0) {
+    u32 w[4] = {v.x, v.y, v.z, v.w};
+    int nb = valid < pieceBytes ? (int)valid : pieceBytes;
+    for (int b = 0; b < nb; b += ESZ) {
+      if (ESZ == 2) {
+        *(uint16_t*)(p + b) = (uint16_t)(w[b >> 2] >> ((b & 2) * 8));
+      } else if (ESZ == 4) {
+        *(u32*)(p + b) = w[b >> 2];
+      } else {
+        *(u64*)(p + b) = (u64)w[b >> 2] | ((u64)w[(b >> 2) + 1] << 32);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- flags
+// Scope of an edge: workgroup when producer and consumer share the
+// workgroup, agent otherwise.
+
+__device__ __forceinline__ u64 ldCounter(const u64* p, bool agent) {
+  u64 v = agent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // every lane read the same word; make the value provably uniform
+  u32 lo = __builtin_amdgcn_readfirstlane((u32)v);
+  u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
+  if (agent) __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  else __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void stRelaxed64(u64* p, u64 v, bool agent) {
+  if (agent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ u64 ldRelaxed64(const u64* p, bool agent) {
+  return agent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void fenceAcquire(bool agent) {
+  if (agent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+__device__ __forceinline__ void fenceRelease(bool agent) {
+  if (agent) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
+
+// Bounded waiting.  Every spin sleeps briefly; every 256 spins the abort word
+// and the wall clock are checked, and a hard cap on spins backs the clock up.
+// On give-up the member records why and the caller returns, so every
+// wavefront of the kernel always exits.
+struct Waiter {
+  u32 spins = 0;
+  u64 t0 = 0;
+};
+
+__device__ __forceinline__ bool keepWaiting(Control* ctrl, u64 timeoutTicks, Waiter& w) {
+  if (w.spins == 0) w.t0 = wall_clock64();
+  ++w.spins;
+  __builtin_amdgcn_s_sleep(1);
+  if ((w.spins & 255u) == 0) {
+    u32 ab = __hip_atomic_load(&ctrl->abortFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    u32 code = 0;
+    if (__builtin_amdgcn_readfirstlane(ab) != 0) code = kStatusAbort;
+    else if (wall_clock64() - w.t0 > timeoutTicks || w.spins >= (1u << 30)) code = kStatusTimeout;
+    if (code != 0) {
+      __hip_atomic_store(&ctrl->status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      return false;
+    }
+  }
+  return true;
+}
+
+// Wait until *p >= target.
+__device__ __forceinline__ bool waitGeq(const KernelArgs& a, const u64* p, u64 target, bool agent) {
+  if (ldCounter(p, agent) >= target) return true;
+  Waiter w;
+  while (true) {
+    if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+    if (ldCounter(p, agent) >= target) return true;
+  }
+}
+
+// ------------------------------------------------------------- one member
+
+struct Member {
+  int lane;
+  char* rfifo;        // my FIFO (predecessor writes it)
+  char* sfifo;        // successor's FIFO (I write it)
+  Conn* self;
+  Conn* succ;
+  u64 recvStep;       // slots consumed from my FIFO so far (== self->head)
+  u64 sendStep;       // slots written into the successor's FIFO (== succ->tail)
+  u32 recvSlot;       // recvStep % nSlots
+  u32 sendSlot;       // sendStep % nSlots
+  bool recvAgent;
+  bool sendAgent;
+  bool aligned;
+};
+
+__device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
+  // slot sendStep % nSlots is free once the successor consumed step sendStep - nSlots
+  u64 need = m.sendStep + 1 > (u64)a.nSlots ? m.sendStep + 1 - (u64)a.nSlots : 0;
+  if (!waitGeq(a, &m.succ->head, need, m.sendAgent)) return false;
+  fenceAcquire(m.sendAgent);
+  return true;
+}
+
+__device__ __forceinline__ void advanceSend(const KernelArgs& a, Member& m) {
+  ++m.sendStep;
+  if (++m.sendSlot == (u32)a.nSlots) m.sendSlot = 0;
+}
+__device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
+  ++m.recvStep;
+  if (m.lane == 0) stCounterRelease(&m.self->head, m.recvStep, m.recvAgent);
+  if (++m.recvSlot == (u32)a.nSlots) m.recvSlot = 0;
+}
+
+// One FIFO step of `kind`; `valid` payload bytes start at inp / outp.
+template <int PROTO, int DT, int OP>
+__device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, const char* inp, char* outp,
+                                     long valid) {
+  constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
+  constexpr int U = PROTO == kSimple ? kSimpleUnroll : PROTO == kLL ? kLLUnroll : kLL128Unroll;
+  constexpr int SLOT = PROTO == kSimple ? kSimpleSlotBytes : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  const bool hasLocal = kind <= kRecvReduceCopySend;
+  const bool hasRecv = kind >= kRecvReduceSend;
+  const bool hasSend = kind <= kRecvCopySend;
+  const bool hasOut = kind >= kRecvReduceCopySend;
+  const int lane = m.lane;
+
+  // piece geometry of this lane: payload offset, payload bytes, wire offset
+  int payOff[U], payBytes[U], wireOff[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (PROTO == kSimple) {
+      payOff[u] = (u * kWave + lane) * 16; payBytes[u] = 16; wireOff[u] = payOff[u];
+    } else if (PROTO == kLL) {
+      payOff[u] = (u * kWave + lane) * 8; payBytes[u] = 8; wireOff[u] = (u * kWave + lane) * 16;
+    } else {
+      const int line = lane >> 3, j = lane & 7;
+      payOff[u] = u * kLL128UnitPayload + (j < 7 ? (line * 7 + j) * 16 : 896 + line * 8);
+      payBytes[u] = j < 7 ? 16 : 8;
+      wireOff[u] = u * kLL128UnitBytes + lane * 16;
+    }
+  }
+
+  if (hasSend && !waitCredit(a, m)) return false;
+
+  v4u v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    v[u] = hasLocal ? loadUser<ESZ>(inp + payOff[u], valid - payOff[u], payBytes[u], m.aligned)
+                    : v4u{0u, 0u, 0u, 0u};
+  }
+
+  if (hasRecv) {
+    const char* slot = m.rfifo + (size_t)m.recvSlot * SLOT;
+    v4u in[U];
+    if (PROTO == kSimple) {
+      if (!waitGeq(a, &m.self->tail, m.recvStep + 1, m.recvAgent)) return false;
+      fenceAcquire(m.recvAgent);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        in[u] = payOff[u] < valid ? *(const v4u*)(slot + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+    } else if (PROTO == kLL) {
+      const u32 flag = (u32)(m.recvStep + 1);
+      bool done[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) { done[u] = payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
+      Waiter w;
+      while (true) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (!done[u]) {
+            const u64* line = (const u64*)(slot + wireOff[u]);
+            u64 w0 = ldRelaxed64(line, m.recvAgent);
+            u64 w1 = ldRelaxed64(line + 1, m.recvAgent);
+            if ((u32)(w0 >> 32) == flag && (u32)(w1 >> 32) == flag) {
+              in[u].x = (u32)w0; in[u].y = (u32)w1; done[u] = true;
+            } else {
+              all = false;
+            }
+          }
+        }
+        if (__all(all)) break;
+        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+      }
+    } else {  // LL128: poll the flag of every live line, then read payload
+      const u64 flag = m.recvStep + 1;
+      const bool flagLane = (lane & 7) == 7;
+      bool done[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
+      Waiter w;
+      while (true) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (!done[u]) {
+            if (ldRelaxed64((const u64*)(slot + wireOff[u] + 8), m.recvAgent) == flag) done[u] = true;
+            else all = false;
+          }
+        }
+        if (__all(all)) break;
+        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+      }
+      fenceAcquire(m.recvAgent);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        in[u] = v4u{0u, 0u, 0u, 0u};
+        if (u * kLL128UnitPayload < valid) {
+          if (payBytes[u] == 16) {
+            in[u] = *(const v4u*)(slot + wireOff[u]);
+          } else {
+            v2u t = *(const v2u*)(slot + wireOff[u]);
+            in[u].x = t.x; in[u].y = t.y;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = hasLocal ? combine<DT, OP>(in[u], v[u]) : in[u];
+  }
+
+  if (hasOut) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) storeUser<ESZ>(outp + payOff[u], v[u], valid - payOff[u], payBytes[u], m.aligned);
+  }
+
+  if (hasSend) {
+    char* slot = m.sfifo + (size_t)m.sendSlot * SLOT;
+    if (PROTO == kSimple) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
+      fenceRelease(m.sendAgent);
+      if (lane == 0) stRelaxed64(&m.succ->tail, m.sendStep + 1, m.sendAgent);
+    } else if (PROTO == kLL) {
+      const u64 flag = (u64)(u32)(m.sendStep + 1) << 32;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (payOff[u] < valid) {
+          u64* line = (u64*)(slot + wireOff[u]);
+          stRelaxed64(line, flag | v[u].x, m.sendAgent);
+          stRelaxed64(line + 1, flag | v[u].y, m.sendAgent);
+        }
+      }
+    } else {  // LL128: payload, release, then the flag word of each live line
+      const bool flagLane = (lane & 7) == 7;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u * kLL128UnitPayload < valid) {
+          if (payBytes[u] == 16) {
+            *(v4u*)(slot + wireOff[u]) = v[u];
+          } else {
+            v2u t; t.x = v[u].x; t.y = v[u].y;
+            *(v2u*)(slot + wireOff[u]) = t;
+          }
+        }
+      }
+      fenceRelease(m.sendAgent);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (flagLane && u * kLL128UnitPayload < valid)
+          stRelaxed64((u64*)(slot + wireOff[u] + 8), m.sendStep + 1, m.sendAgent);
+    }
+    advanceSend(a, m);
+  }
+
+  if (hasRecv) finishRecv(a, m);
+  return true;
+}
+
+template <int PROTO, int DT, int OP>
+__global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
+  constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
+  constexpr u64 A = 16 / ESZ;   // 16-byte grain in elements
+  constexpr int PAYLOAD = PROTO == kSimple ? kSimpleSlotPayload
+                        : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
+  const int wave = threadIdx.x / kWave;
+  const int N = a.nranks;
+  const int lanesTotal = a.nChannels * a.lanes;
+
+  // Workgroup -> (lane id, group).  With several groups per lane, the groups
+  // of one lane get workgroup ids congruent mod 8, i.e. the same XCD under
+  // round-robin dispatch, so their cross-workgroup edges stay in one L2.
+  int L, g;
+  if (a.nGroups == 1) {
+    L = blockIdx.x;
+    g = 0;
+  } else {
+    const int x = blockIdx.x % 8;
+    g = (blockIdx.x / 8) % a.nGroups;
+    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
+  }
+  if (L >= lanesTotal) return;
+  const int r = g * a.groupSize + wave;
+  if (r >= N || r == a.deadRank) return;
+  const int ch = L / a.lanes;
+  const int k = L % a.lanes;
+  const int succ = r + 1 == N ? 0 : r + 1;
+  const int pred = r == 0 ? N - 1 : r - 1;
+
+  // channel share [pages: contiguous split per channel, 16-byte grain]
+  const u64 count = a.count;
+  const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
+  const u64 lo = umin((u64)ch * per, count);
+  const u64 hi = umin(lo + per, count);
+  const u64 len = hi - lo;
+  if (len == 0) return;
+
+  Member m;
+  m.lane = threadIdx.x % kWave;
+  const size_t wSelf = (size_t)L * N + r, wSucc = (size_t)L * N + succ;
+  m.rfifo = a.fifo + wSelf * a.fifoWorkerBytes;
+  m.sfifo = a.fifo + wSucc * a.fifoWorkerBytes;
+  m.self = a.conn + wSelf;
+  m.succ = a.conn + wSucc;
+  m.recvAgent = pred / a.groupSize != g;
+  m.sendAgent = succ / a.groupSize != g;
+  m.aligned = a.aligned16 != 0;
+  // counters carry over from earlier calls (tail == head at call boundaries)
+  m.recvStep = ldCounter(&m.self->head, true);
+  m.sendStep = ldCounter(&m.succ->tail, true);
+  m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
+  m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
+
+  const char* in = (const char*)a.send[r];
+  char* out = (char*)a.recv[r];
+  const u64 C = a.chunkElems;
+  const u64 loopSize = (u64)N * C;
+  const int lastSendStage = 2 * N - 3;
+
+  // Pipelining.  A member's share of a chunk is cut into slot-sized
+  // columns; a batch of at most nSlots/2 columns goes through all 2N-1 stages
+  // before the next batch starts (the pages size a chunk to half the FIFO for
+  // the same reason).  A member then never has more than nSlots/2 sends that
+  // its successor has not matched with receives, so no FIFO can fill up
+  // around the whole ring and the pipeline cannot deadlock, whatever the
+  // chunk size.  The order in which ranks are folded into an element is that
+  // of the stage schedule and does not depend on the batching.
+  const u64 batch = (u64)(a.nSlots / 2 > 0 ? a.nSlots / 2 : 1);
+  for (u64 off = 0; off < len; off += loopSize) {
+    const u64 rem = len - off;
+    // shrunk chunk on the last partial loop [pages: getNextSendAddr]
+    const u64 cur = rem < loopSize ? alignUp(divUp(rem, (u64)N), A) : C;
+    // no lane share of any chunk in this loop exceeds sub0 (chunk 0 is the
+    // longest chunk and a share is at most the per-lane split of its chunk)
+    const u64 sub0 = alignUp(divUp(umin(cur, rem), (u64)a.lanes), A);
+    const u64 nCols = divUp(sub0 * ESZ, (u64)PAYLOAD);
+    for (u64 jb = 0; jb < nCols; jb += batch) {
+      const u64 je = umin(jb + batch, nCols);
+      for (int s = 0; s <= 2 * N - 2; ++s) {
+        int kind;
+        if (s == 0) kind = kSend;
+        else if (s < N - 1) kind = kRecvReduceSend;
+        else if (s == N - 1) kind = kRecvReduceCopySend;
+        else if (s <= lastSendStage) kind = kRecvCopySend;
+        else kind = kRecv;
+        // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
+        const int c = s <= lastSendStage ? (r - 1 - s + 2 * N) % N : succ;
+        const u64 cb = (u64)c * cur;
+        const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
+        // lane k's share of the chunk (pipelining only: the order is per element)
+        const u64 sub = alignUp(divUp(clen, (u64)a.lanes), A);
+        const u64 sb = umin((u64)k * sub, clen);
+        const u64 se = umin(sb + sub, clen);
+        const u64 bytes = (se - sb) * ESZ;
+        const u64 first = lo + off + cb + sb;
+        const char* ip = in + first * ESZ;
+        char* op = out + first * ESZ;
+        for (u64 j = jb; j < je; ++j) {
+          const u64 b = j * (u64)PAYLOAD;
+          if (b >= bytes) break;
+          const long valid = (long)umin((u64)PAYLOAD, bytes - b);
+          if (!step<PROTO, DT, OP>(a, m, kind, ip + b, op + b, valid)) return;
+        }
+      }
+    }
+  }
+  // LL / LL128 never touch the tail counter per slot: publish it once so the
+  // next call starts both ends of this FIFO at the same step.
+  if (PROTO != kSimple && m.lane == 0) stRelaxed64(&m.succ->tail, m.sendStep, true);
+}
+
+// ------------------------------------------------------------- dispatch
+
+typedef void (*KernelFn)(const KernelArgs);
+
+template <int PROTO>
+KernelFn pick(int dtype, int op) {
+  switch (dtype) {
+    case arInt32:
+      if (op == arSum) return ringAllReduceKernel<PROTO, arInt32, arSum>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arInt32, arMax>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arInt32, arMin>;
+      break;
+    case arFloat32:
+      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat32, arSum>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat32, arMax>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat32, arMin>;
+      break;
+    case arFloat16:
+      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat16, arSum>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat16, arMax>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat16, arMin>;
+      break;
+    case arBfloat16:
+      if (op == arSum) return ringAllReduceKernel<PROTO, arBfloat16, arSum>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arBfloat16, arMax>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arBfloat16, arMin>;
+      break;
+    case arUint64:
+      if (op == arProbe) return ringAllReduceKernel<PROTO, arUint64, arProbe>;
+      break;
+  }
+  return nullptr;
+}
+
+KernelFn pickKernel(int proto, int dtype, int op) {
+  if (proto == kLL) return pick<kLL>(dtype, op);
+  if (proto == kLL128) return pick<kLL128>(dtype, op);
+  if (proto == kSimple) return pick<kSimple>(dtype, op);
+  return nullptr;
+}
+
+}  // namespace
+
+hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream) {
+  KernelFn fn = pickKernel(plan.proto, dtype, op);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  if (plan.cooperative) {
+    void* params[] = {(void*)&args};
+    return hipLaunchCooperativeKernel((const void*)fn, dim3(plan.grid), dim3(plan.block), params, 0, stream);
+  }
+  hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.block), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t ringKernelOccupancy(int proto, int dtype, int op, int block, int* blocksPerCU) {
+  KernelFn fn = pickKernel(proto, dtype, op);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocksPerCU, (const void*)fn, block, 0);
+}
+
+}  // namespace ar

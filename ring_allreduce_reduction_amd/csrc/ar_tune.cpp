@@ -1,0 +1,74 @@
+// ar_tune.cpp -- the ring cost model and protocol / channel selection.
+//
+// Model form ["NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程", ch.5 §三 ring.cc]:
+//   busBw = bw * nChannels; LL: min(llMaxBw, 0.5 * busBw) (half of every LL
+//   line is flag); LL128: min(0.92 * busBw, cap) (120 of 128 bytes payload);
+//   algBw = busBw * nRanks / nSteps with nSteps = 2(nRanks - 1) for AllReduce;
+//   lat = baseLat + nSteps * stepLat (one node: every step is intra).
+// Time ["NCCL 源码解析：从硬件拓扑到集合通信选型的完整链路", §五]:
+//   time = lat * latCount + nBytes / (1000 * bw)   (us, GB/s), latCount = 1.
+// Selection [same book, ch.5 §一]: one rank short-cuts to Simple with 0
+// channels; otherwise the strict-< argmin over the candidates, visited in the
+// order the reference's head-inserted list yields (Simple, LL128, LL), so ties
+// keep Simple; channel counts ascend, so ties keep fewer channels.  The pages
+// name no channel rule beyond "interpolate by size"; candidates here are the
+// powers of two up to the maximum whose share is at least the planner's 32 KiB
+// minimum traffic per channel [same book, ch.6 §五].
+#include <float.h>
+#include <stddef.h>
+
+#include "ar.h"
+
+namespace {
+
+constexpr size_t kMinBytesPerChannel = 32 * 1024;
+
+float candidateTime(const arTuneModel_t& m, int proto, int nranks, int nch, size_t nBytes) {
+  float busBw = m.bwPerChGBs * (float)nch;
+  if (proto == arProtoLL) busBw = busBw * 0.5f;
+  else if (proto == arProtoLL128) busBw = busBw * 0.92f;
+  if (busBw > m.maxBwGBs) busBw = m.maxBwGBs;
+  const int nSteps = 2 * (nranks - 1);
+  const float algBw = busBw * (float)nranks / (float)nSteps;
+  const float lat = m.baseLatUs + (float)nSteps * m.stepLatUs;
+  return lat * 1.0f + (float)nBytes / (1000.0f * algBw);
+}
+
+bool validModel(const arTuneModel_t& m) {
+  return m.bwPerChGBs > 0.0f && m.maxBwGBs > 0.0f && m.baseLatUs >= 0.0f && m.stepLatUs >= 0.0f;
+}
+
+}  // namespace
+
+extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
+                                 unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs) {
+  if (nranks < 1 || maxChannels < 1 || models == nullptr) return arInvalidArgument;
+  if ((protoMask & 7u) == 0) return arInvalidArgument;
+  if (nranks == 1) {
+    if (proto) *proto = arProtoSimple;
+    if (nChannels) *nChannels = 0;
+    if (predictedUs) *predictedUs = 0.0f;
+    return arSuccess;
+  }
+  static const int order[3] = {arProtoSimple, arProtoLL128, arProtoLL};
+  float best = FLT_MAX;
+  int bestProto = -1, bestCh = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int p = order[i];
+    if (!(protoMask & (1u << p)) || !validModel(models[p])) continue;
+    for (int nch = 1; nch <= maxChannels; nch *= 2) {
+      if (nch > 1 && nBytes / (size_t)nch < kMinBytesPerChannel) break;
+      const float t = candidateTime(models[p], p, nranks, nch, nBytes);
+      if (t < best) {
+        best = t;
+        bestProto = p;
+        bestCh = nch;
+      }
+    }
+  }
+  if (bestProto < 0) return arInvalidUsage;
+  if (proto) *proto = (arProto_t)bestProto;
+  if (nChannels) *nChannels = bestCh;
+  if (predictedUs) *predictedUs = best;
+  return arSuccess;
+}

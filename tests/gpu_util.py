@@ -1,0 +1,102 @@
+"""Helpers for the GPU parity tests: move seeded host inputs to the device,
+run the library through its C ABI, bring results back as raw bits, and
+compare them with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+from ring_allreduce_reduction_amd import binding as B
+from ring_allreduce_reduction_amd import inputs as gen
+
+TORCH_STORAGE = {"int32": torch.int32, "float32": torch.float32, "float16": torch.int16,
+                 "bfloat16": torch.int16, "uint64": torch.int64}
+TORCH_VIEW = {"float16": torch.float16, "bfloat16": torch.bfloat16}
+RAW = {"int32": np.uint32, "float32": np.uint32, "float16": np.uint16, "bfloat16": np.uint16,
+       "uint64": np.uint64}
+
+
+def note(msg):
+    """Name the case on the real stderr before a GPU step (bypasses capture)."""
+    sys.__stderr__.write("[gpu-case] %s\n" % msg)
+    sys.__stderr__.flush()
+
+
+def to_device(x, dtype, pad_elems=0, offset_elems=0):
+    """Device copy of host array x (raw storage); optional leading offset to
+    make the pointer unaligned."""
+    st = TORCH_STORAGE[dtype]
+    host = torch.from_numpy(x.view({np.int32: np.int32, np.float32: np.float32, np.uint16: np.int16,
+                                    np.uint64: np.int64}[x.dtype.type]))
+    buf = torch.empty(offset_elems + len(x) + pad_elems, dtype=st, device="cuda")
+    buf[offset_elems:offset_elems + len(x)].copy_(host)
+    t = buf[offset_elems:offset_elems + len(x)]
+    if dtype in TORCH_VIEW:
+        t = t.view(TORCH_VIEW[dtype])
+    return t
+
+
+def empty_like_sentinel(count, dtype, offset_elems=0):
+    st = TORCH_STORAGE[dtype]
+    buf = torch.empty(offset_elems + count, dtype=st, device="cuda")
+    buf.view(torch.uint8).fill_(0xFF)           # NaN / -1 everywhere: untouched outputs show
+    t = buf[offset_elems:]
+    if dtype in TORCH_VIEW:
+        t = t.view(TORCH_VIEW[dtype])
+    return t
+
+
+def to_host_raw(t, dtype):
+    st = TORCH_STORAGE[dtype]
+    a = t.view(st).cpu().numpy()
+    return a.view(RAW[dtype])
+
+
+def raw(x, dtype):
+    return np.ascontiguousarray(x).view(RAW[dtype])
+
+
+def assert_bits_equal(got, want, dtype, what=""):
+    g, w = raw(got, dtype), raw(want, dtype)
+    if not np.array_equal(g, w):
+        bad = np.nonzero(g != w)[0]
+        raise AssertionError("%s: %d of %d elements differ; first at %d: got %#x want %#x"
+                             % (what, len(bad), len(w), bad[0], int(g[bad[0]]), int(w[bad[0]])))
+
+
+def run_ring(comm, sends, recvs, dtype, op, stream=None):
+    B.arAllReduce(comm.handle, sends, recvs, count=sends[0].numel(), dtype=B.DTYPE_BY_NAME[dtype],
+                  op=B.OP_BY_NAME[op], stream=stream)
+    torch.cuda.synchronize()
+    err = B.arCommGetAsyncError(comm.handle)
+    assert err == B.arSuccess, B.arGetErrorString(err)
+
+
+def parity_case(n, count, dtype, op, proto, nch, seed=0, inplace=False, offset=0, comm=None, inputs=None):
+    """Run one AllReduce on the GPU and compare every rank's output bit for bit
+    with the oracle run on the same inputs, channels and chunk size."""
+    import oracle
+    note("parity n=%d count=%d dtype=%s op=%s proto=%s nch=%d seed=%d inplace=%s offset=%d"
+         % (n, count, dtype, op, proto, nch, seed, inplace, offset))
+    xs = inputs if inputs is not None else (
+        gen.probe_inputs(n, count) if op == "probe" else gen.make_inputs(n, count, dtype, seed=seed))
+    own = comm is None
+    if own:
+        comm = B.Comm(n, nch, proto)
+    else:
+        comm.set_config(proto, nch)
+    try:
+        plan = comm.plan(count, dtype, aligned128=(offset == 0))
+        sends = [to_device(x, dtype, offset_elems=offset) for x in xs]
+        recvs = sends if inplace else [empty_like_sentinel(count, dtype, offset_elems=offset) for _ in range(n)]
+        run_ring(comm, sends, recvs, dtype, op)
+        nch_used = max(1, plan["nChannels"])                      # one rank: no channels run
+        chunk = plan["chunkElems"] or 16 // gen.ELEM_SIZE[dtype]
+        want = oracle.allreduce(xs, dtype, op, nch_used, chunk)
+        for r in range(n):
+            assert_bits_equal(to_host_raw(recvs[r], dtype), want, dtype,
+                              "rank %d (%s, n=%d, count=%d, %s)" % (r, dtype, n, count, B.PROTO_NAMES[plan["proto"]]))
+        return plan, want, xs
+    finally:
+        if own:
+            comm.close()

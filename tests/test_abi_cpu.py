@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ar.h declares, rejects bad arguments before touching HIP, and the
+tuner's closed forms and tie-breaks hold."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from ring_allreduce_reduction_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from ring_allreduce_reduction_amd.build import build
+        build()
+    binding.lib()
+    return binding
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ar.h")).read()
+    return re.findall(r"^(?:arResult_t|const char\*)\s+(ar\w+)\s*\(", src, re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    for fn in ("arInit", "arAllReduce", "arTune", "arCommGetAsyncError", "arCommAbort", "arDestroy",
+               "arGetErrorString", "arTuneEval", "arGetPlan", "arSetConfig"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(B):
+    L = ctypes.CDLL(B.LIB_PATH)
+    for fn in _declared():
+        assert hasattr(L, fn), fn
+
+
+def test_error_strings(B):
+    for code in range(8):
+        s = B.arGetErrorString(code)
+        assert isinstance(s, str) and len(s) > 3
+    assert "unknown" in B.arGetErrorString(99)
+
+
+def test_init_rejects_bad_arguments_before_hip(B):
+    L = B.lib()
+    h = ctypes.c_void_p()
+    assert L.arInit(None, 4, 1, B.arProtoSimple, B.arAlgoRing) == B.arInvalidArgument
+    for n, ch, p, a in [(0, 1, 2, 0), (129, 1, 2, 0), (4, 0, 2, 0), (4, 65, 2, 0), (4, 1, 7, 0), (4, 1, -2, 0),
+                        (4, 1, 2, 1)]:
+        assert L.arInit(ctypes.byref(h), n, ch, p, a) == B.arInvalidArgument, (n, ch, p, a)
+        assert h.value is None
+
+
+def test_init_without_gpu_reports_hip_error(B):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = B.lib()
+    h = ctypes.c_void_p()
+    assert L.arInit(ctypes.byref(h), 4, 1, B.arProtoSimple, B.arAlgoRing) == B.arHipError
+    assert h.value is None
+
+
+def test_calls_on_a_null_comm(B):
+    L = B.lib()
+    ptrs = (ctypes.c_void_p * 1)(0)
+    assert L.arAllReduce(None, ptrs, ptrs, 4, B.arFloat32, B.arSum, None) == B.arInvalidArgument
+    assert L.arTune(None, 1024, None, None, None) == B.arInvalidArgument
+    assert L.arCommAbort(None) == B.arInvalidArgument
+    assert L.arSetConfig(None, 2, 1) == B.arInvalidArgument
+    assert L.arDestroy(None) == B.arSuccess
+    e = ctypes.c_int()
+    assert L.arCommGetAsyncError(None, ctypes.byref(e)) == B.arInvalidArgument
+    # a pointer that is not a comm (no magic) is refused, not dereferenced as one
+    junk = ctypes.create_string_buffer(4096)
+    assert L.arAllReduce(ctypes.cast(junk, ctypes.c_void_p), ptrs, ptrs, 4, 1, 0, None) == B.arInvalidArgument
+
+
+# ---------------------------------------------------------------- tuner
+
+def _t(model, proto, n, nch, nbytes):
+    """The pages' ring model written out: busBw = bw*nch, LL x0.5, LL128 x0.92,
+    capped; algBw = busBw*N/(2(N-1)); t = base + 2(N-1)*step + nBytes/(1000*algBw)."""
+    base, step, bw, cap = model
+    bus = bw * nch * {0: 0.5, 1: 0.92, 2: 1.0}[proto]
+    bus = min(bus, cap)
+    alg = bus * n / (2 * (n - 1))
+    return base + 2 * (n - 1) * step + nbytes / (1000.0 * alg)
+
+
+MODELS = [(5.0, 0.5, 10.0, 100.0), (6.0, 0.7, 10.0, 200.0), (9.0, 1.0, 10.0, 300.0)]
+
+
+def test_single_rank_short_cut(B):
+    assert B.arTuneEval(1, 16, 1 << 20, MODELS) == (B.arProtoSimple, 0, 0.0)
+
+
+@pytest.mark.parametrize("nbytes", [8, 4096, 1 << 16, 1 << 20, 1 << 24, 1 << 28])
+@pytest.mark.parametrize("n", [2, 8, 72])
+def test_argmin_matches_closed_form(B, n, nbytes):
+    p, ch, t = B.arTuneEval(n, 64, nbytes, MODELS)
+    best = None
+    for proto in (2, 1, 0):
+        c = 1
+        while c <= 64:
+            if c > 1 and nbytes // c < 32768:
+                break
+            tt = _t(MODELS[proto], proto, n, c, nbytes)
+            if best is None or tt < best[2] * (1 - 1e-6):
+                best = (proto, c, tt)
+            c *= 2
+    assert (p, ch) == best[:2]
+    assert t == pytest.approx(best[2], rel=1e-5)
+
+
+def test_small_messages_pick_ll_large_pick_simple(B):
+    assert B.arTuneEval(8, 64, 64, MODELS)[0] == B.arProtoLL
+    assert B.arTuneEval(8, 64, 1 << 28, MODELS)[0] == B.arProtoSimple
+
+
+def test_channels_keep_32k_per_channel(B):
+    for nbytes in (1 << 15, 1 << 16, 3 << 16, 1 << 22):
+        _, ch, _ = B.arTuneEval(8, 64, nbytes, MODELS)
+        assert ch == 1 or nbytes // ch >= 32768
+    assert B.arTuneEval(8, 64, 1 << 16, MODELS)[1] == 2   # more channels only help bandwidth
+
+
+def test_ties_prefer_simple_then_fewer_channels(B):
+    same = [(5.0, 0.5, 10.0, 10.0)] * 3    # capped: every channel count and protocol ties
+    same = [(5.0, 0.5, 1e9, 10.0)] * 3
+    p, ch, _ = B.arTuneEval(8, 64, 1 << 24, same)
+    assert p == B.arProtoSimple and ch == 1
+    p, ch, _ = B.arTuneEval(8, 64, 1 << 24, same, protoMask=0b011)
+    assert p == B.arProtoLL128
+
+
+def test_tuner_errors(B):
+    with pytest.raises(B.ArError) as e:
+        B.arTuneEval(8, 64, 1024, MODELS, protoMask=0)
+    assert e.value.code == B.arInvalidArgument
+    bad = [(1.0, 1.0, 0.0, 1.0)] * 3
+    with pytest.raises(B.ArError) as e:
+        B.arTuneEval(8, 64, 1024, bad)
+    assert e.value.code == B.arInvalidUsage
