@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="8B..256MiB sweep, every protocol + auto")
     ap.add_argument("--sweep-max-log2", type=int, default=28)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--lanes", type=int, default=0, help="force wavefronts per (rank, channel)")
+    ap.add_argument("--explore", default="", help="'nch1,nch2:lanes1,lanes2' grid of configurations")
+    ap.add_argument("--copy-probe-bytes", type=int, default=0,
+                    help="time a plain elementwise copy (torch.neg) of this many bytes instead")
     return ap.parse_args()
 
 
@@ -71,6 +75,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
 
+    if args.copy_probe_bytes:
+        return copy_probe(args, torch)
     if args.sweep:
         return sweep(args, B, gen, torch, np)
 
@@ -92,6 +98,10 @@ def main():
     torch.cuda.synchronize()
 
     comm = B.Comm(N, args.nchannels, args.proto)
+    if args.lanes:
+        B.arSetDebug(comm.handle, B.arDebugLanes, args.lanes)
+    if args.explore:
+        return explore(args, B, torch, comm, sends, recvs, count, dtype, N, S)
     plan = comm.plan(count, dtype)
     log("plan: %s" % json.dumps(plan))
     stream = torch.cuda.Stream()
@@ -196,6 +206,67 @@ def cpu_baseline(xs, dtype, plan, N, S):
     return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "the full %d x %d MiB %s workload, %d run(s) of the single-threaded C oracle, "
                       "%.2f s each" % (N, S >> 20, dtype, reps, t)}
+
+
+def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=dt_code)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=dt_code)
+        b.record(stream)
+        torch.cuda.synchronize()
+    err = comm.async_error()
+    if err != B.arSuccess:
+        raise SystemExit("run failed: " + B.arGetErrorString(err))
+    return a.elapsed_time(b) / steps
+
+
+def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
+    """Time a grid of configurations in one process:
+    --explore 'channels:lanes[:slotKiB[:direct]]', each a comma list."""
+    parts = args.explore.split(":") + ["4", "1"]
+    chs, lanes, slots, directs = [[int(x) for x in p.split(",")] for p in parts[:4]]
+    for nch in chs:
+        for ln in lanes:
+            for sk in slots:
+                for d in directs:
+                    comm.set_config("simple" if args.proto == "auto" else args.proto, nch)
+                    B.arSetDebug(comm.handle, B.arDebugLanes, ln)
+                    B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
+                    B.arSetDebug(comm.handle, B.arDebugDirect, d)
+                    plan = comm.plan(count, dtype)
+                    ms = time_calls(B, torch, comm, sends, recvs, count, B.DTYPE_BY_NAME[dtype], 2, args.steps)
+                    frac = 5.0 * (N - 1) * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
+                    print(json.dumps({"nch": nch, "lanes": plan["lanesPerChannel"], "slotKiB": sk, "direct": d,
+                                      "grid": plan["workgroups"], "block": plan["threadsPerGroup"],
+                                      "ms": round(ms, 4),
+                                      "busbw": round(S / (ms / 1e3) / 1e9 * 2 * (N - 1) / N, 2),
+                                      "frac": round(frac, 4)}), flush=True)
+    comm.close()
+
+
+def copy_probe(args, torch):
+    """A plain elementwise kernel that reads and writes a known number of bytes
+    (the yardstick for the FETCH_SIZE / WRITE_SIZE counters)."""
+    n = args.copy_probe_bytes // 4
+    src = torch.rand(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        torch.neg(src, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"copy_probe_bytes": n * 4, "ms": round(ms, 4),
+                      "read_plus_write_GBs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
 def sweep(args, B, gen, torch, np):

@@ -89,8 +89,8 @@ typedef enum {
  * Allocates the FIFOs, counters and flags of every protocol on the device
  * (owned by the comm, freed by arDestroy).  Environment overrides, read once
  * per process: AR_PROTO (LL|LL128|SIMPLE), AR_NCHANNELS, AR_SLICE_BYTES
- * (Simple slice, default 512 KiB; chunk = 2 slices), AR_STEPS (FIFO depth,
- * default 8), AR_TIMEOUT_MS.
+ * (Simple slice, default 512 KiB; chunk = 2 slices), AR_STEPS (FIFO depth
+ * in slots, 2..8; default 2 for Simple, 8 for LL and LL128), AR_TIMEOUT_MS.
  * Errors: arInvalidArgument (bad counts or enums), arHipError (no device or a
  * HIP failure), arSystemError (host allocation).
  */
@@ -212,6 +212,11 @@ arResult_t arDestroy(arComm_t comm);
 typedef enum {
   arDebugTimeoutUs = 0,  /* a wait longer than this gives up (default 5e6) */
   arDebugDeadRank = 1,   /* rank whose ring members return at once (-1: none) */
+  arDebugLanes = 2,      /* wavefronts per (rank, channel); 0 = automatic */
+  arDebugSimpleSlotKiB = 3,  /* Simple FIFO slot per wavefront: 1, 2, 4 or 8 KiB */
+  arDebugDirect = 4,     /* 1: Simple all-gather writes the successor's output
+                            directly (default); 0: through the FIFO */
+  arDebugSlots = 5,      /* FIFO depth in slots for every protocol, 2..8 */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 

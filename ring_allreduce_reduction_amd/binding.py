@@ -20,7 +20,7 @@ arProtoAuto, arProtoLL, arProtoLL128, arProtoSimple = -1, 0, 1, 2
 arAlgoRing = 0
 arInt32, arFloat32, arFloat16, arBfloat16, arUint64 = 0, 1, 2, 3, 4
 arSum, arMax, arMin, arProbe = 0, 1, 2, 3
-arDebugTimeoutUs, arDebugDeadRank = 0, 1
+arDebugTimeoutUs, arDebugDeadRank, arDebugLanes, arDebugSimpleSlotKiB, arDebugDirect, arDebugSlots = 0, 1, 2, 3, 4, 5
 AR_MAX_RANKS, AR_MAX_CHANNELS = 128, 64
 
 PROTO_NAMES = {arProtoLL: "LL", arProtoLL128: "LL128", arProtoSimple: "Simple", arProtoAuto: "auto"}

@@ -31,7 +31,7 @@ struct Env {
   int forcedProto = -2;   // -2: none
   int nChannels = 0;      // 0: not set
   size_t sliceBytes = kDefaultSliceBytes;
-  int nSteps = kDefaultSteps;
+  int nSteps = 0;         // 0: per-protocol defaults
   int64_t timeoutUs = 5000000;
   int debug = 0;          // 0 warn, 1 info, 2 trace
 };
@@ -77,7 +77,8 @@ const Env& env() {
     }
     if (const char* p = getenv("AR_STEPS")) {
       int v = atoi(p);
-      if (v >= 2 && v <= 64) e.nSteps = v;
+      if (v >= 2 && v <= kMaxSlots) e.nSteps = v;
+      else fprintf(stderr, "[ar] WARN ignoring AR_STEPS=%s (2..%d)\n", p, kMaxSlots);
     }
     if (const char* p = getenv("AR_TIMEOUT_MS")) {
       long long v = atoll(p);
@@ -110,7 +111,7 @@ struct arComm {
   int device;
   int numCUs;
   int wallClockKHz;
-  int nSlots;
+  int nSlots[3];        // FIFO depth per protocol
   size_t sliceBytes;
   int lanesMax;         // lanes (channel x lane) per rank provisioned
   char* fifo[3];
@@ -121,6 +122,9 @@ struct arComm {
   arTuneModel_t models[3];
   int64_t timeoutUs;
   int deadRank;
+  int forcedLanes;      // 0: automatic
+  int simpleUnroll;     // Simple slot size in KiB (1, 2, 4)
+  bool direct;          // Simple all-gather writes outputs directly
   hipStream_t lastStream;
   bool launched;
   bool aborted;
@@ -134,11 +138,13 @@ bool commOk(const arComm* c) {
   return c != nullptr && c->startMagic == kCommMagic && c->endMagic == kCommMagic;
 }
 
-int slotBytesOf(int proto) {
-  return proto == kSimple ? kSimpleSlotBytes : proto == kLL ? kLLSlotBytes : kLL128SlotBytes;
+// Slot geometry: Simple slots are `unroll` KiB; the FIFO is provisioned for
+// the largest Simple slot.
+int slotBytesOf(int proto, int unroll) {
+  return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotBytes : kLL128SlotBytes;
 }
-int slotPayloadOf(int proto) {
-  return proto == kSimple ? kSimpleSlotPayload : proto == kLL ? kLLSlotPayload : kLL128SlotPayload;
+int slotPayloadOf(int proto, int unroll) {
+  return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotPayload : kLL128SlotPayload;
 }
 
 size_t chunkBytesOf(const arComm* c, int proto) {
@@ -187,40 +193,74 @@ arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned12
   plan->proto = proto;
   plan->nChannels = nch;
   plan->chunkElems = chunkBytesOf(c, proto) / (uint64_t)esz;
-  plan->slotBytes = slotBytesOf(proto);
-  plan->slotPayload = slotPayloadOf(proto);
-  plan->nSlots = c->nSlots;
+  plan->unroll = proto == kSimple ? c->simpleUnroll : proto == kLL ? kLLUnroll : kLL128Unroll;
+  plan->direct = proto == kSimple && c->direct;
+  plan->slotBytes = slotBytesOf(proto, plan->unroll);
+  plan->slotPayload = slotPayloadOf(proto, plan->unroll);
+  plan->nSlots = c->nSlots[proto];
   plan->predictedUs = predicted;
 
-  // Members per workgroup: the whole ring when it fits (N <= 16), else
-  // balanced groups joined by agent-scope edges.
-  int nGroups = (N + kMaxMembersPerGroup - 1) / kMaxMembersPerGroup;
-  int groupSize = (N + nGroups - 1) / nGroups;
+  // Members per workgroup: the whole ring when it fits (N <= 16).  Longer
+  // rings are cut into balanced groups joined by agent-scope edges; the
+  // launch is then cooperative, so the largest group size whose grid (one
+  // lane per channel at least) is co-resident is taken.
+  auto layout = [&](int gs, int* nGroupsOut, int* gsOut) {
+    int ng = (N + gs - 1) / gs;
+    *nGroupsOut = ng;
+    *gsOut = (N + ng - 1) / ng;
+  };
+  // A Simple slot smaller than the default keeps more wavefronts resident
+  // (fewer registers) when the whole grid must be co-resident.
+  int nGroups = 1, groupSize = N;
+  if (N > kMaxMembersPerGroup) {
+    bool found = false;
+    for (int u = plan->unroll; u >= 1 && !found; u /= 2) {
+      if (proto == kSimple) {
+        plan->unroll = u;
+        plan->slotBytes = slotBytesOf(proto, u);
+        plan->slotPayload = slotPayloadOf(proto, u);
+      }
+      for (int gs = kMaxMembersPerGroup; gs >= 1 && !found; --gs) {
+        layout(gs, &nGroups, &groupSize);
+        plan->block = groupSize * kWave;
+        int perCU = 0;
+        if (ringKernelOccupancy(*plan, dtype, op, &perCU) != hipSuccess) return arHipError;
+        const int grid1 = ((nch + 7) / 8) * 8 * nGroups;
+        found = perCU * c->numCUs >= grid1;
+      }
+      if (proto != kSimple) break;
+    }
+    if (!found) return arInvalidUsage;
+  }
   plan->groupSize = groupSize;
   plan->nGroups = nGroups;
   plan->block = groupSize * kWave;
   plan->cooperative = nGroups > 1;
 
-  // Lanes per (rank, channel): enough wavefronts to fill the chip (about 32
-  // per CU), but never a lane share below two FIFO slots of the largest chunk.
+  // Lanes per (rank, channel): one resident round of workgroups (the grid is
+  // sized to what the chip holds at once, so no tail round), but never a
+  // lane share below two FIFO slots of the largest chunk.
   const uint64_t per = alignUpU(divUpU(count, (uint64_t)nch), A);
   const uint64_t loop = (uint64_t)N * plan->chunkElems;
   const uint64_t cur = per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
   const uint64_t chunkBytes = cur * (uint64_t)esz;
-  int lanes = (int)((uint64_t)c->numCUs * 32 / ((uint64_t)N * (uint64_t)nch));
-  const int byChunk = (int)(chunkBytes / (2 * (uint64_t)plan->slotPayload));
-  if (lanes > byChunk) lanes = byChunk;
-  if (lanes > c->lanesMax / nch) lanes = c->lanesMax / nch;
-  if (lanes < 1) lanes = 1;
-
+  int perCU = 0;
+  if (ringKernelOccupancy(*plan, dtype, op, &perCU) != hipSuccess) return arHipError;
+  if (perCU < 1) perCU = 1;
+  const int capacity = perCU * c->numCUs;   // resident workgroups
   auto gridFor = [&](int ln) {
     const int lt = nch * ln;
     return nGroups == 1 ? lt : ((lt + 7) / 8) * 8 * nGroups;
   };
+  // About 64 wavefronts per CU: measured best on MI355X (workgroups finish
+  // unevenly, so a grid of a few resident rounds balances better than one).
+  int lanes = (int)((uint64_t)c->numCUs * 64 / ((uint64_t)N * (uint64_t)nch));
+  const int byChunk = (int)(chunkBytes / (2 * (uint64_t)plan->slotPayload));
+  if (lanes > byChunk) lanes = byChunk;
+  if (lanes > c->lanesMax / nch) lanes = c->lanesMax / nch;
+  if (lanes < 1) lanes = 1;
+  if (c->forcedLanes > 0) lanes = c->forcedLanes <= c->lanesMax / nch ? c->forcedLanes : c->lanesMax / nch;
   if (plan->cooperative) {
-    int perCU = 0;
-    if (ringKernelOccupancy(proto, dtype, op, plan->block, &perCU) != hipSuccess) return arHipError;
-    const int capacity = perCU * c->numCUs;
     while (lanes > 1 && gridFor(lanes) > capacity) --lanes;
     if (gridFor(lanes) > capacity) return arInvalidUsage;
   }
@@ -276,10 +316,12 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->device = dev;
   c->numCUs = cus;
   c->wallClockKHz = clk;
-  c->nSlots = e.nSteps;
+  for (int p = 0; p < 3; ++p) c->nSlots[p] = e.nSteps > 0 ? e.nSteps : kDefaultSlots[p];
   c->sliceBytes = e.sliceBytes;
   c->timeoutUs = e.timeoutUs;
   c->deadRank = -1;
+  c->simpleUnroll = kSimpleUnrollDefault;
+  c->direct = true;
   for (int p = 0; p < 3; ++p) c->models[p] = kDefaultModels[p];
 
   // FIFOs and counters, one set per protocol (a line of one protocol must
@@ -289,7 +331,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   const size_t workers = (size_t)nranks * (size_t)lanesMax;
   if (nranks > 1) {
     for (int p = 0; p < 3; ++p) {
-      c->fifoWorkerBytes[p] = (size_t)c->nSlots * (size_t)slotBytesOf(p);
+      c->fifoWorkerBytes[p] = (size_t)kMaxSlots * (size_t)slotBytesOf(p, kSimpleUnrollMax);
       const size_t fb = workers * c->fifoWorkerBytes[p];
       const size_t cb = workers * sizeof(Conn);
       if (hipMalloc((void**)&c->fifo[p], fb) != hipSuccess || hipMalloc((void**)&c->conn[p], cb) != hipSuccess ||
@@ -315,7 +357,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   }
   if (e.debug >= 1)
     fprintf(stderr, "[ar] INFO init nranks=%d maxChannels=%d proto=%d CUs=%d slots=%d slice=%zu\n", nranks,
-            nChannels, (int)proto, cus, c->nSlots, c->sliceBytes);
+            nChannels, (int)proto, cus, c->nSlots[kSimple], c->sliceBytes);
   *out = c;
   return arSuccess;
 }
@@ -340,6 +382,26 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   if (knob == arDebugDeadRank) {
     if (value < -1 || value >= c->nranks) return arInvalidArgument;
     c->deadRank = (int)value;
+    return arSuccess;
+  }
+  if (knob == arDebugLanes) {
+    if (value < 0 || value > c->lanesMax) return arInvalidArgument;
+    c->forcedLanes = (int)value;
+    return arSuccess;
+  }
+  if (knob == arDebugSimpleSlotKiB) {
+    if (value != 1 && value != 2 && value != 4 && value != 8) return arInvalidArgument;
+    c->simpleUnroll = (int)value;
+    return arSuccess;
+  }
+  if (knob == arDebugSlots) {
+    if (value < 2 || value > kMaxSlots) return arInvalidArgument;
+    for (int p = 0; p < 3; ++p) c->nSlots[p] = (int)value;
+    return arSuccess;
+  }
+  if (knob == arDebugDirect) {
+    if (value != 0 && value != 1) return arInvalidArgument;
+    c->direct = value != 0;
     return arSuccess;
   }
   return arInvalidArgument;
@@ -461,15 +523,16 @@ arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* rec
   a.nGroups = plan.nGroups;
   a.nSlots = plan.nSlots;
   a.aligned16 = aligned16 ? 1 : 0;
+  a.direct = plan.direct ? 1 : 0;
   a.deadRank = c->deadRank;
 
   if (env().debug >= 1)
     fprintf(stderr,
             "[ar] INFO op %llu count=%zu dtype=%d op=%d proto=%d nch=%d chunk=%llu lanes=%d groups=%dx%d grid=%d "
-            "block=%d coop=%d pred=%.1fus\n",
+            "block=%d coop=%d unroll=%d direct=%d pred=%.1fus\n",
             (unsigned long long)c->opCount, count, (int)dtype, (int)op, plan.proto, plan.nChannels,
             (unsigned long long)plan.chunkElems, plan.lanes, plan.nGroups, plan.groupSize, plan.grid, plan.block,
-            (int)plan.cooperative, plan.predictedUs);
+            (int)plan.cooperative, plan.unroll, (int)plan.direct, plan.predictedUs);
   hipError_t he = launchRing(plan, dtype, op, a, st);
   if (he != hipSuccess) {
     fprintf(stderr, "[ar] WARN kernel launch failed: %s\n", hipGetErrorString(he));

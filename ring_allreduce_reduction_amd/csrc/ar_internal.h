@@ -12,21 +12,25 @@ namespace ar {
 
 constexpr int kWave = 64;                 // CDNA wavefront width
 constexpr int kMaxMembersPerGroup = 16;   // ring members (one wavefront each) per workgroup
-constexpr int kMaxWorkers = 16384;        // (rank, lane) wavefronts a comm provisions FIFOs for
-constexpr int kDefaultSteps = 8;          // FIFO depth in slots, the pages' step count
+constexpr int kMaxWorkers = 32768;        // (rank, lane) wavefronts a comm provisions FIFOs for
+// FIFO depth in slots per protocol (LL, LL128, Simple).  The pages' ring
+// FIFO has 8 steps; on MI355X a 2-slot Simple FIFO of 8 KiB slots measured
+// fastest (the smaller live footprint outweighs the lost slack).
+constexpr int kDefaultSlots[3] = {8, 8, 2};
+constexpr int kMaxSlots = 8;              // FIFO depth provisioned per worker
 
 // One ring member is one wavefront.  Per FIFO slot ("step") a wavefront moves
-// kUnroll pieces per lane:
-//   Simple: 16-byte pieces, slot = kUnroll KiB, all payload.
+// `unroll` pieces per lane:
+//   Simple: 16-byte pieces, slot = unroll KiB, all payload.
 //   LL:     16-byte lines {data0, flag, data1, flag}: 8 payload bytes per lane.
 //   LL128:  each wavefront instruction fills 8 lines of 128 bytes; a line is
 //           seven 16-byte payload pieces, 8 payload bytes and an 8-byte flag.
-constexpr int kSimpleUnroll = 4;
+constexpr int kSimpleUnrollMax = 8;       // Simple slot = unroll KiB (1, 2, 4 or 8)
+constexpr int kSimpleUnrollDefault = 8;
 constexpr int kLLUnroll = 2;
 constexpr int kLL128Unroll = 2;
 
-constexpr int kSimpleSlotBytes = kSimpleUnroll * kWave * 16;   // 4096
-constexpr int kSimpleSlotPayload = kSimpleSlotBytes;
+constexpr int kSimpleSlotBytesMax = kSimpleUnrollMax * kWave * 16;   // 8192
 constexpr int kLLSlotBytes = kLLUnroll * kWave * 16;           // 2048 wire
 constexpr int kLLSlotPayload = kLLUnroll * kWave * 8;          // 1024 payload
 constexpr int kLL128LinePayload = 120;
@@ -83,6 +87,7 @@ struct KernelArgs {
   int nGroups;                // workgroups per (channel, lane)
   int nSlots;
   int aligned16;              // every send/recv base is 16-byte aligned
+  int direct;                 // Simple: all-gather writes the successor's output directly
   int deadRank;               // debug: this rank's members return at once
 };
 
@@ -99,13 +104,15 @@ struct Plan {
   int slotBytes;
   int slotPayload;
   int nSlots;
+  int unroll;                 // pieces per lane per slot
+  bool direct;
   bool cooperative;
   float predictedUs;
 };
 
 // Provided by ar_kernels.hip.
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream);
-hipError_t ringKernelOccupancy(int proto, int dtype, int op, int block, int* blocksPerCU);
+hipError_t ringKernelOccupancy(const Plan& plan, int dtype, int op, int* blocksPerCU);
 
 inline int elemSize(int dtype) {
   switch (dtype) {

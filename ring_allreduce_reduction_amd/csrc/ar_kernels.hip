@@ -117,14 +117,14 @@ __device__ __forceinline__ void stNt8(char* p, v2u v) { __builtin_nontemporal_st
 
 // Load `pieceBytes` (16 or 8) user bytes at p of which `valid` are in range;
 // bytes past the range read as zero.  Element-wise when short or unaligned.
-template <int ESZ>
+template <int ESZ, bool NT>
 __device__ __forceinline__ v4u loadUser(const char* p, long valid, int pieceBytes, bool aligned) {
   v4u v = {0u, 0u, 0u, 0u};
   if (valid >= pieceBytes && aligned) {
     if (pieceBytes == 16) {
-      v = ldNt16(p);
+      v = NT ? ldNt16(p) : *(const v4u*)p;
     } else {
-      v2u t = ldNt8(p);
+      v2u t = NT ? ldNt8(p) : *(const v2u*)p;
       v.x = t.x; v.y = t.y;
     }
   } else if (valid > 0) {
@@ -147,14 +147,16 @@ __device__ __forceinline__ v4u loadUser(const char* p, long valid, int pieceByte
   return v;
 }
 
-template <int ESZ>
+template <int ESZ, bool NT>
 __device__ __forceinline__ void storeUser(char* p, v4u v, long valid, int pieceBytes, bool aligned) {
   if (valid >= pieceBytes && aligned) {
     if (pieceBytes == 16) {
-      stNt16(p, v);
+      if (NT) stNt16(p, v);
+      else *(v4u*)p = v;
     } else {
       v2u t; t.x = v.x; t.y = v.y;
-      stNt8(p, t);
+      if (NT) stNt8(p, t);
+      else *(v2u*)p = t;
     }
   } else if (valid > 0) {
     u32 w[4] = {v.x, v.y, v.z, v.w};
@@ -255,6 +257,7 @@ struct Member {
   bool recvAgent;
   bool sendAgent;
   bool aligned;
+  bool direct;
 };
 
 __device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
@@ -275,17 +278,24 @@ __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
   if (++m.recvSlot == (u32)a.nSlots) m.recvSlot = 0;
 }
 
-// One FIFO step of `kind`; `valid` payload bytes start at inp / outp.
-template <int PROTO, int DT, int OP>
+// One FIFO step of `kind`; `valid` payload bytes start at inp / outp (and at
+// succOutp in the successor's output, for a direct all-gather step).
+template <int PROTO, int DT, int OP, int U>
 __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, const char* inp, char* outp,
-                                     long valid) {
+                                     char* succOutp, long valid) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
-  constexpr int U = PROTO == kSimple ? kSimpleUnroll : PROTO == kLL ? kLLUnroll : kLL128Unroll;
-  constexpr int SLOT = PROTO == kSimple ? kSimpleSlotBytes : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
   const bool hasLocal = kind <= kRecvReduceCopySend;
   const bool hasRecv = kind >= kRecvReduceSend;
   const bool hasSend = kind <= kRecvCopySend;
   const bool hasOut = kind >= kRecvReduceCopySend;
+  // Direct all-gather (Simple): the member that finishes a chunk and every
+  // member forwarding it write the successor's output buffer instead of its
+  // FIFO, so the all-gather half moves no FIFO bytes; the receiver then
+  // reads the finished chunk from its own output.  [The pages' FIFO slot
+  // descriptor can carry a pointer, and a work item can be flagged direct.]
+  const bool directSend = PROTO == kSimple && m.direct && (kind == kRecvReduceCopySend || kind == kRecvCopySend);
+  const bool directRecv = PROTO == kSimple && m.direct && kind >= kRecvCopySend;
   const int lane = m.lane;
 
   // piece geometry of this lane: payload offset, payload bytes, wire offset
@@ -304,12 +314,12 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
     }
   }
 
-  if (hasSend && !waitCredit(a, m)) return false;
+  if (hasSend && !directSend && !waitCredit(a, m)) return false;
 
   v4u v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    v[u] = hasLocal ? loadUser<ESZ>(inp + payOff[u], valid - payOff[u], payBytes[u], m.aligned)
+    v[u] = hasLocal ? loadUser<ESZ, true>(inp + payOff[u], valid - payOff[u], payBytes[u], m.aligned)
                     : v4u{0u, 0u, 0u, 0u};
   }
 
@@ -320,8 +330,14 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
       if (!waitGeq(a, &m.self->tail, m.recvStep + 1, m.recvAgent)) return false;
       fenceAcquire(m.recvAgent);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        in[u] = payOff[u] < valid ? *(const v4u*)(slot + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+      for (int u = 0; u < U; ++u) {
+        if (directRecv)   // the predecessor wrote it into my output
+          in[u] = kind == kRecvCopySend
+                      ? loadUser<ESZ, false>(outp + payOff[u], valid - payOff[u], 16, m.aligned)
+                      : v4u{0u, 0u, 0u, 0u};
+        else
+          in[u] = payOff[u] < valid ? *(const v4u*)(slot + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+      }
     } else if (PROTO == kLL) {
       const u32 flag = (u32)(m.recvStep + 1);
       bool done[U];
@@ -383,17 +399,25 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
     for (int u = 0; u < U; ++u) v[u] = hasLocal ? combine<DT, OP>(in[u], v[u]) : in[u];
   }
 
-  if (hasOut) {
+  if (hasOut && !directRecv) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) storeUser<ESZ>(outp + payOff[u], v[u], valid - payOff[u], payBytes[u], m.aligned);
+    for (int u = 0; u < U; ++u)
+      storeUser<ESZ, true>(outp + payOff[u], v[u], valid - payOff[u], payBytes[u], m.aligned);
   }
 
   if (hasSend) {
     char* slot = m.sfifo + (size_t)m.sendSlot * SLOT;
     if (PROTO == kSimple) {
+      if (directSend) {
+        // the successor reads this back at its next stage: keep it cacheable
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
+        for (int u = 0; u < U; ++u)
+          storeUser<ESZ, false>(succOutp + payOff[u], v[u], valid - payOff[u], 16, m.aligned);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
+      }
       fenceRelease(m.sendAgent);
       if (lane == 0) stRelaxed64(&m.succ->tail, m.sendStep + 1, m.sendAgent);
     } else if (PROTO == kLL) {
@@ -432,11 +456,11 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
   return true;
 }
 
-template <int PROTO, int DT, int OP>
+template <int PROTO, int DT, int OP, int U>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr u64 A = 16 / ESZ;   // 16-byte grain in elements
-  constexpr int PAYLOAD = PROTO == kSimple ? kSimpleSlotPayload
+  constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
                         : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
   const int wave = threadIdx.x / kWave;
   const int N = a.nranks;
@@ -480,6 +504,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   m.recvAgent = pred / a.groupSize != g;
   m.sendAgent = succ / a.groupSize != g;
   m.aligned = a.aligned16 != 0;
+  m.direct = a.direct != 0;
   // counters carry over from earlier calls (tail == head at call boundaries)
   m.recvStep = ldCounter(&m.self->head, true);
   m.sendStep = ldCounter(&m.succ->tail, true);
@@ -488,6 +513,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
 
   const char* in = (const char*)a.send[r];
   char* out = (char*)a.recv[r];
+  char* succOut = (char*)a.recv[succ];
   const u64 C = a.chunkElems;
   const u64 loopSize = (u64)N * C;
   const int lastSendStage = 2 * N - 3;
@@ -527,14 +553,13 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
         const u64 sb = umin((u64)k * sub, clen);
         const u64 se = umin(sb + sub, clen);
         const u64 bytes = (se - sb) * ESZ;
-        const u64 first = lo + off + cb + sb;
-        const char* ip = in + first * ESZ;
-        char* op = out + first * ESZ;
+        const u64 first = (lo + off + cb + sb) * ESZ;
         for (u64 j = jb; j < je; ++j) {
           const u64 b = j * (u64)PAYLOAD;
           if (b >= bytes) break;
           const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-          if (!step<PROTO, DT, OP>(a, m, kind, ip + b, op + b, valid)) return;
+          if (!step<PROTO, DT, OP, U>(a, m, kind, in + first + b, out + first + b, succOut + first + b, valid))
+            return;
         }
       }
     }
@@ -548,47 +573,52 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
 
 typedef void (*KernelFn)(const KernelArgs);
 
-template <int PROTO>
+template <int PROTO, int U>
 KernelFn pick(int dtype, int op) {
   switch (dtype) {
     case arInt32:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arInt32, arSum>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arInt32, arMax>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arInt32, arMin>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arInt32, arSum, U>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arInt32, arMax, U>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arInt32, arMin, U>;
       break;
     case arFloat32:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat32, arSum>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat32, arMax>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat32, arMin>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat32, arSum, U>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat32, arMax, U>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat32, arMin, U>;
       break;
     case arFloat16:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat16, arSum>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat16, arMax>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat16, arMin>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat16, arSum, U>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat16, arMax, U>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat16, arMin, U>;
       break;
     case arBfloat16:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arBfloat16, arSum>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arBfloat16, arMax>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arBfloat16, arMin>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arBfloat16, arSum, U>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arBfloat16, arMax, U>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arBfloat16, arMin, U>;
       break;
     case arUint64:
-      if (op == arProbe) return ringAllReduceKernel<PROTO, arUint64, arProbe>;
+      if (op == arProbe) return ringAllReduceKernel<PROTO, arUint64, arProbe, U>;
       break;
   }
   return nullptr;
 }
 
-KernelFn pickKernel(int proto, int dtype, int op) {
-  if (proto == kLL) return pick<kLL>(dtype, op);
-  if (proto == kLL128) return pick<kLL128>(dtype, op);
-  if (proto == kSimple) return pick<kSimple>(dtype, op);
+KernelFn pickKernel(const Plan& plan, int dtype, int op) {
+  if (plan.proto == kLL) return pick<kLL, kLLUnroll>(dtype, op);
+  if (plan.proto == kLL128) return pick<kLL128, kLL128Unroll>(dtype, op);
+  if (plan.proto == kSimple) {
+    if (plan.unroll == 1) return pick<kSimple, 1>(dtype, op);
+    if (plan.unroll == 2) return pick<kSimple, 2>(dtype, op);
+    if (plan.unroll == 4) return pick<kSimple, 4>(dtype, op);
+    if (plan.unroll == 8) return pick<kSimple, 8>(dtype, op);
+  }
   return nullptr;
 }
 
 }  // namespace
 
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream) {
-  KernelFn fn = pickKernel(plan.proto, dtype, op);
+  KernelFn fn = pickKernel(plan, dtype, op);
   if (fn == nullptr) return hipErrorInvalidValue;
   if (plan.cooperative) {
     void* params[] = {(void*)&args};
@@ -598,10 +628,10 @@ hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& arg
   return hipGetLastError();
 }
 
-hipError_t ringKernelOccupancy(int proto, int dtype, int op, int block, int* blocksPerCU) {
-  KernelFn fn = pickKernel(proto, dtype, op);
+hipError_t ringKernelOccupancy(const Plan& plan, int dtype, int op, int* blocksPerCU) {
+  KernelFn fn = pickKernel(plan, dtype, op);
   if (fn == nullptr) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocksPerCU, (const void*)fn, block, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocksPerCU, (const void*)fn, plan.block, 0);
 }
 
 }  // namespace ar

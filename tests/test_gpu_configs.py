@@ -1,0 +1,189 @@
+"""GPU parity at the workload configurations' real sizes.
+
+Small and medium cases compare every element of every rank with the oracle.
+At the largest sizes the comparison is on sampled elements the oracle folds
+one by one (random indices plus the first and last element of every chunk),
+together with properties that hold at any size: every rank's output is
+bit-identical, and the float bounds against a float64 direct sum."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ring_allreduce_reduction_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+def chunk_edges(orc, n, count, dtype, nch, chunk):
+    """First and last element of every (channel, loop, chunk), walked with the
+    oracle's locate()."""
+    edges, e = [], 0
+    while e < count:
+        _, _, _, first, ln = orc.locate(n, count, dtype, nch, chunk, e)
+        edges += [first, first + ln - 1]
+        e = first + ln
+    return np.array(edges, dtype=np.int64)
+
+
+def sampled_check(B, gu, orc, xs, sends, recvs, dtype, op, plan, nsample=200000, seed=0):
+    n, count = len(xs), len(xs[0])
+    raw_t = gu.TORCH_STORAGE[dtype]
+    r0 = recvs[0].view(raw_t)
+    for r in range(1, n):
+        assert torch.equal(r0, recvs[r].view(raw_t)), "rank %d differs from rank 0" % r
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([rng.integers(0, count, nsample),
+                                    chunk_edges(orc, n, count, dtype, plan["nChannels"], plan["chunkElems"])]))
+    got = r0[torch.from_numpy(idx).cuda()].cpu().numpy().view(gu.RAW[dtype])
+    want = orc.elements(xs, dtype, op, plan["nChannels"], plan["chunkElems"], idx)
+    gu.assert_bits_equal(got, want, dtype, "sampled %s %s n=%d count=%d" % (dtype, op, n, count))
+    if op == "sum" and dtype != "int32":
+        ok, info = orc.within_tolerance(want, [x[idx] for x in xs], dtype)
+        assert ok, info
+    return idx
+
+
+def upload(gu, xs, dtype):
+    return [gu.to_device(x, dtype) for x in xs]
+
+
+# ------------------------------------------------ 8 ranks x 64 MiB fp32, Simple, 16 ch
+
+def test_cfg_8x64MiB_fp32_simple_16ch_full(B, gu, orc):
+    from ring_allreduce_reduction_amd import inputs as gen
+    n, count = 8, 16 * MiB
+    gu.note("8 x 64 MiB fp32 Simple 16 ch (full compare)")
+    xs = gen.make_inputs(n, count, "float32", seed=0)
+    with B.Comm(n, 16, "simple") as comm:
+        plan = comm.plan(count, "float32")
+        assert plan["nChannels"] == 16 and plan["chunkElems"] == 2 * 512 * 1024 // 4
+        sends = upload(gu, xs, "float32")
+        recvs = [gu.empty_like_sentinel(count, "float32") for _ in range(n)]
+        gu.run_ring(comm, sends, recvs, "float32", "sum")
+        want = orc.allreduce(xs, "float32", "sum", 16, plan["chunkElems"])
+        for r in range(n):
+            gu.assert_bits_equal(gu.to_host_raw(recvs[r], "float32"), want, "float32", "rank %d" % r)
+        ok, info = orc.within_tolerance(want, xs, "float32")
+        assert ok, info
+
+
+# ------------------------------------------------ 8 ranks fp32 sweep 8 B .. 256 MiB
+
+@pytest.fixture(scope="module")
+def sweep_data(B, gu):
+    from ring_allreduce_reduction_amd import inputs as gen
+    n, maxc = 8, 64 * MiB
+    xs = gen.make_inputs(n, maxc, "float32", seed=0)   # prefixes are the smaller sizes' inputs
+    sends = upload(gu, xs, "float32")
+    recvs = [torch.empty_like(s) for s in sends]
+    yield xs, sends, recvs
+    del sends, recvs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("log2_bytes", list(range(3, 29)))
+def test_cfg_fp32_sweep_every_protocol(B, gu, orc, sweep_data, log2_bytes):
+    xs_full, sends_full, recvs_full = sweep_data
+    n, count = 8, (1 << log2_bytes) // 4
+    xs = [x[:count] for x in xs_full]
+    sends = [s[:count] for s in sends_full]
+    recvs = [r[:count] for r in recvs_full]
+    with B.Comm(n, 64, "auto") as comm:
+        for proto in ("ll", "ll128", "simple", "auto"):
+            comm.set_config(proto, 64)
+            plan = comm.plan(count, "float32")
+            gu.note("sweep %d B proto=%s -> %s nch=%d" % (count * 4, proto, B.PROTO_NAMES[plan["proto"]],
+                                                           plan["nChannels"]))
+            for r in recvs:
+                r.view(torch.int32).fill_(-1)
+            gu.run_ring(comm, sends, recvs, "float32", "sum")
+            if count <= 4 * MiB:
+                want = orc.allreduce(xs, "float32", "sum", plan["nChannels"], plan["chunkElems"])
+                for r in range(n):
+                    gu.assert_bits_equal(gu.to_host_raw(recvs[r], "float32"), want, "float32",
+                                         "rank %d %s" % (r, proto))
+            else:
+                sampled_check(B, gu, orc, xs, sends, recvs, "float32", "sum", plan, nsample=50000)
+
+
+# ------------------------------------------------ 8 ranks x 128 MiB int32 / bf16 / fp16, Sum/Max/Min, 32 ch
+
+@pytest.mark.parametrize("dtype", ["int32", "bfloat16", "float16"])
+def test_cfg_8x128MiB_dtypes_ops_32ch(B, gu, orc, dtype):
+    from ring_allreduce_reduction_amd import inputs as gen
+    n = 8
+    count = 128 * MiB // gen.ELEM_SIZE[dtype]
+    xs = gen.make_inputs(n, count, dtype, seed=0)
+    sends = upload(gu, xs, dtype)
+    recvs = [gu.empty_like_sentinel(count, dtype) for _ in range(n)]
+    with B.Comm(n, 32, "simple") as comm:
+        plan = comm.plan(count, dtype)
+        assert plan["nChannels"] == 32
+        for op in ("sum", "max", "min"):
+            gu.note("8 x 128 MiB %s %s Simple 32 ch" % (dtype, op))
+            gu.run_ring(comm, sends, recvs, dtype, op)
+            idx = sampled_check(B, gu, orc, xs, sends, recvs, dtype, op, plan, seed={"sum": 1, "max": 2, "min": 3}[op])
+            if op != "sum" or dtype == "int32":   # order-free results: also exact against numpy
+                vals = np.stack([orc.to_float64(x[idx], dtype) for x in xs])
+                ref = vals.sum(0) if op == "sum" else vals.max(0) if op == "max" else vals.min(0)
+                got = orc.to_float64(recvs[3].view(gu.TORCH_STORAGE[dtype])[torch.from_numpy(idx).cuda()]
+                                     .cpu().numpy().view(gu.RAW[dtype]).view(orc.NP_STORAGE[dtype]), dtype)
+                assert np.array_equal(got, ref)
+    del sends, recvs
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------ 72 ranks x 4 MiB fp32, LL128 and Simple, 64 ch
+
+@pytest.mark.parametrize("proto", ["ll128", "simple"])
+def test_cfg_72x4MiB_fp32_64ch_full(B, gu, orc, proto):
+    from ring_allreduce_reduction_amd import inputs as gen
+    n, count = 72, MiB
+    gu.note("72 x 4 MiB fp32 %s 64 ch (full compare)" % proto)
+    xs = gen.make_inputs(n, count, "float32", seed=0)
+    with B.Comm(n, 64, proto) as comm:
+        plan = comm.plan(count, "float32")
+        assert plan["nChannels"] == 64 and plan["ranksPerGroup"] <= 16
+        sends = upload(gu, xs, "float32")
+        recvs = [gu.empty_like_sentinel(count, "float32") for _ in range(n)]
+        gu.run_ring(comm, sends, recvs, "float32", "sum")
+        want = orc.allreduce(xs, "float32", "sum", 64, plan["chunkElems"])
+        for r in range(n):
+            gu.assert_bits_equal(gu.to_host_raw(recvs[r], "float32"), want, "float32", "rank %d" % r)
+        ok, info = orc.within_tolerance(want, xs, "float32")
+        assert ok, info
+
+
+# ------------------------------------------------ 16 ranks x 512 MiB bf16, LL128 and Simple, 64 ch
+
+def test_cfg_16x512MiB_bf16_64ch(B, gu, orc):
+    from ring_allreduce_reduction_amd import inputs as gen
+    n, count = 16, 256 * MiB
+    gu.note("16 x 512 MiB bf16: generating inputs")
+    xs = gen.make_inputs(n, count, "bfloat16", seed=0)
+    sends = upload(gu, xs, "bfloat16")
+    recvs = [gu.empty_like_sentinel(count, "bfloat16") for _ in range(n)]
+    with B.Comm(n, 64, "simple") as comm:
+        for proto in ("ll128", "simple"):
+            comm.set_config(proto, 64)
+            plan = comm.plan(count, "bfloat16")
+            gu.note("16 x 512 MiB bf16 %s 64 ch" % proto)
+            gu.run_ring(comm, sends, recvs, "bfloat16", "sum")
+            sampled_check(B, gu, orc, xs, sends, recvs, "bfloat16", "sum", plan, nsample=100000)
+    del sends, recvs
+    torch.cuda.empty_cache()

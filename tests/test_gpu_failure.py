@@ -1,0 +1,77 @@
+"""Failure handling on the GPU, with the failing condition forced from the
+host so every kernel still exits normally: a rank whose ring members return
+at once (so its neighbours' bounded waits give up after a short timeout),
+and an abort raised while members are waiting."""
+import time
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ring_allreduce_reduction_amd import binding
+    binding.lib()
+    return binding
+
+
+def _bufs(n, count):
+    s = [torch.randn(count, device="cuda") for _ in range(n)]
+    return s, [torch.empty_like(x) for x in s]
+
+
+@pytest.mark.parametrize("proto", ["simple", "ll", "ll128"])
+def test_dead_rank_times_out_and_poisons_the_comm(B, proto):
+    import gpu_util
+    gpu_util.note("dead rank 3, timeout 2 ms, proto=%s" % proto)
+    sends, recvs = _bufs(8, 100000)
+    with B.Comm(8, 4, proto) as comm:
+        B.arSetDebug(comm.handle, B.arDebugTimeoutUs, 2000)
+        B.arSetDebug(comm.handle, B.arDebugDeadRank, 3)
+        t0 = time.perf_counter()
+        comm.allreduce(sends, recvs, "sum")
+        torch.cuda.synchronize()
+        assert time.perf_counter() - t0 < 10.0
+        assert comm.async_error() == B.arRemoteError
+        with pytest.raises(B.ArError) as e:       # only destroy is accepted now
+            comm.allreduce(sends, recvs, "sum")
+        assert e.value.code == B.arInvalidUsage
+    # a fresh comm works again
+    with B.Comm(8, 4, proto) as comm:
+        comm.allreduce(sends, recvs, "sum")
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arSuccess
+        ref = sum(s.double() for s in sends)
+        assert torch.allclose(recvs[5].double(), ref, atol=1e-5)
+
+
+def test_abort_releases_waiting_members(B):
+    import gpu_util
+    gpu_util.note("abort while rank 0 is dead, timeout 4 s")
+    sends, recvs = _bufs(4, 1 << 16)
+    with B.Comm(4, 2, "simple") as comm:
+        B.arSetDebug(comm.handle, B.arDebugTimeoutUs, 4000000)
+        B.arSetDebug(comm.handle, B.arDebugDeadRank, 0)
+        t0 = time.perf_counter()
+        comm.allreduce(sends, recvs, "sum")
+        time.sleep(0.05)
+        B.arCommAbort(comm.handle)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert comm.async_error() == B.arRemoteError
+        assert elapsed < 3.0, elapsed   # well before the 4 s timeout
+
+
+def test_debug_knob_validation(B):
+    with B.Comm(4, 2, "simple") as comm:
+        for knob, bad in [(B.arDebugTimeoutUs, 0), (B.arDebugDeadRank, 4), (B.arDebugDeadRank, -2),
+                          (B.arDebugSimpleSlotKiB, 3), (B.arDebugDirect, 2), (B.arDebugSlots, 1),
+                          (B.arDebugSlots, 9), (99, 1)]:
+            with pytest.raises(B.ArError):
+                B.arSetDebug(comm.handle, knob, bad)
+        with pytest.raises(B.ArError):
+            comm.set_config("simple", 3)    # more channels than provisioned at init

@@ -97,6 +97,20 @@ def test_unaligned_buffers(B, gu, proto, dtype):
     gu.parity_case(4, 30011, dtype, "sum", proto, 3, seed=5, offset=1)
 
 
+@pytest.mark.parametrize("slot_kib", [1, 2, 4])
+@pytest.mark.parametrize("direct", [0, 1])
+def test_simple_slot_and_direct_variants(B, gu, slot_kib, direct):
+    with B.Comm(8, 16, "simple") as comm:
+        B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, slot_kib)
+        B.arSetDebug(comm.handle, B.arDebugDirect, direct)
+        for count, nch, lanes in [(300007, 5, 0), (1 << 20, 16, 3), (4099, 2, 0)]:
+            B.arSetDebug(comm.handle, B.arDebugLanes, lanes)
+            gu.parity_case(8, count, "float32", "sum", "simple", nch, seed=count, comm=comm)
+        B.arSetDebug(comm.handle, B.arDebugLanes, 0)
+        gu.parity_case(8, 100003, "bfloat16", "sum", "simple", 4, seed=1, comm=comm, inplace=True)
+        gu.parity_case(5, 77777, "int32", "max", "simple", 3, seed=2, comm=None)
+
+
 def test_ll128_needs_128_byte_alignment(B, gu):
     from ring_allreduce_reduction_amd import inputs as gen
     xs = gen.make_inputs(4, 1000, "float32")
