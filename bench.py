@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--lanes", type=int, default=0, help="force wavefronts per (rank, channel)")
     ap.add_argument("--explore", default="", help="'nch1,nch2:lanes1,lanes2' grid of configurations")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure latency vs ranks and bandwidth vs channels per protocol and fit arTune's model")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="time a plain elementwise copy (torch.neg) of this many bytes instead")
     return ap.parse_args()
@@ -79,6 +81,8 @@ def main():
         return copy_probe(args, torch)
     if args.sweep:
         return sweep(args, B, gen, torch, np)
+    if args.calibrate:
+        return calibrate(args, B, torch, np)
 
     N, count, dtype = args.nranks, args.count, args.dtype
     esz = gen.ELEM_SIZE[dtype]
@@ -227,25 +231,26 @@ def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):
 
 def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
     """Time a grid of configurations in one process:
-    --explore 'channels:lanes[:slotKiB[:direct]]', each a comma list."""
-    parts = args.explore.split(":") + ["4", "1"]
-    chs, lanes, slots, directs = [[int(x) for x in p.split(",")] for p in parts[:4]]
-    for nch in chs:
-        for ln in lanes:
-            for sk in slots:
-                for d in directs:
-                    comm.set_config("simple" if args.proto == "auto" else args.proto, nch)
-                    B.arSetDebug(comm.handle, B.arDebugLanes, ln)
-                    B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
-                    B.arSetDebug(comm.handle, B.arDebugDirect, d)
-                    plan = comm.plan(count, dtype)
-                    ms = time_calls(B, torch, comm, sends, recvs, count, B.DTYPE_BY_NAME[dtype], 2, args.steps)
-                    frac = 5.0 * (N - 1) * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
-                    print(json.dumps({"nch": nch, "lanes": plan["lanesPerChannel"], "slotKiB": sk, "direct": d,
-                                      "grid": plan["workgroups"], "block": plan["threadsPerGroup"],
-                                      "ms": round(ms, 4),
-                                      "busbw": round(S / (ms / 1e3) / 1e9 * 2 * (N - 1) / N, 2),
-                                      "frac": round(frac, 4)}), flush=True)
+    --explore 'channels:lanes[:slotKiB[:direct[:depth]]]', each a comma list
+    (lanes 0 = automatic, depth 0 = the protocol's default)."""
+    parts = args.explore.split(":")
+    parts += ["8", "1", "0"][len(parts) - 2:]
+    chs, lanes, slots, directs, depths = [[int(x) for x in p.split(",")] for p in parts[:5]]
+    grid = [(a, b, c, e, f) for a in chs for b in lanes for c in slots for e in directs for f in depths]
+    for nch, ln, sk, d, dp in grid:
+        if dp:
+            B.arSetDebug(comm.handle, B.arDebugSlots, dp)
+        comm.set_config("simple" if args.proto == "auto" else args.proto, nch)
+        B.arSetDebug(comm.handle, B.arDebugLanes, ln)
+        B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
+        B.arSetDebug(comm.handle, B.arDebugDirect, d)
+        plan = comm.plan(count, dtype)
+        ms = time_calls(B, torch, comm, sends, recvs, count, B.DTYPE_BY_NAME[dtype], 2, args.steps)
+        frac = 5.0 * (N - 1) * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
+        print(json.dumps({"nch": nch, "lanes": plan["lanesPerChannel"], "slotKiB": sk, "direct": d,
+                          "depth": plan["nSlots"], "grid": plan["workgroups"], "block": plan["threadsPerGroup"],
+                          "ms": round(ms, 4), "busbw": round(S / (ms / 1e3) / 1e9 * 2 * (N - 1) / N, 2),
+                          "frac": round(frac, 4)}), flush=True)
     comm.close()
 
 
@@ -269,42 +274,84 @@ def copy_probe(args, torch):
                       "read_plus_write_GBs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
+def calibrate(args, B, torch, np):
+    """Fit the ring cost model's constants per protocol on this GPU.
+
+    latency:   t at a 4 KiB message (every chunk non-empty), 1 channel,
+               N = 2, 4, 8, 16 ranks;
+               least squares t = base + 2(N-1) * step
+    bandwidth: t at 128 MiB per rank, N = 8, 1..64 channels;
+               busBw = S/(t - lat) * 2(N-1)/N, then bwPerCh from the smallest
+               channel count (divided by the protocol's payload factor) and
+               the cap from the largest measured busBw.
+    Prints one JSON line per measurement and one with the fitted models."""
+    factor = {B.arProtoLL: 0.5, B.arProtoLL128: 0.92, B.arProtoSimple: 1.0}
+    fits = {}
+    big = 32 << 20
+    base = [torch.rand(big, device="cuda") for _ in range(16)]
+    outs = [torch.empty_like(x) for x in base]
+    for proto in (B.arProtoLL, B.arProtoLL128, B.arProtoSimple):
+        name = B.PROTO_NAMES[proto]
+        xs, ys = [], []
+        for n in (2, 4, 8, 16):
+            comm = B.Comm(n, 1, proto)
+            ms = time_calls(B, torch, comm, base[:n], outs[:n], 1024, B.arFloat32, 20, 200)
+            comm.close()
+            xs.append(2 * (n - 1))
+            ys.append(ms * 1e3)
+            print(json.dumps({"calib": "latency", "proto": name, "nranks": n, "us": round(ms * 1e3, 3)}), flush=True)
+        step, b0 = np.polyfit(np.array(xs, float), np.array(ys, float), 1)
+        b0, step = max(float(b0), 0.0), max(float(step), 0.0)
+        lat8 = b0 + 14 * step
+        comm = B.Comm(8, 64, proto)
+        bus = {}
+        for nch in (1, 2, 4, 8, 16, 32, 64):
+            comm.set_config(proto, nch)
+            ms = time_calls(B, torch, comm, base[:8], outs[:8], big, B.arFloat32, 3, 10)
+            S = big * 4
+            bus[nch] = S / max(ms * 1e3 - lat8, 1e-3) / 1e3 * 2 * 7 / 8
+            print(json.dumps({"calib": "bandwidth", "proto": name, "nch": nch, "us": round(ms * 1e3, 2),
+                              "busbw_GBs": round(bus[nch], 2)}), flush=True)
+        comm.close()
+        fits[name] = {"baseLatUs": round(b0, 3), "stepLatUs": round(step, 4),
+                      "bwPerChGBs": round(bus[1] / factor[proto], 2), "maxBwGBs": round(max(bus.values()), 2)}
+    print(json.dumps({"calib": "fit", "models": fits}), flush=True)
+
+
 def sweep(args, B, gen, torch, np):
-    """8 ranks fp32 Sum, per-rank sizes 8 B .. 2^max bytes: every protocol and
-    the arTune choice; one JSON line per (size, protocol)."""
+    """8 ranks fp32 Sum, per-rank sizes 8 B .. 2^max bytes.  Each protocol runs
+    at the channel count arTune's model gives that protocol for the size (the
+    pages fix channels by size: at least 32 KiB per channel), then arTune's own
+    choice; one JSON line per size with the regret t(chosen)/min_p t(p) - 1."""
     N = args.nranks
     maxc = (1 << args.sweep_max_log2) // 4
     xs = gen.make_inputs(N, maxc, "float32", seed=args.seed)
     sends = [torch.from_numpy(x).cuda() for x in xs]
     recvs = [torch.empty_like(s) for s in sends]
     comm = B.Comm(N, args.nchannels, "auto")
-    stream = torch.cuda.Stream()
+    models = [B.arTuneGetModel(comm.handle, p) for p in (0, 1, 2)]
     for lg in range(3, args.sweep_max_log2 + 1):
         count = (1 << lg) // 4
+        S = count * 4
+        iters = 200 if S < (64 << 20) else 20
+        res = {}
         for proto in ("ll", "ll128", "simple", "auto"):
-            comm.set_config(proto, args.nchannels)
+            pcode = B.PROTO_BY_NAME[proto]
+            if proto == "auto":
+                comm.set_config("auto", args.nchannels)
+            else:
+                _, nch, _ = B.arTuneEval(N, args.nchannels, S, models, protoMask=1 << pcode)
+                comm.set_config(proto, max(1, nch))
             plan = comm.plan(count, "float32")
-            iters = 200 if count * 4 < (64 << 20) else 20
-            with torch.cuda.stream(stream):
-                for _ in range(5):
-                    comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=B.arFloat32)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(iters):
-                    comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=B.arFloat32)
-                b.record(stream)
-                torch.cuda.synchronize()
-            err = comm.async_error()
-            if err != B.arSuccess:
-                raise SystemExit("sweep failed at %d B %s: %s" % (count * 4, proto, B.arGetErrorString(err)))
-            us = a.elapsed_time(b) / iters * 1e3
-            S = count * 4
-            print(json.dumps({"bytes": S, "proto": proto, "chosen": B.PROTO_NAMES[plan["proto"]],
-                              "nChannels": plan["nChannels"], "lanes": plan["lanesPerChannel"],
-                              "us": round(us, 3), "predicted_us": round(plan["predictedUs"], 3),
-                              "busbw_GBs": round(S / (us / 1e6) / 1e9 * 2 * (N - 1) / N, 3)}), flush=True)
+            ms = time_calls(B, torch, comm, sends, recvs, count, B.arFloat32, 5, iters)
+            res[proto] = {"us": round(ms * 1e3, 3), "proto": B.PROTO_NAMES[plan["proto"]],
+                          "nch": plan["nChannels"], "pred_us": round(plan["predictedUs"], 2)}
+        best = min(res[p]["us"] for p in ("ll", "ll128", "simple"))
+        out = {"bytes": S, "regret": round(res["auto"]["us"] / best - 1, 4),
+               "busbw_auto_GBs": round(S / (res["auto"]["us"] / 1e6) / 1e9 * 2 * (N - 1) / N, 3)}
+        out.update(res)
+        print(json.dumps(out), flush=True)
     comm.close()
-
 
 if __name__ == "__main__":
     main()

@@ -130,8 +130,8 @@ arResult_t arAllReduce(arComm_t comm, const void* const* sendbufs, void* const* 
  * Candidates: protocols not disabled (AR_PROTO, LL128 alignment is the
  * caller's concern: arAllReduce re-tunes without LL128 when buffers are not
  * 128-byte aligned) times power-of-two channel counts up to the comm's
- * maximum with at least 32 KiB per channel.  Ties keep the earlier candidate:
- * Simple before LL128 before LL, fewer channels first.
+ * maximum with at least 32 KiB per channel.  Protocol ties keep Simple before
+ * LL128 before LL; channel-count ties keep the larger count.
  */
 arResult_t arTune(arComm_t comm, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs);
 

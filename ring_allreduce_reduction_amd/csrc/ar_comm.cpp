@@ -92,12 +92,14 @@ const Env& env() {
   return e;
 }
 
-// Tuner constants for MI355X, fitted to a protocol x size x channel sweep of
-// this library on one MI355X (see the benchmark's calibration mode).
+// Tuner constants for MI355X (us, us, GB/s, GB/s), fitted by the benchmark's
+// calibration mode on one MI355X: latency from 4 KiB messages at 2, 4, 8
+// and 16 ranks (least squares on 2(N-1) steps), per-channel bandwidth from
+// one channel at 128 MiB per rank, cap from the best of 1..64 channels.
 const arTuneModel_t kDefaultModels[3] = {
-    /* LL     */ {6.0f, 0.9f, 6.0f, 120.0f},
-    /* LL128  */ {7.0f, 1.1f, 6.0f, 220.0f},
-    /* Simple */ {9.0f, 1.5f, 6.0f, 330.0f},
+    /* LL     */ {0.57f, 2.31f, 48.4f, 107.5f},
+    /* LL128  */ {0.28f, 2.46f, 75.8f, 175.1f},
+    /* Simple */ {0.00f, 3.71f, 193.8f, 326.7f},
 };
 
 }  // namespace
@@ -254,11 +256,31 @@ arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned12
   };
   // About 64 wavefronts per CU: measured best on MI355X (workgroups finish
   // unevenly, so a grid of a few resident rounds balances better than one).
-  int lanes = (int)((uint64_t)c->numCUs * 64 / ((uint64_t)N * (uint64_t)nch));
-  const int byChunk = (int)(chunkBytes / (2 * (uint64_t)plan->slotPayload));
-  if (lanes > byChunk) lanes = byChunk;
-  if (lanes > c->lanesMax / nch) lanes = c->lanesMax / nch;
-  if (lanes < 1) lanes = 1;
+  // A lane's share of a chunk is at least one slot.  When the chunk is too
+  // small to give every lane a full Simple slot, smaller slots are used so
+  // that more lanes share the work: the time of a short message is the number
+  // of sequential steps per lane, not bandwidth.
+  const int target = (int)((uint64_t)c->numCUs * 64 / ((uint64_t)N * (uint64_t)nch));
+  auto lanesFor = [&](int slotPayload) {
+    int ln = target;
+    // round up: a 120-byte-line LL128 slot never divides a power-of-two chunk
+    const int byChunk = (int)((chunkBytes + (uint64_t)slotPayload - 1) / (uint64_t)slotPayload);
+    if (ln > byChunk) ln = byChunk;
+    if (ln > c->lanesMax / nch) ln = c->lanesMax / nch;
+    return ln < 1 ? 1 : ln;
+  };
+  int lanes = lanesFor(plan->slotPayload);
+  if (proto == kSimple && !plan->cooperative && c->forcedLanes == 0) {
+    while (lanes < target && plan->unroll > 1 && (uint64_t)lanes * plan->slotPayload >= chunkBytes / 2) {
+      const int u = plan->unroll / 2;
+      const int ln = lanesFor(slotPayloadOf(proto, u));
+      if (ln <= lanes) break;
+      plan->unroll = u;
+      plan->slotBytes = slotBytesOf(proto, u);
+      plan->slotPayload = slotPayloadOf(proto, u);
+      lanes = ln;
+    }
+  }
   if (c->forcedLanes > 0) lanes = c->forcedLanes <= c->lanesMax / nch ? c->forcedLanes : c->lanesMax / nch;
   if (plan->cooperative) {
     while (lanes > 1 && gridFor(lanes) > capacity) --lanes;

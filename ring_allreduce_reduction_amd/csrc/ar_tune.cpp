@@ -8,12 +8,14 @@
 // Time ["NCCL 源码解析：从硬件拓扑到集合通信选型的完整链路", §五]:
 //   time = lat * latCount + nBytes / (1000 * bw)   (us, GB/s), latCount = 1.
 // Selection [same book, ch.5 §一]: one rank short-cuts to Simple with 0
-// channels; otherwise the strict-< argmin over the candidates, visited in the
-// order the reference's head-inserted list yields (Simple, LL128, LL), so ties
-// keep Simple; channel counts ascend, so ties keep fewer channels.  The pages
-// name no channel rule beyond "interpolate by size"; candidates here are the
-// powers of two up to the maximum whose share is at least the planner's 32 KiB
-// minimum traffic per channel [same book, ch.6 §五].
+// channels; otherwise the argmin over the candidates, protocols visited in the
+// order the reference's head-inserted list yields (Simple, LL128, LL) with a
+// strict <, so protocol ties keep Simple.  The pages name no channel rule
+// beyond "interpolate by size"; candidates here are the powers of two up to
+// the maximum whose share is at least the planner's 32 KiB minimum traffic per
+// channel [same book, ch.6 §五].  Within a protocol a channel-count tie keeps
+// the larger count: every channel runs in the same single launch here, and on
+// MI355X extra channels past the bandwidth cap still spread the work better.
 #include <float.h>
 #include <stddef.h>
 
@@ -56,14 +58,20 @@ extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, con
   for (int i = 0; i < 3; ++i) {
     const int p = order[i];
     if (!(protoMask & (1u << p)) || !validModel(models[p])) continue;
+    float bestP = FLT_MAX;
+    int bestChP = 0;
     for (int nch = 1; nch <= maxChannels; nch *= 2) {
       if (nch > 1 && nBytes / (size_t)nch < kMinBytesPerChannel) break;
       const float t = candidateTime(models[p], p, nranks, nch, nBytes);
-      if (t < best) {
-        best = t;
-        bestProto = p;
-        bestCh = nch;
+      if (t <= bestP) {
+        bestP = t;
+        bestChP = nch;
       }
+    }
+    if (bestP < best) {
+      best = bestP;
+      bestProto = p;
+      bestCh = bestChP;
     }
   }
   if (bestProto < 0) return arInvalidUsage;
