@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--explore", default="", help="'nch1,nch2:lanes1,lanes2' grid of configurations")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure latency vs ranks and bandwidth vs channels per protocol and fit arTune's model")
+    ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="summarize rocprofv3 CSV output directories into markdown + profiles/traffic.json")
+    ap.add_argument("--profile-label", default="", help="workload key for --summarize-profiles")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="time a plain elementwise copy (torch.neg) of this many bytes instead")
     return ap.parse_args()
@@ -59,6 +62,8 @@ def parse():
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        return summarize_profiles(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build emulates all ranks on one GPU; --gpus %d (WORLD_SIZE %d) is not "
@@ -153,9 +158,11 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            key = "%s_n%d_count%d_%s" % (B.PROTO_NAMES[plan["proto"]], N, count, dtype)
-            if key in tj:
+            key = workload_key(B.PROTO_NAMES[plan["proto"]], N, count, dtype)
+            if key in tj and tj[key]["kernel_src_sha256"] == kernel_src_sha():
                 traffic = tj[key]["bytes_per_launch"]
+            elif key in tj:
+                log("traffic counters predate the current kernel source: reporting null")
         except Exception as e:  # a stale or partial file must not break the bench
             log("traffic file unreadable: %s" % e)
 
@@ -192,6 +199,72 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def workload_key(proto, N, count, dtype):
+    return "%s_n%d_count%d_%s" % (proto, N, count, dtype)
+
+
+def kernel_src_sha():
+    import hashlib
+    src = os.path.join(ROOT, "ring_allreduce_reduction_amd", "csrc", "ar_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def summarize_profiles(args):
+    """Read rocprofv3 CSV directories (kernel trace with --stats; FETCH_SIZE and
+    WRITE_SIZE passes of the ring kernel and of the copy probe) and print a
+    markdown summary; store the per-launch HBM traffic in profiles/traffic.json."""
+    import csv
+    import glob
+
+    def rows(d, suffix):
+        fs = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+        if not fs:
+            raise SystemExit("no *%s under %s" % (suffix, d))
+        return list(csv.DictReader(open(fs[0])))
+
+    def counter(d, name, match):
+        vals = [float(r["Counter_Value"]) for r in rows(d, "counter_collection.csv")
+                if match in r["Kernel_Name"] and r["Counter_Name"] == name]
+        return sum(vals) / len(vals), len(vals)
+
+    trace_dir, fetch_dir, write_dir, cf_dir, cw_dir = args.summarize_profiles
+    stats = rows(trace_dir, "kernel_stats.csv")
+    ring = [r for r in stats if "ringAllReduceKernel" in r["Name"]]
+    fetch_kib, nf = counter(fetch_dir, "FETCH_SIZE", "ringAllReduceKernel")
+    write_kib, nw = counter(write_dir, "WRITE_SIZE", "ringAllReduceKernel")
+    cf_kib, _ = counter(cf_dir, "FETCH_SIZE", "vectorized_elementwise_kernel")
+    cw_kib, _ = counter(cw_dir, "WRITE_SIZE", "vectorized_elementwise_kernel")
+    copy_bytes = 1 << 30
+    fscale = copy_bytes / (cf_kib * 1024.0)
+    wscale = copy_bytes / (cw_kib * 1024.0)
+    read_b = fetch_kib * 1024.0 * fscale
+    write_b = write_kib * 1024.0 * wscale
+    print("| kernel | calls | avg duration (us) | min | max |")
+    print("|---|---|---|---|---|")
+    for r in stats[:6]:
+        print("| `%s` | %s | %.1f | %.1f | %.1f |" % (r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                   float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    print()
+    print("Copy-probe calibration (torch.neg over 1 GiB: reads 1 GiB, writes 1 GiB):")
+    print("FETCH_SIZE reads %.0f KiB per dispatch (scale x%.3f), WRITE_SIZE %.0f KiB (scale x%.3f).\n"
+          % (cf_kib, fscale, cw_kib, wscale))
+    print("Ring kernel, per launch (mean of %d / %d dispatches): FETCH_SIZE %.0f KiB -> %.3f GiB read; "
+          "WRITE_SIZE %.0f KiB -> %.3f GiB written; total %.3f GiB (%.0f bytes)."
+          % (nf, nw, fetch_kib, read_b / 2 ** 30, write_kib, write_b / 2 ** 30, (read_b + write_b) / 2 ** 30,
+             read_b + write_b))
+    if args.profile_label and ring:
+        path = args.traffic_json
+        tj = json.load(open(path)) if os.path.exists(path) else {}
+        tj[args.profile_label] = {"bytes_per_launch": round(read_b + write_b), "read_bytes": round(read_b),
+                                  "write_bytes": round(write_b), "fetch_scale": round(fscale, 4),
+                                  "write_scale": round(wscale, 4),
+                                  "kernel_avg_ns": float(ring[0]["AverageNs"]),
+                                  "kernel_src_sha256": kernel_src_sha()}
+        with open(path, "w") as f:
+            json.dump(tj, f, indent=1, sort_keys=True)
+        print("\nwrote %s[%s]" % (path, args.profile_label))
 
 
 def cpu_baseline(xs, dtype, plan, N, S):
