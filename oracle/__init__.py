@@ -6,6 +6,7 @@ ring_oracle.c (plain single-threaded C); this file only marshals numpy arrays.
 
 Functions mirror what the pages define (see ring_oracle.c for citations):
   allreduce()  -- the order-matched ring fold over every element
+  reduce_scatter(), all_gather() -- the two halves of the ring on their own
   elements()   -- the same fold for a list of single elements
   locate()     -- channel / loop / chunk of one element
   direct_sum_f64(), within_tolerance() -- the float64 direct sum and the
@@ -42,6 +43,8 @@ def lib():
         L.ar_oracle_locate.argtypes = [i, sz, i, i, sz, sz, ctypes.POINTER(i),
                                        ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(i),
                                        ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.ar_oracle_reduce_scatter.argtypes = [i, sz, i, i, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        L.ar_oracle_all_gather.argtypes = [i, sz, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         for name in ("ar_oracle_f32_to_bf16", "ar_oracle_f32_to_f16",
                      "ar_oracle_f16_to_f32", "ar_oracle_bf16_to_f32"):
             getattr(L, name).argtypes = [vp, vp, sz]
@@ -77,6 +80,38 @@ def allreduce(inputs, dtype, op, nchannels, chunk_elems, all_ranks=False):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return outs_np if all_ranks else outs_np[0]
+
+
+def reduce_scatter(inputs, dtype, op):
+    """Ring ReduceScatter: inputs[r] has N*count elements; returns the list of
+    per-rank outputs (count elements each)."""
+    n = len(inputs)
+    total = _check_inputs(inputs, dtype)
+    if total % n:
+        raise ValueError("ReduceScatter inputs must hold nranks * count elements")
+    count = total // n
+    st = NP_STORAGE[dtype]
+    outs = [np.empty(count, dtype=st) for _ in range(n)]
+    vp = ctypes.c_void_p
+    ins = (vp * n)(*[x.ctypes.data for x in inputs])
+    outp = (vp * n)(*[o.ctypes.data for o in outs])
+    if lib().ar_oracle_reduce_scatter(n, count, DTYPES[dtype], OPS[op], ins, outp) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return outs
+
+
+def all_gather(inputs, dtype):
+    """AllGather: returns the list of per-rank outputs (N*count elements)."""
+    n = len(inputs)
+    count = _check_inputs(inputs, dtype)
+    st = NP_STORAGE[dtype]
+    outs = [np.empty(n * count, dtype=st) for _ in range(n)]
+    vp = ctypes.c_void_p
+    ins = (vp * n)(*[x.ctypes.data for x in inputs])
+    outp = (vp * n)(*[o.ctypes.data for o in outs])
+    if lib().ar_oracle_all_gather(n, count, ELEM_SIZE[dtype], ins, outp) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return outs
 
 
 def elements(inputs, dtype, op, nchannels, chunk_elems, idx):

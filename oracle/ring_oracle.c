@@ -43,6 +43,17 @@
  *  - A debug-only uint64 "probe" op, acc = acc*16 + x, is not commutative, so a
  *    folded value spells out the order in which ranks were visited.
  *
+ *  - ReduceScatter and AllGather, the two halves of the same ring [same book,
+ *    ch.5 §三: nSteps is 2(nRanks-1) for AllReduce and nRanks-1 for the
+ *    others; ch.6 §三: their traffic is nRanks times the count, and AllGather
+ *    moves bytes with no reduction].  With the collective's usual meaning
+ *    (rank r's ReduceScatter output is the reduction of block r of every
+ *    rank's input; AllGather's output is every rank's input in rank order),
+ *    the reduce-scatter half of the ring gives block b the order
+ *        acc = x[b+1][b-th block]; acc = OP(acc, x[b+k][b-th block]), k=2..N
+ *    (it leaves rank b+1 raw and is finished at its owner b), whatever the
+ *    channel and chunk split.
+ *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math; x86-64 SSE
  * arithmetic, default MXCSR, so no flush-to-zero).
  */
@@ -308,6 +319,43 @@ int ar_oracle_elements(int nranks, size_t count, int dtype, int op, int nchannel
                                (size_t)idx[i], (unsigned char*)results + i * esz);
     if (rc != 0) return rc;
   }
+  return 0;
+}
+
+/* ReduceScatter: in[r] holds nranks*count elements (block q at q*count),
+ * out[r] receives count elements: the ring fold of block r over all ranks. */
+int ar_oracle_reduce_scatter(int nranks, size_t count, int dtype, int op, const void* const* in,
+                             void* const* out) {
+  if (check_args(nranks, dtype, op, 1, 16 / (elem_size(dtype) ? elem_size(dtype) : 1)) != 0) return -1;
+  size_t esz = elem_size(dtype);
+  if (count == 0) return 0;
+  enum { TMP_BYTES = 1 << 16 };
+  unsigned char acc[TMP_BYTES];
+  size_t tmp_elems = TMP_BYTES / esz;
+  for (int b = 0; b < nranks; ++b) {              /* block b is finished at rank b */
+    size_t base = (size_t)b * count;
+    for (size_t p = 0; p < count; p += tmp_elems) {
+      size_t n = min_sz(tmp_elems, count - p);
+      int start = nranks == 1 ? 0 : (b + 1) % nranks;
+      memcpy(acc, (const unsigned char*)in[start] + (base + p) * esz, n * esz);
+      for (int k = 2; k <= nranks; ++k) {
+        int r = (b + k) % nranks;
+        fold(dtype, op, acc, (const unsigned char*)in[r] + (base + p) * esz, n);
+      }
+      memcpy((unsigned char*)out[b] + p * esz, acc, n * esz);
+    }
+  }
+  return 0;
+}
+
+/* AllGather: in[r] holds count elements of elem_bytes each; out[r] receives
+ * nranks*count elements, rank q's input at q*count. */
+int ar_oracle_all_gather(int nranks, size_t count, size_t elem_bytes, const void* const* in,
+                         void* const* out) {
+  if (nranks < 1 || elem_bytes == 0) return -1;
+  for (int r = 0; r < nranks; ++r)
+    for (int q = 0; q < nranks; ++q)
+      memcpy((unsigned char*)out[r] + (size_t)q * count * elem_bytes, in[q], count * elem_bytes);
   return 0;
 }
 

@@ -296,3 +296,66 @@ def test_nan_stays_nan(orc):
     x = np.array([np.nan, -np.nan], dtype=np.float32)
     assert np.all(np.isnan(orc.f16_to_f32(orc.f32_to_f16(x))))
     assert np.all(np.isnan(orc.bf16_to_f32(orc.f32_to_bf16(x))))
+
+
+# ---------------------------------------------------------------- ReduceScatter / AllGather
+
+@pytest.mark.parametrize("n", [1, 2, 3, 6])
+@pytest.mark.parametrize("count", [1, 17, 64])
+def test_reduce_scatter_int_brute_force(orc, n, count):
+    xs = gen.make_inputs(n, n * count, "int32", seed=n + count)
+    outs = orc.reduce_scatter(xs, "int32", "sum")
+    total = np.sum(np.stack(xs).astype(np.int64), axis=0).astype(np.int32)
+    for r in range(n):
+        assert np.array_equal(outs[r], total[r * count:(r + 1) * count])
+    for op, f in (("max", np.max), ("min", np.min)):
+        outs = orc.reduce_scatter(xs, "int32", op)
+        ref = f(np.stack(xs), axis=0)
+        for r in range(n):
+            assert np.array_equal(outs[r], ref[r * count:(r + 1) * count])
+
+
+@pytest.mark.parametrize("n", [2, 5, 13])
+def test_reduce_scatter_order_probe(orc, n):
+    # block b is folded b+1, b+2, ..., b (the reduce-scatter half of the ring)
+    count = 3
+    xs = gen.probe_inputs(n, n * count)
+    outs = orc.reduce_scatter(xs, "uint64", "probe")
+    for b in range(n):
+        expect = [((b + k) % n) + 1 for k in range(1, n + 1)]
+        for e in range(count):
+            assert _digits(int(outs[b][e]), n) == expect
+
+
+def test_reduce_scatter_fp16_hops_match_numpy(orc):
+    n, count = 4, 50
+    xs = gen.make_inputs(n, n * count, "float16", seed=3)
+    h = [x.view(np.float16) for x in xs]
+    outs = orc.reduce_scatter(xs, "float16", "sum")
+    for b in range(n):
+        sl = slice(b * count, (b + 1) * count)
+        acc = h[(b + 1) % n][sl].copy()
+        for k in range(2, n + 1):
+            acc = acc + h[(b + k) % n][sl]
+        assert np.array_equal(outs[b], acc.view(np.uint16))
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bfloat16"])
+def test_all_gather_is_concatenation(orc, dtype):
+    n, count = 5, 333
+    xs = gen.make_inputs(n, count, dtype, seed=4)
+    outs = orc.all_gather(xs, dtype)
+    ref = np.concatenate(xs)
+    for o in outs:
+        assert np.array_equal(o, ref)
+
+
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+def test_allreduce_is_allgather_of_reducescatter_for_int(orc, op):
+    # AllReduce = ReduceScatter + AllGather [ch.5 §四]; exact for integers
+    n, count = 6, 1000
+    xs = gen.make_inputs(n, n * count, "int32", seed=8)
+    ag = orc.all_gather(orc.reduce_scatter(xs, "int32", op), "int32")
+    ar = orc.allreduce(xs, "int32", op, 3, 64)
+    for o in ag:
+        assert np.array_equal(o, ar)
