@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--lanes", type=int, default=0, help="force wavefronts per (rank, channel)")
     ap.add_argument("--explore", default="", help="'nch1,nch2:lanes1,lanes2' grid of configurations")
+    ap.add_argument("--coll", default="allreduce", choices=["allreduce", "reducescatter", "allgather"],
+                    help="collective to time; for the two halves --count is the per-rank block "
+                         "(default: 256 MiB per rank on the larger side)")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure latency vs ranks and bandwidth vs channels per protocol and fit arTune's model")
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -88,6 +91,9 @@ def main():
         return sweep(args, B, gen, torch, np)
     if args.calibrate:
         return calibrate(args, B, torch, np)
+
+    if args.coll != "allreduce":
+        return bench_halves(args, B, gen, torch, np)
 
     N, count, dtype = args.nranks, args.count, args.dtype
     esz = gen.ELEM_SIZE[dtype]
@@ -283,6 +289,96 @@ def cpu_baseline(xs, dtype, plan, N, S):
     return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "the full %d x %d MiB %s workload, %d run(s) of the single-threaded C oracle, "
                       "%.2f s each" % (N, S >> 20, dtype, reps, t)}
+
+
+def bench_halves(args, B, gen, torch, np):
+    """ReduceScatter or AllGather on their own (the two halves of the ring).
+    B = block bytes; algbw = N*B/t, busbw = algbw*(N-1)/N; model bytes
+    3N(N-1)B (reduce-scatter steps read 2 blocks, write 1) or 2N(N-1)B
+    (all-gather steps read 1, write 1)."""
+    N, dtype = args.nranks, args.dtype
+    esz = gen.ELEM_SIZE[dtype]
+    count = args.count // N if args.count == 64 << 20 else args.count   # block elements
+    rs = args.coll == "reducescatter"
+    Bb = count * esz
+    tdt = {"float32": torch.float32, "int32": torch.int32, "float16": torch.float16,
+           "bfloat16": torch.bfloat16}[dtype]
+    in_count = N * count if rs else count
+    log("generating inputs: %d ranks x %d %s (seed %d)" % (N, in_count, dtype, args.seed))
+    xs = gen.make_inputs(N, in_count, dtype, seed=args.seed)
+
+    def dev(x):
+        d = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to("cuda")
+        return d.view(tdt) if d.dtype != tdt else d
+    sends = [dev(x) for x in xs]
+    recvs = [torch.empty(count if rs else N * count, dtype=tdt, device="cuda") for _ in range(N)]
+    comm = B.Comm(N, args.nchannels, args.proto)
+    plan = comm.plan(count, dtype, func=args.coll)
+    log("plan: %s" % json.dumps(plan))
+    stream = torch.cuda.Stream()
+    dt_code = B.DTYPE_BY_NAME[dtype]
+
+    def call():
+        if rs:
+            comm.reduce_scatter(sends, recvs, B.arSum, stream=stream, recvcount=count, dtype=dt_code)
+        else:
+            comm.all_gather(sends, recvs, stream=stream, sendcount=count, dtype=dt_code)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+    if comm.async_error() != B.arSuccess:
+        raise SystemExit("timed run failed")
+    ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    t = ms / 1e3
+    algbw = N * Bb / t / 1e9
+    busbw = algbw * (N - 1) / N
+    model_bytes = plan["modelBytes"]
+    achieved = model_bytes / t / 1e9
+    if rs:   # sanity: a sample of rank 3's block against a float64 direct sum (torch, no oracle)
+        idx = torch.randint(0, count, (100000,), device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+        s64 = sum(x[3 * count + idx].double() for x in sends)
+        log("sample max |err| vs float64 = %.3g" % (recvs[3][idx].double() - s64).abs().max().item())
+    else:
+        log("every rank holds the concatenation: %s" % all(torch.equal(r, torch.cat(sends)) for r in recvs))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        reps, total = 0, 0.0
+        while total < 10.0 and reps < 50:
+            t0 = time.perf_counter()
+            if rs:
+                oracle.reduce_scatter(xs, dtype, "sum")
+            else:
+                oracle.all_gather(xs, dtype)
+            total += time.perf_counter() - t0
+            reps += 1
+        tc = total / reps
+        cpu = {"value": round(N * Bb / tc / 1e9 * (N - 1) / N, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the full workload, %d run(s) of the single-threaded C oracle, %.2f s each" % (reps, tc)}
+    comm.close()
+    name = "ReduceScatter" if rs else "AllGather"
+    print(json.dumps({
+        "metric": "emulated ring %s busbw GB/s + %% HBM peak" % name, "value": round(busbw, 3), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"float32": "f32", "bfloat16": "bf16", "float16": "f16", "int32": "i32"}[dtype],
+        "data": "synthetic",
+        "config": {"workload": "ring %s Sum, %d virtual ranks, %d MiB blocks (%d MiB per rank on the larger side)"
+                               % (name, N, Bb >> 20, (N * Bb) >> 20), "nranks": N, "block_elems": count,
+                   "proto": B.PROTO_NAMES[plan["proto"]], "nChannels": plan["nChannels"],
+                   "lanesPerChannel": plan["lanesPerChannel"], "workgroups": plan["workgroups"]},
+        "algbw_GBs": round(algbw, 3), "busbw_GBs": round(busbw, 3), "model_bytes_per_step": model_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):

@@ -121,6 +121,34 @@ arResult_t arAllReduce(arComm_t comm, const void* const* sendbufs, void* const* 
                        size_t count, arDataType_t dtype, arRedOp_t op, void* stream);
 
 /*
+ * arReduceScatter -- rank r's recvbuf receives the reduction, over all ranks,
+ * of block r of their sendbufs: the reduce-scatter half of the ring on its own
+ * [B ch.5 §三: nSteps = nRanks-1; ch.6 §三: traffic nRanks x count].
+ *  sendbufs  (host array of nranks device pointers) nranks*recvcount elements
+ *            each; block q is elements [q*recvcount, (q+1)*recvcount).
+ *  recvbufs  (host array of nranks device pointers) recvcount elements each.
+ *            In place is recvbufs[r] == sendbufs[r] + r*recvcount elements.
+ * Block b is folded in ring order b+1, b+2, ..., b (acc the incoming partial),
+ * whatever the channel split.  Same protocols, errors and stream semantics as
+ * arAllReduce.
+ */
+arResult_t arReduceScatter(arComm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                           size_t recvcount, arDataType_t dtype, arRedOp_t op, void* stream);
+
+/*
+ * arAllGather -- rank r's recvbuf receives every rank's sendbuf in rank order:
+ * the all-gather half of the ring on its own [B ch.5 §三; ch.6 §三: it moves
+ * data without reduction].
+ *  sendbufs  (host array) sendcount elements each.
+ *  recvbufs  (host array) nranks*sendcount elements each; rank q's data at
+ *            [q*sendcount, (q+1)*sendcount).  In place is sendbufs[r] ==
+ *            recvbufs[r] + r*sendcount elements.
+ * dtype only sets the element size (arUint64 included).
+ */
+arResult_t arAllGather(arComm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                       size_t sendcount, arDataType_t dtype, void* stream);
+
+/*
  * arTune -- choose protocol and channel count for a per-rank message of
  * nBytes with the pages' cost model [B ch.5 §一 (argmin over candidates),
  * §三 (ring bandwidth and latency); T §五, time = lat*latCount +
@@ -157,6 +185,19 @@ typedef struct {
 arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
                       unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs);
 
+/* Collectives, for the tuner and plan queries. */
+typedef enum { arFuncAllReduce = 0, arFuncReduceScatter = 1, arFuncAllGather = 2 } arFunc_t;
+
+/*
+ * arTuneEvalColl -- arTuneEval for any of the three collectives: nSteps is
+ * 2(N-1) for AllReduce and N-1 for ReduceScatter / AllGather, algBw =
+ * busBw*N/nSteps [B ch.5 §三].  nBytes is the per-rank message for AllReduce
+ * and nranks x count x element size for the other two (their traffic)
+ * [B ch.6 §三].
+ */
+arResult_t arTuneEvalColl(arFunc_t func, int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
+                          unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs);
+
 /* Read / replace the tuner constants of a comm (calibration). */
 arResult_t arTuneGetModel(arComm_t comm, arProto_t proto, arTuneModel_t* model);
 arResult_t arTuneSetModel(arComm_t comm, arProto_t proto, const arTuneModel_t* model);
@@ -188,6 +229,14 @@ typedef struct {
  * would use for buffers that are 128-byte aligned (aligned128 = 1) or not.
  */
 arResult_t arGetPlan(arComm_t comm, size_t count, arDataType_t dtype, int aligned128, arPlan_t* plan);
+
+/* Same for any collective; count as in that collective's call (recvcount /
+ * sendcount for ReduceScatter / AllGather).  modelBytes is 5(N-1)*S for
+ * AllReduce, 3N(N-1)*B for ReduceScatter and 2N(N-1)*B for AllGather (B =
+ * block bytes): each reduce-scatter step reads 2 blocks and writes 1, each
+ * all-gather step reads 1 and writes 1. */
+arResult_t arGetPlanColl(arComm_t comm, arFunc_t func, size_t count, arDataType_t dtype, int aligned128,
+                         arPlan_t* plan);
 
 /*
  * arCommGetAsyncError -- non-blocking: arRemoteError once any ring member of

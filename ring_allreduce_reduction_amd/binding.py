@@ -22,6 +22,9 @@ arInt32, arFloat32, arFloat16, arBfloat16, arUint64 = 0, 1, 2, 3, 4
 arSum, arMax, arMin, arProbe = 0, 1, 2, 3
 arDebugTimeoutUs, arDebugDeadRank, arDebugLanes, arDebugSimpleSlotKiB, arDebugDirect, arDebugSlots = 0, 1, 2, 3, 4, 5
 AR_MAX_RANKS, AR_MAX_CHANNELS = 128, 64
+arFuncAllReduce, arFuncReduceScatter, arFuncAllGather = 0, 1, 2
+FUNC_BY_NAME = {"allreduce": arFuncAllReduce, "reducescatter": arFuncReduceScatter,
+                "allgather": arFuncAllGather}
 
 PROTO_NAMES = {arProtoLL: "LL", arProtoLL128: "LL128", arProtoSimple: "Simple", arProtoAuto: "auto"}
 PROTO_BY_NAME = {"ll": arProtoLL, "ll128": arProtoLL128, "simple": arProtoSimple, "auto": arProtoAuto}
@@ -63,7 +66,12 @@ def lib():
         c_int, c_sz, vp, c_f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
         L.arInit.argtypes = [ctypes.POINTER(vp), c_int, c_int, c_int, c_int]
         L.arAllReduce.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), c_sz, c_int, c_int, vp]
+        L.arReduceScatter.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), c_sz, c_int, c_int, vp]
+        L.arAllGather.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), c_sz, c_int, vp]
         L.arTune.argtypes = [vp, c_sz, ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_f)]
+        L.arTuneEvalColl.argtypes = [c_int, c_int, c_int, c_sz, ctypes.POINTER(arTuneModel_t), ctypes.c_uint,
+                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_f)]
+        L.arGetPlanColl.argtypes = [vp, c_int, c_sz, c_int, c_int, ctypes.POINTER(arPlan_t)]
         L.arTuneEval.argtypes = [c_int, c_int, c_sz, ctypes.POINTER(arTuneModel_t), ctypes.c_uint,
                                  ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_f)]
         L.arTuneGetModel.argtypes = [vp, c_int, ctypes.POINTER(arTuneModel_t)]
@@ -76,8 +84,9 @@ def lib():
         L.arSetDebug.argtypes = [vp, c_int, ctypes.c_int64]
         L.arGetErrorString.argtypes = [c_int]
         L.arGetErrorString.restype = ctypes.c_char_p
-        for fn in ("arInit", "arAllReduce", "arTune", "arTuneEval", "arTuneGetModel", "arTuneSetModel",
-                   "arSetConfig", "arGetPlan", "arCommGetAsyncError", "arCommAbort", "arDestroy", "arSetDebug"):
+        for fn in ("arInit", "arAllReduce", "arReduceScatter", "arAllGather", "arTune", "arTuneEval",
+                   "arTuneEvalColl", "arTuneGetModel", "arTuneSetModel", "arSetConfig", "arGetPlan", "arGetPlanColl",
+                   "arCommGetAsyncError", "arCommAbort", "arDestroy", "arSetDebug"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -131,6 +140,48 @@ def arAllReduce(comm, sendbufs, recvbufs, count=None, dtype=None, op=arSum, stre
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     _check(lib().arAllReduce(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(count), int(dtype), int(op),
                              ctypes.c_void_p(handle)), "arAllReduce")
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def arReduceScatter(comm, sendbufs, recvbufs, recvcount=None, dtype=None, op=arSum, stream=None):
+    """sendbufs[r]: nranks*recvcount elements; recvbufs[r]: recvcount elements."""
+    if recvcount is None:
+        recvcount = recvbufs[0].numel()
+    if dtype is None:
+        dtype = _dtype_of(sendbufs[0])
+    _check(lib().arReduceScatter(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(recvcount), int(dtype), int(op),
+                                 ctypes.c_void_p(_stream_handle(stream))), "arReduceScatter")
+
+
+def arAllGather(comm, sendbufs, recvbufs, sendcount=None, dtype=None, stream=None):
+    """sendbufs[r]: sendcount elements; recvbufs[r]: nranks*sendcount elements."""
+    if sendcount is None:
+        sendcount = sendbufs[0].numel()
+    if dtype is None:
+        dtype = _dtype_of(sendbufs[0])
+    _check(lib().arAllGather(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(sendcount), int(dtype),
+                             ctypes.c_void_p(_stream_handle(stream))), "arAllGather")
+
+
+def arTuneEvalColl(func, nranks, maxChannels, nBytes, models, protoMask=7):
+    arr = (arTuneModel_t * 3)(*[arTuneModel_t(*m) for m in models])
+    p, ch, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_float()
+    rc = lib().arTuneEvalColl(int(func), int(nranks), int(maxChannels), int(nBytes), arr, int(protoMask),
+                              ctypes.byref(p), ctypes.byref(ch), ctypes.byref(t))
+    _check(rc, "arTuneEvalColl")
+    return p.value, ch.value, t.value
+
+
+def arGetPlanColl(comm, func, count, dtype, aligned128=True):
+    p = arPlan_t()
+    _check(lib().arGetPlanColl(comm, int(func), int(count), int(dtype), 1 if aligned128 else 0, ctypes.byref(p)),
+           "arGetPlanColl")
+    return {f: getattr(p, f) for f, _ in arPlan_t._fields_}
 
 
 def arTune(comm, nBytes):
@@ -201,10 +252,20 @@ class Comm:
             op = OP_BY_NAME[op]
         arAllReduce(self.handle, sendbufs, recvbufs, count=count, dtype=dtype, op=op, stream=stream)
 
-    def plan(self, count, dtype, aligned128=True):
+    def plan(self, count, dtype, aligned128=True, func=arFuncAllReduce):
         if isinstance(dtype, str):
             dtype = DTYPE_BY_NAME[dtype]
-        return arGetPlan(self.handle, count, dtype, aligned128)
+        if isinstance(func, str):
+            func = FUNC_BY_NAME[func]
+        return arGetPlanColl(self.handle, func, count, dtype, aligned128)
+
+    def reduce_scatter(self, sendbufs, recvbufs, op=arSum, stream=None, recvcount=None, dtype=None):
+        if isinstance(op, str):
+            op = OP_BY_NAME[op]
+        arReduceScatter(self.handle, sendbufs, recvbufs, recvcount=recvcount, dtype=dtype, op=op, stream=stream)
+
+    def all_gather(self, sendbufs, recvbufs, stream=None, sendcount=None, dtype=None):
+        arAllGather(self.handle, sendbufs, recvbufs, sendcount=sendcount, dtype=dtype, stream=stream)
 
     def set_config(self, proto, nChannels):
         if isinstance(proto, str):

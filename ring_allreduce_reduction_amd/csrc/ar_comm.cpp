@@ -168,10 +168,12 @@ void freeComm(arComm* c) {
 }
 
 // Protocol, channels, chunk, lanes and grid for one call.
-arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned128, Plan* plan) {
+arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool aligned128, Plan* plan) {
   const Env& e = env();
   const int esz = elemSize(dtype);
-  const uint64_t nBytes = count * (uint64_t)esz;
+  // the tuner's message: per rank for AllReduce, the whole nranks x count
+  // traffic for ReduceScatter / AllGather [ch.6 §三]
+  const uint64_t nBytes = count * (uint64_t)esz * (func == kCollAllReduce ? 1u : (uint64_t)c->nranks);
   int proto = e.forcedProto != -2 ? e.forcedProto : c->proto;
   int nch = e.nChannels > 0 ? e.nChannels : c->nChannels;
   if (nch > c->maxChannels) nch = c->maxChannels;
@@ -182,13 +184,15 @@ arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned12
     if (mask == 0) mask = 1u << arProtoSimple;
     arProto_t p;
     int ch;
-    arResult_t r = arTuneEval(c->nranks, c->maxChannels, nBytes, c->models, mask, &p, &ch, &predicted);
+    arResult_t r = arTuneEvalColl((arFunc_t)func, c->nranks, c->maxChannels, nBytes, c->models, mask, &p, &ch,
+                                  &predicted);
     if (r != arSuccess) return r;
     proto = p;
     nch = ch < 1 ? 1 : ch;
   } else {
     if (proto == arProtoLL128 && !aligned128) return arInvalidUsage;   // LL128 needs 128-byte buffers
-    (void)arTuneEval(c->nranks, nch, nBytes, c->models, 1u << proto, nullptr, nullptr, &predicted);
+    (void)arTuneEvalColl((arFunc_t)func, c->nranks, nch, nBytes, c->models, 1u << proto, nullptr, nullptr,
+                         &predicted);
   }
   const int N = c->nranks;
   const uint64_t A = 16 / (uint64_t)esz;
@@ -226,7 +230,7 @@ arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned12
         layout(gs, &nGroups, &groupSize);
         plan->block = groupSize * kWave;
         int perCU = 0;
-        if (ringKernelOccupancy(*plan, dtype, op, &perCU) != hipSuccess) return arHipError;
+        if (ringKernelOccupancy(*plan, func, dtype, op, &perCU) != hipSuccess) return arHipError;
         const int grid1 = ((nch + 7) / 8) * 8 * nGroups;
         found = perCU * c->numCUs >= grid1;
       }
@@ -244,10 +248,13 @@ arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned12
   // lane share below two FIFO slots of the largest chunk.
   const uint64_t per = alignUpU(divUpU(count, (uint64_t)nch), A);
   const uint64_t loop = (uint64_t)N * plan->chunkElems;
-  const uint64_t cur = per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
+  // elements one stage of one member covers: a chunk of the AllReduce loop,
+  // or the loop's range of one rank block for ReduceScatter / AllGather
+  const uint64_t cur = func != kCollAllReduce ? (per < plan->chunkElems ? per : plan->chunkElems)
+                       : per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
   const uint64_t chunkBytes = cur * (uint64_t)esz;
   int perCU = 0;
-  if (ringKernelOccupancy(*plan, dtype, op, &perCU) != hipSuccess) return arHipError;
+  if (ringKernelOccupancy(*plan, func, dtype, op, &perCU) != hipSuccess) return arHipError;
   if (perCU < 1) perCU = 1;
   const int capacity = perCU * c->numCUs;   // resident workgroups
   auto gridFor = [&](int ln) {
@@ -290,8 +297,6 @@ arResult_t makePlan(arComm* c, uint64_t count, int dtype, int op, bool aligned12
   plan->grid = gridFor(lanes);
   return arSuccess;
 }
-
-bool rangesOverlap(uintptr_t a, uintptr_t b, size_t n) { return a < b + n && b < a + n; }
 
 }  // namespace
 
@@ -450,18 +455,22 @@ arResult_t arTune(arComm_t c, size_t nBytes, arProto_t* proto, int* nChannels, f
                     predictedUs);
 }
 
-arResult_t arGetPlan(arComm_t c, size_t count, arDataType_t dtype, int aligned128, arPlan_t* out) {
+arResult_t arGetPlanColl(arComm_t c, arFunc_t func, size_t count, arDataType_t dtype, int aligned128,
+                         arPlan_t* out) {
   if (!commOk(c) || out == nullptr || elemSize(dtype) == 0) return arInvalidArgument;
+  if (func != arFuncAllReduce && func != arFuncReduceScatter && func != arFuncAllGather) return arInvalidArgument;
   const int op = dtype == arUint64 ? arProbe : arSum;
   memset(out, 0, sizeof(*out));
   const double S = (double)count * elemSize(dtype);
-  out->modelBytes = 5.0 * (double)(c->nranks - 1) * S;
+  const double N = (double)c->nranks;
+  out->modelBytes = func == arFuncAllReduce ? 5.0 * (N - 1.0) * S
+                    : func == arFuncReduceScatter ? 3.0 * N * (N - 1.0) * S : 2.0 * N * (N - 1.0) * S;
   if (c->nranks == 1 || count == 0) {
     out->proto = arProtoSimple;
     return arSuccess;
   }
   Plan p;
-  arResult_t r = makePlan(c, count, dtype, op, aligned128 != 0, &p);
+  arResult_t r = makePlan(c, func, count, dtype, op, aligned128 != 0, &p);
   if (r != arSuccess) return r;
   out->proto = p.proto;
   out->nChannels = p.nChannels;
@@ -477,19 +486,32 @@ arResult_t arGetPlan(arComm_t c, size_t count, arDataType_t dtype, int aligned12
   return arSuccess;
 }
 
-arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t count,
-                       arDataType_t dtype, arRedOp_t op, void* stream) {
+arResult_t arGetPlan(arComm_t c, size_t count, arDataType_t dtype, int aligned128, arPlan_t* out) {
+  return arGetPlanColl(c, arFuncAllReduce, count, dtype, aligned128, out);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One collective call: argument checks (nothing is enqueued on failure), the
+// empty and one-rank short cuts, planning, kernel arguments, one launch.
+// `count` is per rank for AllReduce and per rank block for the other two.
+arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const* recvbufs, size_t count,
+                   arDataType_t dtype, arRedOp_t op, void* stream) {
   if (!commOk(c)) return arInvalidArgument;
   if (c->aborted) return arInvalidUsage;
   const int esz = elemSize(dtype);
   if (esz == 0) return arInvalidArgument;
   if (op != arSum && op != arMax && op != arMin && op != arProbe) return arInvalidArgument;
-  if ((op == arProbe) != (dtype == arUint64)) return arInvalidArgument;
-  if (count == 0) return arSuccess;   // empty collective: no work
+  if ((op == arProbe) != (dtype == arUint64) && func != kCollAllGather) return arInvalidArgument;
+  if (count == 0) return arSuccess;   // empty collective: no work [ch.6 §三]
   if (sendbufs == nullptr || recvbufs == nullptr) return arInvalidArgument;
   const int N = c->nranks;
   if (count > (uint64_t)1 << 40) return arInvalidArgument;
-  const size_t bytes = count * (size_t)esz;
+  const size_t block = count * (size_t)esz;
+  const size_t sendBytes = func == kCollReduceScatter ? block * (size_t)N : block;
+  const size_t recvBytes = func == kCollAllGather ? block * (size_t)N : block;
   bool aligned16 = true, aligned128 = true;
   for (int r = 0; r < N; ++r) {
     const uintptr_t s = (uintptr_t)sendbufs[r], d = (uintptr_t)recvbufs[r];
@@ -498,15 +520,25 @@ arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* rec
     aligned16 = aligned16 && s % 16 == 0 && d % 16 == 0;
     aligned128 = aligned128 && s % 128 == 0 && d % 128 == 0;
   }
-  // Outputs must not overlap each other or another rank's input; an output
-  // may be its own rank's input exactly (in place).
+  if (func != kCollAllReduce) {   // rank blocks start inside the buffers
+    aligned16 = aligned16 && block % 16 == 0;
+    aligned128 = aligned128 && block % 128 == 0;
+  }
+  // Outputs must not overlap each other or another rank's input.  Against its
+  // own input an output is either disjoint or exactly in place: the same
+  // buffer (AllReduce), block r of the input (ReduceScatter), or the input as
+  // block r of the output (AllGather).
   for (int i = 0; i < N; ++i) {
-    const uintptr_t di = (uintptr_t)recvbufs[i];
-    if (di != (uintptr_t)sendbufs[i] && rangesOverlap(di, (uintptr_t)sendbufs[i], bytes)) return arInvalidArgument;
+    const uintptr_t di = (uintptr_t)recvbufs[i], si = (uintptr_t)sendbufs[i];
+    const bool inPlace = func == kCollAllReduce ? di == si
+                         : func == kCollReduceScatter ? di == si + (uintptr_t)i * block
+                                                      : si == di + (uintptr_t)i * block;
+    if (!inPlace && di < si + sendBytes && si < di + recvBytes) return arInvalidArgument;
     for (int j = 0; j < N; ++j) {
       if (j == i) continue;
-      if (rangesOverlap(di, (uintptr_t)recvbufs[j], bytes)) return arInvalidArgument;
-      if (rangesOverlap(di, (uintptr_t)sendbufs[j], bytes)) return arInvalidArgument;
+      const uintptr_t dj = (uintptr_t)recvbufs[j], sj = (uintptr_t)sendbufs[j];
+      if (di < dj + recvBytes && dj < di + recvBytes) return arInvalidArgument;
+      if (di < sj + sendBytes && sj < di + recvBytes) return arInvalidArgument;
     }
   }
   hipStream_t st = (hipStream_t)stream;
@@ -516,13 +548,14 @@ arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* rec
     c->lastStream = st;
     c->launched = true;
     if (recvbufs[0] == sendbufs[0]) return arSuccess;
-    return hipMemcpyAsync(recvbufs[0], sendbufs[0], bytes, hipMemcpyDeviceToDevice, st) == hipSuccess
+    return hipMemcpyAsync(recvbufs[0], sendbufs[0], block, hipMemcpyDeviceToDevice, st) == hipSuccess
                ? arSuccess
                : arHipError;
   }
 
   Plan plan;
-  arResult_t r = makePlan(c, count, dtype, op, aligned128, &plan);
+  const int kop = func == kCollAllGather ? (dtype == arUint64 ? arProbe : arSum) : op;
+  arResult_t r = makePlan(c, func, count, dtype, kop, aligned128, &plan);
   if (r != arSuccess) return r;
 
   KernelArgs a;
@@ -546,16 +579,17 @@ arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* rec
   a.nSlots = plan.nSlots;
   a.aligned16 = aligned16 ? 1 : 0;
   a.direct = plan.direct ? 1 : 0;
+  a.coll = func;
   a.deadRank = c->deadRank;
 
   if (env().debug >= 1)
     fprintf(stderr,
-            "[ar] INFO op %llu count=%zu dtype=%d op=%d proto=%d nch=%d chunk=%llu lanes=%d groups=%dx%d grid=%d "
-            "block=%d coop=%d unroll=%d direct=%d pred=%.1fus\n",
-            (unsigned long long)c->opCount, count, (int)dtype, (int)op, plan.proto, plan.nChannels,
+            "[ar] INFO op %llu func=%d count=%zu dtype=%d op=%d proto=%d nch=%d chunk=%llu lanes=%d groups=%dx%d "
+            "grid=%d block=%d coop=%d unroll=%d direct=%d pred=%.1fus\n",
+            (unsigned long long)c->opCount, func, count, (int)dtype, (int)op, plan.proto, plan.nChannels,
             (unsigned long long)plan.chunkElems, plan.lanes, plan.nGroups, plan.groupSize, plan.grid, plan.block,
             (int)plan.cooperative, plan.unroll, (int)plan.direct, plan.predictedUs);
-  hipError_t he = launchRing(plan, dtype, op, a, st);
+  hipError_t he = launchRing(plan, dtype, kop, a, st);
   if (he != hipSuccess) {
     fprintf(stderr, "[ar] WARN kernel launch failed: %s\n", hipGetErrorString(he));
     return arHipError;
@@ -563,6 +597,25 @@ arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* rec
   c->lastStream = st;
   c->launched = true;
   return arSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t count,
+                       arDataType_t dtype, arRedOp_t op, void* stream) {
+  return runColl(c, kCollAllReduce, sendbufs, recvbufs, count, dtype, op, stream);
+}
+
+arResult_t arReduceScatter(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t recvcount,
+                           arDataType_t dtype, arRedOp_t op, void* stream) {
+  return runColl(c, kCollReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream);
+}
+
+arResult_t arAllGather(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t sendcount,
+                       arDataType_t dtype, void* stream) {
+  return runColl(c, kCollAllGather, sendbufs, recvbufs, sendcount, dtype, arSum, stream);
 }
 
 arResult_t arCommGetAsyncError(arComm_t c, arResult_t* err) {

@@ -69,6 +69,8 @@ constexpr uint32_t kStatusTimeout = 1;
 constexpr uint32_t kStatusAbort = 2;
 
 enum Proto : int { kLL = 0, kLL128 = 1, kSimple = 2 };
+// Collectives run by the ring kernel (values of arFunc_t).
+enum Coll : int { kCollAllReduce = 0, kCollReduceScatter = 1, kCollAllGather = 2 };
 
 struct KernelArgs {
   const void* send[AR_MAX_RANKS];
@@ -76,7 +78,7 @@ struct KernelArgs {
   char* fifo;                 // this protocol's FIFOs, fifoWorkerBytes per worker
   Conn* conn;                 // this protocol's counters, one per worker
   Control* ctrl;              // host-pinned control block (device address)
-  uint64_t count;             // elements per rank
+  uint64_t count;             // elements per rank (per rank block for ReduceScatter / AllGather)
   uint64_t chunkElems;        // nominal chunk (elements)
   uint64_t fifoWorkerBytes;   // nSlots * slot bytes
   uint64_t timeoutTicks;      // wall-clock ticks a wait may take
@@ -88,6 +90,7 @@ struct KernelArgs {
   int nSlots;
   int aligned16;              // every send/recv base is 16-byte aligned
   int direct;                 // Simple: all-gather writes the successor's output directly
+  int coll;                   // kCollAllReduce / kCollReduceScatter / kCollAllGather (selects the kernel)
   int deadRank;               // debug: this rank's members return at once
 };
 
@@ -112,7 +115,7 @@ struct Plan {
 
 // Provided by ar_kernels.hip.
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream);
-hipError_t ringKernelOccupancy(const Plan& plan, int dtype, int op, int* blocksPerCU);
+hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, int* blocksPerCU);
 
 inline int elemSize(int dtype) {
   switch (dtype) {

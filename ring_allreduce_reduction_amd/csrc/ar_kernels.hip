@@ -35,7 +35,21 @@ typedef uint64_t u64;
 typedef u32 v4u __attribute__((ext_vector_type(4)));
 typedef u32 v2u __attribute__((ext_vector_type(2)));
 
-enum Kind : int { kSend = 0, kRecvReduceSend = 1, kRecvReduceCopySend = 2, kRecvCopySend = 3, kRecv = 4 };
+// A step kind is the set of things a member does with one slot: read its
+// local operand, receive from its predecessor, send to its successor, write
+// its output.  AllReduce uses send / recv-reduce-send / recv-reduce-copy-send /
+// recv-copy-send / recv; ReduceScatter ends with recv-reduce-copy; AllGather
+// starts with copy-send.
+constexpr int kLocalBit = 1, kRecvBit = 2, kSendBit = 4, kOutBit = 8;
+enum Kind : int {
+  kSend = kLocalBit | kSendBit,
+  kRecvReduceSend = kLocalBit | kRecvBit | kSendBit,
+  kRecvReduceCopySend = kLocalBit | kRecvBit | kSendBit | kOutBit,
+  kRecvCopySend = kRecvBit | kSendBit | kOutBit,
+  kRecv = kRecvBit | kOutBit,
+  kRecvReduceCopy = kLocalBit | kRecvBit | kOutBit,
+  kCopySend = kLocalBit | kSendBit | kOutBit,
+};
 
 __device__ __forceinline__ u64 divUp(u64 x, u64 y) { return (x + y - 1) / y; }
 __device__ __forceinline__ u64 alignUp(u64 x, u64 a) { return divUp(x, a) * a; }
@@ -285,17 +299,17 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
                                      char* succOutp, long valid) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
-  const bool hasLocal = kind <= kRecvReduceCopySend;
-  const bool hasRecv = kind >= kRecvReduceSend;
-  const bool hasSend = kind <= kRecvCopySend;
-  const bool hasOut = kind >= kRecvReduceCopySend;
+  const bool hasLocal = (kind & kLocalBit) != 0;
+  const bool hasRecv = (kind & kRecvBit) != 0;
+  const bool hasSend = (kind & kSendBit) != 0;
+  const bool hasOut = (kind & kOutBit) != 0;
   // Direct all-gather (Simple): the member that finishes a chunk and every
   // member forwarding it write the successor's output buffer instead of its
   // FIFO, so the all-gather half moves no FIFO bytes; the receiver then
   // reads the finished chunk from its own output.  [The pages' FIFO slot
   // descriptor can carry a pointer, and a work item can be flagged direct.]
-  const bool directSend = PROTO == kSimple && m.direct && (kind == kRecvReduceCopySend || kind == kRecvCopySend);
-  const bool directRecv = PROTO == kSimple && m.direct && kind >= kRecvCopySend;
+  const bool directSend = PROTO == kSimple && m.direct && hasSend && hasOut;
+  const bool directRecv = PROTO == kSimple && m.direct && hasRecv && hasOut && !hasLocal;
   const int lane = m.lane;
 
   // piece geometry of this lane: payload offset, payload bytes, wire offset
@@ -456,7 +470,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
   return true;
 }
 
-template <int PROTO, int DT, int OP, int U>
+template <int PROTO, int DT, int OP, int U, int COLL>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr u64 A = 16 / ESZ;   // 16-byte grain in elements
@@ -527,39 +541,84 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // chunk size.  The order in which ranks are folded into an element is that
   // of the stage schedule and does not depend on the batching.
   const u64 batch = (u64)(a.nSlots / 2 > 0 ? a.nSlots / 2 : 1);
-  for (u64 off = 0; off < len; off += loopSize) {
-    const u64 rem = len - off;
-    // shrunk chunk on the last partial loop [pages: getNextSendAddr]
-    const u64 cur = rem < loopSize ? alignUp(divUp(rem, (u64)N), A) : C;
-    // no lane share of any chunk in this loop exceeds sub0 (chunk 0 is the
-    // longest chunk and a share is at most the per-lane split of its chunk)
-    const u64 sub0 = alignUp(divUp(umin(cur, rem), (u64)a.lanes), A);
-    const u64 nCols = divUp(sub0 * ESZ, (u64)PAYLOAD);
-    for (u64 jb = 0; jb < nCols; jb += batch) {
-      const u64 je = umin(jb + batch, nCols);
-      for (int s = 0; s <= 2 * N - 2; ++s) {
-        int kind;
-        if (s == 0) kind = kSend;
-        else if (s < N - 1) kind = kRecvReduceSend;
-        else if (s == N - 1) kind = kRecvReduceCopySend;
-        else if (s <= lastSendStage) kind = kRecvCopySend;
-        else kind = kRecv;
-        // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
-        const int c = s <= lastSendStage ? (r - 1 - s + 2 * N) % N : succ;
-        const u64 cb = (u64)c * cur;
-        const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
-        // lane k's share of the chunk (pipelining only: the order is per element)
-        const u64 sub = alignUp(divUp(clen, (u64)a.lanes), A);
-        const u64 sb = umin((u64)k * sub, clen);
-        const u64 se = umin(sb + sub, clen);
-        const u64 bytes = (se - sb) * ESZ;
-        const u64 first = (lo + off + cb + sb) * ESZ;
-        for (u64 j = jb; j < je; ++j) {
-          const u64 b = j * (u64)PAYLOAD;
-          if (b >= bytes) break;
-          const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-          if (!step<PROTO, DT, OP, U>(a, m, kind, in + first + b, out + first + b, succOut + first + b, valid))
-            return;
+  if (COLL == kCollAllReduce) {
+    for (u64 off = 0; off < len; off += loopSize) {
+      const u64 rem = len - off;
+      // shrunk chunk on the last partial loop [pages: getNextSendAddr]
+      const u64 cur = rem < loopSize ? alignUp(divUp(rem, (u64)N), A) : C;
+      // no lane share of any chunk in this loop exceeds sub0 (chunk 0 is the
+      // longest chunk and a share is at most the per-lane split of its chunk)
+      const u64 sub0 = alignUp(divUp(umin(cur, rem), (u64)a.lanes), A);
+      const u64 nCols = divUp(sub0 * ESZ, (u64)PAYLOAD);
+      for (u64 jb = 0; jb < nCols; jb += batch) {
+        const u64 je = umin(jb + batch, nCols);
+        for (int s = 0; s <= 2 * N - 2; ++s) {
+          int kind;
+          if (s == 0) kind = kSend;
+          else if (s < N - 1) kind = kRecvReduceSend;
+          else if (s == N - 1) kind = kRecvReduceCopySend;
+          else if (s <= lastSendStage) kind = kRecvCopySend;
+          else kind = kRecv;
+          // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
+          const int c = s <= lastSendStage ? (r - 1 - s + 2 * N) % N : succ;
+          const u64 cb = (u64)c * cur;
+          const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
+          // lane k's share of the chunk (pipelining only: the order is per element)
+          const u64 sub = alignUp(divUp(clen, (u64)a.lanes), A);
+          const u64 sb = umin((u64)k * sub, clen);
+          const u64 se = umin(sb + sub, clen);
+          const u64 bytes = (se - sb) * ESZ;
+          const u64 first = (lo + off + cb + sb) * ESZ;
+          for (u64 j = jb; j < je; ++j) {
+            const u64 b = j * (u64)PAYLOAD;
+            if (b >= bytes) break;
+            const long valid = (long)umin((u64)PAYLOAD, bytes - b);
+            if (!step<PROTO, DT, OP, U>(a, m, kind, in + first + b, out + first + b, succOut + first + b, valid))
+              return;
+          }
+        }
+      }
+    }
+  } else {
+    // ReduceScatter / AllGather, the two halves of the ring on their own
+    // [pages: nSteps = nRanks-1 for them].  Every stage works on the same
+    // element range of a different rank block (block = `count` elements):
+    //   ReduceScatter: send | recv-reduce-send x (N-2) | recv-reduce-copy, on
+    //                  block (r - 1 - s) mod N, so block b ends at its owner b;
+    //   AllGather:     copy-send | recv-copy-send x (N-2) | recv, on block
+    //                  (r - s) mod N, so block b starts at its owner b.
+    constexpr bool rs = COLL == kCollReduceScatter;
+    const u64 blk = count * ESZ;
+    for (u64 off = 0; off < len; off += C) {
+      const u64 cur = umin(C, len - off);
+      const u64 sub = alignUp(divUp(cur, (u64)a.lanes), A);
+      const u64 sb = umin((u64)k * sub, cur);
+      const u64 se = umin(sb + sub, cur);
+      const u64 bytes = (se - sb) * ESZ;
+      const u64 first = (lo + off + sb) * ESZ;   // byte offset inside a block
+      const u64 nCols = divUp(bytes, (u64)PAYLOAD);
+      for (u64 jb = 0; jb < nCols; jb += batch) {
+        const u64 je = umin(jb + batch, nCols);
+        for (int s = 0; s <= N - 1; ++s) {
+          int kind, blkIdx;
+          if (rs) {
+            kind = s == 0 ? kSend : s < N - 1 ? kRecvReduceSend : kRecvReduceCopy;
+            blkIdx = (r - 1 - s + 2 * N) % N;
+          } else {
+            kind = s == 0 ? kCopySend : s < N - 1 ? kRecvCopySend : kRecv;
+            blkIdx = (r - s + N) % N;
+          }
+          // ReduceScatter reads block b of its input and writes its one
+          // output block; AllGather reads its one input block and writes block b
+          const u64 inOff = rs ? (u64)blkIdx * blk + first : first;
+          const u64 outOff = rs ? first : (u64)blkIdx * blk + first;
+          for (u64 j = jb; j < je; ++j) {
+            const u64 b = j * (u64)PAYLOAD;
+            const long valid = (long)umin((u64)PAYLOAD, bytes - b);
+            if (!step<PROTO, DT, OP, U>(a, m, kind, in + inOff + b, out + outOff + b, succOut + outOff + b,
+                                         valid))
+              return;
+          }
         }
       }
     }
@@ -573,52 +632,68 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
 
 typedef void (*KernelFn)(const KernelArgs);
 
-template <int PROTO, int U>
+template <int PROTO, int U, int COLL>
 KernelFn pick(int dtype, int op) {
+  if (COLL == kCollAllGather) {   // no arithmetic: one kernel per element size
+    switch (dtype) {
+      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL>;
+      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL>;
+      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL>;
+    }
+    return nullptr;
+  }
   switch (dtype) {
     case arInt32:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arInt32, arSum, U>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arInt32, arMax, U>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arInt32, arMin, U>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arInt32, arMax, U, COLL>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arInt32, arMin, U, COLL>;
       break;
     case arFloat32:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat32, arSum, U>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat32, arMax, U>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat32, arMin, U>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat32, arSum, U, COLL>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat32, arMax, U, COLL>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat32, arMin, U, COLL>;
       break;
     case arFloat16:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat16, arSum, U>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat16, arMax, U>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat16, arMin, U>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat16, arSum, U, COLL>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat16, arMax, U, COLL>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat16, arMin, U, COLL>;
       break;
     case arBfloat16:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arBfloat16, arSum, U>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arBfloat16, arMax, U>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arBfloat16, arMin, U>;
+      if (op == arSum) return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL>;
+      if (op == arMax) return ringAllReduceKernel<PROTO, arBfloat16, arMax, U, COLL>;
+      if (op == arMin) return ringAllReduceKernel<PROTO, arBfloat16, arMin, U, COLL>;
       break;
     case arUint64:
-      if (op == arProbe) return ringAllReduceKernel<PROTO, arUint64, arProbe, U>;
+      if (op == arProbe) return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL>;
       break;
   }
   return nullptr;
 }
 
-KernelFn pickKernel(const Plan& plan, int dtype, int op) {
-  if (plan.proto == kLL) return pick<kLL, kLLUnroll>(dtype, op);
-  if (plan.proto == kLL128) return pick<kLL128, kLL128Unroll>(dtype, op);
+template <int COLL>
+KernelFn pickProto(const Plan& plan, int dtype, int op) {
+  if (plan.proto == kLL) return pick<kLL, kLLUnroll, COLL>(dtype, op);
+  if (plan.proto == kLL128) return pick<kLL128, kLL128Unroll, COLL>(dtype, op);
   if (plan.proto == kSimple) {
-    if (plan.unroll == 1) return pick<kSimple, 1>(dtype, op);
-    if (plan.unroll == 2) return pick<kSimple, 2>(dtype, op);
-    if (plan.unroll == 4) return pick<kSimple, 4>(dtype, op);
-    if (plan.unroll == 8) return pick<kSimple, 8>(dtype, op);
+    if (plan.unroll == 1) return pick<kSimple, 1, COLL>(dtype, op);
+    if (plan.unroll == 2) return pick<kSimple, 2, COLL>(dtype, op);
+    if (plan.unroll == 4) return pick<kSimple, 4, COLL>(dtype, op);
+    if (plan.unroll == 8) return pick<kSimple, 8, COLL>(dtype, op);
   }
+  return nullptr;
+}
+
+KernelFn pickKernel(const Plan& plan, int coll, int dtype, int op) {
+  if (coll == kCollAllReduce) return pickProto<kCollAllReduce>(plan, dtype, op);
+  if (coll == kCollReduceScatter) return pickProto<kCollReduceScatter>(plan, dtype, op);
+  if (coll == kCollAllGather) return pickProto<kCollAllGather>(plan, dtype, op);
   return nullptr;
 }
 
 }  // namespace
 
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream) {
-  KernelFn fn = pickKernel(plan, dtype, op);
+  KernelFn fn = pickKernel(plan, args.coll, dtype, op);
   if (fn == nullptr) return hipErrorInvalidValue;
   if (plan.cooperative) {
     void* params[] = {(void*)&args};
@@ -628,8 +703,8 @@ hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& arg
   return hipGetLastError();
 }
 
-hipError_t ringKernelOccupancy(const Plan& plan, int dtype, int op, int* blocksPerCU) {
-  KernelFn fn = pickKernel(plan, dtype, op);
+hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, int* blocksPerCU) {
+  KernelFn fn = pickKernel(plan, coll, dtype, op);
   if (fn == nullptr) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocksPerCU, (const void*)fn, plan.block, 0);
 }

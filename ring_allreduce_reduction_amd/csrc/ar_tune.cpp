@@ -25,12 +25,11 @@ namespace {
 
 constexpr size_t kMinBytesPerChannel = 32 * 1024;
 
-float candidateTime(const arTuneModel_t& m, int proto, int nranks, int nch, size_t nBytes) {
+float candidateTime(const arTuneModel_t& m, int proto, int nranks, int nSteps, int nch, size_t nBytes) {
   float busBw = m.bwPerChGBs * (float)nch;
   if (proto == arProtoLL) busBw = busBw * 0.5f;
   else if (proto == arProtoLL128) busBw = busBw * 0.92f;
   if (busBw > m.maxBwGBs) busBw = m.maxBwGBs;
-  const int nSteps = 2 * (nranks - 1);
   const float algBw = busBw * (float)nranks / (float)nSteps;
   const float lat = m.baseLatUs + (float)nSteps * m.stepLatUs;
   return lat * 1.0f + (float)nBytes / (1000.0f * algBw);
@@ -42,9 +41,13 @@ bool validModel(const arTuneModel_t& m) {
 
 }  // namespace
 
-extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
-                                 unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs) {
+extern "C" arResult_t arTuneEvalColl(arFunc_t func, int nranks, int maxChannels, size_t nBytes,
+                                     const arTuneModel_t* models, unsigned protoMask, arProto_t* proto,
+                                     int* nChannels, float* predictedUs) {
   if (nranks < 1 || maxChannels < 1 || models == nullptr) return arInvalidArgument;
+  if (func != arFuncAllReduce && func != arFuncReduceScatter && func != arFuncAllGather) return arInvalidArgument;
+  // ring steps per call [ch.5 §三]: 2(N-1) for AllReduce, N-1 for the halves
+  const int nSteps = func == arFuncAllReduce ? 2 * (nranks - 1) : nranks - 1;
   if ((protoMask & 7u) == 0) return arInvalidArgument;
   if (nranks == 1) {
     if (proto) *proto = arProtoSimple;
@@ -62,7 +65,7 @@ extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, con
     int bestChP = 0;
     for (int nch = 1; nch <= maxChannels; nch *= 2) {
       if (nch > 1 && nBytes / (size_t)nch < kMinBytesPerChannel) break;
-      const float t = candidateTime(models[p], p, nranks, nch, nBytes);
+      const float t = candidateTime(models[p], p, nranks, nSteps, nch, nBytes);
       if (t <= bestP) {
         bestP = t;
         bestChP = nch;
@@ -79,4 +82,10 @@ extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, con
   if (nChannels) *nChannels = bestCh;
   if (predictedUs) *predictedUs = best;
   return arSuccess;
+}
+
+extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
+                                 unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs) {
+  return arTuneEvalColl(arFuncAllReduce, nranks, maxChannels, nBytes, models, protoMask, proto, nChannels,
+                        predictedUs);
 }

@@ -12,6 +12,7 @@ from ring_allreduce_reduction_amd import inputs as gen
 TORCH_STORAGE = {"int32": torch.int32, "float32": torch.float32, "float16": torch.int16,
                  "bfloat16": torch.int16, "uint64": torch.int64}
 TORCH_VIEW = {"float16": torch.float16, "bfloat16": torch.bfloat16}
+ELEM = {"int32": 4, "float32": 4, "float16": 2, "bfloat16": 2, "uint64": 8}
 RAW = {"int32": np.uint32, "float32": np.uint32, "float16": np.uint16, "bfloat16": np.uint16,
        "uint64": np.uint64}
 

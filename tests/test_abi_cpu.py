@@ -150,3 +150,17 @@ def test_tuner_errors(B):
     with pytest.raises(B.ArError) as e:
         B.arTuneEval(8, 64, 1024, bad)
     assert e.value.code == B.arInvalidUsage
+
+
+@pytest.mark.parametrize("func", [1, 2])
+@pytest.mark.parametrize("nbytes", [64, 1 << 20, 1 << 28])
+def test_halves_use_n_minus_1_steps(B, func, nbytes):
+    # ReduceScatter / AllGather: nSteps = N-1, algBw = busBw*N/(N-1) [ch.5 §三]
+    n = 8
+    p, ch, t = B.arTuneEvalColl(func, n, 64, nbytes, MODELS)
+    base, step, bw, cap = MODELS[p]
+    bus = min(bw * ch * {0: 0.5, 1: 0.92, 2: 1.0}[p], cap)
+    assert t == pytest.approx(base + (n - 1) * step + nbytes / (1000.0 * bus * n / (n - 1)), rel=1e-5)
+    assert B.arTuneEvalColl(0, n, 64, nbytes, MODELS) == B.arTuneEval(n, 64, nbytes, MODELS)
+    with pytest.raises(B.ArError):
+        B.arTuneEvalColl(3, n, 64, nbytes, MODELS)
