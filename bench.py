@@ -443,17 +443,37 @@ def copy_probe(args, torch):
                       "read_plus_write_GBs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
+def _ring_model_us(params, factor, n, nch, S):
+    """The ring cost model arTune evaluates (same form, any constants)."""
+    base, step, bw, cap = params
+    bus = min(bw * nch * factor, cap)
+    return base + 2 * (n - 1) * step + S / (1000.0 * bus * n / (2 * (n - 1)))
+
+
+def _channels_for(S, maxch=64):
+    """Channels where the model is capped: the most whose share is >= 32 KiB."""
+    c = 1
+    while c * 2 <= maxch and S // (c * 2) >= 32768:
+        c *= 2
+    return c
+
+
 def calibrate(args, B, torch, np):
     """Fit the ring cost model's constants per protocol on this GPU.
 
-    latency:   t at a 4 KiB message (every chunk non-empty), 1 channel,
-               N = 2, 4, 8, 16 ranks;
-               least squares t = base + 2(N-1) * step
-    bandwidth: t at 128 MiB per rank, N = 8, 1..64 channels;
-               busBw = S/(t - lat) * 2(N-1)/N, then bwPerCh from the smallest
-               channel count (divided by the protocol's payload factor) and
-               the cap from the largest measured busBw.
-    Prints one JSON line per measurement and one with the fitted models."""
+    Measured, fp32 Sum:
+      latency:   4 KiB per rank, 1 channel, N = 2, 4, 8, 16;
+      bandwidth: 128 MiB per rank, N = 8, 1..64 channels;
+      mid sizes: 16 KiB .. 64 MiB per rank, N = 8, at the channel count the
+                 32 KiB-per-channel rule allows (where arTune lands once the
+                 bandwidth is capped).
+    The four constants (base, step, bwPerCh, cap) are the least-squares fit of
+    log(model time / measured time) over all of these points, started from the
+    closed-form estimates (line fit of the latency points; busBw of one channel
+    and the largest busBw at 128 MiB).  Prints one JSON line per measurement,
+    one per protocol with the fit's worst relative error, and one with the
+    fitted models."""
+    from scipy.optimize import least_squares
     factor = {B.arProtoLL: 0.5, B.arProtoLL128: 0.92, B.arProtoSimple: 1.0}
     fits = {}
     big = 32 << 20
@@ -461,6 +481,7 @@ def calibrate(args, B, torch, np):
     outs = [torch.empty_like(x) for x in base]
     for proto in (B.arProtoLL, B.arProtoLL128, B.arProtoSimple):
         name = B.PROTO_NAMES[proto]
+        pts = []   # (n, nch, bytes per rank, measured us)
         xs, ys = [], []
         for n in (2, 4, 8, 16):
             comm = B.Comm(n, 1, proto)
@@ -468,6 +489,7 @@ def calibrate(args, B, torch, np):
             comm.close()
             xs.append(2 * (n - 1))
             ys.append(ms * 1e3)
+            pts.append((n, 1, 4096, ms * 1e3))
             print(json.dumps({"calib": "latency", "proto": name, "nranks": n, "us": round(ms * 1e3, 3)}), flush=True)
         step, b0 = np.polyfit(np.array(xs, float), np.array(ys, float), 1)
         b0, step = max(float(b0), 0.0), max(float(step), 0.0)
@@ -478,12 +500,31 @@ def calibrate(args, B, torch, np):
             comm.set_config(proto, nch)
             ms = time_calls(B, torch, comm, base[:8], outs[:8], big, B.arFloat32, 3, 10)
             S = big * 4
+            pts.append((8, nch, S, ms * 1e3))
             bus[nch] = S / max(ms * 1e3 - lat8, 1e-3) / 1e3 * 2 * 7 / 8
             print(json.dumps({"calib": "bandwidth", "proto": name, "nch": nch, "us": round(ms * 1e3, 2),
                               "busbw_GBs": round(bus[nch], 2)}), flush=True)
+        for lg in range(14, 27, 2):
+            S = 1 << lg
+            nch = _channels_for(S)
+            comm.set_config(proto, nch)
+            ms = time_calls(B, torch, comm, base[:8], outs[:8], S // 4, B.arFloat32, 5, 100 if lg < 24 else 20)
+            pts.append((8, nch, S, ms * 1e3))
+            print(json.dumps({"calib": "mid", "proto": name, "bytes": S, "nch": nch, "us": round(ms * 1e3, 3)}),
+                  flush=True)
         comm.close()
-        fits[name] = {"baseLatUs": round(b0, 3), "stepLatUs": round(step, 4),
-                      "bwPerChGBs": round(bus[1] / factor[proto], 2), "maxBwGBs": round(max(bus.values()), 2)}
+        f = factor[proto]
+        x0 = np.array([b0, step, max(bus[1] / f, 1e-2), max(max(bus.values()), 1e-2)])
+
+        def resid(p):
+            return [np.log(_ring_model_us(p, f, n, c, S) / t) for n, c, S, t in pts]
+
+        sol = least_squares(resid, x0, bounds=([0.0, 0.0, 1e-2, 1e-2], [np.inf] * 4))
+        worst = float(np.max(np.abs(np.expm1(sol.fun))))
+        fits[name] = {"baseLatUs": round(float(sol.x[0]), 3), "stepLatUs": round(float(sol.x[1]), 4),
+                      "bwPerChGBs": round(float(sol.x[2]), 2), "maxBwGBs": round(float(sol.x[3]), 2)}
+        print(json.dumps({"calib": "fit_error", "proto": name, "points": len(pts),
+                          "worst_rel_err": round(worst, 3)}), flush=True)
     print(json.dumps({"calib": "fit", "models": fits}), flush=True)
 
 

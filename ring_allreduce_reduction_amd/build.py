@@ -15,7 +15,7 @@ def build(verbose: bool = False) -> str:
            "-Wall", "-Wno-unused-function",
            # every add is one IEEE add; binary32 subnormals are kept
            "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
-           # packed FP32 instructions stay off
+           # no packed-FP32 instructions: each float add is one lane's own add
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
