@@ -9,6 +9,8 @@ Functions mirror what the pages define (see ring_oracle.c for citations):
   reduce_scatter(), all_gather() -- the two halves of the ring on their own
   elements()   -- the same fold for a list of single elements
   locate()     -- channel / loop / chunk of one element
+  btree(), dtree(), tree_of_channel() -- the pages' binary and double trees
+  tree_allreduce(), tree_elements() -- the double-tree AllReduce fold
   direct_sum_f64(), within_tolerance() -- the float64 direct sum and the
                   error bounds the order-matched result must also meet
 Pinned by tests/test_oracle_*.py (worked example, brute force, order probe,
@@ -45,6 +47,11 @@ def lib():
                                        ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.ar_oracle_reduce_scatter.argtypes = [i, sz, i, i, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.ar_oracle_all_gather.argtypes = [i, sz, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        L.ar_oracle_btree.argtypes = [i, i] + [ctypes.POINTER(i)] * 4
+        L.ar_oracle_dtree.argtypes = [i, i, i] + [ctypes.POINTER(i)] * 3
+        L.ar_oracle_tree_of_channel.argtypes = [i, i]
+        L.ar_oracle_tree_allreduce.argtypes = [i, sz, i, i, i, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        L.ar_oracle_tree_elements.argtypes = [i, sz, i, i, i, ctypes.POINTER(vp), vp, sz, vp]
         for name in ("ar_oracle_f32_to_bf16", "ar_oracle_f32_to_f16",
                      "ar_oracle_f16_to_f32", "ar_oracle_bf16_to_f32"):
             getattr(L, name).argtypes = [vp, vp, sz]
@@ -140,6 +147,56 @@ def locate(nranks, count, dtype, nchannels, chunk_elems, idx):
     if rc != 0:
         raise ValueError("index out of range")
     return ch.value, lp.value, c.value, first.value, ln.value
+
+
+def btree(nranks, rank):
+    """(up, d0, d1, child_type) of rank in the binary tree; -1 for none."""
+    v = [ctypes.c_int() for _ in range(4)]
+    if lib().ar_oracle_btree(nranks, rank, *[ctypes.byref(x) for x in v]) != 0:
+        raise ValueError("bad rank")
+    return tuple(x.value for x in v)
+
+
+def dtree(nranks, rank, tree):
+    """(up, d0, d1) of rank in tree 0 or 1 of the double binary tree."""
+    v = [ctypes.c_int() for _ in range(3)]
+    if lib().ar_oracle_dtree(nranks, rank, tree, *[ctypes.byref(x) for x in v]) != 0:
+        raise ValueError("bad rank or tree")
+    return tuple(x.value for x in v)
+
+
+def tree_of_channel(nchannels, ch):
+    t = lib().ar_oracle_tree_of_channel(nchannels, ch)
+    if t < 0:
+        raise ValueError("bad channel")
+    return t
+
+
+def tree_allreduce(inputs, dtype, op, nchannels):
+    """Double-tree AllReduce; returns the one result every rank receives."""
+    count = _check_inputs(inputs, dtype)
+    n = len(inputs)
+    one = np.empty(count, dtype=NP_STORAGE[dtype])
+    vp = ctypes.c_void_p
+    ins = (vp * n)(*[x.ctypes.data for x in inputs])
+    outs = (vp * n)(*([one.ctypes.data] * n))
+    if lib().ar_oracle_tree_allreduce(n, count, DTYPES[dtype], OPS[op], nchannels, ins, outs) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return one
+
+
+def tree_elements(inputs, dtype, op, nchannels, idx):
+    """The tree fold for the listed element indices only."""
+    count = _check_inputs(inputs, dtype)
+    n = len(inputs)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    res = np.empty(len(idx), dtype=NP_STORAGE[dtype])
+    vp = ctypes.c_void_p
+    ins = (vp * n)(*[x.ctypes.data for x in inputs])
+    if lib().ar_oracle_tree_elements(n, count, DTYPES[dtype], OPS[op], nchannels, ins, idx.ctypes.data,
+                                     len(idx), res.ctypes.data) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return res
 
 
 def _conv(name, x, out_dtype):

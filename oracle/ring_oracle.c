@@ -54,6 +54,29 @@
  *    (it leaves rank b+1 raw and is finished at its owner b), whatever the
  *    channel and chunk split.
  *
+ *  - Tree AllReduce, the pages' second algorithm.  The binary tree over the
+ *    ranks ["NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程", ch.4 "Ring 與
+ *    Tree：把搜尋結果變成演算法拓撲", ncclGetBtree]: a rank's parent and children
+ *    follow from its lowest set bit (see ar_oracle_btree).  The double tree
+ *    [same passage, ncclGetDtree; "NCCL Tree拓扑介绍", "Double Binary Tree"]
+ *    adds a second tree: the first mirrored (rank -> N-1-rank) when N is even,
+ *    shifted by one rank when N is odd; every peer the btree gives for the
+ *    mirrored or shifted rank is mapped back the same way (the pages elide
+ *    this mapping; it is the inverse of the relabelling).  One tree is bound
+ *    to one channel and the first half of the data goes to the first tree,
+ *    the rest to the second; here channel ch of nCh runs on the second tree
+ *    when 2*ch >= nCh (with one channel, only the first tree is used).
+ *    Reduce phase: a node combines what it received from its children with
+ *    its own data and passes the result to its parent; the root ends with the
+ *    full reduction, which the broadcast phase copies down to every rank
+ *    ["NCCL Tree拓扑介绍", "Single Binary Tree"].  The pages do not fix the
+ *    order inside a node; the reading here, like the ring's OP(incoming,
+ *    local), folds the received partials first, in the order the tree names
+ *    the children (d0, then d1), and the node's own value last:
+ *        partial(v) = OP(OP(partial(d0), partial(d1)), x[v])
+ *    (a missing child drops out; a leaf's partial is x[v]).  Chunking and
+ *    pipelining never change this per-element expression.
+ *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math; x86-64 SSE
  * arithmetic, default MXCSR, so no flush-to-zero).
  */
@@ -371,4 +394,140 @@ void ar_oracle_f16_to_f32(const uint16_t* x, float* y, size_t n) {
 }
 void ar_oracle_bf16_to_f32(const uint16_t* x, float* y, size_t n) {
   for (size_t i = 0; i < n; ++i) y[i] = bf16_to_f32(x[i]);
+}
+
+/* ---------------- tree AllReduce ------------------------------------------ */
+
+/* Binary tree over ranks 0..nranks-1 [pages: ch.4, ncclGetBtree].  Let `bit` be the
+ * lowest set bit of rank (for rank 0: the first power of two >= nranks).
+ *  - rank 0 is the root; its only child is bit/2 (none when nranks == 1), and
+ *    the pages name that child d1.
+ *  - any other rank's parent is rank with `bit` cleared and the next bit up
+ *    set; when that is out of range, just rank with `bit` cleared.  It is the
+ *    parent's first child (child_type 0) when rank < parent, else its second.
+ *  - its children are rank - bit/2 (d0) and rank + h (d1) for the largest h
+ *    among bit/2, bit/4, ..., 1 that stays below nranks; a rank whose lowest
+ *    bit is 1 has none. */
+int ar_oracle_btree(int nranks, int rank, int* up, int* d0, int* d1, int* child_type) {
+  if (nranks < 1 || rank < 0 || rank >= nranks) return -1;
+  int bit = 1;
+  while (bit < nranks && (bit & rank) == 0) bit <<= 1;
+  int u = -1, c0 = -1, c1 = -1, t = 0;
+  if (rank == 0) {
+    if (nranks > 1) c1 = bit >> 1;
+  } else {
+    u = (rank ^ bit) | (bit << 1);
+    if (u >= nranks) u = rank ^ bit;
+    t = rank < u ? 0 : 1;
+    int h = bit >> 1;
+    if (h > 0) {
+      c0 = rank - h;
+      while (h > 0 && rank + h >= nranks) h >>= 1;
+      c1 = h > 0 ? rank + h : -1;
+    }
+  }
+  if (up) *up = u;
+  if (d0) *d0 = c0;
+  if (d1) *d1 = c1;
+  if (child_type) *child_type = t;
+  return 0;
+}
+
+/* Tree `tree` (0 or 1) of the double binary tree [pages: ch.4, ncclGetDtree]. */
+int ar_oracle_dtree(int nranks, int rank, int tree, int* up, int* d0, int* d1) {
+  if (nranks < 1 || rank < 0 || rank >= nranks || tree < 0 || tree > 1) return -1;
+  if (tree == 0) return ar_oracle_btree(nranks, rank, up, d0, d1, NULL);
+  int peer[3];
+  if (nranks % 2 == 0) {                 /* mirror: relabel r -> N-1-r */
+    ar_oracle_btree(nranks, nranks - 1 - rank, &peer[0], &peer[1], &peer[2], NULL);
+    for (int i = 0; i < 3; ++i) peer[i] = peer[i] < 0 ? -1 : nranks - 1 - peer[i];
+  } else {                               /* shift: relabel r -> r-1 */
+    ar_oracle_btree(nranks, (rank - 1 + nranks) % nranks, &peer[0], &peer[1], &peer[2], NULL);
+    for (int i = 0; i < 3; ++i) peer[i] = peer[i] < 0 ? -1 : (peer[i] + 1) % nranks;
+  }
+  if (up) *up = peer[0];
+  if (d0) *d0 = peer[1];
+  if (d1) *d1 = peer[2];
+  return 0;
+}
+
+/* The tree a channel is bound to: the first half of the channels (the first
+ * half of the data) on tree 0, the rest on tree 1. */
+int ar_oracle_tree_of_channel(int nchannels, int ch) {
+  if (nchannels < 1 || ch < 0 || ch >= nchannels) return -1;
+  return 2 * ch >= nchannels && nchannels > 1 ? 1 : 0;
+}
+
+enum { TREE_TMP_ELEMS_BYTES = 1 << 13 };
+
+/* partial(v) over elements [p, p+n) of tree `tree`, into acc (n elements). */
+static void tree_partial(int nranks, int tree, int v, int dtype, int op, const void* const* in,
+                         size_t p, size_t n, unsigned char* acc) {
+  size_t esz = elem_size(dtype);
+  int d[2];
+  ar_oracle_dtree(nranks, v, tree, NULL, &d[0], &d[1]);
+  int have = 0;
+  for (int i = 0; i < 2; ++i) {
+    if (d[i] < 0) continue;
+    if (!have) {
+      tree_partial(nranks, tree, d[i], dtype, op, in, p, n, acc);
+      have = 1;
+    } else {
+      unsigned char tmp[TREE_TMP_ELEMS_BYTES];
+      tree_partial(nranks, tree, d[i], dtype, op, in, p, n, tmp);
+      fold(dtype, op, acc, tmp, n);
+    }
+  }
+  const unsigned char* x = (const unsigned char*)in[v] + p * esz;
+  if (have) fold(dtype, op, acc, x, n);
+  else memcpy(acc, x, n * esz);
+}
+
+static int tree_root(int nranks, int tree) {
+  for (int r = 0; r < nranks; ++r) {
+    int u;
+    ar_oracle_dtree(nranks, r, tree, &u, NULL, NULL);
+    if (u < 0) return r;
+  }
+  return -1;
+}
+
+/* Full double-tree AllReduce: out[r][0..count) for every rank r (channel
+ * split as for the ring; the tree follows from the channel). */
+int ar_oracle_tree_allreduce(int nranks, size_t count, int dtype, int op, int nchannels,
+                             const void* const* in, void* const* out) {
+  size_t esz = elem_size(dtype);
+  if (check_args(nranks, dtype, op, nchannels, 16 / (esz ? esz : 1)) != 0) return -1;
+  if (count == 0) return 0;
+  size_t grain = 16 / esz;
+  size_t per_ch = align_up(div_up(count, (size_t)nchannels), grain);
+  size_t tmp_elems = TREE_TMP_ELEMS_BYTES / esz;
+  unsigned char acc[TREE_TMP_ELEMS_BYTES];
+  for (int ch = 0; ch < nchannels; ++ch) {
+    size_t lo = min_sz((size_t)ch * per_ch, count);
+    size_t hi = min_sz((size_t)(ch + 1) * per_ch, count);
+    int tree = ar_oracle_tree_of_channel(nchannels, ch);
+    int root = tree_root(nranks, tree);
+    for (size_t p = lo; p < hi; p += tmp_elems) {
+      size_t n = min_sz(tmp_elems, hi - p);
+      tree_partial(nranks, tree, root, dtype, op, in, p, n, acc);
+      for (int r = 0; r < nranks; ++r) memcpy((unsigned char*)out[r] + p * esz, acc, n * esz);
+    }
+  }
+  return 0;
+}
+
+/* The tree fold for a list of single elements (sampled checks at full size). */
+int ar_oracle_tree_elements(int nranks, size_t count, int dtype, int op, int nchannels,
+                            const void* const* in, const int64_t* idx, size_t nidx, void* results) {
+  size_t esz = elem_size(dtype);
+  if (check_args(nranks, dtype, op, nchannels, 16 / (esz ? esz : 1)) != 0) return -1;
+  size_t per_ch = align_up(div_up(count, (size_t)nchannels), 16 / esz);
+  for (size_t i = 0; i < nidx; ++i) {
+    if (idx[i] < 0 || (size_t)idx[i] >= count) return -1;
+    int tree = ar_oracle_tree_of_channel(nchannels, (int)((size_t)idx[i] / per_ch));
+    tree_partial(nranks, tree, tree_root(nranks, tree), dtype, op, in, (size_t)idx[i], 1,
+                 (unsigned char*)results + i * esz);
+  }
+  return 0;
 }

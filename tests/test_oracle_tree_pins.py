@@ -1,0 +1,177 @@
+"""Pins of the oracle's double-tree AllReduce against things other than
+itself: the tree shapes the pages print, structural invariants of every tree
+the pages' construction yields, brute force and numpy on small inputs, the
+float64 bound, and the order probe worked out by hand.  CPU only."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from ring_allreduce_reduction_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    with open(os.path.join(GOLDEN, "tree_structures.json")) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- printed shapes
+
+def test_btree_walkthrough_rank1(orc):
+    g = _golden()["btree_rank1_of_8"]
+    assert orc.btree(g["nranks"], g["rank"]) == (g["up"], g["d0"], g["d1"], g["child_type"])
+
+
+def test_single_tree_32(orc):
+    g = _golden()["single_tree_32"]
+    n = g["nranks"]
+    peers = [orc.btree(n, r) for r in range(n)]
+    leaves = [r for r in range(n) if peers[r][1] < 0 and peers[r][2] < 0]
+    assert leaves == g["leaves"]
+    assert sorted({peers[r][0] for r in leaves}) == g["leaf_parents"]
+    assert peers[g["root"]][0] == -1
+    assert [c for c in peers[g["root"]][1:3] if c >= 0] == g["root_children"]
+    assert [c for c in peers[16][1:3] if c >= 0] == g["children_of_16"]
+
+
+def test_double_tree_4(orc):
+    g = _golden()["double_tree_4_nodes"]
+    n = g["nranks"]
+    for t, key in ((0, "tree0"), (1, "tree1")):
+        peers = [orc.dtree(n, r, t) for r in range(n)]
+        assert [r for r in range(n) if peers[r][0] < 0] == [g[key]["root"]]
+        assert sorted([[r, peers[r][0]] for r in range(n) if peers[r][0] >= 0]) == sorted(g[key]["edges"])
+
+
+# ---------------------------------------------------------------- structure
+
+def _check_tree(orc, n, t):
+    peers = [orc.dtree(n, r, t) for r in range(n)]
+    roots = [r for r in range(n) if peers[r][0] < 0]
+    assert len(roots) == 1
+    for r in range(n):
+        up, d0, d1 = peers[r]
+        for c in (d0, d1):
+            if c >= 0:
+                assert 0 <= c < n and peers[c][0] == r      # child names us as parent
+        assert d0 < 0 or d0 != d1
+        if up >= 0:
+            assert r in peers[up][1:3]                      # parent names us as child
+        # every rank reaches the root, and not too deep
+        depth, v = 0, r
+        while peers[v][0] >= 0:
+            v = peers[v][0]
+            depth += 1
+            assert depth <= n
+        assert v == roots[0]
+        assert depth <= max(1, int(np.ceil(np.log2(n)))) + 1
+    return peers
+
+
+@pytest.mark.parametrize("n", list(range(1, 34)) + [48, 64, 72, 100, 127, 128])
+def test_trees_are_trees(orc, n):
+    for t in (0, 1):
+        _check_tree(orc, n, t)
+
+
+@pytest.mark.parametrize("n", [2, 4, 6, 8, 10, 16, 24, 32, 72, 128])
+def test_even_roles_swap(orc, n):
+    # the pages: in the second tree the leaves of the first become inner nodes
+    inner = [set(r for r in range(n) if max(orc.dtree(n, r, t)[1:3]) >= 0) for t in (0, 1)]
+    assert inner[0].isdisjoint(inner[1])
+    assert len(inner[0] | inner[1]) == n
+
+
+@pytest.mark.parametrize("n", [3, 5, 7, 9, 15, 33])
+def test_odd_second_tree_is_shift(orc, n):
+    # odd sizes: the second tree is the first relabelled by one rank
+    for r in range(n):
+        up, d0, d1 = orc.dtree(n, (r + 1) % n, 1)
+        b = orc.btree(n, r)[:3]
+        assert (up, d0, d1) == tuple(-1 if x < 0 else (x + 1) % n for x in b)
+
+
+def test_channel_halves(orc):
+    assert orc.tree_of_channel(1, 0) == 0
+    assert [orc.tree_of_channel(2, c) for c in range(2)] == [0, 1]
+    assert [orc.tree_of_channel(4, c) for c in range(4)] == [0, 0, 1, 1]
+    assert [orc.tree_of_channel(3, c) for c in range(3)] == [0, 0, 1]
+
+
+# ---------------------------------------------------------------- order probe
+
+def test_probe_by_hand_n4(orc):
+    # acc*16 + x with x_r = r+1.  Tree 0 of 4: 0 <- 2 <- {1, 3}:
+    #   partial(2) = ((x1*16 + x3)*16 + x2) = ((2*16+4)*16+3) = 579
+    #   partial(0) = 579*16 + x0 = 9265
+    # Tree 1 (mirror): 3 <- 1 <- {d0 = 2, d1 = 0}:
+    #   partial(1) = ((x2*16 + x0)*16 + x1) = ((3*16+1)*16+2) = 786
+    #   partial(3) = 786*16 + x3 = 12580
+    xs = gen.probe_inputs(4, 64)
+    out = orc.tree_allreduce(xs, "uint64", "probe", 2)
+    assert set(out[:32].tolist()) == {9265} and set(out[32:].tolist()) == {12580}
+
+
+def test_probe_two_ranks_matches_ring(orc):
+    # N = 2, tree 0 is 0 <- 1: OP(x1, x0), the ring's order for chunk 0
+    xs = gen.probe_inputs(2, 16)
+    assert set(orc.tree_allreduce(xs, "uint64", "probe", 1).tolist()) == {2 * 16 + 1}
+
+
+# ---------------------------------------------------------------- values
+
+def test_identity_and_empty(orc):
+    x = gen.make_inputs(1, 1000, "float32", seed=3)
+    assert np.array_equal(orc.tree_allreduce(x, "float32", "sum", 2), x[0])
+    assert len(orc.tree_allreduce(gen.make_inputs(5, 0, "float32"), "float32", "sum", 2)) == 0
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 13])
+@pytest.mark.parametrize("nch", [1, 2, 3])
+def test_int_and_order_free_ops_equal_numpy(orc, n, nch):
+    xs = gen.make_inputs(n, 4099, "int32", seed=n + 10 * nch)
+    st = np.stack(xs).astype(np.int64)
+    assert np.array_equal(orc.tree_allreduce(xs, "int32", "sum", nch), st.sum(0).astype(np.int32))
+    assert np.array_equal(orc.tree_allreduce(xs, "int32", "max", nch), st.max(0).astype(np.int32))
+    fs = gen.make_inputs(n, 4099, "float32", seed=n)
+    assert np.array_equal(orc.tree_allreduce(fs, "float32", "min", nch), np.stack(fs).min(0))
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 6])
+def test_float_brute_force_bound(orc, n):
+    # the exact rational sum, within (N-1) * u * sum|x| for float32
+    xs = gen.make_inputs(n, 64, "float32", seed=50 + n)
+    out = orc.tree_allreduce(xs, "float32", "sum", 2)
+    u = Fraction(1, 2 ** 24)
+    for e in range(64):
+        exact = sum(Fraction(float(x[e])) for x in xs)
+        bound = (n - 1) * u * sum(abs(Fraction(float(x[e]))) for x in xs) * (1 + Fraction(1, 10 ** 6))
+        assert abs(Fraction(float(out[e])) - exact) <= bound
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "float16"])
+def test_stated_tolerance(orc, dtype):
+    xs = gen.make_inputs(8, 100003, dtype, seed=4)
+    ok, info = orc.within_tolerance(orc.tree_allreduce(xs, dtype, "sum", 4), xs, dtype)
+    assert ok, info
+
+
+def test_tree_order_differs_from_ring(orc):
+    # a different association: the fp32 sums are not all bit-equal to the ring's
+    xs = gen.make_inputs(8, 20000, "float32", seed=9)
+    assert not np.array_equal(orc.tree_allreduce(xs, "float32", "sum", 2),
+                              orc.allreduce(xs, "float32", "sum", 2, 4096))
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "sum"), ("bfloat16", "sum"), ("int32", "max"),
+                                      ("uint64", "probe")])
+def test_elements_match_full(orc, dtype, op):
+    n, count, nch = 7, 30011, 5
+    xs = gen.probe_inputs(n, count) if op == "probe" else gen.make_inputs(n, count, dtype, seed=1)
+    full = orc.tree_allreduce(xs, dtype, op, nch)
+    idx = np.random.default_rng(0).integers(0, count, 500)
+    assert np.array_equal(orc.tree_elements(xs, dtype, op, nch, idx), full[idx])
