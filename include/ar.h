@@ -55,7 +55,13 @@ typedef enum {
   arProtoSimple = 2  /* bulk FIFO slots with head/tail counters */
 } arProto_t;
 
-typedef enum { arAlgoRing = 0 } arAlgo_t;
+/* Algorithms [B ch.4 "Ring 與 Tree：把搜尋結果變成演算法拓撲"; ch.5 §一]. */
+typedef enum {
+  arAlgoAuto = -1,   /* arTune picks ring or tree per AllReduce */
+  arAlgoRing = 0,    /* ring reduce-scatter + all-gather */
+  arAlgoTree = 1     /* double binary tree: reduce up, broadcast down
+                        (AllReduce only; ReduceScatter / AllGather use the ring) */
+} arAlgo_t;
 
 typedef enum {
   arInt32 = 0,
@@ -85,7 +91,8 @@ typedef enum {
  *            a chunk, hence the summation order).  With arProtoAuto it is the
  *            upper bound arTune may choose.
  *  proto     default protocol, or arProtoAuto.
- *  algo      arAlgoRing.
+ *  algo      arAlgoRing, arAlgoTree or arAlgoAuto (the default algorithm for
+ *            AllReduce; arAlgoAuto lets arTune choose per call).
  * Allocates the FIFOs, counters and flags of every protocol on the device
  * (owned by the comm, freed by arDestroy).  Environment overrides, read once
  * per process: AR_PROTO (LL|LL128|SIMPLE), AR_NCHANNELS, AR_SLICE_BYTES
@@ -99,6 +106,12 @@ arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, ar
 /*
  * arAllReduce -- every rank's recvbuf receives the reduction over all ranks'
  * sendbufs [B ch.1 §1.3, ch.2 §2.3 ring reduce-scatter + all-gather].
+ * With the tree algorithm [B ch.4, ncclGetBtree / ncclGetDtree; "NCCL
+ * Tree拓扑介绍"] channel ch of nCh runs on the second tree of the double
+ * binary tree when nCh > 1 and 2*ch >= nCh, else on the first; each node
+ * folds OP(OP(partial of child d0, partial of child d1), own value) and the
+ * root's result is broadcast back down.  The ring's result depends on the
+ * channel count and chunk size, the tree's on the channel count only.
  *  sendbufs  (host array of nranks device pointers) rank r's input, `count`
  *            contiguous elements.  The array itself is copied at call time.
  *  recvbufs  (host array of nranks device pointers) rank r's output.  In place
@@ -163,6 +176,14 @@ arResult_t arAllGather(arComm_t comm, const void* const* sendbufs, void* const* 
  */
 arResult_t arTune(arComm_t comm, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs);
 
+/*
+ * arTuneAlgo -- arTune that also reports the algorithm.  Over the comm's
+ * algorithm setting: ring only, tree only, or both for arAlgoAuto (arTune
+ * uses the same setting).  algo (host, out; may be NULL).
+ */
+arResult_t arTuneAlgo(arComm_t comm, size_t nBytes, arAlgo_t* algo, arProto_t* proto, int* nChannels,
+                      float* predictedUs);
+
 /* Per-protocol constants of the ring cost model (microseconds, GB/s). */
 typedef struct {
   float baseLatUs;    /* per-call latency */
@@ -198,15 +219,39 @@ typedef enum { arFuncAllReduce = 0, arFuncReduceScatter = 1, arFuncAllGather = 2
 arResult_t arTuneEvalColl(arFunc_t func, int nranks, int maxChannels, size_t nBytes, const arTuneModel_t* models,
                           unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs);
 
-/* Read / replace the tuner constants of a comm (calibration). */
+/*
+ * arTuneEvalAlgo -- the ring and tree cost models as a pure function.
+ *  ringModels, treeModels (host) 3 entries each, indexed by protocol; either
+ *             may be NULL when its bit is clear in algoMask.
+ *  algoMask   bit 0 ring, bit 1 tree.  The tree is only a candidate for
+ *             arFuncAllReduce.
+ * Tree [B ch.5 §四]: busBw = nCh*bwPerCh*0.92, LL x 1/3.8, LL128 x 120/128,
+ * capped at maxBw; times the pages' treeCorrectionFactor[proto][log2i(nBytes
+ * >> 6)] when that index is in [0, 23); lat = baseLat + 2*log2i(N)*stepLat;
+ * t = lat + nBytes/(1000*busBw).  Candidates: ring (Simple, LL128, LL), then
+ * tree (Simple, LL128, LL), each over the same channel counts; ties keep the
+ * earlier candidate.  Errors as arTuneEval.
+ */
+arResult_t arTuneEvalAlgo(arFunc_t func, int nranks, int maxChannels, size_t nBytes,
+                          const arTuneModel_t* ringModels, const arTuneModel_t* treeModels, unsigned algoMask,
+                          unsigned protoMask, arAlgo_t* algo, arProto_t* proto, int* nChannels,
+                          float* predictedUs);
+
+/* Read / replace the tuner constants of a comm (calibration): the ring's
+ * (arTuneGetModel / arTuneSetModel) or either algorithm's. */
 arResult_t arTuneGetModel(arComm_t comm, arProto_t proto, arTuneModel_t* model);
 arResult_t arTuneSetModel(arComm_t comm, arProto_t proto, const arTuneModel_t* model);
+arResult_t arTuneGetAlgoModel(arComm_t comm, arAlgo_t algo, arProto_t proto, arTuneModel_t* model);
+arResult_t arTuneSetAlgoModel(arComm_t comm, arAlgo_t algo, arProto_t proto, const arTuneModel_t* model);
 
 /*
  * arSetConfig -- change the comm's default protocol and channel count, same
  * meaning as in arInit (nChannels must not exceed the value given there).
  */
 arResult_t arSetConfig(arComm_t comm, arProto_t proto, int nChannels);
+
+/* arSetAlgo -- change the comm's AllReduce algorithm (as arInit's algo). */
+arResult_t arSetAlgo(arComm_t comm, arAlgo_t algo);
 
 /* What arAllReduce would run for a message (for tests and benchmarks). */
 typedef struct {
@@ -221,7 +266,11 @@ typedef struct {
   int stepPayload;      /* payload bytes per FIFO slot */
   int nSlots;           /* FIFO depth in slots */
   float predictedUs;    /* cost-model time */
-  double modelBytes;    /* 5(N-1)*S: the stated HBM traffic model */
+  double modelBytes;    /* ring: 5(N-1)*S, the stated HBM traffic model; tree:
+                           2N*S + 4(N-1)*S (every input read and output
+                           written once, every tree edge written and read
+                           once going up and once coming down) */
+  int algo;             /* arAlgo_t actually used */
 } arPlan_t;
 
 /*

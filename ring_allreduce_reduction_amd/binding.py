@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libar.so")
 arSuccess, arHipError, arSystemError, arInternalError = 0, 1, 2, 3
 arInvalidArgument, arInvalidUsage, arRemoteError, arInProgress = 4, 5, 6, 7
 arProtoAuto, arProtoLL, arProtoLL128, arProtoSimple = -1, 0, 1, 2
-arAlgoRing = 0
+arAlgoAuto, arAlgoRing, arAlgoTree = -1, 0, 1
 arInt32, arFloat32, arFloat16, arBfloat16, arUint64 = 0, 1, 2, 3, 4
 arSum, arMax, arMin, arProbe = 0, 1, 2, 3
 arDebugTimeoutUs, arDebugDeadRank, arDebugLanes, arDebugSimpleSlotKiB, arDebugDirect, arDebugSlots = 0, 1, 2, 3, 4, 5
@@ -31,6 +31,8 @@ PROTO_BY_NAME = {"ll": arProtoLL, "ll128": arProtoLL128, "simple": arProtoSimple
 DTYPE_BY_NAME = {"int32": arInt32, "float32": arFloat32, "float16": arFloat16,
                  "bfloat16": arBfloat16, "uint64": arUint64}
 OP_BY_NAME = {"sum": arSum, "max": arMax, "min": arMin, "probe": arProbe}
+ALGO_NAMES = {arAlgoRing: "ring", arAlgoTree: "tree", arAlgoAuto: "auto"}
+ALGO_BY_NAME = {"ring": arAlgoRing, "tree": arAlgoTree, "auto": arAlgoAuto}
 
 
 class arTuneModel_t(ctypes.Structure):
@@ -43,7 +45,7 @@ class arPlan_t(ctypes.Structure):
                 ("lanesPerChannel", ctypes.c_int), ("ranksPerGroup", ctypes.c_int),
                 ("workgroups", ctypes.c_int), ("threadsPerGroup", ctypes.c_int),
                 ("stepBytes", ctypes.c_int), ("stepPayload", ctypes.c_int), ("nSlots", ctypes.c_int),
-                ("predictedUs", ctypes.c_float), ("modelBytes", ctypes.c_double)]
+                ("predictedUs", ctypes.c_float), ("modelBytes", ctypes.c_double), ("algo", ctypes.c_int)]
 
 
 class ArError(RuntimeError):
@@ -77,6 +79,15 @@ def lib():
         L.arTuneGetModel.argtypes = [vp, c_int, ctypes.POINTER(arTuneModel_t)]
         L.arTuneSetModel.argtypes = [vp, c_int, ctypes.POINTER(arTuneModel_t)]
         L.arSetConfig.argtypes = [vp, c_int, c_int]
+        L.arSetAlgo.argtypes = [vp, c_int]
+        L.arTuneAlgo.argtypes = [vp, c_sz, ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                 ctypes.POINTER(c_f)]
+        L.arTuneEvalAlgo.argtypes = [c_int, c_int, c_int, c_sz, ctypes.POINTER(arTuneModel_t),
+                                     ctypes.POINTER(arTuneModel_t), ctypes.c_uint, ctypes.c_uint,
+                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                     ctypes.POINTER(c_f)]
+        L.arTuneGetAlgoModel.argtypes = [vp, c_int, c_int, ctypes.POINTER(arTuneModel_t)]
+        L.arTuneSetAlgoModel.argtypes = [vp, c_int, c_int, ctypes.POINTER(arTuneModel_t)]
         L.arGetPlan.argtypes = [vp, c_sz, c_int, c_int, ctypes.POINTER(arPlan_t)]
         L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arCommAbort.argtypes = [vp]
@@ -86,6 +97,7 @@ def lib():
         L.arGetErrorString.restype = ctypes.c_char_p
         for fn in ("arInit", "arAllReduce", "arReduceScatter", "arAllGather", "arTune", "arTuneEval",
                    "arTuneEvalColl", "arTuneGetModel", "arTuneSetModel", "arSetConfig", "arGetPlan", "arGetPlanColl",
+                   "arSetAlgo", "arTuneAlgo", "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel",
                    "arCommGetAsyncError", "arCommAbort", "arDestroy", "arSetDebug"):
             getattr(L, fn).restype = c_int
         _lib = L
@@ -214,6 +226,39 @@ def arSetConfig(comm, proto, nChannels):
     _check(lib().arSetConfig(comm, int(proto), int(nChannels)), "arSetConfig")
 
 
+def arSetAlgo(comm, algo):
+    _check(lib().arSetAlgo(comm, int(algo)), "arSetAlgo")
+
+
+def arTuneAlgo(comm, nBytes):
+    a, p, ch, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_float()
+    _check(lib().arTuneAlgo(comm, int(nBytes), ctypes.byref(a), ctypes.byref(p), ctypes.byref(ch), ctypes.byref(t)),
+           "arTuneAlgo")
+    return a.value, p.value, ch.value, t.value
+
+
+def arTuneEvalAlgo(func, nranks, maxChannels, nBytes, ringModels, treeModels, algoMask=3, protoMask=7):
+    def arr(models):
+        return None if models is None else (arTuneModel_t * 3)(*[arTuneModel_t(*m) for m in models])
+    a, p, ch, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_float()
+    rc = lib().arTuneEvalAlgo(int(func), int(nranks), int(maxChannels), int(nBytes), arr(ringModels),
+                              arr(treeModels), int(algoMask), int(protoMask), ctypes.byref(a), ctypes.byref(p),
+                              ctypes.byref(ch), ctypes.byref(t))
+    _check(rc, "arTuneEvalAlgo")
+    return a.value, p.value, ch.value, t.value
+
+
+def arTuneGetAlgoModel(comm, algo, proto):
+    m = arTuneModel_t()
+    _check(lib().arTuneGetAlgoModel(comm, int(algo), int(proto), ctypes.byref(m)), "arTuneGetAlgoModel")
+    return (m.baseLatUs, m.stepLatUs, m.bwPerChGBs, m.maxBwGBs)
+
+
+def arTuneSetAlgoModel(comm, algo, proto, model):
+    m = arTuneModel_t(*model)
+    _check(lib().arTuneSetAlgoModel(comm, int(algo), int(proto), ctypes.byref(m)), "arTuneSetAlgoModel")
+
+
 def arGetPlan(comm, count, dtype, aligned128=True):
     p = arPlan_t()
     _check(lib().arGetPlan(comm, int(count), int(dtype), 1 if aligned128 else 0, ctypes.byref(p)), "arGetPlan")
@@ -241,11 +286,13 @@ def arDestroy(comm):
 class Comm:
     """Small convenience wrapper owning one communicator."""
 
-    def __init__(self, nranks, nChannels, proto=arProtoSimple):
+    def __init__(self, nranks, nChannels, proto=arProtoSimple, algo=arAlgoRing):
         if isinstance(proto, str):
             proto = PROTO_BY_NAME[proto.lower()]
+        if isinstance(algo, str):
+            algo = ALGO_BY_NAME[algo.lower()]
         self.nranks = nranks
-        self.handle = arInit(nranks, nChannels, proto)
+        self.handle = arInit(nranks, nChannels, proto, algo)
 
     def allreduce(self, sendbufs, recvbufs, op=arSum, stream=None, count=None, dtype=None):
         if isinstance(op, str):
@@ -272,8 +319,16 @@ class Comm:
             proto = PROTO_BY_NAME[proto.lower()]
         arSetConfig(self.handle, proto, nChannels)
 
+    def set_algo(self, algo):
+        if isinstance(algo, str):
+            algo = ALGO_BY_NAME[algo.lower()]
+        arSetAlgo(self.handle, algo)
+
     def tune(self, nBytes):
         return arTune(self.handle, nBytes)
+
+    def tune_algo(self, nBytes):
+        return arTuneAlgo(self.handle, nBytes)
 
     def async_error(self):
         return arCommGetAsyncError(self.handle)

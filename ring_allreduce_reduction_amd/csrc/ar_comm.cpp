@@ -29,6 +29,7 @@ constexpr uint64_t kCommMagic = 0x4152434f4d4d3031ull;   // "ARCOMM01"
 struct Env {
   int protoMask = 7;      // allowed protocols for tuning
   int forcedProto = -2;   // -2: none
+  int forcedAlgo = -2;    // -2: none; else arAlgoRing / arAlgoTree (AR_ALGO)
   int nChannels = 0;      // 0: not set
   size_t sliceBytes = kDefaultSliceBytes;
   int nSteps = 0;         // 0: per-protocol defaults
@@ -69,6 +70,11 @@ const Env& env() {
         if (mask == 1 || mask == 2 || mask == 4) e.forcedProto = mask == 1 ? 0 : mask == 2 ? 1 : 2;
       }
     }
+    if (const char* p = getenv("AR_ALGO")) {
+      if (!strcasecmp(p, "RING")) e.forcedAlgo = arAlgoRing;
+      else if (!strcasecmp(p, "TREE")) e.forcedAlgo = arAlgoTree;
+      else fprintf(stderr, "[ar] WARN ignoring AR_ALGO=%s (RING or TREE)\n", p);
+    }
     if (const char* p = getenv("AR_NCHANNELS")) e.nChannels = atoi(p);
     if (const char* p = getenv("AR_SLICE_BYTES")) {
       long long v = atoll(p);
@@ -104,6 +110,13 @@ const arTuneModel_t kDefaultModels[3] = {
     /* Simple */ {2.963f, 1.4816f, 187.6f, 277.45f},
 };
 
+// Tree constants (same units; stepLatUs is per tree level each way).
+const arTuneModel_t kDefaultTreeModels[3] = {
+    /* LL     */ {2.965f, 1.9533f, 47.77f, 116.98f},
+    /* LL128  */ {2.701f, 2.6319f, 61.44f, 152.67f},
+    /* Simple */ {2.963f, 1.4816f, 187.6f, 277.45f},
+};
+
 }  // namespace
 
 struct arComm {
@@ -111,6 +124,7 @@ struct arComm {
   int nranks;
   int maxChannels;
   int proto;            // default protocol or arProtoAuto
+  int algo;             // AllReduce algorithm or arAlgoAuto
   int nChannels;        // default channel count
   int device;
   int numCUs;
@@ -123,7 +137,8 @@ struct arComm {
   size_t fifoWorkerBytes[3];
   Control* ctrlHost;
   Control* ctrlDev;
-  arTuneModel_t models[3];
+  arTuneModel_t models[3];       // ring
+  arTuneModel_t treeModels[3];
   int64_t timeoutUs;
   int deadRank;
   int forcedLanes;      // 0: automatic
@@ -179,30 +194,41 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   int proto = e.forcedProto != -2 ? e.forcedProto : c->proto;
   int nch = e.nChannels > 0 ? e.nChannels : c->nChannels;
   if (nch > c->maxChannels) nch = c->maxChannels;
+  // the algorithm: the tree serves AllReduce only [ch.5 §四]
+  int algo = e.forcedAlgo != -2 ? e.forcedAlgo : c->algo;
+  if (func != kCollAllReduce) algo = arAlgoRing;
+  const unsigned algoMask = algo == arAlgoAuto ? 3u : 1u << algo;
   float predicted = 0.0f;
+  arAlgo_t al = algo == arAlgoAuto ? arAlgoRing : (arAlgo_t)algo;
   if (proto == arProtoAuto) {
     unsigned mask = (unsigned)e.protoMask;
     if (!aligned128) mask &= ~(1u << arProtoLL128);
     if (mask == 0) mask = 1u << arProtoSimple;
     arProto_t p;
     int ch;
-    arResult_t r = arTuneEvalColl((arFunc_t)func, c->nranks, c->maxChannels, nBytes, c->models, mask, &p, &ch,
-                                  &predicted);
+    arResult_t r = arTuneEvalAlgo((arFunc_t)func, c->nranks, c->maxChannels, nBytes, c->models, c->treeModels,
+                                  algoMask, mask, &al, &p, &ch, &predicted);
     if (r != arSuccess) return r;
     proto = p;
     nch = ch < 1 ? 1 : ch;
   } else {
     if (proto == arProtoLL128 && !aligned128) return arInvalidUsage;   // LL128 needs 128-byte buffers
-    (void)arTuneEvalColl((arFunc_t)func, c->nranks, nch, nBytes, c->models, 1u << proto, nullptr, nullptr,
-                         &predicted);
+    // a fixed protocol and channel count; with arAlgoAuto the model picks the algorithm
+    (void)arTuneEvalAlgo((arFunc_t)func, c->nranks, nch, nBytes, c->models, c->treeModels, algoMask, 1u << proto,
+                         &al, nullptr, nullptr, &predicted);
   }
+  const bool tree = al == arAlgoTree;
   const int N = c->nranks;
   const uint64_t A = 16 / (uint64_t)esz;
+  // FIFOs per (rank, lane): one for the ring, one per incoming edge for the tree
+  const int edges = tree ? kTreeEdges : 1;
+  plan->algo = al;
   plan->proto = proto;
   plan->nChannels = nch;
   plan->chunkElems = chunkBytesOf(c, proto) / (uint64_t)esz;
   plan->unroll = proto == kSimple ? c->simpleUnroll : proto == kLL ? kLLUnroll : kLL128Unroll;
-  plan->direct = proto == kSimple && c->direct;
+  if (tree && proto == kSimple && plan->unroll > kTreeSimpleUnrollMax) plan->unroll = kTreeSimpleUnrollMax;
+  plan->direct = !tree && proto == kSimple && c->direct;
   plan->slotBytes = slotBytesOf(proto, plan->unroll);
   plan->slotPayload = slotPayloadOf(proto, plan->unroll);
   plan->nSlots = c->nSlots[proto];
@@ -251,8 +277,10 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   const uint64_t per = alignUpU(divUpU(count, (uint64_t)nch), A);
   const uint64_t loop = (uint64_t)N * plan->chunkElems;
   // elements one stage of one member covers: a chunk of the AllReduce loop,
-  // or the loop's range of one rank block for ReduceScatter / AllGather
-  const uint64_t cur = func != kCollAllReduce ? (per < plan->chunkElems ? per : plan->chunkElems)
+  // or the loop's range of one rank block for ReduceScatter / AllGather; the
+  // tree's lanes split the whole channel share
+  const uint64_t cur = tree ? per
+                       : func != kCollAllReduce ? (per < plan->chunkElems ? per : plan->chunkElems)
                        : per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
   const uint64_t chunkBytes = cur * (uint64_t)esz;
   int perCU = 0;
@@ -275,7 +303,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     // round up: a 120-byte-line LL128 slot never divides a power-of-two chunk
     const int byChunk = (int)((chunkBytes + (uint64_t)slotPayload - 1) / (uint64_t)slotPayload);
     if (ln > byChunk) ln = byChunk;
-    if (ln > c->lanesMax / nch) ln = c->lanesMax / nch;
+    if (ln > c->lanesMax / (edges * nch)) ln = c->lanesMax / (edges * nch);
     return ln < 1 ? 1 : ln;
   };
   int lanes = lanesFor(plan->slotPayload);
@@ -293,7 +321,10 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       lanes = ln;
     }
   }
-  if (c->forcedLanes > 0) lanes = c->forcedLanes <= c->lanesMax / nch ? c->forcedLanes : c->lanesMax / nch;
+  if (c->forcedLanes > 0) {
+    const int cap = c->lanesMax / (edges * nch);
+    lanes = c->forcedLanes <= cap ? c->forcedLanes : cap;
+  }
   if (plan->cooperative) {
     while (lanes > 1 && gridFor(lanes) > capacity) --lanes;
     if (gridFor(lanes) > capacity) return arInvalidUsage;
@@ -328,7 +359,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   if (nChannels < 1 || nChannels > AR_MAX_CHANNELS) return arInvalidArgument;
   if (proto != arProtoAuto && proto != arProtoLL && proto != arProtoLL128 && proto != arProtoSimple)
     return arInvalidArgument;
-  if (algo != arAlgoRing) return arInvalidArgument;
+  if (algo != arAlgoRing && algo != arAlgoTree && algo != arAlgoAuto) return arInvalidArgument;
   const Env& e = env();
 
   int dev = 0, ndev = 0;
@@ -344,6 +375,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->nranks = nranks;
   c->maxChannels = nChannels;
   c->proto = proto;
+  c->algo = algo;
   c->nChannels = nChannels;
   c->device = dev;
   c->numCUs = cus;
@@ -355,6 +387,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->simpleUnroll = kSimpleUnrollDefault;
   c->direct = true;
   for (int p = 0; p < 3; ++p) c->models[p] = kDefaultModels[p];
+  for (int p = 0; p < 3; ++p) c->treeModels[p] = kDefaultTreeModels[p];
 
   // FIFOs and counters, one set per protocol (a line of one protocol must
   // never be read as another's: LL flags live inside the data).
@@ -439,25 +472,49 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   return arInvalidArgument;
 }
 
-arResult_t arTuneGetModel(arComm_t c, arProto_t proto, arTuneModel_t* model) {
+arResult_t arTuneGetAlgoModel(arComm_t c, arAlgo_t algo, arProto_t proto, arTuneModel_t* model) {
   if (!commOk(c) || model == nullptr || proto < arProtoLL || proto > arProtoSimple) return arInvalidArgument;
-  *model = c->models[proto];
+  if (algo != arAlgoRing && algo != arAlgoTree) return arInvalidArgument;
+  *model = algo == arAlgoRing ? c->models[proto] : c->treeModels[proto];
   return arSuccess;
 }
 
-arResult_t arTuneSetModel(arComm_t c, arProto_t proto, const arTuneModel_t* model) {
+arResult_t arTuneSetAlgoModel(arComm_t c, arAlgo_t algo, arProto_t proto, const arTuneModel_t* model) {
   if (!commOk(c) || model == nullptr || proto < arProtoLL || proto > arProtoSimple) return arInvalidArgument;
+  if (algo != arAlgoRing && algo != arAlgoTree) return arInvalidArgument;
   if (!(model->bwPerChGBs > 0.0f) || !(model->maxBwGBs > 0.0f) || model->baseLatUs < 0.0f ||
       model->stepLatUs < 0.0f)
     return arInvalidArgument;
-  c->models[proto] = *model;
+  (algo == arAlgoRing ? c->models : c->treeModels)[proto] = *model;
   return arSuccess;
 }
 
-arResult_t arTune(arComm_t c, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs) {
+arResult_t arTuneGetModel(arComm_t c, arProto_t proto, arTuneModel_t* model) {
+  return arTuneGetAlgoModel(c, arAlgoRing, proto, model);
+}
+
+arResult_t arTuneSetModel(arComm_t c, arProto_t proto, const arTuneModel_t* model) {
+  return arTuneSetAlgoModel(c, arAlgoRing, proto, model);
+}
+
+arResult_t arTuneAlgo(arComm_t c, size_t nBytes, arAlgo_t* algo, arProto_t* proto, int* nChannels,
+                      float* predictedUs) {
   if (!commOk(c)) return arInvalidArgument;
-  return arTuneEval(c->nranks, c->maxChannels, nBytes, c->models, (unsigned)env().protoMask, proto, nChannels,
-                    predictedUs);
+  const int a = env().forcedAlgo != -2 ? env().forcedAlgo : c->algo;
+  const unsigned algoMask = a == arAlgoAuto ? 3u : 1u << a;
+  return arTuneEvalAlgo(arFuncAllReduce, c->nranks, c->maxChannels, nBytes, c->models, c->treeModels, algoMask,
+                        (unsigned)env().protoMask, algo, proto, nChannels, predictedUs);
+}
+
+arResult_t arTune(arComm_t c, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs) {
+  return arTuneAlgo(c, nBytes, nullptr, proto, nChannels, predictedUs);
+}
+
+arResult_t arSetAlgo(arComm_t c, arAlgo_t algo) {
+  if (!commOk(c)) return arInvalidArgument;
+  if (algo != arAlgoRing && algo != arAlgoTree && algo != arAlgoAuto) return arInvalidArgument;
+  c->algo = algo;
+  return arSuccess;
 }
 
 arResult_t arGetPlanColl(arComm_t c, arFunc_t func, size_t count, arDataType_t dtype, int aligned128,
@@ -472,11 +529,14 @@ arResult_t arGetPlanColl(arComm_t c, arFunc_t func, size_t count, arDataType_t d
                     : func == arFuncReduceScatter ? 3.0 * N * (N - 1.0) * S : 2.0 * N * (N - 1.0) * S;
   if (c->nranks == 1 || count == 0) {
     out->proto = arProtoSimple;
+    out->algo = arAlgoRing;
     return arSuccess;
   }
   Plan p;
   arResult_t r = makePlan(c, func, count, dtype, op, aligned128 != 0, &p);
   if (r != arSuccess) return r;
+  out->algo = p.algo;
+  if (p.algo == arAlgoTree) out->modelBytes = (2.0 * N + 4.0 * (N - 1.0)) * S;
   out->proto = p.proto;
   out->nChannels = p.nChannels;
   out->chunkElems = p.chunkElems;
@@ -562,6 +622,9 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   const int kop = func == kCollAllGather ? (dtype == arUint64 ? arProbe : arSum) : op;
   arResult_t r = makePlan(c, func, count, dtype, kop, aligned128, &plan);
   if (r != arSuccess) return r;
+  // every (channel, lane, rank, edge) FIFO the kernel indexes must exist
+  const int edges = plan.algo == arAlgoTree ? kTreeEdges : 1;
+  if ((size_t)plan.nChannels * (size_t)plan.lanes * (size_t)edges > (size_t)c->lanesMax) return arInternalError;
 
   KernelArgs a;
   memset(&a, 0, sizeof(a));
@@ -589,9 +652,9 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
 
   if (env().debug >= 1)
     fprintf(stderr,
-            "[ar] INFO op %llu func=%d count=%zu dtype=%d op=%d proto=%d nch=%d chunk=%llu lanes=%d groups=%dx%d "
-            "grid=%d block=%d coop=%d unroll=%d direct=%d pred=%.1fus\n",
-            (unsigned long long)c->opCount, func, count, (int)dtype, (int)op, plan.proto, plan.nChannels,
+            "[ar] INFO op %llu func=%d count=%zu dtype=%d op=%d algo=%d proto=%d nch=%d chunk=%llu lanes=%d "
+            "groups=%dx%d grid=%d block=%d coop=%d unroll=%d direct=%d pred=%.1fus\n",
+            (unsigned long long)c->opCount, func, count, (int)dtype, (int)op, plan.algo, plan.proto, plan.nChannels,
             (unsigned long long)plan.chunkElems, plan.lanes, plan.nGroups, plan.groupSize, plan.grid, plan.block,
             (int)plan.cooperative, plan.unroll, (int)plan.direct, plan.predictedUs);
   hipError_t he = launchRing(plan, dtype, kop, a, st);

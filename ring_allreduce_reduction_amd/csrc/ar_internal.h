@@ -27,6 +27,9 @@ constexpr int kMaxSlots = 8;              // FIFO depth provisioned per worker
 //           seven 16-byte payload pieces, 8 payload bytes and an 8-byte flag.
 constexpr int kSimpleUnrollMax = 8;       // Simple slot = unroll KiB (1, 2, 4 or 8)
 constexpr int kSimpleUnrollDefault = 8;
+constexpr int kTreeSimpleUnrollMax = 2;   // the tree's Simple slot is at most 2 KiB (three slot
+                                          // arrays live per lane: 4 KiB would spill)
+constexpr int kTreeEdges = 3;             // a tree node's FIFOs: from d0, from d1, from its parent
 constexpr int kLLUnroll = 2;
 constexpr int kLL128Unroll = 2;
 
@@ -96,6 +99,7 @@ struct KernelArgs {
 
 // Everything arAllReduce decides for one call.
 struct Plan {
+  int algo;                   // arAlgoRing or arAlgoTree
   int proto;
   int nChannels;
   uint64_t chunkElems;

@@ -652,6 +652,361 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   if (PROTO != kSimple && m.lane == 0) stRelaxed64(&m.succ->tail, m.sendStep, true);
 }
 
+// ------------------------------------------------------------- tree AllReduce
+//
+// The pages' second algorithm ["NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程",
+// ch.4 "Ring 與 Tree：把搜尋結果變成演算法拓撲", ncclGetBtree / ncclGetDtree;
+// "NCCL Tree拓扑介绍", single and double binary trees].  Each virtual rank is
+// a tree node and, as in the ring, one wavefront per (rank, channel, lane).
+// Reduce: a node folds the partials its children send (d0 first, then d1)
+// and then its own value, OP(OP(p_d0, p_d1), x), and sends the result to its
+// parent; the root's result is the answer, which it writes and sends back
+// down; every other node receives it from its parent, writes it and forwards
+// it to its children.  The first half of the channels runs on the first
+// tree, the second half on the second (mirrored for an even rank count,
+// shifted by one rank for an odd one).
+//
+// FIFOs: a node owns three, one per incoming edge (from d0, from d1, from its
+// parent), at worker index (lane * N + rank) * 3 + edge, with the same slot
+// and counter layout as the ring's.  A member works through its lane share
+// in batches of nSlots columns: the reduce pass of a batch, then its
+// broadcast pass.  A member starts batch b+1 only after its broadcast pass of
+// batch b, which needs data its parent sent after consuming the member's
+// batch-b columns and, in turn, after its children consumed its batch-b
+// broadcast; so no edge ever holds more than one batch and neither pass can
+// wait on the other: the tree cannot deadlock for any size.
+
+// Binary tree over ranks [pages: ncclGetBtree]: with `bit` the lowest set
+// bit of r (for the root r = 0, the first power of two >= n), the parent
+// clears `bit` and sets the next bit up (or only clears it, if that is out
+// of range); the children are r - bit/2 and r + h for the largest power of
+// two h <= bit/2 with r + h < n.  The root's only child is bit/2, named d1.
+__device__ __forceinline__ void btreeNode(int n, int r, int& up, int& d0, int& d1) {
+  up = d0 = d1 = -1;
+  if (r == 0) {
+    if (n > 1) d1 = (int)((1u << (32 - __builtin_clz((u32)n - 1u))) >> 1);   // bit_ceil(n) / 2
+    return;
+  }
+  const int bit = r & -r;
+  up = (r & ~bit) | (bit << 1);
+  if (up >= n) up = r & ~bit;
+  const int h = bit >> 1;
+  if (h == 0) return;
+  d0 = r - h;
+  const int room = n - 1 - r;   // r + h' < n  <=>  h' <= room
+  if (room >= 1) d1 = r + (int)(1u << (31 - __builtin_clz((u32)(h < room ? h : room))));   // bit_floor
+}
+
+// Tree t of the double tree [pages: ncclGetDtree]: tree 1 relabels rank x as
+// n-1-x (even n) or x-1 (odd n), takes the binary tree of the relabelled
+// rank and maps every peer back.
+__device__ __forceinline__ void dtreeNode(int n, int r, int t, int& up, int& d0, int& d1) {
+  if (t == 0) {
+    btreeNode(n, r, up, d0, d1);
+    return;
+  }
+  const bool mirror = (n & 1) == 0;
+  btreeNode(n, mirror ? n - 1 - r : (r == 0 ? n - 1 : r - 1), up, d0, d1);
+  auto back = [&](int x) { return x < 0 ? -1 : mirror ? n - 1 - x : (x + 1 == n ? 0 : x + 1); };
+  up = back(up);
+  d0 = back(d0);
+  d1 = back(d1);
+}
+
+// One end of one FIFO.
+struct Edge {
+  char* fifo;   // slot 0 (the FIFO is owned by the receiving end)
+  Conn* conn;   // its counters
+  u64 step;     // next step on this FIFO
+  u32 slot;     // step % nSlots
+  bool agent;   // the other end is in another workgroup
+};
+
+__device__ __forceinline__ Edge openEdge(const KernelArgs& a, size_t worker, bool agent, bool recvEnd) {
+  Edge e;
+  e.fifo = a.fifo + worker * a.fifoWorkerBytes;
+  e.conn = a.conn + worker;
+  // counters carry over from earlier calls (tail == head at call boundaries)
+  e.step = ldCounter(recvEnd ? &e.conn->head : &e.conn->tail, true);
+  e.slot = (u32)(e.step % (u64)a.nSlots);
+  e.agent = agent;
+  return e;
+}
+
+template <int PROTO, int U>
+struct Pieces {   // this lane's pieces of one slot (as in the ring's step)
+  int payOff[U], payBytes[U], wireOff[U];
+  __device__ __forceinline__ explicit Pieces(int lane) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (PROTO == kSimple) {
+        payOff[u] = (u * kWave + lane) * 16; payBytes[u] = 16; wireOff[u] = payOff[u];
+      } else if (PROTO == kLL) {
+        payOff[u] = (u * kWave + lane) * 8; payBytes[u] = 8; wireOff[u] = (u * kWave + lane) * 16;
+      } else {
+        const int line = lane >> 3, j = lane & 7;
+        payOff[u] = u * kLL128UnitPayload + (j < 7 ? (line * 7 + j) * 16 : 896 + line * 8);
+        payBytes[u] = j < 7 ? 16 : 8;
+        wireOff[u] = u * kLL128UnitBytes + lane * 16;
+      }
+    }
+  }
+};
+
+template <int PROTO, int U>
+__device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, const Pieces<PROTO, U>& pc, int lane,
+                                         long valid, v4u (&in)[U]) {
+  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  const char* slot = e.fifo + (size_t)e.slot * SLOT;
+  if (PROTO == kSimple) {
+    if (!waitGeq(a, &e.conn->tail, e.step + 1, e.agent)) return false;
+    fenceAcquire(e.agent);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      in[u] = pc.payOff[u] < valid ? *(const v4u*)(slot + pc.wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+  } else if (PROTO == kLL) {
+    const u32 flag = (u32)(e.step + 1);
+    bool done[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { done[u] = pc.payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
+    Waiter w;
+    while (true) {
+      bool all = true;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!done[u]) {
+          const u64* line = (const u64*)(slot + pc.wireOff[u]);
+          const u64 w0 = ldRelaxed64(line, e.agent);
+          const u64 w1 = ldRelaxed64(line + 1, e.agent);
+          if ((u32)(w0 >> 32) == flag && (u32)(w1 >> 32) == flag) {
+            in[u].x = (u32)w0; in[u].y = (u32)w1; done[u] = true;
+          } else {
+            all = false;
+          }
+        }
+      }
+      if (__all(all)) break;
+      if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+    }
+  } else {
+    const u64 flag = e.step + 1;
+    const bool flagLane = (lane & 7) == 7;
+    bool done[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
+    Waiter w;
+    while (true) {
+      bool all = true;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!done[u]) {
+          if (ldRelaxed64((const u64*)(slot + pc.wireOff[u] + 8), e.agent) == flag) done[u] = true;
+          else all = false;
+        }
+      }
+      if (__all(all)) break;
+      if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+    }
+    fenceAcquire(e.agent);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      in[u] = v4u{0u, 0u, 0u, 0u};
+      if (u * kLL128UnitPayload < valid) {
+        if (pc.payBytes[u] == 16) {
+          in[u] = *(const v4u*)(slot + pc.wireOff[u]);
+        } else {
+          const v2u t = *(const v2u*)(slot + pc.wireOff[u]);
+          in[u].x = t.x; in[u].y = t.y;
+        }
+      }
+    }
+  }
+  return true;
+}
+
+__device__ __forceinline__ void edgeFinishRecv(const KernelArgs& a, Edge& e, int lane) {
+  ++e.step;
+  if (lane == 0) stCounterRelease(&e.conn->head, e.step, e.agent);
+  if (++e.slot == (u32)a.nSlots) e.slot = 0;
+}
+
+template <int PROTO, int U>
+__device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pieces<PROTO, U>& pc, int lane,
+                                         long valid, const v4u (&v)[U]) {
+  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  // slot step % nSlots is free once the receiver consumed step - nSlots
+  const u64 need = e.step + 1 > (u64)a.nSlots ? e.step + 1 - (u64)a.nSlots : 0;
+  if (!waitGeq(a, &e.conn->head, need, e.agent)) return false;
+  fenceAcquire(e.agent);
+  char* slot = e.fifo + (size_t)e.slot * SLOT;
+  if (PROTO == kSimple) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (pc.payOff[u] < valid) *(v4u*)(slot + pc.wireOff[u]) = v[u];
+    fenceRelease(e.agent);
+    if (lane == 0) stRelaxed64(&e.conn->tail, e.step + 1, e.agent);
+  } else if (PROTO == kLL) {
+    const u64 flag = (u64)(u32)(e.step + 1) << 32;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (pc.payOff[u] < valid) {
+        u64* line = (u64*)(slot + pc.wireOff[u]);
+        stRelaxed64(line, flag | v[u].x, e.agent);
+        stRelaxed64(line + 1, flag | v[u].y, e.agent);
+      }
+    }
+  } else {
+    const bool flagLane = (lane & 7) == 7;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u * kLL128UnitPayload < valid) {
+        if (pc.payBytes[u] == 16) {
+          *(v4u*)(slot + pc.wireOff[u]) = v[u];
+        } else {
+          v2u t; t.x = v[u].x; t.y = v[u].y;
+          *(v2u*)(slot + pc.wireOff[u]) = t;
+        }
+      }
+    }
+    fenceRelease(e.agent);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (flagLane && u * kLL128UnitPayload < valid)
+        stRelaxed64((u64*)(slot + pc.wireOff[u] + 8), e.step + 1, e.agent);
+  }
+  ++e.step;
+  if (++e.slot == (u32)a.nSlots) e.slot = 0;
+  return true;
+}
+
+template <int PROTO, int DT, int OP, int U>
+__global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
+  constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
+  constexpr u64 A = 16 / ESZ;
+  constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
+                        : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int N = a.nranks;
+  const int lanesTotal = a.nChannels * a.lanes;
+
+  int L, g;   // (lane id, group), as in the ring kernel
+  if (a.nGroups == 1) {
+    L = blockIdx.x;
+    g = 0;
+  } else {
+    const int x = blockIdx.x % 8;
+    g = (blockIdx.x / 8) % a.nGroups;
+    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
+  }
+  if (L >= lanesTotal) return;
+  const int r = g * a.groupSize + wave;
+  if (r >= N || r == a.deadRank) return;
+  const int ch = L / a.lanes;
+  const int k = L % a.lanes;
+
+  const u64 count = a.count;
+  const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
+  const u64 lo = umin((u64)ch * per, count);
+  const u64 len = umin(lo + per, count) - lo;
+  const u64 sub = alignUp(divUp(len, (u64)a.lanes), A);
+  const u64 sb = umin((u64)k * sub, len);
+  const u64 bytes = (umin(sb + sub, len) - sb) * ESZ;
+  if (bytes == 0) return;
+
+  // this member's place in its channel's tree
+  const int t = a.nChannels > 1 && 2 * ch >= a.nChannels ? 1 : 0;
+  int up, d[2];
+  dtreeNode(N, r, t, up, d[0], d[1]);
+  const bool leaf = d[0] < 0 && d[1] < 0;
+  auto worker = [&](int node, int edge) { return ((size_t)L * N + node) * 3 + edge; };
+  auto cross = [&](int node) { return node / a.groupSize != g; };
+  Edge fromChild[2], toChild[2], fromParent, toParent;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (d[i] >= 0) {
+      fromChild[i] = openEdge(a, worker(r, i), cross(d[i]), true);
+      toChild[i] = openEdge(a, worker(d[i], 2), cross(d[i]), false);
+    }
+  }
+  if (up >= 0) {
+    int pu, p0, p1;
+    dtreeNode(N, up, t, pu, p0, p1);
+    fromParent = openEdge(a, worker(r, 2), cross(up), true);
+    toParent = openEdge(a, worker(up, r == p0 ? 0 : 1), cross(up), false);
+  }
+
+  const char* in = (const char*)a.send[r] + (lo + sb) * ESZ;
+  char* out = (char*)a.recv[r] + (lo + sb) * ESZ;
+  const bool aligned = a.aligned16 != 0;
+  const Pieces<PROTO, U> pc(lane);
+  const u64 nCols = divUp(bytes, (u64)PAYLOAD);
+  const u64 batch = (u64)a.nSlots;
+  v4u acc[U], x[U];
+  for (u64 jb = 0; jb < nCols; jb += batch) {
+    const u64 je = umin(jb + batch, nCols);
+    // reduce pass: children's partials, then my own value; up (or, at the
+    // root, straight into the broadcast)
+    for (u64 j = jb; j < je; ++j) {
+      const u64 b = j * (u64)PAYLOAD;
+      const long valid = (long)umin((u64)PAYLOAD, bytes - b);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        x[u] = loadUser<ESZ, true>(in + b + pc.payOff[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
+      if (leaf) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = x[u];
+      } else {
+        bool have = false;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (d[i] < 0) continue;
+          v4u got[U];
+          if (!edgeRecv<PROTO, U>(a, fromChild[i], pc, lane, valid, got)) return;
+          edgeFinishRecv(a, fromChild[i], lane);
+#pragma unroll
+          for (int u = 0; u < U; ++u) acc[u] = have ? combine<DT, OP>(acc[u], got[u]) : got[u];
+          have = true;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = combine<DT, OP>(acc[u], x[u]);
+      }
+      if (up >= 0) {
+        if (!edgeSend<PROTO, U>(a, toParent, pc, lane, valid, acc)) return;
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (d[i] >= 0 && !edgeSend<PROTO, U>(a, toChild[i], pc, lane, valid, acc)) return;
+      }
+    }
+    if (up < 0) continue;
+    // broadcast pass: the result from the parent, to my output and children
+    for (u64 j = jb; j < je; ++j) {
+      const u64 b = j * (u64)PAYLOAD;
+      const long valid = (long)umin((u64)PAYLOAD, bytes - b);
+      if (!edgeRecv<PROTO, U>(a, fromParent, pc, lane, valid, acc)) return;
+      edgeFinishRecv(a, fromParent, lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (d[i] >= 0 && !edgeSend<PROTO, U>(a, toChild[i], pc, lane, valid, acc)) return;
+    }
+  }
+  // LL / LL128 never touch the tail counter per slot: publish it once so the
+  // next call starts both ends of each FIFO at the same step.
+  if (PROTO != kSimple && lane == 0) {
+    if (up >= 0) stRelaxed64(&toParent.conn->tail, toParent.step, true);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (d[i] >= 0) stRelaxed64(&toChild[i].conn->tail, toChild[i].step, true);
+  }
+}
+
 // ------------------------------------------------------------- dispatch
 
 typedef void (*KernelFn)(const KernelArgs);
@@ -707,7 +1062,48 @@ KernelFn pickProto(const Plan& plan, int dtype, int op) {
   return nullptr;
 }
 
+template <int PROTO, int U>
+KernelFn pickTree(int dtype, int op) {
+  switch (dtype) {
+    case arInt32:
+      if (op == arSum) return treeAllReduceKernel<PROTO, arInt32, arSum, U>;
+      if (op == arMax) return treeAllReduceKernel<PROTO, arInt32, arMax, U>;
+      if (op == arMin) return treeAllReduceKernel<PROTO, arInt32, arMin, U>;
+      break;
+    case arFloat32:
+      if (op == arSum) return treeAllReduceKernel<PROTO, arFloat32, arSum, U>;
+      if (op == arMax) return treeAllReduceKernel<PROTO, arFloat32, arMax, U>;
+      if (op == arMin) return treeAllReduceKernel<PROTO, arFloat32, arMin, U>;
+      break;
+    case arFloat16:
+      if (op == arSum) return treeAllReduceKernel<PROTO, arFloat16, arSum, U>;
+      if (op == arMax) return treeAllReduceKernel<PROTO, arFloat16, arMax, U>;
+      if (op == arMin) return treeAllReduceKernel<PROTO, arFloat16, arMin, U>;
+      break;
+    case arBfloat16:
+      if (op == arSum) return treeAllReduceKernel<PROTO, arBfloat16, arSum, U>;
+      if (op == arMax) return treeAllReduceKernel<PROTO, arBfloat16, arMax, U>;
+      if (op == arMin) return treeAllReduceKernel<PROTO, arBfloat16, arMin, U>;
+      break;
+    case arUint64:
+      if (op == arProbe) return treeAllReduceKernel<PROTO, arUint64, arProbe, U>;
+      break;
+  }
+  return nullptr;
+}
+
+KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
+  if (plan.proto == kLL) return pickTree<kLL, kLLUnroll>(dtype, op);
+  if (plan.proto == kLL128) return pickTree<kLL128, kLL128Unroll>(dtype, op);
+  if (plan.proto == kSimple) {
+    if (plan.unroll == 1) return pickTree<kSimple, 1>(dtype, op);
+    if (plan.unroll == 2) return pickTree<kSimple, 2>(dtype, op);
+  }
+  return nullptr;
+}
+
 KernelFn pickKernel(const Plan& plan, int coll, int dtype, int op) {
+  if (plan.algo == arAlgoTree) return coll == kCollAllReduce ? pickTreeProto(plan, dtype, op) : nullptr;
   if (coll == kCollAllReduce) return pickProto<kCollAllReduce>(plan, dtype, op);
   if (coll == kCollReduceScatter) return pickProto<kCollReduceScatter>(plan, dtype, op);
   if (coll == kCollAllGather) return pickProto<kCollAllGather>(plan, dtype, op);

@@ -73,17 +73,29 @@ def run_ring(comm, sends, recvs, dtype, op, stream=None):
     assert err == B.arSuccess, B.arGetErrorString(err)
 
 
-def parity_case(n, count, dtype, op, proto, nch, seed=0, inplace=False, offset=0, comm=None, inputs=None):
-    """Run one AllReduce on the GPU and compare every rank's output bit for bit
-    with the oracle run on the same inputs, channels and chunk size."""
+def expected(xs, dtype, op, plan):
+    """The oracle's result for what the plan ran: the ring fold on its own
+    channels and chunk size, or the double-tree fold on its channels."""
     import oracle
-    note("parity n=%d count=%d dtype=%s op=%s proto=%s nch=%d seed=%d inplace=%s offset=%d"
-         % (n, count, dtype, op, proto, nch, seed, inplace, offset))
+    nch_used = max(1, plan["nChannels"])                      # one rank: no channels run
+    if plan.get("algo", B.arAlgoRing) == B.arAlgoTree:
+        return oracle.tree_allreduce(xs, dtype, op, nch_used)
+    chunk = plan["chunkElems"] or 16 // gen.ELEM_SIZE[dtype]
+    return oracle.allreduce(xs, dtype, op, nch_used, chunk)
+
+
+def parity_case(n, count, dtype, op, proto, nch, seed=0, inplace=False, offset=0, comm=None, inputs=None,
+                algo="ring"):
+    """Run one AllReduce on the GPU and compare every rank's output bit for bit
+    with the oracle run on the same inputs and the same plan (algorithm,
+    channels and chunk size)."""
+    note("parity n=%d count=%d dtype=%s op=%s proto=%s nch=%d seed=%d inplace=%s offset=%d algo=%s"
+         % (n, count, dtype, op, proto, nch, seed, inplace, offset, algo if comm is None else "comm's"))
     xs = inputs if inputs is not None else (
         gen.probe_inputs(n, count) if op == "probe" else gen.make_inputs(n, count, dtype, seed=seed))
     own = comm is None
     if own:
-        comm = B.Comm(n, nch, proto)
+        comm = B.Comm(n, nch, proto, algo)
     else:
         comm.set_config(proto, nch)
     try:
@@ -91,12 +103,12 @@ def parity_case(n, count, dtype, op, proto, nch, seed=0, inplace=False, offset=0
         sends = [to_device(x, dtype, offset_elems=offset) for x in xs]
         recvs = sends if inplace else [empty_like_sentinel(count, dtype, offset_elems=offset) for _ in range(n)]
         run_ring(comm, sends, recvs, dtype, op)
-        nch_used = max(1, plan["nChannels"])                      # one rank: no channels run
-        chunk = plan["chunkElems"] or 16 // gen.ELEM_SIZE[dtype]
-        want = oracle.allreduce(xs, dtype, op, nch_used, chunk)
+        want = expected(xs, dtype, op, plan)
         for r in range(n):
             assert_bits_equal(to_host_raw(recvs[r], dtype), want, dtype,
-                              "rank %d (%s, n=%d, count=%d, %s)" % (r, dtype, n, count, B.PROTO_NAMES[plan["proto"]]))
+                              "rank %d (%s, n=%d, count=%d, %s %s)" % (r, dtype, n, count,
+                                                                       B.ALGO_NAMES[plan["algo"]],
+                                                                       B.PROTO_NAMES[plan["proto"]]))
         return plan, want, xs
     finally:
         if own:

@@ -28,7 +28,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = set(_declared())
     for fn in ("arInit", "arAllReduce", "arTune", "arCommGetAsyncError", "arCommAbort", "arDestroy",
-               "arGetErrorString", "arTuneEval", "arGetPlan", "arSetConfig"):
+               "arGetErrorString", "arTuneEval", "arGetPlan", "arSetConfig", "arSetAlgo", "arTuneAlgo",
+               "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel"):
         assert fn in names
 
 
@@ -50,7 +51,7 @@ def test_init_rejects_bad_arguments_before_hip(B):
     h = ctypes.c_void_p()
     assert L.arInit(None, 4, 1, B.arProtoSimple, B.arAlgoRing) == B.arInvalidArgument
     for n, ch, p, a in [(0, 1, 2, 0), (129, 1, 2, 0), (4, 0, 2, 0), (4, 65, 2, 0), (4, 1, 7, 0), (4, 1, -2, 0),
-                        (4, 1, 2, 1)]:
+                        (4, 1, 2, 2), (4, 1, 2, -2)]:
         assert L.arInit(ctypes.byref(h), n, ch, p, a) == B.arInvalidArgument, (n, ch, p, a)
         assert h.value is None
 
@@ -72,6 +73,7 @@ def test_calls_on_a_null_comm(B):
     assert L.arTune(None, 1024, None, None, None) == B.arInvalidArgument
     assert L.arCommAbort(None) == B.arInvalidArgument
     assert L.arSetConfig(None, 2, 1) == B.arInvalidArgument
+    assert L.arSetAlgo(None, 1) == B.arInvalidArgument
     assert L.arDestroy(None) == B.arSuccess
     e = ctypes.c_int()
     assert L.arCommGetAsyncError(None, ctypes.byref(e)) == B.arInvalidArgument
@@ -164,3 +166,79 @@ def test_halves_use_n_minus_1_steps(B, func, nbytes):
     assert B.arTuneEvalColl(0, n, 64, nbytes, MODELS) == B.arTuneEval(n, 64, nbytes, MODELS)
     with pytest.raises(B.ArError):
         B.arTuneEvalColl(3, n, 64, nbytes, MODELS)
+
+
+# ---------------------------------------------------------------- tree model
+
+# the pages' treeCorrectionFactor rows (LL, LL128, Simple), column i = 64 B * 2^i
+CORR = [
+    [1.0, 1.0, 1.0, 1.0, .9, .8, .7, .7, .7, .7, .6, .5, .4, .4, .5, .6, .7, .8, .9, 1.0, 1.0, 1.0, 1.0, 1.0],
+    [1.0, 1.0, 1.0, 1.0, 1.0, .9, .8, .8, .8, .7, .6, .6, .6, .6, .6, .6, .8, .9, .9, .9, .9, 1.0, 1.0, 1.0],
+    [.9, .9, .9, .9, .9, .9, .9, .8, .7, .6, .6, .5, .5, .5, .5, .6, .7, .8, .7, .7, .8, .9, .9, .9],
+]
+
+
+def _tree_t(model, proto, n, nch, nbytes):
+    """The pages' tree model written out [ch.5 §四]: busBw = bw*nch*0.92, LL
+    x1/3.8, LL128 x120/128, capped; x correction[proto][log2(nBytes>>6)];
+    lat = base + 2*floor(log2 N)*step."""
+    base, step, bw, cap = model
+    bus = bw * nch * 0.92 * {0: 1 / 3.8, 1: 120 / 128, 2: 1.0}[proto]
+    bus = min(bus, cap)
+    q = nbytes >> 6
+    if q > 0 and q.bit_length() - 1 < 23:
+        bus *= CORR[proto][q.bit_length() - 1]
+    return base + 2 * (n.bit_length() - 1) * step + nbytes / (1000.0 * bus)
+
+
+TREE = [(3.0, 0.4, 12.0, 90.0), (4.0, 0.5, 12.0, 150.0), (6.0, 0.6, 12.0, 250.0)]
+
+
+@pytest.mark.parametrize("nbytes", [8, 64, 4096, 1 << 16, 3 << 18, 1 << 20, 1 << 24, 1 << 28])
+@pytest.mark.parametrize("n", [2, 8, 24, 72])
+def test_tree_argmin_matches_closed_form(B, n, nbytes):
+    a, p, ch, t = B.arTuneEvalAlgo(0, n, 64, nbytes, MODELS, TREE)
+    best = None
+    for algo, models, tf in ((0, MODELS, _t), (1, TREE, _tree_t)):
+        for proto in (2, 1, 0):
+            bp = None
+            c = 1
+            while c <= 64:
+                if c > 1 and nbytes // c < 32768:
+                    break
+                tt = tf(models[proto], proto, n, c, nbytes)
+                if bp is None or tt <= bp[3] * (1 + 1e-6):
+                    bp = (algo, proto, c, tt)
+                c *= 2
+            if best is None or bp[3] < best[3] * (1 - 1e-6):
+                best = bp
+    assert (a, p, ch) == best[:3]
+    assert t == pytest.approx(best[3], rel=1e-5)
+
+
+def test_tree_only_for_allreduce_and_masks(B):
+    fast_tree = [(0.0, 0.0, 1e6, 1e6)] * 3
+    slow_ring = [(100.0, 10.0, 1.0, 1.0)] * 3
+    assert B.arTuneEvalAlgo(0, 8, 64, 4096, slow_ring, fast_tree)[0] == B.arAlgoTree
+    for func in (1, 2):   # ReduceScatter / AllGather: ring only
+        assert B.arTuneEvalAlgo(func, 8, 64, 4096, slow_ring, fast_tree)[0] == B.arAlgoRing
+    assert B.arTuneEvalAlgo(0, 8, 64, 4096, slow_ring, fast_tree, algoMask=1)[0] == B.arAlgoRing
+    assert B.arTuneEvalAlgo(0, 8, 64, 4096, None, fast_tree, algoMask=2)[0] == B.arAlgoTree
+    with pytest.raises(B.ArError):
+        B.arTuneEvalAlgo(0, 8, 64, 4096, None, fast_tree, algoMask=3)
+    with pytest.raises(B.ArError):
+        B.arTuneEvalAlgo(0, 8, 64, 4096, slow_ring, fast_tree, algoMask=0)
+    # an exact tie keeps the ring: at N = 8 both take 12 us of latency and
+    # 8 GB/s (ring: cap 14 * 8/14; tree: cap 8, no correction past 512 MiB)
+    ring = [(5.0, 0.5, 1e9, 14.0)] * 3
+    tree = [(6.0, 1.0, 1e9, 8.0)] * 3
+    r = B.arTuneEvalAlgo(0, 8, 64, 1 << 30, ring, tree, protoMask=4)
+    assert r[0] == B.arAlgoRing and r[3] == pytest.approx(12 + (1 << 30) / 8000.0)
+    assert B.arTuneEvalAlgo(0, 8, 64, 1 << 30, ring, tree, algoMask=2, protoMask=4)[3] == r[3]
+    assert B.arTuneEvalAlgo(0, 1, 64, 1 << 20, ring, tree) == (B.arAlgoRing, B.arProtoSimple, 0, 0.0)
+
+
+def test_ring_eval_unchanged_by_tree(B):
+    for nbytes in (64, 1 << 20, 1 << 28):
+        a, p, ch, t = B.arTuneEvalAlgo(0, 8, 64, nbytes, MODELS, None, algoMask=1)
+        assert (p, ch) == B.arTuneEval(8, 64, nbytes, MODELS)[:2] and a == B.arAlgoRing
