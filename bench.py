@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--count", type=int, default=64 << 20, help="elements per rank")
     ap.add_argument("--dtype", default="float32")
     ap.add_argument("--proto", default="auto")
+    ap.add_argument("--algo", default="ring", choices=["ring", "tree", "auto"],
+                    help="AllReduce algorithm (the headline metric is the ring's)")
     ap.add_argument("--nchannels", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,7 +114,7 @@ def main():
         recvs.append(torch.empty_like(sends[-1]))
     torch.cuda.synchronize()
 
-    comm = B.Comm(N, args.nchannels, args.proto)
+    comm = B.Comm(N, args.nchannels, args.proto, args.algo)
     if args.lanes:
         B.arSetDebug(comm.handle, B.arDebugLanes, args.lanes)
     if args.explore:
@@ -147,7 +149,7 @@ def main():
     t = ms / 1e3
     algbw = S / t / 1e9
     busbw = algbw * 2 * (N - 1) / N
-    model_bytes = 5.0 * (N - 1) * S
+    model_bytes = plan["modelBytes"]   # ring: 5(N-1)S; tree: (2N + 4(N-1))S
     achieved = model_bytes / t / 1e9
     log("per-launch ms: mean %.4f min %.4f max %.4f; wall per step %.4f ms"
         % (ms, min(launch_ms), max(launch_ms), wall / args.steps * 1e3))
@@ -165,6 +167,8 @@ def main():
         try:
             tj = json.load(open(args.traffic_json))
             key = workload_key(B.PROTO_NAMES[plan["proto"]], N, count, dtype)
+            if plan["algo"] == B.arAlgoTree:
+                key = "Tree" + key
             if key in tj and tj[key]["kernel_src_sha256"] == kernel_src_sha():
                 traffic = tj[key]["bytes_per_launch"]
             elif key in tj:
@@ -172,11 +176,13 @@ def main():
         except Exception as e:  # a stale or partial file must not break the bench
             log("traffic file unreadable: %s" % e)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(xs, dtype, plan, N, S)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(xs, dtype, plan, N, S, B)
     comm.close()
 
+    algo = B.ALGO_NAMES[plan["algo"]]
     out = {
-        "metric": "emulated ring AllReduce busbw GB/s + % HBM peak, 8 ranks x 256 MiB fp32",
+        "metric": ("emulated ring AllReduce busbw GB/s + % HBM peak, 8 ranks x 256 MiB fp32" if algo == "ring"
+                   else "emulated %s AllReduce busbw GB/s + %% HBM peak" % algo),
         "value": round(busbw, 3),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -188,8 +194,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"float32": "f32", "bfloat16": "bf16", "float16": "f16", "int32": "i32"}[dtype],
         "data": "synthetic",
-        "config": {"workload": "ring AllReduce Sum, %d virtual ranks x %d MiB %s per rank on one GPU"
-                               % (N, S >> 20, dtype),
+        "config": {"workload": "%s AllReduce Sum, %d virtual ranks x %d MiB %s per rank on one GPU"
+                               % (algo, N, S >> 20, dtype), "algo": algo,
                    "nranks": N, "count_per_rank": count, "bytes_per_rank": S,
                    "proto": B.PROTO_NAMES[plan["proto"]], "nChannels": plan["nChannels"],
                    "chunkElems": plan["chunkElems"], "lanesPerChannel": plan["lanesPerChannel"],
@@ -273,14 +279,17 @@ def summarize_profiles(args):
         print("\nwrote %s[%s]" % (path, args.profile_label))
 
 
-def cpu_baseline(xs, dtype, plan, N, S):
+def cpu_baseline(xs, dtype, plan, N, S, B):
     """The oracle, as it stands, on the headline inputs (single thread),
     repeated until about 10 s of CPU work; reported in the metric's unit."""
     import oracle
     reps, total = 0, 0.0
     while total < 10.0 and reps < 50:
         t0 = time.perf_counter()
-        oracle.allreduce(xs, dtype, "sum", plan["nChannels"], plan["chunkElems"])
+        if plan["algo"] == B.arAlgoTree:
+            oracle.tree_allreduce(xs, dtype, "sum", plan["nChannels"])
+        else:
+            oracle.allreduce(xs, dtype, "sum", plan["nChannels"], plan["chunkElems"])
         total += time.perf_counter() - t0
         reps += 1
     t = total / reps
@@ -450,6 +459,24 @@ def _ring_model_us(params, factor, n, nch, S):
     return base + 2 * (n - 1) * step + S / (1000.0 * bus * n / (2 * (n - 1)))
 
 
+# the pages' tree efficiency by message size (rows LL, LL128, Simple), as arTune applies it
+_TREE_CORR = [
+    [1.0, 1.0, 1.0, 1.0, .9, .8, .7, .7, .7, .7, .6, .5, .4, .4, .5, .6, .7, .8, .9, 1.0, 1.0, 1.0, 1.0, 1.0],
+    [1.0, 1.0, 1.0, 1.0, 1.0, .9, .8, .8, .8, .7, .6, .6, .6, .6, .6, .6, .8, .9, .9, .9, .9, 1.0, 1.0, 1.0],
+    [.9, .9, .9, .9, .9, .9, .9, .8, .7, .6, .6, .5, .5, .5, .5, .6, .7, .8, .7, .7, .8, .9, .9, .9],
+]
+
+
+def _tree_model_us(params, proto, n, nch, S):
+    """The tree cost model arTune evaluates (same form, any constants)."""
+    base, step, bw, cap = params
+    bus = min(bw * nch * 0.92 * {0: 1 / 3.8, 1: 120 / 128, 2: 1.0}[proto], cap)
+    q = S >> 6
+    if q > 0 and q.bit_length() - 1 < 23:
+        bus *= _TREE_CORR[proto][q.bit_length() - 1]
+    return base + 2 * (n.bit_length() - 1) * step + S / (1000.0 * bus)
+
+
 def _channels_for(S, maxch=64):
     """Channels where the model is capped: the most whose share is >= 32 KiB."""
     c = 1
@@ -459,105 +486,131 @@ def _channels_for(S, maxch=64):
 
 
 def calibrate(args, B, torch, np):
-    """Fit the ring cost model's constants per protocol on this GPU.
+    """Fit the cost model's constants per protocol on this GPU, for the ring
+    (default) or, with --algo tree, for the tree.
 
     Measured, fp32 Sum:
-      latency:   4 KiB per rank, 1 channel, N = 2, 4, 8, 16;
+      latency:   4 KiB per rank, 1 channel, N = 2, 4, 8, 16 (one workgroup
+                 holds a channel's members, as at the sweep's 8 ranks; past 16
+                 the cross-workgroup edges add a cost neither model has);
       bandwidth: 128 MiB per rank, N = 8, 1..64 channels;
       mid sizes: 16 KiB .. 64 MiB per rank, N = 8, at the channel count the
                  32 KiB-per-channel rule allows (where arTune lands once the
                  bandwidth is capped).
     The four constants (base, step, bwPerCh, cap) are the least-squares fit of
-    log(model time / measured time) over all of these points, started from the
-    closed-form estimates (line fit of the latency points; busBw of one channel
-    and the largest busBw at 128 MiB).  Prints one JSON line per measurement,
-    one per protocol with the fit's worst relative error, and one with the
-    fitted models."""
+    log(model time / measured time) over all of these points, the best of
+    several starts (the closed-form estimates first).  Prints one JSON line per measurement, one per
+    protocol with the fit's worst relative error, and one with the fitted
+    models."""
     from scipy.optimize import least_squares
+    tree = args.algo == "tree"
     factor = {B.arProtoLL: 0.5, B.arProtoLL128: 0.92, B.arProtoSimple: 1.0}
+    ranks = (2, 4, 8, 16)
     fits = {}
     big = 32 << 20
     base = [torch.rand(big, device="cuda") for _ in range(16)]
+    small = [torch.rand(1024, device="cuda") for _ in range(max(ranks))]
+    small_out = [torch.empty_like(x) for x in small]
     outs = [torch.empty_like(x) for x in base]
     for proto in (B.arProtoLL, B.arProtoLL128, B.arProtoSimple):
         name = B.PROTO_NAMES[proto]
         pts = []   # (n, nch, bytes per rank, measured us)
         xs, ys = [], []
-        for n in (2, 4, 8, 16):
-            comm = B.Comm(n, 1, proto)
-            ms = time_calls(B, torch, comm, base[:n], outs[:n], 1024, B.arFloat32, 20, 200)
+        for n in ranks:
+            comm = B.Comm(n, 1, proto, args.algo)
+            ms = time_calls(B, torch, comm, small[:n], small_out[:n], 1024, B.arFloat32, 20, 200)
             comm.close()
-            xs.append(2 * (n - 1))
+            xs.append(2 * (n.bit_length() - 1) if tree else 2 * (n - 1))
             ys.append(ms * 1e3)
             pts.append((n, 1, 4096, ms * 1e3))
-            print(json.dumps({"calib": "latency", "proto": name, "nranks": n, "us": round(ms * 1e3, 3)}), flush=True)
+            print(json.dumps({"calib": "latency", "algo": args.algo, "proto": name, "nranks": n,
+                              "us": round(ms * 1e3, 3)}), flush=True)
         step, b0 = np.polyfit(np.array(xs, float), np.array(ys, float), 1)
         b0, step = max(float(b0), 0.0), max(float(step), 0.0)
-        lat8 = b0 + 14 * step
-        comm = B.Comm(8, 64, proto)
+        lat8 = b0 + (6 if tree else 14) * step
+        comm = B.Comm(8, 64, proto, args.algo)
         bus = {}
         for nch in (1, 2, 4, 8, 16, 32, 64):
             comm.set_config(proto, nch)
             ms = time_calls(B, torch, comm, base[:8], outs[:8], big, B.arFloat32, 3, 10)
             S = big * 4
             pts.append((8, nch, S, ms * 1e3))
-            bus[nch] = S / max(ms * 1e3 - lat8, 1e-3) / 1e3 * 2 * 7 / 8
-            print(json.dumps({"calib": "bandwidth", "proto": name, "nch": nch, "us": round(ms * 1e3, 2),
-                              "busbw_GBs": round(bus[nch], 2)}), flush=True)
+            bus[nch] = S / max(ms * 1e3 - lat8, 1e-3) / 1e3 * (1.0 if tree else 2 * 7 / 8)
+            print(json.dumps({"calib": "bandwidth", "algo": args.algo, "proto": name, "nch": nch,
+                              "us": round(ms * 1e3, 2), "busbw_GBs": round(bus[nch], 2)}), flush=True)
         for lg in range(14, 27, 2):
             S = 1 << lg
             nch = _channels_for(S)
             comm.set_config(proto, nch)
             ms = time_calls(B, torch, comm, base[:8], outs[:8], S // 4, B.arFloat32, 5, 100 if lg < 24 else 20)
             pts.append((8, nch, S, ms * 1e3))
-            print(json.dumps({"calib": "mid", "proto": name, "bytes": S, "nch": nch, "us": round(ms * 1e3, 3)}),
-                  flush=True)
+            print(json.dumps({"calib": "mid", "algo": args.algo, "proto": name, "bytes": S, "nch": nch,
+                              "us": round(ms * 1e3, 3)}), flush=True)
         comm.close()
-        f = factor[proto]
-        x0 = np.array([b0, step, max(bus[1] / f, 1e-2), max(max(bus.values()), 1e-2)])
+        # the protocol's bandwidth factor in the model, to start bwPerCh from one channel's busBw
+        f = 0.92 * {0: 1 / 3.8, 1: 120 / 128, 2: 1.0}[proto] if tree else factor[proto]
+
+        def model(p, n, c, S):
+            return _tree_model_us(p, proto, n, c, S) if tree else _ring_model_us(p, factor[proto], n, c, S)
 
         def resid(p):
-            return [np.log(_ring_model_us(p, f, n, c, S) / t) for n, c, S, t in pts]
+            return [np.log(model(p, n, c, S) / t) for n, c, S, t in pts]
 
-        sol = least_squares(resid, x0, bounds=([0.0, 0.0, 1e-2, 1e-2], [np.inf] * 4))
+        starts = [[b0, step, max(bus[1] / f, 1e-2), max(max(bus.values()), 1e-2)],
+                  [3.0, 2.0, 50.0, 100.0], [1.0, 1.0, 100.0, 100.0], [5.0, 3.0, 20.0, 60.0]]
+        sol = None
+        for x0 in starts:
+            cand = least_squares(resid, np.array(x0, float), bounds=([0.0, 0.0, 1e-2, 1e-2], [np.inf] * 4))
+            if sol is None or cand.cost < sol.cost:
+                sol = cand
         worst = float(np.max(np.abs(np.expm1(sol.fun))))
         fits[name] = {"baseLatUs": round(float(sol.x[0]), 3), "stepLatUs": round(float(sol.x[1]), 4),
                       "bwPerChGBs": round(float(sol.x[2]), 2), "maxBwGBs": round(float(sol.x[3]), 2)}
-        print(json.dumps({"calib": "fit_error", "proto": name, "points": len(pts),
+        print(json.dumps({"calib": "fit_error", "algo": args.algo, "proto": name, "points": len(pts),
                           "worst_rel_err": round(worst, 3)}), flush=True)
-    print(json.dumps({"calib": "fit", "models": fits}), flush=True)
+    print(json.dumps({"calib": "fit", "algo": args.algo, "models": fits}), flush=True)
+
+
+SWEEP_CANDIDATES = [("ring", "ll"), ("ring", "ll128"), ("ring", "simple"),
+                    ("tree", "ll"), ("tree", "ll128"), ("tree", "simple")]
 
 
 def sweep(args, B, gen, torch, np):
-    """8 ranks fp32 Sum, per-rank sizes 8 B .. 2^max bytes.  Each protocol runs
-    at the channel count arTune's model gives that protocol for the size (the
-    pages fix channels by size: at least 32 KiB per channel), then arTune's own
-    choice; one JSON line per size with the regret t(chosen)/min_p t(p) - 1."""
+    """N ranks (default 8) fp32 Sum, per-rank sizes 8 B .. 2^max bytes.  Each
+    algorithm x protocol runs at the channel count arTune's model gives that
+    pair for the size (the pages fix channels by size: at least 32 KiB per
+    channel), then arTune's own choice over both algorithms; one JSON line per
+    size with the regret t(chosen)/min t - 1."""
     N = args.nranks
     maxc = (1 << args.sweep_max_log2) // 4
     xs = gen.make_inputs(N, maxc, "float32", seed=args.seed)
     sends = [torch.from_numpy(x).cuda() for x in xs]
     recvs = [torch.empty_like(s) for s in sends]
-    comm = B.Comm(N, args.nchannels, "auto")
-    models = [B.arTuneGetModel(comm.handle, p) for p in (0, 1, 2)]
+    comm = B.Comm(N, args.nchannels, "auto", "auto")
+    ring = [B.arTuneGetAlgoModel(comm.handle, B.arAlgoRing, p) for p in (0, 1, 2)]
+    tree = [B.arTuneGetAlgoModel(comm.handle, B.arAlgoTree, p) for p in (0, 1, 2)]
     for lg in range(3, args.sweep_max_log2 + 1):
         count = (1 << lg) // 4
         S = count * 4
         iters = 200 if S < (64 << 20) else 20
         res = {}
-        for proto in ("ll", "ll128", "simple", "auto"):
-            pcode = B.PROTO_BY_NAME[proto]
-            if proto == "auto":
+        for algo, proto in SWEEP_CANDIDATES + [("auto", "auto")]:
+            key = "auto" if algo == "auto" else (proto if algo == "ring" else "tree_" + proto)
+            comm.set_algo(algo)
+            if algo == "auto":
                 comm.set_config("auto", args.nchannels)
             else:
-                _, nch, _ = B.arTuneEval(N, args.nchannels, S, models, protoMask=1 << pcode)
+                pcode = B.PROTO_BY_NAME[proto]
+                _, _, nch, _ = B.arTuneEvalAlgo(0, N, args.nchannels, S, ring, tree,
+                                                algoMask=1 << B.ALGO_BY_NAME[algo], protoMask=1 << pcode)
                 comm.set_config(proto, max(1, nch))
             plan = comm.plan(count, "float32")
             ms = time_calls(B, torch, comm, sends, recvs, count, B.arFloat32, 5, iters)
-            res[proto] = {"us": round(ms * 1e3, 3), "proto": B.PROTO_NAMES[plan["proto"]],
-                          "nch": plan["nChannels"], "pred_us": round(plan["predictedUs"], 2)}
-        best = min(res[p]["us"] for p in ("ll", "ll128", "simple"))
-        out = {"bytes": S, "regret": round(res["auto"]["us"] / best - 1, 4),
+            res[key] = {"us": round(ms * 1e3, 3), "algo": B.ALGO_NAMES[plan["algo"]],
+                        "proto": B.PROTO_NAMES[plan["proto"]], "nch": plan["nChannels"],
+                        "pred_us": round(plan["predictedUs"], 2)}
+        best = min(v["us"] for k, v in res.items() if k != "auto")
+        out = {"bytes": S, "nranks": N, "regret": round(res["auto"]["us"] / best - 1, 4),
                "busbw_auto_GBs": round(S / (res["auto"]["us"] / 1e6) / 1e9 * 2 * (N - 1) / N, 3)}
         out.update(res)
         print(json.dumps(out), flush=True)

@@ -110,11 +110,16 @@ const arTuneModel_t kDefaultModels[3] = {
     /* Simple */ {2.963f, 1.4816f, 187.6f, 277.45f},
 };
 
-// Tree constants (same units; stepLatUs is per tree level each way).
+// Tree constants (same units; stepLatUs is per tree level each way), fitted
+// the same way (`bench.py --calibrate --algo tree`) with the pages' tree
+// model and its size correction: worst point off by 52% (LL, where the
+// correction's mid-size dip does not match this GPU), 18% (LL128), 27%
+// (Simple).  On the 8-rank sweep arTune then picks the tree (Simple) up to
+// 512 KiB and the ring (Simple) from 1 MiB, the fastest candidate at every size.
 const arTuneModel_t kDefaultTreeModels[3] = {
-    /* LL     */ {2.965f, 1.9533f, 47.77f, 116.98f},
-    /* LL128  */ {2.701f, 2.6319f, 61.44f, 152.67f},
-    /* Simple */ {2.963f, 1.4816f, 187.6f, 277.45f},
+    /* LL     */ {4.088f, 1.5169f, 188.3f, 48.71f},
+    /* LL128  */ {1.828f, 2.4511f, 67.92f, 58.78f},
+    /* Simple */ {4.774f, 0.8563f, 102.91f, 100.21f},
 };
 
 }  // namespace
