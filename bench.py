@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarize rocprofv3 CSV output directories into markdown + profiles/traffic.json")
     ap.add_argument("--profile-label", default="", help="workload key for --summarize-profiles")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="time T AllReduces of --count elements issued one by one and as one group")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="time a plain elementwise copy (torch.neg) of this many bytes instead")
     return ap.parse_args()
@@ -93,6 +95,8 @@ def main():
         return sweep(args, B, gen, torch, np)
     if args.calibrate:
         return calibrate(args, B, torch, np)
+    if args.batch:
+        return bench_batch(args, B, gen, torch, np)
 
     if args.coll != "allreduce":
         return bench_halves(args, B, gen, torch, np)
@@ -388,6 +392,62 @@ def bench_halves(args, B, gen, torch, np):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": cpu}), flush=True)
+
+
+def bench_batch(args, B, gen, torch, np):
+    """T AllReduces of `count` fp32 elements per rank on N ranks, each with its
+    own buffers: issued one by one, then between arGroupStart / arGroupEnd
+    (aggregated into batched launches).  Reports microseconds per AllReduce
+    for both (events around the whole set, mean over --steps repetitions)."""
+    N, T, count = args.nranks, args.batch, args.count
+    xs = gen.make_inputs(N, count, "float32", seed=args.seed)
+    sends = [[torch.from_numpy(x).cuda() for x in xs] for _ in range(T)]
+    recvs = [[torch.empty_like(t) for t in row] for row in sends]
+    comm = B.Comm(N, args.nchannels, args.proto, args.algo)
+    stream = torch.cuda.Stream()
+    # marshal once: the timed loop calls the C ABI directly, so the host side
+    # costs about what a C caller's would
+    import ctypes
+    L = B.lib()
+    sp = [B._ptrs(row) for row in sends]
+    rp = [B._ptrs(row) for row in recvs]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for mode in ("single", "group"):
+        def one_set():
+            if mode == "group":
+                L.arGroupStart()
+            for i in range(T):
+                rc = L.arAllReduce(comm.handle, sp[i], rp[i], count, B.arFloat32, B.arSum, sh)
+                if rc != B.arSuccess:
+                    raise SystemExit("arAllReduce: " + B.arGetErrorString(rc))
+            if mode == "group" and L.arGroupEnd() != B.arSuccess:
+                raise SystemExit("arGroupEnd failed")
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                one_set()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(args.steps):
+                one_set()
+            b.record(stream)
+            torch.cuda.synchronize()
+        if comm.async_error() != B.arSuccess:
+            raise SystemExit("batch run failed")
+        res[mode] = a.elapsed_time(b) * 1e3 / (args.steps * T)
+    plan = comm.group_plan(0)
+    single = comm.plan(count, "float32")
+    comm.close()
+    S = count * 4
+    print(json.dumps({"batch": T, "nranks": N, "bytes_per_rank": S, "us_per_allreduce_single": round(res["single"], 3),
+                      "us_per_allreduce_group": round(res["group"], 3),
+                      "speedup": round(res["single"] / res["group"], 3),
+                      "single_plan": {"algo": B.ALGO_NAMES[single["algo"]], "proto": B.PROTO_NAMES[single["proto"]],
+                                      "nch": single["nChannels"]},
+                      "group_plan": {"algo": B.ALGO_NAMES[plan["algo"]], "proto": B.PROTO_NAMES[plan["proto"]],
+                                     "nch": plan["nChannels"], "tasksInLaunch": plan["tasksInLaunch"]}}),
+          flush=True)
 
 
 def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):

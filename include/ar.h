@@ -271,6 +271,9 @@ typedef struct {
                            written once, every tree edge written and read
                            once going up and once coming down) */
   int algo;             /* arAlgo_t actually used */
+  int groupLaunch;      /* arGetGroupPlan: index of the launch (in launch order)
+                           that carried this call; -1 for a copy or a single call */
+  int tasksInLaunch;    /* collectives sharing that launch (1 unless batched) */
 } arPlan_t;
 
 /*
@@ -317,6 +320,50 @@ typedef enum {
   arDebugSlots = 5,      /* FIFO depth in slots for every protocol, 2..8 */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
+
+/*
+ * arGroupStart / arGroupEnd -- collectives called between them are queued
+ * and launched together at the outermost arGroupEnd [B ch.7 §一, group
+ * semantics: a per-thread nesting depth, the first error kept and reported
+ * at the end, inner ends launch nothing; ch.6 §四, ncclPrepareTasks].
+ * Inside a group each call validates its arguments and returns at once
+ * (enqueuing nothing); its buffers must stay untouched until the group's
+ * work completes, and collectives of one group must not share buffers.  At
+ * the end, per communicator in the order it joined: the calls are
+ * aggregated by arGroupAggregate; AllReduces of one (op, dtype) aggregated
+ * together run in ONE kernel launch on the algorithm / protocol / channels
+ * arTune picks for the largest of them, side by side on separate wavefronts
+ * and FIFOs (as many at once as the FIFOs provisioned allow, the rest in
+ * turn).  Each call's result is exactly that of a single call with that
+ * plan, reported by arGetGroupPlan.  ReduceScatter / AllGather calls run in
+ * launches of their own.  All calls on one comm in a group must use the
+ * same stream (else arInvalidUsage).  arGroupEnd returns the first error of
+ * the group (and launches nothing then), arInvalidUsage without a matching
+ * arGroupStart.  arDestroy refuses a comm with queued calls.  The group
+ * state is per host thread.
+ */
+arResult_t arGroupStart(void);
+arResult_t arGroupEnd(void);
+
+/*
+ * arGroupAggregate -- the aggregation rule as a pure function (no device).
+ *  keys      (host, nTasks) bucket of each task, e.g. (func, op, dtype);
+ *  bytes     (host, nTasks) traffic of each task;
+ *  isolate   (host, nTasks, may be NULL) 1 = never aggregate this task;
+ *  order     (host, out, nTasks) task indices in launch order;
+ *  launchOf  (host, out, nTasks) launch index of each task;
+ *  nLaunches (host, out).
+ * Tasks are sorted by bytes, largest first (ties keep call order), bucketed
+ * by key (buckets in ascending key order), and inside a bucket a run starts
+ * at its first task and takes each following task while 4 * bytes > the
+ * first task's bytes [B ch.6 §四: aggregate tasks within 4x; aggIsolate].
+ */
+arResult_t arGroupAggregate(int nTasks, const int* keys, const size_t* bytes, const int* isolate, int* order,
+                            int* launchOf, int* nLaunches);
+
+/* arGetGroupPlan -- the plan the index-th call (call order, count > 0) of
+ * the comm's last launched group ran with; arInvalidArgument out of range. */
+arResult_t arGetGroupPlan(arComm_t comm, int index, arPlan_t* plan);
 
 const char* arGetErrorString(arResult_t result);
 

@@ -45,7 +45,8 @@ class arPlan_t(ctypes.Structure):
                 ("lanesPerChannel", ctypes.c_int), ("ranksPerGroup", ctypes.c_int),
                 ("workgroups", ctypes.c_int), ("threadsPerGroup", ctypes.c_int),
                 ("stepBytes", ctypes.c_int), ("stepPayload", ctypes.c_int), ("nSlots", ctypes.c_int),
-                ("predictedUs", ctypes.c_float), ("modelBytes", ctypes.c_double), ("algo", ctypes.c_int)]
+                ("predictedUs", ctypes.c_float), ("modelBytes", ctypes.c_double), ("algo", ctypes.c_int),
+                ("groupLaunch", ctypes.c_int), ("tasksInLaunch", ctypes.c_int)]
 
 
 class ArError(RuntimeError):
@@ -88,6 +89,11 @@ def lib():
                                      ctypes.POINTER(c_f)]
         L.arTuneGetAlgoModel.argtypes = [vp, c_int, c_int, ctypes.POINTER(arTuneModel_t)]
         L.arTuneSetAlgoModel.argtypes = [vp, c_int, c_int, ctypes.POINTER(arTuneModel_t)]
+        L.arGroupStart.argtypes = []
+        L.arGroupEnd.argtypes = []
+        L.arGroupAggregate.argtypes = [c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_sz), ctypes.POINTER(c_int),
+                                       ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+        L.arGetGroupPlan.argtypes = [vp, c_int, ctypes.POINTER(arPlan_t)]
         L.arGetPlan.argtypes = [vp, c_sz, c_int, c_int, ctypes.POINTER(arPlan_t)]
         L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arCommAbort.argtypes = [vp]
@@ -98,6 +104,7 @@ def lib():
         for fn in ("arInit", "arAllReduce", "arReduceScatter", "arAllGather", "arTune", "arTuneEval",
                    "arTuneEvalColl", "arTuneGetModel", "arTuneSetModel", "arSetConfig", "arGetPlan", "arGetPlanColl",
                    "arSetAlgo", "arTuneAlgo", "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel",
+                   "arGroupStart", "arGroupEnd", "arGroupAggregate", "arGetGroupPlan",
                    "arCommGetAsyncError", "arCommAbort", "arDestroy", "arSetDebug"):
             getattr(L, fn).restype = c_int
         _lib = L
@@ -265,6 +272,48 @@ def arGetPlan(comm, count, dtype, aligned128=True):
     return {f: getattr(p, f) for f, _ in arPlan_t._fields_}
 
 
+def arGroupStart():
+    _check(lib().arGroupStart(), "arGroupStart")
+
+
+def arGroupEnd():
+    _check(lib().arGroupEnd(), "arGroupEnd")
+
+
+def arGroupAggregate(keys, nbytes, isolate=None):
+    """(order, launchOf, nLaunches) of the aggregation rule."""
+    n = len(keys)
+    k = (ctypes.c_int * n)(*keys)
+    b = (ctypes.c_size_t * n)(*nbytes)
+    iso = None if isolate is None else (ctypes.c_int * n)(*isolate)
+    order, launch_of, nl = (ctypes.c_int * n)(), (ctypes.c_int * n)(), ctypes.c_int()
+    _check(lib().arGroupAggregate(n, k, b, iso, order, launch_of, ctypes.byref(nl)), "arGroupAggregate")
+    return list(order), list(launch_of), nl.value
+
+
+def arGetGroupPlan(comm, index):
+    p = arPlan_t()
+    _check(lib().arGetGroupPlan(comm, int(index), ctypes.byref(p)), "arGetGroupPlan")
+    return {f: getattr(p, f) for f, _ in arPlan_t._fields_}
+
+
+class Group:
+    """with Group(): ... -- arGroupStart on entry, arGroupEnd on exit."""
+
+    def __enter__(self):
+        arGroupStart()
+        return self
+
+    def __exit__(self, exc_type, *exc):
+        if exc_type is None:
+            arGroupEnd()
+        else:   # close the group without masking the original error
+            try:
+                arGroupEnd()
+            except ArError:
+                pass
+
+
 def arCommGetAsyncError(comm):
     e = ctypes.c_int()
     _check(lib().arCommGetAsyncError(comm, ctypes.byref(e)), "arCommGetAsyncError")
@@ -329,6 +378,9 @@ class Comm:
 
     def tune_algo(self, nBytes):
         return arTuneAlgo(self.handle, nBytes)
+
+    def group_plan(self, index):
+        return arGetGroupPlan(self.handle, index)
 
     def async_error(self):
         return arCommGetAsyncError(self.handle)

@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
-SOURCES = ["ar_kernels.hip", "ar_comm.cpp", "ar_tune.cpp"]
+SOURCES = ["ar_kernels.hip", "ar_comm.cpp", "ar_tune.cpp", "ar_group.cpp"]
 ARCH = os.environ.get("AR_OFFLOAD_ARCH", "gfx950")
 
 

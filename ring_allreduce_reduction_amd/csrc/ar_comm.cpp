@@ -14,6 +14,7 @@
 
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "ar_internal.h"
 
@@ -122,6 +123,21 @@ const arTuneModel_t kDefaultTreeModels[3] = {
     /* Simple */ {4.774f, 0.8563f, 102.91f, 100.21f},
 };
 
+constexpr int kStagingBuffers = 4;
+
+// One collective queued inside arGroupStart / arGroupEnd.
+struct GroupTask {
+  int func;
+  size_t count;
+  int dtype;
+  int op;
+  hipStream_t stream;
+  bool aligned16;
+  bool aligned128;
+  std::vector<const void*> send;
+  std::vector<void*> recv;
+};
+
 }  // namespace
 
 struct arComm {
@@ -153,6 +169,18 @@ struct arComm {
   bool launched;
   bool aborted;
   uint64_t opCount;
+  // group calls [ch.7 §一]: collectives queued until the outermost arGroupEnd
+  std::vector<GroupTask> pending;
+  bool inGroup;
+  std::vector<arPlan_t> groupPlans;   // the last launched group's plans, call order
+  uint64_t* taskTable;                // device rows {count, send[N], recv[N]}
+  // pinned host copy sources, used in turn so that the host need not wait
+  // for the previous group's copy before writing the next table
+  uint64_t* taskStaging[kStagingBuffers];
+  hipEvent_t stagingDone[kStagingBuffers];   // the last copy out of each
+  bool stagingBusy[kStagingBuffers];
+  int stagingNext;
+  size_t taskTableWords;
   uint64_t endMagic;
 };
 
@@ -185,16 +213,53 @@ void freeComm(arComm* c) {
     if (c->conn[p]) (void)hipFree(c->conn[p]);
   }
   if (c->ctrlHost) (void)hipHostFree(c->ctrlHost);
+  if (c->taskTable) (void)hipFree(c->taskTable);
+  for (int i = 0; i < kStagingBuffers; ++i) {
+    if (c->taskStaging[i]) (void)hipHostFree(c->taskStaging[i]);
+    if (c->stagingDone[i]) (void)hipEventDestroy(c->stagingDone[i]);
+  }
   c->startMagic = c->endMagic = 0;
   delete c;
 }
 
-// Protocol, channels, chunk, lanes and grid for one call.
-arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool aligned128, Plan* plan) {
+// The public view of a plan (p == nullptr: the one-rank / empty short cut).
+void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* p, arPlan_t* out) {
+  memset(out, 0, sizeof(*out));
+  const double S = (double)count * elemSize(dtype);
+  const double N = (double)c->nranks;
+  out->modelBytes = func == arFuncAllReduce ? 5.0 * (N - 1.0) * S
+                    : func == arFuncReduceScatter ? 3.0 * N * (N - 1.0) * S : 2.0 * N * (N - 1.0) * S;
+  out->groupLaunch = -1;
+  out->tasksInLaunch = 1;
+  if (p == nullptr) {
+    out->proto = arProtoSimple;
+    out->algo = arAlgoRing;
+    return;
+  }
+  out->algo = p->algo;
+  if (p->algo == arAlgoTree) out->modelBytes = (2.0 * N + 4.0 * (N - 1.0)) * S;
+  out->proto = p->proto;
+  out->nChannels = p->nChannels;
+  out->chunkElems = p->chunkElems;
+  out->lanesPerChannel = p->lanes;
+  out->ranksPerGroup = p->groupSize;
+  out->workgroups = p->grid;
+  out->threadsPerGroup = p->block;
+  out->stepBytes = p->slotBytes;
+  out->stepPayload = p->slotPayload;
+  out->nSlots = p->nSlots;
+  out->predictedUs = p->predictedUs;
+}
+
+// Protocol, channels, chunk, lanes and grid for one call, or for a batched
+// launch (`batch`) of `nTasks` collectives whose largest has `count` elements.
+arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool aligned128, Plan* plan,
+                    bool batch = false, int nTasks = 1) {
   const Env& e = env();
   const int esz = elemSize(dtype);
   // the tuner's message: per rank for AllReduce, the whole nranks x count
-  // traffic for ReduceScatter / AllGather [ch.6 §三]
+  // traffic for ReduceScatter / AllGather [ch.6 §三]; an aggregate runs its
+  // collectives side by side, so it is tuned on its largest
   const uint64_t nBytes = count * (uint64_t)esz * (func == kCollAllReduce ? 1u : (uint64_t)c->nranks);
   int proto = e.forcedProto != -2 ? e.forcedProto : c->proto;
   int nch = e.nChannels > 0 ? e.nChannels : c->nChannels;
@@ -233,6 +298,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   plan->chunkElems = chunkBytesOf(c, proto) / (uint64_t)esz;
   plan->unroll = proto == kSimple ? c->simpleUnroll : proto == kLL ? kLLUnroll : kLL128Unroll;
   if (tree && proto == kSimple && plan->unroll > kTreeSimpleUnrollMax) plan->unroll = kTreeSimpleUnrollMax;
+  if (batch && proto == kSimple && plan->unroll > kBatchSimpleUnrollMax) plan->unroll = kBatchSimpleUnrollMax;
   plan->direct = !tree && proto == kSimple && c->direct;
   plan->slotBytes = slotBytesOf(proto, plan->unroll);
   plan->slotPayload = slotPayloadOf(proto, plan->unroll);
@@ -263,7 +329,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
         layout(gs, &nGroups, &groupSize);
         plan->block = groupSize * kWave;
         int perCU = 0;
-        if (ringKernelOccupancy(*plan, func, dtype, op, &perCU) != hipSuccess) return arHipError;
+        if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return arHipError;
         const int grid1 = ((nch + 7) / 8) * 8 * nGroups;
         found = perCU * c->numCUs >= grid1;
       }
@@ -289,7 +355,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
                        : per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
   const uint64_t chunkBytes = cur * (uint64_t)esz;
   int perCU = 0;
-  if (ringKernelOccupancy(*plan, func, dtype, op, &perCU) != hipSuccess) return arHipError;
+  if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return arHipError;
   if (perCU < 1) perCU = 1;
   const int capacity = perCU * c->numCUs;   // resident workgroups
   auto gridFor = [&](int ln) {
@@ -334,8 +400,21 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     while (lanes > 1 && gridFor(lanes) > capacity) --lanes;
     if (gridFor(lanes) > capacity) return arInvalidUsage;
   }
+  // a batched launch runs up to nTasks collectives at once, each on its own
+  // nch x lanes wavefront sets: as many as the FIFOs (and, cooperative, the
+  // resident grid) allow
+  int slots = 1;
+  if (batch) {
+    slots = nTasks;
+    const int byFifo = c->lanesMax / (edges * nch * lanes);
+    if (slots > byFifo) slots = byFifo;
+    if (plan->cooperative)
+      while (slots > 1 && gridFor(lanes * slots) > capacity) --slots;
+    if (slots < 1) slots = 1;
+  }
+  plan->taskSlots = slots;
   plan->lanes = lanes;
-  plan->grid = gridFor(lanes);
+  plan->grid = gridFor(lanes * slots);
   return arSuccess;
 }
 
@@ -417,7 +496,11 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
     return arHipError;
   }
   memset(c->ctrlHost, 0, sizeof(Control));
-  if (hipHostGetDevicePointer((void**)&c->ctrlDev, c->ctrlHost, 0) != hipSuccess) {
+  if (hipHostGetDevicePointer((void**)&c->ctrlDev, c->ctrlHost, 0) != hipSuccess ||
+      hipEventCreateWithFlags(&c->stagingDone[0], hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->stagingDone[1], hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->stagingDone[2], hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->stagingDone[3], hipEventDisableTiming) != hipSuccess) {
     freeComm(c);
     return arHipError;
   }
@@ -527,32 +610,14 @@ arResult_t arGetPlanColl(arComm_t c, arFunc_t func, size_t count, arDataType_t d
   if (!commOk(c) || out == nullptr || elemSize(dtype) == 0) return arInvalidArgument;
   if (func != arFuncAllReduce && func != arFuncReduceScatter && func != arFuncAllGather) return arInvalidArgument;
   const int op = dtype == arUint64 ? arProbe : arSum;
-  memset(out, 0, sizeof(*out));
-  const double S = (double)count * elemSize(dtype);
-  const double N = (double)c->nranks;
-  out->modelBytes = func == arFuncAllReduce ? 5.0 * (N - 1.0) * S
-                    : func == arFuncReduceScatter ? 3.0 * N * (N - 1.0) * S : 2.0 * N * (N - 1.0) * S;
   if (c->nranks == 1 || count == 0) {
-    out->proto = arProtoSimple;
-    out->algo = arAlgoRing;
+    exportPlan(c, func, count, dtype, nullptr, out);
     return arSuccess;
   }
   Plan p;
   arResult_t r = makePlan(c, func, count, dtype, op, aligned128 != 0, &p);
   if (r != arSuccess) return r;
-  out->algo = p.algo;
-  if (p.algo == arAlgoTree) out->modelBytes = (2.0 * N + 4.0 * (N - 1.0)) * S;
-  out->proto = p.proto;
-  out->nChannels = p.nChannels;
-  out->chunkElems = p.chunkElems;
-  out->lanesPerChannel = p.lanes;
-  out->ranksPerGroup = p.groupSize;
-  out->workgroups = p.grid;
-  out->threadsPerGroup = p.block;
-  out->stepBytes = p.slotBytes;
-  out->stepPayload = p.slotPayload;
-  out->nSlots = p.nSlots;
-  out->predictedUs = p.predictedUs;
+  exportPlan(c, func, count, dtype, &p, out);
   return arSuccess;
 }
 
@@ -563,6 +628,48 @@ arResult_t arGetPlan(arComm_t c, size_t count, arDataType_t dtype, int aligned12
 }  // extern "C"
 
 namespace {
+
+// Group state of the calling thread [ch.7 §一: the group depth, the first
+// error and the communicators with queued work are thread-local].
+thread_local int tGroupDepth = 0;
+thread_local arResult_t tGroupError = arSuccess;
+thread_local std::vector<arComm*> tGroupComms;
+
+// Every (channel, lane, rank, edge) FIFO the kernel indexes must exist.
+bool fifosCover(const arComm* c, const Plan& plan) {
+  const int edges = plan.algo == arAlgoTree ? kTreeEdges : 1;
+  return (size_t)plan.nChannels * (size_t)plan.lanes * (size_t)edges * (size_t)plan.taskSlots <=
+         (size_t)c->lanesMax;
+}
+
+// Kernel arguments of one call (batched launches add the task table).
+void buildArgs(const arComm* c, const Plan& plan, int func, size_t count, const void* const* sendbufs,
+               void* const* recvbufs, bool aligned16, KernelArgs* a) {
+  const int N = c->nranks;
+  memset(a, 0, sizeof(*a));
+  for (int i = 0; i < N; ++i) {
+    a->send[i] = sendbufs[i];
+    a->recv[i] = recvbufs[i];
+  }
+  a->fifo = c->fifo[plan.proto];
+  a->conn = c->conn[plan.proto];
+  a->ctrl = c->ctrlDev;
+  a->count = count;
+  a->chunkElems = plan.chunkElems;
+  a->fifoWorkerBytes = c->fifoWorkerBytes[plan.proto];
+  a->timeoutTicks = (uint64_t)c->timeoutUs * (uint64_t)c->wallClockKHz / 1000u;
+  a->nranks = N;
+  a->nChannels = plan.nChannels;
+  a->lanes = plan.lanes;
+  a->groupSize = plan.groupSize;
+  a->nGroups = plan.nGroups;
+  a->nSlots = plan.nSlots;
+  a->aligned16 = aligned16 ? 1 : 0;
+  a->direct = plan.direct ? 1 : 0;
+  a->coll = func;
+  a->deadRank = c->deadRank;
+  a->taskSlots = 1;
+}
 
 // One collective call: argument checks (nothing is enqueued on failure), the
 // empty and one-rank short cuts, planning, kernel arguments, one launch.
@@ -612,6 +719,25 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
     }
   }
   hipStream_t st = (hipStream_t)stream;
+  if (tGroupDepth > 0) {   // queued until the outermost arGroupEnd [ch.7 §一]
+    if (!c->pending.empty() && c->pending[0].stream != st) return arInvalidUsage;
+    GroupTask t;
+    t.func = func;
+    t.count = count;
+    t.dtype = dtype;
+    t.op = op;
+    t.stream = st;
+    t.aligned16 = aligned16;
+    t.aligned128 = aligned128;
+    t.send.assign(sendbufs, sendbufs + N);
+    t.recv.assign(recvbufs, recvbufs + N);
+    c->pending.push_back(std::move(t));
+    if (!c->inGroup) {
+      c->inGroup = true;
+      tGroupComms.push_back(c);
+    }
+    return arSuccess;
+  }
   c->opCount++;
 
   if (N == 1) {   // one rank: the result is the input [ch.6 §三, one-rank path]
@@ -627,33 +753,10 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   const int kop = func == kCollAllGather ? (dtype == arUint64 ? arProbe : arSum) : op;
   arResult_t r = makePlan(c, func, count, dtype, kop, aligned128, &plan);
   if (r != arSuccess) return r;
-  // every (channel, lane, rank, edge) FIFO the kernel indexes must exist
-  const int edges = plan.algo == arAlgoTree ? kTreeEdges : 1;
-  if ((size_t)plan.nChannels * (size_t)plan.lanes * (size_t)edges > (size_t)c->lanesMax) return arInternalError;
+  if (!fifosCover(c, plan)) return arInternalError;
 
   KernelArgs a;
-  memset(&a, 0, sizeof(a));
-  for (int i = 0; i < N; ++i) {
-    a.send[i] = sendbufs[i];
-    a.recv[i] = recvbufs[i];
-  }
-  a.fifo = c->fifo[plan.proto];
-  a.conn = c->conn[plan.proto];
-  a.ctrl = c->ctrlDev;
-  a.count = count;
-  a.chunkElems = plan.chunkElems;
-  a.fifoWorkerBytes = c->fifoWorkerBytes[plan.proto];
-  a.timeoutTicks = (uint64_t)c->timeoutUs * (uint64_t)c->wallClockKHz / 1000u;
-  a.nranks = N;
-  a.nChannels = plan.nChannels;
-  a.lanes = plan.lanes;
-  a.groupSize = plan.groupSize;
-  a.nGroups = plan.nGroups;
-  a.nSlots = plan.nSlots;
-  a.aligned16 = aligned16 ? 1 : 0;
-  a.direct = plan.direct ? 1 : 0;
-  a.coll = func;
-  a.deadRank = c->deadRank;
+  buildArgs(c, plan, func, count, sendbufs, recvbufs, aligned16, &a);
 
   if (env().debug >= 1)
     fprintf(stderr,
@@ -672,23 +775,212 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   return arSuccess;
 }
 
+
+// Device room for `words` task-table words (and the pinned staging copies).
+arResult_t ensureTaskTable(arComm* c, size_t words) {
+  if (words <= c->taskTableWords) return arSuccess;
+  // earlier launches may still read the old table, earlier copies the old staging
+  if (c->launched && hipStreamSynchronize(c->lastStream) != hipSuccess) return arHipError;
+  for (int i = 0; i < kStagingBuffers; ++i) {
+    if (c->stagingBusy[i] && hipEventSynchronize(c->stagingDone[i]) != hipSuccess) return arHipError;
+    c->stagingBusy[i] = false;
+    if (c->taskStaging[i]) (void)hipHostFree(c->taskStaging[i]);
+    c->taskStaging[i] = nullptr;
+  }
+  if (c->taskTable) (void)hipFree(c->taskTable);
+  c->taskTable = nullptr;
+  c->taskTableWords = 0;
+  const size_t cap = words < 4096 ? 4096 : words * 2;
+  if (hipMalloc((void**)&c->taskTable, cap * sizeof(uint64_t)) != hipSuccess) return arHipError;
+  for (int i = 0; i < kStagingBuffers; ++i)
+    if (hipHostMalloc((void**)&c->taskStaging[i], cap * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess)
+      return arHipError;
+  c->taskTableWords = cap;
+  return arSuccess;
+}
+
+// Launch a comm's queued collectives [ch.6 §四, ch.7 §一]: one-rank calls are
+// copies; the rest are aggregated by arGroupAggregate (AllReduces of one
+// (op, type) within 4x of a run's largest share one launch; the halves run
+// alone), each launch planned on its largest collective, and batched
+// launches read their collectives from one task table copied to the device
+// first.
+arResult_t launchGroup(arComm* c) {
+  std::vector<GroupTask>& T = c->pending;
+  const int N = c->nranks;
+  const int n = (int)T.size();
+  const hipStream_t st = T[0].stream;
+  c->groupPlans.assign((size_t)n, arPlan_t());
+  c->opCount += (uint64_t)n;
+  if (N == 1) {   // the result is the input [ch.6 §三, one-rank path]
+    for (int i = 0; i < n; ++i) {
+      exportPlan(c, T[i].func, T[i].count, T[i].dtype, nullptr, &c->groupPlans[(size_t)i]);
+      if (T[i].recv[0] != T[i].send[0] &&
+          hipMemcpyAsync(T[i].recv[0], T[i].send[0], T[i].count * (size_t)elemSize(T[i].dtype),
+                         hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return arHipError;
+    }
+    c->lastStream = st;
+    c->launched = true;
+    return arSuccess;
+  }
+  std::vector<int> keys((size_t)n), isolate((size_t)n), order((size_t)n), launchOf((size_t)n);
+  std::vector<size_t> bytes((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    keys[(size_t)i] = (T[i].func * 4 + T[i].op) * 8 + T[i].dtype;
+    bytes[(size_t)i] = T[i].count * (size_t)elemSize(T[i].dtype) * (T[i].func == kCollAllReduce ? 1u : (size_t)N);
+    isolate[(size_t)i] = T[i].func != kCollAllReduce;   // batched launches are AllReduce only
+  }
+  int nLaunches = 0;
+  arResult_t r = arGroupAggregate(n, keys.data(), bytes.data(), isolate.data(), order.data(), launchOf.data(),
+                                  &nLaunches);
+  if (r != arSuccess) return r;
+
+  // plan every launch before anything is enqueued
+  struct Launch {
+    int first, size;   // range of `order`
+    Plan plan;
+    bool aligned16;
+    size_t row;        // first task-table row (batched launches)
+  };
+  std::vector<Launch> L;
+  size_t rows = 0;
+  for (int pos = 0; pos < n;) {
+    Launch l;
+    l.first = pos;
+    while (pos < n && launchOf[(size_t)order[(size_t)pos]] == launchOf[(size_t)order[(size_t)l.first]]) ++pos;
+    l.size = pos - l.first;
+    const GroupTask& lead = T[(size_t)order[(size_t)l.first]];   // the largest
+    bool a128 = true;
+    l.aligned16 = true;
+    for (int q = l.first; q < pos; ++q) {
+      const GroupTask& t = T[(size_t)order[(size_t)q]];
+      a128 = a128 && t.aligned128;
+      l.aligned16 = l.aligned16 && t.aligned16;
+    }
+    const int kop = lead.func == kCollAllGather ? (lead.dtype == arUint64 ? arProbe : arSum) : lead.op;
+    r = l.size == 1 ? makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan)
+                    : makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan, true, l.size);
+    if (r != arSuccess) return r;
+    if (!fifosCover(c, l.plan)) return arInternalError;
+    l.row = rows;
+    if (l.size > 1) rows += (size_t)l.size;
+    L.push_back(l);
+  }
+
+  // one copy of every batched launch's task rows, stream-ordered before them
+  const size_t rowWords = 1 + 2 * (size_t)N;
+  if (rows > 0) {
+    r = ensureTaskTable(c, rows * rowWords);
+    if (r != arSuccess) return r;
+    const int sb = c->stagingNext;
+    c->stagingNext = (sb + 1) % kStagingBuffers;
+    if (c->stagingBusy[sb] && hipEventSynchronize(c->stagingDone[sb]) != hipSuccess) return arHipError;
+    uint64_t* staging = c->taskStaging[sb];
+    for (const Launch& l : L) {
+      if (l.size == 1) continue;
+      for (int q = 0; q < l.size; ++q) {
+        const GroupTask& t = T[(size_t)order[(size_t)(l.first + q)]];
+        uint64_t* w = staging + (l.row + (size_t)q) * rowWords;
+        w[0] = t.count;
+        for (int k = 0; k < N; ++k) {
+          w[1 + k] = (uint64_t)(uintptr_t)t.send[(size_t)k];
+          w[1 + N + k] = (uint64_t)(uintptr_t)t.recv[(size_t)k];
+        }
+      }
+    }
+    // the device table is rewritten only after the previous group's kernels
+    // (same stream) have finished reading it
+    if (hipMemcpyAsync(c->taskTable, staging, rows * rowWords * sizeof(uint64_t), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipEventRecord(c->stagingDone[sb], st) != hipSuccess)
+      return arHipError;
+    c->stagingBusy[sb] = true;
+  }
+
+  for (int li = 0; li < (int)L.size(); ++li) {
+    const Launch& l = L[(size_t)li];
+    const GroupTask& lead = T[(size_t)order[(size_t)l.first]];
+    KernelArgs a;
+    buildArgs(c, l.plan, lead.func, lead.count, lead.send.data(), lead.recv.data(), l.aligned16, &a);
+    if (l.size > 1) {
+      a.tasks = c->taskTable + l.row * rowWords;
+      a.nTasks = l.size;
+      a.taskSlots = l.plan.taskSlots;
+    }
+    const int kop = lead.func == kCollAllGather ? (lead.dtype == arUint64 ? arProbe : arSum) : lead.op;
+    if (env().debug >= 1)
+      fprintf(stderr, "[ar] INFO group launch %d: %d x func=%d dtype=%d op=%d algo=%d proto=%d nch=%d lanes=%d\n", li,
+              l.size, lead.func, lead.dtype, lead.op, l.plan.algo, l.plan.proto, l.plan.nChannels, l.plan.lanes);
+    const hipError_t he = launchRing(l.plan, lead.dtype, kop, a, st);
+    if (he != hipSuccess) {
+      fprintf(stderr, "[ar] WARN kernel launch failed: %s\n", hipGetErrorString(he));
+      return arHipError;
+    }
+    c->lastStream = st;
+    c->launched = true;
+    for (int q = 0; q < l.size; ++q) {
+      const int ti = order[(size_t)(l.first + q)];
+      arPlan_t& pp = c->groupPlans[(size_t)ti];
+      exportPlan(c, T[(size_t)ti].func, T[(size_t)ti].count, T[(size_t)ti].dtype, &l.plan, &pp);
+      pp.groupLaunch = li;
+      pp.tasksInLaunch = l.size;
+    }
+  }
+  return arSuccess;
+}
 }  // namespace
 
 extern "C" {
 
+static arResult_t noteGroupError(arResult_t r) {
+  if (r != arSuccess && tGroupDepth > 0 && tGroupError == arSuccess) tGroupError = r;
+  return r;
+}
+
 arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t count,
                        arDataType_t dtype, arRedOp_t op, void* stream) {
-  return runColl(c, kCollAllReduce, sendbufs, recvbufs, count, dtype, op, stream);
+  return noteGroupError(runColl(c, kCollAllReduce, sendbufs, recvbufs, count, dtype, op, stream));
 }
 
 arResult_t arReduceScatter(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t recvcount,
                            arDataType_t dtype, arRedOp_t op, void* stream) {
-  return runColl(c, kCollReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream);
+  return noteGroupError(runColl(c, kCollReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream));
 }
 
 arResult_t arAllGather(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t sendcount,
                        arDataType_t dtype, void* stream) {
-  return runColl(c, kCollAllGather, sendbufs, recvbufs, sendcount, dtype, arSum, stream);
+  return noteGroupError(runColl(c, kCollAllGather, sendbufs, recvbufs, sendcount, dtype, arSum, stream));
+}
+
+arResult_t arGroupStart(void) {
+  ++tGroupDepth;
+  return arSuccess;
+}
+
+arResult_t arGroupEnd(void) {
+  if (tGroupDepth == 0) return arInvalidUsage;   // not in a group
+  if (--tGroupDepth > 0) return arSuccess;       // an inner group: the outermost end launches
+  arResult_t r = tGroupError;
+  tGroupError = arSuccess;
+  std::vector<arComm*> comms;
+  comms.swap(tGroupComms);
+  for (arComm* c : comms) {
+    if (r == arSuccess) {
+      const arResult_t rc = launchGroup(c);
+      if (rc != arSuccess) r = rc;
+    }
+    c->pending.clear();
+    c->inGroup = false;
+  }
+  return r;
+}
+
+arResult_t arGetGroupPlan(arComm_t c, int index, arPlan_t* plan) {
+  if (!commOk(c) || plan == nullptr || index < 0 || (size_t)index >= c->groupPlans.size())
+    return arInvalidArgument;
+  *plan = c->groupPlans[(size_t)index];
+  return arSuccess;
 }
 
 arResult_t arCommGetAsyncError(arComm_t c, arResult_t* err) {
@@ -709,6 +1001,7 @@ arResult_t arCommAbort(arComm_t c) {
 arResult_t arDestroy(arComm_t c) {
   if (c == nullptr) return arSuccess;
   if (!commOk(c)) return arInvalidArgument;
+  if (c->inGroup) return arInvalidUsage;   // it has collectives queued in an open group
   arResult_t r = arSuccess;
   if (c->launched && hipStreamSynchronize(c->lastStream) != hipSuccess) r = arHipError;
   freeComm(c);

@@ -27,6 +27,7 @@ constexpr int kMaxSlots = 8;              // FIFO depth provisioned per worker
 //           seven 16-byte payload pieces, 8 payload bytes and an 8-byte flag.
 constexpr int kSimpleUnrollMax = 8;       // Simple slot = unroll KiB (1, 2, 4 or 8)
 constexpr int kSimpleUnrollDefault = 8;
+constexpr int kBatchSimpleUnrollMax = 4;  // batched ring launches: Simple slot at most 4 KiB
 constexpr int kTreeSimpleUnrollMax = 2;   // the tree's Simple slot is at most 2 KiB (three slot
                                           // arrays live per lane: 4 KiB would spill)
 constexpr int kTreeEdges = 3;             // a tree node's FIFOs: from d0, from d1, from its parent
@@ -95,6 +96,12 @@ struct KernelArgs {
   int direct;                 // Simple: all-gather writes the successor's output directly
   int coll;                   // kCollAllReduce / kCollReduceScatter / kCollAllGather (selects the kernel)
   int deadRank;               // debug: this rank's members return at once
+  // Batched launch (several AllReduces of one aggregate): nTasks rows of
+  // 1 + 2 * nranks words {count, send[nranks], recv[nranks]}; 0 = one call
+  // described by count / send / recv above.
+  const uint64_t* tasks;
+  int nTasks;
+  int taskSlots;              // tasks in flight at once (each on nChannels x lanes wavefront sets)
 };
 
 // Everything arAllReduce decides for one call.
@@ -112,6 +119,7 @@ struct Plan {
   int slotPayload;
   int nSlots;
   int unroll;                 // pieces per lane per slot
+  int taskSlots;              // batched launches: collectives running at once
   bool direct;
   bool cooperative;
   float predictedUs;
@@ -119,7 +127,7 @@ struct Plan {
 
 // Provided by ar_kernels.hip.
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream);
-hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, int* blocksPerCU);
+hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bool batch, int* blocksPerCU);
 
 inline int elemSize(int dtype) {
   switch (dtype) {

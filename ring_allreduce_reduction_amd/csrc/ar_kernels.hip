@@ -493,65 +493,24 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
   return true;
 }
 
+// One collective of the ring schedule over one member's (channel, lane)
+// share of `count` elements per rank; false when a wait gave up.
 template <int PROTO, int DT, int OP, int U, int COLL>
-__global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
+__device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, int ch, int k, u64 count,
+                                         const char* in, char* out, char* succOut) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr u64 A = 16 / ESZ;   // 16-byte grain in elements
   constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
                         : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
-  const int wave = threadIdx.x / kWave;
   const int N = a.nranks;
-  const int lanesTotal = a.nChannels * a.lanes;
-
-  // Workgroup -> (lane id, group).  With several groups per lane, the groups
-  // of one lane get workgroup ids congruent mod 8, i.e. the same XCD under
-  // round-robin dispatch, so their cross-workgroup edges stay in one L2.
-  int L, g;
-  if (a.nGroups == 1) {
-    L = blockIdx.x;
-    g = 0;
-  } else {
-    const int x = blockIdx.x % 8;
-    g = (blockIdx.x / 8) % a.nGroups;
-    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
-  }
-  if (L >= lanesTotal) return;
-  const int r = g * a.groupSize + wave;
-  if (r >= N || r == a.deadRank) return;
-  const int ch = L / a.lanes;
-  const int k = L % a.lanes;
   const int succ = r + 1 == N ? 0 : r + 1;
-  const int pred = r == 0 ? N - 1 : r - 1;
-
   // channel share [pages: contiguous split per channel, 16-byte grain]
-  const u64 count = a.count;
   const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
   const u64 lo = umin((u64)ch * per, count);
   const u64 hi = umin(lo + per, count);
   const u64 len = hi - lo;
-  if (len == 0) return;
+  if (len == 0) return true;
 
-  Member m;
-  m.lane = threadIdx.x % kWave;
-  const size_t wSelf = (size_t)L * N + r, wSucc = (size_t)L * N + succ;
-  m.rfifo = a.fifo + wSelf * a.fifoWorkerBytes;
-  m.sfifo = a.fifo + wSucc * a.fifoWorkerBytes;
-  m.self = a.conn + wSelf;
-  m.succ = a.conn + wSucc;
-  m.recvAgent = pred / a.groupSize != g;
-  m.sendAgent = succ / a.groupSize != g;
-  m.aligned = a.aligned16 != 0;
-  m.direct = a.direct != 0;
-  // counters carry over from earlier calls (tail == head at call boundaries)
-  m.recvStep = ldCounter(&m.self->head, true);
-  m.sendStep = ldCounter(&m.succ->tail, true);
-  m.succHead = 0;
-  m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
-  m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
-
-  const char* in = (const char*)a.send[r];
-  char* out = (char*)a.recv[r];
-  char* succOut = (char*)a.recv[succ];
   const u64 C = a.chunkElems;
   const u64 loopSize = (u64)N * C;
   const int lastSendStage = 2 * N - 3;
@@ -598,7 +557,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
             if (b >= bytes) break;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
             if (!step<PROTO, DT, OP, U>(a, m, kind, in + first + b, out + first + b, succOut + first + b, valid))
-              return;
+              return false;
           }
         }
       }
@@ -641,10 +600,77 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
             if (!step<PROTO, DT, OP, U>(a, m, kind, in + inOff + b, out + outOff + b, succOut + outOff + b,
                                          valid))
-              return;
+              return false;
           }
         }
       }
+    }
+  }
+  return true;
+}
+
+// BATCH: the launch runs the a.nTasks AllReduces of one aggregate, each
+// described by a row of a.tasks {count, send[N], recv[N]}.  a.taskSlots of
+// them run at once, each on its own nChannels x lanes wavefront sets (and
+// FIFOs); a set takes tasks slot, slot + taskSlots, ... in turn, so its FIFO
+// steps simply continue from one task to the next.
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH>
+__global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
+  const int wave = threadIdx.x / kWave;
+  const int N = a.nranks;
+  const int perTask = a.nChannels * a.lanes;
+  const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
+
+  // Workgroup -> (lane id, group).  With several groups per lane, the groups
+  // of one lane get workgroup ids congruent mod 8, i.e. the same XCD under
+  // round-robin dispatch, so their cross-workgroup edges stay in one L2.
+  int L, g;
+  if (a.nGroups == 1) {
+    L = blockIdx.x;
+    g = 0;
+  } else {
+    const int x = blockIdx.x % 8;
+    g = (blockIdx.x / 8) % a.nGroups;
+    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
+  }
+  if (L >= lanesTotal) return;
+  const int r = g * a.groupSize + wave;
+  if (r >= N || r == a.deadRank) return;
+  const int Lc = BATCH ? L % perTask : L;   // (channel, lane) inside the task
+  const int ch = Lc / a.lanes;
+  const int k = Lc % a.lanes;
+  const int succ = r + 1 == N ? 0 : r + 1;
+  const int pred = r == 0 ? N - 1 : r - 1;
+
+  Member m;
+  m.lane = threadIdx.x % kWave;
+  const size_t wSelf = (size_t)L * N + r, wSucc = (size_t)L * N + succ;
+  m.rfifo = a.fifo + wSelf * a.fifoWorkerBytes;
+  m.sfifo = a.fifo + wSucc * a.fifoWorkerBytes;
+  m.self = a.conn + wSelf;
+  m.succ = a.conn + wSucc;
+  m.recvAgent = pred / a.groupSize != g;
+  m.sendAgent = succ / a.groupSize != g;
+  m.aligned = a.aligned16 != 0;
+  m.direct = a.direct != 0;
+  // counters carry over from earlier calls (tail == head at call boundaries)
+  m.recvStep = ldCounter(&m.self->head, true);
+  m.sendStep = ldCounter(&m.succ->tail, true);
+  m.succHead = 0;
+  m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
+  m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
+
+  if (!BATCH) {
+    if (!ringPass<PROTO, DT, OP, U, COLL>(a, m, r, ch, k, a.count, (const char*)a.send[r], (char*)a.recv[r],
+                                          (char*)a.recv[succ]))
+      return;
+  } else {
+    const size_t row = 1 + 2 * (size_t)N;
+    for (int t = L / perTask; t < a.nTasks; t += a.taskSlots) {
+      const u64* d = a.tasks + (size_t)t * row;
+      if (!ringPass<PROTO, DT, OP, U, COLL>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
+                                            (char*)d[1 + N + succ]))
+        return;
     }
   }
   // LL / LL128 never touch the tail counter per slot: publish it once so the
@@ -879,65 +905,33 @@ __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pie
   return true;
 }
 
+// A tree node's FIFO ends and peers (independent of the data).
+struct TreeNode {
+  int up, d[2];
+  Edge fromChild[2], toChild[2], fromParent, toParent;
+};
+
+// One AllReduce over one member's (channel, lane) share of `count` elements
+// per rank: batches of nSlots columns, each a reduce pass then (below the
+// root) a broadcast pass; false when a wait gave up.
 template <int PROTO, int DT, int OP, int U>
-__global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
+__device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int ch, int k, int lane, u64 count,
+                                         const char* inBase, char* outBase) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr u64 A = 16 / ESZ;
   constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
                         : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int N = a.nranks;
-  const int lanesTotal = a.nChannels * a.lanes;
-
-  int L, g;   // (lane id, group), as in the ring kernel
-  if (a.nGroups == 1) {
-    L = blockIdx.x;
-    g = 0;
-  } else {
-    const int x = blockIdx.x % 8;
-    g = (blockIdx.x / 8) % a.nGroups;
-    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
-  }
-  if (L >= lanesTotal) return;
-  const int r = g * a.groupSize + wave;
-  if (r >= N || r == a.deadRank) return;
-  const int ch = L / a.lanes;
-  const int k = L % a.lanes;
-
-  const u64 count = a.count;
   const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
   const u64 lo = umin((u64)ch * per, count);
   const u64 len = umin(lo + per, count) - lo;
   const u64 sub = alignUp(divUp(len, (u64)a.lanes), A);
   const u64 sb = umin((u64)k * sub, len);
   const u64 bytes = (umin(sb + sub, len) - sb) * ESZ;
-  if (bytes == 0) return;
+  if (bytes == 0) return true;
 
-  // this member's place in its channel's tree
-  const int t = a.nChannels > 1 && 2 * ch >= a.nChannels ? 1 : 0;
-  int up, d[2];
-  dtreeNode(N, r, t, up, d[0], d[1]);
-  const bool leaf = d[0] < 0 && d[1] < 0;
-  auto worker = [&](int node, int edge) { return ((size_t)L * N + node) * 3 + edge; };
-  auto cross = [&](int node) { return node / a.groupSize != g; };
-  Edge fromChild[2], toChild[2], fromParent, toParent;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (d[i] >= 0) {
-      fromChild[i] = openEdge(a, worker(r, i), cross(d[i]), true);
-      toChild[i] = openEdge(a, worker(d[i], 2), cross(d[i]), false);
-    }
-  }
-  if (up >= 0) {
-    int pu, p0, p1;
-    dtreeNode(N, up, t, pu, p0, p1);
-    fromParent = openEdge(a, worker(r, 2), cross(up), true);
-    toParent = openEdge(a, worker(up, r == p0 ? 0 : 1), cross(up), false);
-  }
-
-  const char* in = (const char*)a.send[r] + (lo + sb) * ESZ;
-  char* out = (char*)a.recv[r] + (lo + sb) * ESZ;
+  const bool leaf = nd.d[0] < 0 && nd.d[1] < 0;
+  const char* in = inBase + (lo + sb) * ESZ;
+  char* out = outBase + (lo + sb) * ESZ;
   const bool aligned = a.aligned16 != 0;
   const Pieces<PROTO, U> pc(lane);
   const u64 nCols = divUp(bytes, (u64)PAYLOAD);
@@ -960,10 +954,10 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
         bool have = false;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          if (d[i] < 0) continue;
+          if (nd.d[i] < 0) continue;
           v4u got[U];
-          if (!edgeRecv<PROTO, U>(a, fromChild[i], pc, lane, valid, got)) return;
-          edgeFinishRecv(a, fromChild[i], lane);
+          if (!edgeRecv<PROTO, U>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
+          edgeFinishRecv(a, nd.fromChild[i], lane);
 #pragma unroll
           for (int u = 0; u < U; ++u) acc[u] = have ? combine<DT, OP>(acc[u], got[u]) : got[u];
           have = true;
@@ -971,39 +965,99 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
 #pragma unroll
         for (int u = 0; u < U; ++u) acc[u] = combine<DT, OP>(acc[u], x[u]);
       }
-      if (up >= 0) {
-        if (!edgeSend<PROTO, U>(a, toParent, pc, lane, valid, acc)) return;
+      if (nd.up >= 0) {
+        if (!edgeSend<PROTO, U>(a, nd.toParent, pc, lane, valid, acc)) return false;
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u)
           storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          if (d[i] >= 0 && !edgeSend<PROTO, U>(a, toChild[i], pc, lane, valid, acc)) return;
+          if (nd.d[i] >= 0 && !edgeSend<PROTO, U>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
       }
     }
-    if (up < 0) continue;
+    if (nd.up < 0) continue;
     // broadcast pass: the result from the parent, to my output and children
     for (u64 j = jb; j < je; ++j) {
       const u64 b = j * (u64)PAYLOAD;
       const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-      if (!edgeRecv<PROTO, U>(a, fromParent, pc, lane, valid, acc)) return;
-      edgeFinishRecv(a, fromParent, lane);
+      if (!edgeRecv<PROTO, U>(a, nd.fromParent, pc, lane, valid, acc)) return false;
+      edgeFinishRecv(a, nd.fromParent, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (d[i] >= 0 && !edgeSend<PROTO, U>(a, toChild[i], pc, lane, valid, acc)) return;
+        if (nd.d[i] >= 0 && !edgeSend<PROTO, U>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
+    }
+  }
+  return true;
+}
+
+// BATCH as for the ring kernel: a.nTasks AllReduces from a.tasks, a.taskSlots
+// of them at once.
+template <int PROTO, int DT, int OP, int U, bool BATCH>
+__global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int N = a.nranks;
+  const int perTask = a.nChannels * a.lanes;
+  const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
+
+  int L, g;   // (lane id, group), as in the ring kernel
+  if (a.nGroups == 1) {
+    L = blockIdx.x;
+    g = 0;
+  } else {
+    const int x = blockIdx.x % 8;
+    g = (blockIdx.x / 8) % a.nGroups;
+    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
+  }
+  if (L >= lanesTotal) return;
+  const int r = g * a.groupSize + wave;
+  if (r >= N || r == a.deadRank) return;
+  const int Lc = BATCH ? L % perTask : L;   // (channel, lane) inside the task
+  const int ch = Lc / a.lanes;
+  const int k = Lc % a.lanes;
+
+  // this member's place in its channel's tree
+  TreeNode nd;
+  const int t = a.nChannels > 1 && 2 * ch >= a.nChannels ? 1 : 0;
+  dtreeNode(N, r, t, nd.up, nd.d[0], nd.d[1]);
+  auto worker = [&](int node, int edge) { return ((size_t)L * N + node) * 3 + edge; };
+  auto cross = [&](int node) { return node / a.groupSize != g; };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (nd.d[i] >= 0) {
+      nd.fromChild[i] = openEdge(a, worker(r, i), cross(nd.d[i]), true);
+      nd.toChild[i] = openEdge(a, worker(nd.d[i], 2), cross(nd.d[i]), false);
+    }
+  }
+  if (nd.up >= 0) {
+    int pu, p0, p1;
+    dtreeNode(N, nd.up, t, pu, p0, p1);
+    nd.fromParent = openEdge(a, worker(r, 2), cross(nd.up), true);
+    nd.toParent = openEdge(a, worker(nd.up, r == p0 ? 0 : 1), cross(nd.up), false);
+  }
+
+  if (!BATCH) {
+    if (!treePass<PROTO, DT, OP, U>(a, nd, ch, k, lane, a.count, (const char*)a.send[r], (char*)a.recv[r]))
+      return;
+  } else {
+    const size_t row = 1 + 2 * (size_t)N;
+    for (int i = L / perTask; i < a.nTasks; i += a.taskSlots) {
+      const u64* d = a.tasks + (size_t)i * row;
+      if (!treePass<PROTO, DT, OP, U>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r], (char*)d[1 + N + r]))
+        return;
     }
   }
   // LL / LL128 never touch the tail counter per slot: publish it once so the
   // next call starts both ends of each FIFO at the same step.
   if (PROTO != kSimple && lane == 0) {
-    if (up >= 0) stRelaxed64(&toParent.conn->tail, toParent.step, true);
+    if (nd.up >= 0) stRelaxed64(&nd.toParent.conn->tail, nd.toParent.step, true);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (d[i] >= 0) stRelaxed64(&toChild[i].conn->tail, toChild[i].step, true);
+      if (nd.d[i] >= 0) stRelaxed64(&nd.toChild[i].conn->tail, nd.toChild[i].step, true);
   }
 }
 
@@ -1011,109 +1065,107 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
 
 typedef void (*KernelFn)(const KernelArgs);
 
-template <int PROTO, int U, int COLL>
-KernelFn pick(int dtype, int op) {
-  if (COLL == kCollAllGather) {   // no arithmetic: one kernel per element size
+// The ring kernel for one collective, element type and op (AllGather has no
+// arithmetic: one kernel per element size).
+template <int PROTO, int U, int COLL, bool BATCH>
+KernelFn pickRing(int dtype, int op) {
+  if (COLL == kCollAllGather) {
     switch (dtype) {
-      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL>;
-      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL>;
-      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL>;
+      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH>;
+      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH>;
+      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH>;
     }
     return nullptr;
   }
+#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH>
   switch (dtype) {
-    case arInt32:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arInt32, arMax, U, COLL>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arInt32, arMin, U, COLL>;
-      break;
-    case arFloat32:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat32, arSum, U, COLL>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat32, arMax, U, COLL>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat32, arMin, U, COLL>;
-      break;
-    case arFloat16:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arFloat16, arSum, U, COLL>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arFloat16, arMax, U, COLL>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arFloat16, arMin, U, COLL>;
-      break;
-    case arBfloat16:
-      if (op == arSum) return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL>;
-      if (op == arMax) return ringAllReduceKernel<PROTO, arBfloat16, arMax, U, COLL>;
-      if (op == arMin) return ringAllReduceKernel<PROTO, arBfloat16, arMin, U, COLL>;
-      break;
-    case arUint64:
-      if (op == arProbe) return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL>;
-      break;
+    case arInt32: return op == arSum ? AR_RING(arInt32, arSum) : op == arMax ? AR_RING(arInt32, arMax)
+                       : op == arMin ? AR_RING(arInt32, arMin) : nullptr;
+    case arFloat32: return op == arSum ? AR_RING(arFloat32, arSum) : op == arMax ? AR_RING(arFloat32, arMax)
+                         : op == arMin ? AR_RING(arFloat32, arMin) : nullptr;
+    case arFloat16: return op == arSum ? AR_RING(arFloat16, arSum) : op == arMax ? AR_RING(arFloat16, arMax)
+                         : op == arMin ? AR_RING(arFloat16, arMin) : nullptr;
+    case arBfloat16: return op == arSum ? AR_RING(arBfloat16, arSum) : op == arMax ? AR_RING(arBfloat16, arMax)
+                          : op == arMin ? AR_RING(arBfloat16, arMin) : nullptr;
+    case arUint64: return op == arProbe ? AR_RING(arUint64, arProbe) : nullptr;
   }
+#undef AR_RING
   return nullptr;
 }
 
-template <int COLL>
-KernelFn pickProto(const Plan& plan, int dtype, int op) {
-  if (plan.proto == kLL) return pick<kLL, kLLUnroll, COLL>(dtype, op);
-  if (plan.proto == kLL128) return pick<kLL128, kLL128Unroll, COLL>(dtype, op);
-  if (plan.proto == kSimple) {
-    if (plan.unroll == 1) return pick<kSimple, 1, COLL>(dtype, op);
-    if (plan.unroll == 2) return pick<kSimple, 2, COLL>(dtype, op);
-    if (plan.unroll == 4) return pick<kSimple, 4, COLL>(dtype, op);
-    if (plan.unroll == 8) return pick<kSimple, 8, COLL>(dtype, op);
-  }
-  return nullptr;
-}
-
-template <int PROTO, int U>
+template <int PROTO, int U, bool BATCH>
 KernelFn pickTree(int dtype, int op) {
+#define AR_TREE(DT, OP) treeAllReduceKernel<PROTO, DT, OP, U, BATCH>
   switch (dtype) {
-    case arInt32:
-      if (op == arSum) return treeAllReduceKernel<PROTO, arInt32, arSum, U>;
-      if (op == arMax) return treeAllReduceKernel<PROTO, arInt32, arMax, U>;
-      if (op == arMin) return treeAllReduceKernel<PROTO, arInt32, arMin, U>;
-      break;
-    case arFloat32:
-      if (op == arSum) return treeAllReduceKernel<PROTO, arFloat32, arSum, U>;
-      if (op == arMax) return treeAllReduceKernel<PROTO, arFloat32, arMax, U>;
-      if (op == arMin) return treeAllReduceKernel<PROTO, arFloat32, arMin, U>;
-      break;
-    case arFloat16:
-      if (op == arSum) return treeAllReduceKernel<PROTO, arFloat16, arSum, U>;
-      if (op == arMax) return treeAllReduceKernel<PROTO, arFloat16, arMax, U>;
-      if (op == arMin) return treeAllReduceKernel<PROTO, arFloat16, arMin, U>;
-      break;
-    case arBfloat16:
-      if (op == arSum) return treeAllReduceKernel<PROTO, arBfloat16, arSum, U>;
-      if (op == arMax) return treeAllReduceKernel<PROTO, arBfloat16, arMax, U>;
-      if (op == arMin) return treeAllReduceKernel<PROTO, arBfloat16, arMin, U>;
-      break;
-    case arUint64:
-      if (op == arProbe) return treeAllReduceKernel<PROTO, arUint64, arProbe, U>;
-      break;
+    case arInt32: return op == arSum ? AR_TREE(arInt32, arSum) : op == arMax ? AR_TREE(arInt32, arMax)
+                       : op == arMin ? AR_TREE(arInt32, arMin) : nullptr;
+    case arFloat32: return op == arSum ? AR_TREE(arFloat32, arSum) : op == arMax ? AR_TREE(arFloat32, arMax)
+                         : op == arMin ? AR_TREE(arFloat32, arMin) : nullptr;
+    case arFloat16: return op == arSum ? AR_TREE(arFloat16, arSum) : op == arMax ? AR_TREE(arFloat16, arMax)
+                         : op == arMin ? AR_TREE(arFloat16, arMin) : nullptr;
+    case arBfloat16: return op == arSum ? AR_TREE(arBfloat16, arSum) : op == arMax ? AR_TREE(arBfloat16, arMax)
+                          : op == arMin ? AR_TREE(arBfloat16, arMin) : nullptr;
+    case arUint64: return op == arProbe ? AR_TREE(arUint64, arProbe) : nullptr;
+  }
+#undef AR_TREE
+  return nullptr;
+}
+
+// Protocol and slot size: the ring's Simple slot is 1, 2, 4 or 8 KiB (at
+// most 4 KiB batched), the tree's 1 or 2 KiB; LL and LL128 have one slot
+// geometry each.
+template <int COLL, bool BATCH>
+KernelFn pickRingProto(const Plan& plan, int dtype, int op) {
+  switch (plan.proto) {
+    case kLL: return pickRing<kLL, kLLUnroll, COLL, BATCH>(dtype, op);
+    case kLL128: return pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
+    case kSimple:
+      switch (plan.unroll) {
+        case 1: return pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
+        case 2: return pickRing<kSimple, 2, COLL, BATCH>(dtype, op);
+        case 4: return pickRing<kSimple, 4, COLL, BATCH>(dtype, op);
+        case 8:   // batched launches use at most 4 KiB slots (8 KiB spills with the task loop)
+          if constexpr (!BATCH) return pickRing<kSimple, 8, COLL, false>(dtype, op);
+          return nullptr;
+      }
   }
   return nullptr;
 }
 
+template <bool BATCH>
 KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
-  if (plan.proto == kLL) return pickTree<kLL, kLLUnroll>(dtype, op);
-  if (plan.proto == kLL128) return pickTree<kLL128, kLL128Unroll>(dtype, op);
-  if (plan.proto == kSimple) {
-    if (plan.unroll == 1) return pickTree<kSimple, 1>(dtype, op);
-    if (plan.unroll == 2) return pickTree<kSimple, 2>(dtype, op);
+  switch (plan.proto) {
+    case kLL: return pickTree<kLL, kLLUnroll, BATCH>(dtype, op);
+    case kLL128: return pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op);
+    case kSimple:
+      switch (plan.unroll) {
+        case 1: return pickTree<kSimple, 1, BATCH>(dtype, op);
+        case 2: return pickTree<kSimple, 2, BATCH>(dtype, op);
+      }
   }
   return nullptr;
 }
 
-KernelFn pickKernel(const Plan& plan, int coll, int dtype, int op) {
-  if (plan.algo == arAlgoTree) return coll == kCollAllReduce ? pickTreeProto(plan, dtype, op) : nullptr;
-  if (coll == kCollAllReduce) return pickProto<kCollAllReduce>(plan, dtype, op);
-  if (coll == kCollReduceScatter) return pickProto<kCollReduceScatter>(plan, dtype, op);
-  if (coll == kCollAllGather) return pickProto<kCollAllGather>(plan, dtype, op);
+// Batched launches (several AllReduces from a task table) exist for
+// AllReduce only.
+KernelFn pickKernel(const Plan& plan, int coll, int dtype, int op, bool batch) {
+  if (plan.algo == arAlgoTree) {
+    if (coll != kCollAllReduce) return nullptr;
+    return batch ? pickTreeProto<true>(plan, dtype, op) : pickTreeProto<false>(plan, dtype, op);
+  }
+  if (coll == kCollAllReduce)
+    return batch ? pickRingProto<kCollAllReduce, true>(plan, dtype, op)
+                 : pickRingProto<kCollAllReduce, false>(plan, dtype, op);
+  if (batch) return nullptr;
+  if (coll == kCollReduceScatter) return pickRingProto<kCollReduceScatter, false>(plan, dtype, op);
+  if (coll == kCollAllGather) return pickRingProto<kCollAllGather, false>(plan, dtype, op);
   return nullptr;
 }
 
 }  // namespace
 
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream) {
-  KernelFn fn = pickKernel(plan, args.coll, dtype, op);
+  KernelFn fn = pickKernel(plan, args.coll, dtype, op, args.nTasks > 0);
   if (fn == nullptr) return hipErrorInvalidValue;
   if (plan.cooperative) {
     void* params[] = {(void*)&args};
@@ -1123,8 +1175,8 @@ hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& arg
   return hipGetLastError();
 }
 
-hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, int* blocksPerCU) {
-  KernelFn fn = pickKernel(plan, coll, dtype, op);
+hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bool batch, int* blocksPerCU) {
+  KernelFn fn = pickKernel(plan, coll, dtype, op, batch);
   if (fn == nullptr) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocksPerCU, (const void*)fn, plan.block, 0);
 }

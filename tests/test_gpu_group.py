@@ -1,0 +1,240 @@
+"""GPU parity of grouped collectives: calls between arGroupStart / arGroupEnd,
+AllReduces aggregated into batched launches; every call's output compared
+bit for bit with the oracle on the plan arGetGroupPlan reports for it."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ring_allreduce_reduction_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+def inputs(n, count, dtype, op, seed):
+    from ring_allreduce_reduction_amd import inputs as gen
+    return gen.probe_inputs(n, count) if op == "probe" else gen.make_inputs(n, count, dtype, seed=seed)
+
+
+def run_group(B, gu, comm, calls, what=""):
+    """calls: list of (count, dtype, op, inplace, seed).  Returns the plans."""
+    n = comm.nranks
+    gu.note("group %s: %d calls on %d ranks: %s" % (what, len(calls), n, [c[:3] for c in calls]))
+    keep = []
+    with B.Group():
+        for count, dtype, op, inplace, seed in calls:
+            xs = inputs(n, count, dtype, op, seed)
+            sends = [gu.to_device(x, dtype) for x in xs]
+            recvs = sends if inplace else [gu.empty_like_sentinel(count, dtype) for _ in range(n)]
+            comm.allreduce(sends, recvs, op, count=count, dtype=B.DTYPE_BY_NAME[dtype])
+            keep.append((xs, sends, recvs))
+    torch.cuda.synchronize()
+    assert comm.async_error() == B.arSuccess
+    plans = []
+    for i, ((count, dtype, op, _, _), (xs, _, recvs)) in enumerate(zip(calls, keep)):
+        plan = comm.group_plan(i)
+        want = gu.expected(xs, dtype, op, plan)
+        for r in range(n):
+            gu.assert_bits_equal(gu.to_host_raw(recvs[r], dtype), want, dtype,
+                                 "call %d rank %d (%s, count %d, %s %s, launch %d of %d tasks)"
+                                 % (i, r, dtype, count, B.ALGO_NAMES[plan["algo"]], B.PROTO_NAMES[plan["proto"]],
+                                    plan["groupLaunch"], plan["tasksInLaunch"]))
+        plans.append(plan)
+    return plans
+
+
+@pytest.mark.parametrize("algo", ["ring", "tree", "auto"])
+@pytest.mark.parametrize("proto", ["simple", "ll", "ll128", "auto"])
+def test_group_mixed_sizes(B, gu, algo, proto):
+    sizes = [1000, 3000, 3500, 20000, 70000, 5, 100003, 4096, 4096, 4100]
+    with B.Comm(8, 16, proto, algo) as comm:
+        plans = run_group(B, gu, comm, [(c, "float32", "sum", False, i) for i, c in enumerate(sizes)], algo + proto)
+    assert max(p["tasksInLaunch"] for p in plans) >= 3            # the 4096-sized calls share a launch
+    launches = {p["groupLaunch"] for p in plans}
+    assert len(launches) < len(sizes)
+
+
+def test_group_buckets_dtypes_ops(B, gu):
+    calls = []
+    for i, (dtype, op) in enumerate([("int32", "sum"), ("float32", "max"), ("bfloat16", "sum"), ("float16", "min"),
+                                     ("uint64", "probe"), ("float32", "sum")]):
+        for j, count in enumerate([5000, 6000, 20011]):
+            calls.append((count, dtype, op, False, 10 * i + j))
+    with B.Comm(8, 8, "auto", "auto") as comm:
+        plans = run_group(B, gu, comm, calls, "buckets")
+    # one launch never mixes (dtype, op)
+    seen = {}
+    for (count, dtype, op, _, _), p in zip(calls, plans):
+        assert seen.setdefault(p["groupLaunch"], (dtype, op)) == (dtype, op)
+
+
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+def test_group_cooperative_24_ranks(B, gu, algo):
+    with B.Comm(24, 4, "simple", algo) as comm:
+        plans = run_group(B, gu, comm, [(c, "float32", "sum", False, c) for c in (3000, 3100, 2900, 12345)], algo)
+    # 12345 takes 3100 (4 x 3100 > 12345); 3000 then takes 2900
+    assert plans[0]["ranksPerGroup"] <= 16 and [p["tasksInLaunch"] for p in plans] == [2, 2, 2, 2]
+
+
+def test_group_in_place_and_halves(B, gu, orc):
+    from ring_allreduce_reduction_amd import inputs as gen
+    n = 8
+    with B.Comm(n, 4, "auto", "auto") as comm:
+        xa = gen.make_inputs(n, 40000, "float32", seed=1)
+        xb = gen.make_inputs(n, 30001, "float32", seed=2)
+        xr = gen.make_inputs(n, n * 5000, "float32", seed=3)
+        xg = gen.make_inputs(n, 7000, "int32", seed=4)
+        a = [gu.to_device(x, "float32") for x in xa]
+        b = [gu.to_device(x, "float32") for x in xb]
+        rs_in = [gu.to_device(x, "float32") for x in xr]
+        rs_out = [gu.empty_like_sentinel(5000, "float32") for _ in range(n)]
+        ag_in = [gu.to_device(x, "int32") for x in xg]
+        ag_out = [gu.empty_like_sentinel(n * 7000, "int32") for _ in range(n)]
+        gu.note("group: in-place AllReduces with ReduceScatter and AllGather")
+        with B.Group():
+            comm.allreduce(a, a, "sum")
+            comm.reduce_scatter(rs_in, rs_out, "sum")
+            comm.allreduce(b, b, "sum")
+            comm.all_gather(ag_in, ag_out)
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arSuccess
+        for i, (xs, bufs) in enumerate(((xa, a), (xb, b))):
+            plan = comm.group_plan(0 if i == 0 else 2)
+            want = gu.expected(xs, "float32", "sum", plan)
+            for r in range(n):
+                gu.assert_bits_equal(gu.to_host_raw(bufs[r], "float32"), want, "float32", "in-place %d rank %d" % (i, r))
+        assert comm.group_plan(1)["tasksInLaunch"] == 1 and comm.group_plan(3)["tasksInLaunch"] == 1
+        want_rs = orc.reduce_scatter(xr, "float32", "sum")
+        want_ag = orc.all_gather(xg, "int32")
+        for r in range(n):
+            gu.assert_bits_equal(gu.to_host_raw(rs_out[r], "float32"), want_rs[r], "float32", "RS rank %d" % r)
+            gu.assert_bits_equal(gu.to_host_raw(ag_out[r], "int32"), want_ag[r], "int32", "AG rank %d" % r)
+
+
+def test_group_error_launches_nothing(B, gu):
+    n = 4
+    with B.Comm(n, 2, "simple") as comm:
+        good_in = [torch.ones(1000, device="cuda") for _ in range(n)]
+        good_out = [gu.empty_like_sentinel(1000, "float32") for _ in range(n)]
+        shared = torch.zeros(1000, device="cuda")
+        gu.note("group with a bad call")
+        B.arGroupStart()
+        comm.allreduce(good_in, good_out, "sum")
+        with pytest.raises(B.ArError):
+            comm.allreduce(good_in, [shared] * n, "sum")          # outputs overlap: refused
+        with pytest.raises(B.ArError) as e:
+            B.arGroupEnd()
+        assert e.value.code == B.arInvalidArgument
+        torch.cuda.synchronize()
+        assert all(torch.isnan(o).all() for o in good_out)        # still the sentinel
+        # the comm is fine afterwards
+        gu.parity_case(n, 5000, "float32", "sum", "simple", 2, comm=comm)
+
+
+def test_group_stream_mismatch(B, gu):
+    n = 4
+    with B.Comm(n, 2, "simple") as comm:
+        x = [torch.ones(100, device="cuda") for _ in range(n)]
+        y = [torch.ones(100, device="cuda") for _ in range(n)]
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        B.arGroupStart()
+        comm.allreduce(x, x, "sum", stream=s1)
+        with pytest.raises(B.ArError) as e:
+            comm.allreduce(y, y, "sum", stream=s2)
+        assert e.value.code == B.arInvalidUsage
+        with pytest.raises(B.ArError):
+            B.arGroupEnd()
+        torch.cuda.synchronize()
+
+
+def test_group_two_comms_and_nesting(B, gu):
+    from ring_allreduce_reduction_amd import inputs as gen
+    with B.Comm(4, 2, "auto", "auto") as c4, B.Comm(8, 4, "ll", "ring") as c8:
+        x4 = gen.make_inputs(4, 9000, "float32", seed=5)
+        x8 = gen.make_inputs(8, 9000, "float32", seed=6)
+        d4 = [gu.to_device(x, "float32") for x in x4]
+        d8 = [gu.to_device(x, "float32") for x in x8]
+        gu.note("nested group over two comms")
+        with B.Group():
+            c4.allreduce(d4, d4, "sum")
+            with B.Group():
+                c8.allreduce(d8, d8, "sum")
+            torch.cuda.synchronize()
+            assert torch.equal(d8[0].cpu(), torch.from_numpy(x8[0]))   # inner end launched nothing
+        torch.cuda.synchronize()
+        for comm, xs, d in ((c4, x4, d4), (c8, x8, d8)):
+            want = gu.expected(xs, "float32", "sum", comm.group_plan(0))
+            for r in range(comm.nranks):
+                gu.assert_bits_equal(gu.to_host_raw(d[r], "float32"), want, "float32", "rank %d" % r)
+
+
+def test_group_many_small_one_launch(B, gu):
+    with B.Comm(8, 4, "simple", "ring") as comm:
+        plans = run_group(B, gu, comm, [(1024 + 16 * i, "float32", "sum", False, i) for i in range(48)], "48 small")
+    assert {p["tasksInLaunch"] for p in plans} == {48}
+
+
+def test_groups_in_a_row_then_single_calls(B, gu):
+    # the task table grows and is reused; counters stay consistent afterwards
+    with B.Comm(8, 8, "auto", "auto") as comm:
+        for g in range(6):
+            run_group(B, gu, comm, [(2000 * (g + 1) + 7 * i, "float32", "sum", False, g * 100 + i)
+                                    for i in range(4 + 20 * g)], "row %d" % g)
+        for proto in ("ll", "ll128", "simple"):
+            gu.parity_case(8, 33333, "float32", "sum", proto, 4, comm=comm)
+
+
+def test_group_one_rank(B, gu):
+    with B.Comm(1, 2, "auto") as comm:
+        run_group(B, gu, comm, [(1000, "float32", "sum", False, 1), (77, "int32", "max", True, 2)], "one rank")
+
+
+def test_destroy_refused_in_group(B):
+    comm = B.Comm(4, 2, "simple")
+    x = [torch.ones(100, device="cuda") for _ in range(4)]
+    B.arGroupStart()
+    comm.allreduce(x, x, "sum")
+    assert B.lib().arDestroy(comm.handle) == B.arInvalidUsage
+    B.arGroupEnd()
+    torch.cuda.synchronize()
+    comm.close()
+
+
+def test_groups_back_to_back_without_sync(B, gu):
+    # tables of many groups in flight at once (the host does not wait between
+    # groups); every call checked at the end
+    from ring_allreduce_reduction_amd import inputs as gen
+    n = 8
+    with B.Comm(n, 4, "auto", "auto") as comm:
+        groups = []
+        gu.note("12 groups back to back")
+        for g in range(12):
+            calls = []
+            with B.Group():
+                for i in range(3 + g % 5):
+                    count = 3000 + 97 * g + 13 * i
+                    xs = gen.make_inputs(n, count, "float32", seed=1000 * g + i)
+                    d = [gu.to_device(x, "float32") for x in xs]
+                    comm.allreduce(d, d, "sum")
+                    calls.append((xs, d))
+            groups.append((calls, [comm.group_plan(i) for i in range(len(calls))]))
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arSuccess
+        for g, (calls, plans) in enumerate(groups):
+            for i, ((xs, d), plan) in enumerate(zip(calls, plans)):
+                want = gu.expected(xs, "float32", "sum", plan)
+                for r in range(n):
+                    gu.assert_bits_equal(gu.to_host_raw(d[r], "float32"), want, "float32",
+                                         "group %d call %d rank %d" % (g, i, r))
