@@ -42,11 +42,15 @@ def parse():
     ap.add_argument("--count", type=int, default=64 << 20, help="elements per rank")
     ap.add_argument("--dtype", default="float32")
     ap.add_argument("--proto", default="auto")
+    ap.add_argument("--op", default="sum", choices=["sum", "max", "min"])
     ap.add_argument("--algo", default="ring", choices=["ring", "tree", "auto"],
                     help="AllReduce algorithm (the headline metric is the ring's)")
     ap.add_argument("--nchannels", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw the inputs on the GPU (same distributions, torch's generator) instead of the host "
+                         "generator; for timing large configurations (no CPU baseline then)")
     ap.add_argument("--sweep", action="store_true", help="8B..256MiB sweep, every protocol + auto")
     ap.add_argument("--sweep-max-log2", type=int, default=28)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
@@ -104,18 +108,34 @@ def main():
     N, count, dtype = args.nranks, args.count, args.dtype
     esz = gen.ELEM_SIZE[dtype]
     S = count * esz
-    log("generating inputs: %d ranks x %d %s (seed %d)" % (N, count, dtype, args.seed))
-    t0 = time.perf_counter()
-    xs = gen.make_inputs(N, count, dtype, seed=args.seed)
-    log("inputs ready in %.1fs; uploading" % (time.perf_counter() - t0))
     tdt = {"float32": torch.float32, "int32": torch.int32, "float16": torch.float16,
            "bfloat16": torch.bfloat16}[dtype]
     sends, recvs = [], []
-    for x in xs:
-        h = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x)
-        d = h.to("cuda")
-        sends.append(d.view(tdt) if d.dtype != tdt else d)
-        recvs.append(torch.empty_like(sends[-1]))
+    if args.device_inputs:
+        # the configurations' distributions: fp32 uniform[-1,1], 16-bit floats
+        # normal(0,1) rounded to nearest-even, int32 uniform[-2^20, 2^20]
+        log("drawing inputs on the GPU: %d ranks x %d %s (seed %d)" % (N, count, dtype, args.seed))
+        xs = None
+        for r in range(N):
+            g = torch.Generator("cuda").manual_seed(args.seed * 1000 + r)
+            if dtype == "float32":
+                d = torch.rand(count, generator=g, device="cuda") * 2 - 1
+            elif dtype == "int32":
+                d = torch.randint(-(1 << 20), (1 << 20) + 1, (count,), generator=g, device="cuda", dtype=torch.int32)
+            else:
+                d = torch.randn(count, generator=g, device="cuda").to(tdt)
+            sends.append(d)
+            recvs.append(torch.empty_like(d))
+    else:
+        log("generating inputs: %d ranks x %d %s (seed %d)" % (N, count, dtype, args.seed))
+        t0 = time.perf_counter()
+        xs = gen.make_inputs(N, count, dtype, seed=args.seed)
+        log("inputs ready in %.1fs; uploading" % (time.perf_counter() - t0))
+        for x in xs:
+            h = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x)
+            d = h.to("cuda")
+            sends.append(d.view(tdt) if d.dtype != tdt else d)
+            recvs.append(torch.empty_like(sends[-1]))
     torch.cuda.synchronize()
 
     comm = B.Comm(N, args.nchannels, args.proto, args.algo)
@@ -129,7 +149,7 @@ def main():
     dt_code = B.DTYPE_BY_NAME[dtype]
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
-            comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=dt_code)
+            comm.allreduce(sends, recvs, B.OP_BY_NAME[args.op], stream=stream, count=count, dtype=dt_code)
         torch.cuda.synchronize()
         err = comm.async_error()
         if err != B.arSuccess:
@@ -141,7 +161,7 @@ def main():
         w0 = time.perf_counter()
         for a, b in evs:
             a.record(stream)
-            comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=dt_code)
+            comm.allreduce(sends, recvs, B.OP_BY_NAME[args.op], stream=stream, count=count, dtype=dt_code)
             b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
@@ -162,9 +182,10 @@ def main():
     # within the fp32 bound of a float64 direct sum computed by torch
     same = all(torch.equal(recvs[0].view(torch.uint8), r.view(torch.uint8)) for r in recvs[1:])
     idx = torch.randint(0, count, (100000,), device="cuda", generator=torch.Generator("cuda").manual_seed(1))
-    s64 = sum(x[idx].double() for x in sends)
-    err_max = (recvs[0][idx].double() - s64).abs().max().item()
-    log("all ranks identical: %s; sample max |err| vs float64 = %.3g" % (same, err_max))
+    vals = torch.stack([x[idx].double() for x in sends])
+    ref = vals.sum(0) if args.op == "sum" else vals.max(0).values if args.op == "max" else vals.min(0).values
+    err_max = (recvs[0][idx].double() - ref).abs().max().item()
+    log("all ranks identical: %s; sample max |err| vs float64 %s = %.3g" % (same, args.op, err_max))
 
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -180,12 +201,13 @@ def main():
         except Exception as e:  # a stale or partial file must not break the bench
             log("traffic file unreadable: %s" % e)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(xs, dtype, plan, N, S, B)
+    cpu = None if (args.no_cpu_baseline or xs is None) else cpu_baseline(xs, dtype, plan, N, S, B)
     comm.close()
 
     algo = B.ALGO_NAMES[plan["algo"]]
     out = {
-        "metric": ("emulated ring AllReduce busbw GB/s + % HBM peak, 8 ranks x 256 MiB fp32" if algo == "ring"
+        "metric": ("emulated ring AllReduce busbw GB/s + % HBM peak, 8 ranks x 256 MiB fp32"
+                   if (algo, N, S, dtype, args.op) == ("ring", 8, 256 << 20, "float32", "sum")
                    else "emulated %s AllReduce busbw GB/s + %% HBM peak" % algo),
         "value": round(busbw, 3),
         "unit": "GB/s",
@@ -197,9 +219,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"float32": "f32", "bfloat16": "bf16", "float16": "f16", "int32": "i32"}[dtype],
-        "data": "synthetic",
-        "config": {"workload": "%s AllReduce Sum, %d virtual ranks x %d MiB %s per rank on one GPU"
-                               % (algo, N, S >> 20, dtype), "algo": algo,
+        "data": "synthetic" + (" (drawn on the GPU)" if xs is None else ""),
+        "config": {"workload": "%s AllReduce %s, %d virtual ranks x %d MiB %s per rank on one GPU"
+                               % (algo, args.op.capitalize(), N, S >> 20, dtype), "algo": algo,
                    "nranks": N, "count_per_rank": count, "bytes_per_rank": S,
                    "proto": B.PROTO_NAMES[plan["proto"]], "nChannels": plan["nChannels"],
                    "chunkElems": plan["chunkElems"], "lanesPerChannel": plan["lanesPerChannel"],

@@ -24,8 +24,9 @@ def kernels():
     if not all(t and os.path.exists(t) for t in tools):
         pytest.skip("ROCm toolchain not found")
     with tempfile.TemporaryDirectory() as d:
-        fat, co = os.path.join(d, "fatbin"), os.path.join(d, "gfx950.co")
-        subprocess.run([tools[0], "--dump-section", ".hip_fatbin=" + fat, lib], check=True)
+        fat, co, copy = os.path.join(d, "fatbin"), os.path.join(d, "gfx950.co"), os.path.join(d, "lib.copy")
+        # an explicit output file: without one objcopy rewrites its input in place
+        subprocess.run([tools[0], "--dump-section", ".hip_fatbin=" + fat, lib, copy], check=True)
         subprocess.run([tools[1], "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--input=" + fat,
                         "--output=" + co, "--unbundle"], check=True)
         notes = subprocess.run([tools[2], "--notes", co], check=True, capture_output=True, text=True).stdout
