@@ -306,9 +306,10 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   plan->predictedUs = predicted;
 
   // Members per workgroup: the whole ring when it fits (N <= 16).  Longer
-  // rings are cut into balanced groups joined by agent-scope edges; the
+  // rings are cut into balanced groups joined by device-coherent edges; the
   // launch is then cooperative, so the largest group size whose grid (one
-  // lane per channel at least) is co-resident is taken.
+  // lane per channel at least) is co-resident is taken, with Simple slots of
+  // at most 4 KiB.
   auto layout = [&](int gs, int* nGroupsOut, int* gsOut) {
     int ng = (N + gs - 1) / gs;
     *nGroupsOut = ng;
@@ -319,7 +320,9 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   int nGroups = 1, groupSize = N;
   if (N > kMaxMembersPerGroup) {
     bool found = false;
-    for (int u = plan->unroll; u >= 1 && !found; u /= 2) {
+    const int u0 = proto == kSimple && plan->unroll > kGroupedSimpleUnrollMax ? kGroupedSimpleUnrollMax
+                                                                               : plan->unroll;
+    for (int u = u0; u >= 1 && !found; u /= 2) {
       if (proto == kSimple) {
         plan->unroll = u;
         plan->slotBytes = slotBytesOf(proto, u);

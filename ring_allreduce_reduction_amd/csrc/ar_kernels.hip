@@ -18,8 +18,9 @@
 // the FIFO handoff needs only workgroup-scope release/acquire, which on gfx950
 // is a plain ordered store / load, and there is no cross-workgroup wait at all
 // (no co-residency requirement, no deadlock from scheduling).  For N > 16 the
-// ring is cut into groups of up to 16 members; an edge between groups uses
-// agent-scope release/acquire and the launch is cooperative so that every
+// ring is cut into groups of up to 16 members; an edge between groups moves
+// its bytes with device-coherent loads and stores (no L2-wide cache
+// maintenance, see releaseEdge) and the launch is cooperative so that every
 // group is resident.
 //
 // Each member reads only its own send buffer, writes only its own receive
@@ -199,10 +200,6 @@ __device__ __forceinline__ u64 ldCounter(const u64* p, bool agent) {
   u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
   return ((u64)hi << 32) | lo;
 }
-__device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
-  if (agent) __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  else __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 __device__ __forceinline__ void stRelaxed64(u64* p, u64 v, bool agent) {
   if (agent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -211,13 +208,64 @@ __device__ __forceinline__ u64 ldRelaxed64(const u64* p, bool agent) {
   return agent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void fenceAcquire(bool agent) {
-  if (agent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+// Edges inside a workgroup order their payload with workgroup-scope
+// release/acquire, which gfx950 compiles to ordered loads and stores with no
+// cache maintenance.
+//
+// Edges between workgroups never use agent-scope fences: on gfx950 an
+// agent-scope release writes back, and an acquire invalidates, the whole L2
+// of the XCD (buffer_wbl2 sc1 / buffer_inv sc1), which at every ring step
+// stalls every wavefront on that XCD.  Instead every byte that crosses such
+// an edge -- slot payload, LL words, LL128 flags, counters -- is moved by a
+// relaxed agent-scope atomic, which gfx950 issues as a plain load or store
+// with the sc1 bit: it is served at the device's coherence point rather than
+// by one XCD's L2, so it is coherent on its own.  What a release adds on top
+// is order: the producer waits until its payload stores have completed
+// (vmcnt(0)) before it stores the counter or flag that publishes them.  On
+// the consumer the payload loads are issued only after the counter or flag
+// read has returned the awaited value, as every wait loop branches on it.
+__device__ __forceinline__ void stCoh16(char* p, v4u v) {
+  __hip_atomic_store((u64*)p, ((u64)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((u64*)p + 1, ((u64)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fenceRelease(bool agent) {
-  if (agent) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+__device__ __forceinline__ void stCoh8(char* p, v2u v) {
+  __hip_atomic_store((u64*)p, ((u64)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ v4u ldCoh16(const char* p) {
+  const u64 a = __hip_atomic_load((const u64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u64 b = __hip_atomic_load((const u64*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v4u{(u32)a, (u32)(a >> 32), (u32)b, (u32)(b >> 32)};
+}
+__device__ __forceinline__ v2u ldCoh8(const char* p) {
+  const u64 a = __hip_atomic_load((const u64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v2u{(u32)a, (u32)(a >> 32)};
+}
+
+// Before publishing what this wavefront stored for its peer.  Workgroup
+// edge: a workgroup-scope release.  Agent edge: the release keeps the
+// compiler from sinking the payload stores below the publishing store, and
+// s_waitcnt vmcnt(0) (gfx9 encoding 0x0F70: vmcnt 0, expcnt and lgkmcnt
+// untouched) holds the wavefront until they have completed.
+__device__ __forceinline__ void releaseEdge(bool agent) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (agent) __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+// After a counter or flag read returned the awaited value, before touching
+// what it publishes (or, for a credit, before overwriting the slot).  Both
+// kinds of edge need only the compiler ordering of a workgroup-scope acquire:
+// an agent edge's payload loads are device-coherent by themselves.
+__device__ __forceinline__ void acquireEdge() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
+
+// Credit: the receiver has drained a slot.  Its loads of the slot returned
+// before this point (their values were used by the stores that precede it).
+__device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
+  if (agent) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    stRelaxed64(p, v, true);
+  } else {
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 }
 
 // Bounded waiting.  Every spin sleeps briefly; every 256 spins the abort word
@@ -294,7 +342,7 @@ __device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
   } else if (!waitGeq(a, &m.succ->head, need, m.sendAgent)) {
     return false;
   }
-  fenceAcquire(m.sendAgent);
+  acquireEdge();
   return true;
 }
 
@@ -324,8 +372,10 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
   // FIFO, so the all-gather half moves no FIFO bytes; the receiver then
   // reads the finished chunk from its own output.  [The pages' FIFO slot
   // descriptor can carry a pointer, and a work item can be flagged direct.]
-  const bool directSend = PROTO == kSimple && m.direct && hasSend && hasOut;
-  const bool directRecv = PROTO == kSimple && m.direct && hasRecv && hasOut && !hasLocal;
+  // An edge between workgroups always goes through the FIFO (both of its
+  // ends see the same sendAgent / recvAgent, so they agree on it).
+  const bool directSend = PROTO == kSimple && m.direct && !m.sendAgent && hasSend && hasOut;
+  const bool directRecv = PROTO == kSimple && m.direct && !m.recvAgent && hasRecv && hasOut && !hasLocal;
   const int lane = m.lane;
 
   // piece geometry of this lane: payload offset, payload bytes, wire offset
@@ -365,7 +415,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
     v4u in[U];
     if (PROTO == kSimple) {
       if (!waitGeq(a, &m.self->tail, m.recvStep + 1, m.recvAgent)) return false;
-      fenceAcquire(m.recvAgent);
+      acquireEdge();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (directRecv)   // the predecessor wrote it into my output
@@ -373,7 +423,8 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
                       ? loadUser<ESZ, false>(outp + payOff[u], valid - payOff[u], 16, m.aligned)
                       : v4u{0u, 0u, 0u, 0u};
         else
-          in[u] = payOff[u] < valid ? *(const v4u*)(slot + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+          in[u] = payOff[u] < valid ? (m.recvAgent ? ldCoh16(slot + wireOff[u]) : *(const v4u*)(slot + wireOff[u]))
+                                    : v4u{0u, 0u, 0u, 0u};
       }
     } else if (PROTO == kLL) {
       const u32 flag = (u32)(m.recvStep + 1);
@@ -418,15 +469,15 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
         if (__all(all)) break;
         if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
       }
-      fenceAcquire(m.recvAgent);
+      acquireEdge();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         in[u] = v4u{0u, 0u, 0u, 0u};
         if (u * kLL128UnitPayload < valid) {
           if (payBytes[u] == 16) {
-            in[u] = *(const v4u*)(slot + wireOff[u]);
+            in[u] = m.recvAgent ? ldCoh16(slot + wireOff[u]) : *(const v4u*)(slot + wireOff[u]);
           } else {
-            v2u t = *(const v2u*)(slot + wireOff[u]);
+            v2u t = m.recvAgent ? ldCoh8(slot + wireOff[u]) : *(const v2u*)(slot + wireOff[u]);
             in[u].x = t.x; in[u].y = t.y;
           }
         }
@@ -450,12 +501,16 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
 #pragma unroll
         for (int u = 0; u < U; ++u)
           storeUser<ESZ, false>(succOutp + payOff[u], v[u], valid - payOff[u], 16, m.aligned);
+      } else if (m.sendAgent) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (payOff[u] < valid) stCoh16(slot + wireOff[u], v[u]);
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u)
           if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
       }
-      fenceRelease(m.sendAgent);
+      releaseEdge(m.sendAgent);
       if (lane == 0) stRelaxed64(&m.succ->tail, m.sendStep + 1, m.sendAgent);
     } else if (PROTO == kLL) {
       const u64 flag = (u64)(u32)(m.sendStep + 1) << 32;
@@ -473,14 +528,16 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
       for (int u = 0; u < U; ++u) {
         if (u * kLL128UnitPayload < valid) {
           if (payBytes[u] == 16) {
-            *(v4u*)(slot + wireOff[u]) = v[u];
+            if (m.sendAgent) stCoh16(slot + wireOff[u], v[u]);
+            else *(v4u*)(slot + wireOff[u]) = v[u];
           } else {
             v2u t; t.x = v[u].x; t.y = v[u].y;
-            *(v2u*)(slot + wireOff[u]) = t;
+            if (m.sendAgent) stCoh8(slot + wireOff[u], t);
+            else *(v2u*)(slot + wireOff[u]) = t;
           }
         }
       }
-      fenceRelease(m.sendAgent);
+      releaseEdge(m.sendAgent);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (flagLane && u * kLL128UnitPayload < valid)
@@ -616,7 +673,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
 // steps simply continue from one task to the next.
 template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: member state stays in SGPRs
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
   const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
@@ -649,8 +706,12 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   m.sfifo = a.fifo + wSucc * a.fifoWorkerBytes;
   m.self = a.conn + wSelf;
   m.succ = a.conn + wSucc;
-  m.recvAgent = pred / a.groupSize != g;
-  m.sendAgent = succ / a.groupSize != g;
+  // The 8 KiB Simple kernel serves single-workgroup rings only (the host
+  // never plans it for a ring cut into groups), so it carries no code for
+  // edges between workgroups.
+  constexpr bool GROUPED = PROTO != kSimple || U <= kGroupedSimpleUnrollMax;
+  m.recvAgent = GROUPED && pred / a.groupSize != g;
+  m.sendAgent = GROUPED && succ / a.groupSize != g;
   m.aligned = a.aligned16 != 0;
   m.direct = a.direct != 0;
   // counters carry over from earlier calls (tail == head at call boundaries)
@@ -786,10 +847,12 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
   const char* slot = e.fifo + (size_t)e.slot * SLOT;
   if (PROTO == kSimple) {
     if (!waitGeq(a, &e.conn->tail, e.step + 1, e.agent)) return false;
-    fenceAcquire(e.agent);
+    acquireEdge();
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      in[u] = pc.payOff[u] < valid ? *(const v4u*)(slot + pc.wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+      in[u] = pc.payOff[u] >= valid ? v4u{0u, 0u, 0u, 0u}
+              : e.agent            ? ldCoh16(slot + pc.wireOff[u])
+                                   : *(const v4u*)(slot + pc.wireOff[u]);
   } else if (PROTO == kLL) {
     const u32 flag = (u32)(e.step + 1);
     bool done[U];
@@ -833,15 +896,15 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
       if (__all(all)) break;
       if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
     }
-    fenceAcquire(e.agent);
+    acquireEdge();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       in[u] = v4u{0u, 0u, 0u, 0u};
       if (u * kLL128UnitPayload < valid) {
         if (pc.payBytes[u] == 16) {
-          in[u] = *(const v4u*)(slot + pc.wireOff[u]);
+          in[u] = e.agent ? ldCoh16(slot + pc.wireOff[u]) : *(const v4u*)(slot + pc.wireOff[u]);
         } else {
-          const v2u t = *(const v2u*)(slot + pc.wireOff[u]);
+          const v2u t = e.agent ? ldCoh8(slot + pc.wireOff[u]) : *(const v2u*)(slot + pc.wireOff[u]);
           in[u].x = t.x; in[u].y = t.y;
         }
       }
@@ -863,13 +926,17 @@ __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pie
   // slot step % nSlots is free once the receiver consumed step - nSlots
   const u64 need = e.step + 1 > (u64)a.nSlots ? e.step + 1 - (u64)a.nSlots : 0;
   if (!waitGeq(a, &e.conn->head, need, e.agent)) return false;
-  fenceAcquire(e.agent);
+  acquireEdge();
   char* slot = e.fifo + (size_t)e.slot * SLOT;
   if (PROTO == kSimple) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (pc.payOff[u] < valid) *(v4u*)(slot + pc.wireOff[u]) = v[u];
-    fenceRelease(e.agent);
+    for (int u = 0; u < U; ++u) {
+      if (pc.payOff[u] < valid) {
+        if (e.agent) stCoh16(slot + pc.wireOff[u], v[u]);
+        else *(v4u*)(slot + pc.wireOff[u]) = v[u];
+      }
+    }
+    releaseEdge(e.agent);
     if (lane == 0) stRelaxed64(&e.conn->tail, e.step + 1, e.agent);
   } else if (PROTO == kLL) {
     const u64 flag = (u64)(u32)(e.step + 1) << 32;
@@ -887,14 +954,16 @@ __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pie
     for (int u = 0; u < U; ++u) {
       if (u * kLL128UnitPayload < valid) {
         if (pc.payBytes[u] == 16) {
-          *(v4u*)(slot + pc.wireOff[u]) = v[u];
+          if (e.agent) stCoh16(slot + pc.wireOff[u], v[u]);
+          else *(v4u*)(slot + pc.wireOff[u]) = v[u];
         } else {
           v2u t; t.x = v[u].x; t.y = v[u].y;
-          *(v2u*)(slot + pc.wireOff[u]) = t;
+          if (e.agent) stCoh8(slot + pc.wireOff[u], t);
+          else *(v2u*)(slot + pc.wireOff[u]) = t;
         }
       }
     }
-    fenceRelease(e.agent);
+    releaseEdge(e.agent);
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (flagLane && u * kLL128UnitPayload < valid)
@@ -998,7 +1067,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
 // of them at once.
 template <int PROTO, int DT, int OP, int U, bool BATCH>
 __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: member state stays in SGPRs
   const int lane = threadIdx.x % kWave;
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
@@ -1167,6 +1236,8 @@ KernelFn pickKernel(const Plan& plan, int coll, int dtype, int op, bool batch) {
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream) {
   KernelFn fn = pickKernel(plan, args.coll, dtype, op, args.nTasks > 0);
   if (fn == nullptr) return hipErrorInvalidValue;
+  if (plan.nGroups > 1 && plan.proto == kSimple && plan.unroll > kGroupedSimpleUnrollMax)
+    return hipErrorInvalidValue;   // that kernel has no cross-workgroup edges
   if (plan.cooperative) {
     void* params[] = {(void*)&args};
     return hipLaunchCooperativeKernel((const void*)fn, dim3(plan.grid), dim3(plan.block), params, 0, stream);
