@@ -491,24 +491,28 @@ def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):
 
 def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
     """Time a grid of configurations in one process:
-    --explore 'channels:lanes[:slotKiB[:direct[:depth]]]', each a comma list
-    (lanes 0 = automatic, depth 0 = the protocol's default)."""
+    --explore 'channels:lanes[:slotKiB[:direct[:depth[:sets]]]]', each a comma list
+    (lanes 0 = automatic, depth 0 = the protocol's default, sets 0 = one
+    workgroup per (channel, lane), else at most that many workgroups)."""
     parts = args.explore.split(":")
-    parts += ["8", "1", "0"][len(parts) - 2:]
-    chs, lanes, slots, directs, depths = [[int(x) for x in p.split(",")] for p in parts[:5]]
-    grid = [(a, b, c, e, f) for a in chs for b in lanes for c in slots for e in directs for f in depths]
-    for nch, ln, sk, d, dp in grid:
+    parts += ["8", "1", "0", "0"][len(parts) - 2:]
+    chs, lanes, slots, directs, depths, setss = [[int(x) for x in p.split(",")] for p in parts[:6]]
+    grid = [(a, b, c, e, f, h) for a in chs for b in lanes for c in slots for e in directs for f in depths
+            for h in setss]
+    for nch, ln, sk, d, dp, st in grid:
         if dp:
             B.arSetDebug(comm.handle, B.arDebugSlots, dp)
         comm.set_config("simple" if args.proto == "auto" else args.proto, nch)
         B.arSetDebug(comm.handle, B.arDebugLanes, ln)
         B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
         B.arSetDebug(comm.handle, B.arDebugDirect, d)
+        B.arSetDebug(comm.handle, B.arDebugLaneSets, st)
         plan = comm.plan(count, dtype)
         ms = time_calls(B, torch, comm, sends, recvs, count, B.DTYPE_BY_NAME[dtype], 2, args.steps)
         frac = 5.0 * (N - 1) * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
         print(json.dumps({"nch": nch, "lanes": plan["lanesPerChannel"], "slotKiB": sk, "direct": d,
-                          "depth": plan["nSlots"], "grid": plan["workgroups"], "block": plan["threadsPerGroup"],
+                          "depth": plan["nSlots"], "sets": st, "grid": plan["workgroups"],
+                          "block": plan["threadsPerGroup"],
                           "ms": round(ms, 4), "busbw": round(S / (ms / 1e3) / 1e9 * 2 * (N - 1) / N, 2),
                           "frac": round(frac, 4)}), flush=True)
     comm.close()

@@ -318,6 +318,9 @@ typedef enum {
   arDebugDirect = 4,     /* 1: Simple all-gather writes the successor's output
                             directly (default); 0: through the FIFO */
   arDebugSlots = 5,      /* FIFO depth in slots for every protocol, 2..8 */
+  arDebugLaneSets = 6,   /* single-workgroup rings, single calls: at most this many workgroups,
+                            each running several (channel, lane) pairs in turn on one FIFO set;
+                            0 = one workgroup per pair */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 

@@ -163,6 +163,7 @@ struct arComm {
   int64_t timeoutUs;
   int deadRank;
   int forcedLanes;      // 0: automatic
+  int laneSetsMax;      // 0: one workgroup per (channel, lane); else at most this many FIFO sets
   int simpleUnroll;     // Simple slot size in KiB (1, 2, 4)
   bool direct;          // Simple all-gather writes outputs directly
   hipStream_t lastStream;
@@ -418,6 +419,11 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   plan->taskSlots = slots;
   plan->lanes = lanes;
   plan->grid = gridFor(lanes * slots);
+  plan->laneSets = nch * lanes;
+  if (!batch && nGroups == 1 && c->laneSetsMax > 0 && c->laneSetsMax < plan->laneSets) {
+    plan->laneSets = c->laneSetsMax;
+    plan->grid = plan->laneSets;
+  }
   return arSuccess;
 }
 
@@ -555,6 +561,11 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
     for (int p = 0; p < 3; ++p) c->nSlots[p] = (int)value;
     return arSuccess;
   }
+  if (knob == arDebugLaneSets) {
+    if (value < 0 || value > c->lanesMax) return arInvalidArgument;
+    c->laneSetsMax = (int)value;
+    return arSuccess;
+  }
   if (knob == arDebugDirect) {
     if (value != 0 && value != 1) return arInvalidArgument;
     c->direct = value != 0;
@@ -672,6 +683,7 @@ void buildArgs(const arComm* c, const Plan& plan, int func, size_t count, const 
   a->coll = func;
   a->deadRank = c->deadRank;
   a->taskSlots = 1;
+  a->laneSets = plan.laneSets;
 }
 
 // One collective call: argument checks (nothing is enqueued on failure), the

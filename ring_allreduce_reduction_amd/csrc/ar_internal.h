@@ -105,6 +105,8 @@ struct KernelArgs {
   const uint64_t* tasks;
   int nTasks;
   int taskSlots;              // tasks in flight at once (each on nChannels x lanes wavefront sets)
+  int laneSets;               // single call: workgroup FIFO sets (<= nChannels x lanes); set L runs
+                              // (channel, lane) pairs L, L + laneSets, ...
 };
 
 // Everything arAllReduce decides for one call.
@@ -123,6 +125,7 @@ struct Plan {
   int nSlots;
   int unroll;                 // pieces per lane per slot
   int taskSlots;              // batched launches: collectives running at once
+  int laneSets;               // single-group single call: FIFO sets the grid runs (see KernelArgs)
   bool direct;
   bool cooperative;
   float predictedUs;

@@ -678,9 +678,9 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   const int perTask = a.nChannels * a.lanes;
   const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
 
-  // Workgroup -> (lane id, group).  With several groups per lane, the groups
-  // of one lane get workgroup ids congruent mod 8, i.e. the same XCD under
-  // round-robin dispatch, so their cross-workgroup edges stay in one L2.
+  // Workgroup -> (FIFO set L, group).  With several groups per lane, the
+  // groups of one lane get workgroup ids congruent mod 8, i.e. the same XCD
+  // under round-robin dispatch, so their cross-workgroup edges stay in one L2.
   int L, g;
   if (a.nGroups == 1) {
     L = blockIdx.x;
@@ -690,12 +690,13 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
     g = (blockIdx.x / 8) % a.nGroups;
     L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
   }
-  if (L >= lanesTotal) return;
+  // A single call's workgroups may be fewer than its (channel, lane) pairs:
+  // set L then runs pairs L, L + sets, L + 2 sets, ... on the same FIFOs,
+  // whose steps simply continue from one pair to the next.
+  const int sets = BATCH ? lanesTotal : a.laneSets;
+  if (L >= sets) return;
   const int r = g * a.groupSize + wave;
   if (r >= N || r == a.deadRank) return;
-  const int Lc = BATCH ? L % perTask : L;   // (channel, lane) inside the task
-  const int ch = Lc / a.lanes;
-  const int k = Lc % a.lanes;
   const int succ = r + 1 == N ? 0 : r + 1;
   const int pred = r == 0 ? N - 1 : r - 1;
 
@@ -722,10 +723,15 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
 
   if (!BATCH) {
-    if (!ringPass<PROTO, DT, OP, U, COLL>(a, m, r, ch, k, a.count, (const char*)a.send[r], (char*)a.recv[r],
-                                          (char*)a.recv[succ]))
-      return;
+    for (int Lp = L; Lp < lanesTotal; Lp += sets) {
+      if (!ringPass<PROTO, DT, OP, U, COLL>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count, (const char*)a.send[r],
+                                            (char*)a.recv[r], (char*)a.recv[succ]))
+        return;
+    }
   } else {
+    const int Lc = L % perTask;   // (channel, lane) inside the task
+    const int ch = Lc / a.lanes;
+    const int k = Lc % a.lanes;
     const size_t row = 1 + 2 * (size_t)N;
     for (int t = L / perTask; t < a.nTasks; t += a.taskSlots) {
       const u64* d = a.tasks + (size_t)t * row;

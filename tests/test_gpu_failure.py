@@ -70,7 +70,8 @@ def test_debug_knob_validation(B):
     with B.Comm(4, 2, "simple") as comm:
         for knob, bad in [(B.arDebugTimeoutUs, 0), (B.arDebugDeadRank, 4), (B.arDebugDeadRank, -2),
                           (B.arDebugSimpleSlotKiB, 3), (B.arDebugDirect, 2), (B.arDebugSlots, 1),
-                          (B.arDebugSlots, 9), (99, 1)]:
+                          (B.arDebugSlots, 9), (B.arDebugLaneSets, -1), (B.arDebugLaneSets, 1 << 20),
+                          (99, 1)]:
             with pytest.raises(B.ArError):
                 B.arSetDebug(comm.handle, knob, bad)
         with pytest.raises(B.ArError):

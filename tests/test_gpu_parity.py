@@ -111,6 +111,22 @@ def test_simple_slot_and_direct_variants(B, gu, slot_kib, direct):
         gu.parity_case(5, 77777, "int32", "max", "simple", 3, seed=2, comm=None)
 
 
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("sets", [1, 3, 7])
+def test_workgroups_running_several_lanes(B, gu, proto, sets):
+    # fewer workgroups than (channel, lane) pairs: workgroup L runs pairs
+    # L, L + sets, ... on one FIFO set, its steps continuing across pairs
+    with B.Comm(8, 16, proto) as comm:
+        B.arSetDebug(comm.handle, B.arDebugLaneSets, sets)
+        for count, nch in [(300007, 5), (1 << 20, 16), (4099, 2)]:
+            plan, _, _ = gu.parity_case(8, count, "float32", "sum", proto, nch, seed=count + sets, comm=comm)
+            assert plan["workgroups"] <= sets
+        gu.parity_case(8, 100003, "bfloat16", "sum", proto, 4, seed=sets, comm=comm, inplace=True)
+        gu.parity_case(8, 3001, "uint64", "probe", proto, 3, comm=comm)
+        B.arSetDebug(comm.handle, B.arDebugLaneSets, 0)
+        gu.parity_case(8, 300007, "float32", "sum", proto, 5, seed=9, comm=comm)
+
+
 def test_ll128_needs_128_byte_alignment(B, gu):
     from ring_allreduce_reduction_amd import inputs as gen
     xs = gen.make_inputs(4, 1000, "float32")

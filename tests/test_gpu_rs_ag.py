@@ -148,6 +148,15 @@ def test_all_gather_simple_variants(B, gu, orc, direct, slot):
         rs_case(B, gu, orc, 8, 262147, "float32", "sum", "simple", 16, comm=comm)
 
 
+@pytest.mark.parametrize("proto", PROTOS)
+def test_rs_ag_workgroups_running_several_lanes(B, gu, orc, proto):
+    with B.Comm(8, 16, proto) as comm:
+        B.arSetDebug(comm.handle, B.arDebugLaneSets, 3)
+        ag_case(B, gu, orc, 8, 262147, "float32", proto, 16, comm=comm)
+        rs_case(B, gu, orc, 8, 262147, "float32", "sum", proto, 16, comm=comm)
+        rs_case(B, gu, orc, 8, 30001, "bfloat16", "max", proto, 4, comm=comm)
+
+
 def test_all_gather_unaligned(B, gu, orc):
     ag_case(B, gu, orc, 4, 30011, "float32", "simple", 3, offset=1)
     ag_case(B, gu, orc, 4, 3001, "bfloat16", "ll", 3, offset=1)
