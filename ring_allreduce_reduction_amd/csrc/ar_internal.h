@@ -27,12 +27,13 @@ constexpr int kMaxSlots = 8;              // FIFO depth provisioned per worker
 //           seven 16-byte payload pieces, 8 payload bytes and an 8-byte flag.
 constexpr int kSimpleUnrollMax = 8;       // Simple slot = unroll KiB (1, 2, 4 or 8)
 constexpr int kSimpleUnrollDefault = 8;
-constexpr int kBatchSimpleUnrollMax = 4;  // batched ring launches: Simple slot at most 4 KiB
+constexpr int kBatchSimpleUnrollMax = 8;  // batched ring launches: any Simple slot (8 KiB fits in
+                                          // 120 VGPRs with the task loop)
 constexpr int kGroupedSimpleUnrollMax = 4;  // rings cut into several workgroups: Simple slot at most
                                            // 4 KiB (the 8 KiB kernel holds no cross-workgroup edge
                                            // code, which would make it spill)
-constexpr int kTreeSimpleUnrollMax = 2;   // the tree's Simple slot is at most 2 KiB (three slot
-                                          // arrays live per lane: 4 KiB would spill)
+constexpr int kTreeSimpleUnrollMax = 4;   // the tree's Simple slot is at most 4 KiB (three slot
+                                          // arrays live per lane: 8 KiB would spill)
 constexpr int kTreeEdges = 3;             // a tree node's FIFOs: from d0, from d1, from its parent
 constexpr int kLLUnroll = 2;
 constexpr int kLL128Unroll = 2;

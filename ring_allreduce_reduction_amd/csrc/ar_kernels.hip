@@ -1187,8 +1187,8 @@ KernelFn pickTree(int dtype, int op) {
 }
 
 // Protocol and slot size: the ring's Simple slot is 1, 2, 4 or 8 KiB (at
-// most 4 KiB batched), the tree's 1 or 2 KiB; LL and LL128 have one slot
-// geometry each.
+// most 4 KiB for a ring cut into workgroups), the tree's 1, 2 or 4 KiB; LL
+// and LL128 have one slot geometry each.
 template <int COLL, bool BATCH>
 KernelFn pickRingProto(const Plan& plan, int dtype, int op) {
   switch (plan.proto) {
@@ -1199,9 +1199,7 @@ KernelFn pickRingProto(const Plan& plan, int dtype, int op) {
         case 1: return pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
         case 2: return pickRing<kSimple, 2, COLL, BATCH>(dtype, op);
         case 4: return pickRing<kSimple, 4, COLL, BATCH>(dtype, op);
-        case 8:   // batched launches use at most 4 KiB slots (8 KiB spills with the task loop)
-          if constexpr (!BATCH) return pickRing<kSimple, 8, COLL, false>(dtype, op);
-          return nullptr;
+        case 8: return pickRing<kSimple, 8, COLL, BATCH>(dtype, op);
       }
   }
   return nullptr;
@@ -1216,6 +1214,7 @@ KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
       switch (plan.unroll) {
         case 1: return pickTree<kSimple, 1, BATCH>(dtype, op);
         case 2: return pickTree<kSimple, 2, BATCH>(dtype, op);
+        case 4: return pickTree<kSimple, 4, BATCH>(dtype, op);
       }
   }
   return nullptr;
