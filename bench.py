@@ -11,6 +11,9 @@ Reported per step (S = bytes per rank, N = ranks, t = time per step):
   all-gather step reads 1, writes 1; N-1 steps each over N ranks)
   roofline.achieved = modelBytes / t, against the 8 TB/s HBM peak.
 The CPU baseline is the oracle (single-threaded C) on the same inputs.
+After the timed region, plain streaming kernels (a copy, two reads and a
+write, a read, a write; csrc/probes/stream_ceiling.hip) measure the box's
+practical HBM ceiling, reported beside the datasheet peak.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--nranks N]
        [--count ELEMS] [--dtype float32] [--proto auto|simple|ll|ll128]
@@ -48,6 +51,8 @@ def parse():
     ap.add_argument("--nchannels", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the streaming-kernel ceiling measured after the timed region")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw the inputs on the GPU (same distributions, torch's generator) instead of the host "
                          "generator; for timing large configurations (no CPU baseline then)")
@@ -203,6 +208,8 @@ def main():
 
     cpu = None if (args.no_cpu_baseline or xs is None) else cpu_baseline(xs, dtype, plan, N, S, B)
     comm.close()
+    del sends, recvs
+    ceiling = None if args.no_stream_ceiling else stream_ceiling(torch)
 
     algo = B.ALGO_NAMES[plan["algo"]]
     out = {
@@ -235,8 +242,50 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "stream_ceiling": ceiling,
     }
+    if ceiling:
+        out["model_vs_copy_ceiling"] = round(achieved / ceiling["copy"], 4)
     print(json.dumps(out), flush=True)
+
+
+def stream_ceiling(torch, nbytes=1 << 30, steps=10):
+    """The box's practical HBM ceiling: plain streaming kernels (16-byte
+    non-temporal vectors, csrc/probes/stream_ceiling.hip) over 1 GiB buffers,
+    four times the Infinity Cache, timed with events on torch's stream.  A
+    context figure beside the 8 TB/s peak, not the roofline's peak."""
+    import ctypes
+    from ring_allreduce_reduction_amd import build as lb
+    if not os.path.exists(lb.PROBE_LIB):
+        log("stream-ceiling probe not built: skipped")
+        return None
+    lib = ctypes.CDLL(lb.PROBE_LIB)
+    lib.streamCeilingLaunch.restype = ctypes.c_int
+    lib.streamCeilingLaunch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    a = torch.ones(nbytes // 4, device="cuda")
+    c = torch.ones(nbytes // 4, device="cuda")
+    b = torch.empty(nbytes // 4, device="cuda")
+    stream = torch.cuda.current_stream()
+    moved = {"copy": 2, "read2_write1": 3, "read": 1, "write": 1}
+    out = {"unit": "GB/s", "buffer_bytes": nbytes}
+    grid = torch.cuda.get_device_properties(0).multi_processor_count * 16
+    for kind, name in enumerate(moved):
+        launch = lambda: lib.streamCeilingLaunch(kind, a.data_ptr(), c.data_ptr(), b.data_ptr(), nbytes, grid,
+                                                 ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(3):
+            if launch() != 0:
+                raise SystemExit("stream-ceiling probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(moved[name] * nbytes / (e0.elapsed_time(e1) / steps / 1e3) / 1e9, 1)
+    log("stream ceiling (GB/s): copy %.0f, 2 reads + 1 write %.0f, read %.0f, write %.0f"
+        % (out["copy"], out["read2_write1"], out["read"], out["write"]))
+    return out
 
 
 def workload_key(proto, N, count, dtype):
@@ -322,8 +371,9 @@ def cpu_baseline(xs, dtype, plan, N, S, B):
     busbw = S / t / 1e9 * 2 * (N - 1) / N
     log("cpu oracle: %d runs, %.3f s per AllReduce" % (reps, t))
     return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "the full %d x %d MiB %s workload, %d run(s) of the single-threaded C oracle, "
-                      "%.2f s each" % (N, S >> 20, dtype, reps, t)}
+            "sample": "the full %d x %d MiB %s workload, %d run(s) of the single-threaded C oracle "
+                      "(its one result array stands for every rank's output), %.2f s each"
+                      % (N, S >> 20, dtype, reps, t)}
 
 
 def bench_halves(args, B, gen, torch, np):

@@ -24,7 +24,23 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    build_probe(verbose)
     return LIB
+
+
+PROBE_LIB = os.path.join(HERE, "libstream_ceiling.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The streaming-ceiling probe bench.py reports beside the HBM peak."""
+    cmd = ["hipcc", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(CSRC, "probes", "stream_ceiling.hip"), "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -394,12 +394,13 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
     }
   }
 
-  // EARLY (LL): the local operand depends on no flag, so start its loads
-  // before the credit wait and keep the last credit read.  Measured on 8
-  // ranks: LL steps 7% shorter; LL128 steps longer (its 1 KiB units hold
-  // more registers across the wait) and the 8 KiB Simple slot has no
-  // registers to spare, so both keep the plain order.
-  constexpr bool EARLY = PROTO == kLL;
+  // EARLY: the local operand depends on no flag, so start its loads before
+  // the credit wait and keep the last credit read.  Measured on 8 ranks: LL
+  // steps 7% shorter; the 8 KiB Simple slot 0.5% faster at 256 MiB per rank
+  // (104 VGPRs, no spill); LL128 steps longer (its 1 KiB units hold more
+  // registers across the wait) and small Simple slots 3% slower on short
+  // messages, so those keep the plain order.
+  constexpr bool EARLY = PROTO == kLL || (PROTO == kSimple && U == 8);
   if (!EARLY && hasSend && !directSend && !waitCredit<false>(a, m)) return false;
 
   v4u v[U];
