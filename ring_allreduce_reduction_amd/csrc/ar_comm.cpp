@@ -103,24 +103,23 @@ const Env& env() {
 // calibration mode on one MI355X: the least-squares fit, in log time, of the
 // model to 4 KiB messages at 2, 4, 8 and 16 ranks (1 channel), 128 MiB at 8
 // ranks over 1..64 channels, and 16 KiB..64 MiB at 8 ranks with the channel
-// count the 32 KiB rule allows.  Worst point off by 32% (LL), 26% (LL128),
-// 25% (Simple); on the 8-rank sweep the choice is within 3% of the best.
+// count the 32 KiB rule allows.  Worst point off by 34% (LL), 28% (LL128),
+// 19% (Simple).
 const arTuneModel_t kDefaultModels[3] = {
-    /* LL     */ {2.965f, 1.9533f, 47.77f, 116.98f},
-    /* LL128  */ {2.701f, 2.6319f, 61.44f, 152.67f},
-    /* Simple */ {2.963f, 1.4816f, 187.6f, 277.45f},
+    /* LL     */ {3.275f, 1.9805f, 47.92f, 117.51f},
+    /* LL128  */ {3.041f, 2.7572f, 59.64f, 149.99f},
+    /* Simple */ {2.603f, 1.5401f, 224.31f, 310.98f},
 };
 
 // Tree constants (same units; stepLatUs is per tree level each way), fitted
 // the same way (`bench.py --calibrate --algo tree`) with the pages' tree
-// model and its size correction: worst point off by 52% (LL, where the
-// correction's mid-size dip does not match this GPU), 18% (LL128), 27%
-// (Simple).  On the 8-rank sweep arTune then picks the tree (Simple) up to
-// 512 KiB and the ring (Simple) from 1 MiB, the fastest candidate at every size.
+// model and its size correction: worst point off by 51% (LL, where the
+// correction's mid-size dip does not match this GPU), 17% (LL128), 42%
+// (Simple).
 const arTuneModel_t kDefaultTreeModels[3] = {
-    /* LL     */ {4.088f, 1.5169f, 188.3f, 48.71f},
-    /* LL128  */ {1.828f, 2.4511f, 67.92f, 58.78f},
-    /* Simple */ {4.774f, 0.8563f, 102.91f, 100.21f},
+    /* LL     */ {2.134f, 1.8129f, 188.67f, 48.44f},
+    /* LL128  */ {0.872f, 2.6381f, 70.15f, 60.84f},
+    /* Simple */ {3.624f, 0.9521f, 138.49f, 140.72f},
 };
 
 constexpr int kStagingBuffers = 4;
@@ -383,13 +382,18 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   };
   int lanes = lanesFor(plan->slotPayload);
   if (proto == kSimple && !plan->cooperative && c->forcedLanes == 0) {
+    // Smaller slots spread a short chunk over more lanes, but only while the
+    // grid stays within half a resident round: past that, each lane is a
+    // chain of 2N-1 one-column steps and extra rounds of such chains cost
+    // more than bigger slots (8 ranks, 16 MiB per rank: 4 lanes of 8 KiB
+    // take 112 us, 32 lanes of 1 KiB in four rounds 165 us).  A halving
+    // that keeps the lane count is taken too: the lane share still fits one
+    // slot, and the smaller slot's kernel is faster on it (a 4 KiB share: 1
+    // lane at 8, 4 and 2 KiB slots, 2 at 1 KiB).
     while (lanes < target && plan->unroll > 1 && (uint64_t)lanes * plan->slotPayload >= chunkBytes / 2) {
       const int u = plan->unroll / 2;
-      // equal lanes: the lane share still fits one slot of either size, and
-      // a later halving may add lanes (a 4 KiB share: 1 lane at 8 and 4 KiB
-      // slots, 2 at 2 KiB, 4 at 1 KiB)
       const int ln = lanesFor(slotPayloadOf(proto, u));
-      if (ln < lanes) break;
+      if (ln < lanes || (ln > lanes && 2 * gridFor(ln) > capacity)) break;
       plan->unroll = u;
       plan->slotBytes = slotBytesOf(proto, u);
       plan->slotPayload = slotPayloadOf(proto, u);

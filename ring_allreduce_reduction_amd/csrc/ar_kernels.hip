@@ -674,7 +674,13 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
 // steps simply continue from one task to the next.
 template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: member state stays in SGPRs
+  // The 8 KiB slot kernels read the wavefront index through readfirstlane,
+  // so every per-member value (pointers, counters, rank, channel) lives in
+  // scalar registers: that keeps them at 101-120 VGPRs instead of spilling.
+  // Smaller slots keep the plain index: with their register room, per-member
+  // state in VGPRs measured faster on short messages (the CU's scalar unit
+  // is shared by all of its wavefronts' polling loops).
+  const int wave = U == 8 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
   const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
@@ -1074,7 +1080,8 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
 // of them at once.
 template <int PROTO, int DT, int OP, int U, bool BATCH>
 __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: member state stays in SGPRs
+  // as in the ring kernel: scalar member state for the largest (4 KiB) slot
+  const int wave = U == 4 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
