@@ -315,39 +315,6 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     *nGroupsOut = ng;
     *gsOut = (N + ng - 1) / ng;
   };
-  // A Simple slot smaller than the default keeps more wavefronts resident
-  // (fewer registers) when the whole grid must be co-resident.
-  int nGroups = 1, groupSize = N;
-  if (N > kMaxMembersPerGroup) {
-    bool found = false;
-    const int u0 = proto == kSimple && plan->unroll > kGroupedSimpleUnrollMax ? kGroupedSimpleUnrollMax
-                                                                               : plan->unroll;
-    for (int u = u0; u >= 1 && !found; u /= 2) {
-      if (proto == kSimple) {
-        plan->unroll = u;
-        plan->slotBytes = slotBytesOf(proto, u);
-        plan->slotPayload = slotPayloadOf(proto, u);
-      }
-      for (int gs = kMaxMembersPerGroup; gs >= 1 && !found; --gs) {
-        layout(gs, &nGroups, &groupSize);
-        plan->block = groupSize * kWave;
-        int perCU = 0;
-        if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return arHipError;
-        const int grid1 = ((nch + 7) / 8) * 8 * nGroups;
-        found = perCU * c->numCUs >= grid1;
-      }
-      if (proto != kSimple) break;
-    }
-    if (!found) return arInvalidUsage;
-  }
-  plan->groupSize = groupSize;
-  plan->nGroups = nGroups;
-  plan->block = groupSize * kWave;
-  plan->cooperative = nGroups > 1;
-
-  // Lanes per (rank, channel): one resident round of workgroups (the grid is
-  // sized to what the chip holds at once, so no tail round), but never a
-  // lane share below two FIFO slots of the largest chunk.
   const uint64_t per = alignUpU(divUpU(count, (uint64_t)nch), A);
   const uint64_t loop = (uint64_t)N * plan->chunkElems;
   // elements one stage of one member covers: a chunk of the AllReduce loop,
@@ -357,6 +324,58 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
                        : func != kCollAllReduce ? (per < plan->chunkElems ? per : plan->chunkElems)
                        : per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
   const uint64_t chunkBytes = cur * (uint64_t)esz;
+
+  // A Simple slot smaller than the default keeps more wavefronts resident
+  // (fewer registers) when the whole grid must be co-resident.  First
+  // choice: the smallest slot of at least half a chunk, with enough lanes
+  // that each lane's share is one slot, if such a grid can be co-resident
+  // (72 ranks x 4 MiB: 912-byte chunks in 1 KiB slots and 12-member groups
+  // run in 520 us, in 4 KiB slots, whose kernel fits only 9 members a group,
+  // in 853 us).  Otherwise the largest slot (at most 4 KiB) whose one-lane
+  // grid is co-resident.
+  int nGroups = 1, groupSize = N;
+  if (N > kMaxMembersPerGroup) {
+    // the largest group size whose grid of `ln` lanes per channel is
+    // co-resident with slot u (0: none; -1: HIP error)
+    auto fit = [&](int u, int ln) -> int {
+      if (proto == kSimple) {
+        plan->unroll = u;
+        plan->slotBytes = slotBytesOf(proto, u);
+        plan->slotPayload = slotPayloadOf(proto, u);
+      }
+      for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
+        layout(gs, &nGroups, &groupSize);
+        plan->block = groupSize * kWave;
+        int perCU = 0;
+        if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return -1;
+        if ((int64_t)perCU * c->numCUs >= (int64_t)((nch * ln + 7) / 8) * 8 * nGroups) return 1;
+      }
+      return 0;
+    };
+    const int uMax = proto == kSimple && plan->unroll > kGroupedSimpleUnrollMax ? kGroupedSimpleUnrollMax
+                                                                                 : plan->unroll;
+    int found = 0;
+    if (proto == kSimple) {
+      int u = uMax;
+      while (u > 1 && 2 * (uint64_t)slotPayloadOf(proto, u / 2) >= chunkBytes) u /= 2;
+      const uint64_t need = (chunkBytes + (uint64_t)slotPayloadOf(proto, u) - 1) / (uint64_t)slotPayloadOf(proto, u);
+      if (u < uMax && need >= 1 && need <= 2) found = fit(u, (int)need);
+    }
+    for (int u = uMax; u >= 1 && found == 0; u /= 2) {
+      found = fit(u, 1);
+      if (proto != kSimple) break;
+    }
+    if (found < 0) return arHipError;
+    if (found == 0) return arInvalidUsage;
+  }
+  plan->groupSize = groupSize;
+  plan->nGroups = nGroups;
+  plan->block = groupSize * kWave;
+  plan->cooperative = nGroups > 1;
+
+  // Lanes per (rank, channel): one resident round of workgroups (the grid is
+  // sized to what the chip holds at once, so no tail round), but never a
+  // lane share below two FIFO slots of the largest chunk.
   int perCU = 0;
   if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return arHipError;
   if (perCU < 1) perCU = 1;
