@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--coll", default="allreduce", choices=["allreduce", "reducescatter", "allgather"],
                     help="collective to time; for the two halves --count is the per-rank block "
                          "(default: 256 MiB per rank on the larger side)")
+    ap.add_argument("--large-n-table", action="store_true",
+                    help="time every algorithm x protocol at 24-72 ranks (rings of several workgroups)")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure latency vs ranks and bandwidth vs channels per protocol and fit arTune's model")
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -104,6 +106,8 @@ def main():
         return sweep(args, B, gen, torch, np)
     if args.calibrate:
         return calibrate(args, B, torch, np)
+    if args.large_n_table:
+        return large_n_table(args, B, torch, np)
     if args.batch:
         return bench_batch(args, B, gen, torch, np)
 
@@ -705,6 +709,32 @@ def calibrate(args, B, torch, np):
         print(json.dumps({"calib": "fit_error", "algo": args.algo, "proto": name, "points": len(pts),
                           "worst_rel_err": round(worst, 3)}), flush=True)
     print(json.dumps({"calib": "fit", "algo": args.algo, "models": fits}), flush=True)
+
+
+def large_n_table(args, B, torch, np):
+    """Rings of more than one workgroup (24, 32, 48, 72 ranks): every
+    algorithm x protocol at 4 KiB per rank on 1 channel, 256 KiB on 8, 4 and
+    16 MiB on 64, fp32 Sum; one JSON line each, with arTune's choice for the
+    size."""
+    ranks = (24, 32, 48, 72)
+    xs = [torch.rand(1 << 22, device="cuda") for _ in range(max(ranks))]
+    ys = [torch.empty_like(x) for x in xs]
+    for n in ranks:
+        for count, nch in ((1024, 1), (1 << 16, 8), (1 << 20, 64), (1 << 22, 64)):
+            with B.Comm(n, 64, "auto", "auto") as comm:
+                a, p, ch, pred = B.arTuneAlgo(comm.handle, count * 4)
+            for algo in ("ring", "tree"):
+                for proto in (B.arProtoLL, B.arProtoLL128, B.arProtoSimple):
+                    row = {"nranks": n, "bytes": count * 4, "nch": nch, "algo": algo,
+                           "proto": B.PROTO_NAMES[proto], "arTune": "%s/%s/%d" % (B.ALGO_NAMES[a], B.PROTO_NAMES[p], ch)}
+                    comm = B.Comm(n, nch, proto, algo)
+                    try:
+                        comm.plan(count, "float32")
+                        row["us"] = round(time_calls(B, torch, comm, xs[:n], ys[:n], count, B.arFloat32, 3, 20) * 1e3, 2)
+                    except B.ArError as e:
+                        row["skipped"] = str(e)
+                    comm.close()
+                    print(json.dumps(row), flush=True)
 
 
 SWEEP_CANDIDATES = [("ring", "ll"), ("ring", "ll128"), ("ring", "simple"),
