@@ -558,7 +558,10 @@ def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
             B.arSetDebug(comm.handle, B.arDebugSlots, dp)
         comm.set_config("simple" if args.proto == "auto" else args.proto, nch)
         B.arSetDebug(comm.handle, B.arDebugLanes, ln)
-        B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
+        if args.proto == "ll128":   # the slot field sets the LL128 slot (2 or 4 KiB)
+            B.arSetDebug(comm.handle, B.arDebugLL128SlotKiB, sk)
+        else:
+            B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
         B.arSetDebug(comm.handle, B.arDebugDirect, d)
         B.arSetDebug(comm.handle, B.arDebugLaneSets, st)
         plan = comm.plan(count, dtype)

@@ -321,6 +321,9 @@ typedef enum {
   arDebugLaneSets = 6,   /* single-workgroup rings, single calls: at most this many workgroups,
                             each running several (channel, lane) pairs in turn on one FIFO set;
                             0 = one workgroup per pair */
+  arDebugLL128SlotKiB = 7,  /* LL128 FIFO slot per wavefront: 2 or 4 KiB of wire (1920 or 3840
+                               payload bytes), 0 = chosen per call (default); tree and group
+                               (arGroupEnd) launches use 2 */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 

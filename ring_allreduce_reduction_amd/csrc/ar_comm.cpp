@@ -164,6 +164,7 @@ struct arComm {
   int forcedLanes;      // 0: automatic
   int laneSetsMax;      // 0: one workgroup per (channel, lane); else at most this many FIFO sets
   int simpleUnroll;     // Simple slot size in KiB (1, 2, 4)
+  int ll128Unroll;      // LL128 slot in 1 KiB units (2 or 4); 0: chosen per call
   bool direct;          // Simple all-gather writes outputs directly
   hipStream_t lastStream;
   bool launched;
@@ -193,10 +194,10 @@ bool commOk(const arComm* c) {
 // Slot geometry: Simple slots are `unroll` KiB; the FIFO is provisioned for
 // the largest Simple slot.
 int slotBytesOf(int proto, int unroll) {
-  return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotBytes : unroll * kLL128UnitBytes;
 }
 int slotPayloadOf(int proto, int unroll) {
-  return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotPayload : kLL128SlotPayload;
+  return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotPayload : unroll * kLL128UnitPayload;
 }
 
 size_t chunkBytesOf(const arComm* c, int proto) {
@@ -296,7 +297,10 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   plan->proto = proto;
   plan->nChannels = nch;
   plan->chunkElems = chunkBytesOf(c, proto) / (uint64_t)esz;
-  plan->unroll = proto == kSimple ? c->simpleUnroll : proto == kLL ? kLLUnroll : kLL128Unroll;
+  plan->unroll = proto == kSimple ? c->simpleUnroll : proto == kLL ? kLLUnroll
+                                                    : c->ll128Unroll > 0 ? c->ll128Unroll : kLL128Unroll;
+  // large LL128 slots serve single-call rings only
+  if (proto == kLL128 && (tree || batch)) plan->unroll = kLL128Unroll;
   if (tree && proto == kSimple && plan->unroll > kTreeSimpleUnrollMax) plan->unroll = kTreeSimpleUnrollMax;
   if (batch && proto == kSimple && plan->unroll > kBatchSimpleUnrollMax) plan->unroll = kBatchSimpleUnrollMax;
   plan->direct = !tree && proto == kSimple && c->direct;
@@ -400,6 +404,21 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     return ln < 1 ? 1 : ln;
   };
   int lanes = lanesFor(plan->slotPayload);
+  // LL128, automatic slot: the large slot when every lane still gets a full
+  // batch of large slots (nSlots/2 columns): that halves the batches, each of
+  // which fills and drains the ring (16 ranks x 512 MiB bf16: 13.3 -> 10.5 ms).
+  // With fewer columns the batch only gets shallower (8 ranks x 128 MiB fp32:
+  // 1.49 -> 1.65 ms), so short shares keep the small slot.
+  if (proto == kLL128 && c->ll128Unroll == 0 && !tree && !batch && !plan->cooperative && c->forcedLanes == 0) {
+    const int pay = slotPayloadOf(proto, kLL128UnrollLarge);
+    const int ln = lanesFor(pay);
+    if (chunkBytes / (uint64_t)ln >= (uint64_t)(plan->nSlots / 2) * (uint64_t)pay) {
+      plan->unroll = kLL128UnrollLarge;
+      plan->slotBytes = slotBytesOf(proto, kLL128UnrollLarge);
+      plan->slotPayload = pay;
+      lanes = ln;
+    }
+  }
   if (proto == kSimple && !plan->cooperative && c->forcedLanes == 0) {
     // Smaller slots spread a short chunk over more lanes, but only while the
     // grid stays within half a resident round: past that, each lane is a
@@ -501,6 +520,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->timeoutUs = e.timeoutUs;
   c->deadRank = -1;
   c->simpleUnroll = kSimpleUnrollDefault;
+  c->ll128Unroll = 0;   // automatic
   c->direct = true;
   for (int p = 0; p < 3; ++p) c->models[p] = kDefaultModels[p];
   for (int p = 0; p < 3; ++p) c->treeModels[p] = kDefaultTreeModels[p];
@@ -512,7 +532,8 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   const size_t workers = (size_t)nranks * (size_t)lanesMax;
   if (nranks > 1) {
     for (int p = 0; p < 3; ++p) {
-      c->fifoWorkerBytes[p] = (size_t)kMaxSlots * (size_t)slotBytesOf(p, kSimpleUnrollMax);
+      c->fifoWorkerBytes[p] = (size_t)kMaxSlots * (size_t)slotBytesOf(p, p == kLL128 ? kLL128UnrollLarge
+                                                                                      : kSimpleUnrollMax);
       const size_t fb = workers * c->fifoWorkerBytes[p];
       const size_t cb = workers * sizeof(Conn);
       if (hipMalloc((void**)&c->fifo[p], fb) != hipSuccess || hipMalloc((void**)&c->conn[p], cb) != hipSuccess ||
@@ -577,6 +598,11 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   if (knob == arDebugSimpleSlotKiB) {
     if (value != 1 && value != 2 && value != 4 && value != 8) return arInvalidArgument;
     c->simpleUnroll = (int)value;
+    return arSuccess;
+  }
+  if (knob == arDebugLL128SlotKiB) {
+    if (value != 0 && value != kLL128Unroll && value != kLL128UnrollLarge) return arInvalidArgument;
+    c->ll128Unroll = (int)value;
     return arSuccess;
   }
   if (knob == arDebugSlots) {

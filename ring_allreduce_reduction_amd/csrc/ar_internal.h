@@ -36,7 +36,8 @@ constexpr int kTreeSimpleUnrollMax = 4;   // the tree's Simple slot is at most 4
                                           // arrays live per lane: 8 KiB would spill)
 constexpr int kTreeEdges = 3;             // a tree node's FIFOs: from d0, from d1, from its parent
 constexpr int kLLUnroll = 2;
-constexpr int kLL128Unroll = 2;
+constexpr int kLL128Unroll = 2;           // LL128 slot in 1 KiB units (8 lines of 128 bytes)
+constexpr int kLL128UnrollLarge = 4;      // single-call rings may use 4-unit LL128 slots
 
 constexpr int kSimpleSlotBytesMax = kSimpleUnrollMax * kWave * 16;   // 8192
 constexpr int kLLSlotBytes = kLLUnroll * kWave * 16;           // 2048 wire
@@ -44,8 +45,7 @@ constexpr int kLLSlotPayload = kLLUnroll * kWave * 8;          // 1024 payload
 constexpr int kLL128LinePayload = 120;
 constexpr int kLL128UnitBytes = kWave * 16;                    // 1024 = 8 lines
 constexpr int kLL128UnitPayload = 8 * kLL128LinePayload;       // 960
-constexpr int kLL128SlotBytes = kLL128Unroll * kLL128UnitBytes;
-constexpr int kLL128SlotPayload = kLL128Unroll * kLL128UnitPayload;
+constexpr int kLL128SlotBytesMax = kLL128UnrollLarge * kLL128UnitBytes;
 
 // Nominal chunk sizes (bytes).  Simple: two slices of AR_SLICE_BYTES (one
 // chunk = 2 slices).  LL and LL128: builder choices, multiples of 16 bytes.

@@ -362,7 +362,7 @@ template <int PROTO, int DT, int OP, int U>
 __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, const char* inp, char* outp,
                                      char* succOutp, long valid) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
-  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
   const bool hasLocal = (kind & kLocalBit) != 0;
   const bool hasRecv = (kind & kRecvBit) != 0;
   const bool hasSend = (kind & kSendBit) != 0;
@@ -559,7 +559,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr u64 A = 16 / ESZ;   // 16-byte grain in elements
   constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
-                        : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
+                        : PROTO == kLL ? kLLSlotPayload : U * kLL128UnitPayload;
   const int N = a.nranks;
   const int succ = r + 1 == N ? 0 : r + 1;
   // channel share [pages: contiguous split per channel, 16-byte grain]
@@ -856,7 +856,7 @@ struct Pieces {   // this lane's pieces of one slot (as in the ring's step)
 template <int PROTO, int U>
 __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, const Pieces<PROTO, U>& pc, int lane,
                                          long valid, v4u (&in)[U]) {
-  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
   const char* slot = e.fifo + (size_t)e.slot * SLOT;
   if (PROTO == kSimple) {
     if (!waitGeq(a, &e.conn->tail, e.step + 1, e.agent)) return false;
@@ -935,7 +935,7 @@ __device__ __forceinline__ void edgeFinishRecv(const KernelArgs& a, Edge& e, int
 template <int PROTO, int U>
 __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pieces<PROTO, U>& pc, int lane,
                                          long valid, const v4u (&v)[U]) {
-  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : kLL128SlotBytes;
+  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
   // slot step % nSlots is free once the receiver consumed step - nSlots
   const u64 need = e.step + 1 > (u64)a.nSlots ? e.step + 1 - (u64)a.nSlots : 0;
   if (!waitGeq(a, &e.conn->head, need, e.agent)) return false;
@@ -1002,7 +1002,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr u64 A = 16 / ESZ;
   constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
-                        : PROTO == kLL ? kLLSlotPayload : kLL128SlotPayload;
+                        : PROTO == kLL ? kLLSlotPayload : U * kLL128UnitPayload;
   const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
   const u64 lo = umin((u64)ch * per, count);
   const u64 len = umin(lo + per, count) - lo;
@@ -1201,7 +1201,11 @@ template <int COLL, bool BATCH>
 KernelFn pickRingProto(const Plan& plan, int dtype, int op) {
   switch (plan.proto) {
     case kLL: return pickRing<kLL, kLLUnroll, COLL, BATCH>(dtype, op);
-    case kLL128: return pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
+    case kLL128:
+      if (plan.unroll == kLL128Unroll) return pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
+      if constexpr (!BATCH)   // large LL128 slots: single calls only
+        if (plan.unroll == kLL128UnrollLarge) return pickRing<kLL128, kLL128UnrollLarge, COLL, false>(dtype, op);
+      return nullptr;
     case kSimple:
       switch (plan.unroll) {
         case 1: return pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
@@ -1217,7 +1221,7 @@ template <bool BATCH>
 KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
   switch (plan.proto) {
     case kLL: return pickTree<kLL, kLLUnroll, BATCH>(dtype, op);
-    case kLL128: return pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op);
+    case kLL128: return plan.unroll == kLL128Unroll ? pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op) : nullptr;
     case kSimple:
       switch (plan.unroll) {
         case 1: return pickTree<kSimple, 1, BATCH>(dtype, op);

@@ -182,6 +182,8 @@ def test_cfg_16x512MiB_bf16_64ch(B, gu, orc):
         for proto in ("ll128", "simple"):
             comm.set_config(proto, 64)
             plan = comm.plan(count, "bfloat16")
+            if proto == "ll128":   # lanes get a full batch of 4 KiB slots here: the large LL128 slot
+                assert plan["stepBytes"] == 4096
             gu.note("16 x 512 MiB bf16 %s 64 ch" % proto)
             gu.run_ring(comm, sends, recvs, "bfloat16", "sum")
             sampled_check(B, gu, orc, xs, sends, recvs, "bfloat16", "sum", plan, nsample=100000)

@@ -127,6 +127,22 @@ def test_workgroups_running_several_lanes(B, gu, proto, sets):
         gu.parity_case(8, 300007, "float32", "sum", proto, 5, seed=9, comm=comm)
 
 
+@pytest.mark.parametrize("slot_kib", [2, 4])
+def test_ll128_slot_variants(B, gu, slot_kib):
+    # LL128 slots of 2 or 4 KiB of wire (16 or 32 lines of 120 payload bytes)
+    with B.Comm(8, 16, "ll128") as comm:
+        B.arSetDebug(comm.handle, B.arDebugLL128SlotKiB, slot_kib)
+        for count, nch in [(300007, 5), (1 << 20, 16), (4099, 2), (777, 1)]:
+            plan, _, _ = gu.parity_case(8, count, "float32", "sum", "ll128", nch, seed=count, comm=comm)
+            assert plan["stepBytes"] == slot_kib * 1024
+        gu.parity_case(8, 100003, "bfloat16", "sum", "ll128", 4, seed=1, comm=comm, inplace=True)
+        gu.parity_case(8, 3001, "uint64", "probe", "ll128", 3, comm=comm)
+        gu.parity_case(8, 50021, "int32", "min", "ll128", 3, seed=2, comm=comm)
+    with B.Comm(24, 4, "ll128") as comm:   # a ring of two workgroups
+        B.arSetDebug(comm.handle, B.arDebugLL128SlotKiB, slot_kib)
+        gu.parity_case(24, 40009, "float32", "sum", "ll128", 4, seed=24, comm=comm)
+
+
 def test_ll128_needs_128_byte_alignment(B, gu):
     from ring_allreduce_reduction_amd import inputs as gen
     xs = gen.make_inputs(4, 1000, "float32")
