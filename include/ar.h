@@ -279,6 +279,10 @@ typedef struct {
 /*
  * arGetPlan -- fill `plan` with what arAllReduce(comm, ..., count, dtype, ...)
  * would use for buffers that are 128-byte aligned (aligned128 = 1) or not.
+ * The channel count that runs can be below the requested one: a ring of more
+ * than 16 ranks needs its whole grid co-resident, and when one lane per
+ * channel does not fit, the channels are halved until it does (the result is
+ * that of the reported count).
  */
 arResult_t arGetPlan(arComm_t comm, size_t count, arDataType_t dtype, int aligned128, arPlan_t* plan);
 
@@ -324,6 +328,9 @@ typedef enum {
   arDebugLL128SlotKiB = 7,  /* LL128 FIFO slot per wavefront: 2 or 4 KiB of wire (1920 or 3840
                                payload bytes), 0 = chosen per call (default); tree and group
                                (arGroupEnd) launches use 2 */
+  arDebugGroupSpread = 8,   /* rings of more than 16 ranks: 1 = place the workgroups of one
+                               (channel, lane) on consecutive ids, i.e. on different XCDs under
+                               round-robin dispatch (default 0: ids congruent mod 8, one XCD) */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 

@@ -163,6 +163,7 @@ struct arComm {
   int deadRank;
   int forcedLanes;      // 0: automatic
   int laneSetsMax;      // 0: one workgroup per (channel, lane); else at most this many FIFO sets
+  int groupSpread;      // debug: a lane's groups on consecutive workgroup ids
   int simpleUnroll;     // Simple slot size in KiB (1, 2, 4)
   int ll128Unroll;      // LL128 slot in 1 KiB units (2 or 4); 0: chosen per call
   bool direct;          // Simple all-gather writes outputs directly
@@ -319,15 +320,18 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     *nGroupsOut = ng;
     *gsOut = (N + ng - 1) / ng;
   };
-  const uint64_t per = alignUpU(divUpU(count, (uint64_t)nch), A);
-  const uint64_t loop = (uint64_t)N * plan->chunkElems;
   // elements one stage of one member covers: a chunk of the AllReduce loop,
   // or the loop's range of one rank block for ReduceScatter / AllGather; the
   // tree's lanes split the whole channel share
-  const uint64_t cur = tree ? per
-                       : func != kCollAllReduce ? (per < plan->chunkElems ? per : plan->chunkElems)
-                       : per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
-  const uint64_t chunkBytes = cur * (uint64_t)esz;
+  const uint64_t loop = (uint64_t)N * plan->chunkElems;
+  auto chunkBytesFor = [&](int ch) {
+    const uint64_t per = alignUpU(divUpU(count, (uint64_t)ch), A);
+    const uint64_t cur = tree ? per
+                         : func != kCollAllReduce ? (per < plan->chunkElems ? per : plan->chunkElems)
+                         : per < loop ? alignUpU(divUpU(per, (uint64_t)N), A) : plan->chunkElems;
+    return cur * (uint64_t)esz;
+  };
+  uint64_t chunkBytes = chunkBytesFor(nch);
 
   // A Simple slot smaller than the default keeps more wavefronts resident
   // (fewer registers) when the whole grid must be co-resident.  First
@@ -336,9 +340,15 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // (72 ranks x 4 MiB: 912-byte chunks in 1 KiB slots and 12-member groups
   // run in 520 us, in 4 KiB slots, whose kernel fits only 9 members a group,
   // in 853 us).  Otherwise the largest slot (at most 4 KiB) whose one-lane
-  // grid is co-resident.
+  // grid is co-resident.  If no grid of one lane per channel can be
+  // co-resident, the channels are halved until one can (the plan reports
+  // the count that runs).
   int nGroups = 1, groupSize = N;
-  if (N > kMaxMembersPerGroup) {
+  const int unroll0 = plan->unroll;
+  while (N > kMaxMembersPerGroup) {
+    plan->unroll = unroll0;
+    plan->slotBytes = slotBytesOf(proto, unroll0);
+    plan->slotPayload = slotPayloadOf(proto, unroll0);
     // the largest group size whose grid of `ln` lanes per channel is
     // co-resident with slot u (0: none; -1: HIP error)
     auto fit = [&](int u, int ln) -> int {
@@ -370,7 +380,11 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       if (proto != kSimple) break;
     }
     if (found < 0) return arHipError;
-    if (found == 0) return arInvalidUsage;
+    if (found > 0) break;
+    if (nch == 1) return arInvalidUsage;
+    nch /= 2;
+    plan->nChannels = nch;
+    chunkBytes = chunkBytesFor(nch);
   }
   plan->groupSize = groupSize;
   plan->nGroups = nGroups;
@@ -600,6 +614,11 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
     c->simpleUnroll = (int)value;
     return arSuccess;
   }
+  if (knob == arDebugGroupSpread) {
+    if (value != 0 && value != 1) return arInvalidArgument;
+    c->groupSpread = (int)value;
+    return arSuccess;
+  }
   if (knob == arDebugLL128SlotKiB) {
     if (value != 0 && value != kLL128Unroll && value != kLL128UnrollLarge) return arInvalidArgument;
     c->ll128Unroll = (int)value;
@@ -733,6 +752,7 @@ void buildArgs(const arComm* c, const Plan& plan, int func, size_t count, const 
   a->deadRank = c->deadRank;
   a->taskSlots = 1;
   a->laneSets = plan.laneSets;
+  a->groupSpread = c->groupSpread;
 }
 
 // One collective call: argument checks (nothing is enqueued on failure), the

@@ -108,6 +108,7 @@ struct KernelArgs {
   int taskSlots;              // tasks in flight at once (each on nChannels x lanes wavefront sets)
   int laneSets;               // single call: workgroup FIFO sets (<= nChannels x lanes); set L runs
                               // (channel, lane) pairs L, L + laneSets, ...
+  int groupSpread;            // debug: groups of one lane on consecutive workgroup ids (other XCDs)
 };
 
 // Everything arAllReduce decides for one call.

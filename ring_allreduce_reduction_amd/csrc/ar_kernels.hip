@@ -304,6 +304,26 @@ __device__ __forceinline__ bool waitGeq(const KernelArgs& a, const u64* p, u64 t
   }
 }
 
+// Workgroup -> (lane id L, group g).  With several groups per lane, the
+// groups of one lane get workgroup ids congruent mod 8, i.e. the same XCD
+// under round-robin dispatch, so their edges stay in one L2: a locality hint
+// only, the edges between workgroups are device-coherent wherever the groups
+// run.  a.groupSpread gives them consecutive ids instead, i.e. different
+// XCDs, which exercises exactly that.
+__device__ __forceinline__ void laneAndGroup(const KernelArgs& a, int& L, int& g) {
+  if (a.nGroups == 1) {
+    L = blockIdx.x;
+    g = 0;
+  } else if (a.groupSpread) {
+    g = blockIdx.x % a.nGroups;
+    L = blockIdx.x / a.nGroups;
+  } else {
+    const int x = blockIdx.x % 8;
+    g = (blockIdx.x / 8) % a.nGroups;
+    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
+  }
+}
+
 // ------------------------------------------------------------- one member
 
 struct Member {
@@ -685,18 +705,8 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   const int perTask = a.nChannels * a.lanes;
   const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
 
-  // Workgroup -> (FIFO set L, group).  With several groups per lane, the
-  // groups of one lane get workgroup ids congruent mod 8, i.e. the same XCD
-  // under round-robin dispatch, so their cross-workgroup edges stay in one L2.
-  int L, g;
-  if (a.nGroups == 1) {
-    L = blockIdx.x;
-    g = 0;
-  } else {
-    const int x = blockIdx.x % 8;
-    g = (blockIdx.x / 8) % a.nGroups;
-    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
-  }
+  int L, g;   // FIFO set and group
+  laneAndGroup(a, L, g);
   // A single call's workgroups may be fewer than its (channel, lane) pairs:
   // set L then runs pairs L, L + sets, L + 2 sets, ... on the same FIFOs,
   // whose steps simply continue from one pair to the next.
@@ -1088,14 +1098,7 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
   const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
 
   int L, g;   // (lane id, group), as in the ring kernel
-  if (a.nGroups == 1) {
-    L = blockIdx.x;
-    g = 0;
-  } else {
-    const int x = blockIdx.x % 8;
-    g = (blockIdx.x / 8) % a.nGroups;
-    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
-  }
+  laneAndGroup(a, L, g);
   if (L >= lanesTotal) return;
   const int r = g * a.groupSize + wave;
   if (r >= N || r == a.deadRank) return;

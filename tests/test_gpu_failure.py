@@ -71,7 +71,7 @@ def test_debug_knob_validation(B):
         for knob, bad in [(B.arDebugTimeoutUs, 0), (B.arDebugDeadRank, 4), (B.arDebugDeadRank, -2),
                           (B.arDebugSimpleSlotKiB, 3), (B.arDebugDirect, 2), (B.arDebugSlots, 1),
                           (B.arDebugSlots, 9), (B.arDebugLaneSets, -1), (B.arDebugLaneSets, 1 << 20),
-                          (B.arDebugLL128SlotKiB, 1), (B.arDebugLL128SlotKiB, 8),
+                          (B.arDebugLL128SlotKiB, 1), (B.arDebugLL128SlotKiB, 8), (B.arDebugGroupSpread, 2),
                           (99, 1)]:
             with pytest.raises(B.ArError):
                 B.arSetDebug(comm.handle, knob, bad)

@@ -184,6 +184,35 @@ def test_rings_across_workgroups(B, gu, proto, n):
     gu.parity_case(n, 40009, "float32", "sum", proto, 4, seed=n)
 
 
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+@pytest.mark.parametrize("proto", ["simple", "ll128", "ll"])
+def test_grid_too_large_for_co_residency_halves_channels(B, gu, algo, proto):
+    # 72 ranks on 64 channels: the LL kernels (and the tree's LL128) cannot
+    # keep one lane per channel resident; the call runs on fewer channels and
+    # reports them, and matches the oracle for that count
+    with B.Comm(72, 64, proto, algo) as comm:
+        plan, _, _ = gu.parity_case(72, 1 << 16, "float32", "sum", proto, 64, seed=72, comm=comm)
+        assert 1 <= plan["nChannels"] <= 64 and plan["ranksPerGroup"] <= 16
+
+
+@pytest.mark.parametrize("proto", ["simple", "ll128", "ll"])
+@pytest.mark.parametrize("n", [24, 72])
+def test_rings_across_xcds(B, gu, proto, n):
+    # the workgroups of one (channel, lane) on consecutive ids, i.e. on
+    # different XCDs (different L2s): the edges between them must be
+    # device-coherent, not merely coherent within one L2
+    with B.Comm(n, 16, proto) as comm:
+        B.arSetDebug(comm.handle, B.arDebugGroupSpread, 1)
+        for count, nch, dtype, op in [(40009, 4, "float32", "sum"), (300007, 16, "bfloat16", "sum"),
+                                      (7001, 2, "int32", "max")]:
+            plan, _, _ = gu.parity_case(n, count, dtype, op, proto, nch, seed=count + n, comm=comm)
+            assert plan["ranksPerGroup"] < n
+        gu.parity_case(n, 3001, "uint64", "probe", proto, 3, comm=comm)
+        for algo in ("tree", "ring"):
+            comm.set_algo(algo)
+            gu.parity_case(n, 100003, "float32", "sum", proto, 8, seed=7, comm=comm)
+
+
 def test_invalid_arguments_enqueue_nothing(B, gu):
     from ring_allreduce_reduction_amd import inputs as gen
     xs = gen.make_inputs(4, 256, "float32")
