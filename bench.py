@@ -297,9 +297,15 @@ def workload_key(proto, N, count, dtype):
 
 
 def kernel_src_sha():
+    """Hash of the kernels' source: the device code and the translation units
+    that instantiate and launch it."""
+    import glob
     import hashlib
-    src = os.path.join(ROOT, "ring_allreduce_reduction_amd", "csrc", "ar_kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    csrc = os.path.join(ROOT, "ring_allreduce_reduction_amd", "csrc")
+    h = hashlib.sha256()
+    for f in [os.path.join(csrc, "ar_device.h")] + sorted(glob.glob(os.path.join(csrc, "ar_kernels*.hip"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def summarize_profiles(args):

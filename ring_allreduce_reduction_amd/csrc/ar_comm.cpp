@@ -435,17 +435,18 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   }
   if (proto == kSimple && !plan->cooperative && c->forcedLanes == 0) {
     // Smaller slots spread a short chunk over more lanes, but only while the
-    // grid stays within half a resident round: past that, each lane is a
-    // chain of 2N-1 one-column steps and extra rounds of such chains cost
-    // more than bigger slots (8 ranks, 16 MiB per rank: 4 lanes of 8 KiB
-    // take 112 us, 32 lanes of 1 KiB in four rounds 165 us).  A halving
-    // that keeps the lane count is taken too: the lane share still fits one
-    // slot, and the smaller slot's kernel is faster on it (a 4 KiB share: 1
-    // lane at 8, 4 and 2 KiB slots, 2 at 1 KiB).
+    // grid stays within one workgroup per CU: past that, each lane is a
+    // chain of 2N-1 one-column steps and more of such chains side by side
+    // cost more than bigger slots (8 ranks, 16 MiB per rank: 4 lanes of
+    // 8 KiB take 112 us, 8 of 4 KiB 130 us, 32 lanes of 1 KiB in four rounds
+    // 165 us; 16 ranks, 4 MiB: 4 lanes of 1 KiB take 88 us, 2 of 2 KiB
+    // 102 us).  A halving that keeps the lane count is taken too: the lane
+    // share still fits one slot, and the smaller slot's kernel is faster on
+    // it (a 4 KiB share: 1 lane at 8, 4 and 2 KiB slots, 2 at 1 KiB).
     while (lanes < target && plan->unroll > 1 && (uint64_t)lanes * plan->slotPayload >= chunkBytes / 2) {
       const int u = plan->unroll / 2;
       const int ln = lanesFor(slotPayloadOf(proto, u));
-      if (ln < lanes || (ln > lanes && 2 * gridFor(ln) > capacity)) break;
+      if (ln < lanes || (ln > lanes && gridFor(ln) > c->numCUs)) break;
       plan->unroll = u;
       plan->slotBytes = slotBytesOf(proto, u);
       plan->slotPayload = slotPayloadOf(proto, u);

@@ -137,6 +137,18 @@ struct Plan {
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream);
 hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bool batch, int* blocksPerCU);
 
+// The kernel for a plan, element type and op, or nullptr; each family is
+// compiled in a translation unit of its own (ar_kernels_*.hip) so the build
+// runs them in parallel.
+typedef void (*KernelFn)(const KernelArgs);
+KernelFn pickRingAllReduceSimple(const Plan& plan, int dtype, int op);   // single call, Simple
+KernelFn pickRingAllReduceLL(const Plan& plan, int dtype, int op);       // single call, LL / LL128
+KernelFn pickRingAllReduceBatch(const Plan& plan, int dtype, int op);    // batched launch
+KernelFn pickRingReduceScatter(const Plan& plan, int dtype, int op);
+KernelFn pickRingAllGather(const Plan& plan, int dtype, int op);
+KernelFn pickTreeAllReduce(const Plan& plan, int dtype, int op);        // single call
+KernelFn pickTreeAllReduceBatch(const Plan& plan, int dtype, int op);   // batched launch
+
 inline int elemSize(int dtype) {
   switch (dtype) {
     case arInt32: case arFloat32: return 4;

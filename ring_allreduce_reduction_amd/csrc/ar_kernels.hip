@@ -1,1253 +1,25 @@
-// ar_kernels.hip -- the ring AllReduce data path for gfx950.
-//
-// What runs: one wavefront per ring member (virtual rank r, channel ch, lane
-// k).  A member walks the ring schedule of the pages ["NCCL 原始碼解讀：一個
-// AllReduce 的 GPU 旅程", ch.2 §2.3, RingARAlgorithm::getNextSendAddr and the
-// reduce-scatter / all-gather walkthrough]: at stage s it sends chunk
-// (r - 1 - s) mod N, so over 2N-1 stage slots it does
-//     send | recv-reduce-send x (N-2) | recv-reduce-copy-send |
-//     recv-copy-send x (N-2) | recv
-// and every transfer goes through a FIFO in HBM owned by the receiver,
-// with credits (head) and readiness (tail counter, or per-line flags for the
-// LL / LL128 wire formats) [same book, ch.2 §2.4, the send/recv memory with
-// head and tail counters on separate cache lines, and the LL / LL128 /
-// Simple protocols].
-//
-// Where it runs: the N members of one (channel, lane) sit in one workgroup
-// (N <= 16), so every producer/consumer pair shares a CU and its vector L1:
-// the FIFO handoff needs only workgroup-scope release/acquire, which on gfx950
-// is a plain ordered store / load, and there is no cross-workgroup wait at all
-// (no co-residency requirement, no deadlock from scheduling).  For N > 16 the
-// ring is cut into groups of up to 16 members; an edge between groups moves
-// its bytes with device-coherent loads and stores (no L2-wide cache
-// maintenance, see releaseEdge) and the launch is cooperative so that every
-// group is resident.
-//
-// Each member reads only its own send buffer, writes only its own receive
-// buffer and its successor's FIFO, so in-place use is safe: a member reads
-// chunk c of its input before it writes chunk c of its output.
+// ar_kernels.hip -- picks and launches the kernel of a plan.  The kernels
+// themselves (device code in ar_device.h) are compiled in the translation
+// units ar_kernels_*.hip, one per family.
 #include "ar_internal.h"
 
 namespace ar {
 namespace {
-
-typedef uint32_t u32;
-typedef uint64_t u64;
-typedef u32 v4u __attribute__((ext_vector_type(4)));
-typedef u32 v2u __attribute__((ext_vector_type(2)));
-
-// A step kind is the set of things a member does with one slot: read its
-// local operand, receive from its predecessor, send to its successor, write
-// its output.  AllReduce uses send / recv-reduce-send / recv-reduce-copy-send /
-// recv-copy-send / recv; ReduceScatter ends with recv-reduce-copy; AllGather
-// starts with copy-send.
-constexpr int kLocalBit = 1, kRecvBit = 2, kSendBit = 4, kOutBit = 8;
-enum Kind : int {
-  kSend = kLocalBit | kSendBit,
-  kRecvReduceSend = kLocalBit | kRecvBit | kSendBit,
-  kRecvReduceCopySend = kLocalBit | kRecvBit | kSendBit | kOutBit,
-  kRecvCopySend = kRecvBit | kSendBit | kOutBit,
-  kRecv = kRecvBit | kOutBit,
-  kRecvReduceCopy = kLocalBit | kRecvBit | kOutBit,
-  kCopySend = kLocalBit | kSendBit | kOutBit,
-};
-
-__device__ __forceinline__ u64 divUp(u64 x, u64 y) { return (x + y - 1) / y; }
-__device__ __forceinline__ u64 alignUp(u64 x, u64 a) { return divUp(x, a) * a; }
-__device__ __forceinline__ u64 umin(u64 a, u64 b) { return a < b ? a : b; }
-
-// ------------------------------------------------------------- element ops
-// Sum / Max / Min with acc the incoming partial and x the local value.
-// 16-bit floats widen exactly to f32, combine, and round back to nearest-even.
-
-__device__ __forceinline__ float bf16ToF32(u32 h) { return __uint_as_float(h << 16); }
-__device__ __forceinline__ u32 f32ToBf16(float f) {
-  u32 u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;   // quiet NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float f16ToF32(u32 h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-__device__ __forceinline__ u32 f32ToF16(float f) {
-  return (u32)__builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32: RNE, keeps subnormals
-}
-
-template <int DT, int OP>
-__device__ __forceinline__ u32 combineHalf(u32 acc, u32 x) {   // one 16-bit element
-  float a = DT == arBfloat16 ? bf16ToF32(acc) : f16ToF32(acc);
-  float b = DT == arBfloat16 ? bf16ToF32(x) : f16ToF32(x);
-  if (OP == arSum) {
-    float s = a + b;
-    return DT == arBfloat16 ? f32ToBf16(s) : f32ToF16(s);
-  }
-  if (OP == arMax) return (b > a) ? x : acc;
-  return (b < a) ? x : acc;
-}
-
-template <int DT, int OP>
-__device__ __forceinline__ u32 combineWord(u32 acc, u32 x) {   // one 32-bit word
-  if (DT == arFloat32) {
-    float a = __uint_as_float(acc), b = __uint_as_float(x);
-    if (OP == arSum) return __float_as_uint(a + b);
-    if (OP == arMax) return (b > a) ? x : acc;
-    return (b < a) ? x : acc;
-  } else if (DT == arInt32) {
-    if (OP == arSum) return acc + x;   // wraps
-    if (OP == arMax) return ((int)x > (int)acc) ? x : acc;
-    return ((int)x < (int)acc) ? x : acc;
-  } else {                             // two 16-bit elements
-    u32 lo = combineHalf<DT, OP>(acc & 0xffffu, x & 0xffffu);
-    u32 hi = combineHalf<DT, OP>(acc >> 16, x >> 16);
-    return lo | (hi << 16);
-  }
-}
-
-template <int DT, int OP>
-__device__ __forceinline__ v4u combine(v4u acc, v4u x) {
-  v4u r;
-  if (DT == arUint64) {                // probe: acc*16 + x on each 64-bit half
-    u64 a0 = ((u64)acc.y << 32) | acc.x, x0 = ((u64)x.y << 32) | x.x;
-    u64 a1 = ((u64)acc.w << 32) | acc.z, x1 = ((u64)x.w << 32) | x.z;
-    a0 = a0 * 16u + x0;
-    a1 = a1 * 16u + x1;
-    r.x = (u32)a0; r.y = (u32)(a0 >> 32); r.z = (u32)a1; r.w = (u32)(a1 >> 32);
-  } else {
-    r.x = combineWord<DT, OP>(acc.x, x.x);
-    r.y = combineWord<DT, OP>(acc.y, x.y);
-    r.z = combineWord<DT, OP>(acc.z, x.z);
-    r.w = combineWord<DT, OP>(acc.w, x.w);
-  }
-  return r;
-}
-
-// ------------------------------------------------------------- memory access
-// User buffers stream through once: non-temporal hints keep them from
-// evicting the FIFO slots, which are re-used and should stay in cache.
-
-__device__ __forceinline__ v4u ldNt16(const char* p) { return __builtin_nontemporal_load((const v4u*)p); }
-__device__ __forceinline__ v2u ldNt8(const char* p) { return __builtin_nontemporal_load((const v2u*)p); }
-__device__ __forceinline__ void stNt16(char* p, v4u v) { __builtin_nontemporal_store(v, (v4u*)p); }
-__device__ __forceinline__ void stNt8(char* p, v2u v) { __builtin_nontemporal_store(v, (v2u*)p); }
-
-// Load `pieceBytes` (16 or 8) user bytes at p of which `valid` are in range;
-// bytes past the range read as zero.  Element-wise when short or unaligned.
-template <int ESZ, bool NT>
-__device__ __forceinline__ v4u loadUser(const char* p, long valid, int pieceBytes, bool aligned) {
-  v4u v = {0u, 0u, 0u, 0u};
-  if (valid >= pieceBytes && aligned) {
-    if (pieceBytes == 16) {
-      v = NT ? ldNt16(p) : *(const v4u*)p;
-    } else {
-      v2u t = NT ? ldNt8(p) : *(const v2u*)p;
-      v.x = t.x; v.y = t.y;
-    }
-  } else if (valid > 0) {
-    u32 w[4] = {0u, 0u, 0u, 0u};
-    int nb = valid < pieceBytes ? (int)valid : pieceBytes;
-    for (int b = 0; b < nb; b += ESZ) {
-      if (ESZ == 2) {
-        u32 h = *(const uint16_t*)(p + b);
-        w[b >> 2] |= h << ((b & 2) * 8);
-      } else if (ESZ == 4) {
-        w[b >> 2] = *(const u32*)(p + b);
-      } else {
-        u64 d = *(const u64*)(p + b);
-        w[b >> 2] = (u32)d;
-        w[(b >> 2) + 1] = (u32)(d >> 32);
-      }
-    }
-    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
-  }
-  return v;
-}
-
-template <int ESZ, bool NT>
-__device__ __forceinline__ void storeUser(char* p, v4u v, long valid, int pieceBytes, bool aligned) {
-  if (valid >= pieceBytes && aligned) {
-    if (pieceBytes == 16) {
-      if (NT) stNt16(p, v);
-      else *(v4u*)p = v;
-    } else {
-      v2u t; t.x = v.x; t.y = v.y;
-      if (NT) stNt8(p, t);
-      else *(v2u*)p = t;
-    }
-  } else if (valid > 0) {
-    u32 w[4] = {v.x, v.y, v.z, v.w};
-    int nb = valid < pieceBytes ? (int)valid : pieceBytes;
-    for (int b = 0; b < nb; b += ESZ) {
-      if (ESZ == 2) {
-        *(uint16_t*)(p + b) = (uint16_t)(w[b >> 2] >> ((b & 2) * 8));
-      } else if (ESZ == 4) {
-        *(u32*)(p + b) = w[b >> 2];
-      } else {
-        *(u64*)(p + b) = (u64)w[b >> 2] | ((u64)w[(b >> 2) + 1] << 32);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------- flags
-// Scope of an edge: workgroup when producer and consumer share the
-// workgroup, agent otherwise.
-
-__device__ __forceinline__ u64 ldCounter(const u64* p, bool agent) {
-  u64 v = agent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  // every lane read the same word; make the value provably uniform
-  u32 lo = __builtin_amdgcn_readfirstlane((u32)v);
-  u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
-  return ((u64)hi << 32) | lo;
-}
-__device__ __forceinline__ void stRelaxed64(u64* p, u64 v, bool agent) {
-  if (agent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ u64 ldRelaxed64(const u64* p, bool agent) {
-  return agent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-               : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Edges inside a workgroup order their payload with workgroup-scope
-// release/acquire, which gfx950 compiles to ordered loads and stores with no
-// cache maintenance.
-//
-// Edges between workgroups never use agent-scope fences: on gfx950 an
-// agent-scope release writes back, and an acquire invalidates, the whole L2
-// of the XCD (buffer_wbl2 sc1 / buffer_inv sc1), which at every ring step
-// stalls every wavefront on that XCD.  Instead every byte that crosses such
-// an edge -- slot payload, LL words, LL128 flags, counters -- is moved by a
-// relaxed agent-scope atomic, which gfx950 issues as a plain load or store
-// with the sc1 bit: it is served at the device's coherence point rather than
-// by one XCD's L2, so it is coherent on its own.  What a release adds on top
-// is order: the producer waits until its payload stores have completed
-// (vmcnt(0)) before it stores the counter or flag that publishes them.  On
-// the consumer the payload loads are issued only after the counter or flag
-// read has returned the awaited value, as every wait loop branches on it.
-__device__ __forceinline__ void stCoh16(char* p, v4u v) {
-  __hip_atomic_store((u64*)p, ((u64)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store((u64*)p + 1, ((u64)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stCoh8(char* p, v2u v) {
-  __hip_atomic_store((u64*)p, ((u64)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ v4u ldCoh16(const char* p) {
-  const u64 a = __hip_atomic_load((const u64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const u64 b = __hip_atomic_load((const u64*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v4u{(u32)a, (u32)(a >> 32), (u32)b, (u32)(b >> 32)};
-}
-__device__ __forceinline__ v2u ldCoh8(const char* p) {
-  const u64 a = __hip_atomic_load((const u64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v2u{(u32)a, (u32)(a >> 32)};
-}
-
-// Before publishing what this wavefront stored for its peer.  Workgroup
-// edge: a workgroup-scope release.  Agent edge: the release keeps the
-// compiler from sinking the payload stores below the publishing store, and
-// s_waitcnt vmcnt(0) (gfx9 encoding 0x0F70: vmcnt 0, expcnt and lgkmcnt
-// untouched) holds the wavefront until they have completed.
-__device__ __forceinline__ void releaseEdge(bool agent) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  if (agent) __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-// After a counter or flag read returned the awaited value, before touching
-// what it publishes (or, for a credit, before overwriting the slot).  Both
-// kinds of edge need only the compiler ordering of a workgroup-scope acquire:
-// an agent edge's payload loads are device-coherent by themselves.
-__device__ __forceinline__ void acquireEdge() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
-
-// Credit: the receiver has drained a slot.  Its loads of the slot returned
-// before this point (their values were used by the stores that precede it).
-__device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
-  if (agent) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    stRelaxed64(p, v, true);
-  } else {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-}
-
-// Bounded waiting.  Every spin sleeps briefly; every 256 spins the abort word
-// and the wall clock are checked, and a hard cap on spins backs the clock up.
-// On give-up the member records why and the caller returns, so every
-// wavefront of the kernel always exits.
-struct Waiter {
-  u32 spins = 0;
-  u64 t0 = 0;
-};
-
-__device__ __forceinline__ bool keepWaiting(Control* ctrl, u64 timeoutTicks, Waiter& w) {
-  if (w.spins == 0) w.t0 = wall_clock64();
-  ++w.spins;
-  __builtin_amdgcn_s_sleep(1);
-  if ((w.spins & 255u) == 0) {
-    u32 ab = __hip_atomic_load(&ctrl->abortFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    u32 code = 0;
-    if (__builtin_amdgcn_readfirstlane(ab) != 0) code = kStatusAbort;
-    else if (wall_clock64() - w.t0 > timeoutTicks || w.spins >= (1u << 30)) code = kStatusTimeout;
-    if (code != 0) {
-      __hip_atomic_store(&ctrl->status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      return false;
-    }
-  }
-  return true;
-}
-
-// Wait until *p >= target.
-__device__ __forceinline__ bool waitGeq(const KernelArgs& a, const u64* p, u64 target, bool agent) {
-  if (ldCounter(p, agent) >= target) return true;
-  Waiter w;
-  while (true) {
-    if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-    if (ldCounter(p, agent) >= target) return true;
-  }
-}
-
-// Workgroup -> (lane id L, group g).  With several groups per lane, the
-// groups of one lane get workgroup ids congruent mod 8, i.e. the same XCD
-// under round-robin dispatch, so their edges stay in one L2: a locality hint
-// only, the edges between workgroups are device-coherent wherever the groups
-// run.  a.groupSpread gives them consecutive ids instead, i.e. different
-// XCDs, which exercises exactly that.
-__device__ __forceinline__ void laneAndGroup(const KernelArgs& a, int& L, int& g) {
-  if (a.nGroups == 1) {
-    L = blockIdx.x;
-    g = 0;
-  } else if (a.groupSpread) {
-    g = blockIdx.x % a.nGroups;
-    L = blockIdx.x / a.nGroups;
-  } else {
-    const int x = blockIdx.x % 8;
-    g = (blockIdx.x / 8) % a.nGroups;
-    L = (blockIdx.x / (8 * a.nGroups)) * 8 + x;
-  }
-}
-
-// ------------------------------------------------------------- one member
-
-struct Member {
-  int lane;
-  char* rfifo;        // my FIFO (predecessor writes it)
-  char* sfifo;        // successor's FIFO (I write it)
-  Conn* self;
-  Conn* succ;
-  u64 recvStep;       // slots consumed from my FIFO so far (== self->head)
-  u64 sendStep;       // slots written into the successor's FIFO (== succ->tail)
-  u32 recvSlot;       // recvStep % nSlots
-  u32 sendSlot;       // sendStep % nSlots
-  u64 succHead;       // last value read from succ->head; head only grows, so
-                      // a stale copy never over-reports free slots
-  bool recvAgent;
-  bool sendAgent;
-  bool aligned;
-  bool direct;
-};
-
-// CACHED: skip the poll while the last credit read still covers this slot.
-template <bool CACHED>
-__device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
-  // slot sendStep % nSlots is free once the successor consumed step sendStep - nSlots
-  u64 need = m.sendStep + 1 > (u64)a.nSlots ? m.sendStep + 1 - (u64)a.nSlots : 0;
-  if (CACHED) {
-    if (m.succHead >= need) return true;   // ordered by the acquire after that read
-    m.succHead = ldCounter(&m.succ->head, m.sendAgent);
-    if (m.succHead < need) {
-      Waiter w;
-      do {
-        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-        m.succHead = ldCounter(&m.succ->head, m.sendAgent);
-      } while (m.succHead < need);
-    }
-  } else if (!waitGeq(a, &m.succ->head, need, m.sendAgent)) {
-    return false;
-  }
-  acquireEdge();
-  return true;
-}
-
-__device__ __forceinline__ void advanceSend(const KernelArgs& a, Member& m) {
-  ++m.sendStep;
-  if (++m.sendSlot == (u32)a.nSlots) m.sendSlot = 0;
-}
-__device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
-  ++m.recvStep;
-  if (m.lane == 0) stCounterRelease(&m.self->head, m.recvStep, m.recvAgent);
-  if (++m.recvSlot == (u32)a.nSlots) m.recvSlot = 0;
-}
-
-// One FIFO step of `kind`; `valid` payload bytes start at inp / outp (and at
-// succOutp in the successor's output, for a direct all-gather step).
-template <int PROTO, int DT, int OP, int U>
-__device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, const char* inp, char* outp,
-                                     char* succOutp, long valid) {
-  constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
-  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
-  const bool hasLocal = (kind & kLocalBit) != 0;
-  const bool hasRecv = (kind & kRecvBit) != 0;
-  const bool hasSend = (kind & kSendBit) != 0;
-  const bool hasOut = (kind & kOutBit) != 0;
-  // Direct all-gather (Simple): the member that finishes a chunk and every
-  // member forwarding it write the successor's output buffer instead of its
-  // FIFO, so the all-gather half moves no FIFO bytes; the receiver then
-  // reads the finished chunk from its own output.  [The pages' FIFO slot
-  // descriptor can carry a pointer, and a work item can be flagged direct.]
-  // An edge between workgroups always goes through the FIFO (both of its
-  // ends see the same sendAgent / recvAgent, so they agree on it).
-  const bool directSend = PROTO == kSimple && m.direct && !m.sendAgent && hasSend && hasOut;
-  const bool directRecv = PROTO == kSimple && m.direct && !m.recvAgent && hasRecv && hasOut && !hasLocal;
-  const int lane = m.lane;
-
-  // piece geometry of this lane: payload offset, payload bytes, wire offset
-  int payOff[U], payBytes[U], wireOff[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (PROTO == kSimple) {
-      payOff[u] = (u * kWave + lane) * 16; payBytes[u] = 16; wireOff[u] = payOff[u];
-    } else if (PROTO == kLL) {
-      payOff[u] = (u * kWave + lane) * 8; payBytes[u] = 8; wireOff[u] = (u * kWave + lane) * 16;
-    } else {
-      const int line = lane >> 3, j = lane & 7;
-      payOff[u] = u * kLL128UnitPayload + (j < 7 ? (line * 7 + j) * 16 : 896 + line * 8);
-      payBytes[u] = j < 7 ? 16 : 8;
-      wireOff[u] = u * kLL128UnitBytes + lane * 16;
-    }
-  }
-
-  // EARLY: the local operand depends on no flag, so start its loads before
-  // the credit wait and keep the last credit read.  Measured on 8 ranks: LL
-  // steps 7% shorter; the 8 KiB Simple slot 0.5% faster at 256 MiB per rank
-  // (104 VGPRs, no spill); LL128 steps longer (its 1 KiB units hold more
-  // registers across the wait) and small Simple slots 3% slower on short
-  // messages, so those keep the plain order.
-  constexpr bool EARLY = PROTO == kLL || (PROTO == kSimple && U == 8);
-  if (!EARLY && hasSend && !directSend && !waitCredit<false>(a, m)) return false;
-
-  v4u v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    v[u] = hasLocal ? loadUser<ESZ, true>(inp + payOff[u], valid - payOff[u], payBytes[u], m.aligned)
-                    : v4u{0u, 0u, 0u, 0u};
-  }
-  if (EARLY && hasSend && !directSend && !waitCredit<true>(a, m)) return false;
-
-  if (hasRecv) {
-    const char* slot = m.rfifo + (size_t)m.recvSlot * SLOT;
-    v4u in[U];
-    if (PROTO == kSimple) {
-      if (!waitGeq(a, &m.self->tail, m.recvStep + 1, m.recvAgent)) return false;
-      acquireEdge();
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (directRecv)   // the predecessor wrote it into my output
-          in[u] = kind == kRecvCopySend
-                      ? loadUser<ESZ, false>(outp + payOff[u], valid - payOff[u], 16, m.aligned)
-                      : v4u{0u, 0u, 0u, 0u};
-        else
-          in[u] = payOff[u] < valid ? (m.recvAgent ? ldCoh16(slot + wireOff[u]) : *(const v4u*)(slot + wireOff[u]))
-                                    : v4u{0u, 0u, 0u, 0u};
-      }
-    } else if (PROTO == kLL) {
-      const u32 flag = (u32)(m.recvStep + 1);
-      bool done[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) { done[u] = payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
-      Waiter w;
-      while (true) {
-        bool all = true;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (!done[u]) {
-            const u64* line = (const u64*)(slot + wireOff[u]);
-            u64 w0 = ldRelaxed64(line, m.recvAgent);
-            u64 w1 = ldRelaxed64(line + 1, m.recvAgent);
-            if ((u32)(w0 >> 32) == flag && (u32)(w1 >> 32) == flag) {
-              in[u].x = (u32)w0; in[u].y = (u32)w1; done[u] = true;
-            } else {
-              all = false;
-            }
-          }
-        }
-        if (__all(all)) break;
-        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-      }
-    } else {  // LL128: poll the flag of every live line, then read payload
-      const u64 flag = m.recvStep + 1;
-      const bool flagLane = (lane & 7) == 7;
-      bool done[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
-      Waiter w;
-      while (true) {
-        bool all = true;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (!done[u]) {
-            if (ldRelaxed64((const u64*)(slot + wireOff[u] + 8), m.recvAgent) == flag) done[u] = true;
-            else all = false;
-          }
-        }
-        if (__all(all)) break;
-        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-      }
-      acquireEdge();
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        in[u] = v4u{0u, 0u, 0u, 0u};
-        if (u * kLL128UnitPayload < valid) {
-          if (payBytes[u] == 16) {
-            in[u] = m.recvAgent ? ldCoh16(slot + wireOff[u]) : *(const v4u*)(slot + wireOff[u]);
-          } else {
-            v2u t = m.recvAgent ? ldCoh8(slot + wireOff[u]) : *(const v2u*)(slot + wireOff[u]);
-            in[u].x = t.x; in[u].y = t.y;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = hasLocal ? combine<DT, OP>(in[u], v[u]) : in[u];
-  }
-
-  if (hasOut && !directRecv) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      storeUser<ESZ, true>(outp + payOff[u], v[u], valid - payOff[u], payBytes[u], m.aligned);
-  }
-
-  if (hasSend) {
-    char* slot = m.sfifo + (size_t)m.sendSlot * SLOT;
-    if (PROTO == kSimple) {
-      if (directSend) {
-        // the successor reads this back at its next stage: keep it cacheable
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          storeUser<ESZ, false>(succOutp + payOff[u], v[u], valid - payOff[u], 16, m.aligned);
-      } else if (m.sendAgent) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (payOff[u] < valid) stCoh16(slot + wireOff[u], v[u]);
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
-      }
-      releaseEdge(m.sendAgent);
-      if (lane == 0) stRelaxed64(&m.succ->tail, m.sendStep + 1, m.sendAgent);
-    } else if (PROTO == kLL) {
-      const u64 flag = (u64)(u32)(m.sendStep + 1) << 32;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (payOff[u] < valid) {
-          u64* line = (u64*)(slot + wireOff[u]);
-          stRelaxed64(line, flag | v[u].x, m.sendAgent);
-          stRelaxed64(line + 1, flag | v[u].y, m.sendAgent);
-        }
-      }
-    } else {  // LL128: payload, release, then the flag word of each live line
-      const bool flagLane = (lane & 7) == 7;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (u * kLL128UnitPayload < valid) {
-          if (payBytes[u] == 16) {
-            if (m.sendAgent) stCoh16(slot + wireOff[u], v[u]);
-            else *(v4u*)(slot + wireOff[u]) = v[u];
-          } else {
-            v2u t; t.x = v[u].x; t.y = v[u].y;
-            if (m.sendAgent) stCoh8(slot + wireOff[u], t);
-            else *(v2u*)(slot + wireOff[u]) = t;
-          }
-        }
-      }
-      releaseEdge(m.sendAgent);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (flagLane && u * kLL128UnitPayload < valid)
-          stRelaxed64((u64*)(slot + wireOff[u] + 8), m.sendStep + 1, m.sendAgent);
-    }
-    advanceSend(a, m);
-  }
-
-  if (hasRecv) finishRecv(a, m);
-  return true;
-}
-
-// One collective of the ring schedule over one member's (channel, lane)
-// share of `count` elements per rank; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL>
-__device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, int ch, int k, u64 count,
-                                         const char* in, char* out, char* succOut) {
-  constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
-  constexpr u64 A = 16 / ESZ;   // 16-byte grain in elements
-  constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
-                        : PROTO == kLL ? kLLSlotPayload : U * kLL128UnitPayload;
-  const int N = a.nranks;
-  const int succ = r + 1 == N ? 0 : r + 1;
-  // channel share [pages: contiguous split per channel, 16-byte grain]
-  const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
-  const u64 lo = umin((u64)ch * per, count);
-  const u64 hi = umin(lo + per, count);
-  const u64 len = hi - lo;
-  if (len == 0) return true;
-
-  const u64 C = a.chunkElems;
-  const u64 loopSize = (u64)N * C;
-  const int lastSendStage = 2 * N - 3;
-
-  // Pipelining.  A member's share of a chunk is cut into slot-sized
-  // columns; a batch of at most nSlots/2 columns goes through all 2N-1 stages
-  // before the next batch starts (the pages size a chunk to half the FIFO for
-  // the same reason).  A member then never has more than nSlots/2 sends that
-  // its successor has not matched with receives, so no FIFO can fill up
-  // around the whole ring and the pipeline cannot deadlock, whatever the
-  // chunk size.  The order in which ranks are folded into an element is that
-  // of the stage schedule and does not depend on the batching.
-  const u64 batch = (u64)(a.nSlots / 2 > 0 ? a.nSlots / 2 : 1);
-  if (COLL == kCollAllReduce) {
-    for (u64 off = 0; off < len; off += loopSize) {
-      const u64 rem = len - off;
-      // shrunk chunk on the last partial loop [pages: getNextSendAddr]
-      const u64 cur = rem < loopSize ? alignUp(divUp(rem, (u64)N), A) : C;
-      // no lane share of any chunk in this loop exceeds sub0 (chunk 0 is the
-      // longest chunk and a share is at most the per-lane split of its chunk)
-      const u64 sub0 = alignUp(divUp(umin(cur, rem), (u64)a.lanes), A);
-      const u64 nCols = divUp(sub0 * ESZ, (u64)PAYLOAD);
-      for (u64 jb = 0; jb < nCols; jb += batch) {
-        const u64 je = umin(jb + batch, nCols);
-        for (int s = 0; s <= 2 * N - 2; ++s) {
-          int kind;
-          if (s == 0) kind = kSend;
-          else if (s < N - 1) kind = kRecvReduceSend;
-          else if (s == N - 1) kind = kRecvReduceCopySend;
-          else if (s <= lastSendStage) kind = kRecvCopySend;
-          else kind = kRecv;
-          // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
-          const int c = s <= lastSendStage ? (r - 1 - s + 2 * N) % N : succ;
-          const u64 cb = (u64)c * cur;
-          const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
-          // lane k's share of the chunk (pipelining only: the order is per element)
-          const u64 sub = alignUp(divUp(clen, (u64)a.lanes), A);
-          const u64 sb = umin((u64)k * sub, clen);
-          const u64 se = umin(sb + sub, clen);
-          const u64 bytes = (se - sb) * ESZ;
-          const u64 first = (lo + off + cb + sb) * ESZ;
-          for (u64 j = jb; j < je; ++j) {
-            const u64 b = j * (u64)PAYLOAD;
-            if (b >= bytes) break;
-            const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U>(a, m, kind, in + first + b, out + first + b, succOut + first + b, valid))
-              return false;
-          }
-        }
-      }
-    }
-  } else {
-    // ReduceScatter / AllGather, the two halves of the ring on their own
-    // [pages: nSteps = nRanks-1 for them].  Every stage works on the same
-    // element range of a different rank block (block = `count` elements):
-    //   ReduceScatter: send | recv-reduce-send x (N-2) | recv-reduce-copy, on
-    //                  block (r - 1 - s) mod N, so block b ends at its owner b;
-    //   AllGather:     copy-send | recv-copy-send x (N-2) | recv, on block
-    //                  (r - s) mod N, so block b starts at its owner b.
-    constexpr bool rs = COLL == kCollReduceScatter;
-    const u64 blk = count * ESZ;
-    for (u64 off = 0; off < len; off += C) {
-      const u64 cur = umin(C, len - off);
-      const u64 sub = alignUp(divUp(cur, (u64)a.lanes), A);
-      const u64 sb = umin((u64)k * sub, cur);
-      const u64 se = umin(sb + sub, cur);
-      const u64 bytes = (se - sb) * ESZ;
-      const u64 first = (lo + off + sb) * ESZ;   // byte offset inside a block
-      const u64 nCols = divUp(bytes, (u64)PAYLOAD);
-      for (u64 jb = 0; jb < nCols; jb += batch) {
-        const u64 je = umin(jb + batch, nCols);
-        for (int s = 0; s <= N - 1; ++s) {
-          int kind, blkIdx;
-          if (rs) {
-            kind = s == 0 ? kSend : s < N - 1 ? kRecvReduceSend : kRecvReduceCopy;
-            blkIdx = (r - 1 - s + 2 * N) % N;
-          } else {
-            kind = s == 0 ? kCopySend : s < N - 1 ? kRecvCopySend : kRecv;
-            blkIdx = (r - s + N) % N;
-          }
-          // ReduceScatter reads block b of its input and writes its one
-          // output block; AllGather reads its one input block and writes block b
-          const u64 inOff = rs ? (u64)blkIdx * blk + first : first;
-          const u64 outOff = rs ? first : (u64)blkIdx * blk + first;
-          for (u64 j = jb; j < je; ++j) {
-            const u64 b = j * (u64)PAYLOAD;
-            const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U>(a, m, kind, in + inOff + b, out + outOff + b, succOut + outOff + b,
-                                         valid))
-              return false;
-          }
-        }
-      }
-    }
-  }
-  return true;
-}
-
-// BATCH: the launch runs the a.nTasks AllReduces of one aggregate, each
-// described by a row of a.tasks {count, send[N], recv[N]}.  a.taskSlots of
-// them run at once, each on its own nChannels x lanes wavefront sets (and
-// FIFOs); a set takes tasks slot, slot + taskSlots, ... in turn, so its FIFO
-// steps simply continue from one task to the next.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH>
-__global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
-  // The 8 KiB slot kernels read the wavefront index through readfirstlane,
-  // so every per-member value (pointers, counters, rank, channel) lives in
-  // scalar registers: that keeps them at 101-120 VGPRs instead of spilling.
-  // Smaller slots keep the plain index: with their register room, per-member
-  // state in VGPRs measured faster on short messages (the CU's scalar unit
-  // is shared by all of its wavefronts' polling loops).
-  const int wave = U == 8 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
-  const int N = a.nranks;
-  const int perTask = a.nChannels * a.lanes;
-  const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
-
-  int L, g;   // FIFO set and group
-  laneAndGroup(a, L, g);
-  // A single call's workgroups may be fewer than its (channel, lane) pairs:
-  // set L then runs pairs L, L + sets, L + 2 sets, ... on the same FIFOs,
-  // whose steps simply continue from one pair to the next.
-  const int sets = BATCH ? lanesTotal : a.laneSets;
-  if (L >= sets) return;
-  const int r = g * a.groupSize + wave;
-  if (r >= N || r == a.deadRank) return;
-  const int succ = r + 1 == N ? 0 : r + 1;
-  const int pred = r == 0 ? N - 1 : r - 1;
-
-  Member m;
-  m.lane = threadIdx.x % kWave;
-  const size_t wSelf = (size_t)L * N + r, wSucc = (size_t)L * N + succ;
-  m.rfifo = a.fifo + wSelf * a.fifoWorkerBytes;
-  m.sfifo = a.fifo + wSucc * a.fifoWorkerBytes;
-  m.self = a.conn + wSelf;
-  m.succ = a.conn + wSucc;
-  // The 8 KiB Simple kernel serves single-workgroup rings only (the host
-  // never plans it for a ring cut into groups), so it carries no code for
-  // edges between workgroups.
-  constexpr bool GROUPED = PROTO != kSimple || U <= kGroupedSimpleUnrollMax;
-  m.recvAgent = GROUPED && pred / a.groupSize != g;
-  m.sendAgent = GROUPED && succ / a.groupSize != g;
-  m.aligned = a.aligned16 != 0;
-  m.direct = a.direct != 0;
-  // counters carry over from earlier calls (tail == head at call boundaries)
-  m.recvStep = ldCounter(&m.self->head, true);
-  m.sendStep = ldCounter(&m.succ->tail, true);
-  m.succHead = 0;
-  m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
-  m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
-
-  if (!BATCH) {
-    for (int Lp = L; Lp < lanesTotal; Lp += sets) {
-      if (!ringPass<PROTO, DT, OP, U, COLL>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count, (const char*)a.send[r],
-                                            (char*)a.recv[r], (char*)a.recv[succ]))
-        return;
-    }
-  } else {
-    const int Lc = L % perTask;   // (channel, lane) inside the task
-    const int ch = Lc / a.lanes;
-    const int k = Lc % a.lanes;
-    const size_t row = 1 + 2 * (size_t)N;
-    for (int t = L / perTask; t < a.nTasks; t += a.taskSlots) {
-      const u64* d = a.tasks + (size_t)t * row;
-      if (!ringPass<PROTO, DT, OP, U, COLL>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
-                                            (char*)d[1 + N + succ]))
-        return;
-    }
-  }
-  // LL / LL128 never touch the tail counter per slot: publish it once so the
-  // next call starts both ends of this FIFO at the same step.
-  if (PROTO != kSimple && m.lane == 0) stRelaxed64(&m.succ->tail, m.sendStep, true);
-}
-
-// ------------------------------------------------------------- tree AllReduce
-//
-// The pages' second algorithm ["NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程",
-// ch.4 "Ring 與 Tree：把搜尋結果變成演算法拓撲", ncclGetBtree / ncclGetDtree;
-// "NCCL Tree拓扑介绍", single and double binary trees].  Each virtual rank is
-// a tree node and, as in the ring, one wavefront per (rank, channel, lane).
-// Reduce: a node folds the partials its children send (d0 first, then d1)
-// and then its own value, OP(OP(p_d0, p_d1), x), and sends the result to its
-// parent; the root's result is the answer, which it writes and sends back
-// down; every other node receives it from its parent, writes it and forwards
-// it to its children.  The first half of the channels runs on the first
-// tree, the second half on the second (mirrored for an even rank count,
-// shifted by one rank for an odd one).
-//
-// FIFOs: a node owns three, one per incoming edge (from d0, from d1, from its
-// parent), at worker index (lane * N + rank) * 3 + edge, with the same slot
-// and counter layout as the ring's.  A member works through its lane share
-// in batches of nSlots columns: the reduce pass of a batch, then its
-// broadcast pass.  A member starts batch b+1 only after its broadcast pass of
-// batch b, which needs data its parent sent after consuming the member's
-// batch-b columns and, in turn, after its children consumed its batch-b
-// broadcast; so no edge ever holds more than one batch and neither pass can
-// wait on the other: the tree cannot deadlock for any size.
-
-// Binary tree over ranks [pages: ncclGetBtree]: with `bit` the lowest set
-// bit of r (for the root r = 0, the first power of two >= n), the parent
-// clears `bit` and sets the next bit up (or only clears it, if that is out
-// of range); the children are r - bit/2 and r + h for the largest power of
-// two h <= bit/2 with r + h < n.  The root's only child is bit/2, named d1.
-__device__ __forceinline__ void btreeNode(int n, int r, int& up, int& d0, int& d1) {
-  up = d0 = d1 = -1;
-  if (r == 0) {
-    if (n > 1) d1 = (int)((1u << (32 - __builtin_clz((u32)n - 1u))) >> 1);   // bit_ceil(n) / 2
-    return;
-  }
-  const int bit = r & -r;
-  up = (r & ~bit) | (bit << 1);
-  if (up >= n) up = r & ~bit;
-  const int h = bit >> 1;
-  if (h == 0) return;
-  d0 = r - h;
-  const int room = n - 1 - r;   // r + h' < n  <=>  h' <= room
-  if (room >= 1) d1 = r + (int)(1u << (31 - __builtin_clz((u32)(h < room ? h : room))));   // bit_floor
-}
-
-// Tree t of the double tree [pages: ncclGetDtree]: tree 1 relabels rank x as
-// n-1-x (even n) or x-1 (odd n), takes the binary tree of the relabelled
-// rank and maps every peer back.
-__device__ __forceinline__ void dtreeNode(int n, int r, int t, int& up, int& d0, int& d1) {
-  if (t == 0) {
-    btreeNode(n, r, up, d0, d1);
-    return;
-  }
-  const bool mirror = (n & 1) == 0;
-  btreeNode(n, mirror ? n - 1 - r : (r == 0 ? n - 1 : r - 1), up, d0, d1);
-  auto back = [&](int x) { return x < 0 ? -1 : mirror ? n - 1 - x : (x + 1 == n ? 0 : x + 1); };
-  up = back(up);
-  d0 = back(d0);
-  d1 = back(d1);
-}
-
-// One end of one FIFO.
-struct Edge {
-  char* fifo;   // slot 0 (the FIFO is owned by the receiving end)
-  Conn* conn;   // its counters
-  u64 step;     // next step on this FIFO
-  u32 slot;     // step % nSlots
-  bool agent;   // the other end is in another workgroup
-};
-
-__device__ __forceinline__ Edge openEdge(const KernelArgs& a, size_t worker, bool agent, bool recvEnd) {
-  Edge e;
-  e.fifo = a.fifo + worker * a.fifoWorkerBytes;
-  e.conn = a.conn + worker;
-  // counters carry over from earlier calls (tail == head at call boundaries)
-  e.step = ldCounter(recvEnd ? &e.conn->head : &e.conn->tail, true);
-  e.slot = (u32)(e.step % (u64)a.nSlots);
-  e.agent = agent;
-  return e;
-}
-
-template <int PROTO, int U>
-struct Pieces {   // this lane's pieces of one slot (as in the ring's step)
-  int payOff[U], payBytes[U], wireOff[U];
-  __device__ __forceinline__ explicit Pieces(int lane) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (PROTO == kSimple) {
-        payOff[u] = (u * kWave + lane) * 16; payBytes[u] = 16; wireOff[u] = payOff[u];
-      } else if (PROTO == kLL) {
-        payOff[u] = (u * kWave + lane) * 8; payBytes[u] = 8; wireOff[u] = (u * kWave + lane) * 16;
-      } else {
-        const int line = lane >> 3, j = lane & 7;
-        payOff[u] = u * kLL128UnitPayload + (j < 7 ? (line * 7 + j) * 16 : 896 + line * 8);
-        payBytes[u] = j < 7 ? 16 : 8;
-        wireOff[u] = u * kLL128UnitBytes + lane * 16;
-      }
-    }
-  }
-};
-
-template <int PROTO, int U>
-__device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, const Pieces<PROTO, U>& pc, int lane,
-                                         long valid, v4u (&in)[U]) {
-  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
-  const char* slot = e.fifo + (size_t)e.slot * SLOT;
-  if (PROTO == kSimple) {
-    if (!waitGeq(a, &e.conn->tail, e.step + 1, e.agent)) return false;
-    acquireEdge();
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      in[u] = pc.payOff[u] >= valid ? v4u{0u, 0u, 0u, 0u}
-              : e.agent            ? ldCoh16(slot + pc.wireOff[u])
-                                   : *(const v4u*)(slot + pc.wireOff[u]);
-  } else if (PROTO == kLL) {
-    const u32 flag = (u32)(e.step + 1);
-    bool done[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) { done[u] = pc.payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
-    Waiter w;
-    while (true) {
-      bool all = true;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!done[u]) {
-          const u64* line = (const u64*)(slot + pc.wireOff[u]);
-          const u64 w0 = ldRelaxed64(line, e.agent);
-          const u64 w1 = ldRelaxed64(line + 1, e.agent);
-          if ((u32)(w0 >> 32) == flag && (u32)(w1 >> 32) == flag) {
-            in[u].x = (u32)w0; in[u].y = (u32)w1; done[u] = true;
-          } else {
-            all = false;
-          }
-        }
-      }
-      if (__all(all)) break;
-      if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-    }
-  } else {
-    const u64 flag = e.step + 1;
-    const bool flagLane = (lane & 7) == 7;
-    bool done[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
-    Waiter w;
-    while (true) {
-      bool all = true;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!done[u]) {
-          if (ldRelaxed64((const u64*)(slot + pc.wireOff[u] + 8), e.agent) == flag) done[u] = true;
-          else all = false;
-        }
-      }
-      if (__all(all)) break;
-      if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-    }
-    acquireEdge();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      in[u] = v4u{0u, 0u, 0u, 0u};
-      if (u * kLL128UnitPayload < valid) {
-        if (pc.payBytes[u] == 16) {
-          in[u] = e.agent ? ldCoh16(slot + pc.wireOff[u]) : *(const v4u*)(slot + pc.wireOff[u]);
-        } else {
-          const v2u t = e.agent ? ldCoh8(slot + pc.wireOff[u]) : *(const v2u*)(slot + pc.wireOff[u]);
-          in[u].x = t.x; in[u].y = t.y;
-        }
-      }
-    }
-  }
-  return true;
-}
-
-__device__ __forceinline__ void edgeFinishRecv(const KernelArgs& a, Edge& e, int lane) {
-  ++e.step;
-  if (lane == 0) stCounterRelease(&e.conn->head, e.step, e.agent);
-  if (++e.slot == (u32)a.nSlots) e.slot = 0;
-}
-
-template <int PROTO, int U>
-__device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pieces<PROTO, U>& pc, int lane,
-                                         long valid, const v4u (&v)[U]) {
-  constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
-  // slot step % nSlots is free once the receiver consumed step - nSlots
-  const u64 need = e.step + 1 > (u64)a.nSlots ? e.step + 1 - (u64)a.nSlots : 0;
-  if (!waitGeq(a, &e.conn->head, need, e.agent)) return false;
-  acquireEdge();
-  char* slot = e.fifo + (size_t)e.slot * SLOT;
-  if (PROTO == kSimple) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (pc.payOff[u] < valid) {
-        if (e.agent) stCoh16(slot + pc.wireOff[u], v[u]);
-        else *(v4u*)(slot + pc.wireOff[u]) = v[u];
-      }
-    }
-    releaseEdge(e.agent);
-    if (lane == 0) stRelaxed64(&e.conn->tail, e.step + 1, e.agent);
-  } else if (PROTO == kLL) {
-    const u64 flag = (u64)(u32)(e.step + 1) << 32;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (pc.payOff[u] < valid) {
-        u64* line = (u64*)(slot + pc.wireOff[u]);
-        stRelaxed64(line, flag | v[u].x, e.agent);
-        stRelaxed64(line + 1, flag | v[u].y, e.agent);
-      }
-    }
-  } else {
-    const bool flagLane = (lane & 7) == 7;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u * kLL128UnitPayload < valid) {
-        if (pc.payBytes[u] == 16) {
-          if (e.agent) stCoh16(slot + pc.wireOff[u], v[u]);
-          else *(v4u*)(slot + pc.wireOff[u]) = v[u];
-        } else {
-          v2u t; t.x = v[u].x; t.y = v[u].y;
-          if (e.agent) stCoh8(slot + pc.wireOff[u], t);
-          else *(v2u*)(slot + pc.wireOff[u]) = t;
-        }
-      }
-    }
-    releaseEdge(e.agent);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (flagLane && u * kLL128UnitPayload < valid)
-        stRelaxed64((u64*)(slot + pc.wireOff[u] + 8), e.step + 1, e.agent);
-  }
-  ++e.step;
-  if (++e.slot == (u32)a.nSlots) e.slot = 0;
-  return true;
-}
-
-// A tree node's FIFO ends and peers (independent of the data).
-struct TreeNode {
-  int up, d[2];
-  Edge fromChild[2], toChild[2], fromParent, toParent;
-};
-
-// One AllReduce over one member's (channel, lane) share of `count` elements
-// per rank: batches of nSlots columns, each a reduce pass then (below the
-// root) a broadcast pass; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U>
-__device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int ch, int k, int lane, u64 count,
-                                         const char* inBase, char* outBase) {
-  constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
-  constexpr u64 A = 16 / ESZ;
-  constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
-                        : PROTO == kLL ? kLLSlotPayload : U * kLL128UnitPayload;
-  const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
-  const u64 lo = umin((u64)ch * per, count);
-  const u64 len = umin(lo + per, count) - lo;
-  const u64 sub = alignUp(divUp(len, (u64)a.lanes), A);
-  const u64 sb = umin((u64)k * sub, len);
-  const u64 bytes = (umin(sb + sub, len) - sb) * ESZ;
-  if (bytes == 0) return true;
-
-  const bool leaf = nd.d[0] < 0 && nd.d[1] < 0;
-  const char* in = inBase + (lo + sb) * ESZ;
-  char* out = outBase + (lo + sb) * ESZ;
-  const bool aligned = a.aligned16 != 0;
-  const Pieces<PROTO, U> pc(lane);
-  const u64 nCols = divUp(bytes, (u64)PAYLOAD);
-  const u64 batch = (u64)a.nSlots;
-  v4u acc[U], x[U];
-  for (u64 jb = 0; jb < nCols; jb += batch) {
-    const u64 je = umin(jb + batch, nCols);
-    // reduce pass: children's partials, then my own value; up (or, at the
-    // root, straight into the broadcast)
-    for (u64 j = jb; j < je; ++j) {
-      const u64 b = j * (u64)PAYLOAD;
-      const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        x[u] = loadUser<ESZ, true>(in + b + pc.payOff[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
-      if (leaf) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = x[u];
-      } else {
-        bool have = false;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          if (nd.d[i] < 0) continue;
-          v4u got[U];
-          if (!edgeRecv<PROTO, U>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
-          edgeFinishRecv(a, nd.fromChild[i], lane);
-#pragma unroll
-          for (int u = 0; u < U; ++u) acc[u] = have ? combine<DT, OP>(acc[u], got[u]) : got[u];
-          have = true;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = combine<DT, OP>(acc[u], x[u]);
-      }
-      if (nd.up >= 0) {
-        if (!edgeSend<PROTO, U>(a, nd.toParent, pc, lane, valid, acc)) return false;
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          if (nd.d[i] >= 0 && !edgeSend<PROTO, U>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
-      }
-    }
-    if (nd.up < 0) continue;
-    // broadcast pass: the result from the parent, to my output and children
-    for (u64 j = jb; j < je; ++j) {
-      const u64 b = j * (u64)PAYLOAD;
-      const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-      if (!edgeRecv<PROTO, U>(a, nd.fromParent, pc, lane, valid, acc)) return false;
-      edgeFinishRecv(a, nd.fromParent, lane);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (nd.d[i] >= 0 && !edgeSend<PROTO, U>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
-    }
-  }
-  return true;
-}
-
-// BATCH as for the ring kernel: a.nTasks AllReduces from a.tasks, a.taskSlots
-// of them at once.
-template <int PROTO, int DT, int OP, int U, bool BATCH>
-__global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
-  // as in the ring kernel: scalar member state for the largest (4 KiB) slot
-  const int wave = U == 4 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int N = a.nranks;
-  const int perTask = a.nChannels * a.lanes;
-  const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
-
-  int L, g;   // (lane id, group), as in the ring kernel
-  laneAndGroup(a, L, g);
-  if (L >= lanesTotal) return;
-  const int r = g * a.groupSize + wave;
-  if (r >= N || r == a.deadRank) return;
-  const int Lc = BATCH ? L % perTask : L;   // (channel, lane) inside the task
-  const int ch = Lc / a.lanes;
-  const int k = Lc % a.lanes;
-
-  // this member's place in its channel's tree
-  TreeNode nd;
-  const int t = a.nChannels > 1 && 2 * ch >= a.nChannels ? 1 : 0;
-  dtreeNode(N, r, t, nd.up, nd.d[0], nd.d[1]);
-  auto worker = [&](int node, int edge) { return ((size_t)L * N + node) * 3 + edge; };
-  auto cross = [&](int node) { return node / a.groupSize != g; };
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (nd.d[i] >= 0) {
-      nd.fromChild[i] = openEdge(a, worker(r, i), cross(nd.d[i]), true);
-      nd.toChild[i] = openEdge(a, worker(nd.d[i], 2), cross(nd.d[i]), false);
-    }
-  }
-  if (nd.up >= 0) {
-    int pu, p0, p1;
-    dtreeNode(N, nd.up, t, pu, p0, p1);
-    nd.fromParent = openEdge(a, worker(r, 2), cross(nd.up), true);
-    nd.toParent = openEdge(a, worker(nd.up, r == p0 ? 0 : 1), cross(nd.up), false);
-  }
-
-  if (!BATCH) {
-    if (!treePass<PROTO, DT, OP, U>(a, nd, ch, k, lane, a.count, (const char*)a.send[r], (char*)a.recv[r]))
-      return;
-  } else {
-    const size_t row = 1 + 2 * (size_t)N;
-    for (int i = L / perTask; i < a.nTasks; i += a.taskSlots) {
-      const u64* d = a.tasks + (size_t)i * row;
-      if (!treePass<PROTO, DT, OP, U>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r], (char*)d[1 + N + r]))
-        return;
-    }
-  }
-  // LL / LL128 never touch the tail counter per slot: publish it once so the
-  // next call starts both ends of each FIFO at the same step.
-  if (PROTO != kSimple && lane == 0) {
-    if (nd.up >= 0) stRelaxed64(&nd.toParent.conn->tail, nd.toParent.step, true);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (nd.d[i] >= 0) stRelaxed64(&nd.toChild[i].conn->tail, nd.toChild[i].step, true);
-  }
-}
-
-// ------------------------------------------------------------- dispatch
-
-typedef void (*KernelFn)(const KernelArgs);
-
-// The ring kernel for one collective, element type and op (AllGather has no
-// arithmetic: one kernel per element size).
-template <int PROTO, int U, int COLL, bool BATCH>
-KernelFn pickRing(int dtype, int op) {
-  if (COLL == kCollAllGather) {
-    switch (dtype) {
-      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH>;
-      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH>;
-      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH>;
-    }
-    return nullptr;
-  }
-#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH>
-  switch (dtype) {
-    case arInt32: return op == arSum ? AR_RING(arInt32, arSum) : op == arMax ? AR_RING(arInt32, arMax)
-                       : op == arMin ? AR_RING(arInt32, arMin) : nullptr;
-    case arFloat32: return op == arSum ? AR_RING(arFloat32, arSum) : op == arMax ? AR_RING(arFloat32, arMax)
-                         : op == arMin ? AR_RING(arFloat32, arMin) : nullptr;
-    case arFloat16: return op == arSum ? AR_RING(arFloat16, arSum) : op == arMax ? AR_RING(arFloat16, arMax)
-                         : op == arMin ? AR_RING(arFloat16, arMin) : nullptr;
-    case arBfloat16: return op == arSum ? AR_RING(arBfloat16, arSum) : op == arMax ? AR_RING(arBfloat16, arMax)
-                          : op == arMin ? AR_RING(arBfloat16, arMin) : nullptr;
-    case arUint64: return op == arProbe ? AR_RING(arUint64, arProbe) : nullptr;
-  }
-#undef AR_RING
-  return nullptr;
-}
-
-template <int PROTO, int U, bool BATCH>
-KernelFn pickTree(int dtype, int op) {
-#define AR_TREE(DT, OP) treeAllReduceKernel<PROTO, DT, OP, U, BATCH>
-  switch (dtype) {
-    case arInt32: return op == arSum ? AR_TREE(arInt32, arSum) : op == arMax ? AR_TREE(arInt32, arMax)
-                       : op == arMin ? AR_TREE(arInt32, arMin) : nullptr;
-    case arFloat32: return op == arSum ? AR_TREE(arFloat32, arSum) : op == arMax ? AR_TREE(arFloat32, arMax)
-                         : op == arMin ? AR_TREE(arFloat32, arMin) : nullptr;
-    case arFloat16: return op == arSum ? AR_TREE(arFloat16, arSum) : op == arMax ? AR_TREE(arFloat16, arMax)
-                         : op == arMin ? AR_TREE(arFloat16, arMin) : nullptr;
-    case arBfloat16: return op == arSum ? AR_TREE(arBfloat16, arSum) : op == arMax ? AR_TREE(arBfloat16, arMax)
-                          : op == arMin ? AR_TREE(arBfloat16, arMin) : nullptr;
-    case arUint64: return op == arProbe ? AR_TREE(arUint64, arProbe) : nullptr;
-  }
-#undef AR_TREE
-  return nullptr;
-}
-
-// Protocol and slot size: the ring's Simple slot is 1, 2, 4 or 8 KiB (at
-// most 4 KiB for a ring cut into workgroups), the tree's 1, 2 or 4 KiB; LL
-// and LL128 have one slot geometry each.
-template <int COLL, bool BATCH>
-KernelFn pickRingProto(const Plan& plan, int dtype, int op) {
-  switch (plan.proto) {
-    case kLL: return pickRing<kLL, kLLUnroll, COLL, BATCH>(dtype, op);
-    case kLL128:
-      if (plan.unroll == kLL128Unroll) return pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
-      if constexpr (!BATCH)   // large LL128 slots: single calls only
-        if (plan.unroll == kLL128UnrollLarge) return pickRing<kLL128, kLL128UnrollLarge, COLL, false>(dtype, op);
-      return nullptr;
-    case kSimple:
-      switch (plan.unroll) {
-        case 1: return pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
-        case 2: return pickRing<kSimple, 2, COLL, BATCH>(dtype, op);
-        case 4: return pickRing<kSimple, 4, COLL, BATCH>(dtype, op);
-        case 8: return pickRing<kSimple, 8, COLL, BATCH>(dtype, op);
-      }
-  }
-  return nullptr;
-}
-
-template <bool BATCH>
-KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
-  switch (plan.proto) {
-    case kLL: return pickTree<kLL, kLLUnroll, BATCH>(dtype, op);
-    case kLL128: return plan.unroll == kLL128Unroll ? pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op) : nullptr;
-    case kSimple:
-      switch (plan.unroll) {
-        case 1: return pickTree<kSimple, 1, BATCH>(dtype, op);
-        case 2: return pickTree<kSimple, 2, BATCH>(dtype, op);
-        case 4: return pickTree<kSimple, 4, BATCH>(dtype, op);
-      }
-  }
-  return nullptr;
-}
 
 // Batched launches (several AllReduces from a task table) exist for
 // AllReduce only.
 KernelFn pickKernel(const Plan& plan, int coll, int dtype, int op, bool batch) {
   if (plan.algo == arAlgoTree) {
     if (coll != kCollAllReduce) return nullptr;
-    return batch ? pickTreeProto<true>(plan, dtype, op) : pickTreeProto<false>(plan, dtype, op);
+    return batch ? pickTreeAllReduceBatch(plan, dtype, op) : pickTreeAllReduce(plan, dtype, op);
   }
-  if (coll == kCollAllReduce)
-    return batch ? pickRingProto<kCollAllReduce, true>(plan, dtype, op)
-                 : pickRingProto<kCollAllReduce, false>(plan, dtype, op);
+  if (coll == kCollAllReduce) {
+    if (batch) return pickRingAllReduceBatch(plan, dtype, op);
+    return plan.proto == kSimple ? pickRingAllReduceSimple(plan, dtype, op) : pickRingAllReduceLL(plan, dtype, op);
+  }
   if (batch) return nullptr;
-  if (coll == kCollReduceScatter) return pickRingProto<kCollReduceScatter, false>(plan, dtype, op);
-  if (coll == kCollAllGather) return pickRingProto<kCollAllGather, false>(plan, dtype, op);
+  if (coll == kCollReduceScatter) return pickRingReduceScatter(plan, dtype, op);
+  if (coll == kCollAllGather) return pickRingAllGather(plan, dtype, op);
   return nullptr;
 }
 

@@ -24,12 +24,26 @@ def kernels():
     if not all(t and os.path.exists(t) for t in tools):
         pytest.skip("ROCm toolchain not found")
     with tempfile.TemporaryDirectory() as d:
-        fat, co, copy = os.path.join(d, "fatbin"), os.path.join(d, "gfx950.co"), os.path.join(d, "lib.copy")
+        fat, copy = os.path.join(d, "fatbin"), os.path.join(d, "lib.copy")
         # an explicit output file: without one objcopy rewrites its input in place
         subprocess.run([tools[0], "--dump-section", ".hip_fatbin=" + fat, lib, copy], check=True)
-        subprocess.run([tools[1], "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--input=" + fat,
-                        "--output=" + co, "--unbundle"], check=True)
-        notes = subprocess.run([tools[2], "--notes", co], check=True, capture_output=True, text=True).stdout
+        # one offload bundle per translation unit with kernels, back to back
+        data = open(fat, "rb").read()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        starts = []
+        i = data.find(magic)
+        while i >= 0:
+            starts.append(i)
+            i = data.find(magic, i + len(magic))
+        assert starts, "no offload bundle in libar.so"
+        notes = ""
+        for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+            part, co = os.path.join(d, "bundle%d" % n), os.path.join(d, "gfx950_%d.co" % n)
+            with open(part, "wb") as f:
+                f.write(data[a:b])
+            subprocess.run([tools[1], "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--input=" + part,
+                            "--output=" + co, "--unbundle"], check=True)
+            notes += subprocess.run([tools[2], "--notes", co], check=True, capture_output=True, text=True).stdout
     out, cur = {}, None
     for line in notes.splitlines():
         m = re.match(r"\s+\.name:\s+(\S+)", line)
