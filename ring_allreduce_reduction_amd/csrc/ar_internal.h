@@ -133,7 +133,7 @@ struct Plan {
   float predictedUs;
 };
 
-// Provided by ar_kernels.hip.
+// Provided by ar_kernels.hip (the picker functions below by ar_kernels_*.hip).
 hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& args, hipStream_t stream);
 hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bool batch, int* blocksPerCU);
 
