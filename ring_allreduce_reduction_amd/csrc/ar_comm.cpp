@@ -103,23 +103,23 @@ const Env& env() {
 // calibration mode on one MI355X: the least-squares fit, in log time, of the
 // model to 4 KiB messages at 2, 4, 8 and 16 ranks (1 channel), 128 MiB at 8
 // ranks over 1..64 channels, and 16 KiB..64 MiB at 8 ranks with the channel
-// count the 32 KiB rule allows.  Worst point off by 34% (LL), 28% (LL128),
+// count the 32 KiB rule allows.  Worst point off by 33% (LL), 26% (LL128),
 // 19% (Simple).
 const arTuneModel_t kDefaultModels[3] = {
-    /* LL     */ {3.275f, 1.9805f, 47.92f, 117.51f},
-    /* LL128  */ {3.041f, 2.7572f, 59.64f, 149.99f},
-    /* Simple */ {2.603f, 1.5401f, 224.31f, 310.98f},
+    /* LL     */ {3.100f, 1.8253f, 51.35f, 119.56f},
+    /* LL128  */ {3.229f, 2.4979f, 61.80f, 152.68f},
+    /* Simple */ {2.920f, 1.3120f, 231.30f, 307.01f},
 };
 
 // Tree constants (same units; stepLatUs is per tree level each way), fitted
 // the same way (`bench.py --calibrate --algo tree`) with the pages' tree
 // model and its size correction: worst point off by 51% (LL, where the
-// correction's mid-size dip does not match this GPU), 17% (LL128), 42%
+// correction's mid-size dip does not match this GPU), 16% (LL128), 46%
 // (Simple).
 const arTuneModel_t kDefaultTreeModels[3] = {
-    /* LL     */ {2.134f, 1.8129f, 188.67f, 48.44f},
-    /* LL128  */ {0.872f, 2.6381f, 70.15f, 60.84f},
-    /* Simple */ {3.624f, 0.9521f, 138.49f, 140.72f},
+    /* LL     */ {2.083f, 1.6977f, 199.27f, 50.59f},
+    /* LL128  */ {1.373f, 2.2690f, 72.95f, 63.33f},
+    /* Simple */ {3.639f, 0.8683f, 145.93f, 144.75f},
 };
 
 constexpr int kStagingBuffers = 4;
