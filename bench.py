@@ -602,9 +602,10 @@ def copy_probe(args, torch):
 
 
 def _ring_model_us(params, factor, n, nch, S):
-    """The ring cost model arTune evaluates (same form, any constants)."""
+    """The ring cost model arTune evaluates (same form, any constants), with
+    the cap scaled for N ranks sharing one HBM (8 / N)."""
     base, step, bw, cap = params
-    bus = min(bw * nch * factor, cap)
+    bus = min(bw * nch * factor, cap * 8.0 / n)
     return base + 2 * (n - 1) * step + S / (1000.0 * bus * n / (2 * (n - 1)))
 
 
@@ -617,9 +618,10 @@ _TREE_CORR = [
 
 
 def _tree_model_us(params, proto, n, nch, S):
-    """The tree cost model arTune evaluates (same form, any constants)."""
+    """The tree cost model arTune evaluates (same form, any constants), with
+    the cap scaled for N ranks sharing one HBM (44 / (6N - 4))."""
     base, step, bw, cap = params
-    bus = min(bw * nch * 0.92 * {0: 1 / 3.8, 1: 120 / 128, 2: 1.0}[proto], cap)
+    bus = min(bw * nch * 0.92 * {0: 1 / 3.8, 1: 120 / 128, 2: 1.0}[proto], cap * 44.0 / (6 * n - 4))
     q = S >> 6
     if q > 0 and q.bit_length() - 1 < 23:
         bus *= _TREE_CORR[proto][q.bit_length() - 1]

@@ -173,6 +173,11 @@ arResult_t arAllGather(arComm_t comm, const void* const* sendbufs, void* const* 
  * 128-byte aligned) times power-of-two channel counts up to the comm's
  * maximum with at least 32 KiB per channel.  Protocol ties keep Simple before
  * LL128 before LL; channel-count ties keep the larger count.
+ * One GPU holds every rank, so a comm evaluates the model with each
+ * algorithm's cap (maxBwGBs) scaled for N ranks sharing its HBM: ring x 8/N,
+ * tree x 44/(6N-4) (the HBM bytes per model byte at 8 ranks, where the
+ * constants are fitted, over that at N).  arTuneEval* take the constants as
+ * given; arTuneGetModel returns them unscaled.
  */
 arResult_t arTune(arComm_t comm, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs);
 

@@ -253,6 +253,29 @@ void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* 
   out->predictedUs = p->predictedUs;
 }
 
+// The cost model a comm evaluates.  The pages' model prices one GPU per rank;
+// here the N virtual ranks share one GPU's HBM, so a bandwidth-bound call
+// slows with N at a fixed per-rank size.  The constants' caps (the
+// bandwidth-bound regime) are fitted at kCalibRanks ranks; each algorithm's
+// cap is scaled by its HBM bytes per model byte there over that at N:
+//   ring (all three collectives): HBM bytes grow as N times the model's
+//     (AllReduce 5(N-1)S against 2(N-1)S/N), so cap x kCalibRanks / N;
+//   tree: (2N + 4(N-1))S against the model's S, so cap x (6*8-4) / (6N-4).
+// Latency and per-channel terms are per ring member and stay as fitted.
+constexpr int kCalibRanks = 8;
+
+void sharedHbmModels(const arComm* c, arTuneModel_t ring[3], arTuneModel_t tree[3]) {
+  const float n = (float)c->nranks;
+  const float ringScale = (float)kCalibRanks / n;
+  const float treeScale = (6.0f * (float)kCalibRanks - 4.0f) / (6.0f * n - 4.0f);
+  for (int p = 0; p < 3; ++p) {
+    ring[p] = c->models[p];
+    ring[p].maxBwGBs *= ringScale;
+    tree[p] = c->treeModels[p];
+    tree[p].maxBwGBs *= treeScale;
+  }
+}
+
 // Protocol, channels, chunk, lanes and grid for one call, or for a batched
 // launch (`batch`) of `nTasks` collectives whose largest has `count` elements.
 arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool aligned128, Plan* plan,
@@ -272,22 +295,24 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   const unsigned algoMask = algo == arAlgoAuto ? 3u : 1u << algo;
   float predicted = 0.0f;
   arAlgo_t al = algo == arAlgoAuto ? arAlgoRing : (arAlgo_t)algo;
+  arTuneModel_t ringM[3], treeM[3];
+  sharedHbmModels(c, ringM, treeM);
   if (proto == arProtoAuto) {
     unsigned mask = (unsigned)e.protoMask;
     if (!aligned128) mask &= ~(1u << arProtoLL128);
     if (mask == 0) mask = 1u << arProtoSimple;
     arProto_t p;
     int ch;
-    arResult_t r = arTuneEvalAlgo((arFunc_t)func, c->nranks, c->maxChannels, nBytes, c->models, c->treeModels,
-                                  algoMask, mask, &al, &p, &ch, &predicted);
+    arResult_t r = arTuneEvalAlgo((arFunc_t)func, c->nranks, c->maxChannels, nBytes, ringM, treeM, algoMask, mask,
+                                  &al, &p, &ch, &predicted);
     if (r != arSuccess) return r;
     proto = p;
     nch = ch < 1 ? 1 : ch;
   } else {
     if (proto == arProtoLL128 && !aligned128) return arInvalidUsage;   // LL128 needs 128-byte buffers
     // a fixed protocol and channel count; with arAlgoAuto the model picks the algorithm
-    (void)arTuneEvalAlgo((arFunc_t)func, c->nranks, nch, nBytes, c->models, c->treeModels, algoMask, 1u << proto,
-                         &al, nullptr, nullptr, &predicted);
+    (void)arTuneEvalAlgo((arFunc_t)func, c->nranks, nch, nBytes, ringM, treeM, algoMask, 1u << proto, &al, nullptr,
+                         nullptr, &predicted);
   }
   const bool tree = al == arAlgoTree;
   const int N = c->nranks;
@@ -673,7 +698,9 @@ arResult_t arTuneAlgo(arComm_t c, size_t nBytes, arAlgo_t* algo, arProto_t* prot
   if (!commOk(c)) return arInvalidArgument;
   const int a = env().forcedAlgo != -2 ? env().forcedAlgo : c->algo;
   const unsigned algoMask = a == arAlgoAuto ? 3u : 1u << a;
-  return arTuneEvalAlgo(arFuncAllReduce, c->nranks, c->maxChannels, nBytes, c->models, c->treeModels, algoMask,
+  arTuneModel_t ringM[3], treeM[3];
+  sharedHbmModels(c, ringM, treeM);
+  return arTuneEvalAlgo(arFuncAllReduce, c->nranks, c->maxChannels, nBytes, ringM, treeM, algoMask,
                         (unsigned)env().protoMask, algo, proto, nChannels, predictedUs);
 }
 

@@ -126,3 +126,24 @@ def test_tree_one_rank_and_empty(B, gu):
         comm.allreduce(x, x, "sum", count=0, dtype=B.arFloat32)
         torch.cuda.synchronize()
         assert comm.async_error() == B.arSuccess
+
+
+@pytest.mark.parametrize("n", [2, 5, 8, 16, 72])
+def test_tuner_caps_shared_hbm(B, n):
+    # a comm prices every algorithm with its cap scaled for N ranks on one
+    # HBM: ring x 8/N, tree x 44/(6N-4); everything else as fitted
+    f32 = np.float32
+    with B.Comm(n, 64, "auto", "auto") as comm:
+        ring = [B.arTuneGetAlgoModel(comm.handle, B.arAlgoRing, p) for p in range(3)]
+        tree = [B.arTuneGetAlgoModel(comm.handle, B.arAlgoTree, p) for p in range(3)]
+        ring_s = [m[:3] + (float(f32(m[3]) * (f32(8) / f32(n))),) for m in ring]
+        tree_s = [m[:3] + (float(f32(m[3]) * (f32(44) / f32(6 * n - 4))),) for m in tree]
+        for log2_bytes in (3, 12, 17, 20, 22, 23, 24, 26, 28):
+            nbytes = 1 << log2_bytes
+            a, p, ch, t = B.arTuneAlgo(comm.handle, nbytes)
+            ea, ep, ech, et = B.arTuneEvalAlgo(0, n, 64, nbytes, ring_s, tree_s)
+            assert (a, p, ch) == (ea, ep, ech) and t == pytest.approx(et, rel=1e-6)
+            if n == 8:
+                assert (a, p, ch) == B.arTuneEvalAlgo(0, n, 64, nbytes, ring, tree)[:3]
+            if n == 16 and log2_bytes in (22, 23):
+                assert a == B.arAlgoRing   # 16 ranks x 4-8 MiB: the ring is measured 1.4-1.5x faster
