@@ -575,7 +575,8 @@ def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
         frac = 5.0 * (N - 1) * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
         print(json.dumps({"nch": nch, "lanes": plan["lanesPerChannel"], "slotKiB": sk, "direct": d,
                           "depth": plan["nSlots"], "sets": st, "grid": plan["workgroups"],
-                          "block": plan["threadsPerGroup"],
+                          "block": plan["threadsPerGroup"], "groupSize": plan["ranksPerGroup"],
+                          "nchRun": plan["nChannels"], "slotBytes": plan["stepBytes"],
                           "ms": round(ms, 4), "busbw": round(S / (ms / 1e3) / 1e9 * 2 * (N - 1) / N, 2),
                           "frac": round(frac, 4)}), flush=True)
     comm.close()

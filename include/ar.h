@@ -284,10 +284,12 @@ typedef struct {
 /*
  * arGetPlan -- fill `plan` with what arAllReduce(comm, ..., count, dtype, ...)
  * would use for buffers that are 128-byte aligned (aligned128 = 1) or not.
- * The channel count that runs can be below the requested one: a ring of more
- * than 16 ranks needs its whole grid co-resident, and when one lane per
- * channel does not fit, the channels are halved until it does (the result is
- * that of the reported count).
+ * The channel count that runs can be below the requested one: a ring or tree
+ * of more than 16 ranks needs its whole grid co-resident.  The ring halves its
+ * channels until one lane per channel fits; the tree (single calls, automatic
+ * lanes) takes the power-of-two fraction of the requested channels, the slot
+ * and the group size that keep the most bytes in flight (channels x lanes x
+ * slot payload).  The result is that of the reported count.
  */
 arResult_t arGetPlan(arComm_t comm, size_t count, arDataType_t dtype, int aligned128, arPlan_t* plan);
 

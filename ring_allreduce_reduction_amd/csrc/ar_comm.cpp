@@ -358,8 +358,95 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   };
   uint64_t chunkBytes = chunkBytesFor(nch);
 
-  // A Simple slot smaller than the default keeps more wavefronts resident
-  // (fewer registers) when the whole grid must be co-resident.  First
+  int nGroups = 1, groupSize = N;
+  auto gridFor = [&](int ln) {
+    const int lt = nch * ln;
+    return nGroups == 1 ? lt : ((lt + 7) / 8) * 8 * nGroups;
+  };
+  // About 64 wavefronts per CU: measured best on MI355X (workgroups finish
+  // unevenly, so a grid of a few resident rounds balances better than one).
+  // A lane's share of a chunk is at least one slot.  When the chunk is too
+  // small to give every lane a full Simple slot, smaller slots are used so
+  // that more lanes share the work: the time of a short message is the number
+  // of sequential steps per lane, not bandwidth.
+  auto targetFor = [&]() { return (int)((uint64_t)c->numCUs * 64 / ((uint64_t)N * (uint64_t)nch)); };
+  auto lanesFor = [&](int slotPayload) {
+    int ln = targetFor();
+    // round up: a 120-byte-line LL128 slot never divides a power-of-two chunk
+    const int byChunk = (int)((chunkBytes + (uint64_t)slotPayload - 1) / (uint64_t)slotPayload);
+    if (ln > byChunk) ln = byChunk;
+    if (ln > c->lanesMax / (edges * nch)) ln = c->lanesMax / (edges * nch);
+    return ln < 1 ? 1 : ln;
+  };
+  auto setSlot = [&](int u) {
+    plan->unroll = u;
+    plan->slotBytes = slotBytesOf(proto, u);
+    plan->slotPayload = slotPayloadOf(proto, u);
+  };
+  const int unroll0 = plan->unroll;
+  const int uMax0 = proto == kSimple && unroll0 > kGroupedSimpleUnrollMax ? kGroupedSimpleUnrollMax : unroll0;
+
+  // A grouped tree: its channels and lanes both cut the data into
+  // independent column streams, each a chain of batches up and down the
+  // tree, and the call takes about as long as the columns those streams keep
+  // in flight allow (72 ranks x 4 MiB: 64 channels x 1 lane of 2 KiB slots in
+  // 9-member groups, 1.16 ms; 16 channels x 3 lanes of 4 KiB in 15-member
+  // groups, 0.60 ms).  So the channel count (at most the one asked for), the
+  // slot and the group size are chosen for the most bytes in flight
+  // (channels x the smaller of lanes x slot payload and a channel's share) in
+  // a co-resident grid.  Ties keep the smaller slot, as more lanes of it take
+  // a share that is in flight at once through the tree a little faster
+  // (24 ranks x 4 KiB: 4 lanes of 1 KiB 38.3 us, 2 of 2 KiB 39.1, 1 of 4 KiB
+  // 42.9), then larger groups, then more channels.
+  bool placed = false;
+  if (tree && !batch && N > kMaxMembersPerGroup && c->forcedLanes == 0) {
+    const int nchAsked = nch;
+    uint64_t bestBytes = 0;
+    int bestU = 0, bestGs = 0, bestCh = 0;
+    for (int u = uMax0; u >= 1; u /= 2) {
+      setSlot(u);
+      for (int ch = nchAsked; ch >= 1; ch /= 2) {
+        nch = ch;
+        chunkBytes = chunkBytesFor(ch);
+        for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
+          layout(gs, &nGroups, &groupSize);
+          plan->block = groupSize * kWave;
+          int pc = 0;
+          if (ringKernelOccupancy(*plan, func, dtype, op, batch, &pc) != hipSuccess) return arHipError;
+          const int cap = pc * c->numCUs;
+          if (cap < gridFor(1)) continue;
+          int ln = lanesFor(plan->slotPayload);
+          while (ln > 1 && gridFor(ln) > cap) --ln;
+          const uint64_t lanesBytes = (uint64_t)ln * (uint64_t)plan->slotPayload;
+          const uint64_t bytes = (uint64_t)ch * (lanesBytes < chunkBytes ? lanesBytes : chunkBytes);
+          if (bytes > bestBytes ||
+              (bytes == bestBytes && (u < bestU || (u == bestU && (gs > bestGs || (gs == bestGs && ch > bestCh)))))) {
+            bestBytes = bytes;
+            bestU = u;
+            bestGs = gs;
+            bestCh = ch;
+          }
+          break;   // the largest group that fits at this (slot, channels)
+        }
+      }
+      if (proto != kSimple) break;
+    }
+    if (bestBytes > 0) {
+      setSlot(bestU);
+      nch = bestCh;
+      plan->nChannels = nch;
+      chunkBytes = chunkBytesFor(nch);
+      layout(bestGs, &nGroups, &groupSize);
+      placed = true;
+    } else {
+      setSlot(unroll0);
+      nch = nchAsked;
+      chunkBytes = chunkBytesFor(nch);
+    }
+  }
+  // Other grouped plans (the ring; a batched or forced-lane tree).  A Simple
+  // slot smaller than the default keeps more wavefronts resident (fewer
+  // registers) when the whole grid must be co-resident.  First
   // choice: the smallest slot of at least half a chunk, with enough lanes
   // that each lane's share is one slot, if such a grid can be co-resident
   // (72 ranks x 4 MiB: 912-byte chunks in 1 KiB slots and 12-member groups
@@ -368,20 +455,12 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // grid is co-resident.  If no grid of one lane per channel can be
   // co-resident, the channels are halved until one can (the plan reports
   // the count that runs).
-  int nGroups = 1, groupSize = N;
-  const int unroll0 = plan->unroll;
-  while (N > kMaxMembersPerGroup) {
-    plan->unroll = unroll0;
-    plan->slotBytes = slotBytesOf(proto, unroll0);
-    plan->slotPayload = slotPayloadOf(proto, unroll0);
+  while (!placed && N > kMaxMembersPerGroup) {
+    setSlot(unroll0);
     // the largest group size whose grid of `ln` lanes per channel is
     // co-resident with slot u (0: none; -1: HIP error)
     auto fit = [&](int u, int ln) -> int {
-      if (proto == kSimple) {
-        plan->unroll = u;
-        plan->slotBytes = slotBytesOf(proto, u);
-        plan->slotPayload = slotPayloadOf(proto, u);
-      }
+      if (proto == kSimple) setSlot(u);
       for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
         layout(gs, &nGroups, &groupSize);
         plan->block = groupSize * kWave;
@@ -391,8 +470,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       }
       return 0;
     };
-    const int uMax = proto == kSimple && plan->unroll > kGroupedSimpleUnrollMax ? kGroupedSimpleUnrollMax
-                                                                                 : plan->unroll;
+    const int uMax = uMax0;
     int found = 0;
     if (proto == kSimple) {
       int u = uMax;
@@ -423,25 +501,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return arHipError;
   if (perCU < 1) perCU = 1;
   const int capacity = perCU * c->numCUs;   // resident workgroups
-  auto gridFor = [&](int ln) {
-    const int lt = nch * ln;
-    return nGroups == 1 ? lt : ((lt + 7) / 8) * 8 * nGroups;
-  };
-  // About 64 wavefronts per CU: measured best on MI355X (workgroups finish
-  // unevenly, so a grid of a few resident rounds balances better than one).
-  // A lane's share of a chunk is at least one slot.  When the chunk is too
-  // small to give every lane a full Simple slot, smaller slots are used so
-  // that more lanes share the work: the time of a short message is the number
-  // of sequential steps per lane, not bandwidth.
-  const int target = (int)((uint64_t)c->numCUs * 64 / ((uint64_t)N * (uint64_t)nch));
-  auto lanesFor = [&](int slotPayload) {
-    int ln = target;
-    // round up: a 120-byte-line LL128 slot never divides a power-of-two chunk
-    const int byChunk = (int)((chunkBytes + (uint64_t)slotPayload - 1) / (uint64_t)slotPayload);
-    if (ln > byChunk) ln = byChunk;
-    if (ln > c->lanesMax / (edges * nch)) ln = c->lanesMax / (edges * nch);
-    return ln < 1 ? 1 : ln;
-  };
+  const int target = targetFor();
   int lanes = lanesFor(plan->slotPayload);
   // LL128, automatic slot: the large slot when every lane still gets a full
   // batch of large slots (nSlots/2 columns): that halves the batches, each of

@@ -1,6 +1,10 @@
 // ar_kernels.hip -- picks and launches the kernel of a plan.  The kernels
 // themselves (device code in ar_device.h) are compiled in the translation
 // units ar_kernels_*.hip, one per family.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "ar_internal.h"
 
 namespace ar {
@@ -38,10 +42,33 @@ hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& arg
   return hipGetLastError();
 }
 
+// Resident workgroups per CU of a kernel at a block size, per device.  The
+// planner asks for many (kernel, block) pairs on every call of a grouped
+// ring or tree; the answers never change, so they are kept.
 hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bool batch, int* blocksPerCU) {
   KernelFn fn = pickKernel(plan, coll, dtype, op, batch);
   if (fn == nullptr) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocksPerCU, (const void*)fn, plan.block, 0);
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int>, int> known;
+  const auto key = std::make_tuple((const void*)fn, plan.block, dev);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = known.find(key);
+    if (it != known.end()) {
+      *blocksPerCU = it->second;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, plan.block, 0);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  known[key] = n;
+  *blocksPerCU = n;
+  return hipSuccess;
 }
 
 }  // namespace ar

@@ -147,3 +147,15 @@ def test_tuner_caps_shared_hbm(B, n):
                 assert (a, p, ch) == B.arTuneEvalAlgo(0, n, 64, nbytes, ring, tree)[:3]
             if n == 16 and log2_bytes in (22, 23):
                 assert a == B.arAlgoRing   # 16 ranks x 4-8 MiB: the ring is measured 1.4-1.5x faster
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("n,count", [(72, 1 << 20), (48, 1 << 20), (24, 3 << 18)])
+def test_grouped_tree_channels_for_bytes_in_flight(B, gu, proto, n, count):
+    # past 16 ranks a single-call tree may run a power-of-two fraction of the
+    # channels asked for, with more lanes; the result is that of the count run
+    plan, _, _ = tree(gu, n, count, "float32", "sum", proto, 64, seed=n)
+    nch = plan["nChannels"]
+    assert 1 <= nch <= 64 and 64 % nch == 0 and plan["ranksPerGroup"] <= 16
+    gu.note("tree n=%d %d B %s: %d ch x %d lanes, %d B slots, groups of %d"
+            % (n, count * 4, proto, nch, plan["lanesPerChannel"], plan["stepBytes"], plan["ranksPerGroup"]))
