@@ -288,8 +288,9 @@ typedef struct {
  * of more than 16 ranks needs its whole grid co-resident.  The ring halves its
  * channels until one lane per channel fits; the tree (single calls, automatic
  * lanes) takes the power-of-two fraction of the requested channels, the slot
- * and the group size that keep the most bytes in flight (channels x lanes x
- * slot payload).  The result is that of the reported count.
+ * and the group size with the largest groups, then the most bytes in flight
+ * (channels x lanes x slot payload).  The result is that of the reported
+ * count.
  */
 arResult_t arGetPlan(arComm_t comm, size_t count, arDataType_t dtype, int aligned128, arPlan_t* plan);
 

@@ -392,17 +392,21 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // in flight allow (72 ranks x 4 MiB: 64 channels x 1 lane of 2 KiB slots in
   // 9-member groups, 1.16 ms; 16 channels x 3 lanes of 4 KiB in 15-member
   // groups, 0.60 ms).  So the channel count (at most the one asked for), the
-  // slot and the group size are chosen for the most bytes in flight
-  // (channels x the smaller of lanes x slot payload and a channel's share) in
-  // a co-resident grid.  Ties keep the smaller slot, as more lanes of it take
-  // a share that is in flight at once through the tree a little faster
-  // (24 ranks x 4 KiB: 4 lanes of 1 KiB 38.3 us, 2 of 2 KiB 39.1, 1 of 4 KiB
-  // 42.9), then larger groups, then more channels.
+  // slot and the group size are chosen, in a co-resident grid, for the
+  // largest groups first: every tree edge between workgroups is a
+  // device-coherent hop two to three times slower than one inside a
+  // workgroup (72 ranks x 4 MiB: 64 channels x 1 lane of 4 KiB in 9-member
+  // groups, 256 KiB in flight, 0.76 ms; 16 x 3 lanes of 4 KiB in 15-member
+  // groups, 192 KiB, 0.59 ms).  Then for the most bytes in flight (channels x
+  // the smaller of lanes x slot payload and a channel's share).  Ties keep the
+  // smaller slot, as more lanes of it take a share that is in flight at once
+  // through the tree a little faster (24 ranks x 4 KiB: 4 lanes of 1 KiB
+  // 38.3 us, 2 of 2 KiB 39.1, 1 of 4 KiB 42.9), then more channels.
   bool placed = false;
   if (tree && !batch && N > kMaxMembersPerGroup && c->forcedLanes == 0) {
     const int nchAsked = nch;
     uint64_t bestBytes = 0;
-    int bestU = 0, bestGs = 0, bestCh = 0;
+    int bestU = 0, bestGs = 0, bestCh = 0, bestSize = 0;
     for (int u = uMax0; u >= 1; u /= 2) {
       setSlot(u);
       for (int ch = nchAsked; ch >= 1; ch /= 2) {
@@ -419,8 +423,10 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
           while (ln > 1 && gridFor(ln) > cap) --ln;
           const uint64_t lanesBytes = (uint64_t)ln * (uint64_t)plan->slotPayload;
           const uint64_t bytes = (uint64_t)ch * (lanesBytes < chunkBytes ? lanesBytes : chunkBytes);
-          if (bytes > bestBytes ||
-              (bytes == bestBytes && (u < bestU || (u == bestU && (gs > bestGs || (gs == bestGs && ch > bestCh)))))) {
+          if (groupSize > bestSize ||
+              (groupSize == bestSize &&
+               (bytes > bestBytes || (bytes == bestBytes && (u < bestU || (u == bestU && ch > bestCh)))))) {
+            bestSize = groupSize;
             bestBytes = bytes;
             bestU = u;
             bestGs = gs;

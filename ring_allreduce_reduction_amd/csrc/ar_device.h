@@ -271,22 +271,37 @@ __device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
 
 // Bounded waiting.  Every spin sleeps briefly; every 256 spins the abort word
 // and the wall clock are checked, and a hard cap on spins backs the clock up.
-// On give-up the member records why and the caller returns, so every
-// wavefront of the kernel always exits.
+// The clock starts at the first of those checks: reading it is a scalar
+// memory access of about a microsecond, and the usual wait in a ring or tree
+// chain (a neighbour a few hundred nanoseconds behind) ends long before, so
+// it must not pay for one.  On give-up the member records why and the caller
+// returns, so every wavefront of the kernel always exits.
+//
+// A waiting wavefront drops to the lowest issue priority until its wait
+// ends; the kernels run at kWorkPrio otherwise.  Up to 15 members of a
+// workgroup can be polling while the one the chain waits on works on the same
+// CU, and at equal priority their polls take its issue slots (16 ranks, 4 KiB
+// per rank: 104 us at equal priority, 75 us with the pollers lowered).
+constexpr int kWorkPrio = 2;
 struct Waiter {
   u32 spins = 0;
   u64 t0 = 0;
+  __device__ __forceinline__ ~Waiter() {
+    if (spins != 0) __builtin_amdgcn_s_setprio(kWorkPrio);
+  }
 };
 
 __device__ __forceinline__ bool keepWaiting(Control* ctrl, u64 timeoutTicks, Waiter& w) {
-  if (w.spins == 0) w.t0 = wall_clock64();
+  if (w.spins == 0) __builtin_amdgcn_s_setprio(0);
   ++w.spins;
-  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_s_sleep(2);
   if ((w.spins & 255u) == 0) {
+    const u64 now = wall_clock64();
+    if (w.spins == 256u) w.t0 = now;
     u32 ab = __hip_atomic_load(&ctrl->abortFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     u32 code = 0;
     if (__builtin_amdgcn_readfirstlane(ab) != 0) code = kStatusAbort;
-    else if (wall_clock64() - w.t0 > timeoutTicks || w.spins >= (1u << 30)) code = kStatusTimeout;
+    else if (now - w.t0 > timeoutTicks || w.spins >= (1u << 30)) code = kStatusTimeout;
     if (code != 0) {
       __hip_atomic_store(&ctrl->status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       return false;
@@ -302,6 +317,45 @@ __device__ __forceinline__ bool waitGeq(const KernelArgs& a, const u64* p, u64 t
   while (true) {
     if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
     if (ldCounter(p, agent) >= target) return true;
+  }
+}
+
+// Counters of the edges inside one workgroup live in LDS: member wave w's
+// tail (what its predecessor has published into its FIFO) at w, its head
+// (what it has consumed) at kLdsHead + w.  The FIFO slots themselves stay
+// in HBM; only the handshake moves.  A wavefront's vector memory operations
+// complete in issue order, so a counter polled with global loads waits
+// behind every load the member issued before it (its local operand from
+// HBM, above all); an LDS poll completes on its own counter.  Ordering is
+// unchanged: the producer's slot stores and the LDS counter store are
+// ordered by the same workgroup-scope release as before, which gfx950
+// compiles to no wait at all (every wavefront of the workgroup shares the
+// CU's vector memory path), and the consumer loads the slot only after the
+// counter read returned.  Global copies are written back when a call ends,
+// so the next call starts every edge at the same step.
+constexpr int kLdsHead = kMaxMembersPerGroup;
+__device__ __forceinline__ u64* ldsCounters() {
+  __shared__ u64 c[2 * kMaxMembersPerGroup];
+  return c;
+}
+__device__ __forceinline__ u64 ldLds(int i) {
+  u64 v = __hip_atomic_load(&ldsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  u32 lo = __builtin_amdgcn_readfirstlane((u32)v);
+  u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ void stLds(int i, u64 v) {
+  __hip_atomic_store(&ldsCounters()[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void stLdsRelease(int i, u64 v) {
+  __hip_atomic_store(&ldsCounters()[i], v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ bool waitLdsGeq(const KernelArgs& a, int i, u64 target) {
+  if (ldLds(i) >= target) return true;
+  Waiter w;
+  while (true) {
+    if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+    if (ldLds(i) >= target) return true;
   }
 }
 
@@ -339,6 +393,8 @@ struct Member {
   u32 sendSlot;       // sendStep % nSlots
   u64 succHead;       // last value read from succ->head; head only grows, so
                       // a stale copy never over-reports free slots
+  int selfW;          // my wavefront in the workgroup: my LDS counters
+  int succW;          // the successor's, when it shares the workgroup
   bool recvAgent;
   bool sendAgent;
   bool aligned;
@@ -350,17 +406,18 @@ template <bool CACHED, bool XWG>
 __device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
   // slot sendStep % nSlots is free once the successor consumed step sendStep - nSlots
   u64 need = m.sendStep + 1 > (u64)a.nSlots ? m.sendStep + 1 - (u64)a.nSlots : 0;
+  const bool agent = XWG && m.sendAgent;
   if (CACHED) {
     if (m.succHead >= need) return true;   // ordered by the acquire after that read
-    m.succHead = ldCounter(&m.succ->head, (XWG && m.sendAgent));
+    m.succHead = agent ? ldCounter(&m.succ->head, true) : ldLds(kLdsHead + m.succW);
     if (m.succHead < need) {
       Waiter w;
       do {
         if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
-        m.succHead = ldCounter(&m.succ->head, (XWG && m.sendAgent));
+        m.succHead = agent ? ldCounter(&m.succ->head, true) : ldLds(kLdsHead + m.succW);
       } while (m.succHead < need);
     }
-  } else if (!waitGeq(a, &m.succ->head, need, (XWG && m.sendAgent))) {
+  } else if (agent ? !waitGeq(a, &m.succ->head, need, true) : !waitLdsGeq(a, kLdsHead + m.succW, need)) {
     return false;
   }
   acquireEdge();
@@ -374,7 +431,10 @@ __device__ __forceinline__ void advanceSend(const KernelArgs& a, Member& m) {
 template <bool XWG>
 __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
   ++m.recvStep;
-  if (m.lane == 0) stCounterRelease(&m.self->head, m.recvStep, (XWG && m.recvAgent));
+  if (m.lane == 0) {
+    if (XWG && m.recvAgent) stCounterRelease(&m.self->head, m.recvStep, true);
+    else stLdsRelease(kLdsHead + m.selfW, m.recvStep);
+  }
   if (++m.recvSlot == (u32)a.nSlots) m.recvSlot = 0;
 }
 
@@ -437,7 +497,9 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
     const char* slot = m.rfifo + (size_t)m.recvSlot * SLOT;
     v4u in[U];
     if (PROTO == kSimple) {
-      if (!waitGeq(a, &m.self->tail, m.recvStep + 1, (XWG && m.recvAgent))) return false;
+      if ((XWG && m.recvAgent) ? !waitGeq(a, &m.self->tail, m.recvStep + 1, true)
+                               : !waitLdsGeq(a, m.selfW, m.recvStep + 1))
+        return false;
       acquireEdge();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -534,7 +596,10 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
           if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
       }
       releaseEdge((XWG && m.sendAgent));
-      if (lane == 0) stRelaxed64(&m.succ->tail, m.sendStep + 1, (XWG && m.sendAgent));
+      if (lane == 0) {
+        if (XWG && m.sendAgent) stRelaxed64(&m.succ->tail, m.sendStep + 1, true);
+        else stLds(m.succW, m.sendStep + 1);
+      }
     } else if (PROTO == kLL) {
       const u64 flag = (u64)(u32)(m.sendStep + 1) << 32;
 #pragma unroll
@@ -730,6 +795,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // state in VGPRs measured faster on short messages (the CU's scalar unit
   // is shared by all of its wavefronts' polling loops).
   const int wave = U == 8 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
+  __builtin_amdgcn_s_setprio(kWorkPrio);
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
   const int lanesTotal = BATCH ? perTask * a.taskSlots : perTask;
@@ -740,10 +806,10 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // set L then runs pairs L, L + sets, L + 2 sets, ... on the same FIFOs,
   // whose steps simply continue from one pair to the next.
   const int sets = BATCH ? lanesTotal : a.laneSets;
-  if (L >= sets) return;
   const int r = g * a.groupSize + wave;
-  if (r >= N || r == a.deadRank) return;
-  const int succ = r + 1 == N ? 0 : r + 1;
+  // every wavefront reaches the barrier below before any returns
+  const bool live = L < sets && r < N;
+  const int succ = r + 1 >= N ? 0 : r + 1;
   const int pred = r == 0 ? N - 1 : r - 1;
 
   Member m;
@@ -759,14 +825,22 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   constexpr bool GROUPED = PROTO != kSimple || U <= kGroupedSimpleUnrollMax;
   m.recvAgent = GROUPED && pred / a.groupSize != g;
   m.sendAgent = GROUPED && succ / a.groupSize != g;
+  m.selfW = wave;
+  m.succW = succ - g * a.groupSize;   // used only when the successor shares the workgroup
   m.aligned = a.aligned16 != 0;
   m.direct = a.direct != 0;
   // counters carry over from earlier calls (tail == head at call boundaries)
-  m.recvStep = ldCounter(&m.self->head, true);
-  m.sendStep = ldCounter(&m.succ->tail, true);
+  m.recvStep = live ? ldCounter(&m.self->head, true) : 0;
+  m.sendStep = live ? ldCounter(&m.succ->tail, true) : 0;
   m.succHead = 0;
   m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
   m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
+  if (live && m.lane == 0) {
+    stLds(wave, m.recvStep);
+    stLds(kLdsHead + wave, m.recvStep);
+  }
+  __syncthreads();
+  if (!live || r == a.deadRank) return;
 
   // A member with an edge to another workgroup runs the pass compiled with
   // that edge's code; every other member runs one with no trace of it (the
@@ -775,9 +849,13 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
                       ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, GROUPED>(a, m, L, sets, lanesTotal, perTask, r, succ)
                       : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false>(a, m, L, sets, lanesTotal, perTask, r, succ);
   if (!ok) return;
-  // LL / LL128 never touch the tail counter per slot: publish it once so the
-  // next call starts both ends of this FIFO at the same step.
-  if (PROTO != kSimple && m.lane == 0) stRelaxed64(&m.succ->tail, m.sendStep, true);
+  // Publish what only LDS (an edge inside the workgroup) or the LL / LL128
+  // flags (which never touch the tail counter per slot) have counted, so the
+  // next call starts both ends of every FIFO at the same step.
+  if (m.lane == 0) {
+    if (!(GROUPED && m.recvAgent)) stRelaxed64(&m.self->head, m.recvStep, true);
+    if (PROTO != kSimple || !(GROUPED && m.sendAgent)) stRelaxed64(&m.succ->tail, m.sendStep, true);
+  }
 }
 
 // ------------------------------------------------------------- tree AllReduce
@@ -1128,6 +1206,7 @@ template <int PROTO, int DT, int OP, int U, bool BATCH>
 __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
   // as in the ring kernel: scalar member state for the largest (4 KiB) slot
   const int wave = U == 4 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
+  __builtin_amdgcn_s_setprio(kWorkPrio);
   const int lane = threadIdx.x % kWave;
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
