@@ -103,23 +103,23 @@ const Env& env() {
 // calibration mode on one MI355X: the least-squares fit, in log time, of the
 // model to 4 KiB messages at 2, 4, 8 and 16 ranks (1 channel), 128 MiB at 8
 // ranks over 1..64 channels, and 16 KiB..64 MiB at 8 ranks with the channel
-// count the 32 KiB rule allows.  Worst point off by 33% (LL), 26% (LL128),
-// 19% (Simple).
+// count the 32 KiB rule allows.  Worst point off by 31% (LL), 23% (LL128),
+// 23% (Simple).
 const arTuneModel_t kDefaultModels[3] = {
-    /* LL     */ {3.100f, 1.8253f, 51.35f, 119.56f},
-    /* LL128  */ {3.229f, 2.4979f, 61.80f, 152.68f},
-    /* Simple */ {2.920f, 1.3120f, 231.30f, 307.01f},
+    /* LL     */ {3.583f, 1.7991f, 51.72f, 121.13f},
+    /* LL128  */ {3.759f, 2.2949f, 77.91f, 171.17f},
+    /* Simple */ {3.453f, 1.1687f, 273.47f, 319.38f},
 };
 
 // Tree constants (same units; stepLatUs is per tree level each way), fitted
 // the same way (`bench.py --calibrate --algo tree`) with the pages' tree
-// model and its size correction: worst point off by 51% (LL, where the
-// correction's mid-size dip does not match this GPU), 16% (LL128), 46%
+// model and its size correction: worst point off by 48% (LL, where the
+// correction's mid-size dip does not match this GPU), 20% (LL128), 48%
 // (Simple).
 const arTuneModel_t kDefaultTreeModels[3] = {
-    /* LL     */ {2.083f, 1.6977f, 199.27f, 50.59f},
-    /* LL128  */ {1.373f, 2.2690f, 72.95f, 63.33f},
-    /* Simple */ {3.639f, 0.8683f, 145.93f, 144.75f},
+    /* LL     */ {2.300f, 1.6984f, 204.74f, 51.25f},
+    /* LL128  */ {1.619f, 2.1802f, 74.49f, 64.24f},
+    /* Simple */ {3.847f, 0.7943f, 142.75f, 145.58f},
 };
 
 constexpr int kStagingBuffers = 4;
