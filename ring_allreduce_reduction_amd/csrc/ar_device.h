@@ -269,13 +269,18 @@ __device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
   }
 }
 
-// Bounded waiting.  Every spin sleeps briefly; every 256 spins the abort word
-// and the wall clock are checked, and a hard cap on spins backs the clock up.
-// The clock starts at the first of those checks: reading it is a scalar
-// memory access of about a microsecond, and the usual wait in a ring or tree
-// chain (a neighbour a few hundred nanoseconds behind) ends long before, so
-// it must not pay for one.  On give-up the member records why and the caller
-// returns, so every wavefront of the kernel always exits.
+// Bounded waiting.  Every spin sleeps briefly; every 4096 spins the abort
+// word and the wall clock are checked, and a hard cap on spins backs the
+// clock up.  The clock starts at the first of those checks: reading it is a
+// scalar memory access of about a microsecond, and the usual wait in a ring
+// or tree chain (a neighbour a few hundred nanoseconds behind) ends long
+// before, so it must not pay for one.  The abort word is in host memory, a
+// PCIe round trip per read: an LDS poll spins in about 100 ns, and with a
+// check every 256 spins the thousands of wavefronts waiting in a ring cut
+// into workgroups read it often enough to stall one another (32 ranks x
+// 64 MiB: 10 of 36 calls 1.1-3.4x slower; none at 4096).  On give-up the
+// member records why and the caller returns, so every wavefront of the
+// kernel always exits.
 //
 // A waiting wavefront drops to the lowest issue priority until its wait
 // ends; the kernels run at kWorkPrio otherwise.  Up to 15 members of a
@@ -295,9 +300,9 @@ __device__ __forceinline__ bool keepWaiting(Control* ctrl, u64 timeoutTicks, Wai
   if (w.spins == 0) __builtin_amdgcn_s_setprio(0);
   ++w.spins;
   __builtin_amdgcn_s_sleep(2);
-  if ((w.spins & 255u) == 0) {
+  if ((w.spins & 4095u) == 0) {
     const u64 now = wall_clock64();
-    if (w.spins == 256u) w.t0 = now;
+    if (w.spins == 4096u) w.t0 = now;
     u32 ab = __hip_atomic_load(&ctrl->abortFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     u32 code = 0;
     if (__builtin_amdgcn_readfirstlane(ab) != 0) code = kStatusAbort;
