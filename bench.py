@@ -237,6 +237,7 @@ def main():
                    "proto": B.PROTO_NAMES[plan["proto"]], "nChannels": plan["nChannels"],
                    "chunkElems": plan["chunkElems"], "lanesPerChannel": plan["lanesPerChannel"],
                    "workgroups": plan["workgroups"], "threadsPerGroup": plan["threadsPerGroup"],
+                   "slotBytes": plan["stepBytes"],
                    "selection": "arTune" if args.proto == "auto" else "forced"},
         "algbw_GBs": round(algbw, 3),
         "busbw_GBs": round(busbw, 3),
