@@ -683,8 +683,11 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
       // longest chunk and a share is at most the per-lane split of its chunk)
       const u64 sub0 = alignUp(divUp(umin(cur, rem), (u64)a.lanes), A);
       const u64 nCols = divUp(sub0 * ESZ, (u64)PAYLOAD);
+      // a whole chunk's lane share, so that only a shortened chunk divides
+      const u64 subCur = alignUp(divUp(cur, (u64)a.lanes), A);
       for (u64 jb = 0; jb < nCols; jb += batch) {
         const u64 je = umin(jb + batch, nCols);
+        int cNext = r == 0 ? N - 1 : r - 1;   // (r - 1 - s) mod N, stepped down each stage
         for (int s = 0; s <= 2 * N - 2; ++s) {
           int kind;
           if (s == 0) kind = kSend;
@@ -693,11 +696,12 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
           else if (s <= lastSendStage) kind = kRecvCopySend;
           else kind = kRecv;
           // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
-          const int c = s <= lastSendStage ? (r - 1 - s + 2 * N) % N : succ;
+          const int c = s <= lastSendStage ? cNext : succ;
+          cNext = cNext == 0 ? N - 1 : cNext - 1;
           const u64 cb = (u64)c * cur;
           const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
           // lane k's share of the chunk (pipelining only: the order is per element)
-          const u64 sub = alignUp(divUp(clen, (u64)a.lanes), A);
+          const u64 sub = clen == cur ? subCur : alignUp(divUp(clen, (u64)a.lanes), A);
           const u64 sb = umin((u64)k * sub, clen);
           const u64 se = umin(sb + sub, clen);
           const u64 bytes = (se - sb) * ESZ;
