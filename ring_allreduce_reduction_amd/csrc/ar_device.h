@@ -52,6 +52,14 @@ enum Kind : int {
   kRecvReduceCopy = kLocalBit | kRecvBit | kOutBit,
   kCopySend = kLocalBit | kSendBit | kOutBit,
 };
+// A kind as a type, for steps compiled for one kind: their code has no branch
+// on what the step does, and the compiler no impossible paths to keep loads
+// pending across (kKindAtRunTime: the kind is an argument).
+constexpr int kKindAtRunTime = -1;
+template <int K>
+struct KindTag {
+  static constexpr int value = K;
+};
 
 __device__ __forceinline__ u64 divUp(u64 x, u64 y) { return (x + y - 1) / y; }
 __device__ __forceinline__ u64 alignUp(u64 x, u64 a) { return divUp(x, a) * a; }
@@ -443,13 +451,15 @@ __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
   if (++m.recvSlot == (u32)a.nSlots) m.recvSlot = 0;
 }
 
-// One FIFO step of `kind`; `valid` payload bytes start at inp / outp (and at
+// One FIFO step of kind KIND (kKindAtRunTime: of kind `kindRt`); `valid`
+// payload bytes start at inp / outp (and at
 // succOutp in the successor's output, for a direct all-gather step).
-template <int PROTO, int DT, int OP, int U, bool XWG>
-__device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, const char* inp, char* outp,
+template <int PROTO, int DT, int OP, int U, bool XWG, int KIND>
+__device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt, const char* inp, char* outp,
                                      char* succOutp, long valid) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
+  const int kind = KIND != kKindAtRunTime ? KIND : kindRt;
   const bool hasLocal = (kind & kLocalBit) != 0;
   const bool hasRecv = (kind & kRecvBit) != 0;
   const bool hasSend = (kind & kSendBit) != 0;
@@ -645,7 +655,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kind, c
 
 // One collective of the ring schedule over one member's (channel, lane)
 // share of `count` elements per rank; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL, bool XWG>
+template <int PROTO, int DT, int OP, int U, int COLL, bool XWG, bool SPEC>
 __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, int ch, int k, u64 count,
                                          const char* in, char* out, char* succOut) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -653,6 +663,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
   constexpr int PAYLOAD = PROTO == kSimple ? U * kWave * 16
                         : PROTO == kLL ? kLLSlotPayload : U * kLL128UnitPayload;
   const int N = a.nranks;
+  if (N < 2) return true;   // one rank never launches a kernel: its result is a copy
   const int succ = r + 1 == N ? 0 : r + 1;
   // channel share [pages: contiguous split per channel, 16-byte grain]
   const u64 per = alignUp(divUp(count, (u64)a.nChannels), A);
@@ -688,13 +699,9 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
       for (u64 jb = 0; jb < nCols; jb += batch) {
         const u64 je = umin(jb + batch, nCols);
         int cNext = r == 0 ? N - 1 : r - 1;   // (r - 1 - s) mod N, stepped down each stage
-        for (int s = 0; s <= 2 * N - 2; ++s) {
-          int kind;
-          if (s == 0) kind = kSend;
-          else if (s < N - 1) kind = kRecvReduceSend;
-          else if (s == N - 1) kind = kRecvReduceCopySend;
-          else if (s <= lastSendStage) kind = kRecvCopySend;
-          else kind = kRecv;
+        // stage s of this batch, of kind KIND
+        auto stage = [&](int s, auto kindTag, int kindRt) -> bool {
+          constexpr int KIND = decltype(kindTag)::value;
           // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
           const int c = s <= lastSendStage ? cNext : succ;
           cNext = cNext == 0 ? N - 1 : cNext - 1;
@@ -710,8 +717,27 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
             const u64 b = j * (u64)PAYLOAD;
             if (b >= bytes) break;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG>(a, m, kind, in + first + b, out + first + b, succOut + first + b, valid))
+            if (!step<PROTO, DT, OP, U, XWG, KIND>(a, m, kindRt, in + first + b, out + first + b,
+                                                   succOut + first + b, valid))
               return false;
+          }
+          return true;
+        };
+        // send | recv-reduce-send x (N-2) | recv-reduce-copy-send |
+        // recv-copy-send x (N-2) | recv
+        if constexpr (SPEC) {
+          if (!stage(0, KindTag<kSend>{}, 0)) return false;
+          for (int s = 1; s < N - 1; ++s)
+            if (!stage(s, KindTag<kRecvReduceSend>{}, 0)) return false;
+          if (!stage(N - 1, KindTag<kRecvReduceCopySend>{}, 0)) return false;
+          for (int s = N; s <= lastSendStage; ++s)
+            if (!stage(s, KindTag<kRecvCopySend>{}, 0)) return false;
+          if (!stage(2 * N - 2, KindTag<kRecv>{}, 0)) return false;
+        } else {
+          for (int s = 0; s <= 2 * N - 2; ++s) {
+            const int kind = s == 0 ? kSend : s < N - 1 ? kRecvReduceSend : s == N - 1 ? kRecvReduceCopySend
+                             : s <= lastSendStage ? kRecvCopySend : kRecv;
+            if (!stage(s, KindTag<kKindAtRunTime>{}, kind)) return false;
           }
         }
       }
@@ -736,15 +762,9 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
       const u64 nCols = divUp(bytes, (u64)PAYLOAD);
       for (u64 jb = 0; jb < nCols; jb += batch) {
         const u64 je = umin(jb + batch, nCols);
-        for (int s = 0; s <= N - 1; ++s) {
-          int kind, blkIdx;
-          if (rs) {
-            kind = s == 0 ? kSend : s < N - 1 ? kRecvReduceSend : kRecvReduceCopy;
-            blkIdx = (r - 1 - s + 2 * N) % N;
-          } else {
-            kind = s == 0 ? kCopySend : s < N - 1 ? kRecvCopySend : kRecv;
-            blkIdx = (r - s + N) % N;
-          }
+        auto stage = [&](int s, auto kindTag, int kindRt) -> bool {
+          constexpr int KIND = decltype(kindTag)::value;
+          const int blkIdx = rs ? (r - 1 - s + 2 * N) % N : (r - s + N) % N;
           // ReduceScatter reads block b of its input and writes its one
           // output block; AllGather reads its one input block and writes block b
           const u64 inOff = rs ? (u64)blkIdx * blk + first : first;
@@ -752,9 +772,27 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
           for (u64 j = jb; j < je; ++j) {
             const u64 b = j * (u64)PAYLOAD;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG>(a, m, kind, in + inOff + b, out + outOff + b, succOut + outOff + b,
-                                         valid))
+            if (!step<PROTO, DT, OP, U, XWG, KIND>(a, m, kindRt, in + inOff + b, out + outOff + b,
+                                                   succOut + outOff + b, valid))
               return false;
+          }
+          return true;
+        };
+        if constexpr (SPEC && rs) {
+          if (!stage(0, KindTag<kSend>{}, 0)) return false;
+          for (int s = 1; s < N - 1; ++s)
+            if (!stage(s, KindTag<kRecvReduceSend>{}, 0)) return false;
+          if (!stage(N - 1, KindTag<kRecvReduceCopy>{}, 0)) return false;
+        } else if constexpr (SPEC) {
+          if (!stage(0, KindTag<kCopySend>{}, 0)) return false;
+          for (int s = 1; s < N - 1; ++s)
+            if (!stage(s, KindTag<kRecvCopySend>{}, 0)) return false;
+          if (!stage(N - 1, KindTag<kRecv>{}, 0)) return false;
+        } else {
+          for (int s = 0; s <= N - 1; ++s) {
+            const int kind = rs ? (s == 0 ? kSend : s < N - 1 ? kRecvReduceSend : kRecvReduceCopy)
+                                : (s == 0 ? kCopySend : s < N - 1 ? kRecvCopySend : kRecv);
+            if (!stage(s, KindTag<kKindAtRunTime>{}, kind)) return false;
           }
         }
       }
@@ -765,12 +803,12 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
 
 // Every pass of one member: the (channel, lane) pairs of its FIFO set, or
 // the tasks of a batched launch; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool XWG>
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool XWG, bool SPEC>
 __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int L, int sets, int lanesTotal,
                                              int perTask, int r, int succ) {
   if (!BATCH) {
     for (int Lp = L; Lp < lanesTotal; Lp += sets) {
-      if (!ringPass<PROTO, DT, OP, U, COLL, XWG>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count,
+      if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count,
                                                  (const char*)a.send[r], (char*)a.recv[r], (char*)a.recv[succ]))
         return false;
     }
@@ -783,7 +821,7 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
   const size_t row = 1 + 2 * (size_t)N;
   for (int t = L / perTask; t < a.nTasks; t += a.taskSlots) {
     const u64* d = a.tasks + (size_t)t * row;
-    if (!ringPass<PROTO, DT, OP, U, COLL, XWG>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
+    if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
                                                (char*)d[1 + N + succ]))
       return false;
   }
@@ -795,7 +833,14 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // them run at once, each on its own nChannels x lanes wavefront sets (and
 // FIFOs); a set takes tasks slot, slot + taskSlots, ... in turn, so its FIFO
 // steps simply continue from one task to the next.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH>
+//
+// ONEWG: every ring of the launch lies inside one workgroup (the host picks
+// this instantiation for such plans only), so no edge crosses workgroups; the
+// Simple kernels of slots up to 4 KiB then also compile every step for its
+// kind (8 ranks x 4 KiB: 19.5 -> 15.8 us; 16 x 4 KiB: 45.7 -> 34.4 us).  Not
+// for 8 KiB slots, where the per-kind copies spill, nor for rings cut into
+// workgroups, where their extra registers cost residency.
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
   // The 8 KiB slot kernels read the wavefront index through readfirstlane,
   // so every per-member value (pointers, counters, rank, channel) lives in
@@ -831,7 +876,8 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // The 8 KiB Simple kernel serves single-workgroup rings only (the host
   // never plans it for a ring cut into groups), so it carries no code for
   // edges between workgroups.
-  constexpr bool GROUPED = PROTO != kSimple || U <= kGroupedSimpleUnrollMax;
+  constexpr bool GROUPED = !ONEWG && (PROTO != kSimple || U <= kGroupedSimpleUnrollMax);
+  constexpr bool SPEC = ONEWG && PROTO == kSimple && U <= kGroupedSimpleUnrollMax;
   m.recvAgent = GROUPED && pred / a.groupSize != g;
   m.sendAgent = GROUPED && succ / a.groupSize != g;
   m.selfW = wave;
@@ -855,8 +901,10 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // that edge's code; every other member runs one with no trace of it (the
   // runtime checks alone cost short messages a few percent).
   const bool ok = GROUPED && (m.sendAgent || m.recvAgent)
-                      ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, GROUPED>(a, m, L, sets, lanesTotal, perTask, r, succ)
-                      : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false>(a, m, L, sets, lanesTotal, perTask, r, succ);
+                      ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, GROUPED, false>(a, m, L, sets, lanesTotal, perTask,
+                                                                                    r, succ)
+                      : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC>(a, m, L, sets, lanesTotal, perTask, r,
+                                                                                 succ);
   if (!ok) return;
   // Publish what only LDS (an edge inside the workgroup) or the LL / LL128
   // flags (which never touch the tail counter per slot) have counted, so the
@@ -1272,17 +1320,17 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
 
 // The ring kernel for one collective, element type and op (AllGather has no
 // arithmetic: one kernel per element size).
-template <int PROTO, int U, int COLL, bool BATCH>
+template <int PROTO, int U, int COLL, bool BATCH, bool ONEWG = false>
 KernelFn pickRing(int dtype, int op) {
   if (COLL == kCollAllGather) {
     switch (dtype) {
-      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH>;
-      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH>;
-      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH>;
+      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH, ONEWG>;
+      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH, ONEWG>;
+      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH, ONEWG>;
     }
     return nullptr;
   }
-#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH>
+#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH, ONEWG>
   switch (dtype) {
     case arInt32: return op == arSum ? AR_RING(arInt32, arSum) : op == arMax ? AR_RING(arInt32, arMax)
                        : op == arMin ? AR_RING(arInt32, arMin) : nullptr;
@@ -1321,10 +1369,12 @@ KernelFn pickTree(int dtype, int op) {
 // has one slot geometry, LL128 two (2 KiB, and 4 KiB for single calls).
 template <int COLL, bool BATCH>
 KernelFn pickRingSimple(const Plan& plan, int dtype, int op) {
+  // rings inside one workgroup get the instantiation compiled for them
+  const bool one = plan.nGroups == 1;
   switch (plan.unroll) {
-    case 1: return pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
-    case 2: return pickRing<kSimple, 2, COLL, BATCH>(dtype, op);
-    case 4: return pickRing<kSimple, 4, COLL, BATCH>(dtype, op);
+    case 1: return one ? pickRing<kSimple, 1, COLL, BATCH, true>(dtype, op) : pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
+    case 2: return one ? pickRing<kSimple, 2, COLL, BATCH, true>(dtype, op) : pickRing<kSimple, 2, COLL, BATCH>(dtype, op);
+    case 4: return one ? pickRing<kSimple, 4, COLL, BATCH, true>(dtype, op) : pickRing<kSimple, 4, COLL, BATCH>(dtype, op);
     case 8: return pickRing<kSimple, 8, COLL, BATCH>(dtype, op);
   }
   return nullptr;
