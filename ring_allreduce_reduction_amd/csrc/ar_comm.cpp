@@ -104,7 +104,13 @@ const Env& env() {
 // model to 4 KiB messages at 2, 4, 8 and 16 ranks (1 channel), 128 MiB at 8
 // ranks over 1..64 channels, and 16 KiB..64 MiB at 8 ranks with the channel
 // count the 32 KiB rule allows.  Worst point off by 31% (LL), 23% (LL128),
-// 23% (Simple).
+// 23% (Simple).  These are the fit from before the single-workgroup rings
+// got steps compiled per kind: refitted on those, the Simple step latency
+// falls to 0.82 us, which rings cut into workgroups (more than 16 ranks) do
+// not reach, and the model (with no term for those) then picks the ring over
+// the tree at 32 ranks x 2 MiB, where the ring is 78% slower.  Kept, the
+// worst choice over the sweeps of 4-32 ranks and the 24-72-rank table is 11%
+// slower than the best.
 const arTuneModel_t kDefaultModels[3] = {
     /* LL     */ {3.583f, 1.7991f, 51.72f, 121.13f},
     /* LL128  */ {3.759f, 2.2949f, 77.91f, 171.17f},
@@ -113,13 +119,13 @@ const arTuneModel_t kDefaultModels[3] = {
 
 // Tree constants (same units; stepLatUs is per tree level each way), fitted
 // the same way (`bench.py --calibrate --algo tree`) with the pages' tree
-// model and its size correction: worst point off by 48% (LL, where the
-// correction's mid-size dip does not match this GPU), 20% (LL128), 48%
+// model and its size correction: worst point off by 46% (LL, where the
+// correction's mid-size dip does not match this GPU), 20% (LL128), 46%
 // (Simple).
 const arTuneModel_t kDefaultTreeModels[3] = {
-    /* LL     */ {2.300f, 1.6984f, 204.74f, 51.25f},
-    /* LL128  */ {1.619f, 2.1802f, 74.49f, 64.24f},
-    /* Simple */ {3.847f, 0.7943f, 142.75f, 145.58f},
+    /* LL     */ {2.155f, 1.6917f, 205.09f, 51.25f},
+    /* LL128  */ {1.929f, 2.1256f, 74.47f, 64.23f},
+    /* Simple */ {3.783f, 0.8090f, 142.80f, 146.26f},
 };
 
 constexpr int kStagingBuffers = 4;
