@@ -420,6 +420,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
         chunkBytes = chunkBytesFor(ch);
         for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
           layout(gs, &nGroups, &groupSize);
+          plan->nGroups = nGroups;
           plan->block = groupSize * kWave;
           int pc = 0;
           if (ringKernelOccupancy(*plan, func, dtype, op, batch, &pc) != hipSuccess) return arHipError;
@@ -475,6 +476,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       if (proto == kSimple) setSlot(u);
       for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
         layout(gs, &nGroups, &groupSize);
+        plan->nGroups = nGroups;
         plan->block = groupSize * kWave;
         int perCU = 0;
         if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return -1;

@@ -113,24 +113,24 @@ struct KernelArgs {
 
 // Everything arAllReduce decides for one call.
 struct Plan {
-  int algo;                   // arAlgoRing or arAlgoTree
-  int proto;
-  int nChannels;
-  uint64_t chunkElems;
-  int lanes;
-  int groupSize;
-  int nGroups;
-  int grid;
-  int block;
-  int slotBytes;
-  int slotPayload;
-  int nSlots;
-  int unroll;                 // pieces per lane per slot
-  int taskSlots;              // batched launches: collectives running at once
-  int laneSets;               // single-group single call: FIFO sets the grid runs (see KernelArgs)
-  bool direct;
-  bool cooperative;
-  float predictedUs;
+  int algo = 0;               // arAlgoRing or arAlgoTree
+  int proto = 0;
+  int nChannels = 0;
+  uint64_t chunkElems = 0;
+  int lanes = 0;
+  int groupSize = 0;
+  int nGroups = 1;            // the kernel picked for the plan depends on it (one group or several)
+  int grid = 0;
+  int block = 0;
+  int slotBytes = 0;
+  int slotPayload = 0;
+  int nSlots = 0;
+  int unroll = 0;             // pieces per lane per slot
+  int taskSlots = 0;          // batched launches: collectives running at once
+  int laneSets = 0;           // single-group single call: FIFO sets the grid runs (see KernelArgs)
+  bool direct = false;
+  bool cooperative = false;
+  float predictedUs = 0.0f;
 };
 
 // Provided by ar_kernels.hip (the picker functions below by ar_kernels_*.hip).
