@@ -1160,7 +1160,12 @@ struct TreeNode {
 // One AllReduce over one member's (channel, lane) share of `count` elements
 // per rank: batches of nSlots columns, each a reduce pass then (below the
 // root) a broadcast pass; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, bool XWG>
+// A tree member's role as a constant: which of its peers exist, as bits
+// kRoleD0 (child d0), kRoleD1 (child d1), kRoleParent.  A binary tree's root
+// has d1 only; every other node with children has d0, and maybe d1.
+// kRoleAtRunTime: read it from the node.
+constexpr int kRoleD0 = 1, kRoleD1 = 2, kRoleParent = 4, kRoleAtRunTime = -1;
+template <int PROTO, int DT, int OP, int U, bool XWG, int ROLE = kRoleAtRunTime>
 __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int ch, int k, int lane, u64 count,
                                          const char* inBase, char* outBase) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -1175,7 +1180,9 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
   const u64 bytes = (umin(sb + sub, len) - sb) * ESZ;
   if (bytes == 0) return true;
 
-  const bool leaf = nd.d[0] < 0 && nd.d[1] < 0;
+  const bool leaf = ROLE != kRoleAtRunTime ? (ROLE & (kRoleD0 | kRoleD1)) == 0 : nd.d[0] < 0 && nd.d[1] < 0;
+  const bool hasUp = ROLE != kRoleAtRunTime ? (ROLE & kRoleParent) != 0 : nd.up >= 0;
+  auto hasChild = [&](int i) { return ROLE != kRoleAtRunTime ? ((ROLE >> i) & 1) != 0 : nd.d[i] >= 0; };
   const char* in = inBase + (lo + sb) * ESZ;
   char* out = outBase + (lo + sb) * ESZ;
   const bool aligned = a.aligned16 != 0;
@@ -1200,7 +1207,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
         bool have = false;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          if (nd.d[i] < 0) continue;
+          if (!hasChild(i)) continue;
           v4u got[U];
           if (!edgeRecv<PROTO, U, XWG>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
           edgeFinishRecv<XWG>(a, nd.fromChild[i], lane);
@@ -1211,7 +1218,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
 #pragma unroll
         for (int u = 0; u < U; ++u) acc[u] = combine<DT, OP>(acc[u], x[u]);
       }
-      if (nd.up >= 0) {
+      if (hasUp) {
         if (!edgeSend<PROTO, U, XWG>(a, nd.toParent, pc, lane, valid, acc)) return false;
       } else {
 #pragma unroll
@@ -1219,10 +1226,10 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
           storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          if (nd.d[i] >= 0 && !edgeSend<PROTO, U, XWG>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
+          if (hasChild(i) && !edgeSend<PROTO, U, XWG>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
       }
     }
-    if (nd.up < 0) continue;
+    if (!hasUp) continue;
     // broadcast pass: the result from the parent, to my output and children
     for (u64 j = jb; j < je; ++j) {
       const u64 b = j * (u64)PAYLOAD;
@@ -1234,7 +1241,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
         storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (nd.d[i] >= 0 && !edgeSend<PROTO, U, XWG>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
+        if (hasChild(i) && !edgeSend<PROTO, U, XWG>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
     }
   }
   return true;
@@ -1242,16 +1249,16 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
 
 // Every pass of one tree member: its one call, or the tasks of a batched
 // launch; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, bool BATCH, bool XWG>
+template <int PROTO, int DT, int OP, int U, bool BATCH, bool XWG, int ROLE = kRoleAtRunTime>
 __device__ __forceinline__ bool treePasses(const KernelArgs& a, TreeNode& nd, int L, int perTask, int ch, int k,
                                            int lane, int r) {
-  if (!BATCH) return treePass<PROTO, DT, OP, U, XWG>(a, nd, ch, k, lane, a.count, (const char*)a.send[r],
-                                                     (char*)a.recv[r]);
+  if (!BATCH) return treePass<PROTO, DT, OP, U, XWG, ROLE>(a, nd, ch, k, lane, a.count, (const char*)a.send[r],
+                                                           (char*)a.recv[r]);
   const int N = a.nranks;
   const size_t row = 1 + 2 * (size_t)N;
   for (int i = L / perTask; i < a.nTasks; i += a.taskSlots) {
     const u64* d = a.tasks + (size_t)i * row;
-    if (!treePass<PROTO, DT, OP, U, XWG>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r], (char*)d[1 + N + r]))
+    if (!treePass<PROTO, DT, OP, U, XWG, ROLE>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r], (char*)d[1 + N + r]))
       return false;
   }
   return true;
@@ -1259,7 +1266,11 @@ __device__ __forceinline__ bool treePasses(const KernelArgs& a, TreeNode& nd, in
 
 // BATCH as for the ring kernel: a.nTasks AllReduces from a.tasks, a.taskSlots
 // of them at once.
-template <int PROTO, int DT, int OP, int U, bool BATCH>
+//
+// ONEWG: every tree of the launch lies inside one workgroup (the host picks
+// this instantiation for such plans only); the Simple kernels then also
+// compile a member's pass for its role (parent or root, number of children).
+template <int PROTO, int DT, int OP, int U, bool BATCH, bool ONEWG>
 __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
   // as in the ring kernel: scalar member state for the largest (4 KiB) slot
   const int wave = U == 4 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
@@ -1298,13 +1309,27 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
     nd.toParent = openEdge(a, worker(nd.up, r == p0 ? 0 : 1), cross(nd.up), false);
   }
 
-  // as in the ring kernel: only a member with an edge to another workgroup
-  // runs the pass compiled with that edge's code
-  bool xwg = nd.up >= 0 && nd.toParent.agent;
+  bool ok;
+  if constexpr (ONEWG && PROTO == kSimple) {
+    const int role = (nd.up >= 0 ? kRoleParent : 0) | (nd.d[0] >= 0 ? kRoleD0 : 0) | (nd.d[1] >= 0 ? kRoleD1 : 0);
+    switch (role) {
+#define AR_ROLE(R) treePasses<PROTO, DT, OP, U, BATCH, false, R>(a, nd, L, perTask, ch, k, lane, r)
+      case kRoleParent: ok = AR_ROLE(kRoleParent); break;                                      // leaf
+      case kRoleParent | kRoleD0: ok = AR_ROLE(kRoleParent | kRoleD0); break;                  // one child
+      case kRoleParent | kRoleD0 | kRoleD1: ok = AR_ROLE(kRoleParent | kRoleD0 | kRoleD1); break;
+      case kRoleD1: ok = AR_ROLE(kRoleD1); break;                                              // the root
+      default: ok = AR_ROLE(kRoleAtRunTime); break;   // any other shape reads its peers at run time
+#undef AR_ROLE
+    }
+  } else {
+    // as in the ring kernel: only a member with an edge to another workgroup
+    // runs the pass compiled with that edge's code
+    bool xwg = nd.up >= 0 && nd.toParent.agent;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) xwg = xwg || (nd.d[i] >= 0 && nd.toChild[i].agent);
-  const bool ok = xwg ? treePasses<PROTO, DT, OP, U, BATCH, true>(a, nd, L, perTask, ch, k, lane, r)
-                      : treePasses<PROTO, DT, OP, U, BATCH, false>(a, nd, L, perTask, ch, k, lane, r);
+    for (int i = 0; i < 2; ++i) xwg = xwg || (nd.d[i] >= 0 && nd.toChild[i].agent);
+    ok = xwg ? treePasses<PROTO, DT, OP, U, BATCH, true>(a, nd, L, perTask, ch, k, lane, r)
+             : treePasses<PROTO, DT, OP, U, BATCH, false>(a, nd, L, perTask, ch, k, lane, r);
+  }
   if (!ok) return;
   // LL / LL128 never touch the tail counter per slot: publish it once so the
   // next call starts both ends of each FIFO at the same step.
@@ -1346,9 +1371,9 @@ KernelFn pickRing(int dtype, int op) {
   return nullptr;
 }
 
-template <int PROTO, int U, bool BATCH>
+template <int PROTO, int U, bool BATCH, bool ONEWG = false>
 KernelFn pickTree(int dtype, int op) {
-#define AR_TREE(DT, OP) treeAllReduceKernel<PROTO, DT, OP, U, BATCH>
+#define AR_TREE(DT, OP) treeAllReduceKernel<PROTO, DT, OP, U, BATCH, ONEWG>
   switch (dtype) {
     case arInt32: return op == arSum ? AR_TREE(arInt32, arSum) : op == arMax ? AR_TREE(arInt32, arMax)
                        : op == arMin ? AR_TREE(arInt32, arMin) : nullptr;
@@ -1399,12 +1424,16 @@ KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
   switch (plan.proto) {
     case kLL: return pickTree<kLL, kLLUnroll, BATCH>(dtype, op);
     case kLL128: return plan.unroll == kLL128Unroll ? pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op) : nullptr;
-    case kSimple:
+    case kSimple: {
+      // trees inside one workgroup get the instantiation compiled for them
+      const bool one = plan.nGroups == 1;
       switch (plan.unroll) {
-        case 1: return pickTree<kSimple, 1, BATCH>(dtype, op);
-        case 2: return pickTree<kSimple, 2, BATCH>(dtype, op);
-        case 4: return pickTree<kSimple, 4, BATCH>(dtype, op);
+        case 1: return one ? pickTree<kSimple, 1, BATCH, true>(dtype, op) : pickTree<kSimple, 1, BATCH>(dtype, op);
+        case 2: return one ? pickTree<kSimple, 2, BATCH, true>(dtype, op) : pickTree<kSimple, 2, BATCH>(dtype, op);
+        case 4: return one ? pickTree<kSimple, 4, BATCH, true>(dtype, op) : pickTree<kSimple, 4, BATCH>(dtype, op);
       }
+      break;
+    }
   }
   return nullptr;
 }
