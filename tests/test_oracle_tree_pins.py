@@ -175,3 +175,20 @@ def test_elements_match_full(orc, dtype, op):
     full = orc.tree_allreduce(xs, dtype, op, nch)
     idx = np.random.default_rng(0).integers(0, count, 500)
     assert np.array_equal(orc.tree_elements(xs, dtype, op, nch, idx), full[idx])
+
+
+@pytest.mark.parametrize("n", list(range(2, 73)))
+def test_node_shapes(orc, n):
+    # every node of both trees has one of four peer shapes: the root has d1
+    # only; a node with children always has d0 (a leaf has neither) -- the
+    # one-workgroup tree kernel compiles a pass per shape and relies on this
+    shapes = set()
+    for t in (0, 1):
+        for r in range(n):
+            up, d0, d1 = orc.dtree(n, r, t)
+            shape = (up >= 0, d0 >= 0, d1 >= 0)
+            shapes.add(shape)
+            assert shape in {(False, False, True), (True, False, False), (True, True, False), (True, True, True)}, \
+                (n, t, r, shape)
+            assert (up < 0) == (shape == (False, False, True))   # exactly the root lacks a parent
+    assert (False, False, True) in shapes and (True, False, False) in shapes
