@@ -122,6 +122,10 @@ const arTuneModel_t kDefaultModels[3] = {
 // model and its size correction: worst point off by 46% (LL, where the
 // correction's mid-size dip does not match this GPU), 20% (LL128), 46%
 // (Simple).
+// These are the fit from before the single-workgroup trees got passes
+// compiled per role: refitted on those (Simple: 3.708, 0.721, 163.85,
+// 164.88), the model picks the tree at 16 ranks x 4 MiB, where it is 2.2x
+// slower than the ring, and at 72 ranks x 4 MiB (+39%).
 const arTuneModel_t kDefaultTreeModels[3] = {
     /* LL     */ {2.155f, 1.6917f, 205.09f, 51.25f},
     /* LL128  */ {1.929f, 2.1256f, 74.47f, 64.23f},
