@@ -109,7 +109,7 @@ const Env& env() {
 // falls to 0.82 us, which rings cut into workgroups (more than 16 ranks) do
 // not reach, and the model (with no term for those) then picks the ring over
 // the tree at 32 ranks x 2 MiB, where the ring is 78% slower.  Kept, the
-// worst choice over the sweeps of 4-32 ranks and the 24-72-rank table is 11%
+// worst choice over the sweeps of 4-32 ranks and the 24-72-rank table is 12%
 // slower than the best.
 const arTuneModel_t kDefaultModels[3] = {
     /* LL     */ {3.583f, 1.7991f, 51.72f, 121.13f},
