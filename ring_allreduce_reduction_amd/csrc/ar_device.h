@@ -53,8 +53,8 @@ enum Kind : int {
   kCopySend = kLocalBit | kSendBit | kOutBit,
 };
 // A kind as a type, for steps compiled for one kind: their code has no branch
-// on what the step does, and the compiler no impossible paths to keep loads
-// pending across (kKindAtRunTime: the kind is an argument).
+// on what the step does, nor paths for kinds no stage has
+// (kKindAtRunTime: the kind is an argument).
 constexpr int kKindAtRunTime = -1;
 template <int K>
 struct KindTag {
@@ -837,7 +837,7 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // ONEWG: every ring of the launch lies inside one workgroup (the host picks
 // this instantiation for such plans only), so no edge crosses workgroups; the
 // Simple kernels of slots up to 4 KiB then also compile every step for its
-// kind (8 ranks x 4 KiB: 19.5 -> 15.8 us; 16 x 4 KiB: 45.7 -> 34.4 us).  Not
+// kind (8 ranks x 4 KiB: 19.5 -> 15.2 us; 16 x 4 KiB: 45.6 -> 34.2 us).  Not
 // for 8 KiB slots, where the per-kind copies spill, nor for rings cut into
 // workgroups, where their extra registers cost residency.
 template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG>
