@@ -67,29 +67,35 @@ __device__ __forceinline__ u64 umin(u64 a, u64 b) { return a < b ? a : b; }
 
 // ------------------------------------------------------------- element ops
 // Sum / Max / Min with acc the incoming partial and x the local value.
-// 16-bit floats widen exactly to f32, combine, and round back to nearest-even.
+// A 16-bit Sum is the f32 sum of the two exactly widened operands, rounded
+// back to nearest-even.  For f16 the packed half add gives those bits
+// directly: f32 carries 24 significand bits, at least twice f16's 11 plus two,
+// so rounding first to f32 and then to f16 equals rounding once.  bf16 adds in
+// f32 and narrows a pair with the packed RNE conversion.  Denormals are kept
+// in both (the kernels run with f16 and f32 denormals on).  A NaN sum stays a
+// quiet NaN; its payload bits are the hardware's.
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16ToF32(u32 h) { return __uint_as_float(h << 16); }
-__device__ __forceinline__ u32 f32ToBf16(float f) {
-  u32 u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;   // quiet NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 __device__ __forceinline__ float f16ToF32(u32 h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
-__device__ __forceinline__ u32 f32ToF16(float f) {
-  return (u32)__builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32: RNE, keeps subnormals
+
+template <int DT>
+__device__ __forceinline__ u32 sumHalfPair(u32 acc, u32 x) {   // two 16-bit elements
+  if (DT == arFloat16) return __builtin_bit_cast(u32, __builtin_bit_cast(h2, acc) + __builtin_bit_cast(h2, x));
+  const f2 s = {bf16ToF32(acc & 0xffffu) + bf16ToF32(x & 0xffffu),
+                __uint_as_float(acc & 0xffff0000u) + __uint_as_float(x & 0xffff0000u)};
+  return __builtin_bit_cast(u32, __builtin_convertvector(s, bf2));
 }
 
 template <int DT, int OP>
-__device__ __forceinline__ u32 combineHalf(u32 acc, u32 x) {   // one 16-bit element
+__device__ __forceinline__ u32 maxMinHalf(u32 acc, u32 x) {   // one 16-bit element
   float a = DT == arBfloat16 ? bf16ToF32(acc) : f16ToF32(acc);
   float b = DT == arBfloat16 ? bf16ToF32(x) : f16ToF32(x);
-  if (OP == arSum) {
-    float s = a + b;
-    return DT == arBfloat16 ? f32ToBf16(s) : f32ToF16(s);
-  }
   if (OP == arMax) return (b > a) ? x : acc;
   return (b < a) ? x : acc;
 }
@@ -105,9 +111,11 @@ __device__ __forceinline__ u32 combineWord(u32 acc, u32 x) {   // one 32-bit wor
     if (OP == arSum) return acc + x;   // wraps
     if (OP == arMax) return ((int)x > (int)acc) ? x : acc;
     return ((int)x < (int)acc) ? x : acc;
+  } else if (OP == arSum) {
+    return sumHalfPair<DT>(acc, x);
   } else {                             // two 16-bit elements
-    u32 lo = combineHalf<DT, OP>(acc & 0xffffu, x & 0xffffu);
-    u32 hi = combineHalf<DT, OP>(acc >> 16, x >> 16);
+    u32 lo = maxMinHalf<DT, OP>(acc & 0xffffu, x & 0xffffu);
+    u32 hi = maxMinHalf<DT, OP>(acc >> 16, x >> 16);
     return lo | (hi << 16);
   }
 }
