@@ -538,18 +538,27 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   }
   if (proto == kSimple && !plan->cooperative && c->forcedLanes == 0) {
     // Smaller slots spread a short chunk over more lanes, but only while the
-    // grid stays within one workgroup per CU: past that, each lane is a
+    // grid stays within one workgroup per CU, or 8 wavefronts per CU where a
+    // workgroup holds fewer than 8 members: past that, each lane is a
     // chain of 2N-1 one-column steps and more of such chains side by side
     // cost more than bigger slots (8 ranks, 16 MiB per rank: 4 lanes of
     // 8 KiB take 112 us, 8 of 4 KiB 130 us, 32 lanes of 1 KiB in four rounds
     // 165 us; 16 ranks, 4 MiB: 4 lanes of 1 KiB take 88 us, 2 of 2 KiB
-    // 102 us).  A halving that keeps the lane count is taken too: the lane
-    // share still fits one slot, and the smaller slot's kernel is faster on
-    // it (a 4 KiB share: 1 lane at 8, 4 and 2 KiB slots, 2 at 1 KiB).
+    // 102 us).  Below 8 members one workgroup per CU leaves the CUs nearly
+    // idle (2 ranks x 4 MiB: 4 lanes of 8 KiB take 12.0 us, 16 of 2 KiB
+    // 8.0 us; 4 ranks x 8 MiB: 34.1 -> 25.7 us).  A halving that keeps the
+    // lane count is taken too while the lane share still fits one slot of the
+    // smaller size, whose kernel is faster on it (a 4 KiB share: 1 lane at
+    // 8, 4 and 2 KiB slots, 2 at 1 KiB); not where the FIFOs cap the lanes
+    // and the share spans several slots (8 ranks x 8 MiB tree: 21 lanes of
+    // 2 KiB slots 104 us, of 4 KiB 69 us).
+    const int members = nGroups == 1 ? N : groupSize;
+    const int maxGrid = c->numCUs * (members < 8 ? 8 / members : 1);
     while (lanes < target && plan->unroll > 1 && (uint64_t)lanes * plan->slotPayload >= chunkBytes / 2) {
       const int u = plan->unroll / 2;
       const int ln = lanesFor(slotPayloadOf(proto, u));
-      if (ln < lanes || (ln > lanes && gridFor(ln) > c->numCUs)) break;
+      if (ln < lanes || (ln > lanes && gridFor(ln) > maxGrid)) break;
+      if (ln == lanes && (uint64_t)ln * slotPayloadOf(proto, u) < chunkBytes) break;
       plan->unroll = u;
       plan->slotBytes = slotBytesOf(proto, u);
       plan->slotPayload = slotPayloadOf(proto, u);
