@@ -1,0 +1,58 @@
+"""GPU parity on the plans two planner rules produce, with the rule itself
+checked on the plan: rings of fewer than 8 ranks spread a short chunk over
+up to 8 wavefronts per CU, and a tree whose lanes the FIFOs cap keeps its
+largest slot.  Bit for bit against the oracle on every rank."""
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ring_allreduce_reduction_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+@pytest.fixture(scope="module")
+def cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("n,nbytes", [(2, 2 * MiB), (2, 4 * MiB), (2, 8 * MiB), (3, 4 * MiB), (4, 8 * MiB)])
+def test_small_ring_spreads_short_chunks(B, gu, cus, n, nbytes):
+    count = nbytes // 4
+    plan, _, _ = gu.parity_case(n, count, "float32", "sum", "simple", 64, seed=n)
+    lanes, slot, nch = plan["lanesPerChannel"], plan["stepBytes"], plan["nChannels"]
+    assert slot < 8192, plan                                  # a halved slot ...
+    assert nch * lanes > cus, plan                            # ... past one workgroup per CU
+    assert nch * lanes <= cus * (8 // n), plan                # ... within 8 wavefronts per CU
+    chunk = nbytes // nch // n                                # one loop: the chunk is a rank's share
+    assert lanes * slot >= chunk // 2, plan                   # a lane's share is about one slot
+
+
+@pytest.mark.parametrize("n,nbytes", [(8, 8 * MiB), (16, 4 * MiB), (3, 16 * MiB), (4, 16 * MiB)])
+def test_fifo_capped_tree_keeps_its_slot(B, gu, n, nbytes):
+    count = nbytes // 4
+    plan, _, _ = gu.parity_case(n, count, "float32", "sum", "simple", 64, algo="tree", seed=n + 1)
+    lanes, slot, nch = plan["lanesPerChannel"], plan["stepBytes"], plan["nChannels"]
+    assert slot == 4096, plan                                 # the tree's largest Simple slot
+    assert lanes * slot < nbytes // nch, plan                 # shares span several slots
+
+
+def test_small_ring_ragged_and_16bit(B, gu):
+    # the spread plan on a count no slot divides, and on both 16-bit types
+    gu.parity_case(2, (4 * MiB) // 4 + 12345, "float32", "sum", "simple", 64, seed=5)
+    gu.parity_case(3, (4 * MiB) // 2 + 777, "bfloat16", "sum", "simple", 64, seed=6)
+    gu.parity_case(4, (8 * MiB) // 2 + 1, "float16", "sum", "simple", 64, seed=7)
