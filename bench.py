@@ -560,10 +560,13 @@ def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
     chs, lanes, slots, directs, depths, setss = [[int(x) for x in p.split(",")] for p in parts[:6]]
     grid = [(a, b, c, e, f, h) for a in chs for b in lanes for c in slots for e in directs for f in depths
             for h in setss]
+    proto = "simple" if args.proto == "auto" else args.proto
+    comm.set_config(proto, chs[0])
+    default_depth = comm.plan(count, dtype)["nSlots"]   # the comm's own depth for this protocol
     for nch, ln, sk, d, dp, st in grid:
-        if dp:
-            B.arSetDebug(comm.handle, B.arDebugSlots, dp)
-        comm.set_config("simple" if args.proto == "auto" else args.proto, nch)
+        # every configuration sets the depth: the knob stays on the comm
+        B.arSetDebug(comm.handle, B.arDebugSlots, dp or default_depth)
+        comm.set_config(proto, nch)
         B.arSetDebug(comm.handle, B.arDebugLanes, ln)
         if args.proto == "ll128":   # the slot field sets the LL128 slot (2 or 4 KiB)
             B.arSetDebug(comm.handle, B.arDebugLL128SlotKiB, sk)
