@@ -187,14 +187,25 @@ def main():
     log("per-launch ms: mean %.4f min %.4f max %.4f; wall per step %.4f ms"
         % (ms, min(launch_ms), max(launch_ms), wall / args.steps * 1e3))
 
-    # sanity (no oracle here): every rank holds identical bits, and a sample is
-    # within the fp32 bound of a float64 direct sum computed by torch
+    # Checks of the timed result: every rank holds identical bits (on the
+    # device), rank 0 equals the oracle bit for bit (below, with the CPU
+    # baseline), and a sample is within the stated bound of a float64 direct
+    # reduction computed by torch.
     same = all(torch.equal(recvs[0].view(torch.uint8), r.view(torch.uint8)) for r in recvs[1:])
     idx = torch.randint(0, count, (100000,), device="cuda", generator=torch.Generator("cuda").manual_seed(1))
     vals = torch.stack([x[idx].double() for x in sends])
     ref = vals.sum(0) if args.op == "sum" else vals.max(0).values if args.op == "max" else vals.min(0).values
     err_max = (recvs[0][idx].double() - ref).abs().max().item()
-    log("all ranks identical: %s; sample max |err| vs float64 %s = %.3g" % (same, args.op, err_max))
+    if args.op != "sum" or dtype == "int32":
+        err_bound = 0.0                                    # order-free results are exact
+    elif dtype == "float32":
+        err_bound = 1e-6 * N * vals.abs().max().item()     # the stated fp32 bound
+    else:                                                  # 16-bit: the dtype's own ring bound
+        u = 2.0 ** -8 if dtype == "bfloat16" else 2.0 ** -11
+        err_bound = (N - 1) * u / (1 - (N - 1) * u) * vals.abs().sum(0).max().item()
+    log("all ranks identical: %s; sample max |err| vs float64 %s = %.3g (bound %.3g)"
+        % (same, args.op, err_max, err_bound))
+    rank0 = None if xs is None else recvs[0].view({4: torch.int32, 2: torch.int16}[esz]).cpu().numpy()
 
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -210,9 +221,15 @@ def main():
         except Exception as e:  # a stale or partial file must not break the bench
             log("traffic file unreadable: %s" % e)
 
-    cpu = None if (args.no_cpu_baseline or xs is None) else cpu_baseline(xs, dtype, plan, N, S, B)
     comm.close()
     del sends, recvs
+    cpu, oracle_exact = None, None
+    if xs is not None:
+        cpu, want = cpu_baseline(xs, dtype, args.op, plan, N, S, B, timed=not args.no_cpu_baseline)
+        raw = {4: np.uint32, 2: np.uint16}[esz]
+        oracle_exact = bool(np.array_equal(rank0.view(raw), want.view(raw)))
+        log("rank 0 bit-exact against the oracle on the plan it ran: %s" % oracle_exact)
+        del rank0, want
     ceiling = None if args.no_stream_ceiling else stream_ceiling(torch)
 
     algo = B.ALGO_NAMES[plan["algo"]]
@@ -244,6 +261,9 @@ def main():
         "model_bytes_per_step": model_bytes,
         "hbm_frac_model": round(achieved / HBM_PEAK_GBS, 4),
         "all_ranks_identical": bool(same),
+        "oracle_exact": oracle_exact,
+        "err_max": err_max,
+        "err_bound": err_bound,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
@@ -252,6 +272,11 @@ def main():
     if ceiling:
         out["model_vs_copy_ceiling"] = round(achieved / ceiling["copy"], 4)
     print(json.dumps(out), flush=True)
+    # a number is published only for a correct result
+    if not same or oracle_exact is False or err_max > err_bound:
+        log("RESULT CHECK FAILED: ranks identical %s, oracle exact %s, sample err %.3g (bound %.3g)"
+            % (same, oracle_exact, err_max, err_bound))
+        sys.exit(3)
 
 
 def stream_ceiling(torch, nbytes=1 << 30, steps=10):
@@ -365,26 +390,50 @@ def summarize_profiles(args):
         print("\nwrote %s[%s]" % (path, args.profile_label))
 
 
-def cpu_baseline(xs, dtype, plan, N, S, B):
-    """The oracle, as it stands, on the headline inputs (single thread),
-    repeated until about 10 s of CPU work; reported in the metric's unit."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(xs, dtype, op, plan, N, S, B, timed=True):
+    """The oracle, as it stands, on the timed inputs and the plan that ran
+    (single thread, pinned to one core of the process's set), repeated until
+    about 10 s of CPU work; reported in the metric's unit.  Returns (the
+    baseline record or None, the oracle's result of the first run)."""
     import oracle
-    reps, total = 0, 0.0
-    while total < 10.0 and reps < 50:
-        t0 = time.perf_counter()
-        if plan["algo"] == B.arAlgoTree:
-            oracle.tree_allreduce(xs, dtype, "sum", plan["nChannels"])
-        else:
-            oracle.allreduce(xs, dtype, "sum", plan["nChannels"], plan["chunkElems"])
-        total += time.perf_counter() - t0
-        reps += 1
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        reps, total, want = 0, 0.0, None
+        while reps == 0 or (timed and total < 10.0 and reps < 50):
+            t0 = time.perf_counter()
+            if plan["algo"] == B.arAlgoTree:
+                res = oracle.tree_allreduce(xs, dtype, op, plan["nChannels"])
+            else:
+                res = oracle.allreduce(xs, dtype, op, plan["nChannels"], plan["chunkElems"])
+            total += time.perf_counter() - t0
+            reps += 1
+            if want is None:
+                want = res
+    finally:
+        os.sched_setaffinity(0, allowed)
+    if not timed:
+        return None, want
     t = total / reps
     busbw = S / t / 1e9 * 2 * (N - 1) / N
-    log("cpu oracle: %d runs, %.3f s per AllReduce" % (reps, t))
+    log("cpu oracle: %d runs, %.3f s per AllReduce on core %d of %d" % (reps, t, core, os.cpu_count()))
     return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "the full %d x %d MiB %s workload, %d run(s) of the single-threaded C oracle "
-                      "(its one result array stands for every rank's output), %.2f s each"
-                      % (N, S >> 20, dtype, reps, t)}
+            "host_cores": os.cpu_count(), "cores_allowed": len(allowed), "cpu_model": cpu_model(),
+            "pinned_core": core,
+            "sample": "the full %d x %d MiB %s %s workload, %d run(s) of the single-threaded C oracle pinned to "
+                      "one core (its one result array stands for every rank's output), %.2f s each"
+                      % (N, S >> 20, dtype, op, reps, t)}, want
 
 
 def bench_halves(args, B, gen, torch, np):

@@ -128,7 +128,10 @@ arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, ar
  * [B ch.2 §2.4, LL128 alignment]; arProtoAuto never picks LL128 then.
  * A ring member that waits longer than the timeout (or an abort) makes the
  * kernel exit early and is reported by arCommGetAsyncError as arRemoteError;
- * the comm then only accepts arDestroy.
+ * the comm then only accepts arDestroy: a later call returns arRemoteError
+ * (arInvalidUsage once arCommGetAsyncError or arCommAbort has been called)
+ * and enqueues nothing, and the kernels of calls queued before the failure
+ * was seen do nothing (their outputs are left untouched).
  */
 arResult_t arAllReduce(arComm_t comm, const void* const* sendbufs, void* const* recvbufs,
                        size_t count, arDataType_t dtype, arRedOp_t op, void* stream);
@@ -308,6 +311,13 @@ arResult_t arGetPlanColl(arComm_t comm, arFunc_t func, size_t count, arDataType_
  * [B ch.2 §2.1 asyncResult; ch.7 group error paths].
  */
 arResult_t arCommGetAsyncError(arComm_t comm, arResult_t* asyncError);
+
+/*
+ * arCommCount -- the number of virtual ranks of a comm [B ch.1 §1.2, the
+ * query calls that check a new communicator: ncclCommCount].
+ *  nranks (host, out).  arInvalidArgument for a bad comm or NULL.
+ */
+arResult_t arCommCount(arComm_t comm, int* nranks);
 
 /*
  * arCommAbort -- raise the comm's abort word (host memory visible to running

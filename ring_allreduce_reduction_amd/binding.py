@@ -98,6 +98,7 @@ def lib():
         L.arGetPlan.argtypes = [vp, c_sz, c_int, c_int, ctypes.POINTER(arPlan_t)]
         L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arCommAbort.argtypes = [vp]
+        L.arCommCount.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arDestroy.argtypes = [vp]
         L.arSetDebug.argtypes = [vp, c_int, ctypes.c_int64]
         L.arGetErrorString.argtypes = [c_int]
@@ -106,7 +107,7 @@ def lib():
                    "arTuneEvalColl", "arTuneGetModel", "arTuneSetModel", "arSetConfig", "arGetPlan", "arGetPlanColl",
                    "arSetAlgo", "arTuneAlgo", "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel",
                    "arGroupStart", "arGroupEnd", "arGroupAggregate", "arGetGroupPlan",
-                   "arCommGetAsyncError", "arCommAbort", "arDestroy", "arSetDebug"):
+                   "arCommGetAsyncError", "arCommAbort", "arCommCount", "arDestroy", "arSetDebug"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -127,6 +128,9 @@ def arInit(nranks, nChannels, proto=arProtoSimple, algo=arAlgoRing):
     return h
 
 
+ELEM_SIZE = {arInt32: 4, arFloat32: 4, arFloat16: 2, arBfloat16: 2, arUint64: 8}
+
+
 def _ptrs(bufs):
     out = []
     for b in bufs:
@@ -137,6 +141,40 @@ def _ptrs(bufs):
         else:
             out.append(int(b))
     return (ctypes.c_void_p * len(out))(*out)
+
+
+def _check_bufs(n, sendbufs, recvbufs, dtype, send_elems, recv_elems):
+    """The checks the C side cannot make: the library reads exactly n
+    pointers from each array, and a tensor shorter than what the call
+    touches would be an out-of-bounds device access.  Tensors must share one
+    element type of the call's element size and hold at least send_elems /
+    recv_elems elements; raw addresses are the caller's responsibility."""
+    if len(sendbufs) != n or len(recvbufs) != n:
+        raise ValueError("need %d send and %d receive buffers, got %d and %d"
+                         % (n, n, len(sendbufs), len(recvbufs)))
+    esz = ELEM_SIZE.get(int(dtype))
+    if esz is None:
+        raise ValueError("unknown dtype %r" % (dtype,))
+    first = None
+    for what, bufs, need in (("send", sendbufs, send_elems), ("receive", recvbufs, recv_elems)):
+        for r, b in enumerate(bufs):
+            if not isinstance(b, torch.Tensor):
+                continue
+            if first is None:
+                first = b.dtype
+            if b.dtype != first:
+                raise ValueError("%s buffer %d is %s, expected %s like the others" % (what, r, b.dtype, first))
+            if b.element_size() != esz:
+                raise ValueError("%s buffer %d has %d-byte elements, the call's dtype %d-byte ones"
+                                 % (what, r, b.element_size(), esz))
+            if b.numel() < need:
+                raise ValueError("%s buffer %d holds %d elements, the call touches %d" % (what, r, b.numel(), need))
+
+
+def _checked_ptrs(comm, sendbufs, recvbufs, dtype, send_elems, recv_elems):
+    """Pointer arrays for a call on `comm`, after _check_bufs."""
+    _check_bufs(arCommCount(comm), sendbufs, recvbufs, dtype, send_elems, recv_elems)
+    return _ptrs(sendbufs), _ptrs(recvbufs)
 
 
 def _dtype_of(t):
@@ -158,8 +196,8 @@ def arAllReduce(comm, sendbufs, recvbufs, count=None, dtype=None, op=arSum, stre
     if stream is None:
         stream = torch.cuda.current_stream()
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _check(lib().arAllReduce(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(count), int(dtype), int(op),
-                             ctypes.c_void_p(handle)), "arAllReduce")
+    sp, rp = _checked_ptrs(comm, sendbufs, recvbufs, dtype, count, count)
+    _check(lib().arAllReduce(comm, sp, rp, int(count), int(dtype), int(op), ctypes.c_void_p(handle)), "arAllReduce")
 
 
 def _stream_handle(stream):
@@ -174,7 +212,9 @@ def arReduceScatter(comm, sendbufs, recvbufs, recvcount=None, dtype=None, op=arS
         recvcount = recvbufs[0].numel()
     if dtype is None:
         dtype = _dtype_of(sendbufs[0])
-    _check(lib().arReduceScatter(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(recvcount), int(dtype), int(op),
+    n = arCommCount(comm)
+    sp, rp = _checked_ptrs(comm, sendbufs, recvbufs, dtype, n * int(recvcount), recvcount)
+    _check(lib().arReduceScatter(comm, sp, rp, int(recvcount), int(dtype), int(op),
                                  ctypes.c_void_p(_stream_handle(stream))), "arReduceScatter")
 
 
@@ -184,8 +224,10 @@ def arAllGather(comm, sendbufs, recvbufs, sendcount=None, dtype=None, stream=Non
         sendcount = sendbufs[0].numel()
     if dtype is None:
         dtype = _dtype_of(sendbufs[0])
-    _check(lib().arAllGather(comm, _ptrs(sendbufs), _ptrs(recvbufs), int(sendcount), int(dtype),
-                             ctypes.c_void_p(_stream_handle(stream))), "arAllGather")
+    n = arCommCount(comm)
+    sp, rp = _checked_ptrs(comm, sendbufs, recvbufs, dtype, sendcount, n * int(sendcount))
+    _check(lib().arAllGather(comm, sp, rp, int(sendcount), int(dtype), ctypes.c_void_p(_stream_handle(stream))),
+           "arAllGather")
 
 
 def arTuneEvalColl(func, nranks, maxChannels, nBytes, models, protoMask=7):
@@ -319,6 +361,12 @@ def arCommGetAsyncError(comm):
     e = ctypes.c_int()
     _check(lib().arCommGetAsyncError(comm, ctypes.byref(e)), "arCommGetAsyncError")
     return e.value
+
+
+def arCommCount(comm):
+    n = ctypes.c_int()
+    _check(lib().arCommCount(comm, ctypes.byref(n)), "arCommCount")
+    return n.value
 
 
 def arCommAbort(comm):

@@ -167,6 +167,7 @@ struct arComm {
   size_t fifoWorkerBytes[3];
   Control* ctrlHost;
   Control* ctrlDev;
+  uint32_t* failedDev;  // device word the kernels set when a member gives up
   arTuneModel_t models[3];       // ring
   arTuneModel_t treeModels[3];
   int64_t timeoutUs;
@@ -225,6 +226,7 @@ void freeComm(arComm* c) {
     if (c->conn[p]) (void)hipFree(c->conn[p]);
   }
   if (c->ctrlHost) (void)hipHostFree(c->ctrlHost);
+  if (c->failedDev) (void)hipFree(c->failedDev);
   if (c->taskTable) (void)hipFree(c->taskTable);
   for (int i = 0; i < kStagingBuffers; ++i) {
     if (c->taskStaging[i]) (void)hipHostFree(c->taskStaging[i]);
@@ -677,6 +679,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   }
   memset(c->ctrlHost, 0, sizeof(Control));
   if (hipHostGetDevicePointer((void**)&c->ctrlDev, c->ctrlHost, 0) != hipSuccess ||
+      hipMalloc((void**)&c->failedDev, 256) != hipSuccess || hipMemset(c->failedDev, 0, 256) != hipSuccess ||
       hipEventCreateWithFlags(&c->stagingDone[0], hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&c->stagingDone[1], hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&c->stagingDone[2], hipEventDisableTiming) != hipSuccess ||
@@ -832,6 +835,15 @@ thread_local int tGroupDepth = 0;
 thread_local arResult_t tGroupError = arSuccess;
 thread_local std::vector<arComm*> tGroupComms;
 
+// A member of an earlier call timed out or saw the abort word: its edges were
+// left mid-call, so the comm accepts no more work (the kernels of calls
+// already queued check the device copy of this word and do nothing).
+bool memberGaveUp(arComm* c) {
+  if (__atomic_load_n(&c->ctrlHost->status, __ATOMIC_ACQUIRE) == 0) return false;
+  c->aborted = true;
+  return true;
+}
+
 // Every (channel, lane, rank, edge) FIFO the kernel indexes must exist.
 bool fifosCover(const arComm* c, const Plan& plan) {
   const int edges = plan.algo == arAlgoTree ? kTreeEdges : 1;
@@ -851,6 +863,7 @@ void buildArgs(const arComm* c, const Plan& plan, int func, size_t count, const 
   a->fifo = c->fifo[plan.proto];
   a->conn = c->conn[plan.proto];
   a->ctrl = c->ctrlDev;
+  a->failed = c->failedDev;
   a->count = count;
   a->chunkElems = plan.chunkElems;
   a->fifoWorkerBytes = c->fifoWorkerBytes[plan.proto];
@@ -877,6 +890,7 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
                    arDataType_t dtype, arRedOp_t op, void* stream) {
   if (!commOk(c)) return arInvalidArgument;
   if (c->aborted) return arInvalidUsage;
+  if (memberGaveUp(c)) return arRemoteError;
   const int esz = elemSize(dtype);
   if (esz == 0) return arInvalidArgument;
   if (op != arSum && op != arMax && op != arMin && op != arProbe) return arInvalidArgument;
@@ -1009,6 +1023,8 @@ arResult_t launchGroup(arComm* c) {
   const int N = c->nranks;
   const int n = (int)T.size();
   const hipStream_t st = T[0].stream;
+  if (c->aborted) return arInvalidUsage;
+  if (memberGaveUp(c)) return arRemoteError;
   c->groupPlans.assign((size_t)n, arPlan_t());
   c->opCount += (uint64_t)n;
   if (N == 1) {   // the result is the input [ch.6 §三, one-rank path]
@@ -1187,6 +1203,12 @@ arResult_t arCommGetAsyncError(arComm_t c, arResult_t* err) {
   const uint32_t st = __atomic_load_n(&c->ctrlHost->status, __ATOMIC_ACQUIRE);
   if (st != 0) c->aborted = true;
   *err = (st != 0 || c->ctrlHost->abortFlag != 0) ? arRemoteError : arSuccess;
+  return arSuccess;
+}
+
+arResult_t arCommCount(arComm_t c, int* nranks) {
+  if (!commOk(c) || nranks == nullptr) return arInvalidArgument;
+  *nranks = c->nranks;
   return arSuccess;
 }
 

@@ -296,7 +296,11 @@ __device__ __forceinline__ void stCounterRelease(u64* p, u64 v, bool agent) {
 // into workgroups read it often enough to stall one another (32 ranks x
 // 64 MiB: 10 of 36 calls 1.1-3.4x slower; none at 4096).  On give-up the
 // member records why and the caller returns, so every wavefront of the
-// kernel always exits.
+// kernel always exits.  The reason goes to the host-visible status word and
+// to the comm's failed word in device memory: a member that gave up left its
+// counters (and LL / LL128 lines) in the middle of a call, so a later call
+// must not start from them; every kernel reads the failed word on entry and
+// does nothing once it is set.
 //
 // A waiting wavefront drops to the lowest issue priority until its wait
 // ends; the kernels run at kWorkPrio otherwise.  Up to 15 members of a
@@ -312,23 +316,30 @@ struct Waiter {
   }
 };
 
-__device__ __forceinline__ bool keepWaiting(Control* ctrl, u64 timeoutTicks, Waiter& w) {
+__device__ __forceinline__ bool keepWaiting(const KernelArgs& a, Waiter& w) {
   if (w.spins == 0) __builtin_amdgcn_s_setprio(0);
   ++w.spins;
   __builtin_amdgcn_s_sleep(2);
   if ((w.spins & 4095u) == 0) {
     const u64 now = wall_clock64();
     if (w.spins == 4096u) w.t0 = now;
-    u32 ab = __hip_atomic_load(&ctrl->abortFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    u32 ab = __hip_atomic_load(&a.ctrl->abortFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     u32 code = 0;
     if (__builtin_amdgcn_readfirstlane(ab) != 0) code = kStatusAbort;
-    else if (now - w.t0 > timeoutTicks || w.spins >= (1u << 30)) code = kStatusTimeout;
+    else if (now - w.t0 > a.timeoutTicks || w.spins >= (1u << 30)) code = kStatusTimeout;
     if (code != 0) {
-      __hip_atomic_store(&ctrl->status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(a.failed, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl->status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       return false;
     }
   }
   return true;
+}
+
+// Nonzero once a member of an earlier call (or of this one) gave up.  Read
+// once per wavefront on entry, before anything of the call is touched.
+__device__ __forceinline__ u32 callFailed(const KernelArgs& a) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.failed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Wait until *p >= target.
@@ -336,7 +347,7 @@ __device__ __forceinline__ bool waitGeq(const KernelArgs& a, const u64* p, u64 t
   if (ldCounter(p, agent) >= target) return true;
   Waiter w;
   while (true) {
-    if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+    if (!keepWaiting(a, w)) return false;
     if (ldCounter(p, agent) >= target) return true;
   }
 }
@@ -375,7 +386,7 @@ __device__ __forceinline__ bool waitLdsGeq(const KernelArgs& a, int i, u64 targe
   if (ldLds(i) >= target) return true;
   Waiter w;
   while (true) {
-    if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+    if (!keepWaiting(a, w)) return false;
     if (ldLds(i) >= target) return true;
   }
 }
@@ -434,7 +445,7 @@ __device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
     if (m.succHead < need) {
       Waiter w;
       do {
-        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+        if (!keepWaiting(a, w)) return false;
         m.succHead = agent ? ldCounter(&m.succ->head, true) : ldLds(kLdsHead + m.succW);
       } while (m.succHead < need);
     }
@@ -556,7 +567,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
           }
         }
         if (__all(all)) break;
-        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+        if (!keepWaiting(a, w)) return false;
       }
     } else {  // LL128: poll the flag of every live line, then read payload
       const u64 flag = m.recvStep + 1;
@@ -575,7 +586,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
           }
         }
         if (__all(all)) break;
-        if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+        if (!keepWaiting(a, w)) return false;
       }
       acquireEdge();
 #pragma unroll
@@ -892,7 +903,9 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   m.succW = succ - g * a.groupSize;   // used only when the successor shares the workgroup
   m.aligned = a.aligned16 != 0;
   m.direct = a.direct != 0;
-  // counters carry over from earlier calls (tail == head at call boundaries)
+  // counters carry over from earlier calls (tail == head at call boundaries,
+  // unless a member of an earlier call gave up: then nothing runs)
+  const u32 failed = live ? callFailed(a) : 0u;
   m.recvStep = live ? ldCounter(&m.self->head, true) : 0;
   m.sendStep = live ? ldCounter(&m.succ->tail, true) : 0;
   m.succHead = 0;
@@ -903,7 +916,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
     stLds(kLdsHead + wave, m.recvStep);
   }
   __syncthreads();
-  if (!live || r == a.deadRank) return;
+  if (!live || r == a.deadRank || failed != 0) return;
 
   // A member with an edge to another workgroup runs the pass compiled with
   // that edge's code; every other member runs one with no trace of it (the
@@ -1059,7 +1072,7 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
         }
       }
       if (__all(all)) break;
-      if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+      if (!keepWaiting(a, w)) return false;
     }
   } else {
     const u64 flag = e.step + 1;
@@ -1078,7 +1091,7 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
         }
       }
       if (__all(all)) break;
-      if (!keepWaiting(a.ctrl, a.timeoutTicks, w)) return false;
+      if (!keepWaiting(a, w)) return false;
     }
     acquireEdge();
 #pragma unroll
@@ -1293,6 +1306,8 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
   if (L >= lanesTotal) return;
   const int r = g * a.groupSize + wave;
   if (r >= N || r == a.deadRank) return;
+  // an earlier call left its edges mid-call when a member gave up
+  if (callFailed(a) != 0) return;
   const int Lc = BATCH ? L % perTask : L;   // (channel, lane) inside the task
   const int ch = Lc / a.lanes;
   const int k = Lc % a.lanes;

@@ -86,6 +86,7 @@ struct KernelArgs {
   char* fifo;                 // this protocol's FIFOs, fifoWorkerBytes per worker
   Conn* conn;                 // this protocol's counters, one per worker
   Control* ctrl;              // host-pinned control block (device address)
+  uint32_t* failed;           // device word: nonzero once a member of this comm gave up
   uint64_t count;             // elements per rank (per rank block for ReduceScatter / AllGather)
   uint64_t chunkElems;        // nominal chunk (elements)
   uint64_t fifoWorkerBytes;   // nSlots * slot bytes

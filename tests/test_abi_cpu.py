@@ -27,7 +27,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = set(_declared())
-    for fn in ("arInit", "arAllReduce", "arTune", "arCommGetAsyncError", "arCommAbort", "arDestroy",
+    for fn in ("arInit", "arAllReduce", "arTune", "arCommGetAsyncError", "arCommAbort", "arCommCount", "arDestroy",
                "arGetErrorString", "arTuneEval", "arGetPlan", "arSetConfig", "arSetAlgo", "arTuneAlgo",
                "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel"):
         assert fn in names
@@ -77,9 +77,54 @@ def test_calls_on_a_null_comm(B):
     assert L.arDestroy(None) == B.arSuccess
     e = ctypes.c_int()
     assert L.arCommGetAsyncError(None, ctypes.byref(e)) == B.arInvalidArgument
+    assert L.arCommCount(None, ctypes.byref(e)) == B.arInvalidArgument
     # a pointer that is not a comm (no magic) is refused, not dereferenced as one
     junk = ctypes.create_string_buffer(4096)
     assert L.arAllReduce(ctypes.cast(junk, ctypes.c_void_p), ptrs, ptrs, 4, 1, 0, None) == B.arInvalidArgument
+    assert L.arCommCount(ctypes.cast(junk, ctypes.c_void_p), ctypes.byref(e)) == B.arInvalidArgument
+
+
+# ---------------------------------------------------------------- binding checks
+# The library reads nranks pointers from each array and trusts the sizes, so
+# the binding rejects short lists, mixed element types and short tensors
+# before anything is passed on (CPU tensors stand in for device ones here:
+# the checks look only at length, element type and element count).
+
+def test_binding_rejects_wrong_buffer_lists(B):
+    import torch
+    four = [torch.zeros(64, dtype=torch.float32) for _ in range(4)]
+    B._check_bufs(4, four, four, B.arFloat32, 64, 64)               # a valid call passes
+    with pytest.raises(ValueError, match="need 4"):
+        B._check_bufs(4, four[:3], four, B.arFloat32, 64, 64)
+    with pytest.raises(ValueError, match="need 4"):
+        B._check_bufs(4, four, four + four[:1], B.arFloat32, 64, 64)
+
+
+def test_binding_rejects_mixed_or_wrong_element_types(B):
+    import torch
+    f32 = [torch.zeros(64, dtype=torch.float32) for _ in range(4)]
+    mixed = f32[:3] + [torch.zeros(64, dtype=torch.int32)]
+    with pytest.raises(ValueError, match="like the others"):
+        B._check_bufs(4, f32, mixed, B.arFloat32, 64, 64)
+    with pytest.raises(ValueError, match="byte elements"):
+        B._check_bufs(4, f32, f32, B.arFloat16, 64, 64)
+    with pytest.raises(ValueError, match="unknown dtype"):
+        B._check_bufs(4, f32, f32, 9, 64, 64)
+
+
+def test_binding_rejects_short_tensors(B):
+    import torch
+    blk = [torch.zeros(64, dtype=torch.float32) for _ in range(4)]
+    big = [torch.zeros(4 * 64, dtype=torch.float32) for _ in range(4)]
+    with pytest.raises(ValueError, match="holds 64 elements, the call touches 65"):
+        B._check_bufs(4, blk, blk, B.arFloat32, 65, 65)
+    # ReduceScatter: sends hold nranks blocks, receives one
+    B._check_bufs(4, big, blk, B.arFloat32, 4 * 64, 64)
+    with pytest.raises(ValueError, match="send buffer 0"):
+        B._check_bufs(4, blk, blk, B.arFloat32, 4 * 64, 64)
+    # AllGather: receives hold nranks blocks
+    with pytest.raises(ValueError, match="receive buffer 0"):
+        B._check_bufs(4, blk, blk, B.arFloat32, 64, 4 * 64)
 
 
 # ---------------------------------------------------------------- tuner

@@ -49,6 +49,67 @@ def test_dead_rank_times_out_and_poisons_the_comm(B, proto):
         assert torch.allclose(recvs[5].double(), ref, atol=1e-5)
 
 
+@pytest.mark.parametrize("n,proto", [(8, "simple"), (8, "ll"), (8, "ll128"), (24, "simple"), (24, "ll128")])
+def test_call_queued_behind_a_timeout_runs_nothing(B, n, proto):
+    """A member that gives up leaves its edges mid-call (LL / LL128 lines
+    carrying later steps' flags; published counters between workgroups past
+    16 ranks).  A call already queued behind it must not start from them:
+    its kernel does nothing and its outputs stay untouched.  The first call's
+    timeout (200 ms) is far longer than the host needs to queue the second."""
+    import gpu_util
+    gpu_util.note("queued behind a timeout: n=%d proto=%s dead rank 3, timeout 200 ms" % (n, proto))
+    count = 100000
+    sends, recvs = _bufs(n, count)
+    second = [gpu_util.empty_like_sentinel(count, "float32") for _ in range(n)]
+    with B.Comm(n, 4, proto) as comm:
+        B.arSetDebug(comm.handle, B.arDebugTimeoutUs, 200000)
+        B.arSetDebug(comm.handle, B.arDebugDeadRank, 3)
+        comm.allreduce(sends, recvs, "sum")
+        B.arSetDebug(comm.handle, B.arDebugDeadRank, -1)
+        try:
+            comm.allreduce(sends, second, "sum")     # normally queued while the first still waits
+        except B.ArError as e:                        # or refused, if the first had already failed
+            assert e.code == B.arRemoteError
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arRemoteError
+        for r in range(n):
+            assert bool((second[r].view(torch.int32) == -1).all()), "rank %d output was written" % r
+        with pytest.raises(B.ArError) as e:
+            comm.allreduce(sends, second, "sum")
+        assert e.value.code == B.arInvalidUsage
+
+
+def test_failure_seen_by_the_host_refuses_the_next_call(B):
+    """Without arCommGetAsyncError, the next call reads the status word itself."""
+    import gpu_util
+    gpu_util.note("status word refuses the next call: n=8 simple dead rank 2, timeout 2 ms")
+    sends, recvs = _bufs(8, 4096)
+    with B.Comm(8, 2, "simple") as comm:
+        B.arSetDebug(comm.handle, B.arDebugTimeoutUs, 2000)
+        B.arSetDebug(comm.handle, B.arDebugDeadRank, 2)
+        comm.allreduce(sends, recvs, "sum")
+        torch.cuda.synchronize()
+        B.arSetDebug(comm.handle, B.arDebugDeadRank, -1)
+        with pytest.raises(B.ArError) as e:
+            comm.allreduce(sends, recvs, "sum")
+        assert e.value.code == B.arRemoteError
+
+
+def test_binding_refuses_short_lists_before_the_library(B):
+    import gpu_util
+    sends, recvs = _bufs(4, 1024)
+    with B.Comm(4, 2, "simple") as comm:
+        assert B.arCommCount(comm.handle) == 4
+        with pytest.raises(ValueError):
+            comm.allreduce(sends[:3], recvs, "sum")
+        with pytest.raises(ValueError):
+            comm.allreduce(sends, recvs[:2] + [recvs[2][:512], recvs[3]], "sum")
+        out = [gpu_util.empty_like_sentinel(1024, "float32") for _ in range(4)]
+        comm.allreduce(sends, out, "sum")
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arSuccess
+
+
 def test_abort_releases_waiting_members(B):
     import gpu_util
     gpu_util.note("abort while rank 0 is dead, timeout 4 s")
