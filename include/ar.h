@@ -396,6 +396,35 @@ arResult_t arGroupAggregate(int nTasks, const int* keys, const size_t* bytes, co
  * the comm's last launched group ran with; arInvalidArgument out of range. */
 arResult_t arGetGroupPlan(arComm_t comm, int index, arPlan_t* plan);
 
+/*
+ * arAllReduceNoAlloc -- arAllReduce for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It needs no communicator and allocates nothing (no
+ * hipMalloc, hipFree or allocating library call, on any call).
+ * What it computes: exactly arAllReduce on a comm of `nranks` ranks with
+ * arProtoSimple, arAlgoRing and `nChannels` channels (same channel split and
+ * chunk, hence the same bits); the same environment overrides apply.
+ *  sendbufs, recvbufs, count, dtype, op, stream: as in arAllReduce.
+ *  nranks     1..16: every ring fits one workgroup, so every FIFO edge keeps
+ *             its counters in LDS and each call starts from step 0.
+ *  nChannels  1..AR_MAX_CHANNELS.
+ * Its FIFOs live in a fixed 64 MiB device array inside the library, one per
+ * GPU it runs on, held until the process ends; the device's first call looks
+ * up that array's address and clears its header with a small kernel on
+ * `stream`.  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (several host threads, or streams not ordered with each other)
+ * race and give undefined results; order them on one stream.  Lanes per
+ * channel are capped by what the array holds (never a different result).
+ * Errors: arInvalidArgument for bad arguments (nothing enqueued);
+ * arInvalidUsage when even one lane per channel does not fit the array (the
+ * maximum: nranks x nChannels x FIFO depth x 8 KiB plus 256 bytes per lane)
+ * or when AR_PROTO / AR_ALGO force another protocol or algorithm; arHipError
+ * for HIP failures.  A member that waits longer than the timeout gives up and
+ * that call's output is incomplete; with no comm, this path does not report it.
+ */
+arResult_t arAllReduceNoAlloc(const void* const* sendbufs, void* const* recvbufs, int nranks, int nChannels,
+                              size_t count, arDataType_t dtype, arRedOp_t op, void* stream);
+
 const char* arGetErrorString(arResult_t result);
 
 /* Library limits. */

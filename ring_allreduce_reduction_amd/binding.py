@@ -99,6 +99,7 @@ def lib():
         L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arCommAbort.argtypes = [vp]
         L.arCommCount.argtypes = [vp, ctypes.POINTER(c_int)]
+        L.arAllReduceNoAlloc.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_int, c_int, c_sz, c_int, c_int, vp]
         L.arDestroy.argtypes = [vp]
         L.arSetDebug.argtypes = [vp, c_int, ctypes.c_int64]
         L.arGetErrorString.argtypes = [c_int]
@@ -107,7 +108,8 @@ def lib():
                    "arTuneEvalColl", "arTuneGetModel", "arTuneSetModel", "arSetConfig", "arGetPlan", "arGetPlanColl",
                    "arSetAlgo", "arTuneAlgo", "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel",
                    "arGroupStart", "arGroupEnd", "arGroupAggregate", "arGetGroupPlan",
-                   "arCommGetAsyncError", "arCommAbort", "arCommCount", "arDestroy", "arSetDebug"):
+                   "arCommGetAsyncError", "arCommAbort", "arCommCount", "arDestroy", "arSetDebug",
+                   "arAllReduceNoAlloc"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -198,6 +200,19 @@ def arAllReduce(comm, sendbufs, recvbufs, count=None, dtype=None, op=arSum, stre
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     sp, rp = _checked_ptrs(comm, sendbufs, recvbufs, dtype, count, count)
     _check(lib().arAllReduce(comm, sp, rp, int(count), int(dtype), int(op), ctypes.c_void_p(handle)), "arAllReduce")
+
+
+def arAllReduceNoAlloc(sendbufs, recvbufs, nChannels, count=None, dtype=None, op=arSum, stream=None):
+    """The comm-less, allocation-free AllReduce (ring, Simple, nranks =
+    len(sendbufs) <= 16); same buffers and arguments as arAllReduce."""
+    if count is None:
+        count = sendbufs[0].numel()
+    if dtype is None:
+        dtype = _dtype_of(sendbufs[0])
+    n = len(sendbufs)
+    _check_bufs(n, sendbufs, recvbufs, dtype, count, count)
+    _check(lib().arAllReduceNoAlloc(_ptrs(sendbufs), _ptrs(recvbufs), n, int(nChannels), int(count), int(dtype),
+                                    int(op), ctypes.c_void_p(_stream_handle(stream))), "arAllReduceNoAlloc")
 
 
 def _stream_handle(stream):

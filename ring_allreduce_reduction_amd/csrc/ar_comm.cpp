@@ -883,21 +883,22 @@ void buildArgs(const arComm* c, const Plan& plan, int func, size_t count, const 
   a->groupSpread = c->groupSpread;
 }
 
-// One collective call: argument checks (nothing is enqueued on failure), the
-// empty and one-rank short cuts, planning, kernel arguments, one launch.
-// `count` is per rank for AllReduce and per rank block for the other two.
-arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const* recvbufs, size_t count,
-                   arDataType_t dtype, arRedOp_t op, void* stream) {
-  if (!commOk(c)) return arInvalidArgument;
-  if (c->aborted) return arInvalidUsage;
-  if (memberGaveUp(c)) return arRemoteError;
+}  // namespace
+
+// Argument checks of one collective call [ch.6 §二, ArgsCheck]: element type
+// and op, buffer pointers (set, element-aligned), and no output overlapping
+// another rank's buffers or its own input except exactly in place.  `count`
+// is per rank for AllReduce and per rank block for the other two; count == 0
+// passes with nothing checked (the empty call does no work).  Also reports
+// whether every buffer (and rank block) is 16- and 128-byte aligned.
+arResult_t ar::checkCollArgs(int N, int func, const void* const* sendbufs, void* const* recvbufs, size_t count,
+                             int dtype, int op, bool* aligned16Out, bool* aligned128Out) {
   const int esz = elemSize(dtype);
   if (esz == 0) return arInvalidArgument;
   if (op != arSum && op != arMax && op != arMin && op != arProbe) return arInvalidArgument;
   if ((op == arProbe) != (dtype == arUint64) && func != kCollAllGather) return arInvalidArgument;
   if (count == 0) return arSuccess;   // empty collective: no work [ch.6 §三]
   if (sendbufs == nullptr || recvbufs == nullptr) return arInvalidArgument;
-  const int N = c->nranks;
   if (count > (uint64_t)1 << 40) return arInvalidArgument;
   const size_t block = count * (size_t)esz;
   const size_t sendBytes = func == kCollReduceScatter ? block * (size_t)N : block;
@@ -931,6 +932,27 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
       if (di < sj + sendBytes && sj < di + recvBytes) return arInvalidArgument;
     }
   }
+  *aligned16Out = aligned16;
+  *aligned128Out = aligned128;
+  return arSuccess;
+}
+
+namespace {
+
+// One collective call: argument checks (nothing is enqueued on failure), the
+// empty and one-rank short cuts, planning, kernel arguments, one launch.
+// `count` is per rank for AllReduce and per rank block for the other two.
+arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const* recvbufs, size_t count,
+                   arDataType_t dtype, arRedOp_t op, void* stream) {
+  if (!commOk(c)) return arInvalidArgument;
+  if (c->aborted) return arInvalidUsage;
+  if (memberGaveUp(c)) return arRemoteError;
+  const int N = c->nranks;
+  bool aligned16 = true, aligned128 = true;
+  const arResult_t chk = checkCollArgs(N, func, sendbufs, recvbufs, count, dtype, op, &aligned16, &aligned128);
+  if (chk != arSuccess) return chk;
+  if (count == 0) return arSuccess;   // empty collective: no work [ch.6 §三]
+  const size_t block = count * (size_t)elemSize(dtype);
   hipStream_t st = (hipStream_t)stream;
   if (tGroupDepth > 0) {   // queued until the outermost arGroupEnd [ch.7 §一]
     if (!c->pending.empty() && c->pending[0].stream != st) return arInvalidUsage;
@@ -988,6 +1010,112 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   return arSuccess;
 }
 
+
+// Compute units and wall-clock rate of a device, read once per device.
+void deviceInfo(int dev, int* cus, int* clkKHz) {
+  static std::mutex mu;
+  static int known[64][2];
+  static bool have[64];
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < 64 && have[dev]) {
+    *cus = known[dev][0];
+    *clkKHz = known[dev][1];
+    return;
+  }
+  int c = 0, k = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 0;
+  if (hipDeviceGetAttribute(&k, hipDeviceAttributeWallClockRate, dev) != hipSuccess || k <= 0) k = 100000;
+  if (dev >= 0 && dev < 64 && c > 0) {
+    known[dev][0] = c;
+    known[dev][1] = k;
+    have[dev] = true;
+  }
+  *cus = c;
+  *clkKHz = k;
+}
+
+}  // namespace
+
+arResult_t ar::allReduceInScratch(char* scratch, size_t scratchBytes, const void* const* sendbufs,
+                                  void* const* recvbufs, int nranks, int nChannels, size_t count, int dtype, int op,
+                                  hipStream_t stream) {
+  if (nranks < 1 || nranks > kMaxMembersPerGroup) return arInvalidArgument;   // one workgroup per ring
+  if (nChannels < 1 || nChannels > AR_MAX_CHANNELS) return arInvalidArgument;
+  bool aligned16 = true, aligned128 = true;
+  const arResult_t chk =
+      checkCollArgs(nranks, kCollAllReduce, sendbufs, recvbufs, count, dtype, op, &aligned16, &aligned128);
+  if (chk != arSuccess || count == 0) return chk;
+  if (nranks == 1) {   // the result is the input [ch.6 §三, one-rank path]
+    if (recvbufs[0] == sendbufs[0]) return arSuccess;
+    return hipMemcpyAsync(recvbufs[0], sendbufs[0], count * (size_t)elemSize(dtype), hipMemcpyDeviceToDevice,
+                          stream) == hipSuccess
+               ? arSuccess
+               : arHipError;
+  }
+  const Env& e = env();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return arHipError;
+  // A comm description on the stack, for the planner: the same defaults as
+  // arInit with a Simple ring of nChannels, and as many lanes as the scratch
+  // FIFOs hold at the largest slot (the lane count never changes a result).
+  arComm c = arComm();   // value-initialised: every field not set below is zero
+  c.startMagic = c.endMagic = kCommMagic;
+  c.nranks = nranks;
+  c.maxChannels = c.nChannels = nChannels;
+  c.proto = arProtoSimple;
+  c.algo = arAlgoRing;
+  c.device = dev;
+  deviceInfo(dev, &c.numCUs, &c.wallClockKHz);
+  if (c.numCUs <= 0) return arHipError;
+  for (int p = 0; p < 3; ++p) c.nSlots[p] = e.nSteps > 0 ? e.nSteps : kDefaultSlots[p];
+  c.sliceBytes = e.sliceBytes;
+  c.timeoutUs = e.timeoutUs;
+  c.deadRank = -1;
+  c.simpleUnroll = kSimpleUnrollDefault;
+  c.ll128Unroll = 0;
+  c.direct = true;
+  for (int p = 0; p < 3; ++p) c.models[p] = kDefaultModels[p];
+  for (int p = 0; p < 3; ++p) c.treeModels[p] = kDefaultTreeModels[p];
+  const size_t workerBytesMax = (size_t)c.nSlots[kSimple] * (size_t)kSimpleSlotBytesMax + sizeof(Conn);
+  if (scratchBytes <= kScratchHeaderBytes) return arInvalidUsage;
+  const size_t workersFit = (scratchBytes - kScratchHeaderBytes) / workerBytesMax;
+  const size_t lanesFit = workersFit / (size_t)nranks;
+  if (lanesFit < (size_t)nChannels) return arInvalidUsage;   // not even one lane per channel fits
+  const int lanesDefault = kMaxWorkers / nranks > nChannels ? kMaxWorkers / nranks : nChannels;
+  c.lanesMax = (size_t)lanesDefault < lanesFit ? lanesDefault : (int)lanesFit;
+
+  Plan plan;
+  const arResult_t r = makePlan(&c, kCollAllReduce, count, dtype, op, aligned128, &plan);
+  if (r != arSuccess) return r;
+  // the environment can force another protocol or algorithm (AR_PROTO, AR_ALGO)
+  if (plan.proto != kSimple || plan.algo != arAlgoRing || plan.nGroups != 1) return arInvalidUsage;
+  if (!fifosCover(&c, plan)) return arInternalError;
+  // layout: header (control block, failed word), FIFOs, counters
+  const size_t workers = (size_t)nranks * (size_t)c.lanesMax;
+  c.fifoWorkerBytes[kSimple] = (size_t)plan.nSlots * (size_t)plan.slotBytes;
+  c.ctrlDev = (Control*)scratch;
+  c.failedDev = (uint32_t*)(scratch + 256);
+  c.fifo[kSimple] = scratch + kScratchHeaderBytes;
+  c.conn[kSimple] = (Conn*)(scratch + kScratchHeaderBytes + workers * c.fifoWorkerBytes[kSimple]);
+  if (kScratchHeaderBytes + workers * (c.fifoWorkerBytes[kSimple] + sizeof(Conn)) > scratchBytes)
+    return arInternalError;
+
+  KernelArgs a;
+  buildArgs(&c, plan, kCollAllReduce, count, sendbufs, recvbufs, aligned16, &a);
+  a.freshSteps = 1;
+  if (e.debug >= 1)
+    fprintf(stderr, "[ar] INFO no-alloc allreduce n=%d count=%zu dtype=%d op=%d nch=%d lanes=%d grid=%d unroll=%d\n",
+            nranks, count, dtype, op, plan.nChannels, plan.lanes, plan.grid, plan.unroll);
+  const hipError_t he = launchRing(plan, dtype, op, a, stream);
+  c.startMagic = c.endMagic = 0;
+  if (he != hipSuccess) {
+    fprintf(stderr, "[ar] WARN kernel launch failed: %s\n", hipGetErrorString(he));
+    return arHipError;
+  }
+  return arSuccess;
+}
+
+namespace {
 
 // Device room for `words` task-table words (and the pinned staging copies).
 arResult_t ensureTaskTable(arComm* c, size_t words) {

@@ -904,10 +904,12 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   m.aligned = a.aligned16 != 0;
   m.direct = a.direct != 0;
   // counters carry over from earlier calls (tail == head at call boundaries,
-  // unless a member of an earlier call gave up: then nothing runs)
-  const u32 failed = live ? callFailed(a) : 0u;
-  m.recvStep = live ? ldCounter(&m.self->head, true) : 0;
-  m.sendStep = live ? ldCounter(&m.succ->tail, true) : 0;
+  // unless a member of an earlier call gave up: then nothing runs); with
+  // freshSteps every edge is in LDS and starts at step 0 instead
+  const bool carry = live && a.freshSteps == 0;
+  const u32 failed = carry ? callFailed(a) : 0u;
+  m.recvStep = carry ? ldCounter(&m.self->head, true) : 0;
+  m.sendStep = carry ? ldCounter(&m.succ->tail, true) : 0;
   m.succHead = 0;
   m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
   m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
@@ -930,7 +932,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // Publish what only LDS (an edge inside the workgroup) or the LL / LL128
   // flags (which never touch the tail counter per slot) have counted, so the
   // next call starts both ends of every FIFO at the same step.
-  if (m.lane == 0) {
+  if (m.lane == 0 && a.freshSteps == 0) {
     if (!(GROUPED && m.recvAgent)) stRelaxed64(&m.self->head, m.recvStep, true);
     if (PROTO != kSimple || !(GROUPED && m.sendAgent)) stRelaxed64(&m.succ->tail, m.sendStep, true);
   }

@@ -110,6 +110,10 @@ struct KernelArgs {
   int laneSets;               // single call: workgroup FIFO sets (<= nChannels x lanes); set L runs
                               // (channel, lane) pairs L, L + laneSets, ...
   int groupSpread;            // debug: groups of one lane on consecutive workgroup ids (other XCDs)
+  // 1: every member starts at step 0 and publishes nothing when it ends (the
+  // comm-less AllReduce, whose rings keep every edge's counters in LDS): no
+  // state carries from one call to the next, so no counter need persist
+  int freshSteps;
 };
 
 // Everything arAllReduce decides for one call.
@@ -149,6 +153,18 @@ KernelFn pickRingReduceScatter(const Plan& plan, int dtype, int op);
 KernelFn pickRingAllGather(const Plan& plan, int dtype, int op);
 KernelFn pickTreeAllReduce(const Plan& plan, int dtype, int op);        // single call
 KernelFn pickTreeAllReduceBatch(const Plan& plan, int dtype, int op);   // batched launch
+
+// Argument checks of one collective (shared by the comm calls and the
+// comm-less AllReduce); also reports 16- and 128-byte alignment.
+arResult_t checkCollArgs(int N, int func, const void* const* sendbufs, void* const* recvbufs, size_t count,
+                         int dtype, int op, bool* aligned16, bool* aligned128);
+
+// The comm-less AllReduce: ring, Simple, rings of at most 16 ranks, its FIFOs
+// in `scratch` (scratchBytes of device memory on the current device, owned by
+// the caller of this function).  Allocates nothing.
+constexpr size_t kScratchHeaderBytes = 4096;   // control block and failed word
+arResult_t allReduceInScratch(char* scratch, size_t scratchBytes, const void* const* sendbufs, void* const* recvbufs,
+                              int nranks, int nChannels, size_t count, int dtype, int op, hipStream_t stream);
 
 inline int elemSize(int dtype) {
   switch (dtype) {
