@@ -349,6 +349,10 @@ typedef enum {
   arDebugGroupSpread = 8,   /* rings of more than 16 ranks: 1 = place the workgroups of one
                                (channel, lane) on consecutive ids, i.e. on different XCDs under
                                round-robin dispatch (default 0: ids congruent mod 8, one XCD) */
+  arDebugLLChunkBytes = 9,     /* nominal chunk of the LL protocol in bytes, a multiple of 16
+                                  from 16 to 64 MiB (0: the default); changes the summation
+                                  order like the channel count, reported by arGetPlan */
+  arDebugLL128ChunkBytes = 10, /* the same for LL128 */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 

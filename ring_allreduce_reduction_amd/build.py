@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["ar_kernels_ring_simple.hip", "ar_kernels_ring_ll.hip", "ar_kernels_ring_batch.hip",
+SOURCES = ["ar_kernels_ring_simple.hip", "ar_kernels_ring_ll.hip", "ar_kernels_ring_ll128.hip", "ar_kernels_ring_batch.hip",
            "ar_kernels_ring_rs.hip", "ar_kernels_ring_ag.hip", "ar_kernels_tree.hip", "ar_kernels_tree_batch.hip",
            "ar_kernels.hip", "ar_noalloc.hip",
            "ar_comm.cpp", "ar_tune.cpp", "ar_group.cpp"]

@@ -161,6 +161,8 @@ struct arComm {
   int wallClockKHz;
   int nSlots[3];        // FIFO depth per protocol
   size_t sliceBytes;
+  size_t llChunkBytes;     // nominal LL / LL128 chunks (0: the defaults)
+  size_t ll128ChunkBytes;
   int lanesMax;         // lanes (channel x lane) per rank provisioned
   char* fifo[3];
   Conn* conn[3];
@@ -214,7 +216,8 @@ int slotPayloadOf(int proto, int unroll) {
 
 size_t chunkBytesOf(const arComm* c, int proto) {
   if (proto == kSimple) return 2 * c->sliceBytes;   // one chunk = 2 slices
-  return proto == kLL ? kLLChunkBytes : kLL128ChunkBytes;
+  if (proto == kLL) return c->llChunkBytes > 0 ? c->llChunkBytes : kLLChunkBytes;
+  return c->ll128ChunkBytes > 0 ? c->ll128ChunkBytes : kLL128ChunkBytes;
 }
 
 uint64_t divUpU(uint64_t x, uint64_t y) { return (x + y - 1) / y; }
@@ -748,6 +751,11 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   if (knob == arDebugLaneSets) {
     if (value < 0 || value > c->lanesMax) return arInvalidArgument;
     c->laneSetsMax = (int)value;
+    return arSuccess;
+  }
+  if (knob == arDebugLLChunkBytes || knob == arDebugLL128ChunkBytes) {
+    if (value < 0 || value > ((int64_t)64 << 20) || value % 16 != 0) return arInvalidArgument;
+    (knob == arDebugLLChunkBytes ? c->llChunkBytes : c->ll128ChunkBytes) = (size_t)value;
     return arSuccess;
   }
   if (knob == arDebugDirect) {

@@ -391,6 +391,113 @@ __device__ __forceinline__ bool waitLdsGeq(const KernelArgs& a, int i, u64 targe
   }
 }
 
+// LL receive: every live 16-byte line {d0, flag, d1, flag} of this lane's U
+// pieces is polled until both of its 8-byte words carry `flag`.  Each poll
+// issues every piece's loads back to back and only then compares them (with
+// selects, no branch per piece): a branch per piece made the compiler wait
+// for one piece's loads before issuing the next piece's, one L2 round trip
+// per piece per poll.  Each word is one 64-bit atomic load, so its data and
+// flag are seen together; a line already seen is read again harmlessly (its
+// slot is not reused before this step releases it).
+template <int U>
+__device__ __forceinline__ bool pollLL(const KernelArgs& a, const char* slot, const int (&wireOff)[U],
+                                       const int (&payOff)[U], long valid, u32 flag, bool agent, v4u (&in)[U]) {
+  bool done[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) { done[u] = payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
+  Waiter w;
+  while (true) {
+    u64 w0[U], w1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // a piece already seen is not read again
+      const u64* line = (const u64*)(slot + wireOff[u]);
+      w0[u] = done[u] ? 0 : ldRelaxed64(line, agent);
+      w1[u] = done[u] ? 0 : ldRelaxed64(line + 1, agent);
+    }
+    bool all = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool now = !done[u] && (u32)(w0[u] >> 32) == flag && (u32)(w1[u] >> 32) == flag;
+      in[u].x = now ? (u32)w0[u] : in[u].x;
+      in[u].y = now ? (u32)w1[u] : in[u].y;
+      done[u] = done[u] || now;
+      all = all && done[u];
+    }
+    if (__all(all)) return true;
+    if (!keepWaiting(a, w)) return false;
+  }
+}
+
+// LL128 receive, first half: the flag lane of every 128-byte line (lane 7
+// of each group of 8) polls the 8-byte flag of each live line of its U
+// pieces, all U loads in flight at once, until every one carries `flag`.
+template <int U>
+__device__ __forceinline__ bool pollLL128Flags(const KernelArgs& a, const char* slot, const int (&wireOff)[U], int lane,
+                                               long valid, u64 flag, bool agent) {
+  const bool flagLane = (lane & 7) == 7;
+  bool done[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
+  Waiter w;
+  while (true) {
+    bool all = true;
+    if (flagLane) {
+      u64 f[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)   // a flag already seen is not read again
+        f[u] = done[u] ? flag : ldRelaxed64((const u64*)(slot + wireOff[u] + 8), agent);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        done[u] = done[u] || f[u] == flag;
+        all = all && done[u];
+      }
+    }
+    if (__all(all)) return true;
+    if (!keepWaiting(a, w)) return false;
+  }
+}
+
+// LL128 receive on an edge inside the workgroup, in one round trip: every
+// lane loads its line's 8-byte flag with a workgroup-scope acquire and then
+// its payload piece, with no wait in between, and keeps the payload only if
+// every live line's flag matched (otherwise it polls again).  Each lane's
+// acquire orders its own payload load after its flag load: if the flag is
+// the sender's (published after its payload stores by a workgroup-scope
+// release), the payload is that step's.  gfx950 implements a workgroup-scope
+// acquire load as the plain load itself (the wavefronts of a workgroup share
+// the CU's in-order vector memory path), so the payload loads issue right
+// behind the flag loads and one L2 round trip serves both.  Across
+// workgroups the payload is read only after the flags returned
+// (pollLL128Flags), as device-coherent loads carry no such order.
+template <int U>
+__device__ __forceinline__ bool pollLL128Lines(const KernelArgs& a, const char* slot, const int (&wireOff)[U], int lane,
+                                               long valid, u64 flag, v4u (&in)[U]) {
+  const int lineOff = (lane >> 3) * kLL128LineBytes + kLL128LinePayload;   // this lane's line's flag word
+  Waiter w;
+  while (true) {
+    u64 f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      f[u] = __hip_atomic_load((const u64*)(slot + u * kLL128UnitBytes + lineOff), __ATOMIC_ACQUIRE,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    // every lane loads its whole 16-byte piece (no branch, so nothing waits
+    // between these loads and the flags'); the flag lane's upper half is the
+    // flag itself, which no store of that lane (8 payload bytes) ever writes
+#pragma unroll
+    for (int u = 0; u < U; ++u) in[u] = *(const v4u*)(slot + wireOff[u]);
+    bool all = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) all = all && (u * kLL128UnitPayload >= valid || f[u] == flag);
+    if (__all(all)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u * kLL128UnitPayload >= valid) in[u] = v4u{0u, 0u, 0u, 0u};
+      return true;
+    }
+    if (!keepWaiting(a, w)) return false;
+  }
+}
+
 // Workgroup -> (lane id L, group g).  With several groups per lane, the
 // groups of one lane get workgroup ids congruent mod 8, i.e. the same XCD
 // under round-robin dispatch, so their edges stay in one L2: a locality hint
@@ -473,7 +580,11 @@ __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
 // One FIFO step of kind KIND (kKindAtRunTime: of kind `kindRt`); `valid`
 // payload bytes start at inp / outp (and at
 // succOutp in the successor's output, for a direct all-gather step).
-template <int PROTO, int DT, int OP, int U, bool XWG, int KIND>
+// LINES: every edge of the launch is inside one workgroup, so an LL128
+// receive reads flags and payload in one poll (pollLL128Lines); kernels with
+// edges between workgroups keep the two-phase read, which needs fewer
+// registers (their grids must be co-resident).
+template <int PROTO, int DT, int OP, int U, bool XWG, int KIND, bool LINES = false>
 __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt, const char* inp, char* outp,
                                      char* succOutp, long valid) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -546,48 +657,11 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
                                     : v4u{0u, 0u, 0u, 0u};
       }
     } else if (PROTO == kLL) {
-      const u32 flag = (u32)(m.recvStep + 1);
-      bool done[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) { done[u] = payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
-      Waiter w;
-      while (true) {
-        bool all = true;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (!done[u]) {
-            const u64* line = (const u64*)(slot + wireOff[u]);
-            u64 w0 = ldRelaxed64(line, (XWG && m.recvAgent));
-            u64 w1 = ldRelaxed64(line + 1, (XWG && m.recvAgent));
-            if ((u32)(w0 >> 32) == flag && (u32)(w1 >> 32) == flag) {
-              in[u].x = (u32)w0; in[u].y = (u32)w1; done[u] = true;
-            } else {
-              all = false;
-            }
-          }
-        }
-        if (__all(all)) break;
-        if (!keepWaiting(a, w)) return false;
-      }
+      if (!pollLL<U>(a, slot, wireOff, payOff, valid, (u32)(m.recvStep + 1), XWG && m.recvAgent, in)) return false;
+    } else if (LINES) {   // LL128, every edge inside the workgroup: flags and payload in one poll
+      if (!pollLL128Lines<U>(a, slot, wireOff, lane, valid, m.recvStep + 1, in)) return false;
     } else {  // LL128: poll the flag of every live line, then read payload
-      const u64 flag = m.recvStep + 1;
-      const bool flagLane = (lane & 7) == 7;
-      bool done[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
-      Waiter w;
-      while (true) {
-        bool all = true;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (!done[u]) {
-            if (ldRelaxed64((const u64*)(slot + wireOff[u] + 8), (XWG && m.recvAgent)) == flag) done[u] = true;
-            else all = false;
-          }
-        }
-        if (__all(all)) break;
-        if (!keepWaiting(a, w)) return false;
-      }
+      if (!pollLL128Flags<U>(a, slot, wireOff, lane, valid, m.recvStep + 1, XWG && m.recvAgent)) return false;
       acquireEdge();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -674,7 +748,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
 
 // One collective of the ring schedule over one member's (channel, lane)
 // share of `count` elements per rank; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL, bool XWG, bool SPEC>
+template <int PROTO, int DT, int OP, int U, int COLL, bool XWG, bool SPEC, bool LINES>
 __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, int ch, int k, u64 count,
                                          const char* in, char* out, char* succOut) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -736,8 +810,8 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
             const u64 b = j * (u64)PAYLOAD;
             if (b >= bytes) break;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG, KIND>(a, m, kindRt, in + first + b, out + first + b,
-                                                   succOut + first + b, valid))
+            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES>(a, m, kindRt, in + first + b, out + first + b,
+                                                          succOut + first + b, valid))
               return false;
           }
           return true;
@@ -791,8 +865,8 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
           for (u64 j = jb; j < je; ++j) {
             const u64 b = j * (u64)PAYLOAD;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG, KIND>(a, m, kindRt, in + inOff + b, out + outOff + b,
-                                                   succOut + outOff + b, valid))
+            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES>(a, m, kindRt, in + inOff + b, out + outOff + b,
+                                                          succOut + outOff + b, valid))
               return false;
           }
           return true;
@@ -822,12 +896,12 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
 
 // Every pass of one member: the (channel, lane) pairs of its FIFO set, or
 // the tasks of a batched launch; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool XWG, bool SPEC>
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool XWG, bool SPEC, bool LINES>
 __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int L, int sets, int lanesTotal,
                                              int perTask, int r, int succ) {
   if (!BATCH) {
     for (int Lp = L; Lp < lanesTotal; Lp += sets) {
-      if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count,
+      if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC, LINES>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count,
                                                  (const char*)a.send[r], (char*)a.recv[r], (char*)a.recv[succ]))
         return false;
     }
@@ -840,7 +914,7 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
   const size_t row = 1 + 2 * (size_t)N;
   for (int t = L / perTask; t < a.nTasks; t += a.taskSlots) {
     const u64* d = a.tasks + (size_t)t * row;
-    if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
+    if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC, LINES>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
                                                (char*)d[1 + N + succ]))
       return false;
   }
@@ -897,6 +971,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // edges between workgroups.
   constexpr bool GROUPED = !ONEWG && (PROTO != kSimple || U <= kGroupedSimpleUnrollMax);
   constexpr bool SPEC = ONEWG && PROTO == kSimple && U <= kGroupedSimpleUnrollMax;
+  constexpr bool LINES = ONEWG && PROTO == kLL128;
   m.recvAgent = GROUPED && pred / a.groupSize != g;
   m.sendAgent = GROUPED && succ / a.groupSize != g;
   m.selfW = wave;
@@ -923,11 +998,16 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // A member with an edge to another workgroup runs the pass compiled with
   // that edge's code; every other member runs one with no trace of it (the
   // runtime checks alone cost short messages a few percent).
-  const bool ok = GROUPED && (m.sendAgent || m.recvAgent)
-                      ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, GROUPED, false>(a, m, L, sets, lanesTotal, perTask,
-                                                                                    r, succ)
-                      : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC>(a, m, L, sets, lanesTotal, perTask, r,
-                                                                                 succ);
+  bool ok;
+  if constexpr (GROUPED) {
+    ok = m.sendAgent || m.recvAgent
+             ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, true, false, false>(a, m, L, sets, lanesTotal, perTask, r,
+                                                                               succ)
+             : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, false, false>(a, m, L, sets, lanesTotal, perTask, r,
+                                                                                succ);
+  } else {
+    ok = memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC, LINES>(a, m, L, sets, lanesTotal, perTask, r, succ);
+  }
   if (!ok) return;
   // Publish what only LDS (an edge inside the workgroup) or the LL / LL128
   // flags (which never touch the tail counter per slot) have counted, so the
@@ -1039,7 +1119,7 @@ struct Pieces {   // this lane's pieces of one slot (as in the ring's step)
   }
 };
 
-template <int PROTO, int U, bool XWG>
+template <int PROTO, int U, bool XWG, bool LINES = false>
 __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, const Pieces<PROTO, U>& pc, int lane,
                                          long valid, v4u (&in)[U]) {
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
@@ -1053,48 +1133,11 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
               : (XWG && e.agent)            ? ldCoh16(slot + pc.wireOff[u])
                                    : *(const v4u*)(slot + pc.wireOff[u]);
   } else if (PROTO == kLL) {
-    const u32 flag = (u32)(e.step + 1);
-    bool done[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) { done[u] = pc.payOff[u] >= valid; in[u] = v4u{0u, 0u, 0u, 0u}; }
-    Waiter w;
-    while (true) {
-      bool all = true;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!done[u]) {
-          const u64* line = (const u64*)(slot + pc.wireOff[u]);
-          const u64 w0 = ldRelaxed64(line, (XWG && e.agent));
-          const u64 w1 = ldRelaxed64(line + 1, (XWG && e.agent));
-          if ((u32)(w0 >> 32) == flag && (u32)(w1 >> 32) == flag) {
-            in[u].x = (u32)w0; in[u].y = (u32)w1; done[u] = true;
-          } else {
-            all = false;
-          }
-        }
-      }
-      if (__all(all)) break;
-      if (!keepWaiting(a, w)) return false;
-    }
+    if (!pollLL<U>(a, slot, pc.wireOff, pc.payOff, valid, (u32)(e.step + 1), XWG && e.agent, in)) return false;
+  } else if (LINES) {   // LL128, every edge inside the workgroup: flags and payload in one poll
+    if (!pollLL128Lines<U>(a, slot, pc.wireOff, lane, valid, e.step + 1, in)) return false;
   } else {
-    const u64 flag = e.step + 1;
-    const bool flagLane = (lane & 7) == 7;
-    bool done[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) done[u] = !flagLane || u * kLL128UnitPayload >= valid;
-    Waiter w;
-    while (true) {
-      bool all = true;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!done[u]) {
-          if (ldRelaxed64((const u64*)(slot + pc.wireOff[u] + 8), (XWG && e.agent)) == flag) done[u] = true;
-          else all = false;
-        }
-      }
-      if (__all(all)) break;
-      if (!keepWaiting(a, w)) return false;
-    }
+    if (!pollLL128Flags<U>(a, slot, pc.wireOff, lane, valid, e.step + 1, XWG && e.agent)) return false;
     acquireEdge();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1188,7 +1231,7 @@ struct TreeNode {
 // has d1 only; every other node with children has d0, and maybe d1.
 // kRoleAtRunTime: read it from the node.
 constexpr int kRoleD0 = 1, kRoleD1 = 2, kRoleParent = 4, kRoleAtRunTime = -1;
-template <int PROTO, int DT, int OP, int U, bool XWG, int ROLE = kRoleAtRunTime>
+template <int PROTO, int DT, int OP, int U, bool XWG, int ROLE = kRoleAtRunTime, bool LINES = false>
 __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int ch, int k, int lane, u64 count,
                                          const char* inBase, char* outBase) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -1232,7 +1275,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
         for (int i = 0; i < 2; ++i) {
           if (!hasChild(i)) continue;
           v4u got[U];
-          if (!edgeRecv<PROTO, U, XWG>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
+          if (!edgeRecv<PROTO, U, XWG, LINES>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
           edgeFinishRecv<XWG>(a, nd.fromChild[i], lane);
 #pragma unroll
           for (int u = 0; u < U; ++u) acc[u] = have ? combine<DT, OP>(acc[u], got[u]) : got[u];
@@ -1257,7 +1300,7 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
     for (u64 j = jb; j < je; ++j) {
       const u64 b = j * (u64)PAYLOAD;
       const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-      if (!edgeRecv<PROTO, U, XWG>(a, nd.fromParent, pc, lane, valid, acc)) return false;
+      if (!edgeRecv<PROTO, U, XWG, LINES>(a, nd.fromParent, pc, lane, valid, acc)) return false;
       edgeFinishRecv<XWG>(a, nd.fromParent, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -1272,16 +1315,17 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
 
 // Every pass of one tree member: its one call, or the tasks of a batched
 // launch; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, bool BATCH, bool XWG, int ROLE = kRoleAtRunTime>
+template <int PROTO, int DT, int OP, int U, bool BATCH, bool XWG, int ROLE = kRoleAtRunTime, bool LINES = false>
 __device__ __forceinline__ bool treePasses(const KernelArgs& a, TreeNode& nd, int L, int perTask, int ch, int k,
                                            int lane, int r) {
-  if (!BATCH) return treePass<PROTO, DT, OP, U, XWG, ROLE>(a, nd, ch, k, lane, a.count, (const char*)a.send[r],
+  if (!BATCH) return treePass<PROTO, DT, OP, U, XWG, ROLE, LINES>(a, nd, ch, k, lane, a.count, (const char*)a.send[r],
                                                            (char*)a.recv[r]);
   const int N = a.nranks;
   const size_t row = 1 + 2 * (size_t)N;
   for (int i = L / perTask; i < a.nTasks; i += a.taskSlots) {
     const u64* d = a.tasks + (size_t)i * row;
-    if (!treePass<PROTO, DT, OP, U, XWG, ROLE>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r], (char*)d[1 + N + r]))
+    if (!treePass<PROTO, DT, OP, U, XWG, ROLE, LINES>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r],
+                                                     (char*)d[1 + N + r]))
       return false;
   }
   return true;
@@ -1346,6 +1390,8 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
       default: ok = AR_ROLE(kRoleAtRunTime); break;   // any other shape reads its peers at run time
 #undef AR_ROLE
     }
+  } else if constexpr (ONEWG) {   // LL / LL128, every edge inside the workgroup
+    ok = treePasses<PROTO, DT, OP, U, BATCH, false, kRoleAtRunTime, PROTO == kLL128>(a, nd, L, perTask, ch, k, lane, r);
   } else {
     // as in the ring kernel: only a member with an edge to another workgroup
     // runs the pass compiled with that edge's code
@@ -1430,13 +1476,33 @@ KernelFn pickRingSimple(const Plan& plan, int dtype, int op) {
   return nullptr;
 }
 
+// LL and LL128; single calls whose rings lie inside one workgroup get the
+// instantiation compiled for them (no code for edges between workgroups; an
+// LL128 receive in one poll).
+template <int COLL, bool BATCH>
+KernelFn pickRingLLOnly(const Plan& plan, int dtype, int op) {
+  if (plan.proto != kLL) return nullptr;
+  if (!BATCH && plan.nGroups == 1) return pickRing<kLL, kLLUnroll, COLL, false, true>(dtype, op);
+  return pickRing<kLL, kLLUnroll, COLL, BATCH>(dtype, op);
+}
+
+template <int COLL, bool BATCH>
+KernelFn pickRingLL128Only(const Plan& plan, int dtype, int op) {
+  if (plan.proto != kLL128) return nullptr;
+  const bool one = !BATCH && plan.nGroups == 1;
+  if (plan.unroll == kLL128Unroll)
+    return one ? pickRing<kLL128, kLL128Unroll, COLL, false, true>(dtype, op)
+               : pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
+  if constexpr (!BATCH)   // large LL128 slots: single calls only
+    if (plan.unroll == kLL128UnrollLarge)
+      return one ? pickRing<kLL128, kLL128UnrollLarge, COLL, false, true>(dtype, op)
+                 : pickRing<kLL128, kLL128UnrollLarge, COLL, false>(dtype, op);
+  return nullptr;
+}
+
 template <int COLL, bool BATCH>
 KernelFn pickRingLL(const Plan& plan, int dtype, int op) {
-  if (plan.proto == kLL) return pickRing<kLL, kLLUnroll, COLL, BATCH>(dtype, op);
-  if (plan.unroll == kLL128Unroll) return pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
-  if constexpr (!BATCH)   // large LL128 slots: single calls only
-    if (plan.unroll == kLL128UnrollLarge) return pickRing<kLL128, kLL128UnrollLarge, COLL, false>(dtype, op);
-  return nullptr;
+  return plan.proto == kLL ? pickRingLLOnly<COLL, BATCH>(plan, dtype, op) : pickRingLL128Only<COLL, BATCH>(plan, dtype, op);
 }
 
 template <int COLL, bool BATCH>
@@ -1446,9 +1512,15 @@ KernelFn pickRingProto(const Plan& plan, int dtype, int op) {
 
 template <bool BATCH>
 KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
+  // single calls whose trees lie inside one workgroup get the instantiation
+  // compiled for them (batched LL / LL128 launches keep the general one)
+  const bool oneLL = !BATCH && plan.nGroups == 1;
   switch (plan.proto) {
-    case kLL: return pickTree<kLL, kLLUnroll, BATCH>(dtype, op);
-    case kLL128: return plan.unroll == kLL128Unroll ? pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op) : nullptr;
+    case kLL: return oneLL ? pickTree<kLL, kLLUnroll, false, true>(dtype, op) : pickTree<kLL, kLLUnroll, BATCH>(dtype, op);
+    case kLL128:
+      if (plan.unroll != kLL128Unroll) return nullptr;
+      return oneLL ? pickTree<kLL128, kLL128Unroll, false, true>(dtype, op)
+                   : pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op);
     case kSimple: {
       // trees inside one workgroup get the instantiation compiled for them
       const bool one = plan.nGroups == 1;

@@ -43,6 +43,7 @@ constexpr int kSimpleSlotBytesMax = kSimpleUnrollMax * kWave * 16;   // 8192
 constexpr int kLLSlotBytes = kLLUnroll * kWave * 16;           // 2048 wire
 constexpr int kLLSlotPayload = kLLUnroll * kWave * 8;          // 1024 payload
 constexpr int kLL128LinePayload = 120;
+constexpr int kLL128LineBytes = 128;                           // 120 payload + the 8-byte flag
 constexpr int kLL128UnitBytes = kWave * 16;                    // 1024 = 8 lines
 constexpr int kLL128UnitPayload = 8 * kLL128LinePayload;       // 960
 constexpr int kLL128SlotBytesMax = kLL128UnrollLarge * kLL128UnitBytes;
@@ -148,6 +149,7 @@ hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bo
 typedef void (*KernelFn)(const KernelArgs);
 KernelFn pickRingAllReduceSimple(const Plan& plan, int dtype, int op);   // single call, Simple
 KernelFn pickRingAllReduceLL(const Plan& plan, int dtype, int op);       // single call, LL / LL128
+KernelFn pickRingAllReduceLL128(const Plan& plan, int dtype, int op);    // single call, LL128
 KernelFn pickRingAllReduceBatch(const Plan& plan, int dtype, int op);    // batched launch
 KernelFn pickRingReduceScatter(const Plan& plan, int dtype, int op);
 KernelFn pickRingAllGather(const Plan& plan, int dtype, int op);

@@ -133,6 +133,8 @@ def test_debug_knob_validation(B):
                           (B.arDebugSimpleSlotKiB, 3), (B.arDebugDirect, 2), (B.arDebugSlots, 1),
                           (B.arDebugSlots, 9), (B.arDebugLaneSets, -1), (B.arDebugLaneSets, 1 << 20),
                           (B.arDebugLL128SlotKiB, 1), (B.arDebugLL128SlotKiB, 8), (B.arDebugGroupSpread, 2),
+                          (B.arDebugLLChunkBytes, 8), (B.arDebugLL128ChunkBytes, -16),
+                          (B.arDebugLL128ChunkBytes, (64 << 20) + 16),
                           (99, 1)]:
             with pytest.raises(B.ArError):
                 B.arSetDebug(comm.handle, knob, bad)
