@@ -598,6 +598,11 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     plan->laneSets = c->laneSetsMax;
     plan->grid = plan->laneSets;
   }
+  // Single-workgroup LL128 rings compile each step for its kind only when the
+  // grid is one workgroup per CU at most: there the steps' chain is the
+  // time; the per-kind kernel's extra registers cost a grid of several
+  // resident rounds more than they save.
+  plan->perKind = proto == kLL128 && nGroups == 1 && !batch && plan->grid <= c->numCUs;
   return arSuccess;
 }
 

@@ -475,6 +475,8 @@ __device__ __forceinline__ bool pollLL128Lines(const KernelArgs& a, const char* 
   const int lineOff = (lane >> 3) * kLL128LineBytes + kLL128LinePayload;   // this lane's line's flag word
   Waiter w;
   while (true) {
+    // Every unit is read, live or not: skipping the units past the step's
+    // bytes (a branch around their loads) measured 4-10% slower.
     u64 f[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -933,7 +935,14 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // kind (8 ranks x 4 KiB: 19.5 -> 15.2 us; 16 x 4 KiB: 45.6 -> 34.2 us).  Not
 // for 8 KiB slots, where the per-kind copies spill, nor for rings cut into
 // workgroups, where their extra registers cost residency.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG>
+//
+// PERKIND (with ONEWG): compile each step for its kind.  LL and LL128 get it
+// too (8 ranks x 4 KiB: LL 24.0 -> 18.6 us, LL128 26.9 -> 20.4 us), but the
+// copies raise LL128's registers from 80 to 91 (6 -> 5 wavefronts per SIMD),
+// which costs a grid of several resident rounds (8 x 256 MiB: 2.34 -> 2.47
+// ms), so the host picks it for LL128 only when the grid is one workgroup per
+// CU at most.
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG, bool PERKIND = ONEWG>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
   // The 8 KiB slot kernels read the wavefront index through readfirstlane,
   // so every per-member value (pointers, counters, rank, channel) lives in
@@ -970,7 +979,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // never plans it for a ring cut into groups), so it carries no code for
   // edges between workgroups.
   constexpr bool GROUPED = !ONEWG && (PROTO != kSimple || U <= kGroupedSimpleUnrollMax);
-  constexpr bool SPEC = ONEWG && PROTO == kSimple && U <= kGroupedSimpleUnrollMax;
+  constexpr bool SPEC = ONEWG && PERKIND && (PROTO != kSimple || U <= kGroupedSimpleUnrollMax);
   constexpr bool LINES = ONEWG && PROTO == kLL128;
   m.recvAgent = GROUPED && pred / a.groupSize != g;
   m.sendAgent = GROUPED && succ / a.groupSize != g;
@@ -1416,17 +1425,18 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
 
 // The ring kernel for one collective, element type and op (AllGather has no
 // arithmetic: one kernel per element size).
-template <int PROTO, int U, int COLL, bool BATCH, bool ONEWG = false>
+template <int PROTO, int U, int COLL, bool BATCH, bool ONEWG = false, bool PERKIND = ONEWG>
 KernelFn pickRing(int dtype, int op) {
   if (COLL == kCollAllGather) {
     switch (dtype) {
-      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH, ONEWG>;
-      case arFloat16: case arBfloat16: return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH, ONEWG>;
-      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH, ONEWG>;
+      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH, ONEWG, PERKIND>;
+      case arFloat16: case arBfloat16:
+        return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH, ONEWG, PERKIND>;
+      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH, ONEWG, PERKIND>;
     }
     return nullptr;
   }
-#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH, ONEWG>
+#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH, ONEWG, PERKIND>
   switch (dtype) {
     case arInt32: return op == arSum ? AR_RING(arInt32, arSum) : op == arMax ? AR_RING(arInt32, arMax)
                        : op == arMin ? AR_RING(arInt32, arMin) : nullptr;
@@ -1490,13 +1500,18 @@ template <int COLL, bool BATCH>
 KernelFn pickRingLL128Only(const Plan& plan, int dtype, int op) {
   if (plan.proto != kLL128) return nullptr;
   const bool one = !BATCH && plan.nGroups == 1;
-  if (plan.unroll == kLL128Unroll)
-    return one ? pickRing<kLL128, kLL128Unroll, COLL, false, true>(dtype, op)
-               : pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
-  if constexpr (!BATCH)   // large LL128 slots: single calls only
-    if (plan.unroll == kLL128UnrollLarge)
-      return one ? pickRing<kLL128, kLL128UnrollLarge, COLL, false, true>(dtype, op)
-                 : pickRing<kLL128, kLL128UnrollLarge, COLL, false>(dtype, op);
+  if (plan.unroll == kLL128Unroll) {
+    if (!one) return pickRing<kLL128, kLL128Unroll, COLL, BATCH>(dtype, op);
+    return plan.perKind ? pickRing<kLL128, kLL128Unroll, COLL, false, true, true>(dtype, op)
+                        : pickRing<kLL128, kLL128Unroll, COLL, false, true, false>(dtype, op);
+  }
+  if constexpr (!BATCH) {   // large LL128 slots: single calls only
+    if (plan.unroll == kLL128UnrollLarge) {
+      if (!one) return pickRing<kLL128, kLL128UnrollLarge, COLL, false>(dtype, op);
+      return plan.perKind ? pickRing<kLL128, kLL128UnrollLarge, COLL, false, true, true>(dtype, op)
+                          : pickRing<kLL128, kLL128UnrollLarge, COLL, false, true, false>(dtype, op);
+    }
+  }
   return nullptr;
 }
 

@@ -136,6 +136,7 @@ struct Plan {
   int laneSets = 0;           // single-group single call: FIFO sets the grid runs (see KernelArgs)
   bool direct = false;
   bool cooperative = false;
+  bool perKind = false;       // single-workgroup LL128 rings: steps compiled per kind (small grids)
   float predictedUs = 0.0f;
 };
 
