@@ -68,6 +68,9 @@ def parse():
                     help="time every algorithm x protocol at 24-72 ranks (rings of several workgroups)")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure latency vs ranks and bandwidth vs channels per protocol and fit arTune's model")
+    ap.add_argument("--calib-grid", default="",
+                    help="'N1,N2,..:log2size1,log2size2,..': time every algorithm x protocol at each rank count and "
+                         "per-rank size (fp32 Sum, channels by the 32 KiB rule); one JSON line each")
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarize rocprofv3 CSV output directories into markdown + profiles/traffic.json")
     ap.add_argument("--profile-label", default="", help="workload key for --summarize-profiles")
@@ -108,6 +111,8 @@ def main():
         return calibrate(args, B, torch, np)
     if args.large_n_table:
         return large_n_table(args, B, torch, np)
+    if args.calib_grid:
+        return calib_grid(args, B, torch, np)
     if args.batch:
         return bench_batch(args, B, gen, torch, np)
 
@@ -583,16 +588,30 @@ def bench_batch(args, B, gen, torch, np):
 
 
 def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):
+    """Mean ms per AllReduce over `steps` calls on one stream (HIP events).
+    The pointer arrays are built and checked once and the loop calls the C
+    ABI directly: per-call marshalling in Python (tens of microseconds at 24
+    ranks, a hundred at 72) would otherwise starve the GPU on short calls and
+    time the host instead."""
+    import ctypes
+    L = B.lib()
+    sp, rp = B._checked_ptrs(comm.handle, sends, recvs, dt_code, count, count)
     stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=dt_code)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(steps):
-            comm.allreduce(sends, recvs, B.arSum, stream=stream, count=count, dtype=dt_code)
-        b.record(stream)
-        torch.cuda.synchronize()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call():
+        rc = L.arAllReduce(comm.handle, sp, rp, count, dt_code, B.arSum, sh)
+        if rc != B.arSuccess:
+            raise B.ArError(rc, "arAllReduce")
+    for _ in range(warmup):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
     err = comm.async_error()
     if err != B.arSuccess:
         raise SystemExit("run failed: " + B.arGetErrorString(err))
@@ -800,6 +819,64 @@ def large_n_table(args, B, torch, np):
                         row["skipped"] = str(e)
                     comm.close()
                     print(json.dumps(row), flush=True)
+
+
+def calib_grid(args, B, torch, np):
+    """The calibration record: every algorithm x protocol at every rank count
+    and per-rank size of the grid, fp32 Sum, on device-drawn inputs, at the
+    channel count the 32 KiB-per-channel rule gives the size (where the model
+    lands in every regime: one channel below 64 KiB, the most allowed above).
+    The six candidates of a size are timed round-robin, five rounds, each a
+    run of back-to-back calls; the median round is reported, so a phase of
+    the GPU (its clock moves under these loads) weighs on every candidate
+    alike.  Sizes whose N buffers of send and receive would pass 24 GiB are
+    skipped.  One JSON line per (N, size, algorithm, protocol) with the median
+    and the spread of the rounds and the plan that ran."""
+    rank_s, size_s = args.calib_grid.split(":")
+    ranks = [int(x) for x in rank_s.split(",")]
+    sizes = [1 << int(x) for x in size_s.split(",")]
+    rounds = 5
+    for n in ranks:
+        fit = [S for S in sizes if 2 * n * S <= (24 << 30)]
+        maxc = max(fit) // 4
+        sends = [torch.rand(maxc, device="cuda") * 2 - 1 for _ in range(n)]
+        recvs = [torch.empty_like(x) for x in sends]
+        comm = B.Comm(n, 64, "simple", "ring")
+        for S in fit:
+            count = max(1, S // 4)
+            nch = _channels_for(S)
+            steps = 50 if S < (4 << 20) else 10 if S < (64 << 20) else 3
+            rows, times = [], []
+            for algo, proto in SWEEP_CANDIDATES:
+                row = {"nranks": n, "bytes": S, "nch": nch, "algo": algo, "proto": proto}
+                try:
+                    comm.set_algo(algo)
+                    comm.set_config(proto, nch)
+                    plan = comm.plan(count, "float32")
+                    row.update({"nchRun": plan["nChannels"], "lanes": plan["lanesPerChannel"],
+                                "groupSize": plan["ranksPerGroup"], "grid": plan["workgroups"],
+                                "slot": plan["stepBytes"]})
+                except B.ArError as e:
+                    row["skipped"] = str(e)
+                rows.append(row)
+                times.append([])
+            for _ in range(rounds):
+                for i, (algo, proto) in enumerate(SWEEP_CANDIDATES):
+                    if "skipped" in rows[i]:
+                        continue
+                    comm.set_algo(algo)
+                    comm.set_config(proto, nch)
+                    times[i].append(time_calls(B, torch, comm, sends, recvs, count, B.arFloat32, 2, steps) * 1e3)
+            for row, ts in zip(rows, times):
+                if ts:
+                    ts.sort()
+                    row["us"] = round(ts[len(ts) // 2], 3)
+                    row["us_min"] = round(ts[0], 3)
+                    row["us_max"] = round(ts[-1], 3)
+                print(json.dumps(row), flush=True)
+        comm.close()
+        del sends, recvs
+        torch.cuda.empty_cache()
 
 
 SWEEP_CANDIDATES = [("ring", "ll"), ("ring", "ll128"), ("ring", "simple"),

@@ -126,6 +126,13 @@ arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, ar
  * until the work completes.  Element pointers need only element alignment;
  * forcing LL128 needs 128-byte aligned buffers, otherwise arInvalidUsage
  * [B ch.2 §2.4, LL128 alignment]; arProtoAuto never picks LL128 then.
+ * Residency: a ring or tree of more than 16 ranks is cut into workgroups
+ * that wait on one another, so all workgroups of its launch must be resident
+ * at once.  The planner sizes that grid to what the GPU holds; a kernel
+ * running beside it on another stream only delays the rest of the grid.  Two
+ * such launches (of different comms, on streams not ordered with each other)
+ * running at the same time could each hold part of the GPU: order them, or
+ * set arDebugCooperative to 1, which makes the runtime run them one at a time.
  * A ring member that waits longer than the timeout (or an abort) makes the
  * kernel exit early and is reported by arCommGetAsyncError as arRemoteError;
  * the comm then only accepts arDestroy: a later call returns arRemoteError
@@ -353,6 +360,10 @@ typedef enum {
                                   from 16 to 64 MiB (0: the default); changes the summation
                                   order like the channel count, reported by arGetPlan */
   arDebugLL128ChunkBytes = 10, /* the same for LL128 */
+  arDebugCooperative = 11,     /* rings / trees of more than 16 ranks: 1 = cooperative launch (the
+                                  runtime checks residency and runs such launches one at a time,
+                                  at 15-70 us per launch), 0 = plain launch of the same grid
+                                  (default; see arAllReduce on residency) */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 

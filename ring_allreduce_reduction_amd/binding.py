@@ -22,7 +22,7 @@ arInt32, arFloat32, arFloat16, arBfloat16, arUint64 = 0, 1, 2, 3, 4
 arSum, arMax, arMin, arProbe = 0, 1, 2, 3
 (arDebugTimeoutUs, arDebugDeadRank, arDebugLanes, arDebugSimpleSlotKiB, arDebugDirect, arDebugSlots,
  arDebugLaneSets, arDebugLL128SlotKiB, arDebugGroupSpread, arDebugLLChunkBytes,
- arDebugLL128ChunkBytes) = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
+ arDebugLL128ChunkBytes, arDebugCooperative) = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11
 AR_MAX_RANKS, AR_MAX_CHANNELS = 128, 64
 arFuncAllReduce, arFuncReduceScatter, arFuncAllGather = 0, 1, 2
 FUNC_BY_NAME = {"allreduce": arFuncAllReduce, "reducescatter": arFuncReduceScatter,

@@ -180,6 +180,7 @@ struct arComm {
   int simpleUnroll;     // Simple slot size in KiB (1, 2, 4)
   int ll128Unroll;      // LL128 slot in 1 KiB units (2 or 4); 0: chosen per call
   bool direct;          // Simple all-gather writes outputs directly
+  bool plainLaunch;     // grouped plans launched without the cooperative launch call
   hipStream_t lastStream;
   bool launched;
   bool aborted;
@@ -515,7 +516,8 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   plan->groupSize = groupSize;
   plan->nGroups = nGroups;
   plan->block = groupSize * kWave;
-  plan->cooperative = nGroups > 1;
+  plan->cooperative = nGroups > 1;   // the whole grid must be co-resident
+  plan->launchCoop = plan->cooperative && !c->plainLaunch;
 
   // Lanes per (rank, channel): one resident round of workgroups (the grid is
   // sized to what the chip holds at once, so no tail round), but never a
@@ -659,6 +661,11 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->simpleUnroll = kSimpleUnrollDefault;
   c->ll128Unroll = 0;   // automatic
   c->direct = true;
+  // Grouped plans are launched plainly: the planner sizes their grid to what
+  // the GPU holds at once, and the cooperative launch call cost 15-20 us per
+  // launch, 60-70 us more on some streams (the runtime routes it through a
+  // queue of its own), for the same residency on an otherwise idle GPU.
+  c->plainLaunch = true;
   for (int p = 0; p < 3; ++p) c->models[p] = kDefaultModels[p];
   for (int p = 0; p < 3; ++p) c->treeModels[p] = kDefaultTreeModels[p];
 
@@ -761,6 +768,11 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   if (knob == arDebugLLChunkBytes || knob == arDebugLL128ChunkBytes) {
     if (value < 0 || value > ((int64_t)64 << 20) || value % 16 != 0) return arInvalidArgument;
     (knob == arDebugLLChunkBytes ? c->llChunkBytes : c->ll128ChunkBytes) = (size_t)value;
+    return arSuccess;
+  }
+  if (knob == arDebugCooperative) {
+    if (value != 0 && value != 1) return arInvalidArgument;
+    c->plainLaunch = value == 0;
     return arSuccess;
   }
   if (knob == arDebugDirect) {

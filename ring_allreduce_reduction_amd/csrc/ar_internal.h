@@ -135,7 +135,8 @@ struct Plan {
   int taskSlots = 0;          // batched launches: collectives running at once
   int laneSets = 0;           // single-group single call: FIFO sets the grid runs (see KernelArgs)
   bool direct = false;
-  bool cooperative = false;
+  bool cooperative = false;   // the whole grid must be co-resident (rings / trees cut into workgroups)
+  bool launchCoop = false;    // launched with the cooperative launch call (else a plain launch)
   bool perKind = false;       // single-workgroup LL128 rings: steps compiled per kind (small grids)
   float predictedUs = 0.0f;
 };

@@ -34,7 +34,7 @@ hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& arg
   if (fn == nullptr) return hipErrorInvalidValue;
   if (plan.nGroups > 1 && plan.proto == kSimple && plan.unroll > kGroupedSimpleUnrollMax)
     return hipErrorInvalidValue;   // that kernel has no cross-workgroup edges
-  if (plan.cooperative) {
+  if (plan.launchCoop) {
     void* params[] = {(void*)&args};
     return hipLaunchCooperativeKernel((const void*)fn, dim3(plan.grid), dim3(plan.block), params, 0, stream);
   }

@@ -56,3 +56,16 @@ def test_small_ring_ragged_and_16bit(B, gu):
     gu.parity_case(2, (4 * MiB) // 4 + 12345, "float32", "sum", "simple", 64, seed=5)
     gu.parity_case(3, (4 * MiB) // 2 + 777, "bfloat16", "sum", "simple", 64, seed=6)
     gu.parity_case(4, (8 * MiB) // 2 + 1, "float16", "sum", "simple", 64, seed=7)
+
+
+@pytest.mark.parametrize("n,proto,algo", [(24, "simple", "ring"), (24, "ll128", "ring"), (40, "ll", "tree"),
+                                          (72, "simple", "tree")])
+def test_cooperative_and_plain_launches_agree(B, gu, orc, n, proto, algo):
+    """Rings and trees cut into workgroups run plainly launched by default;
+    the cooperative launch (arDebugCooperative = 1) runs the same grid and
+    gives the same bits, both equal to the oracle on the plan."""
+    with B.Comm(n, 16, proto, algo) as comm:
+        for coop in (1, 0):
+            B.arSetDebug(comm.handle, B.arDebugCooperative, coop)
+            plan, _, _ = gu.parity_case(n, 70001, "float32", "sum", proto, 16, seed=n + coop, comm=comm)
+            assert plan["ranksPerGroup"] < n
