@@ -68,6 +68,12 @@ def parse():
                     help="time every algorithm x protocol at 24-72 ranks (rings of several workgroups)")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure latency vs ranks and bandwidth vs channels per protocol and fit arTune's model")
+    ap.add_argument("--calib-table", nargs="+", metavar="GRID_JSONL",
+                    help="write the tuner's time table (the text format of AR_TUNE_FILE and of the library's "
+                         "compiled table) from --calib-grid records; with --fit-models also fit the cost model")
+    ap.add_argument("--fit-models", action="store_true",
+                    help="with --calib-table: least-squares fit of the pages' cost model per algorithm and protocol "
+                         "on the records of rings and trees inside one workgroup (at most 16 ranks)")
     ap.add_argument("--calib-grid", default="",
                     help="'N1,N2,..:log2size1,log2size2,..': time every algorithm x protocol at each rank count and "
                          "per-rank size (fp32 Sum, channels by the 32 KiB rule); one JSON line each")
@@ -85,6 +91,8 @@ def main():
     args = parse()
     if args.summarize_profiles:
         return summarize_profiles(args)
+    if args.calib_table:
+        return calib_table(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build emulates all ranks on one GPU; --gpus %d (WORLD_SIZE %d) is not "
@@ -821,6 +829,59 @@ def large_n_table(args, B, torch, np):
                     print(json.dumps(row), flush=True)
 
 
+TABLE_COLUMNS = [("ring", "ll"), ("ring", "ll128"), ("ring", "simple"), ("tree", "ll"), ("tree", "ll128"),
+                 ("tree", "simple")]
+
+
+def calib_table(args):
+    """The tuner's time table from --calib-grid records: one line per (ranks,
+    bytes per rank) with the median microseconds of ring LL, LL128, Simple and
+    tree LL, LL128, Simple ("-" where a candidate could not run), the text
+    format AR_TUNE_FILE reads and from which the build compiles the library's
+    own table.  With --fit-models, "model" lines follow: the pages' cost model
+    fitted per algorithm and protocol (least squares in log time) on the
+    records of at most 16 ranks (rings and trees inside one workgroup, the
+    regime that model describes)."""
+    import collections
+    T = collections.defaultdict(dict)
+    for path in args.calib_table:
+        for line in open(path):
+            r = json.loads(line)
+            if "us" in r and r["algo"] != "auto":
+                T[(r["nranks"], r["bytes"])][(r["algo"], r["proto"])] = r["us"]
+    print("# ranks bytes_per_rank  ring_LL ring_LL128 ring_Simple tree_LL tree_LL128 tree_Simple  (us, fp32 Sum,")
+    print("# channels by the 32 KiB-per-channel rule; '-' = that candidate cannot run there)")
+    for (n, S) in sorted(T):
+        d = T[(n, S)]
+        print("%d %d  %s" % (n, S, " ".join(("%.3f" % d[c]) if c in d else "-" for c in TABLE_COLUMNS)))
+    if not args.fit_models:
+        return
+    import numpy as np
+    from scipy.optimize import least_squares
+    for algo in ("ring", "tree"):
+        for proto in ("ll", "ll128", "simple"):
+            pc = {"ll": 0, "ll128": 1, "simple": 2}[proto]
+            pts = [(n, S, d[(algo, proto)]) for (n, S), d in T.items() if n <= 16 and (algo, proto) in d]
+
+            def model(p, n, S):
+                c = _channels_for(S)
+                if algo == "tree":
+                    return _tree_model_us(p, pc, n, c, S)
+                return _ring_model_us(p, {0: 0.5, 1: 0.92, 2: 1.0}[pc], n, c, S)
+
+            def resid(p):
+                return [np.log(model(p, n, S) / t) for n, S, t in pts]
+            sol = None
+            for x0 in ([3.0, 1.0, 100.0, 200.0], [5.0, 2.0, 50.0, 100.0], [2.0, 0.5, 200.0, 300.0],
+                       [10.0, 3.0, 20.0, 60.0]):
+                cand = least_squares(resid, np.array(x0), bounds=([0.0, 0.0, 1e-2, 1e-2], [np.inf] * 4))
+                if sol is None or cand.cost < sol.cost:
+                    sol = cand
+            worst = float(np.max(np.abs(np.expm1(sol.fun))))
+            print("model %s %s %.3f %.4f %.2f %.2f   # %d points, worst %.0f%% off" % (
+                algo, proto, sol.x[0], sol.x[1], sol.x[2], sol.x[3], len(pts), 100 * worst))
+
+
 def calib_grid(args, B, torch, np):
     """The calibration record: every algorithm x protocol at every rank count
     and per-rank size of the grid, fp32 Sum, on device-drawn inputs, at the
@@ -847,25 +908,27 @@ def calib_grid(args, B, torch, np):
             nch = _channels_for(S)
             steps = 50 if S < (4 << 20) else 10 if S < (64 << 20) else 3
             rows, times = [], []
-            for algo, proto in SWEEP_CANDIDATES:
+            cands = SWEEP_CANDIDATES + [("auto", "auto")]
+            for algo, proto in cands:
                 row = {"nranks": n, "bytes": S, "nch": nch, "algo": algo, "proto": proto}
                 try:
                     comm.set_algo(algo)
-                    comm.set_config(proto, nch)
+                    comm.set_config(proto, 64 if algo == "auto" else nch)
                     plan = comm.plan(count, "float32")
                     row.update({"nchRun": plan["nChannels"], "lanes": plan["lanesPerChannel"],
                                 "groupSize": plan["ranksPerGroup"], "grid": plan["workgroups"],
-                                "slot": plan["stepBytes"]})
+                                "slot": plan["stepBytes"], "ranAlgo": B.ALGO_NAMES[plan["algo"]],
+                                "ranProto": B.PROTO_NAMES[plan["proto"]], "predUs": round(plan["predictedUs"], 2)})
                 except B.ArError as e:
                     row["skipped"] = str(e)
                 rows.append(row)
                 times.append([])
             for _ in range(rounds):
-                for i, (algo, proto) in enumerate(SWEEP_CANDIDATES):
+                for i, (algo, proto) in enumerate(cands):
                     if "skipped" in rows[i]:
                         continue
                     comm.set_algo(algo)
-                    comm.set_config(proto, nch)
+                    comm.set_config(proto, 64 if algo == "auto" else nch)
                     times[i].append(time_calls(B, torch, comm, sends, recvs, count, B.arFloat32, 2, steps) * 1e3)
             for row, ts in zip(rows, times):
                 if ts:

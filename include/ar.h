@@ -252,6 +252,27 @@ arResult_t arTuneEvalAlgo(arFunc_t func, int nranks, int maxChannels, size_t nBy
                           unsigned protoMask, arAlgo_t* algo, arProto_t* proto, int* nChannels,
                           float* predictedUs);
 
+/*
+ * arTuneTableTime -- the tuner's measured time of one candidate (pure
+ * function, no device).  The pages let a tuner plugin override the cost of
+ * any (algorithm, protocol) candidate before the argmin [B ch.5 §一, step 3;
+ * T §五, the tuner plugin]; here the override is a table of times measured on
+ * MI355X per (ranks, bytes per rank) for the six candidates at the 32 KiB
+ * channel rule, compiled in from the library's calibration record or read
+ * once per process from the file AR_TUNE_FILE names (lines "ranks bytes
+ * t_ringLL t_ringLL128 t_ringSimple t_treeLL t_treeLL128 t_treeSimple" in us,
+ * "-" where a candidate cannot run; optional lines "model ring|tree
+ * ll|ll128|simple base step bwPerCh cap" replace the cost model's constants;
+ * a malformed file is ignored with a warning).  Between lines the time is
+ * interpolated log-log in bytes, then log-log between the two nearest rank
+ * counts; past a rank count's largest size it grows in proportion to bytes.
+ * arTune, arTuneAlgo and arAllReduce (arProtoAuto or arAlgoAuto) pick the
+ * fastest covered candidate where the comm may use the table's channel count.
+ *  predictedUs (host, out).  arInvalidUsage where the table does not cover
+ *  (nranks, nBytes) for that candidate; arInvalidArgument for bad arguments.
+ */
+arResult_t arTuneTableTime(int nranks, size_t nBytes, arAlgo_t algo, arProto_t proto, float* predictedUs);
+
 /* Read / replace the tuner constants of a comm (calibration): the ring's
  * (arTuneGetModel / arTuneSetModel) or either algorithm's. */
 arResult_t arTuneGetModel(arComm_t comm, arProto_t proto, arTuneModel_t* model);

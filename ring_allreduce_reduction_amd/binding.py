@@ -100,6 +100,7 @@ def lib():
         L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arCommAbort.argtypes = [vp]
         L.arCommCount.argtypes = [vp, ctypes.POINTER(c_int)]
+        L.arTuneTableTime.argtypes = [c_int, c_sz, c_int, c_int, ctypes.POINTER(c_f)]
         L.arAllReduceNoAlloc.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_int, c_int, c_sz, c_int, c_int, vp]
         L.arDestroy.argtypes = [vp]
         L.arSetDebug.argtypes = [vp, c_int, ctypes.c_int64]
@@ -110,7 +111,7 @@ def lib():
                    "arSetAlgo", "arTuneAlgo", "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel",
                    "arGroupStart", "arGroupEnd", "arGroupAggregate", "arGetGroupPlan",
                    "arCommGetAsyncError", "arCommAbort", "arCommCount", "arDestroy", "arSetDebug",
-                   "arAllReduceNoAlloc"):
+                   "arAllReduceNoAlloc", "arTuneTableTime"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -312,6 +313,16 @@ def arTuneEvalAlgo(func, nranks, maxChannels, nBytes, ringModels, treeModels, al
                               ctypes.byref(ch), ctypes.byref(t))
     _check(rc, "arTuneEvalAlgo")
     return a.value, p.value, ch.value, t.value
+
+
+def arTuneTableTime(nranks, nBytes, algo, proto):
+    """The tuner table's time (us) of one candidate, or None where the table does not cover it."""
+    t = ctypes.c_float()
+    rc = lib().arTuneTableTime(int(nranks), int(nBytes), int(algo), int(proto), ctypes.byref(t))
+    if rc == arInvalidUsage:
+        return None
+    _check(rc, "arTuneTableTime")
+    return t.value
 
 
 def arTuneGetAlgoModel(comm, algo, proto):

@@ -8,6 +8,7 @@
 // count == 0 and one-rank short cuts, tuning, channel split, kernel arguments,
 // one launch on the caller's stream.
 #include <ctype.h>
+#include <float.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -17,6 +18,7 @@
 #include <vector>
 
 #include "ar_internal.h"
+#include "ar_tune_table.h"
 
 using namespace ar;
 
@@ -99,38 +101,8 @@ const Env& env() {
   return e;
 }
 
-// Tuner constants for MI355X (us, us, GB/s, GB/s), fitted by the benchmark's
-// calibration mode on one MI355X: the least-squares fit, in log time, of the
-// model to 4 KiB messages at 2, 4, 8 and 16 ranks (1 channel), 128 MiB at 8
-// ranks over 1..64 channels, and 16 KiB..64 MiB at 8 ranks with the channel
-// count the 32 KiB rule allows.  Worst point off by 31% (LL), 23% (LL128),
-// 23% (Simple).  These are the fit from before the single-workgroup rings
-// got steps compiled per kind: refitted on those, the Simple step latency
-// falls to 0.82 us, which rings cut into workgroups (more than 16 ranks) do
-// not reach, and the model (with no term for those) then picks the ring over
-// the tree at 32 ranks x 2 MiB, where the ring is 78% slower.  Kept, the
-// worst choice over the sweeps of 4-32 ranks and the 24-72-rank table is 12%
-// slower than the best.
-const arTuneModel_t kDefaultModels[3] = {
-    /* LL     */ {3.583f, 1.7991f, 51.72f, 121.13f},
-    /* LL128  */ {3.759f, 2.2949f, 77.91f, 171.17f},
-    /* Simple */ {3.453f, 1.1687f, 273.47f, 319.38f},
-};
-
-// Tree constants (same units; stepLatUs is per tree level each way), fitted
-// the same way (`bench.py --calibrate --algo tree`) with the pages' tree
-// model and its size correction: worst point off by 46% (LL, where the
-// correction's mid-size dip does not match this GPU), 20% (LL128), 46%
-// (Simple).
-// These are the fit from before the single-workgroup trees got passes
-// compiled per role: refitted on those (Simple: 3.708, 0.721, 163.85,
-// 164.88), the model picks the tree at 16 ranks x 4 MiB, where it is 2.2x
-// slower than the ring, and at 72 ranks x 4 MiB (+39%).
-const arTuneModel_t kDefaultTreeModels[3] = {
-    /* LL     */ {2.155f, 1.6917f, 205.09f, 51.25f},
-    /* LL128  */ {1.929f, 2.1256f, 74.47f, 64.23f},
-    /* Simple */ {3.783f, 0.8090f, 142.80f, 146.26f},
-};
+// The cost model's constants are the fit in ar_tune_table.txt (or AR_TUNE_FILE's
+// "model" lines), read through ar::tuneTableModels.
 
 constexpr int kStagingBuffers = 4;
 
@@ -292,16 +264,76 @@ void sharedHbmModels(const arComm* c, arTuneModel_t ring[3], arTuneModel_t tree[
   }
 }
 
+// The channel count of the 32 KiB-per-channel rule for nBytes (at most 64):
+// the count the tuner's table was measured at.
+int ruleChannels(uint64_t nBytes) {
+  int c = 1;
+  while (c * 2 <= AR_MAX_CHANNELS && nBytes / (uint64_t)(c * 2) >= 32768) c *= 2;
+  return c;
+}
+
+// Algorithm, protocol and channels for a call of nBytes (per rank for
+// AllReduce).  First the pages' cost model [ch.5 §一]; then, for an
+// AllReduce whose candidates the tuner's table covers at the channel count it
+// was measured at, the table's times override the model's, as the pages let a
+// tuner plugin override the cost table before the argmin (step 3): the
+// candidate with the shortest time wins (ring Simple, LL128, LL, then tree
+// Simple, LL128, LL on ties), at the channel count the model gives it.
+arResult_t tuneCall(const arComm* c, int func, uint64_t nBytes, int maxCh, unsigned algoMask, unsigned protoMask,
+                    arAlgo_t* algoOut, arProto_t* protoOut, int* nchOut, float* predOut) {
+  arTuneModel_t ringM[3], treeM[3];
+  sharedHbmModels(c, ringM, treeM);
+  arAlgo_t al = arAlgoRing;
+  arProto_t pr = arProtoSimple;
+  int ch = 1;
+  float pred = 0.0f;
+  arResult_t r = arTuneEvalAlgo((arFunc_t)func, c->nranks, maxCh, nBytes, ringM, treeM, algoMask, protoMask, &al,
+                                &pr, &ch, &pred);
+  if (r != arSuccess) return r;
+  if (func == kCollAllReduce && c->nranks > 1 && nBytes > 0 && maxCh >= ruleChannels(nBytes)) {
+    static const int order[6][2] = {{arAlgoRing, arProtoSimple}, {arAlgoRing, arProtoLL128}, {arAlgoRing, arProtoLL},
+                                    {arAlgoTree, arProtoSimple}, {arAlgoTree, arProtoLL128}, {arAlgoTree, arProtoLL}};
+    float best = FLT_MAX;
+    int bi = -1;
+    for (int i = 0; i < 6 && tuneTableCovers(c->nranks); ++i) {
+      const int a = order[i][0], p = order[i][1];
+      if (!(algoMask & (1u << a)) || !(protoMask & (1u << p))) continue;
+      float t = 0.0f;
+      if (!tuneTableTime(c->nranks, nBytes, a, p, &t)) continue;   // it cannot run there
+      if (t < best) {
+        best = t;
+        bi = i;
+      }
+    }
+    if (bi >= 0) {
+      al = (arAlgo_t)order[bi][0];
+      pr = (arProto_t)order[bi][1];
+      r = arTuneEvalAlgo((arFunc_t)func, c->nranks, maxCh, nBytes, ringM, treeM, 1u << al, 1u << pr, nullptr, nullptr,
+                         &ch, nullptr);
+      if (r != arSuccess) return r;
+      pred = best;
+    }
+  }
+  if (algoOut) *algoOut = al;
+  if (protoOut) *protoOut = pr;
+  if (nchOut) *nchOut = ch;
+  if (predOut) *predOut = pred;
+  return arSuccess;
+}
+
 // Protocol, channels, chunk, lanes and grid for one call, or for a batched
-// launch (`batch`) of `nTasks` collectives whose largest has `count` elements.
+// launch (`batch`) of `nTasks` collectives whose largest has `count` elements
+// and whose bytes together are `tuneBytes` (0: a single call).
 arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool aligned128, Plan* plan,
-                    bool batch = false, int nTasks = 1) {
+                    bool batch = false, int nTasks = 1, uint64_t tuneBytes = 0) {
   const Env& e = env();
   const int esz = elemSize(dtype);
   // the tuner's message: per rank for AllReduce, the whole nranks x count
-  // traffic for ReduceScatter / AllGather [ch.6 §三]; an aggregate runs its
-  // collectives side by side, so it is tuned on its largest
-  const uint64_t nBytes = count * (uint64_t)esz * (func == kCollAllReduce ? 1u : (uint64_t)c->nranks);
+  // traffic for ReduceScatter / AllGather [ch.6 §三]; an aggregate's
+  // collectives share one launch and run side by side, so it is tuned on
+  // their bytes together [ch.6 §四: aggregate, then select]
+  const uint64_t nBytes = tuneBytes > 0 ? tuneBytes
+                                        : count * (uint64_t)esz * (func == kCollAllReduce ? 1u : (uint64_t)c->nranks);
   int proto = e.forcedProto != -2 ? e.forcedProto : c->proto;
   int nch = e.nChannels > 0 ? e.nChannels : c->nChannels;
   if (nch > c->maxChannels) nch = c->maxChannels;
@@ -311,24 +343,20 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   const unsigned algoMask = algo == arAlgoAuto ? 3u : 1u << algo;
   float predicted = 0.0f;
   arAlgo_t al = algo == arAlgoAuto ? arAlgoRing : (arAlgo_t)algo;
-  arTuneModel_t ringM[3], treeM[3];
-  sharedHbmModels(c, ringM, treeM);
   if (proto == arProtoAuto) {
     unsigned mask = (unsigned)e.protoMask;
     if (!aligned128) mask &= ~(1u << arProtoLL128);
     if (mask == 0) mask = 1u << arProtoSimple;
     arProto_t p;
     int ch;
-    arResult_t r = arTuneEvalAlgo((arFunc_t)func, c->nranks, c->maxChannels, nBytes, ringM, treeM, algoMask, mask,
-                                  &al, &p, &ch, &predicted);
+    arResult_t r = tuneCall(c, func, nBytes, c->maxChannels, algoMask, mask, &al, &p, &ch, &predicted);
     if (r != arSuccess) return r;
     proto = p;
     nch = ch < 1 ? 1 : ch;
   } else {
     if (proto == arProtoLL128 && !aligned128) return arInvalidUsage;   // LL128 needs 128-byte buffers
-    // a fixed protocol and channel count; with arAlgoAuto the model picks the algorithm
-    (void)arTuneEvalAlgo((arFunc_t)func, c->nranks, nch, nBytes, ringM, treeM, algoMask, 1u << proto, &al, nullptr,
-                         nullptr, &predicted);
+    // a fixed protocol and channel count; with arAlgoAuto the tuner picks the algorithm
+    (void)tuneCall(c, func, nBytes, nch, algoMask, 1u << proto, &al, nullptr, nullptr, &predicted);
   }
   const bool tree = al == arAlgoTree;
   const int N = c->nranks;
@@ -666,8 +694,7 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   // launch, 60-70 us more on some streams (the runtime routes it through a
   // queue of its own), for the same residency on an otherwise idle GPU.
   c->plainLaunch = true;
-  for (int p = 0; p < 3; ++p) c->models[p] = kDefaultModels[p];
-  for (int p = 0; p < 3; ++p) c->treeModels[p] = kDefaultTreeModels[p];
+  tuneTableModels(c->models, c->treeModels);
 
   // FIFOs and counters, one set per protocol (a line of one protocol must
   // never be read as another's: LL flags live inside the data).
@@ -813,10 +840,8 @@ arResult_t arTuneAlgo(arComm_t c, size_t nBytes, arAlgo_t* algo, arProto_t* prot
   if (!commOk(c)) return arInvalidArgument;
   const int a = env().forcedAlgo != -2 ? env().forcedAlgo : c->algo;
   const unsigned algoMask = a == arAlgoAuto ? 3u : 1u << a;
-  arTuneModel_t ringM[3], treeM[3];
-  sharedHbmModels(c, ringM, treeM);
-  return arTuneEvalAlgo(arFuncAllReduce, c->nranks, c->maxChannels, nBytes, ringM, treeM, algoMask,
-                        (unsigned)env().protoMask, algo, proto, nChannels, predictedUs);
+  return tuneCall(c, arFuncAllReduce, nBytes, c->maxChannels, algoMask, (unsigned)env().protoMask, algo, proto,
+                  nChannels, predictedUs);
 }
 
 arResult_t arTune(arComm_t c, size_t nBytes, arProto_t* proto, int* nChannels, float* predictedUs) {
@@ -1099,8 +1124,7 @@ arResult_t ar::allReduceInScratch(char* scratch, size_t scratchBytes, const void
   c.simpleUnroll = kSimpleUnrollDefault;
   c.ll128Unroll = 0;
   c.direct = true;
-  for (int p = 0; p < 3; ++p) c.models[p] = kDefaultModels[p];
-  for (int p = 0; p < 3; ++p) c.treeModels[p] = kDefaultTreeModels[p];
+  tuneTableModels(c.models, c.treeModels);
   const size_t workerBytesMax = (size_t)c.nSlots[kSimple] * (size_t)kSimpleSlotBytesMax + sizeof(Conn);
   if (scratchBytes <= kScratchHeaderBytes) return arInvalidUsage;
   const size_t workersFit = (scratchBytes - kScratchHeaderBytes) / workerBytesMax;
@@ -1227,8 +1251,10 @@ arResult_t launchGroup(arComm* c) {
       l.aligned16 = l.aligned16 && t.aligned16;
     }
     const int kop = lead.func == kCollAllGather ? (lead.dtype == arUint64 ? arProbe : arSum) : lead.op;
+    uint64_t aggBytes = 0;   // the aggregate's bytes together (its tasks run side by side)
+    for (int q = l.first; q < pos; ++q) aggBytes += bytes[(size_t)order[(size_t)q]];
     r = l.size == 1 ? makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan)
-                    : makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan, true, l.size);
+                    : makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan, true, l.size, aggBytes);
     if (r != arSuccess) return r;
     if (!fifosCover(c, l.plan)) return arInternalError;
     l.row = rows;

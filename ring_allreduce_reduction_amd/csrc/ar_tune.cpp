@@ -28,10 +28,22 @@
 // order the pages' head-inserted candidate list gives when the ring's
 // candidates are registered after the tree's.
 #include <float.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <array>
+#include <mutex>
+#include <vector>
 
 #include "ar.h"
+#include "ar_tune_table.h"
+
+#include "ar_tune_table.inc"
 
 namespace {
 
@@ -151,4 +163,198 @@ extern "C" arResult_t arTuneEval(int nranks, int maxChannels, size_t nBytes, con
                                  unsigned protoMask, arProto_t* proto, int* nChannels, float* predictedUs) {
   return arTuneEvalColl(arFuncAllReduce, nranks, maxChannels, nBytes, models, protoMask, proto, nChannels,
                         predictedUs);
+}
+
+// ---------------------------------------------------------------- the tuner's time table
+//
+// The pages let a tuner plugin see the cost of every (algorithm, protocol)
+// candidate and override it before the argmin ["NCCL 原始碼解讀：一個
+// AllReduce 的 GPU 旅程", ch.5 §一, step 3; "NCCL 源码解析：从硬件拓扑到集合通信
+// 选型的完整链路", §五, the tuner plugin].  The overriding costs here are
+// times measured on MI355X: one line per (ranks, bytes per rank) with the six
+// candidates' microseconds, compiled in from the calibration record
+// (ar_tune_table.txt) or read from the file AR_TUNE_FILE names.  A query
+// between lines is interpolated log-log in bytes along each rank count's
+// lines, then log-log between the two nearest rank counts; past a rank
+// count's largest size the time grows in proportion to the bytes.  Rank
+// counts outside the table are not covered (the cost model decides).
+
+namespace {
+
+struct TableRank {
+  int nranks;
+  std::vector<uint64_t> bytes;        // ascending
+  std::vector<std::array<float, 6>> us;   // < 0: that candidate cannot run
+};
+
+struct TuneTable {
+  std::vector<TableRank> ranks;       // ascending nranks
+  bool haveModels[2][3] = {};
+  arTuneModel_t models[2][3] = {};    // [algo][proto], from "model" lines
+};
+
+void addRow(TuneTable& t, int n, uint64_t bytes, const float us[6]) {
+  auto it = std::find_if(t.ranks.begin(), t.ranks.end(), [&](const TableRank& r) { return r.nranks >= n; });
+  if (it == t.ranks.end() || it->nranks != n) {
+    TableRank r;
+    r.nranks = n;
+    it = t.ranks.insert(it, r);
+  }
+  auto jt = std::lower_bound(it->bytes.begin(), it->bytes.end(), bytes);
+  const size_t j = (size_t)(jt - it->bytes.begin());
+  std::array<float, 6> a;
+  for (int k = 0; k < 6; ++k) a[k] = us[k];
+  if (jt != it->bytes.end() && *jt == bytes) {
+    it->us[j] = a;
+  } else {
+    it->bytes.insert(jt, bytes);
+    it->us.insert(it->us.begin() + (ptrdiff_t)j, a);
+  }
+}
+
+// Parse a table file; false (with a warning) if it holds a malformed line or no line.
+bool parseTableFile(const char* path, TuneTable& t) {
+  FILE* f = fopen(path, "r");
+  if (f == nullptr) {
+    fprintf(stderr, "[ar] WARN AR_TUNE_FILE=%s cannot be opened; using the compiled table\n", path);
+    return false;
+  }
+  char line[1024];
+  int lineNo = 0, rows = 0;
+  bool ok = true;
+  while (ok && fgets(line, sizeof(line), f) != nullptr) {
+    ++lineNo;
+    if (char* h = strchr(line, '#')) *h = 0;
+    char* tok[16];
+    int nt = 0;
+    for (char* p = strtok(line, " \t\r\n"); p != nullptr && nt < 16; p = strtok(nullptr, " \t\r\n")) tok[nt++] = p;
+    if (nt == 0) continue;
+    if (!strcmp(tok[0], "model")) {
+      const int al = nt == 7 ? (!strcmp(tok[1], "ring") ? 0 : !strcmp(tok[1], "tree") ? 1 : -1) : -1;
+      const int pr = nt == 7 ? (!strcmp(tok[2], "ll") ? 0 : !strcmp(tok[2], "ll128") ? 1 : !strcmp(tok[2], "simple") ? 2 : -1)
+                             : -1;
+      if (al < 0 || pr < 0) {
+        ok = false;
+        break;
+      }
+      arTuneModel_t m = {(float)atof(tok[3]), (float)atof(tok[4]), (float)atof(tok[5]), (float)atof(tok[6])};
+      if (!(m.bwPerChGBs > 0.0f) || !(m.maxBwGBs > 0.0f) || m.baseLatUs < 0.0f || m.stepLatUs < 0.0f) {
+        ok = false;
+        break;
+      }
+      t.models[al][pr] = m;
+      t.haveModels[al][pr] = true;
+      continue;
+    }
+    if (nt != 8) {
+      ok = false;
+      break;
+    }
+    const long n = strtol(tok[0], nullptr, 10);
+    const unsigned long long b = strtoull(tok[1], nullptr, 10);
+    float us[6];
+    for (int k = 0; k < 6; ++k) us[k] = !strcmp(tok[2 + k], "-") ? -1.0f : (float)atof(tok[2 + k]);
+    if (n < 2 || n > AR_MAX_RANKS || b == 0) {
+      ok = false;
+      break;
+    }
+    addRow(t, (int)n, (uint64_t)b, us);
+    ++rows;
+  }
+  fclose(f);
+  if (!ok || rows == 0) {
+    fprintf(stderr, "[ar] WARN AR_TUNE_FILE=%s: bad line %d (or no table line); using the compiled table\n", path,
+            lineNo);
+    return false;
+  }
+  return true;
+}
+
+// The table in force, read once per process: AR_TUNE_FILE if it parses, else
+// the compiled one [the reference's parameter cache, ch.3 §3.5].
+const TuneTable& table() {
+  static TuneTable t;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    TuneTable f;
+    for (int p = 0; p < 3; ++p) {   // the compiled constants, unless the file names others
+      f.models[0][p] = kCompiledRingModels[p];
+      f.models[1][p] = kCompiledTreeModels[p];
+      f.haveModels[0][p] = f.haveModels[1][p] = true;
+    }
+    const char* path = getenv("AR_TUNE_FILE");
+    if (path != nullptr && *path != 0) {
+      TuneTable g = f;
+      if (parseTableFile(path, g)) {
+        t = g;
+        return;
+      }
+    }
+    for (const ar::TuneRow& r : kCompiledTuneRows) addRow(f, r.nranks, r.bytes, r.us);
+    t = f;
+  });
+  return t;
+}
+
+// One rank count's time for a candidate at `bytes`, or a negative value where
+// a line it needs marks the candidate as unable to run.
+float rankTime(const TableRank& r, uint64_t bytes, int k) {
+  const size_t m = r.bytes.size();
+  size_t hi = 0;   // first line with at least `bytes`
+  while (hi < m && r.bytes[hi] < bytes) ++hi;
+  if (hi == 0) return r.us[0][(size_t)k];             // at or below the smallest size: its time
+  const size_t lo = hi - 1;
+  const float tl = r.us[lo][(size_t)k];
+  if (hi == m)                                        // past the largest: in proportion to the bytes
+    return tl < 0.0f ? -1.0f : tl * (float)((double)bytes / (double)r.bytes[lo]);
+  const float th = r.us[hi][(size_t)k];
+  if (r.bytes[hi] == bytes) return th;
+  if (tl < 0.0f || th < 0.0f) return -1.0f;
+  const double w = (log((double)bytes) - log((double)r.bytes[lo])) / (log((double)r.bytes[hi]) - log((double)r.bytes[lo]));
+  return (float)exp((1.0 - w) * log((double)tl) + w * log((double)th));
+}
+
+}  // namespace
+
+bool ar::tuneTableTime(int nranks, uint64_t nBytes, int algo, int proto, float* us) {
+  const TuneTable& t = table();
+  if (algo < 0 || algo > 1 || proto < 0 || proto > 2 || nBytes == 0 || t.ranks.empty()) return false;
+  if (nranks < t.ranks.front().nranks || nranks > t.ranks.back().nranks) return false;
+  const int k = algo * 3 + proto;
+  size_t i = 0;
+  while (t.ranks[i].nranks < nranks) ++i;   // first rank count >= nranks
+  float v;
+  if (t.ranks[i].nranks == nranks) {
+    v = rankTime(t.ranks[i], nBytes, k);
+  } else {
+    const TableRank& a = t.ranks[i - 1];
+    const TableRank& b = t.ranks[i];
+    const float ta = rankTime(a, nBytes, k), tb = rankTime(b, nBytes, k);
+    if (ta < 0.0f || tb < 0.0f) return false;
+    const double w = (log((double)nranks) - log((double)a.nranks)) / (log((double)b.nranks) - log((double)a.nranks));
+    v = (float)exp((1.0 - w) * log((double)ta) + w * log((double)tb));
+  }
+  if (v < 0.0f) return false;
+  *us = v;
+  return true;
+}
+
+bool ar::tuneTableCovers(int nranks) {
+  const TuneTable& t = table();
+  return !t.ranks.empty() && nranks >= t.ranks.front().nranks && nranks <= t.ranks.back().nranks;
+}
+
+void ar::tuneTableModels(arTuneModel_t ring[3], arTuneModel_t tree[3]) {
+  const TuneTable& t = table();
+  for (int p = 0; p < 3; ++p) {
+    if (t.haveModels[0][p]) ring[p] = t.models[0][p];
+    if (t.haveModels[1][p]) tree[p] = t.models[1][p];
+  }
+}
+
+extern "C" arResult_t arTuneTableTime(int nranks, size_t nBytes, arAlgo_t algo, arProto_t proto, float* predictedUs) {
+  if (predictedUs == nullptr || nranks < 1 || nBytes == 0) return arInvalidArgument;
+  if (algo != arAlgoRing && algo != arAlgoTree) return arInvalidArgument;
+  if (proto != arProtoLL && proto != arProtoLL128 && proto != arProtoSimple) return arInvalidArgument;
+  return ar::tuneTableTime(nranks, (uint64_t)nBytes, (int)algo, (int)proto, predictedUs) ? arSuccess : arInvalidUsage;
 }

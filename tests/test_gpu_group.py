@@ -238,3 +238,28 @@ def test_groups_back_to_back_without_sync(B, gu):
                 for r in range(n):
                     gu.assert_bits_equal(gu.to_host_raw(d[r], "float32"), want, "float32",
                                          "group %d call %d rank %d" % (g, i, r))
+
+
+def test_aggregate_is_tuned_on_its_bytes_together(B, gu):
+    """Sixteen AllReduces of 1 MiB per rank at 8 ranks share one launch and
+    run side by side: the aggregate is tuned on their 16 MiB together, where
+    the ring is the faster algorithm (a single 1 MiB call takes the tree)."""
+    n, count, T = 8, 1 << 18, 16
+    gu.note("aggregate of 16 x 1 MiB at 8 ranks: tuned on 16 MiB")
+    xs = [torch.rand(count, device="cuda") for _ in range(n)]
+    outs = [[torch.empty_like(x) for x in xs] for _ in range(T)]
+    with B.Comm(n, 64, "auto", "auto") as comm:
+        single = comm.plan(count, "float32")
+        with B.Group():
+            for i in range(T):
+                comm.allreduce(xs, outs[i], "sum")
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arSuccess
+        plans = [comm.group_plan(i) for i in range(T)]
+        assert {p["tasksInLaunch"] for p in plans} == {T}
+        a16, _, _, _ = B.arTuneAlgo(comm.handle, T * count * 4)
+        assert plans[0]["algo"] == a16 == B.arAlgoRing
+        assert single["algo"] == B.arAlgoTree
+        ref = sum(x.double() for x in xs)
+        for i in range(T):
+            assert torch.allclose(outs[i][3].double(), ref, atol=1e-5)

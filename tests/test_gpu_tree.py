@@ -128,11 +128,14 @@ def test_tree_one_rank_and_empty(B, gu):
         assert comm.async_error() == B.arSuccess
 
 
-@pytest.mark.parametrize("n", [2, 5, 8, 16, 72])
-def test_tuner_caps_shared_hbm(B, n):
-    # a comm prices every algorithm with its cap scaled for N ranks on one
-    # HBM: ring x 8/N, tree x 44/(6N-4); everything else as fitted
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 16, 40, 72])
+def test_tuner_follows_the_table_with_model_channels(B, n):
+    # a comm takes the candidate with the shortest time in the tuner's table
+    # (ring Simple, LL128, LL, then tree on ties), at the channel count the
+    # cost model gives that candidate with its caps scaled for N ranks on one
+    # HBM (ring x 8/N, tree x 44/(6N-4))
     f32 = np.float32
+    order = [(0, 2), (0, 1), (0, 0), (1, 2), (1, 1), (1, 0)]
     with B.Comm(n, 64, "auto", "auto") as comm:
         ring = [B.arTuneGetAlgoModel(comm.handle, B.arAlgoRing, p) for p in range(3)]
         tree = [B.arTuneGetAlgoModel(comm.handle, B.arAlgoTree, p) for p in range(3)]
@@ -141,12 +144,41 @@ def test_tuner_caps_shared_hbm(B, n):
         for log2_bytes in (3, 12, 17, 20, 22, 23, 24, 26, 28):
             nbytes = 1 << log2_bytes
             a, p, ch, t = B.arTuneAlgo(comm.handle, nbytes)
-            ea, ep, ech, et = B.arTuneEvalAlgo(0, n, 64, nbytes, ring_s, tree_s)
-            assert (a, p, ch) == (ea, ep, ech) and t == pytest.approx(et, rel=1e-6)
-            if n == 8:
-                assert (a, p, ch) == B.arTuneEvalAlgo(0, n, 64, nbytes, ring, tree)[:3]
+            times = [(B.arTuneTableTime(n, nbytes, al, pr), i) for i, (al, pr) in enumerate(order)]
+            best, bi = min((tt, i) for tt, i in times if tt is not None)
+            assert (a, p) == order[bi] and t == pytest.approx(best, rel=1e-6)
+            _, _, ech, _ = B.arTuneEvalAlgo(0, n, 64, nbytes, ring_s, tree_s, algoMask=1 << a, protoMask=1 << p)
+            assert ch == ech
             if n == 16 and log2_bytes in (22, 23):
                 assert a == B.arAlgoRing   # 16 ranks x 4-8 MiB: the ring is measured 1.4-1.5x faster
+            if n == 3 and log2_bytes == 22:
+                assert a == B.arAlgoTree   # 3 ranks x 4 MiB: the tree is measured 14% faster
+
+
+def test_tune_file_models_reach_a_comm(B):
+    """AR_TUNE_FILE's "model" lines replace the cost model's constants of
+    every comm (checked in a child process: the file is read once per process)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = os.path.join(os.environ.get("TMPDIR", "/tmp"), "ar_tune_models_%d.txt" % os.getpid())
+    with open(path, "w") as f:
+        f.write("8 4096 1 2 3 4 5 6\nmodel tree ll128 1.5 2.5 30 40\n")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from ring_allreduce_reduction_amd import binding as B\n"
+            "with B.Comm(8, 4, 'auto', 'auto') as c:\n"
+            "    print(B.arTuneGetAlgoModel(c.handle, B.arAlgoTree, B.arProtoLL128))\n"
+            "    print(B.arTuneAlgo(c.handle, 4096))\n" % root)
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, AR_TUNE_FILE=path),
+                           capture_output=True, text=True, timeout=300)
+    finally:
+        os.remove(path)
+    assert r.returncode == 0, r.stderr
+    lines = r.stdout.strip().splitlines()
+    assert lines[0] == str((1.5, 2.5, 30.0, 40.0))
+    assert lines[1].startswith("(0, 0, 1,")   # the file's table: ring LL is the fastest there
 
 
 @pytest.mark.parametrize("proto", PROTOS)
