@@ -166,7 +166,8 @@ def main():
     if args.explore:
         return explore(args, B, torch, comm, sends, recvs, count, dtype, N, S)
     plan = comm.plan(count, dtype)
-    log("plan: %s" % json.dumps(plan))
+    footprint = comm.footprint()
+    log("plan: %s; comm device footprint %.1f MiB" % (json.dumps(plan), footprint / 2 ** 20))
     stream = torch.cuda.Stream()
     dt_code = B.DTYPE_BY_NAME[dtype]
     with torch.cuda.stream(stream):
@@ -267,7 +268,7 @@ def main():
                    "proto": B.PROTO_NAMES[plan["proto"]], "nChannels": plan["nChannels"],
                    "chunkElems": plan["chunkElems"], "lanesPerChannel": plan["lanesPerChannel"],
                    "workgroups": plan["workgroups"], "threadsPerGroup": plan["threadsPerGroup"],
-                   "slotBytes": plan["stepBytes"],
+                   "slotBytes": plan["stepBytes"], "commDeviceBytes": footprint,
                    "selection": "arTune" if args.proto == "auto" else "forced"},
         "algbw_GBs": round(algbw, 3),
         "busbw_GBs": round(busbw, 3),

@@ -93,8 +93,8 @@ typedef enum {
  *  proto     default protocol, or arProtoAuto.
  *  algo      arAlgoRing, arAlgoTree or arAlgoAuto (the default algorithm for
  *            AllReduce; arAlgoAuto lets arTune choose per call).
- * Allocates the FIFOs, counters and flags of every protocol on the device
- * (owned by the comm, freed by arDestroy).  Environment overrides, read once
+ * Allocates the FIFOs, counters and flags of the protocols the comm may run
+ * on the device (owned by the comm, freed by arDestroy; see arCommFootprint).  Environment overrides, read once
  * per process: AR_PROTO (LL|LL128|SIMPLE), AR_NCHANNELS, AR_SLICE_BYTES
  * (Simple slice, default 512 KiB; chunk = 2 slices), AR_STEPS (FIFO depth
  * in slots, 2..8; default 2 for Simple, 8 for LL and LL128), AR_TIMEOUT_MS.
@@ -283,6 +283,9 @@ arResult_t arTuneSetAlgoModel(arComm_t comm, arAlgo_t algo, arProto_t proto, con
 /*
  * arSetConfig -- change the comm's default protocol and channel count, same
  * meaning as in arInit (nChannels must not exceed the value given there).
+ * Provisions the FIFOs of a protocol the comm had not run (arHipError if that
+ * allocation fails); arInvalidUsage while the comm has calls queued in an
+ * open group.
  */
 arResult_t arSetConfig(arComm_t comm, arProto_t proto, int nChannels);
 
@@ -339,6 +342,21 @@ arResult_t arGetPlanColl(arComm_t comm, arFunc_t func, size_t count, arDataType_
  * [B ch.2 §2.1 asyncResult; ch.7 group error paths].
  */
 arResult_t arCommGetAsyncError(arComm_t comm, arResult_t* asyncError);
+
+/*
+ * arCommFootprint -- device memory a comm holds [B ch.2 §2.1, the
+ * per-protocol FIFO buffers; ch.3 §3.6, device state set up for the comm]:
+ * the FIFOs and counters of the protocols provisioned (N ranks x lanesMax
+ * workers, each FIFO depth x the protocol's largest slot: 8 KiB Simple,
+ * 2 KiB LL, 4 KiB LL128, plus 256 bytes of counters), the failed word and the
+ * task table of grouped launches.  arInit provisions the comm's protocol at
+ * its depth (all three with arProtoAuto); a protocol switched to later is
+ * provisioned by arSetConfig or by its first call (which then allocates),
+ * and a deeper FIFO (arDebugSlots) re-provisions after the comm's last
+ * stream has finished.
+ *  deviceBytes (host, out).
+ */
+arResult_t arCommFootprint(arComm_t comm, size_t* deviceBytes);
 
 /*
  * arCommCount -- the number of virtual ranks of a comm [B ch.1 §1.2, the

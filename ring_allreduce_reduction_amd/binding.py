@@ -100,6 +100,7 @@ def lib():
         L.arCommGetAsyncError.argtypes = [vp, ctypes.POINTER(c_int)]
         L.arCommAbort.argtypes = [vp]
         L.arCommCount.argtypes = [vp, ctypes.POINTER(c_int)]
+        L.arCommFootprint.argtypes = [vp, ctypes.POINTER(c_sz)]
         L.arTuneTableTime.argtypes = [c_int, c_sz, c_int, c_int, ctypes.POINTER(c_f)]
         L.arAllReduceNoAlloc.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_int, c_int, c_sz, c_int, c_int, vp]
         L.arDestroy.argtypes = [vp]
@@ -111,7 +112,7 @@ def lib():
                    "arSetAlgo", "arTuneAlgo", "arTuneEvalAlgo", "arTuneGetAlgoModel", "arTuneSetAlgoModel",
                    "arGroupStart", "arGroupEnd", "arGroupAggregate", "arGetGroupPlan",
                    "arCommGetAsyncError", "arCommAbort", "arCommCount", "arDestroy", "arSetDebug",
-                   "arAllReduceNoAlloc", "arTuneTableTime"):
+                   "arAllReduceNoAlloc", "arTuneTableTime", "arCommFootprint"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -396,6 +397,12 @@ def arCommCount(comm):
     return n.value
 
 
+def arCommFootprint(comm):
+    b = ctypes.c_size_t()
+    _check(lib().arCommFootprint(comm, ctypes.byref(b)), "arCommFootprint")
+    return b.value
+
+
 def arCommAbort(comm):
     _check(lib().arCommAbort(comm), "arCommAbort")
 
@@ -457,6 +464,9 @@ class Comm:
 
     def group_plan(self, index):
         return arGetGroupPlan(self.handle, index)
+
+    def footprint(self):
+        return arCommFootprint(self.handle)
 
     def async_error(self):
         return arCommGetAsyncError(self.handle)

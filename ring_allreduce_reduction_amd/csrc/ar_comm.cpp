@@ -139,6 +139,7 @@ struct arComm {
   char* fifo[3];
   Conn* conn[3];
   size_t fifoWorkerBytes[3];
+  int fifoDepth[3];     // slots per worker the protocol's FIFOs are provisioned for (0: none yet)
   Control* ctrlHost;
   Control* ctrlDev;
   uint32_t* failedDev;  // device word the kernels set when a member gives up
@@ -185,6 +186,51 @@ int slotBytesOf(int proto, int unroll) {
 }
 int slotPayloadOf(int proto, int unroll) {
   return proto == kSimple ? unroll * kWave * 16 : proto == kLL ? kLLSlotPayload : unroll * kLL128UnitPayload;
+}
+
+// FIFOs and counters of one protocol [ch.2 §2.1 buffSizes per protocol;
+// ch.3 §3.6 devCommSetup]: every worker (N ranks x lanesMax (channel, lane)
+// pairs) gets `depth` slots of the protocol's largest slot, zeroed with its
+// counters.  A protocol's lines are never read as another's (LL flags live
+// inside the data), so each has its own region.  Re-provisioning (a deeper
+// FIFO) first waits for the comm's last stream, then starts the new region
+// from zero: its counters restart at 0 along with every slot, so both ends
+// of each FIFO still agree.
+arResult_t provisionFifo(arComm* c, int p, int depth) {
+  if (c->nranks < 2) return arSuccess;
+  if (c->fifo[p] != nullptr && c->fifoDepth[p] >= depth) return arSuccess;
+  if (c->fifo[p] != nullptr) {
+    if (c->launched && hipStreamSynchronize(c->lastStream) != hipSuccess) return arHipError;
+    (void)hipFree(c->fifo[p]);
+    (void)hipFree(c->conn[p]);
+    c->fifo[p] = nullptr;
+    c->conn[p] = nullptr;
+    c->fifoDepth[p] = 0;
+  }
+  const size_t workers = (size_t)c->nranks * (size_t)c->lanesMax;
+  const size_t workerBytes = (size_t)depth * (size_t)slotBytesOf(p, p == kLL128 ? kLL128UnrollLarge : kSimpleUnrollMax);
+  const size_t fb = workers * workerBytes, cb = workers * sizeof(Conn);
+  if (hipMalloc((void**)&c->fifo[p], fb) != hipSuccess || hipMalloc((void**)&c->conn[p], cb) != hipSuccess ||
+      hipMemset(c->fifo[p], 0, fb) != hipSuccess || hipMemset(c->conn[p], 0, cb) != hipSuccess) {
+    if (c->fifo[p]) (void)hipFree(c->fifo[p]);
+    if (c->conn[p]) (void)hipFree(c->conn[p]);
+    c->fifo[p] = nullptr;
+    c->conn[p] = nullptr;
+    return arHipError;
+  }
+  c->fifoWorkerBytes[p] = workerBytes;
+  c->fifoDepth[p] = depth;
+  return arSuccess;
+}
+
+// Device bytes a comm holds: FIFOs and counters of the protocols provisioned,
+// the failed word, and the task table of grouped launches.
+size_t deviceFootprint(const arComm* c) {
+  size_t b = 256;   // the failed word's line
+  const size_t workers = (size_t)c->nranks * (size_t)c->lanesMax;
+  for (int p = 0; p < 3; ++p)
+    if (c->fifo[p] != nullptr) b += workers * (c->fifoWorkerBytes[p] + sizeof(Conn));
+  return b + c->taskTableWords * sizeof(uint64_t);
 }
 
 size_t chunkBytesOf(const arComm* c, int proto) {
@@ -696,22 +742,15 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->plainLaunch = true;
   tuneTableModels(c->models, c->treeModels);
 
-  // FIFOs and counters, one set per protocol (a line of one protocol must
-  // never be read as another's: LL flags live inside the data).
-  const int lanesMax = kMaxWorkers / nranks > nChannels ? kMaxWorkers / nranks : nChannels;
-  c->lanesMax = lanesMax;
-  const size_t workers = (size_t)nranks * (size_t)lanesMax;
-  if (nranks > 1) {
-    for (int p = 0; p < 3; ++p) {
-      c->fifoWorkerBytes[p] = (size_t)kMaxSlots * (size_t)slotBytesOf(p, p == kLL128 ? kLL128UnrollLarge
-                                                                                      : kSimpleUnrollMax);
-      const size_t fb = workers * c->fifoWorkerBytes[p];
-      const size_t cb = workers * sizeof(Conn);
-      if (hipMalloc((void**)&c->fifo[p], fb) != hipSuccess || hipMalloc((void**)&c->conn[p], cb) != hipSuccess ||
-          hipMemset(c->fifo[p], 0, fb) != hipSuccess || hipMemset(c->conn[p], 0, cb) != hipSuccess) {
-        freeComm(c);
-        return arHipError;
-      }
+  // FIFOs and counters: every protocol the comm may run (all three when it
+  // tunes per call), each at the depth it runs with; a protocol switched to
+  // later is provisioned by arSetConfig or its first call.
+  c->lanesMax = kMaxWorkers / nranks > nChannels ? kMaxWorkers / nranks : nChannels;
+  for (int p = 0; p < 3; ++p) {
+    const bool used = proto == arProtoAuto || proto == p || e.forcedProto == p;
+    if (used && provisionFifo(c, p, c->nSlots[p]) != arSuccess) {
+      freeComm(c);
+      return arHipError;
     }
   }
   if (hipHostMalloc((void**)&c->ctrlHost, sizeof(Control), hipHostMallocCoherent | hipHostMallocMapped) !=
@@ -745,8 +784,11 @@ arResult_t arSetConfig(arComm_t c, arProto_t proto, int nChannels) {
   if (proto != arProtoAuto && proto != arProtoLL && proto != arProtoLL128 && proto != arProtoSimple)
     return arInvalidArgument;
   if (nChannels < 1 || nChannels > c->maxChannels) return arInvalidArgument;
+  if (c->inGroup) return arInvalidUsage;   // queued calls may still plan with the old setting
   c->proto = proto;
   c->nChannels = nChannels;
+  for (int p = 0; p < 3; ++p)   // the FIFOs of every protocol it may now run
+    if ((proto == arProtoAuto || proto == p) && provisionFifo(c, p, c->nSlots[p]) != arSuccess) return arHipError;
   return arSuccess;
 }
 
@@ -784,7 +826,11 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   }
   if (knob == arDebugSlots) {
     if (value < 2 || value > kMaxSlots) return arInvalidArgument;
-    for (int p = 0; p < 3; ++p) c->nSlots[p] = (int)value;
+    if (c->inGroup) return arInvalidUsage;
+    for (int p = 0; p < 3; ++p) {
+      c->nSlots[p] = (int)value;
+      if (c->fifo[p] != nullptr && provisionFifo(c, p, c->nSlots[p]) != arSuccess) return arHipError;
+    }
     return arSuccess;
   }
   if (knob == arDebugLaneSets) {
@@ -1039,6 +1085,8 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   arResult_t r = makePlan(c, func, count, dtype, kop, aligned128, &plan);
   if (r != arSuccess) return r;
   if (!fifosCover(c, plan)) return arInternalError;
+  r = provisionFifo(c, plan.proto, plan.nSlots);   // a protocol this comm has not run yet
+  if (r != arSuccess) return r;
 
   KernelArgs a;
   buildArgs(c, plan, func, count, sendbufs, recvbufs, aligned16, &a);
@@ -1257,6 +1305,8 @@ arResult_t launchGroup(arComm* c) {
                     : makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan, true, l.size, aggBytes);
     if (r != arSuccess) return r;
     if (!fifosCover(c, l.plan)) return arInternalError;
+    r = provisionFifo(c, l.plan.proto, l.plan.nSlots);
+    if (r != arSuccess) return r;
     l.row = rows;
     if (l.size > 1) rows += (size_t)l.size;
     L.push_back(l);
@@ -1382,6 +1432,12 @@ arResult_t arCommGetAsyncError(arComm_t c, arResult_t* err) {
   const uint32_t st = __atomic_load_n(&c->ctrlHost->status, __ATOMIC_ACQUIRE);
   if (st != 0) c->aborted = true;
   *err = (st != 0 || c->ctrlHost->abortFlag != 0) ? arRemoteError : arSuccess;
+  return arSuccess;
+}
+
+arResult_t arCommFootprint(arComm_t c, size_t* deviceBytes) {
+  if (!commOk(c) || deviceBytes == nullptr) return arInvalidArgument;
+  *deviceBytes = deviceFootprint(c);
   return arSuccess;
 }
 

@@ -69,3 +69,27 @@ def test_cooperative_and_plain_launches_agree(B, gu, orc, n, proto, algo):
             B.arSetDebug(comm.handle, B.arDebugCooperative, coop)
             plan, _, _ = gu.parity_case(n, 70001, "float32", "sum", proto, 16, seed=n + coop, comm=comm)
             assert plan["ranksPerGroup"] < n
+
+
+def test_fifo_footprint_follows_the_protocols(B, gu, orc):
+    """A comm provisions the FIFOs of the protocols it may run, each at the
+    depth it runs with: N x lanesMax workers x depth x the largest slot (8 KiB
+    Simple, 2 KiB LL, 4 KiB LL128) plus 256 bytes of counters each."""
+    n = 8
+    workers = n * (32768 // n)
+    simple = workers * (2 * 8192 + 256)
+    ll = workers * (8 * 2048 + 256)
+    ll128 = workers * (8 * 4096 + 256)
+    with B.Comm(n, 16, "simple") as comm:
+        assert comm.footprint() == 256 + simple
+        gu.parity_case(n, 300007, "float32", "sum", "simple", 16, seed=1, comm=comm)
+        comm.set_config("ll", 16)                         # a protocol switched to is provisioned then
+        assert comm.footprint() == 256 + simple + ll
+        gu.parity_case(n, 300007, "float32", "sum", "ll", 16, seed=2, comm=comm)
+        B.arSetDebug(comm.handle, B.arDebugSlots, 4)      # Simple deeper (2 -> 4): re-provisioned from zero;
+        assert comm.footprint() == 256 + workers * (4 * 8192 + 256) + ll   # LL shallower (8 -> 4): kept
+        gu.parity_case(n, 300007, "float32", "sum", "ll", 16, seed=3, comm=comm)
+        gu.parity_case(n, 300007, "float32", "sum", "simple", 16, seed=4, comm=comm)
+    with B.Comm(n, 64, "auto", "auto") as comm:
+        assert comm.footprint() == 256 + simple + ll + ll128
+        assert comm.footprint() < (5 << 29)                # 2.5 GiB, every protocol
