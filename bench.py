@@ -7,9 +7,12 @@ arAllReduce over all ranks with inputs already resident in HBM.
 
 Reported per step (S = bytes per rank, N = ranks, t = time per step):
   algbw = S / t;  busbw = algbw * 2(N-1)/N  (the pages' ring factor)
-  modelBytes = 5(N-1) * S  (reduce-scatter step reads 2 chunks, writes 1;
-  all-gather step reads 1, writes 1; N-1 steps each over N ranks)
-  roofline.achieved = modelBytes / t, against the 8 TB/s HBM peak.
+  deviceBytes = the device-memory bytes the plan's kernel must move: 2N * S
+  when the ring's FIFO slots are in LDS (every input read once, every
+  output written once), else modelBytes = 5(N-1) * S (a reduce-scatter step
+  reads 2 chunks and writes 1, an all-gather step reads 1 and writes 1, N-1
+  steps each over N ranks, every FIFO slot in device memory)
+  roofline.achieved = deviceBytes / t, against the 8 TB/s HBM peak.
 The CPU baseline is the oracle (single-threaded C) on the same inputs.
 After the timed region, plain streaming kernels (a copy, two reads and a
 write, a read, a write; csrc/probes/stream_ceiling.hip) measure the box's
@@ -77,6 +80,10 @@ def parse():
     ap.add_argument("--calib-grid", default="",
                     help="'N1,N2,..:log2size1,log2size2,..': time every algorithm x protocol at each rank count and "
                          "per-rank size (fp32 Sum, channels by the 32 KiB rule); one JSON line each")
+    ap.add_argument("--group-sweep", default="",
+                    help="'N:bytes:gs1,gs2,..': a ring (or --algo tree) of N ranks at this many bytes per rank "
+                         "with at most gs members per workgroup, every protocol; one JSON line each, then a "
+                         "per-protocol fit of time against the groups per ring (hops inside vs between groups)")
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarize rocprofv3 CSV output directories into markdown + profiles/traffic.json")
     ap.add_argument("--profile-label", default="", help="workload key for --summarize-profiles")
@@ -119,6 +126,8 @@ def main():
         return calibrate(args, B, torch, np)
     if args.large_n_table:
         return large_n_table(args, B, torch, np)
+    if args.group_sweep:
+        return group_sweep(args, B, torch, np)
     if args.calib_grid:
         return calib_grid(args, B, torch, np)
     if args.batch:
@@ -196,8 +205,9 @@ def main():
     t = ms / 1e3
     algbw = S / t / 1e9
     busbw = algbw * 2 * (N - 1) / N
-    model_bytes = plan["modelBytes"]   # ring: 5(N-1)S; tree: (2N + 4(N-1))S
-    achieved = model_bytes / t / 1e9
+    model_bytes = plan["modelBytes"]     # ring: 5(N-1)S; tree: (2N + 4(N-1))S
+    device_bytes = plan["deviceBytes"]   # the kernel's own: 2NS with LDS FIFOs, else modelBytes
+    achieved = device_bytes / t / 1e9
     log("per-launch ms: mean %.4f min %.4f max %.4f; wall per step %.4f ms"
         % (ms, min(launch_ms), max(launch_ms), wall / args.steps * 1e3))
 
@@ -272,8 +282,10 @@ def main():
                    "selection": "arTune" if args.proto == "auto" else "forced"},
         "algbw_GBs": round(algbw, 3),
         "busbw_GBs": round(busbw, 3),
+        "fifo_in_lds": plan["ldsFifoBytes"] > 0,
+        "device_bytes_per_step": device_bytes,
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "model_bytes_per_step": model_bytes,
-        "hbm_frac_model": round(achieved / HBM_PEAK_GBS, 4),
         "all_ranks_identical": bool(same),
         "oracle_exact": oracle_exact,
         "err_max": err_max,
@@ -284,7 +296,7 @@ def main():
         "stream_ceiling": ceiling,
     }
     if ceiling:
-        out["model_vs_copy_ceiling"] = round(achieved / ceiling["copy"], 4)
+        out["device_vs_copy_ceiling"] = round(achieved / ceiling["copy"], 4)
     print(json.dumps(out), flush=True)
     # a number is published only for a correct result
     if not same or oracle_exact is False or err_max > err_bound:
@@ -500,7 +512,7 @@ def bench_halves(args, B, gen, torch, np):
     algbw = N * Bb / t / 1e9
     busbw = algbw * (N - 1) / N
     model_bytes = plan["modelBytes"]
-    achieved = model_bytes / t / 1e9
+    achieved = plan["deviceBytes"] / t / 1e9
     if rs:   # sanity: a sample of rank 3's block against a float64 direct sum (torch, no oracle)
         idx = torch.randint(0, count, (100000,), device="cuda", generator=torch.Generator("cuda").manual_seed(1))
         s64 = sum(x[3 * count + idx].double() for x in sends)
@@ -629,21 +641,22 @@ def time_calls(B, torch, comm, sends, recvs, count, dt_code, warmup, steps):
 
 def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
     """Time a grid of configurations in one process:
-    --explore 'channels:lanes[:slotKiB[:direct[:depth[:sets]]]]', each a comma list
+    --explore 'channels:lanes[:slotKiB[:direct[:depth[:sets[:lds]]]]]', each a comma list
     (lanes 0 = automatic, depth 0 = the protocol's default, sets 0 = one
-    workgroup per (channel, lane), else at most that many workgroups)."""
+    workgroup per (channel, lane), else at most that many workgroups; lds 1 =
+    FIFO slots in LDS where they fit, the default, 0 = in device memory)."""
     parts = args.explore.split(":")
-    parts += ["8", "1", "0", "0"][len(parts) - 2:]
-    chs, lanes, slots, directs, depths, setss = [[int(x) for x in p.split(",")] for p in parts[:6]]
-    grid = [(a, b, c, e, f, h) for a in chs for b in lanes for c in slots for e in directs for f in depths
-            for h in setss]
+    parts += ["8", "1", "0", "0", "1"][len(parts) - 2:]
+    chs, lanes, slots, directs, depths, setss, ldss = [[int(x) for x in p.split(",")] for p in parts[:7]]
+    grid = [(a, b, c, e, f, h, q) for a in chs for b in lanes for c in slots for e in directs for f in depths
+            for h in setss for q in ldss]
     proto = "simple" if args.proto == "auto" else args.proto
-    comm.set_config(proto, chs[0])
-    default_depth = comm.plan(count, dtype)["nSlots"]   # the comm's own depth for this protocol
-    for nch, ln, sk, d, dp, st in grid:
-        # every configuration sets the depth: the knob stays on the comm
-        B.arSetDebug(comm.handle, B.arDebugSlots, dp or default_depth)
-        comm.set_config(proto, nch)
+    comm.close()
+    for nch, ln, sk, d, dp, st, lq in grid:
+        # a fresh comm per configuration: knobs stay on a comm
+        comm = B.Comm(N, nch, proto)
+        if dp:
+            B.arSetDebug(comm.handle, B.arDebugSlots, dp)
         B.arSetDebug(comm.handle, B.arDebugLanes, ln)
         if args.proto == "ll128":   # the slot field sets the LL128 slot (2 or 4 KiB)
             B.arSetDebug(comm.handle, B.arDebugLL128SlotKiB, sk)
@@ -651,16 +664,18 @@ def explore(args, B, torch, comm, sends, recvs, count, dtype, N, S):
             B.arSetDebug(comm.handle, B.arDebugSimpleSlotKiB, sk)
         B.arSetDebug(comm.handle, B.arDebugDirect, d)
         B.arSetDebug(comm.handle, B.arDebugLaneSets, st)
+        B.arSetDebug(comm.handle, B.arDebugLdsFifo, lq)
         plan = comm.plan(count, dtype)
         ms = time_calls(B, torch, comm, sends, recvs, count, B.DTYPE_BY_NAME[dtype], 2, args.steps)
-        frac = 5.0 * (N - 1) * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
+        frac = plan["deviceBytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
         print(json.dumps({"nch": nch, "lanes": plan["lanesPerChannel"], "slotKiB": sk, "direct": d,
-                          "depth": plan["nSlots"], "sets": st, "grid": plan["workgroups"],
+                          "depth": plan["nSlots"], "sets": st, "lds": plan["ldsFifoBytes"],
+                          "grid": plan["workgroups"],
                           "block": plan["threadsPerGroup"], "groupSize": plan["ranksPerGroup"],
                           "nchRun": plan["nChannels"], "slotBytes": plan["stepBytes"],
                           "ms": round(ms, 4), "busbw": round(S / (ms / 1e3) / 1e9 * 2 * (N - 1) / N, 2),
                           "frac": round(frac, 4)}), flush=True)
-    comm.close()
+        comm.close()
 
 
 def copy_probe(args, torch):
@@ -941,6 +956,71 @@ def calib_grid(args, B, torch, np):
         comm.close()
         del sends, recvs
         torch.cuda.empty_cache()
+
+
+def group_sweep(args, B, torch, np):
+    """Time a ring or tree of N ranks cut into groups of at most gs members
+    (arDebugGroupSize), fp32 Sum on device-drawn inputs, for each protocol.
+    The configurations of a protocol are timed round-robin, five rounds of
+    back-to-back calls, and the median round is reported.  A ring cut into G
+    groups (G > 1) has G edges between workgroups out of N, and a chunk's
+    walk of 2(N-1) hops takes that share of them, so its time is about
+    t(G) = c + 2(N-1) h + 2(N-1) (G/N) (H - h), with h a hop inside a
+    workgroup and H one between workgroups; the last line per protocol is
+    the least-squares line through the grouped points and the h and H - h it
+    gives (c, the launch and fill, is folded into h)."""
+    n_s, bytes_s, gs_s = args.group_sweep.split(":")
+    N, S = int(n_s), int(bytes_s)
+    sizes = [int(x) for x in gs_s.split(",")]
+    count = max(1, S // 4)
+    rounds = 5
+    steps = 50 if S < (4 << 20) else 20
+    sends = [torch.rand(count, device="cuda") * 2 - 1 for _ in range(N)]
+    recvs = [torch.empty_like(x) for x in sends]
+    comm = B.Comm(N, args.nchannels, "simple", args.algo if args.algo != "auto" else "ring")
+    for proto in ["simple", "ll", "ll128"]:
+        comm.set_config(proto, args.nchannels)
+        rows, times = [], []
+        for gs in sizes:
+            B.arSetDebug(comm.handle, B.arDebugGroupSize, gs)
+            row = {"nranks": N, "bytes": S, "algo": args.algo, "proto": proto, "gsMax": gs}
+            try:
+                plan = comm.plan(count, "float32")
+                row.update({"nch": plan["nChannels"], "lanes": plan["lanesPerChannel"],
+                            "groupSize": plan["ranksPerGroup"], "groups": -(-N // plan["ranksPerGroup"]),
+                            "grid": plan["workgroups"], "block": plan["threadsPerGroup"],
+                            "slot": plan["stepBytes"]})
+            except B.ArError as e:
+                row["skipped"] = str(e)
+            rows.append(row)
+            times.append([])
+        for _ in range(rounds):
+            for i, gs in enumerate(sizes):
+                if "skipped" in rows[i]:
+                    continue
+                B.arSetDebug(comm.handle, B.arDebugGroupSize, gs)
+                times[i].append(time_calls(B, torch, comm, sends, recvs, count, B.arFloat32, 2, steps) * 1e3)
+        pts = []
+        for row, ts in zip(rows, times):
+            if ts:
+                ts.sort()
+                row["us"] = round(ts[len(ts) // 2], 2)
+                row["us_min"] = round(ts[0], 2)
+                row["us_max"] = round(ts[-1], 2)
+                if row["groups"] > 1:
+                    pts.append((row["groups"], row["us"]))
+            print(json.dumps(row), flush=True)
+        if len(pts) >= 2:
+            g = np.array([p[0] for p in pts], dtype=np.float64)
+            t = np.array([p[1] for p in pts], dtype=np.float64)
+            slope, icpt = np.polyfit(g, t, 1)
+            hops = 2 * (N - 1)
+            print(json.dumps({"fit": proto, "nranks": N, "bytes": S, "points": len(pts),
+                              "us_at_0_groups": round(float(icpt), 2), "us_per_group": round(float(slope), 3),
+                              "hop_inside_us": round(float(icpt) / hops, 3),
+                              "hop_between_extra_us": round(float(slope) * N / hops, 3)}), flush=True)
+    B.arSetDebug(comm.handle, B.arDebugGroupSize, 0)
+    comm.close()
 
 
 SWEEP_CANDIDATES = [("ring", "ll"), ("ring", "ll128"), ("ring", "simple"),

@@ -126,6 +126,10 @@ arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, ar
  * until the work completes.  Element pointers need only element alignment;
  * forcing LL128 needs 128-byte aligned buffers, otherwise arInvalidUsage
  * [B ch.2 §2.4, LL128 alignment]; arProtoAuto never picks LL128 then.
+ * A Simple ring of at most 16 ranks runs each (channel, lane) in one
+ * workgroup and keeps its FIFO slots in that workgroup's LDS (arPlan_t
+ * ldsFifoBytes; arDebugLdsFifo): its kernel then moves no FIFO bytes through
+ * device memory, only the inputs and outputs.
  * Residency: a ring or tree of more than 16 ranks is cut into workgroups
  * that wait on one another, so all workgroups of its launch must be resident
  * at once.  The planner sizes that grid to what the GPU holds; a kernel
@@ -313,6 +317,13 @@ typedef struct {
   int groupLaunch;      /* arGetGroupPlan: index of the launch (in launch order)
                            that carried this call; -1 for a copy or a single call */
   int tasksInLaunch;    /* collectives sharing that launch (1 unless batched) */
+  int ldsFifoBytes;     /* Simple rings inside one workgroup, single calls: the FIFO slots
+                           live in LDS, this many bytes per workgroup (N x nSlots x
+                           stepBytes); 0: FIFO slots in device memory */
+  double deviceBytes;   /* device-memory bytes the plan's kernel must move: modelBytes,
+                           except with LDS FIFOs, where only the inputs are read and the
+                           outputs written (AllReduce 2N*S; ReduceScatter and AllGather
+                           (N+1)*N*S, S the per-rank block) */
 } arPlan_t;
 
 /*
@@ -403,6 +414,13 @@ typedef enum {
                                   runtime checks residency and runs such launches one at a time,
                                   at 15-70 us per launch), 0 = plain launch of the same grid
                                   (default; see arAllReduce on residency) */
+  arDebugLdsFifo = 13,         /* 1 (default): Simple rings inside one workgroup keep their FIFO
+                                  slots in LDS when N x depth x slot fits a workgroup's LDS
+                                  (single calls); 0: in device memory */
+  arDebugGroupSize = 12,       /* at most this many ring or tree members per workgroup, 1..16
+                                  (0: 16, the default): a ring or tree longer than this is cut
+                                  into groups joined by device-coherent edges, as rings of more
+                                  than 16 ranks always are; single calls only */
 } arDebugKnob_t;
 arResult_t arSetDebug(arComm_t comm, arDebugKnob_t knob, int64_t value);
 
@@ -462,17 +480,20 @@ arResult_t arGetGroupPlan(arComm_t comm, int index, arPlan_t* plan);
  *  nranks     1..16: every ring fits one workgroup, so every FIFO edge keeps
  *             its counters in LDS and each call starts from step 0.
  *  nChannels  1..AR_MAX_CHANNELS.
- * Its FIFOs live in a fixed 64 MiB device array inside the library, one per
- * GPU it runs on, held until the process ends; the device's first call looks
- * up that array's address and clears its header with a small kernel on
- * `stream`.  Every call on a GPU shares that GPU's array: calls that overlap
- * on one GPU (several host threads, or streams not ordered with each other)
- * race and give undefined results; order them on one stream.  Lanes per
- * channel are capped by what the array holds (never a different result).
+ * Its control header (and its FIFOs, if a plan's cannot sit in LDS) live in
+ * a fixed 64 MiB device
+ * array inside the library, one per GPU it runs on, held until the process
+ * ends; the device's first call looks up that array's address and clears its
+ * header with a small kernel on `stream`.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (several host threads, or
+ * streams not ordered with each other) race and give undefined results;
+ * order them on one stream.  FIFOs in the array cap the lanes per channel at
+ * what it holds (never a different result).
  * Errors: arInvalidArgument for bad arguments (nothing enqueued);
- * arInvalidUsage when even one lane per channel does not fit the array (the
- * maximum: nranks x nChannels x FIFO depth x 8 KiB plus 256 bytes per lane)
- * or when AR_PROTO / AR_ALGO force another protocol or algorithm; arHipError
+ * arInvalidUsage when FIFOs must go into the array and even one lane per
+ * channel does not fit (the maximum: nranks x nChannels x FIFO depth x 8 KiB
+ * plus 256 bytes per lane) or when AR_PROTO / AR_ALGO force another protocol
+ * or algorithm; arHipError
  * for HIP failures.  A member that waits longer than the timeout gives up and
  * that call's output is incomplete; with no comm, this path does not report it.
  */

@@ -22,7 +22,8 @@ arInt32, arFloat32, arFloat16, arBfloat16, arUint64 = 0, 1, 2, 3, 4
 arSum, arMax, arMin, arProbe = 0, 1, 2, 3
 (arDebugTimeoutUs, arDebugDeadRank, arDebugLanes, arDebugSimpleSlotKiB, arDebugDirect, arDebugSlots,
  arDebugLaneSets, arDebugLL128SlotKiB, arDebugGroupSpread, arDebugLLChunkBytes,
- arDebugLL128ChunkBytes, arDebugCooperative) = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11
+ arDebugLL128ChunkBytes, arDebugCooperative, arDebugGroupSize, arDebugLdsFifo) = (
+    0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13)
 AR_MAX_RANKS, AR_MAX_CHANNELS = 128, 64
 arFuncAllReduce, arFuncReduceScatter, arFuncAllGather = 0, 1, 2
 FUNC_BY_NAME = {"allreduce": arFuncAllReduce, "reducescatter": arFuncReduceScatter,
@@ -48,7 +49,8 @@ class arPlan_t(ctypes.Structure):
                 ("workgroups", ctypes.c_int), ("threadsPerGroup", ctypes.c_int),
                 ("stepBytes", ctypes.c_int), ("stepPayload", ctypes.c_int), ("nSlots", ctypes.c_int),
                 ("predictedUs", ctypes.c_float), ("modelBytes", ctypes.c_double), ("algo", ctypes.c_int),
-                ("groupLaunch", ctypes.c_int), ("tasksInLaunch", ctypes.c_int)]
+                ("groupLaunch", ctypes.c_int), ("tasksInLaunch", ctypes.c_int), ("ldsFifoBytes", ctypes.c_int),
+                ("deviceBytes", ctypes.c_double)]
 
 
 class ArError(RuntimeError):

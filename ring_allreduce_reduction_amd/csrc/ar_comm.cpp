@@ -150,6 +150,10 @@ struct arComm {
   int forcedLanes;      // 0: automatic
   int laneSetsMax;      // 0: one workgroup per (channel, lane); else at most this many FIFO sets
   int groupSpread;      // debug: a lane's groups on consecutive workgroup ids
+  int groupSizeMax;     // members per workgroup at most (debug; kMaxMembersPerGroup by default)
+  bool ldsFifo;         // Simple rings inside one workgroup may keep their FIFO slots in LDS
+  int ldsSlots;         // depth of such LDS FIFOs
+  int ldsPerBlock;      // LDS bytes a workgroup may use
   int simpleUnroll;     // Simple slot size in KiB (1, 2, 4)
   int ll128Unroll;      // LL128 slot in 1 KiB units (2 or 4); 0: chosen per call
   bool direct;          // Simple all-gather writes outputs directly
@@ -267,6 +271,7 @@ void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* 
                     : func == arFuncReduceScatter ? 3.0 * N * (N - 1.0) * S : 2.0 * N * (N - 1.0) * S;
   out->groupLaunch = -1;
   out->tasksInLaunch = 1;
+  out->deviceBytes = out->modelBytes;
   if (p == nullptr) {
     out->proto = arProtoSimple;
     out->algo = arAlgoRing;
@@ -285,6 +290,11 @@ void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* 
   out->stepPayload = p->slotPayload;
   out->nSlots = p->nSlots;
   out->predictedUs = p->predictedUs;
+  out->deviceBytes = out->modelBytes;
+  if (p->ldsFifo) {
+    out->ldsFifoBytes = p->ldsBytes;
+    out->deviceBytes = func == arFuncAllReduce ? 2.0 * N * S : (N + 1.0) * N * S;
+  }
 }
 
 // The cost model a comm evaluates.  The pages' model prices one GPU per rank;
@@ -455,11 +465,17 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   };
   // About 64 wavefronts per CU: measured best on MI355X (workgroups finish
   // unevenly, so a grid of a few resident rounds balances better than one).
+  // Rings whose FIFOs will sit in LDS (below) hold one or two workgroups per
+  // CU at once, and twice that many lanes measured faster (8 ranks x 256 MiB
+  // fp32, 4 KiB slots at depth 3: 32 lanes 0.818 ms, 64 lanes 0.778 ms).
   // A lane's share of a chunk is at least one slot.  When the chunk is too
   // small to give every lane a full Simple slot, smaller slots are used so
   // that more lanes share the work: the time of a short message is the number
   // of sequential steps per lane, not bandwidth.
-  auto targetFor = [&]() { return (int)((uint64_t)c->numCUs * 64 / ((uint64_t)N * (uint64_t)nch)); };
+  const int gsMax = batch ? kMaxMembersPerGroup : c->groupSizeMax;   // members per workgroup at most
+  const bool ldsPlan = proto == kSimple && !tree && !batch && c->ldsFifo && N <= gsMax && c->ldsPerBlock > 0;
+  const uint64_t wavesPerCU = ldsPlan ? 128 : 64;
+  auto targetFor = [&]() { return (int)((uint64_t)c->numCUs * wavesPerCU / ((uint64_t)N * (uint64_t)nch)); };
   auto lanesFor = [&](int slotPayload) {
     int ln = targetFor();
     // round up: a 120-byte-line LL128 slot never divides a power-of-two chunk
@@ -493,7 +509,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // through the tree a little faster (24 ranks x 4 KiB: 4 lanes of 1 KiB
   // 38.3 us, 2 of 2 KiB 39.1, 1 of 4 KiB 42.9), then more channels.
   bool placed = false;
-  if (tree && !batch && N > kMaxMembersPerGroup && c->forcedLanes == 0) {
+  if (tree && !batch && N > gsMax && c->forcedLanes == 0) {
     const int nchAsked = nch;
     uint64_t bestBytes = 0;
     int bestU = 0, bestGs = 0, bestCh = 0, bestSize = 0;
@@ -502,7 +518,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       for (int ch = nchAsked; ch >= 1; ch /= 2) {
         nch = ch;
         chunkBytes = chunkBytesFor(ch);
-        for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
+        for (int gs = gsMax; gs >= 1; --gs) {
           layout(gs, &nGroups, &groupSize);
           plan->nGroups = nGroups;
           plan->block = groupSize * kWave;
@@ -552,13 +568,13 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // grid is co-resident.  If no grid of one lane per channel can be
   // co-resident, the channels are halved until one can (the plan reports
   // the count that runs).
-  while (!placed && N > kMaxMembersPerGroup) {
+  while (!placed && N > gsMax) {
     setSlot(unroll0);
     // the largest group size whose grid of `ln` lanes per channel is
     // co-resident with slot u (0: none; -1: HIP error)
     auto fit = [&](int u, int ln) -> int {
       if (proto == kSimple) setSlot(u);
-      for (int gs = kMaxMembersPerGroup; gs >= 1; --gs) {
+      for (int gs = gsMax; gs >= 1; --gs) {
         layout(gs, &nGroups, &groupSize);
         plan->nGroups = nGroups;
         plan->block = groupSize * kWave;
@@ -679,6 +695,30 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // time; the per-kind kernel's extra registers cost a grid of several
   // resident rounds more than they save.
   plan->perKind = proto == kLL128 && nGroups == 1 && !batch && plan->grid <= c->numCUs;
+  // A Simple ring inside one workgroup (single calls) keeps its FIFO slots in
+  // LDS: every handoff is then LDS to LDS, and the kernel reads each input
+  // and writes each output once, nothing more.  The counters of such edges
+  // are in LDS already; the static ones take 256 bytes.  The FIFOs get the
+  // comm's LDS depth (3) at the largest slot, at most the planned one, whose
+  // N x depth slots fit a workgroup's LDS (8 ranks: 4 KiB, 96 KiB of LDS; 16
+  // ranks: 2 KiB): measured on MI355X, depth 3 at 4 KiB beats depth 2 at
+  // 8 KiB by 3% at 8 ranks x 256 MiB fp32 and ties at 16 ranks x 512 MiB
+  // bf16; the lane count stays, so a lane's share spans more, smaller slots.
+  plan->ldsFifo = false;
+  plan->ldsBytes = 0;
+  if (ldsPlan && nGroups == 1) {
+    const int d = c->ldsSlots;
+    int u = plan->unroll;
+    while (u > 1 && (int64_t)N * d * slotBytesOf(kSimple, u) + 256 > (int64_t)c->ldsPerBlock) u /= 2;
+    const int64_t bytes = (int64_t)N * d * slotBytesOf(kSimple, u);
+    if (bytes + 256 <= (int64_t)c->ldsPerBlock) {
+      setSlot(u);
+      plan->ldsFifo = true;
+      plan->ldsBytes = (int)bytes;
+      plan->nSlots = d;
+      plan->direct = false;
+    }
+  }
   return arSuccess;
 }
 
@@ -735,6 +775,11 @@ arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arA
   c->simpleUnroll = kSimpleUnrollDefault;
   c->ll128Unroll = 0;   // automatic
   c->direct = true;
+  c->groupSizeMax = kMaxMembersPerGroup;
+  c->ldsFifo = true;
+  c->ldsSlots = e.nSteps > 0 ? e.nSteps : kLdsFifoSlots;
+  if (hipDeviceGetAttribute(&c->ldsPerBlock, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    c->ldsPerBlock = 0;
   // Grouped plans are launched plainly: the planner sizes their grid to what
   // the GPU holds at once, and the cooperative launch call cost 15-20 us per
   // launch, 60-70 us more on some streams (the runtime routes it through a
@@ -831,6 +876,7 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
       c->nSlots[p] = (int)value;
       if (c->fifo[p] != nullptr && provisionFifo(c, p, c->nSlots[p]) != arSuccess) return arHipError;
     }
+    c->ldsSlots = (int)value;
     return arSuccess;
   }
   if (knob == arDebugLaneSets) {
@@ -846,6 +892,16 @@ arResult_t arSetDebug(arComm_t c, arDebugKnob_t knob, int64_t value) {
   if (knob == arDebugCooperative) {
     if (value != 0 && value != 1) return arInvalidArgument;
     c->plainLaunch = value == 0;
+    return arSuccess;
+  }
+  if (knob == arDebugLdsFifo) {
+    if (value != 0 && value != 1) return arInvalidArgument;
+    c->ldsFifo = value != 0;
+    return arSuccess;
+  }
+  if (knob == arDebugGroupSize) {
+    if (value < 0 || value > kMaxMembersPerGroup) return arInvalidArgument;
+    c->groupSizeMax = value == 0 ? kMaxMembersPerGroup : (int)value;
     return arSuccess;
   }
   if (knob == arDebugDirect) {
@@ -1085,8 +1141,10 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   arResult_t r = makePlan(c, func, count, dtype, kop, aligned128, &plan);
   if (r != arSuccess) return r;
   if (!fifosCover(c, plan)) return arInternalError;
-  r = provisionFifo(c, plan.proto, plan.nSlots);   // a protocol this comm has not run yet
-  if (r != arSuccess) return r;
+  if (!plan.ldsFifo) {   // FIFOs in LDS need no device memory
+    r = provisionFifo(c, plan.proto, plan.nSlots);   // a protocol this comm has not run yet
+    if (r != arSuccess) return r;
+  }
 
   KernelArgs a;
   buildArgs(c, plan, func, count, sendbufs, recvbufs, aligned16, &a);
@@ -1109,27 +1167,32 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
 }
 
 
-// Compute units and wall-clock rate of a device, read once per device.
-void deviceInfo(int dev, int* cus, int* clkKHz) {
+// Compute units, wall-clock rate and LDS per workgroup of a device, read
+// once per device.
+void deviceInfo(int dev, int* cus, int* clkKHz, int* ldsPerBlock) {
   static std::mutex mu;
-  static int known[64][2];
+  static int known[64][3];
   static bool have[64];
   std::lock_guard<std::mutex> lock(mu);
   if (dev >= 0 && dev < 64 && have[dev]) {
     *cus = known[dev][0];
     *clkKHz = known[dev][1];
+    *ldsPerBlock = known[dev][2];
     return;
   }
-  int c = 0, k = 0;
+  int c = 0, k = 0, l = 0;
   if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 0;
   if (hipDeviceGetAttribute(&k, hipDeviceAttributeWallClockRate, dev) != hipSuccess || k <= 0) k = 100000;
+  if (hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) l = 0;
   if (dev >= 0 && dev < 64 && c > 0) {
     known[dev][0] = c;
     known[dev][1] = k;
+    known[dev][2] = l;
     have[dev] = true;
   }
   *cus = c;
   *clkKHz = k;
+  *ldsPerBlock = l;
 }
 
 }  // namespace
@@ -1163,8 +1226,11 @@ arResult_t ar::allReduceInScratch(char* scratch, size_t scratchBytes, const void
   c.proto = arProtoSimple;
   c.algo = arAlgoRing;
   c.device = dev;
-  deviceInfo(dev, &c.numCUs, &c.wallClockKHz);
+  deviceInfo(dev, &c.numCUs, &c.wallClockKHz, &c.ldsPerBlock);
   if (c.numCUs <= 0) return arHipError;
+  c.groupSizeMax = kMaxMembersPerGroup;
+  c.ldsFifo = true;   // where the slots fit LDS, the scratch FIFOs go unused
+  c.ldsSlots = e.nSteps > 0 ? e.nSteps : kLdsFifoSlots;
   for (int p = 0; p < 3; ++p) c.nSlots[p] = e.nSteps > 0 ? e.nSteps : kDefaultSlots[p];
   c.sliceBytes = e.sliceBytes;
   c.timeoutUs = e.timeoutUs;
@@ -1177,13 +1243,20 @@ arResult_t ar::allReduceInScratch(char* scratch, size_t scratchBytes, const void
   if (scratchBytes <= kScratchHeaderBytes) return arInvalidUsage;
   const size_t workersFit = (scratchBytes - kScratchHeaderBytes) / workerBytesMax;
   const size_t lanesFit = workersFit / (size_t)nranks;
-  if (lanesFit < (size_t)nChannels) return arInvalidUsage;   // not even one lane per channel fits
   const int lanesDefault = kMaxWorkers / nranks > nChannels ? kMaxWorkers / nranks : nChannels;
-  c.lanesMax = (size_t)lanesDefault < lanesFit ? lanesDefault : (int)lanesFit;
+  c.lanesMax = lanesDefault;
 
+  // The plan arAllReduce makes; if its FIFOs are not in LDS, they go into the
+  // scratch array, with as many lanes as it holds.
   Plan plan;
-  const arResult_t r = makePlan(&c, kCollAllReduce, count, dtype, op, aligned128, &plan);
+  arResult_t r = makePlan(&c, kCollAllReduce, count, dtype, op, aligned128, &plan);
   if (r != arSuccess) return r;
+  if (!plan.ldsFifo) {
+    if (lanesFit < (size_t)nChannels) return arInvalidUsage;   // not even one lane per channel fits
+    c.lanesMax = (size_t)lanesDefault < lanesFit ? lanesDefault : (int)lanesFit;
+    r = makePlan(&c, kCollAllReduce, count, dtype, op, aligned128, &plan);
+    if (r != arSuccess) return r;
+  }
   // the environment can force another protocol or algorithm (AR_PROTO, AR_ALGO)
   if (plan.proto != kSimple || plan.algo != arAlgoRing || plan.nGroups != 1) return arInvalidUsage;
   if (!fifosCover(&c, plan)) return arInternalError;
@@ -1194,8 +1267,8 @@ arResult_t ar::allReduceInScratch(char* scratch, size_t scratchBytes, const void
   c.failedDev = (uint32_t*)(scratch + 256);
   c.fifo[kSimple] = scratch + kScratchHeaderBytes;
   c.conn[kSimple] = (Conn*)(scratch + kScratchHeaderBytes + workers * c.fifoWorkerBytes[kSimple]);
-  if (kScratchHeaderBytes + workers * (c.fifoWorkerBytes[kSimple] + sizeof(Conn)) > scratchBytes)
-    return arInternalError;
+  if (!plan.ldsFifo && kScratchHeaderBytes + workers * (c.fifoWorkerBytes[kSimple] + sizeof(Conn)) > scratchBytes)
+    return arInternalError;   // (FIFOs in LDS leave the scratch FIFOs unused)
 
   KernelArgs a;
   buildArgs(&c, plan, kCollAllReduce, count, sendbufs, recvbufs, aligned16, &a);
@@ -1305,7 +1378,7 @@ arResult_t launchGroup(arComm* c) {
                     : makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan, true, l.size, aggBytes);
     if (r != arSuccess) return r;
     if (!fifosCover(c, l.plan)) return arInternalError;
-    r = provisionFifo(c, l.plan.proto, l.plan.nSlots);
+    r = l.plan.ldsFifo ? arSuccess : provisionFifo(c, l.plan.proto, l.plan.nSlots);
     if (r != arSuccess) return r;
     l.row = rows;
     if (l.size > 1) rows += (size_t)l.size;

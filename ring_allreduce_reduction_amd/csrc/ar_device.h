@@ -382,6 +382,13 @@ __device__ __forceinline__ void stLds(int i, u64 v) {
 __device__ __forceinline__ void stLdsRelease(int i, u64 v) {
   __hip_atomic_store(&ldsCounters()[i], v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// FIFO slots of the edges of a Simple ring that lies inside one workgroup,
+// when they live in LDS too (dynamic LDS sized at launch): member wave w's
+// nSlots slots, written by its predecessor, at w * nSlots * slot bytes.  A
+// handoff is then an LDS store, the counter store and an LDS load, and the
+// ring's device-memory traffic is its inputs and outputs alone.
+extern __shared__ __align__(16) char ldsFifoBase[];
+
 __device__ __forceinline__ bool waitLdsGeq(const KernelArgs& a, int i, u64 target) {
   if (ldLds(i) >= target) return true;
   Waiter w;
@@ -586,7 +593,10 @@ __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
 // receive reads flags and payload in one poll (pollLL128Lines); kernels with
 // edges between workgroups keep the two-phase read, which needs fewer
 // registers (their grids must be co-resident).
-template <int PROTO, int DT, int OP, int U, bool XWG, int KIND, bool LINES = false>
+// LDSQ (Simple, every edge inside the workgroup): the FIFO slots are in LDS;
+// the all-gather goes through them too (never direct), so each member
+// writes its own output once and reads nothing back.
+template <int PROTO, int DT, int OP, int U, bool XWG, int KIND, bool LINES = false, bool LDSQ = false>
 __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt, const char* inp, char* outp,
                                      char* succOutp, long valid) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -603,8 +613,9 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
   // descriptor can carry a pointer, and a work item can be flagged direct.]
   // An edge between workgroups always goes through the FIFO (both of its
   // ends see the same sendAgent / recvAgent, so they agree on it).
-  const bool directSend = PROTO == kSimple && m.direct && !(XWG && m.sendAgent) && hasSend && hasOut;
-  const bool directRecv = PROTO == kSimple && m.direct && !(XWG && m.recvAgent) && hasRecv && hasOut && !hasLocal;
+  const bool directSend = PROTO == kSimple && !LDSQ && m.direct && !(XWG && m.sendAgent) && hasSend && hasOut;
+  const bool directRecv = PROTO == kSimple && !LDSQ && m.direct && !(XWG && m.recvAgent) && hasRecv && hasOut &&
+                          !hasLocal;
   const int lane = m.lane;
 
   // piece geometry of this lane: payload offset, payload bytes, wire offset
@@ -648,9 +659,12 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
                                : !waitLdsGeq(a, m.selfW, m.recvStep + 1))
         return false;
       acquireEdge();
+      const char* ls = ldsFifoBase + ((size_t)m.selfW * (size_t)a.nSlots + m.recvSlot) * SLOT;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (directRecv)   // the predecessor wrote it into my output
+        if (LDSQ)
+          in[u] = payOff[u] < valid ? *(const v4u*)(ls + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
+        else if (directRecv)   // the predecessor wrote it into my output
           in[u] = kind == kRecvCopySend
                       ? loadUser<ESZ, false>(outp + payOff[u], valid - payOff[u], 16, m.aligned)
                       : v4u{0u, 0u, 0u, 0u};
@@ -696,6 +710,11 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
 #pragma unroll
         for (int u = 0; u < U; ++u)
           storeUser<ESZ, false>(succOutp + payOff[u], v[u], valid - payOff[u], 16, m.aligned);
+      } else if (LDSQ) {
+        char* ls = ldsFifoBase + ((size_t)m.succW * (size_t)a.nSlots + m.sendSlot) * SLOT;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (payOff[u] < valid) *(v4u*)(ls + wireOff[u]) = v[u];
       } else if ((XWG && m.sendAgent)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -750,7 +769,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
 
 // One collective of the ring schedule over one member's (channel, lane)
 // share of `count` elements per rank; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL, bool XWG, bool SPEC, bool LINES>
+template <int PROTO, int DT, int OP, int U, int COLL, bool XWG, bool SPEC, bool LINES, bool LDSQ>
 __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, int ch, int k, u64 count,
                                          const char* in, char* out, char* succOut) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -812,7 +831,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
             const u64 b = j * (u64)PAYLOAD;
             if (b >= bytes) break;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES>(a, m, kindRt, in + first + b, out + first + b,
+            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES, LDSQ>(a, m, kindRt, in + first + b, out + first + b,
                                                           succOut + first + b, valid))
               return false;
           }
@@ -867,7 +886,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
           for (u64 j = jb; j < je; ++j) {
             const u64 b = j * (u64)PAYLOAD;
             const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES>(a, m, kindRt, in + inOff + b, out + outOff + b,
+            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES, LDSQ>(a, m, kindRt, in + inOff + b, out + outOff + b,
                                                           succOut + outOff + b, valid))
               return false;
           }
@@ -898,12 +917,12 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
 
 // Every pass of one member: the (channel, lane) pairs of its FIFO set, or
 // the tasks of a batched launch; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool XWG, bool SPEC, bool LINES>
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool XWG, bool SPEC, bool LINES, bool LDSQ = false>
 __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int L, int sets, int lanesTotal,
                                              int perTask, int r, int succ) {
   if (!BATCH) {
     for (int Lp = L; Lp < lanesTotal; Lp += sets) {
-      if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC, LINES>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count,
+      if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC, LINES, LDSQ>(a, m, r, Lp / a.lanes, Lp % a.lanes, a.count,
                                                  (const char*)a.send[r], (char*)a.recv[r], (char*)a.recv[succ]))
         return false;
     }
@@ -916,7 +935,7 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
   const size_t row = 1 + 2 * (size_t)N;
   for (int t = L / perTask; t < a.nTasks; t += a.taskSlots) {
     const u64* d = a.tasks + (size_t)t * row;
-    if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC, LINES>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
+    if (!ringPass<PROTO, DT, OP, U, COLL, XWG, SPEC, LINES, LDSQ>(a, m, r, ch, k, d[0], (const char*)d[1 + r], (char*)d[1 + N + r],
                                                (char*)d[1 + N + succ]))
       return false;
   }
@@ -942,15 +961,22 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // which costs a grid of several resident rounds (8 x 256 MiB: 2.34 -> 2.47
 // ms), so the host picks it for LL128 only when the grid is one workgroup per
 // CU at most.
-template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG, bool PERKIND = ONEWG>
+//
+// LDSQ (Simple, ONEWG, single calls): the FIFO slots are in LDS (the launch
+// gives N x nSlots x slot bytes of dynamic LDS), every counter starts at step
+// 0 and nothing is published when the call ends: no state of these edges
+// outlives the workgroup, and the comm's device FIFOs and counters are not
+// touched (they keep tail == head for whatever ran before or runs after).
+template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG, bool PERKIND = ONEWG, bool LDSQ = false>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
+  static_assert(!LDSQ || (PROTO == kSimple && ONEWG && !BATCH), "LDS FIFOs: Simple rings inside one workgroup");
   // The 8 KiB slot kernels read the wavefront index through readfirstlane,
   // so every per-member value (pointers, counters, rank, channel) lives in
   // scalar registers: that keeps them at 101-120 VGPRs instead of spilling.
   // Smaller slots keep the plain index: with their register room, per-member
   // state in VGPRs measured faster on short messages (the CU's scalar unit
   // is shared by all of its wavefronts' polling loops).
-  const int wave = U == 8 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
+  const int wave = (U == 8 || LDSQ) ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
   __builtin_amdgcn_s_setprio(kWorkPrio);
   const int N = a.nranks;
   const int perTask = a.nChannels * a.lanes;
@@ -986,12 +1012,12 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   m.selfW = wave;
   m.succW = succ - g * a.groupSize;   // used only when the successor shares the workgroup
   m.aligned = a.aligned16 != 0;
-  m.direct = a.direct != 0;
+  m.direct = !LDSQ && a.direct != 0;
   // counters carry over from earlier calls (tail == head at call boundaries,
   // unless a member of an earlier call gave up: then nothing runs); with
-  // freshSteps every edge is in LDS and starts at step 0 instead
-  const bool carry = live && a.freshSteps == 0;
-  const u32 failed = carry ? callFailed(a) : 0u;
+  // freshSteps or LDS FIFOs every edge is in LDS and starts at step 0 instead
+  const bool carry = live && a.freshSteps == 0 && !LDSQ;
+  const u32 failed = (LDSQ ? live : carry) ? callFailed(a) : 0u;
   m.recvStep = carry ? ldCounter(&m.self->head, true) : 0;
   m.sendStep = carry ? ldCounter(&m.succ->tail, true) : 0;
   m.succHead = 0;
@@ -1015,13 +1041,14 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
              : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, false, false>(a, m, L, sets, lanesTotal, perTask, r,
                                                                                 succ);
   } else {
-    ok = memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC, LINES>(a, m, L, sets, lanesTotal, perTask, r, succ);
+    ok = memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC, LINES, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
+                                                                             succ);
   }
   if (!ok) return;
   // Publish what only LDS (an edge inside the workgroup) or the LL / LL128
   // flags (which never touch the tail counter per slot) have counted, so the
   // next call starts both ends of every FIFO at the same step.
-  if (m.lane == 0 && a.freshSteps == 0) {
+  if (m.lane == 0 && a.freshSteps == 0 && !LDSQ) {
     if (!(GROUPED && m.recvAgent)) stRelaxed64(&m.self->head, m.recvStep, true);
     if (PROTO != kSimple || !(GROUPED && m.sendAgent)) stRelaxed64(&m.succ->tail, m.sendStep, true);
   }
@@ -1425,18 +1452,19 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
 
 // The ring kernel for one collective, element type and op (AllGather has no
 // arithmetic: one kernel per element size).
-template <int PROTO, int U, int COLL, bool BATCH, bool ONEWG = false, bool PERKIND = ONEWG>
+template <int PROTO, int U, int COLL, bool BATCH, bool ONEWG = false, bool PERKIND = ONEWG, bool LDSQ = false>
 KernelFn pickRing(int dtype, int op) {
   if (COLL == kCollAllGather) {
     switch (dtype) {
-      case arInt32: case arFloat32: return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH, ONEWG, PERKIND>;
+      case arInt32: case arFloat32:
+        return ringAllReduceKernel<PROTO, arInt32, arSum, U, COLL, BATCH, ONEWG, PERKIND, LDSQ>;
       case arFloat16: case arBfloat16:
-        return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH, ONEWG, PERKIND>;
-      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH, ONEWG, PERKIND>;
+        return ringAllReduceKernel<PROTO, arBfloat16, arSum, U, COLL, BATCH, ONEWG, PERKIND, LDSQ>;
+      case arUint64: return ringAllReduceKernel<PROTO, arUint64, arProbe, U, COLL, BATCH, ONEWG, PERKIND, LDSQ>;
     }
     return nullptr;
   }
-#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH, ONEWG, PERKIND>
+#define AR_RING(DT, OP) ringAllReduceKernel<PROTO, DT, OP, U, COLL, BATCH, ONEWG, PERKIND, LDSQ>
   switch (dtype) {
     case arInt32: return op == arSum ? AR_RING(arInt32, arSum) : op == arMax ? AR_RING(arInt32, arMax)
                        : op == arMin ? AR_RING(arInt32, arMin) : nullptr;
@@ -1475,8 +1503,20 @@ KernelFn pickTree(int dtype, int op) {
 // has one slot geometry, LL128 two (2 KiB, and 4 KiB for single calls).
 template <int COLL, bool BATCH>
 KernelFn pickRingSimple(const Plan& plan, int dtype, int op) {
-  // rings inside one workgroup get the instantiation compiled for them
+  // rings inside one workgroup get the instantiation compiled for them, with
+  // FIFO slots in LDS when the plan says so (single calls)
   const bool one = plan.nGroups == 1;
+  if constexpr (!BATCH) {
+    if (one && plan.ldsFifo) {
+      switch (plan.unroll) {
+        case 1: return pickRing<kSimple, 1, COLL, false, true, true, true>(dtype, op);
+        case 2: return pickRing<kSimple, 2, COLL, false, true, true, true>(dtype, op);
+        case 4: return pickRing<kSimple, 4, COLL, false, true, true, true>(dtype, op);
+        case 8: return pickRing<kSimple, 8, COLL, false, true, true, true>(dtype, op);
+      }
+      return nullptr;
+    }
+  }
   switch (plan.unroll) {
     case 1: return one ? pickRing<kSimple, 1, COLL, BATCH, true>(dtype, op) : pickRing<kSimple, 1, COLL, BATCH>(dtype, op);
     case 2: return one ? pickRing<kSimple, 2, COLL, BATCH, true>(dtype, op) : pickRing<kSimple, 2, COLL, BATCH>(dtype, op);

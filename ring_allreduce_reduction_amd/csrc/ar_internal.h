@@ -18,6 +18,7 @@ constexpr int kMaxWorkers = 32768;        // (rank, lane) wavefronts a comm prov
 // fastest (the smaller live footprint outweighs the lost slack).
 constexpr int kDefaultSlots[3] = {8, 8, 2};
 constexpr int kMaxSlots = 8;              // FIFO depth provisioned per worker
+constexpr int kLdsFifoSlots = 3;          // depth of FIFOs kept in LDS
 
 // One ring member is one wavefront.  Per FIFO slot ("step") a wavefront moves
 // `unroll` pieces per lane:
@@ -138,6 +139,8 @@ struct Plan {
   bool cooperative = false;   // the whole grid must be co-resident (rings / trees cut into workgroups)
   bool launchCoop = false;    // launched with the cooperative launch call (else a plain launch)
   bool perKind = false;       // single-workgroup LL128 rings: steps compiled per kind (small grids)
+  bool ldsFifo = false;       // single-workgroup Simple rings, single calls: FIFO slots in LDS
+  int ldsBytes = 0;           // dynamic LDS per workgroup (N x nSlots x slot bytes with ldsFifo)
   float predictedUs = 0.0f;
 };
 

@@ -36,9 +36,10 @@ hipError_t launchRing(const Plan& plan, int dtype, int op, const KernelArgs& arg
     return hipErrorInvalidValue;   // that kernel has no cross-workgroup edges
   if (plan.launchCoop) {
     void* params[] = {(void*)&args};
-    return hipLaunchCooperativeKernel((const void*)fn, dim3(plan.grid), dim3(plan.block), params, 0, stream);
+    return hipLaunchCooperativeKernel((const void*)fn, dim3(plan.grid), dim3(plan.block), params,
+                                      (unsigned)plan.ldsBytes, stream);
   }
-  hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.block), 0, stream, args);
+  hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.block), (unsigned)plan.ldsBytes, stream, args);
   return hipGetLastError();
 }
 
@@ -52,8 +53,8 @@ hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bo
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   static std::mutex mu;
-  static std::map<std::tuple<const void*, int, int>, int> known;
-  const auto key = std::make_tuple((const void*)fn, plan.block, dev);
+  static std::map<std::tuple<const void*, int, int, int>, int> known;
+  const auto key = std::make_tuple((const void*)fn, plan.block, plan.ldsBytes, dev);
   {
     std::lock_guard<std::mutex> lock(mu);
     auto it = known.find(key);
@@ -63,7 +64,7 @@ hipError_t ringKernelOccupancy(const Plan& plan, int coll, int dtype, int op, bo
     }
   }
   int n = 0;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, plan.block, 0);
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, plan.block, (size_t)plan.ldsBytes);
   if (err != hipSuccess) return err;
   std::lock_guard<std::mutex> lock(mu);
   known[key] = n;

@@ -63,11 +63,15 @@ def _kernel(kernels, tmpl):
 
 
 def test_headline_kernel_fits_without_spills(kernels):
-    # ring, Simple, fp32, Sum, 8 KiB slot, AllReduce, single call
-    (name,) = _kernel(kernels, "ringAllReduceKernelILi2ELi1ELi0ELi8ELi0ELb0E")
-    k = kernels[name]
-    assert k["private_segment_fixed_size"] == 0 and k["vgpr_spill_count"] == 0
-    assert k["vgpr_count"] <= 128   # 16 wavefronts of a workgroup fit a CU's register file
+    # ring, Simple, fp32, Sum, 4 and 8 KiB slots, AllReduce, single call: FIFOs in
+    # device memory and in LDS
+    names = _kernel(kernels, "ringAllReduceKernelILi2ELi1ELi0ELi8ELi0ELb0E")
+    names += _kernel(kernels, "ringAllReduceKernelILi2ELi1ELi0ELi4ELi0ELb0ELb1ELb1ELb1E")
+    assert len(names) == 3
+    for name in names:
+        k = kernels[name]
+        assert k["private_segment_fixed_size"] == 0 and k["vgpr_spill_count"] == 0, name
+        assert k["vgpr_count"] <= 128, name   # 16 wavefronts of a workgroup fit a CU's register file
 
 
 def test_no_spills_on_the_fp32_int32_allreduce_paths(kernels):
