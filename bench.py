@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--sweep-max-log2", type=int, default=28)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--lanes", type=int, default=0, help="force wavefronts per (rank, channel)")
+    ap.add_argument("--no-lds-fifo", action="store_true",
+                    help="keep every FIFO slot in device memory (arDebugLdsFifo 0), for comparison")
     ap.add_argument("--explore", default="", help="'nch1,nch2:lanes1,lanes2' grid of configurations")
     ap.add_argument("--coll", default="allreduce", choices=["allreduce", "reducescatter", "allgather"],
                     help="collective to time; for the two halves --count is the per-rank block "
@@ -172,6 +174,8 @@ def main():
     comm = B.Comm(N, args.nchannels, args.proto, args.algo)
     if args.lanes:
         B.arSetDebug(comm.handle, B.arDebugLanes, args.lanes)
+    if args.no_lds_fifo:
+        B.arSetDebug(comm.handle, B.arDebugLdsFifo, 0)
     if args.explore:
         return explore(args, B, torch, comm, sends, recvs, count, dtype, N, S)
     plan = comm.plan(count, dtype)
@@ -978,12 +982,15 @@ def group_sweep(args, B, torch, np):
     sends = [torch.rand(count, device="cuda") * 2 - 1 for _ in range(N)]
     recvs = [torch.empty_like(x) for x in sends]
     comm = B.Comm(N, args.nchannels, "simple", args.algo if args.algo != "auto" else "ring")
+    if args.no_lds_fifo:
+        B.arSetDebug(comm.handle, B.arDebugLdsFifo, 0)
     for proto in ["simple", "ll", "ll128"]:
         comm.set_config(proto, args.nchannels)
         rows, times = [], []
         for gs in sizes:
             B.arSetDebug(comm.handle, B.arDebugGroupSize, gs)
-            row = {"nranks": N, "bytes": S, "algo": args.algo, "proto": proto, "gsMax": gs}
+            row = {"nranks": N, "bytes": S, "algo": args.algo, "proto": proto, "gsMax": gs,
+                   "ldsFifo": not args.no_lds_fifo}
             try:
                 plan = comm.plan(count, "float32")
                 row.update({"nch": plan["nChannels"], "lanes": plan["lanesPerChannel"],

@@ -475,6 +475,15 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   const int gsMax = batch ? kMaxMembersPerGroup : c->groupSizeMax;   // members per workgroup at most
   const bool ldsPlan = proto == kSimple && !tree && !batch && c->ldsFifo && N <= gsMax && c->ldsPerBlock > 0;
   const uint64_t wavesPerCU = ldsPlan ? 128 : 64;
+  // A Simple ring cut into workgroups keeps the slots of the edges inside each
+  // group in that group's LDS (the edges between groups keep device FIFOs),
+  // at the comm's Simple depth; the co-residency checks below count that LDS.
+  const bool ldsGrouped = proto == kSimple && !tree && !batch && c->ldsFifo && N > gsMax && c->ldsPerBlock > 0;
+  auto groupLds = [&](int members) {
+    const int64_t bytes = (int64_t)members * plan->nSlots * plan->slotBytes;
+    plan->ldsFifo = ldsGrouped && bytes + 256 <= (int64_t)c->ldsPerBlock;
+    plan->ldsBytes = plan->ldsFifo ? (int)bytes : 0;
+  };
   auto targetFor = [&]() { return (int)((uint64_t)c->numCUs * wavesPerCU / ((uint64_t)N * (uint64_t)nch)); };
   auto lanesFor = [&](int slotPayload) {
     int ln = targetFor();
@@ -578,6 +587,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
         layout(gs, &nGroups, &groupSize);
         plan->nGroups = nGroups;
         plan->block = groupSize * kWave;
+        groupLds(groupSize);
         int perCU = 0;
         if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return -1;
         if ((int64_t)perCU * c->numCUs >= (int64_t)((nch * ln + 7) / 8) * 8 * nGroups) return 1;
@@ -699,16 +709,22 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // LDS: every handoff is then LDS to LDS, and the kernel reads each input
   // and writes each output once, nothing more.  The counters of such edges
   // are in LDS already; the static ones take 256 bytes.  The FIFOs get the
-  // comm's LDS depth (3) at the largest slot, at most the planned one, whose
-  // N x depth slots fit a workgroup's LDS (8 ranks: 4 KiB, 96 KiB of LDS; 16
-  // ranks: 2 KiB): measured on MI355X, depth 3 at 4 KiB beats depth 2 at
-  // 8 KiB by 3% at 8 ranks x 256 MiB fp32 and ties at 16 ranks x 512 MiB
-  // bf16; the lane count stays, so a lane's share spans more, smaller slots.
+  // comm's LDS depth (3) at the largest slot, at most the planned one and
+  // 4 KiB, whose N x depth slots fit a workgroup's LDS (8 ranks: 4 KiB, 96
+  // KiB of LDS; 16 ranks: 2 KiB): measured on MI355X, depth 3 at 4 KiB beats
+  // depth 2 at 8 KiB by 3% at 8 ranks x 256 MiB fp32 and ties at 16 ranks x
+  // 512 MiB bf16, and 8 KiB gains nothing where it fits (4 ranks x 8 MiB);
+  // the lane count stays, so a lane's share spans more, smaller slots.
+  if (ldsGrouped && nGroups > 1) {
+    groupLds(groupSize);   // as the co-residency check above counted it
+    if (plan->ldsFifo) plan->direct = false;
+    return arSuccess;
+  }
   plan->ldsFifo = false;
   plan->ldsBytes = 0;
   if (ldsPlan && nGroups == 1) {
     const int d = c->ldsSlots;
-    int u = plan->unroll;
+    int u = plan->unroll < kGroupedSimpleUnrollMax ? plan->unroll : kGroupedSimpleUnrollMax;
     while (u > 1 && (int64_t)N * d * slotBytesOf(kSimple, u) + 256 > (int64_t)c->ldsPerBlock) u /= 2;
     const int64_t bytes = (int64_t)N * d * slotBytesOf(kSimple, u);
     if (bytes + 256 <= (int64_t)c->ldsPerBlock) {

@@ -593,9 +593,10 @@ __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
 // receive reads flags and payload in one poll (pollLL128Lines); kernels with
 // edges between workgroups keep the two-phase read, which needs fewer
 // registers (their grids must be co-resident).
-// LDSQ (Simple, every edge inside the workgroup): the FIFO slots are in LDS;
-// the all-gather goes through them too (never direct), so each member
-// writes its own output once and reads nothing back.
+// LDSQ (Simple): the FIFO slots of the edges inside the workgroup are in
+// LDS (an edge between workgroups keeps its device FIFO); the all-gather
+// goes through them too (never direct), so each member writes its own
+// output once and reads nothing back.
 template <int PROTO, int DT, int OP, int U, bool XWG, int KIND, bool LINES = false, bool LDSQ = false>
 __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt, const char* inp, char* outp,
                                      char* succOutp, long valid) {
@@ -662,7 +663,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
       const char* ls = ldsFifoBase + ((size_t)m.selfW * (size_t)a.nSlots + m.recvSlot) * SLOT;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (LDSQ)
+        if (LDSQ && !(XWG && m.recvAgent))
           in[u] = payOff[u] < valid ? *(const v4u*)(ls + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
         else if (directRecv)   // the predecessor wrote it into my output
           in[u] = kind == kRecvCopySend
@@ -710,7 +711,7 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
 #pragma unroll
         for (int u = 0; u < U; ++u)
           storeUser<ESZ, false>(succOutp + payOff[u], v[u], valid - payOff[u], 16, m.aligned);
-      } else if (LDSQ) {
+      } else if (LDSQ && !(XWG && m.sendAgent)) {
         char* ls = ldsFifoBase + ((size_t)m.succW * (size_t)a.nSlots + m.sendSlot) * SLOT;
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -962,14 +963,18 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // ms), so the host picks it for LL128 only when the grid is one workgroup per
 // CU at most.
 //
-// LDSQ (Simple, ONEWG, single calls): the FIFO slots are in LDS (the launch
-// gives N x nSlots x slot bytes of dynamic LDS), every counter starts at step
-// 0 and nothing is published when the call ends: no state of these edges
-// outlives the workgroup, and the comm's device FIFOs and counters are not
-// touched (they keep tail == head for whatever ran before or runs after).
+// LDSQ (Simple, single calls): the FIFO slots of the edges inside a
+// workgroup are in LDS (the launch gives members x nSlots x slot bytes of
+// dynamic LDS).  With ONEWG too, every counter starts at step 0 and nothing
+// is published when the call ends: no state of these edges outlives the
+// workgroup, and the comm's device FIFOs and counters are not touched (they
+// keep tail == head for whatever ran before or runs after).  A ring cut into
+// workgroups keeps the usual carried counters (its edges between workgroups
+// need them); only the slots of the edges inside a group move.
 template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG, bool PERKIND = ONEWG, bool LDSQ = false>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
-  static_assert(!LDSQ || (PROTO == kSimple && ONEWG && !BATCH), "LDS FIFOs: Simple rings inside one workgroup");
+  static_assert(!LDSQ || (PROTO == kSimple && !BATCH), "LDS FIFOs: Simple single calls");
+  constexpr bool FRESH = LDSQ && ONEWG;   // no counter carries over
   // The 8 KiB slot kernels read the wavefront index through readfirstlane,
   // so every per-member value (pointers, counters, rank, channel) lives in
   // scalar registers: that keeps them at 101-120 VGPRs instead of spilling.
@@ -1016,8 +1021,8 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // counters carry over from earlier calls (tail == head at call boundaries,
   // unless a member of an earlier call gave up: then nothing runs); with
   // freshSteps or LDS FIFOs every edge is in LDS and starts at step 0 instead
-  const bool carry = live && a.freshSteps == 0 && !LDSQ;
-  const u32 failed = (LDSQ ? live : carry) ? callFailed(a) : 0u;
+  const bool carry = live && a.freshSteps == 0 && !FRESH;
+  const u32 failed = (FRESH ? live : carry) ? callFailed(a) : 0u;
   m.recvStep = carry ? ldCounter(&m.self->head, true) : 0;
   m.sendStep = carry ? ldCounter(&m.succ->tail, true) : 0;
   m.succHead = 0;
@@ -1036,9 +1041,9 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   bool ok;
   if constexpr (GROUPED) {
     ok = m.sendAgent || m.recvAgent
-             ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, true, false, false>(a, m, L, sets, lanesTotal, perTask, r,
+             ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, true, false, false, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
                                                                                succ)
-             : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, false, false>(a, m, L, sets, lanesTotal, perTask, r,
+             : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, false, false, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
                                                                                 succ);
   } else {
     ok = memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC, LINES, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
@@ -1048,7 +1053,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   // Publish what only LDS (an edge inside the workgroup) or the LL / LL128
   // flags (which never touch the tail counter per slot) have counted, so the
   // next call starts both ends of every FIFO at the same step.
-  if (m.lane == 0 && a.freshSteps == 0 && !LDSQ) {
+  if (m.lane == 0 && a.freshSteps == 0 && !FRESH) {
     if (!(GROUPED && m.recvAgent)) stRelaxed64(&m.self->head, m.recvStep, true);
     if (PROTO != kSimple || !(GROUPED && m.sendAgent)) stRelaxed64(&m.succ->tail, m.sendStep, true);
   }
@@ -1512,7 +1517,14 @@ KernelFn pickRingSimple(const Plan& plan, int dtype, int op) {
         case 1: return pickRing<kSimple, 1, COLL, false, true, true, true>(dtype, op);
         case 2: return pickRing<kSimple, 2, COLL, false, true, true, true>(dtype, op);
         case 4: return pickRing<kSimple, 4, COLL, false, true, true, true>(dtype, op);
-        case 8: return pickRing<kSimple, 8, COLL, false, true, true, true>(dtype, op);
+      }
+      return nullptr;
+    }
+    if (plan.ldsFifo) {   // a ring cut into workgroups: LDS slots on the edges inside each
+      switch (plan.unroll) {
+        case 1: return pickRing<kSimple, 1, COLL, false, false, false, true>(dtype, op);
+        case 2: return pickRing<kSimple, 2, COLL, false, false, false, true>(dtype, op);
+        case 4: return pickRing<kSimple, 4, COLL, false, false, false, true>(dtype, op);
       }
       return nullptr;
     }
