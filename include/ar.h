@@ -323,7 +323,10 @@ typedef struct {
   double deviceBytes;   /* device-memory bytes the plan's kernel must move: modelBytes,
                            except with LDS FIFOs, where only the inputs are read and the
                            outputs written (AllReduce 2N*S; ReduceScatter and AllGather
-                           (N+1)*N*S, S the per-rank block) */
+                           (N+1)*N*S, S the per-rank block), plus, for a ring cut into G
+                           workgroups, a slot written and read on each of the G edges
+                           between them per send (AllReduce 4(N-1)*G*S/N; the halves
+                           2(N-1)*G*S) */
 } arPlan_t;
 
 /*

@@ -292,8 +292,14 @@ void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* 
   out->predictedUs = p->predictedUs;
   out->deviceBytes = out->modelBytes;
   if (p->ldsFifo) {
+    // inputs read and outputs written once; a ring cut into G workgroups
+    // also writes and reads a slot on each of its G edges between them at
+    // every send (2N-2 sends of S/N per AllReduce member, N-1 of a block for
+    // the two halves)
     out->ldsFifoBytes = p->ldsBytes;
-    out->deviceBytes = func == arFuncAllReduce ? 2.0 * N * S : (N + 1.0) * N * S;
+    const double G = p->nGroups > 1 ? (double)p->nGroups : 0.0;
+    out->deviceBytes = func == arFuncAllReduce ? 2.0 * N * S + 4.0 * (N - 1.0) * G * S / N
+                                               : (N + 1.0) * N * S + 2.0 * (N - 1.0) * G * S;
   }
 }
 
@@ -579,20 +585,37 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // the count that runs).
   while (!placed && N > gsMax) {
     setSlot(unroll0);
-    // the largest group size whose grid of `ln` lanes per channel is
-    // co-resident with slot u (0: none; -1: HIP error)
+    // the group size for a grid of `ln` lanes per channel with slot u whose
+    // grid is co-resident (0: none; -1: HIP error): the largest one whose
+    // grid is also balanced over the CUs (a multiple of their count, or at
+    // most one workgroup per CU) down to half the largest co-resident size,
+    // else that largest size.  Measured on MI355X (Simple, 1 KiB slots, 64
+    // channels): 72 ranks x 4 MiB in groups of 12 (384 workgroups on 256 CUs)
+    // 417 us, of 9 (512) 393 us; 72 x 1 MiB 386 -> 361 us; 128 ranks x 1 MiB
+    // in 16 (256 workgroups) 594 us against 690 in 12 (352); 24 and 48 ranks
+    // already balanced in 12.
     auto fit = [&](int u, int ln) -> int {
       if (proto == kSimple) setSlot(u);
+      int first = 0;
       for (int gs = gsMax; gs >= 1; --gs) {
         layout(gs, &nGroups, &groupSize);
+        if (first > 0 && 2 * groupSize < first) break;
         plan->nGroups = nGroups;
         plan->block = groupSize * kWave;
         groupLds(groupSize);
         int perCU = 0;
         if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return -1;
-        if ((int64_t)perCU * c->numCUs >= (int64_t)((nch * ln + 7) / 8) * 8 * nGroups) return 1;
+        const int64_t grid = (int64_t)((nch * ln + 7) / 8) * 8 * nGroups;
+        if ((int64_t)perCU * c->numCUs < grid) continue;
+        if (grid <= c->numCUs || grid % c->numCUs == 0) return 1;
+        if (first == 0) first = groupSize;
       }
-      return 0;
+      if (first == 0) return 0;
+      layout(first, &nGroups, &groupSize);
+      plan->nGroups = nGroups;
+      plan->block = groupSize * kWave;
+      groupLds(groupSize);
+      return 1;
     };
     const int uMax = uMax0;
     int found = 0;
