@@ -17,8 +17,21 @@
 #include <new>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "ar_internal.h"
 #include "ar_tune_table.h"
+
+// A ROCTx range around an API call, as the pages mark each API entry with an
+// NVTX range ["NCCL 原始碼解讀：一個 AllReduce 的 GPU 旅程", ch.3 §3.1, ch.6, the
+// ncclAllReduce call chain]: rocprofv3 --marker-trace records one per call
+// (host time of the call: argument checks, planning and the enqueue).
+struct ApiRange {
+  explicit ApiRange(const char* name) { roctxRangePushA(name); }
+  ~ApiRange() { roctxRangePop(); }
+  ApiRange(const ApiRange&) = delete;
+  ApiRange& operator=(const ApiRange&) = delete;
+};
 
 using namespace ar;
 
@@ -780,6 +793,7 @@ const char* arGetErrorString(arResult_t r) {
 }
 
 arResult_t arInit(arComm_t* out, int nranks, int nChannels, arProto_t proto, arAlgo_t algo) {
+  ApiRange range("arInit");
   if (out == nullptr) return arInvalidArgument;
   *out = nullptr;
   if (nranks < 1 || nranks > AR_MAX_RANKS) return arInvalidArgument;
@@ -1496,16 +1510,19 @@ static arResult_t noteGroupError(arResult_t r) {
 
 arResult_t arAllReduce(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t count,
                        arDataType_t dtype, arRedOp_t op, void* stream) {
+  ApiRange range("arAllReduce");
   return noteGroupError(runColl(c, kCollAllReduce, sendbufs, recvbufs, count, dtype, op, stream));
 }
 
 arResult_t arReduceScatter(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t recvcount,
                            arDataType_t dtype, arRedOp_t op, void* stream) {
+  ApiRange range("arReduceScatter");
   return noteGroupError(runColl(c, kCollReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream));
 }
 
 arResult_t arAllGather(arComm_t c, const void* const* sendbufs, void* const* recvbufs, size_t sendcount,
                        arDataType_t dtype, void* stream) {
+  ApiRange range("arAllGather");
   return noteGroupError(runColl(c, kCollAllGather, sendbufs, recvbufs, sendcount, dtype, arSum, stream));
 }
 
@@ -1515,6 +1532,7 @@ arResult_t arGroupStart(void) {
 }
 
 arResult_t arGroupEnd(void) {
+  ApiRange range("arGroupEnd");
   if (tGroupDepth == 0) return arInvalidUsage;   // not in a group
   if (--tGroupDepth > 0) return arSuccess;       // an inner group: the outermost end launches
   arResult_t r = tGroupError;

@@ -287,3 +287,20 @@ def test_ring_eval_unchanged_by_tree(B):
     for nbytes in (64, 1 << 20, 1 << 28):
         a, p, ch, t = B.arTuneEvalAlgo(0, 8, 64, nbytes, MODELS, None, algoMask=1)
         assert (p, ch) == B.arTuneEval(8, 64, nbytes, MODELS)[:2] and a == B.arAlgoRing
+
+
+def test_library_links_roctx_for_api_ranges():
+    """The API entry points carry ROCTx ranges (arInit, arAllReduce,
+    arReduceScatter, arAllGather, arGroupEnd): the library links the ROCTx
+    runtime and names the ranges.  CPU only (readelf and the file's bytes)."""
+    import shutil
+    import subprocess
+    from ring_allreduce_reduction_amd import binding
+    if shutil.which("readelf") is None:
+        import pytest
+        pytest.skip("readelf not found")
+    dyn = subprocess.run(["readelf", "-d", binding.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "librocprofiler-sdk-roctx" in dyn
+    blob = open(binding.LIB_PATH, "rb").read()
+    for name in (b"arInit", b"arAllReduce", b"arReduceScatter", b"arAllGather", b"arGroupEnd"):
+        assert name + b"\x00" in blob
