@@ -81,6 +81,7 @@
  * arithmetic, default MXCSR, so no flush-to-zero).
  */
 #include <stdint.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <string.h>
 
@@ -398,38 +399,52 @@ void ar_oracle_bf16_to_f32(const uint16_t* x, float* y, size_t n) {
 
 /* ---------------- tree AllReduce ------------------------------------------ */
 
-/* Binary tree over ranks 0..nranks-1 [pages: ch.4, ncclGetBtree].  Let `bit` be the
- * lowest set bit of rank (for rank 0: the first power of two >= nranks).
- *  - rank 0 is the root; its only child is bit/2 (none when nranks == 1), and
- *    the pages name that child d1.
- *  - any other rank's parent is rank with `bit` cleared and the next bit up
- *    set; when that is out of range, just rank with `bit` cleared.  It is the
- *    parent's first child (child_type 0) when rank < parent, else its second.
- *  - its children are rank - bit/2 (d0) and rank + h (d1) for the largest h
- *    among bit/2, bit/4, ..., 1 that stays below nranks; a rank whose lowest
- *    bit is 1 has none. */
+/* Binary tree over ranks 0..nranks-1 [pages: ch.4, ncclGetBtree; "NCCL Tree
+ *拓扑介绍", the binary tree drawn over the ranks].  The tree is the in-order
+ * tree of the ranks' binary numbering, built here from that definition over
+ * spans of ranks:
+ *  - rank 0 is the root and has one child, the root of the span [1, nranks)
+ *    (the pages name it d1);
+ *  - the root of a non-empty span [lo, hi) is its rank with the largest lowest
+ *    set bit (the "roundest" number); its first child (d0, child_type 0) is
+ *    the root of [lo, root) and its second (d1, child_type 1) the root of
+ *    [root + 1, hi).
+ * Every rank but 0 is the root of exactly one span, so each query builds the
+ * whole tree (O(nranks), recursion depth log2 nranks) and reads its entry. */
+static int span_root(int lo, int hi) {   /* the rank in [lo, hi) with the largest lowest set bit */
+  int p = 1;
+  while (p * 2 <= hi) p *= 2;            /* from the largest power of two below hi down */
+  for (; p >= 1; p /= 2) {
+    int m = (lo + p - 1) / p * p;        /* the first multiple of p at or above lo */
+    if (m < hi) return m;
+  }
+  return -1;
+}
+
+static int span_tree(int lo, int hi, int parent, int side, int* up, int* d0, int* d1, int* type) {
+  if (lo >= hi) return -1;
+  int r = span_root(lo, hi);
+  up[r] = parent;
+  type[r] = side;
+  d0[r] = span_tree(lo, r, r, 0, up, d0, d1, type);
+  d1[r] = span_tree(r + 1, hi, r, 1, up, d0, d1, type);
+  return r;
+}
+
 int ar_oracle_btree(int nranks, int rank, int* up, int* d0, int* d1, int* child_type) {
   if (nranks < 1 || rank < 0 || rank >= nranks) return -1;
-  int bit = 1;
-  while (bit < nranks && (bit & rank) == 0) bit <<= 1;
-  int u = -1, c0 = -1, c1 = -1, t = 0;
-  if (rank == 0) {
-    if (nranks > 1) c1 = bit >> 1;
-  } else {
-    u = (rank ^ bit) | (bit << 1);
-    if (u >= nranks) u = rank ^ bit;
-    t = rank < u ? 0 : 1;
-    int h = bit >> 1;
-    if (h > 0) {
-      c0 = rank - h;
-      while (h > 0 && rank + h >= nranks) h >>= 1;
-      c1 = h > 0 ? rank + h : -1;
-    }
-  }
-  if (up) *up = u;
-  if (d0) *d0 = c0;
-  if (d1) *d1 = c1;
-  if (child_type) *child_type = t;
+  int* a = (int*)malloc(4 * sizeof(int) * (size_t)nranks);
+  if (a == NULL) return -1;
+  int *u = a, *c0 = a + nranks, *c1 = a + 2 * nranks, *t = a + 3 * nranks;
+  u[0] = -1;
+  c0[0] = -1;
+  t[0] = 0;
+  c1[0] = span_tree(1, nranks, 0, 1, u, c0, c1, t);
+  if (up) *up = u[rank];
+  if (d0) *d0 = c0[rank];
+  if (d1) *d1 = c1[rank];
+  if (child_type) *child_type = rank == 0 ? 0 : t[rank];
+  free(a);
   return 0;
 }
 
