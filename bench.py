@@ -550,7 +550,9 @@ def bench_halves(args, B, gen, torch, np):
                                % (name, N, Bb >> 20, (N * Bb) >> 20), "nranks": N, "block_elems": count,
                    "proto": B.PROTO_NAMES[plan["proto"]], "nChannels": plan["nChannels"],
                    "lanesPerChannel": plan["lanesPerChannel"], "workgroups": plan["workgroups"]},
-        "algbw_GBs": round(algbw, 3), "busbw_GBs": round(busbw, 3), "model_bytes_per_step": model_bytes,
+        "algbw_GBs": round(algbw, 3), "busbw_GBs": round(busbw, 3), "fifo_in_lds": plan["ldsFifoBytes"] > 0,
+        "device_bytes_per_step": plan["deviceBytes"], "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "model_bytes_per_step": model_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": cpu}), flush=True)

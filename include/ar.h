@@ -317,8 +317,8 @@ typedef struct {
   int groupLaunch;      /* arGetGroupPlan: index of the launch (in launch order)
                            that carried this call; -1 for a copy or a single call */
   int tasksInLaunch;    /* collectives sharing that launch (1 unless batched) */
-  int ldsFifoBytes;     /* Simple rings inside one workgroup, single calls: the FIFO slots
-                           live in LDS, this many bytes per workgroup (N x nSlots x
+  int ldsFifoBytes;     /* Simple rings: the FIFO slots of the edges inside a workgroup
+                           live in LDS, this many bytes per workgroup (members x nSlots x
                            stepBytes); 0: FIFO slots in device memory */
   double deviceBytes;   /* device-memory bytes the plan's kernel must move: modelBytes,
                            except with LDS FIFOs, where only the inputs are read and the
@@ -417,9 +417,10 @@ typedef enum {
                                   runtime checks residency and runs such launches one at a time,
                                   at 15-70 us per launch), 0 = plain launch of the same grid
                                   (default; see arAllReduce on residency) */
-  arDebugLdsFifo = 13,         /* 1 (default): Simple rings inside one workgroup keep their FIFO
-                                  slots in LDS when N x depth x slot fits a workgroup's LDS
-                                  (single calls); 0: in device memory */
+  arDebugLdsFifo = 13,         /* 1 (default): Simple rings keep the FIFO slots of their edges
+                                  inside a workgroup in LDS (rings of at most 16 ranks, single
+                                  calls and arGroupEnd's batched launches; rings cut into
+                                  workgroups, single calls); 0: in device memory */
   arDebugGroupSize = 12,       /* at most this many ring or tree members per workgroup, 1..16
                                   (0: 16, the default): a ring or tree longer than this is cut
                                   into groups joined by device-coherent edges, as rings of more

@@ -492,7 +492,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // that more lanes share the work: the time of a short message is the number
   // of sequential steps per lane, not bandwidth.
   const int gsMax = batch ? kMaxMembersPerGroup : c->groupSizeMax;   // members per workgroup at most
-  const bool ldsPlan = proto == kSimple && !tree && !batch && c->ldsFifo && N <= gsMax && c->ldsPerBlock > 0;
+  const bool ldsPlan = proto == kSimple && !tree && c->ldsFifo && N <= gsMax && c->ldsPerBlock > 0;
   const uint64_t wavesPerCU = ldsPlan ? 128 : 64;
   // A Simple ring cut into workgroups keeps the slots of the edges inside each
   // group in that group's LDS (the edges between groups keep device FIFOs),
@@ -741,7 +741,8 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // time; the per-kind kernel's extra registers cost a grid of several
   // resident rounds more than they save.
   plan->perKind = proto == kLL128 && nGroups == 1 && !batch && plan->grid <= c->numCUs;
-  // A Simple ring inside one workgroup (single calls) keeps its FIFO slots in
+  // A Simple ring inside one workgroup (single calls and batched launches,
+  // whose tasks then continue on the workgroup's LDS FIFOs) keeps its slots in
   // LDS: every handoff is then LDS to LDS, and the kernel reads each input
   // and writes each output once, nothing more.  The counters of such edges
   // are in LDS already; the static ones take 256 bytes.  The FIFOs get the

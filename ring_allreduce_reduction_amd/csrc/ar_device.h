@@ -963,8 +963,8 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // ms), so the host picks it for LL128 only when the grid is one workgroup per
 // CU at most.
 //
-// LDSQ (Simple, single calls): the FIFO slots of the edges inside a
-// workgroup are in LDS (the launch gives members x nSlots x slot bytes of
+// LDSQ (Simple; a ring cut into workgroups only in single calls): the FIFO
+// slots of the edges inside a workgroup are in LDS (the launch gives members x nSlots x slot bytes of
 // dynamic LDS).  With ONEWG too, every counter starts at step 0 and nothing
 // is published when the call ends: no state of these edges outlives the
 // workgroup, and the comm's device FIFOs and counters are not touched (they
@@ -973,7 +973,7 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // need them); only the slots of the edges inside a group move.
 template <int PROTO, int DT, int OP, int U, int COLL, bool BATCH, bool ONEWG, bool PERKIND = ONEWG, bool LDSQ = false>
 __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) {
-  static_assert(!LDSQ || (PROTO == kSimple && !BATCH), "LDS FIFOs: Simple single calls");
+  static_assert(!LDSQ || PROTO == kSimple, "LDS FIFOs: Simple");
   constexpr bool FRESH = LDSQ && ONEWG;   // no counter carries over
   // The 8 KiB slot kernels read the wavefront index through readfirstlane,
   // so every per-member value (pointers, counters, rank, channel) lives in
@@ -1511,15 +1511,15 @@ KernelFn pickRingSimple(const Plan& plan, int dtype, int op) {
   // rings inside one workgroup get the instantiation compiled for them, with
   // FIFO slots in LDS when the plan says so (single calls)
   const bool one = plan.nGroups == 1;
-  if constexpr (!BATCH) {
-    if (one && plan.ldsFifo) {
-      switch (plan.unroll) {
-        case 1: return pickRing<kSimple, 1, COLL, false, true, true, true>(dtype, op);
-        case 2: return pickRing<kSimple, 2, COLL, false, true, true, true>(dtype, op);
-        case 4: return pickRing<kSimple, 4, COLL, false, true, true, true>(dtype, op);
-      }
-      return nullptr;
+  if (one && plan.ldsFifo) {   // single calls and batched launches
+    switch (plan.unroll) {
+      case 1: return pickRing<kSimple, 1, COLL, BATCH, true, true, true>(dtype, op);
+      case 2: return pickRing<kSimple, 2, COLL, BATCH, true, true, true>(dtype, op);
+      case 4: return pickRing<kSimple, 4, COLL, BATCH, true, true, true>(dtype, op);
     }
+    return nullptr;
+  }
+  if constexpr (!BATCH) {
     if (plan.ldsFifo) {   // a ring cut into workgroups: LDS slots on the edges inside each
       switch (plan.unroll) {
         case 1: return pickRing<kSimple, 1, COLL, false, false, false, true>(dtype, op);
