@@ -772,6 +772,20 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       plan->direct = false;
     }
   }
+  // A Simple tree inside one workgroup keeps its FIFOs in LDS too: one up and
+  // one down per node (2N), at the comm's depth, with the largest slot (at
+  // most the planned one) that fits beside the tree's 512 bytes of counters.
+  if (tree && proto == kSimple && nGroups == 1 && c->ldsFifo && c->ldsPerBlock > 0 && N <= gsMax) {
+    const int d = plan->nSlots;
+    int u = plan->unroll;
+    while (u > 1 && (int64_t)2 * N * d * slotBytesOf(kSimple, u) + 512 > (int64_t)c->ldsPerBlock) u /= 2;
+    const int64_t bytes = (int64_t)2 * N * d * slotBytesOf(kSimple, u);
+    if (bytes + 512 <= (int64_t)c->ldsPerBlock) {
+      setSlot(u);
+      plan->ldsFifo = true;
+      plan->ldsBytes = (int)bytes;
+    }
+  }
   return arSuccess;
 }
 

@@ -1127,7 +1127,41 @@ struct Edge {
   u64 step;     // next step on this FIFO
   u32 slot;     // step % nSlots
   bool agent;   // the other end is in another workgroup
+  int lds;      // LDS FIFOs (trees inside one workgroup): the FIFO's index
 };
+
+// A tree inside one workgroup with its FIFOs in LDS: every node but the root
+// has one FIFO up to its parent (index 2r) and one down from it (2r + 1),
+// nSlots slots each in the dynamic LDS, tail and head counters in
+// treeLdsCounters (2 per FIFO, at most 16 nodes).
+__device__ __forceinline__ u64* treeLdsCounters() {
+  __shared__ u64 c[2 * 2 * kMaxMembersPerGroup];
+  return c;
+}
+__device__ __forceinline__ u64 ldTreeLds(int i) {
+  u64 v = __hip_atomic_load(&treeLdsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  u32 lo = __builtin_amdgcn_readfirstlane((u32)v);
+  u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ bool waitTreeLdsGeq(const KernelArgs& a, int i, u64 target) {
+  if (ldTreeLds(i) >= target) return true;
+  Waiter w;
+  while (true) {
+    if (!keepWaiting(a, w)) return false;
+    if (ldTreeLds(i) >= target) return true;
+  }
+}
+__device__ __forceinline__ Edge openLdsEdge(int fifoIndex) {
+  Edge e;
+  e.fifo = nullptr;
+  e.conn = nullptr;
+  e.step = 0;
+  e.slot = 0;
+  e.agent = false;
+  e.lds = fifoIndex;
+  return e;
+}
 
 __device__ __forceinline__ Edge openEdge(const KernelArgs& a, size_t worker, bool agent, bool recvEnd) {
   Edge e;
@@ -1160,10 +1194,19 @@ struct Pieces {   // this lane's pieces of one slot (as in the ring's step)
   }
 };
 
-template <int PROTO, int U, bool XWG, bool LINES = false>
+template <int PROTO, int U, bool XWG, bool LINES = false, bool LDSQ = false>
 __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, const Pieces<PROTO, U>& pc, int lane,
                                          long valid, v4u (&in)[U]) {
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
+  if constexpr (LDSQ) {   // Simple, FIFO and counters in LDS
+    if (!waitTreeLdsGeq(a, 2 * e.lds, e.step + 1)) return false;
+    acquireEdge();
+    const char* ls = ldsFifoBase + ((size_t)e.lds * (size_t)a.nSlots + e.slot) * SLOT;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      in[u] = pc.payOff[u] >= valid ? v4u{0u, 0u, 0u, 0u} : *(const v4u*)(ls + pc.wireOff[u]);
+    return true;
+  }
   const char* slot = e.fifo + (size_t)e.slot * SLOT;
   if (PROTO == kSimple) {
     if (!waitGeq(a, &e.conn->tail, e.step + 1, (XWG && e.agent))) return false;
@@ -1196,19 +1239,38 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
   return true;
 }
 
-template <bool XWG>
+template <bool XWG, bool LDSQ = false>
 __device__ __forceinline__ void edgeFinishRecv(const KernelArgs& a, Edge& e, int lane) {
   ++e.step;
-  if (lane == 0) stCounterRelease(&e.conn->head, e.step, (XWG && e.agent));
+  if (lane == 0) {
+    if (LDSQ)
+      __hip_atomic_store(&treeLdsCounters()[2 * e.lds + 1], e.step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+      stCounterRelease(&e.conn->head, e.step, (XWG && e.agent));
+  }
   if (++e.slot == (u32)a.nSlots) e.slot = 0;
 }
 
-template <int PROTO, int U, bool XWG>
+template <int PROTO, int U, bool XWG, bool LDSQ = false>
 __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pieces<PROTO, U>& pc, int lane,
                                          long valid, const v4u (&v)[U]) {
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
   // slot step % nSlots is free once the receiver consumed step - nSlots
   const u64 need = e.step + 1 > (u64)a.nSlots ? e.step + 1 - (u64)a.nSlots : 0;
+  if constexpr (LDSQ) {   // Simple, FIFO and counters in LDS
+    if (!waitTreeLdsGeq(a, 2 * e.lds + 1, need)) return false;
+    acquireEdge();
+    char* ls = ldsFifoBase + ((size_t)e.lds * (size_t)a.nSlots + e.slot) * SLOT;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (pc.payOff[u] < valid) *(v4u*)(ls + pc.wireOff[u]) = v[u];
+    releaseEdge(false);   // the LDS stores before the counter
+    if (lane == 0)
+      __hip_atomic_store(&treeLdsCounters()[2 * e.lds], e.step + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ++e.step;
+    if (++e.slot == (u32)a.nSlots) e.slot = 0;
+    return true;
+  }
   if (!waitGeq(a, &e.conn->head, need, (XWG && e.agent))) return false;
   acquireEdge();
   char* slot = e.fifo + (size_t)e.slot * SLOT;
@@ -1272,7 +1334,8 @@ struct TreeNode {
 // has d1 only; every other node with children has d0, and maybe d1.
 // kRoleAtRunTime: read it from the node.
 constexpr int kRoleD0 = 1, kRoleD1 = 2, kRoleParent = 4, kRoleAtRunTime = -1;
-template <int PROTO, int DT, int OP, int U, bool XWG, int ROLE = kRoleAtRunTime, bool LINES = false>
+template <int PROTO, int DT, int OP, int U, bool XWG, int ROLE = kRoleAtRunTime, bool LINES = false,
+          bool LDSQ = false>
 __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int ch, int k, int lane, u64 count,
                                          const char* inBase, char* outBase) {
   constexpr int ESZ = DT == arUint64 ? 8 : (DT == arFloat16 || DT == arBfloat16) ? 2 : 4;
@@ -1316,8 +1379,8 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
         for (int i = 0; i < 2; ++i) {
           if (!hasChild(i)) continue;
           v4u got[U];
-          if (!edgeRecv<PROTO, U, XWG, LINES>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
-          edgeFinishRecv<XWG>(a, nd.fromChild[i], lane);
+          if (!edgeRecv<PROTO, U, XWG, LINES, LDSQ>(a, nd.fromChild[i], pc, lane, valid, got)) return false;
+          edgeFinishRecv<XWG, LDSQ>(a, nd.fromChild[i], lane);
 #pragma unroll
           for (int u = 0; u < U; ++u) acc[u] = have ? combine<DT, OP>(acc[u], got[u]) : got[u];
           have = true;
@@ -1326,14 +1389,14 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
         for (int u = 0; u < U; ++u) acc[u] = combine<DT, OP>(acc[u], x[u]);
       }
       if (hasUp) {
-        if (!edgeSend<PROTO, U, XWG>(a, nd.toParent, pc, lane, valid, acc)) return false;
+        if (!edgeSend<PROTO, U, XWG, LDSQ>(a, nd.toParent, pc, lane, valid, acc)) return false;
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u)
           storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          if (hasChild(i) && !edgeSend<PROTO, U, XWG>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
+          if (hasChild(i) && !edgeSend<PROTO, U, XWG, LDSQ>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
       }
     }
     if (!hasUp) continue;
@@ -1341,14 +1404,14 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
     for (u64 j = jb; j < je; ++j) {
       const u64 b = j * (u64)PAYLOAD;
       const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-      if (!edgeRecv<PROTO, U, XWG, LINES>(a, nd.fromParent, pc, lane, valid, acc)) return false;
-      edgeFinishRecv<XWG>(a, nd.fromParent, lane);
+      if (!edgeRecv<PROTO, U, XWG, LINES, LDSQ>(a, nd.fromParent, pc, lane, valid, acc)) return false;
+      edgeFinishRecv<XWG, LDSQ>(a, nd.fromParent, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         storeUser<ESZ, true>(out + b + pc.payOff[u], acc[u], valid - pc.payOff[u], pc.payBytes[u], aligned);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (hasChild(i) && !edgeSend<PROTO, U, XWG>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
+        if (hasChild(i) && !edgeSend<PROTO, U, XWG, LDSQ>(a, nd.toChild[i], pc, lane, valid, acc)) return false;
     }
   }
   return true;
@@ -1356,17 +1419,19 @@ __device__ __forceinline__ bool treePass(const KernelArgs& a, TreeNode& nd, int 
 
 // Every pass of one tree member: its one call, or the tasks of a batched
 // launch; false when a wait gave up.
-template <int PROTO, int DT, int OP, int U, bool BATCH, bool XWG, int ROLE = kRoleAtRunTime, bool LINES = false>
+template <int PROTO, int DT, int OP, int U, bool BATCH, bool XWG, int ROLE = kRoleAtRunTime, bool LINES = false,
+          bool LDSQ = false>
 __device__ __forceinline__ bool treePasses(const KernelArgs& a, TreeNode& nd, int L, int perTask, int ch, int k,
                                            int lane, int r) {
-  if (!BATCH) return treePass<PROTO, DT, OP, U, XWG, ROLE, LINES>(a, nd, ch, k, lane, a.count, (const char*)a.send[r],
-                                                           (char*)a.recv[r]);
+  if (!BATCH)
+    return treePass<PROTO, DT, OP, U, XWG, ROLE, LINES, LDSQ>(a, nd, ch, k, lane, a.count, (const char*)a.send[r],
+                                                             (char*)a.recv[r]);
   const int N = a.nranks;
   const size_t row = 1 + 2 * (size_t)N;
   for (int i = L / perTask; i < a.nTasks; i += a.taskSlots) {
     const u64* d = a.tasks + (size_t)i * row;
-    if (!treePass<PROTO, DT, OP, U, XWG, ROLE, LINES>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r],
-                                                     (char*)d[1 + N + r]))
+    if (!treePass<PROTO, DT, OP, U, XWG, ROLE, LINES, LDSQ>(a, nd, ch, k, lane, d[0], (const char*)d[1 + r],
+                                                           (char*)d[1 + N + r]))
       return false;
   }
   return true;
@@ -1378,10 +1443,16 @@ __device__ __forceinline__ bool treePasses(const KernelArgs& a, TreeNode& nd, in
 // ONEWG: every tree of the launch lies inside one workgroup (the host picks
 // this instantiation for such plans only); the Simple kernels then also
 // compile a member's pass for its role (parent or root, number of children).
-template <int PROTO, int DT, int OP, int U, bool BATCH, bool ONEWG>
+//
+// LDSQ (Simple, ONEWG): every FIFO of the tree and its counters are in LDS
+// (the launch gives 2N x nSlots x slot bytes of dynamic LDS); the counters
+// start at 0 in each launch and the comm's device FIFOs are not touched.
+template <int PROTO, int DT, int OP, int U, bool BATCH, bool ONEWG, bool LDSQ = false>
 __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
+  static_assert(!LDSQ || (PROTO == kSimple && ONEWG), "LDS FIFOs: Simple trees inside one workgroup");
   // as in the ring kernel: scalar member state for the largest (4 KiB) slot
-  const int wave = U == 4 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
+  const int wave = (U == 4 || LDSQ) ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave)
+                                    : (int)(threadIdx.x / kWave);
   __builtin_amdgcn_s_setprio(kWorkPrio);
   const int lane = threadIdx.x % kWave;
   const int N = a.nranks;
@@ -1390,8 +1461,13 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
 
   int L, g;   // (lane id, group), as in the ring kernel
   laneAndGroup(a, L, g);
-  if (L >= lanesTotal) return;
   const int r = g * a.groupSize + wave;
+  if constexpr (LDSQ) {   // every wavefront clears the counters and meets the others before any returns
+    for (int i = (int)threadIdx.x; i < 4 * kMaxMembersPerGroup; i += (int)blockDim.x)
+      __hip_atomic_store(&treeLdsCounters()[i], (u64)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+  }
+  if (L >= lanesTotal) return;
   if (r >= N || r == a.deadRank) return;
   // an earlier call left its edges mid-call when a member gave up
   if (callFailed(a) != 0) return;
@@ -1405,25 +1481,39 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
   dtreeNode(N, r, t, nd.up, nd.d[0], nd.d[1]);
   auto worker = [&](int node, int edge) { return ((size_t)L * N + node) * 3 + edge; };
   auto cross = [&](int node) { return node / a.groupSize != g; };
+  if constexpr (LDSQ) {   // node x's FIFO up is 2x, its FIFO down 2x + 1
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (nd.d[i] >= 0) {
-      nd.fromChild[i] = openEdge(a, worker(r, i), cross(nd.d[i]), true);
-      nd.toChild[i] = openEdge(a, worker(nd.d[i], 2), cross(nd.d[i]), false);
+    for (int i = 0; i < 2; ++i) {
+      if (nd.d[i] >= 0) {
+        nd.fromChild[i] = openLdsEdge(2 * nd.d[i]);
+        nd.toChild[i] = openLdsEdge(2 * nd.d[i] + 1);
+      }
     }
-  }
-  if (nd.up >= 0) {
-    int pu, p0, p1;
-    dtreeNode(N, nd.up, t, pu, p0, p1);
-    nd.fromParent = openEdge(a, worker(r, 2), cross(nd.up), true);
-    nd.toParent = openEdge(a, worker(nd.up, r == p0 ? 0 : 1), cross(nd.up), false);
+    if (nd.up >= 0) {
+      nd.fromParent = openLdsEdge(2 * r + 1);
+      nd.toParent = openLdsEdge(2 * r);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (nd.d[i] >= 0) {
+        nd.fromChild[i] = openEdge(a, worker(r, i), cross(nd.d[i]), true);
+        nd.toChild[i] = openEdge(a, worker(nd.d[i], 2), cross(nd.d[i]), false);
+      }
+    }
+    if (nd.up >= 0) {
+      int pu, p0, p1;
+      dtreeNode(N, nd.up, t, pu, p0, p1);
+      nd.fromParent = openEdge(a, worker(r, 2), cross(nd.up), true);
+      nd.toParent = openEdge(a, worker(nd.up, r == p0 ? 0 : 1), cross(nd.up), false);
+    }
   }
 
   bool ok;
   if constexpr (ONEWG && PROTO == kSimple) {
     const int role = (nd.up >= 0 ? kRoleParent : 0) | (nd.d[0] >= 0 ? kRoleD0 : 0) | (nd.d[1] >= 0 ? kRoleD1 : 0);
     switch (role) {
-#define AR_ROLE(R) treePasses<PROTO, DT, OP, U, BATCH, false, R>(a, nd, L, perTask, ch, k, lane, r)
+#define AR_ROLE(R) treePasses<PROTO, DT, OP, U, BATCH, false, R, false, LDSQ>(a, nd, L, perTask, ch, k, lane, r)
       case kRoleParent: ok = AR_ROLE(kRoleParent); break;                                      // leaf
       case kRoleParent | kRoleD0: ok = AR_ROLE(kRoleParent | kRoleD0); break;                  // one child
       case kRoleParent | kRoleD0 | kRoleD1: ok = AR_ROLE(kRoleParent | kRoleD0 | kRoleD1); break;
@@ -1485,9 +1575,9 @@ KernelFn pickRing(int dtype, int op) {
   return nullptr;
 }
 
-template <int PROTO, int U, bool BATCH, bool ONEWG = false>
+template <int PROTO, int U, bool BATCH, bool ONEWG = false, bool LDSQ = false>
 KernelFn pickTree(int dtype, int op) {
-#define AR_TREE(DT, OP) treeAllReduceKernel<PROTO, DT, OP, U, BATCH, ONEWG>
+#define AR_TREE(DT, OP) treeAllReduceKernel<PROTO, DT, OP, U, BATCH, ONEWG, LDSQ>
   switch (dtype) {
     case arInt32: return op == arSum ? AR_TREE(arInt32, arSum) : op == arMax ? AR_TREE(arInt32, arMax)
                        : op == arMin ? AR_TREE(arInt32, arMin) : nullptr;
@@ -1589,8 +1679,17 @@ KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
       return oneLL ? pickTree<kLL128, kLL128Unroll, false, true>(dtype, op)
                    : pickTree<kLL128, kLL128Unroll, BATCH>(dtype, op);
     case kSimple: {
-      // trees inside one workgroup get the instantiation compiled for them
+      // trees inside one workgroup get the instantiation compiled for them,
+      // with their FIFOs in LDS when the plan says so
       const bool one = plan.nGroups == 1;
+      if (one && plan.ldsFifo) {
+        switch (plan.unroll) {
+          case 1: return pickTree<kSimple, 1, BATCH, true, true>(dtype, op);
+          case 2: return pickTree<kSimple, 2, BATCH, true, true>(dtype, op);
+          case 4: return pickTree<kSimple, 4, BATCH, true, true>(dtype, op);
+        }
+        return nullptr;
+      }
       switch (plan.unroll) {
         case 1: return one ? pickTree<kSimple, 1, BATCH, true>(dtype, op) : pickTree<kSimple, 1, BATCH>(dtype, op);
         case 2: return one ? pickTree<kSimple, 2, BATCH, true>(dtype, op) : pickTree<kSimple, 2, BATCH>(dtype, op);
