@@ -47,7 +47,12 @@ def test_fifo_capped_tree_keeps_its_slot(B, gu, n, nbytes):
     count = nbytes // 4
     plan, _, _ = gu.parity_case(n, count, "float32", "sum", "simple", 64, algo="tree", seed=n + 1)
     lanes, slot, nch = plan["lanesPerChannel"], plan["stepBytes"], plan["nChannels"]
-    assert slot == 4096, plan                                 # the tree's largest Simple slot
+    want = 4096                                               # the tree's largest Simple slot,
+    if plan["ldsFifoBytes"]:                                  # or the largest whose 2N FIFOs fit LDS
+        while 2 * n * plan["nSlots"] * want + 512 > 160 * 1024:
+            want //= 2
+        assert plan["ldsFifoBytes"] == 2 * n * plan["nSlots"] * slot
+    assert slot == want, plan
     assert lanes * slot < nbytes // nch, plan                 # shares span several slots
 
 

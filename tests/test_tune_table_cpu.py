@@ -111,9 +111,9 @@ def test_outside_the_table(B):
 
 
 def test_picks_follow_the_table_where_it_differs_from_the_model(B):
-    # 4 ranks x 8 B: the ring runs faster than the tree on this GPU (the
-    # fitted model would take the tree)
-    assert B.arTuneTableTime(4, 8, 0, 2) < B.arTuneTableTime(4, 8, 1, 2)
+    # 4 ranks x 1 MiB: the tree runs faster than the ring on this GPU (the
+    # fitted model would take the ring)
+    assert B.arTuneTableTime(4, 1 << 20, 1, 2) < B.arTuneTableTime(4, 1 << 20, 0, 2)
     # 2 ranks x 64 B: the tree (the model would take the ring)
     assert B.arTuneTableTime(2, 64, 1, 2) < B.arTuneTableTime(2, 64, 0, 2)
     # 16 ranks x 4 MiB: the ring
