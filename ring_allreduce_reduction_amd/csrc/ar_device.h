@@ -697,7 +697,13 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
     for (int u = 0; u < U; ++u) v[u] = hasLocal ? combine<DT, OP>(in[u], v[u]) : in[u];
   }
 
-  if (hasOut && !directRecv) {
+  // A Simple send across workgroups waits for its payload stores to complete
+  // before publishing them, and gfx9 counts stores and loads on one counter,
+  // so there the output store comes after the send (nothing downstream waits
+  // for it) instead of being waited for too.  Elsewhere it comes first: LL128
+  // rings cut into workgroups measured 8% slower with it last.
+  constexpr bool OUT_LAST = PROTO == kSimple && XWG;
+  if (!OUT_LAST && hasOut && !directRecv) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       storeUser<ESZ, true>(outp + payOff[u], v[u], valid - payOff[u], payBytes[u], m.aligned);
@@ -762,6 +768,12 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
           stRelaxed64((u64*)(slot + wireOff[u] + 8), m.sendStep + 1, (XWG && m.sendAgent));
     }
     advanceSend(a, m);
+  }
+
+  if (OUT_LAST && hasOut && !directRecv) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      storeUser<ESZ, true>(outp + payOff[u], v[u], valid - payOff[u], payBytes[u], m.aligned);
   }
 
   if (hasRecv) finishRecv<XWG>(a, m);
@@ -953,8 +965,16 @@ __device__ __forceinline__ bool memberPasses(const KernelArgs& a, Member& m, int
 // this instantiation for such plans only), so no edge crosses workgroups; the
 // Simple kernels of slots up to 4 KiB then also compile every step for its
 // kind (8 ranks x 4 KiB: 19.5 -> 15.2 us; 16 x 4 KiB: 45.6 -> 34.2 us).  Not
-// for 8 KiB slots, where the per-kind copies spill, nor for rings cut into
-// workgroups, where their extra registers cost residency.
+// for 8 KiB slots, where the per-kind copies spill.  Rings cut into
+// workgroups compile their steps per kind when their FIFO slots are in LDS
+// (LDSQ): with the kind known, a copy step's LDS handoff no longer waits on
+// the vector memory counter for a local load that kind never issues -- which
+// on gfx9 meant waiting for the previous step's output store to complete --
+// so the chain of hops inside a workgroup runs at LDS speed (72 ranks x
+// 4 MiB: 391 -> 325 us; 128 x 1 MiB: 595 -> 487 us; 24 x 4 KiB: 92 -> 72 us,
+// with the output store after the send on edges between workgroups).
+// Those with HBM FIFOs keep one step for every kind: there the extra
+// registers of the copies cost residency.
 //
 // PERKIND (with ONEWG): compile each step for its kind.  LL and LL128 get it
 // too (8 ranks x 4 KiB: LL 24.0 -> 18.6 us, LL128 26.9 -> 20.4 us), but the
@@ -1041,10 +1061,10 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   bool ok;
   if constexpr (GROUPED) {
     ok = m.sendAgent || m.recvAgent
-             ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, true, false, false, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
-                                                                               succ)
-             : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, false, false, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
-                                                                                succ);
+             ? memberPasses<PROTO, DT, OP, U, COLL, BATCH, true, LDSQ, false, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
+                                                                              succ)
+             : memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, LDSQ, false, LDSQ>(a, m, L, sets, lanesTotal, perTask,
+                                                                               r, succ);
   } else {
     ok = memberPasses<PROTO, DT, OP, U, COLL, BATCH, false, SPEC, LINES, LDSQ>(a, m, L, sets, lanesTotal, perTask, r,
                                                                              succ);
