@@ -209,6 +209,22 @@ __device__ __forceinline__ void storeUser(char* p, v4u v, long valid, int pieceB
 // Scope of an edge: workgroup when producer and consumer share the
 // workgroup, agent otherwise.
 
+// Counter comparisons use the low 32 bits, modulo 2^32: the two ends of one
+// FIFO are never further apart than its depth (at most 8 slots), so the sign
+// of the 32-bit difference decides.  The scalar unit compares 32-bit values
+// in one instruction and has no ordered 64-bit compare (a u64 comparison of
+// uniform values costs two moves to vector registers, a vector compare and a
+// mask test): every wait and credit check of every step pays for it, and the
+// waves of a workgroup step in lockstep, sharing their SIMDs' issue slots.
+__device__ __forceinline__ bool reached(u32 have, u32 target) { return (int)(have - target) >= 0; }
+
+__device__ __forceinline__ u32 ldCounter32(const u64* p, bool agent) {
+  const u32* q = (const u32*)p;   // the low word (little-endian)
+  u32 v = agent ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                : __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 __device__ __forceinline__ u64 ldCounter(const u64* p, bool agent) {
   u64 v = agent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                 : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -344,11 +360,12 @@ __device__ __forceinline__ u32 callFailed(const KernelArgs& a) {
 
 // Wait until *p >= target.
 __device__ __forceinline__ bool waitGeq(const KernelArgs& a, const u64* p, u64 target, bool agent) {
-  if (ldCounter(p, agent) >= target) return true;
+  const u32 t = (u32)target;
+  if (reached(ldCounter32(p, agent), t)) return true;
   Waiter w;
   while (true) {
     if (!keepWaiting(a, w)) return false;
-    if (ldCounter(p, agent) >= target) return true;
+    if (reached(ldCounter32(p, agent), t)) return true;
   }
 }
 
@@ -370,11 +387,9 @@ __device__ __forceinline__ u64* ldsCounters() {
   __shared__ u64 c[2 * kMaxMembersPerGroup];
   return c;
 }
-__device__ __forceinline__ u64 ldLds(int i) {
-  u64 v = __hip_atomic_load(&ldsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  u32 lo = __builtin_amdgcn_readfirstlane((u32)v);
-  u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
-  return ((u64)hi << 32) | lo;
+__device__ __forceinline__ u32 ldLds32(int i) {
+  const u32 v = __hip_atomic_load((u32*)&ldsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ __forceinline__ void stLds(int i, u64 v) {
   __hip_atomic_store(&ldsCounters()[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -390,11 +405,12 @@ __device__ __forceinline__ void stLdsRelease(int i, u64 v) {
 extern __shared__ __align__(16) char ldsFifoBase[];
 
 __device__ __forceinline__ bool waitLdsGeq(const KernelArgs& a, int i, u64 target) {
-  if (ldLds(i) >= target) return true;
+  const u32 t = (u32)target;
+  if (reached(ldLds32(i), t)) return true;
   Waiter w;
   while (true) {
     if (!keepWaiting(a, w)) return false;
-    if (ldLds(i) >= target) return true;
+    if (reached(ldLds32(i), t)) return true;
   }
 }
 
@@ -539,8 +555,8 @@ struct Member {
   u64 sendStep;       // slots written into the successor's FIFO (== succ->tail)
   u32 recvSlot;       // recvStep % nSlots
   u32 sendSlot;       // sendStep % nSlots
-  u64 succHead;       // last value read from succ->head; head only grows, so
-                      // a stale copy never over-reports free slots
+  u32 succHead;       // low word of the last value read from succ->head; head
+                      // only grows, so a stale copy never over-reports free slots
   int selfW;          // my wavefront in the workgroup: my LDS counters
   int succW;          // the successor's, when it shares the workgroup
   bool recvAgent;
@@ -552,18 +568,20 @@ struct Member {
 // CACHED: skip the poll while the last credit read still covers this slot.
 template <bool CACHED, bool XWG>
 __device__ __forceinline__ bool waitCredit(const KernelArgs& a, Member& m) {
-  // slot sendStep % nSlots is free once the successor consumed step sendStep - nSlots
-  u64 need = m.sendStep + 1 > (u64)a.nSlots ? m.sendStep + 1 - (u64)a.nSlots : 0;
+  // slot sendStep % nSlots is free once the successor consumed step
+  // sendStep - nSlots (modulo 2^32: before the first nSlots steps of a FIFO
+  // the target is "negative" and any head reaches it)
+  const u32 need = (u32)m.sendStep + 1u - (u32)a.nSlots;
   const bool agent = XWG && m.sendAgent;
   if (CACHED) {
-    if (m.succHead >= need) return true;   // ordered by the acquire after that read
-    m.succHead = agent ? ldCounter(&m.succ->head, true) : ldLds(kLdsHead + m.succW);
-    if (m.succHead < need) {
+    if (reached(m.succHead, need)) return true;   // ordered by the acquire after that read
+    m.succHead = agent ? ldCounter32(&m.succ->head, true) : ldLds32(kLdsHead + m.succW);
+    if (!reached(m.succHead, need)) {
       Waiter w;
       do {
         if (!keepWaiting(a, w)) return false;
-        m.succHead = agent ? ldCounter(&m.succ->head, true) : ldLds(kLdsHead + m.succW);
-      } while (m.succHead < need);
+        m.succHead = agent ? ldCounter32(&m.succ->head, true) : ldLds32(kLdsHead + m.succW);
+      } while (!reached(m.succHead, need));
     }
   } else if (agent ? !waitGeq(a, &m.succ->head, need, true) : !waitLdsGeq(a, kLdsHead + m.succW, need)) {
     return false;
@@ -823,6 +841,16 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
       const u64 nCols = divUp(sub0 * ESZ, (u64)PAYLOAD);
       // a whole chunk's lane share, so that only a shortened chunk divides
       const u64 subCur = alignUp(divUp(cur, (u64)a.lanes), A);
+      // chunks [0, cWhole) hold `cur` elements each (all N on a full loop):
+      // their lane shares have one length, and chunk c's starts c * cur
+      // elements after chunk 0's, so a stage over one of them needs no
+      // multiply-and-clamp of its own (kernels with LDS FIFOs, whose steps
+      // are short enough for it to matter; the others keep their registers)
+      const u64 cWhole = !LDSQ ? 0 : rem >= loopSize ? (u64)N : rem / cur;
+      const u64 sbWhole = umin((u64)k * subCur, cur);
+      const u64 bytesWhole = (umin(sbWhole + subCur, cur) - sbWhole) * ESZ;
+      const u64 firstWhole = (lo + off + sbWhole) * ESZ;
+      const u64 curBytes = cur * ESZ;
       for (u64 jb = 0; jb < nCols; jb += batch) {
         const u64 je = umin(jb + batch, nCols);
         int cNext = r == 0 ? N - 1 : r - 1;   // (r - 1 - s) mod N, stepped down each stage
@@ -832,14 +860,20 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
           // chunk sent at stage s is (r - 1 - s) mod N; the final receive gets r + 1
           const int c = s <= lastSendStage ? cNext : succ;
           cNext = cNext == 0 ? N - 1 : cNext - 1;
-          const u64 cb = (u64)c * cur;
-          const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
-          // lane k's share of the chunk (pipelining only: the order is per element)
-          const u64 sub = clen == cur ? subCur : alignUp(divUp(clen, (u64)a.lanes), A);
-          const u64 sb = umin((u64)k * sub, clen);
-          const u64 se = umin(sb + sub, clen);
-          const u64 bytes = (se - sb) * ESZ;
-          const u64 first = (lo + off + cb + sb) * ESZ;
+          u64 bytes, first;
+          if (LDSQ && (u64)c < cWhole) {
+            bytes = bytesWhole;
+            first = firstWhole + (u64)(u32)c * curBytes;
+          } else {
+            const u64 cb = (u64)c * cur;
+            const u64 clen = cb < rem ? umin(cur, rem - cb) : 0;
+            // lane k's share of the chunk (pipelining only: the order is per element)
+            const u64 sub = clen == cur ? subCur : alignUp(divUp(clen, (u64)a.lanes), A);
+            const u64 sb = umin((u64)k * sub, clen);
+            const u64 se = umin(sb + sub, clen);
+            bytes = (se - sb) * ESZ;
+            first = (lo + off + cb + sb) * ESZ;
+          }
           for (u64 j = jb; j < je; ++j) {
             const u64 b = j * (u64)PAYLOAD;
             if (b >= bytes) break;
@@ -1045,7 +1079,7 @@ __global__ void __launch_bounds__(1024) ringAllReduceKernel(const KernelArgs a) 
   const u32 failed = (FRESH ? live : carry) ? callFailed(a) : 0u;
   m.recvStep = carry ? ldCounter(&m.self->head, true) : 0;
   m.sendStep = carry ? ldCounter(&m.succ->tail, true) : 0;
-  m.succHead = 0;
+  m.succHead = (u32)m.sendStep;   // at a call boundary the successor has consumed all we sent
   m.recvSlot = (u32)(m.recvStep % (u64)a.nSlots);
   m.sendSlot = (u32)(m.sendStep % (u64)a.nSlots);
   if (live && m.lane == 0) {
@@ -1158,18 +1192,17 @@ __device__ __forceinline__ u64* treeLdsCounters() {
   __shared__ u64 c[2 * 2 * kMaxMembersPerGroup];
   return c;
 }
-__device__ __forceinline__ u64 ldTreeLds(int i) {
-  u64 v = __hip_atomic_load(&treeLdsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  u32 lo = __builtin_amdgcn_readfirstlane((u32)v);
-  u32 hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
-  return ((u64)hi << 32) | lo;
+__device__ __forceinline__ u32 ldTreeLds32(int i) {
+  const u32 v = __hip_atomic_load((u32*)&treeLdsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ __forceinline__ bool waitTreeLdsGeq(const KernelArgs& a, int i, u64 target) {
-  if (ldTreeLds(i) >= target) return true;
+  const u32 t = (u32)target;
+  if (reached(ldTreeLds32(i), t)) return true;
   Waiter w;
   while (true) {
     if (!keepWaiting(a, w)) return false;
-    if (ldTreeLds(i) >= target) return true;
+    if (reached(ldTreeLds32(i), t)) return true;
   }
 }
 __device__ __forceinline__ Edge openLdsEdge(int fifoIndex) {
@@ -1276,7 +1309,8 @@ __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pie
                                          long valid, const v4u (&v)[U]) {
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
   // slot step % nSlots is free once the receiver consumed step - nSlots
-  const u64 need = e.step + 1 > (u64)a.nSlots ? e.step + 1 - (u64)a.nSlots : 0;
+  // (modulo 2^32, as the ring's credit)
+  const u32 need = (u32)e.step + 1u - (u32)a.nSlots;
   if constexpr (LDSQ) {   // Simple, FIFO and counters in LDS
     if (!waitTreeLdsGeq(a, 2 * e.lds + 1, need)) return false;
     acquireEdge();
