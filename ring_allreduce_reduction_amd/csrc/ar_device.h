@@ -391,6 +391,15 @@ __device__ __forceinline__ u32 ldLds32(int i) {
   const u32 v = __hip_atomic_load((u32*)&ldsCounters()[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return __builtin_amdgcn_readfirstlane(v);
 }
+// A counter of an edge inside the workgroup is read as its low word only,
+// so a step publishes just that word; every lane of the wavefront stores the
+// same value (one LDS write, and no execution-mask change around it).
+__device__ __forceinline__ void stLds32(int i, u32 v) {
+  __hip_atomic_store((u32*)&ldsCounters()[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void stLds32Release(int i, u32 v) {
+  __hip_atomic_store((u32*)&ldsCounters()[i], v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 __device__ __forceinline__ void stLds(int i, u64 v) {
   __hip_atomic_store(&ldsCounters()[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -597,9 +606,10 @@ __device__ __forceinline__ void advanceSend(const KernelArgs& a, Member& m) {
 template <bool XWG>
 __device__ __forceinline__ void finishRecv(const KernelArgs& a, Member& m) {
   ++m.recvStep;
-  if (m.lane == 0) {
-    if (XWG && m.recvAgent) stCounterRelease(&m.self->head, m.recvStep, true);
-    else stLdsRelease(kLdsHead + m.selfW, m.recvStep);
+  if (XWG && m.recvAgent) {
+    if (m.lane == 0) stCounterRelease(&m.self->head, m.recvStep, true);
+  } else {
+    stLds32Release(kLdsHead + m.selfW, (u32)m.recvStep);
   }
   if (++m.recvSlot == (u32)a.nSlots) m.recvSlot = 0;
 }
@@ -660,7 +670,12 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
   // registers across the wait) and small Simple slots 3% slower on short
   // messages, so those keep the plain order.
   constexpr bool EARLY = PROTO == kLL || (PROTO == kSimple && U == 8);
-  if (!EARLY && hasSend && !directSend && !waitCredit<false, XWG>(a, m)) return false;
+  // LEAN: LDS-FIFO kernels with slots of at most 2 KiB, whose steps are short
+  // enough for a few instructions to show (the plans of latency-bound sizes):
+  // they keep the last credit read, and move whole LDS slots.  Measured on
+  // the 4 KiB headline slot, the same changes cost 2%; it keeps the others.
+  constexpr bool LEAN = LDSQ && U <= 2;
+  if (!EARLY && hasSend && !directSend && !waitCredit<LEAN, XWG>(a, m)) return false;
 
   v4u v[U];
 #pragma unroll
@@ -681,7 +696,9 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
       const char* ls = ldsFifoBase + ((size_t)m.selfW * (size_t)a.nSlots + m.recvSlot) * SLOT;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (LDSQ && !(XWG && m.recvAgent))
+        if (LEAN && !(XWG && m.recvAgent))   // past the payload: stale, never stored
+          in[u] = *(const v4u*)(ls + wireOff[u]);
+        else if (LDSQ && !(XWG && m.recvAgent))
           in[u] = payOff[u] < valid ? *(const v4u*)(ls + wireOff[u]) : v4u{0u, 0u, 0u, 0u};
         else if (directRecv)   // the predecessor wrote it into my output
           in[u] = kind == kRecvCopySend
@@ -736,10 +753,11 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
         for (int u = 0; u < U; ++u)
           storeUser<ESZ, false>(succOutp + payOff[u], v[u], valid - payOff[u], 16, m.aligned);
       } else if (LDSQ && !(XWG && m.sendAgent)) {
+        // LEAN: the whole slot (lanes past the payload carry values no one stores)
         char* ls = ldsFifoBase + ((size_t)m.succW * (size_t)a.nSlots + m.sendSlot) * SLOT;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (payOff[u] < valid) *(v4u*)(ls + wireOff[u]) = v[u];
+          if (LEAN || payOff[u] < valid) *(v4u*)(ls + wireOff[u]) = v[u];
       } else if ((XWG && m.sendAgent)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -750,9 +768,10 @@ __device__ __forceinline__ bool step(const KernelArgs& a, Member& m, int kindRt,
           if (payOff[u] < valid) *(v4u*)(slot + wireOff[u]) = v[u];
       }
       releaseEdge((XWG && m.sendAgent));
-      if (lane == 0) {
-        if (XWG && m.sendAgent) stRelaxed64(&m.succ->tail, m.sendStep + 1, true);
-        else stLds(m.succW, m.sendStep + 1);
+      if (XWG && m.sendAgent) {
+        if (lane == 0) stRelaxed64(&m.succ->tail, m.sendStep + 1, true);
+      } else {
+        stLds32(m.succW, (u32)m.sendStep + 1u);
       }
     } else if (PROTO == kLL) {
       const u64 flag = (u64)(u32)(m.sendStep + 1) << 32;
@@ -846,7 +865,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
       // elements after chunk 0's, so a stage over one of them needs no
       // multiply-and-clamp of its own (kernels with LDS FIFOs, whose steps
       // are short enough for it to matter; the others keep their registers)
-      const u64 cWhole = !LDSQ ? 0 : rem >= loopSize ? (u64)N : rem / cur;
+      const int cWhole = !LDSQ ? 0 : rem >= loopSize ? N : (int)(rem / cur);
       const u64 sbWhole = umin((u64)k * subCur, cur);
       const u64 bytesWhole = (umin(sbWhole + subCur, cur) - sbWhole) * ESZ;
       const u64 firstWhole = (lo + off + sbWhole) * ESZ;
@@ -861,7 +880,7 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
           const int c = s <= lastSendStage ? cNext : succ;
           cNext = cNext == 0 ? N - 1 : cNext - 1;
           u64 bytes, first;
-          if (LDSQ && (u64)c < cWhole) {
+          if (LDSQ && c < cWhole) {
             bytes = bytesWhole;
             first = firstWhole + (u64)(u32)c * curBytes;
           } else {
@@ -874,13 +893,25 @@ __device__ __forceinline__ bool ringPass(const KernelArgs& a, Member& m, int r, 
             bytes = (se - sb) * ESZ;
             first = (lo + off + cb + sb) * ESZ;
           }
-          for (u64 j = jb; j < je; ++j) {
-            const u64 b = j * (u64)PAYLOAD;
-            if (b >= bytes) break;
-            const long valid = (long)umin((u64)PAYLOAD, bytes - b);
-            if (!step<PROTO, DT, OP, U, XWG, KIND, LINES, LDSQ>(a, m, kindRt, in + first + b, out + first + b,
-                                                          succOut + first + b, valid))
-              return false;
+          if constexpr (LDSQ && U <= 2) {   // a lane's share of one chunk is at most a chunk: 32 bits
+            const u32 bytes32 = (u32)bytes;
+            for (u32 j = (u32)jb; j < (u32)je; ++j) {
+              const u32 b = j * (u32)PAYLOAD;
+              if (b >= bytes32) break;
+              const long valid = (long)(bytes32 - b < (u32)PAYLOAD ? bytes32 - b : (u32)PAYLOAD);
+              if (!step<PROTO, DT, OP, U, XWG, KIND, LINES, LDSQ>(a, m, kindRt, in + first + b, out + first + b,
+                                                            succOut + first + b, valid))
+                return false;
+            }
+          } else {
+            for (u64 j = jb; j < je; ++j) {
+              const u64 b = j * (u64)PAYLOAD;
+              if (b >= bytes) break;
+              const long valid = (long)umin((u64)PAYLOAD, bytes - b);
+              if (!step<PROTO, DT, OP, U, XWG, KIND, LINES, LDSQ>(a, m, kindRt, in + first + b, out + first + b,
+                                                            succOut + first + b, valid))
+                return false;
+            }
           }
           return true;
         };
