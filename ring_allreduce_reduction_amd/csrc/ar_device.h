@@ -1286,9 +1286,11 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
     if (!waitTreeLdsGeq(a, 2 * e.lds, e.step + 1)) return false;
     acquireEdge();
     const char* ls = ldsFifoBase + ((size_t)e.lds * (size_t)a.nSlots + e.slot) * SLOT;
+    // slots of at most 2 KiB are moved whole, as in the ring (past the
+    // payload: stale lanes that are never stored)
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      in[u] = pc.payOff[u] >= valid ? v4u{0u, 0u, 0u, 0u} : *(const v4u*)(ls + pc.wireOff[u]);
+      in[u] = U <= 2 || pc.payOff[u] < valid ? *(const v4u*)(ls + pc.wireOff[u]) : v4u{0u, 0u, 0u, 0u};
     return true;
   }
   const char* slot = e.fifo + (size_t)e.slot * SLOT;
@@ -1326,12 +1328,11 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
 template <bool XWG, bool LDSQ = false>
 __device__ __forceinline__ void edgeFinishRecv(const KernelArgs& a, Edge& e, int lane) {
   ++e.step;
-  if (lane == 0) {
-    if (LDSQ)
-      __hip_atomic_store(&treeLdsCounters()[2 * e.lds + 1], e.step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    else
-      stCounterRelease(&e.conn->head, e.step, (XWG && e.agent));
-  }
+  if (LDSQ)   // the low word, by every lane (as the ring's LDS counters)
+    __hip_atomic_store((u32*)&treeLdsCounters()[2 * e.lds + 1], (u32)e.step, __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  else if (lane == 0)
+    stCounterRelease(&e.conn->head, e.step, (XWG && e.agent));
   if (++e.slot == (u32)a.nSlots) e.slot = 0;
 }
 
@@ -1348,10 +1349,10 @@ __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pie
     char* ls = ldsFifoBase + ((size_t)e.lds * (size_t)a.nSlots + e.slot) * SLOT;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (pc.payOff[u] < valid) *(v4u*)(ls + pc.wireOff[u]) = v[u];
+      if (U <= 2 || pc.payOff[u] < valid) *(v4u*)(ls + pc.wireOff[u]) = v[u];
     releaseEdge(false);   // the LDS stores before the counter
-    if (lane == 0)
-      __hip_atomic_store(&treeLdsCounters()[2 * e.lds], e.step + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store((u32*)&treeLdsCounters()[2 * e.lds], (u32)e.step + 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
     ++e.step;
     if (++e.slot == (u32)a.nSlots) e.slot = 0;
     return true;
