@@ -275,6 +275,23 @@ void freeComm(arComm* c) {
   delete c;
 }
 
+// Parent of rank r in tree t of the double binary tree over n ranks (-1 for
+// the root), as the kernel builds it: tree 0 is the in-order binary tree
+// whose node r has parent (r with its lowest set bit cleared and the next bit
+// up set, or only cleared when that is out of range); tree 1 relabels rank x
+// as n-1-x (even n) or x-1 (odd n) and maps the parent back.  Used to count
+// the tree edges that cross workgroups in a plan's device bytes.
+int treeParent(int n, int r, int t) {
+  const bool mirror = (n & 1) == 0;
+  const int x = t == 0 ? r : mirror ? n - 1 - r : (r == 0 ? n - 1 : r - 1);
+  if (x == 0) return -1;
+  const int bit = x & -x;
+  int up = (x & ~bit) | (bit << 1);
+  if (up >= n) up = x & ~bit;
+  if (t == 0) return up;
+  return mirror ? n - 1 - up : (up + 1 == n ? 0 : up + 1);
+}
+
 // The public view of a plan (p == nullptr: the one-rank / empty short cut).
 void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* p, arPlan_t* out) {
   memset(out, 0, sizeof(*out));
@@ -304,7 +321,20 @@ void exportPlan(const arComm* c, int func, size_t count, int dtype, const Plan* 
   out->nSlots = p->nSlots;
   out->predictedUs = p->predictedUs;
   out->deviceBytes = out->modelBytes;
-  if (p->ldsFifo) {
+  if (p->ldsFifo && p->algo == arAlgoTree) {
+    // inputs read and outputs written once; each tree edge between
+    // workgroups carries its share of the data up and back down, each slot
+    // written and read once
+    out->ldsFifoBytes = p->ldsBytes;
+    double cross = 0.0;
+    const int trees = p->nChannels > 1 ? 2 : 1;
+    for (int t = 0; t < trees; ++t)
+      for (int r = 0; r < N; ++r) {
+        const int up = treeParent(N, r, t);
+        if (up >= 0 && up / p->groupSize != r / p->groupSize) cross += 1.0 / trees;
+      }
+    out->deviceBytes = 2.0 * N * S + 4.0 * cross * S;
+  } else if (p->ldsFifo) {
     // inputs read and outputs written once; a ring cut into G workgroups
     // also writes and reads a slot on each of its G edges between them at
     // every send (2N-2 sends of S/N per AllReduce member, N-1 of a block for
@@ -536,6 +566,22 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // smaller slot, as more lanes of it take a share that is in flight at once
   // through the tree a little faster (24 ranks x 4 KiB: 4 lanes of 1 KiB
   // 38.3 us, 2 of 2 KiB 39.1, 1 of 4 KiB 42.9), then more channels.
+  // A Simple tree cut into workgroups (single calls) keeps the FIFOs of the
+  // edges inside each workgroup in its LDS, two per node (up and down) at the
+  // comm's Simple depth beside 512 bytes of counters, wherever they fit at
+  // the slot and group size the search below picks (which counts their LDS
+  // in its co-residency checks); the edges between workgroups keep device
+  // FIFOs.  The search keeps its own order: preferring plans whose FIFOs fit
+  // took smaller slots than the bytes in flight want (72 ranks x 1 MiB in
+  // 2 KiB slots 780 us, in 4 KiB slots with device FIFOs 562 us), while at
+  // the same geometry the LDS FIFOs win (72 x 4 KiB 27.5 -> 27.0 us, 32 x
+  // 4 KiB 18.1 -> 15.2 us, 128 x 4 KiB 26.3 -> 23.5 us).
+  const bool treeLdsOk = tree && proto == kSimple && !batch && c->ldsFifo && c->ldsPerBlock > 0;
+  auto treeLds = [&](int members) {
+    const int64_t bytes = (int64_t)2 * members * plan->nSlots * plan->slotBytes;
+    plan->ldsFifo = treeLdsOk && bytes + 512 <= (int64_t)c->ldsPerBlock;
+    plan->ldsBytes = plan->ldsFifo ? (int)bytes : 0;
+  };
   bool placed = false;
   if (tree && !batch && N > gsMax && c->forcedLanes == 0) {
     const int nchAsked = nch;
@@ -550,6 +596,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
           layout(gs, &nGroups, &groupSize);
           plan->nGroups = nGroups;
           plan->block = groupSize * kWave;
+          treeLds(groupSize);
           int pc = 0;
           if (ringKernelOccupancy(*plan, func, dtype, op, batch, &pc) != hipSuccess) return arHipError;
           const int cap = pc * c->numCUs;
@@ -578,8 +625,11 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       plan->nChannels = nch;
       chunkBytes = chunkBytesFor(nch);
       layout(bestGs, &nGroups, &groupSize);
+      treeLds(groupSize);
       placed = true;
     } else {
+      plan->ldsFifo = false;
+      plan->ldsBytes = 0;
       setSlot(unroll0);
       nch = nchAsked;
       chunkBytes = chunkBytesFor(nch);
@@ -752,6 +802,10 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // depth 2 at 8 KiB by 3% at 8 ranks x 256 MiB fp32 and ties at 16 ranks x
   // 512 MiB bf16, and 8 KiB gains nothing where it fits (4 ranks x 8 MiB);
   // the lane count stays, so a lane's share spans more, smaller slots.
+  if (treeLdsOk && placed && nGroups > 1) {
+    treeLds(groupSize);   // as the co-residency checks above counted it
+    return arSuccess;
+  }
   if (ldsGrouped && nGroups > 1) {
     groupLds(groupSize);   // as the co-residency check above counted it
     if (plan->ldsFifo) plan->direct = false;
@@ -1209,7 +1263,9 @@ arResult_t runColl(arComm* c, int func, const void* const* sendbufs, void* const
   arResult_t r = makePlan(c, func, count, dtype, kop, aligned128, &plan);
   if (r != arSuccess) return r;
   if (!fifosCover(c, plan)) return arInternalError;
-  if (!plan.ldsFifo) {   // FIFOs in LDS need no device memory
+  // FIFOs in LDS need no device memory, but the edges between the
+  // workgroups of a ring or tree cut into groups keep theirs in it
+  if (!plan.ldsFifo || plan.nGroups > 1) {
     r = provisionFifo(c, plan.proto, plan.nSlots);   // a protocol this comm has not run yet
     if (r != arSuccess) return r;
   }
@@ -1446,7 +1502,7 @@ arResult_t launchGroup(arComm* c) {
                     : makePlan(c, lead.func, lead.count, lead.dtype, kop, a128, &l.plan, true, l.size, aggBytes);
     if (r != arSuccess) return r;
     if (!fifosCover(c, l.plan)) return arInternalError;
-    r = l.plan.ldsFifo ? arSuccess : provisionFifo(c, l.plan.proto, l.plan.nSlots);
+    r = l.plan.ldsFifo && l.plan.nGroups == 1 ? arSuccess : provisionFifo(c, l.plan.proto, l.plan.nSlots);
     if (r != arSuccess) return r;
     l.row = rows;
     if (l.size > 1) rows += (size_t)l.size;

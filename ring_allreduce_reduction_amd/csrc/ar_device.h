@@ -1212,7 +1212,7 @@ struct Edge {
   u64 step;     // next step on this FIFO
   u32 slot;     // step % nSlots
   bool agent;   // the other end is in another workgroup
-  int lds;      // LDS FIFOs (trees inside one workgroup): the FIFO's index
+  int lds;      // LDS FIFOs: the FIFO's index in the workgroup's LDS (-1: device memory)
 };
 
 // A tree inside one workgroup with its FIFOs in LDS: every node but the root
@@ -1255,6 +1255,7 @@ __device__ __forceinline__ Edge openEdge(const KernelArgs& a, size_t worker, boo
   e.step = ldCounter(recvEnd ? &e.conn->head : &e.conn->tail, true);
   e.slot = (u32)(e.step % (u64)a.nSlots);
   e.agent = agent;
+  e.lds = -1;
   return e;
 }
 
@@ -1282,7 +1283,9 @@ template <int PROTO, int U, bool XWG, bool LINES = false, bool LDSQ = false>
 __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, const Pieces<PROTO, U>& pc, int lane,
                                          long valid, v4u (&in)[U]) {
   constexpr int SLOT = PROTO == kSimple ? U * kWave * 16 : PROTO == kLL ? kLLSlotBytes : U * kLL128UnitBytes;
-  if constexpr (LDSQ) {   // Simple, FIFO and counters in LDS
+  // LDSQ: an edge inside the workgroup has its FIFO and counters in LDS
+  // (every edge of a member compiled without edges between workgroups)
+  if (LDSQ && (!XWG || e.lds >= 0)) {   // Simple
     if (!waitTreeLdsGeq(a, 2 * e.lds, e.step + 1)) return false;
     acquireEdge();
     const char* ls = ldsFifoBase + ((size_t)e.lds * (size_t)a.nSlots + e.slot) * SLOT;
@@ -1328,7 +1331,7 @@ __device__ __forceinline__ bool edgeRecv(const KernelArgs& a, const Edge& e, con
 template <bool XWG, bool LDSQ = false>
 __device__ __forceinline__ void edgeFinishRecv(const KernelArgs& a, Edge& e, int lane) {
   ++e.step;
-  if (LDSQ)   // the low word, by every lane (as the ring's LDS counters)
+  if (LDSQ && (!XWG || e.lds >= 0))   // the low word, by every lane (as the ring's LDS counters)
     __hip_atomic_store((u32*)&treeLdsCounters()[2 * e.lds + 1], (u32)e.step, __ATOMIC_RELEASE,
                        __HIP_MEMORY_SCOPE_WORKGROUP);
   else if (lane == 0)
@@ -1343,7 +1346,7 @@ __device__ __forceinline__ bool edgeSend(const KernelArgs& a, Edge& e, const Pie
   // slot step % nSlots is free once the receiver consumed step - nSlots
   // (modulo 2^32, as the ring's credit)
   const u32 need = (u32)e.step + 1u - (u32)a.nSlots;
-  if constexpr (LDSQ) {   // Simple, FIFO and counters in LDS
+  if (LDSQ && (!XWG || e.lds >= 0)) {   // Simple, FIFO and counters in LDS
     if (!waitTreeLdsGeq(a, 2 * e.lds + 1, need)) return false;
     acquireEdge();
     char* ls = ldsFifoBase + ((size_t)e.lds * (size_t)a.nSlots + e.slot) * SLOT;
@@ -1535,7 +1538,7 @@ __device__ __forceinline__ bool treePasses(const KernelArgs& a, TreeNode& nd, in
 // start at 0 in each launch and the comm's device FIFOs are not touched.
 template <int PROTO, int DT, int OP, int U, bool BATCH, bool ONEWG, bool LDSQ = false>
 __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) {
-  static_assert(!LDSQ || (PROTO == kSimple && ONEWG), "LDS FIFOs: Simple trees inside one workgroup");
+  static_assert(!LDSQ || (PROTO == kSimple && (ONEWG || !BATCH)), "LDS FIFOs: Simple trees (cut into groups: single calls)");
   // as in the ring kernel: scalar member state for the largest (4 KiB) slot
   const int wave = (U == 4 || LDSQ) ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave)
                                     : (int)(threadIdx.x / kWave);
@@ -1567,17 +1570,33 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
   dtreeNode(N, r, t, nd.up, nd.d[0], nd.d[1]);
   auto worker = [&](int node, int edge) { return ((size_t)L * N + node) * 3 + edge; };
   auto cross = [&](int node) { return node / a.groupSize != g; };
-  if constexpr (LDSQ) {   // node x's FIFO up is 2x, its FIFO down 2x + 1
+  if constexpr (LDSQ) {
+    // An edge inside the workgroup: node x's FIFO up is 2x, its FIFO down
+    // 2x + 1, x its index in the workgroup.  An edge to another workgroup
+    // keeps its FIFO and carried counters in device memory.
+    const int base = g * a.groupSize;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (nd.d[i] >= 0) {
-        nd.fromChild[i] = openLdsEdge(2 * nd.d[i]);
-        nd.toChild[i] = openLdsEdge(2 * nd.d[i] + 1);
+        if (!cross(nd.d[i])) {
+          nd.fromChild[i] = openLdsEdge(2 * (nd.d[i] - base));
+          nd.toChild[i] = openLdsEdge(2 * (nd.d[i] - base) + 1);
+        } else {
+          nd.fromChild[i] = openEdge(a, worker(r, i), true, true);
+          nd.toChild[i] = openEdge(a, worker(nd.d[i], 2), true, false);
+        }
       }
     }
     if (nd.up >= 0) {
-      nd.fromParent = openLdsEdge(2 * r + 1);
-      nd.toParent = openLdsEdge(2 * r);
+      if (!cross(nd.up)) {
+        nd.fromParent = openLdsEdge(2 * (r - base) + 1);
+        nd.toParent = openLdsEdge(2 * (r - base));
+      } else {
+        int pu, p0, p1;
+        dtreeNode(N, nd.up, t, pu, p0, p1);
+        nd.fromParent = openEdge(a, worker(r, 2), true, true);
+        nd.toParent = openEdge(a, worker(nd.up, r == p0 ? 0 : 1), true, false);
+      }
     }
   } else {
 #pragma unroll
@@ -1615,8 +1634,26 @@ __global__ void __launch_bounds__(1024) treeAllReduceKernel(const KernelArgs a) 
     bool xwg = nd.up >= 0 && nd.toParent.agent;
 #pragma unroll
     for (int i = 0; i < 2; ++i) xwg = xwg || (nd.d[i] >= 0 && nd.toChild[i].agent);
-    ok = xwg ? treePasses<PROTO, DT, OP, U, BATCH, true>(a, nd, L, perTask, ch, k, lane, r)
-             : treePasses<PROTO, DT, OP, U, BATCH, false>(a, nd, L, perTask, ch, k, lane, r);
+    if constexpr (PROTO == kSimple && !BATCH) {
+      // Simple trees cut into workgroups: the members whose edges all stay
+      // inside the workgroup run a pass compiled for their role too
+      const int role = (nd.up >= 0 ? kRoleParent : 0) | (nd.d[0] >= 0 ? kRoleD0 : 0) | (nd.d[1] >= 0 ? kRoleD1 : 0);
+      if (xwg) {
+        ok = treePasses<PROTO, DT, OP, U, BATCH, true, kRoleAtRunTime, false, LDSQ>(a, nd, L, perTask, ch, k, lane, r);
+      } else {
+        switch (role) {
+#define AR_ROLE(R) treePasses<PROTO, DT, OP, U, BATCH, false, R, false, LDSQ>(a, nd, L, perTask, ch, k, lane, r)
+          case kRoleParent: ok = AR_ROLE(kRoleParent); break;
+          case kRoleParent | kRoleD0: ok = AR_ROLE(kRoleParent | kRoleD0); break;
+          case kRoleParent | kRoleD0 | kRoleD1: ok = AR_ROLE(kRoleParent | kRoleD0 | kRoleD1); break;
+          default: ok = AR_ROLE(kRoleAtRunTime); break;
+#undef AR_ROLE
+        }
+      }
+    } else {
+      ok = xwg ? treePasses<PROTO, DT, OP, U, BATCH, true>(a, nd, L, perTask, ch, k, lane, r)
+               : treePasses<PROTO, DT, OP, U, BATCH, false>(a, nd, L, perTask, ch, k, lane, r);
+    }
   }
   if (!ok) return;
   // LL / LL128 never touch the tail counter per slot: publish it once so the
@@ -1773,6 +1810,16 @@ KernelFn pickTreeProto(const Plan& plan, int dtype, int op) {
           case 1: return pickTree<kSimple, 1, BATCH, true, true>(dtype, op);
           case 2: return pickTree<kSimple, 2, BATCH, true, true>(dtype, op);
           case 4: return pickTree<kSimple, 4, BATCH, true, true>(dtype, op);
+        }
+        return nullptr;
+      }
+      if (plan.ldsFifo) {   // a tree cut into workgroups, its inside edges in LDS (single calls)
+        if constexpr (!BATCH) {
+          switch (plan.unroll) {
+            case 1: return pickTree<kSimple, 1, false, false, true>(dtype, op);
+            case 2: return pickTree<kSimple, 2, false, false, true>(dtype, op);
+            case 4: return pickTree<kSimple, 4, false, false, true>(dtype, op);
+          }
         }
         return nullptr;
       }
