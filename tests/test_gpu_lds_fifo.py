@@ -109,3 +109,29 @@ def test_lds_fifo_grouped_launch(B, gu):
                                         for i, c in enumerate([4096, 4100, 5000, 65537, 70000, 1 << 20])], "lds")
         assert max(p["tasksInLaunch"] for p in plans) >= 2
         assert all(p["ldsFifoBytes"] > 0 for p in plans)
+
+
+@pytest.mark.parametrize("n,count,nch,dtype", [(17, 4096, 64, "float32"), (32, 1027, 64, "float32"),
+                                               (72, 1024, 64, "float32"), (40, 2048, 64, "bfloat16"),
+                                               (128, 1024, 64, "int32"), (64, 16384, 64, "float32"),
+                                               (24, 32771, 64, "float16")])
+def test_tree_cut_into_workgroups_keeps_inside_edges_in_lds(B, gu, n, count, nch, dtype):
+    """A Simple tree past 16 ranks: the edges inside each workgroup in LDS,
+    the edges between workgroups in device memory with carried counters.  The
+    plan says so, the result is the oracle's either way, and calls with and
+    without the LDS FIFOs alternate on one comm (the device edges' counters
+    must still meet at tail == head)."""
+    from ring_allreduce_reduction_amd import binding
+    with B.Comm(n, nch, "simple", "tree") as comm:
+        plan = comm.plan(count, dtype)
+        gs = plan["ranksPerGroup"]
+        assert plan["algo"] == binding.arAlgoTree and gs < n, plan
+        assert plan["ldsFifoBytes"] == 2 * gs * plan["nSlots"] * plan["stepBytes"] > 0, plan
+        esz = 2 if dtype in ("bfloat16", "float16") else 4
+        assert plan["deviceBytes"] > 2.0 * n * count * esz   # edges between workgroups move bytes too
+        for i, lds in enumerate([1, 0, 1, 1, 0]):
+            B.arSetDebug(comm.handle, B.arDebugLdsFifo, lds)
+            p = comm.plan(count, dtype)
+            assert (p["ldsFifoBytes"] > 0) == bool(lds), p
+            gu.parity_case(n, count, dtype, "sum", "simple", nch, seed=n + i, comm=comm)
+        gu.parity_case(n, count, "uint64", "probe", "simple", nch, comm=comm)
