@@ -129,7 +129,10 @@ arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, ar
  * A Simple ring of at most 16 ranks runs each (channel, lane) in one
  * workgroup and keeps its FIFO slots in that workgroup's LDS (arPlan_t
  * ldsFifoBytes; arDebugLdsFifo): its kernel then moves no FIFO bytes through
- * device memory, only the inputs and outputs.
+ * device memory, only the inputs and outputs.  A Simple tree inside one
+ * workgroup does the same; longer rings and trees keep the FIFOs of the
+ * edges inside each workgroup in LDS (a tree where they fit its plan's slot)
+ * and those of the edges between workgroups in device memory.
  * Residency: a ring or tree of more than 16 ranks is cut into workgroups
  * that wait on one another, so all workgroups of its launch must be resident
  * at once.  The planner sizes that grid to what the GPU holds; a kernel
@@ -317,16 +320,18 @@ typedef struct {
   int groupLaunch;      /* arGetGroupPlan: index of the launch (in launch order)
                            that carried this call; -1 for a copy or a single call */
   int tasksInLaunch;    /* collectives sharing that launch (1 unless batched) */
-  int ldsFifoBytes;     /* Simple rings: the FIFO slots of the edges inside a workgroup
-                           live in LDS, this many bytes per workgroup (members x nSlots x
-                           stepBytes); 0: FIFO slots in device memory */
+  int ldsFifoBytes;     /* Simple rings and trees: the FIFO slots of the edges inside a
+                           workgroup live in LDS, this many bytes per workgroup (ring:
+                           members x nSlots x stepBytes; tree: two FIFOs per member);
+                           0: FIFO slots in device memory */
   double deviceBytes;   /* device-memory bytes the plan's kernel must move: modelBytes,
                            except with LDS FIFOs, where only the inputs are read and the
                            outputs written (AllReduce 2N*S; ReduceScatter and AllGather
                            (N+1)*N*S, S the per-rank block), plus, for a ring cut into G
                            workgroups, a slot written and read on each of the G edges
                            between them per send (AllReduce 4(N-1)*G*S/N; the halves
-                           2(N-1)*G*S) */
+                           2(N-1)*G*S), and for a tree cut into workgroups 4*S for each
+                           tree edge between them (its share up and back down) */
 } arPlan_t;
 
 /*
@@ -417,10 +422,10 @@ typedef enum {
                                   runtime checks residency and runs such launches one at a time,
                                   at 15-70 us per launch), 0 = plain launch of the same grid
                                   (default; see arAllReduce on residency) */
-  arDebugLdsFifo = 13,         /* 1 (default): Simple rings keep the FIFO slots of their edges
-                                  inside a workgroup in LDS (rings of at most 16 ranks, single
-                                  calls and arGroupEnd's batched launches; rings cut into
-                                  workgroups, single calls); 0: in device memory */
+  arDebugLdsFifo = 13,         /* 1 (default): Simple rings and trees keep the FIFO slots of
+                                  their edges inside a workgroup in LDS (those of at most 16
+                                  ranks, single calls and arGroupEnd's batched launches; those
+                                  cut into workgroups, single calls); 0: in device memory */
   arDebugGroupSize = 12,       /* at most this many ring or tree members per workgroup, 1..16
                                   (0: 16, the default): a ring or tree longer than this is cut
                                   into groups joined by device-coherent edges, as rings of more
