@@ -104,7 +104,7 @@ def main():
         return calib_table(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build emulates all ranks on one GPU; --gpus %d (WORLD_SIZE %d) is not "
+        print("bench.py: this library emulates all ranks on one GPU; --gpus %d (WORLD_SIZE %d) is not "
               "supported -- run with --gpus 1" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 

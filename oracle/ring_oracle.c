@@ -37,7 +37,7 @@
  *    round-to-nearest-even, because the partial crosses the ring in its own
  *    type at every hop.  Max is acc = (x > acc) ? x : acc and Min is
  *    acc = (x < acc) ? x : acc with acc the incoming partial and x the local
- *    value.  The pages fix none of these; they are the readings this build
+ *    value.  The pages fix none of these; they are the readings this library
  *    takes and both sides implement them independently.
  *
  *  - A debug-only uint64 "probe" op, acc = acc*16 + x, is not commutative, so a
