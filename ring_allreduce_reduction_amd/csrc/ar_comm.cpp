@@ -533,6 +533,19 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     plan->ldsFifo = ldsGrouped && bytes + 256 <= (int64_t)c->ldsPerBlock;
     plan->ldsBytes = plan->ldsFifo ? (int)bytes : 0;
   };
+  // A single-call ring cut into workgroups puts at most 24 of its wavefronts
+  // on one CU (the grid spread evenly over the CUs).  Its hops are bound by
+  // instruction issue (the members of a workgroup step in lockstep), and past
+  // 24 the time per hop doubles: 2 MiB per rank over 64 channels in 8 groups,
+  // 96 ranks (two 12-member workgroups per CU) 345 us, 100 and 104 ranks (two
+  // of 13) 637 and 659 us, 120 ranks on 32 channels (one of 15) 401 us; 8 MiB
+  // per rank, 48 ranks (two of 12) 254 us, 52 (two of 13) 419 us, 60 (one of
+  // 15) 335 us.  Batched launches and trees keep their own rules.
+  auto ringWavesCapped = [&](int64_t grid, int members) {
+    if (tree || batch) return false;
+    const int64_t perCUUsed = grid <= c->numCUs ? 1 : (grid + c->numCUs - 1) / c->numCUs;
+    return perCUUsed * members > kGroupedRingWavesPerCU;
+  };
   auto targetFor = [&]() { return (int)((uint64_t)c->numCUs * wavesPerCU / ((uint64_t)N * (uint64_t)nch)); };
   auto lanesFor = [&](int slotPayload) {
     int ln = targetFor();
@@ -670,6 +683,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
         if (ringKernelOccupancy(*plan, func, dtype, op, batch, &perCU) != hipSuccess) return -1;
         const int64_t grid = (int64_t)((nch * ln + 7) / 8) * 8 * nGroups;
         if ((int64_t)perCU * c->numCUs < grid) continue;
+        if (ringWavesCapped(grid, groupSize)) continue;
         if (grid <= c->numCUs || grid % c->numCUs == 0) return 1;
         if (first == 0) first = groupSize;
       }
@@ -688,9 +702,34 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
       const uint64_t need = (chunkBytes + (uint64_t)slotPayloadOf(proto, u) - 1) / (uint64_t)slotPayloadOf(proto, u);
       if (u < uMax && need >= 1 && need <= 2) found = fit(u, (int)need);
     }
-    for (int u = uMax; u >= 1 && found == 0; u /= 2) {
-      found = fit(u, 1);
-      if (proto != kSimple) break;
+    // One lane per channel: every Simple slot is tried.  The plan whose edges
+    // inside a workgroup keep their FIFOs in LDS is taken first, then the
+    // largest groups, then the smallest slot that holds a whole chunk (else
+    // the largest slot).  Taking the largest slot that fits at all put 76
+    // ranks x 8 MiB (1.8 KiB chunks) in one-member groups of 4 KiB slots,
+    // every hop between workgroups (1390 us; in 10-member groups of 2 KiB
+    // slots 365 us), and 72 ranks x 8 MiB in 9-member groups of 4 KiB slots
+    // (654 us), a step of the 4 KiB kernel moving the same 1.8 KiB as one of
+    // the 2 KiB kernel.
+    if (found == 0) {
+      int bestU = 0, bestSize = 0;
+      bool bestLds = false;
+      auto covers = [&](int u) { return (uint64_t)slotPayloadOf(proto, u) >= chunkBytes; };
+      for (int u = uMax; u >= 1; u /= 2) {
+        const int f = fit(u, 1);
+        if (f < 0) return arHipError;
+        const bool lds = plan->ldsFifo && groupSize > 1;
+        const bool better = bestU == 0 || (lds && !bestLds) ||
+                            (lds == bestLds && (groupSize > bestSize ||
+                                                (groupSize == bestSize && covers(u) && covers(bestU))));
+        if (f > 0 && better) {
+          bestU = u;
+          bestSize = groupSize;
+          bestLds = lds;
+        }
+        if (proto != kSimple) break;
+      }
+      if (bestU > 0) found = fit(bestU, 1);
     }
     if (found < 0) return arHipError;
     if (found > 0) break;
@@ -763,7 +802,7 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     lanes = c->forcedLanes <= cap ? c->forcedLanes : cap;
   }
   if (plan->cooperative) {
-    while (lanes > 1 && gridFor(lanes) > capacity) --lanes;
+    while (lanes > 1 && (gridFor(lanes) > capacity || ringWavesCapped(gridFor(lanes), groupSize))) --lanes;
     if (gridFor(lanes) > capacity) return arInvalidUsage;
   }
   // a batched launch runs up to nTasks collectives at once, each on its own

@@ -1,7 +1,9 @@
-"""GPU parity on the plans two planner rules produce, with the rule itself
+"""GPU parity on the plans three planner rules produce, with the rule itself
 checked on the plan: rings of fewer than 8 ranks spread a short chunk over
-up to 8 wavefronts per CU, and a tree whose lanes the FIFOs cap keeps its
-largest slot.  Bit for bit against the oracle on every rank."""
+up to 8 wavefronts per CU, a tree whose lanes the FIFOs cap keeps its
+largest slot, and a ring cut into workgroups keeps at most 24 of its
+wavefronts on a CU, its inside FIFOs in LDS and a slot that fits its chunk.
+Bit for bit against the oracle on every rank."""
 import pytest
 import torch
 
@@ -54,6 +56,20 @@ def test_fifo_capped_tree_keeps_its_slot(B, gu, n, nbytes):
         assert plan["ldsFifoBytes"] == 2 * n * plan["nSlots"] * slot
     assert slot == want, plan
     assert lanes * slot < nbytes // nch, plan                 # shares span several slots
+
+
+@pytest.mark.parametrize("n,nbytes", [(76, 8 * MiB), (72, 8 * MiB), (52, 8 * MiB), (100, 2 * MiB)])
+def test_ring_cut_into_workgroups_plan(B, gu, cus, n, nbytes):
+    # sizes whose earlier plans fell into one-member groups (76 ranks), 4 KiB
+    # slots for 1.8 KiB chunks (72), or two 13-member workgroups per CU (52,
+    # 100): each took 1.4-3.8x the time of the plan checked here
+    count = nbytes // 4
+    plan, _, _ = gu.parity_case(n, count, "float32", "sum", "simple", 64, seed=n + 2)
+    gs, wg, slot = plan["ranksPerGroup"], plan["workgroups"], plan["stepBytes"]
+    assert 1 < gs <= 16 and plan["ldsFifoBytes"] > 0, plan
+    assert -(-wg // cus) * gs <= 24, plan                     # ring wavefronts per CU
+    chunk = nbytes // plan["nChannels"] // n                  # one loop: a rank's share of a channel
+    assert chunk <= slot and (slot == 1024 or slot // 2 < chunk), plan
 
 
 def test_small_ring_ragged_and_16bit(B, gu):
