@@ -533,19 +533,23 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     plan->ldsFifo = ldsGrouped && bytes + 256 <= (int64_t)c->ldsPerBlock;
     plan->ldsBytes = plan->ldsFifo ? (int)bytes : 0;
   };
-  // A single-call ring cut into workgroups puts at most 24 of its wavefronts
-  // on one CU (the grid spread evenly over the CUs).  Its hops are bound by
-  // instruction issue (the members of a workgroup step in lockstep), and past
-  // 24 the time per hop doubles: 2 MiB per rank over 64 channels in 8 groups,
-  // 96 ranks (two 12-member workgroups per CU) 345 us, 100 and 104 ranks (two
-  // of 13) 637 and 659 us, 120 ranks on 32 channels (one of 15) 401 us; 8 MiB
-  // per rank, 48 ranks (two of 12) 254 us, 52 (two of 13) 419 us, 60 (one of
-  // 15) 335 us.  Batched launches and trees keep their own rules.
-  auto ringWavesCapped = [&](int64_t grid, int members) {
-    if (tree || batch) return false;
+  // A single call of a ring or tree cut into workgroups puts at most 24 of
+  // its wavefronts on one CU (the grid spread evenly over the CUs).  Its hops
+  // are bound by instruction issue (the members of a workgroup step in
+  // lockstep), and past 24 the time per hop doubles.  Rings, 2 MiB per rank
+  // over 64 channels in 8 groups: 96 ranks (two 12-member workgroups per CU)
+  // 345 us, 100 and 104 ranks (two of 13) 637 and 659 us, 120 ranks on 32
+  // channels (one of 15) 401 us; 8 MiB per rank, 48 ranks (two of 12) 254 us,
+  // 52 (two of 13) 419 us, 60 (one of 15) 335 us.  Trees, 128 KiB per rank
+  // over 4 channels: 38-42 ranks (two of 13-14 on a CU) 41-43 us, 44 and 48
+  // (one of 15-16) 28 and 22 us, 50-56 (two of 13-14) 42-46 us, 60 and 64
+  // (one of 15-16) 27 and 24 us.  Batched launches keep their own rules, and
+  // forced lanes are taken as given.
+  auto wavesOverCap = [&](int64_t grid, int members) {
     const int64_t perCUUsed = grid <= c->numCUs ? 1 : (grid + c->numCUs - 1) / c->numCUs;
-    return perCUUsed * members > kGroupedRingWavesPerCU;
+    return perCUUsed * members > kGroupedWavesPerCU;
   };
+  auto ringWavesCapped = [&](int64_t grid, int members) { return !tree && !batch && wavesOverCap(grid, members); };
   auto targetFor = [&]() { return (int)((uint64_t)c->numCUs * wavesPerCU / ((uint64_t)N * (uint64_t)nch)); };
   auto lanesFor = [&](int slotPayload) {
     int ln = targetFor();
@@ -613,9 +617,9 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
           int pc = 0;
           if (ringKernelOccupancy(*plan, func, dtype, op, batch, &pc) != hipSuccess) return arHipError;
           const int cap = pc * c->numCUs;
-          if (cap < gridFor(1)) continue;
+          if (cap < gridFor(1) || wavesOverCap(gridFor(1), groupSize)) continue;
           int ln = lanesFor(plan->slotPayload);
-          while (ln > 1 && gridFor(ln) > cap) --ln;
+          while (ln > 1 && (gridFor(ln) > cap || wavesOverCap(gridFor(ln), groupSize))) --ln;
           const uint64_t lanesBytes = (uint64_t)ln * (uint64_t)plan->slotPayload;
           const uint64_t bytes = (uint64_t)ch * (lanesBytes < chunkBytes ? lanesBytes : chunkBytes);
           if (groupSize > bestSize ||
@@ -802,7 +806,9 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
     lanes = c->forcedLanes <= cap ? c->forcedLanes : cap;
   }
   if (plan->cooperative) {
-    while (lanes > 1 && (gridFor(lanes) > capacity || ringWavesCapped(gridFor(lanes), groupSize))) --lanes;
+    while (lanes > 1 && (gridFor(lanes) > capacity ||
+                         (!batch && c->forcedLanes == 0 && wavesOverCap(gridFor(lanes), groupSize))))
+      --lanes;
     if (gridFor(lanes) > capacity) return arInvalidUsage;
   }
   // a batched launch runs up to nTasks collectives at once, each on its own

@@ -33,8 +33,8 @@ constexpr int kBatchSimpleUnrollMax = 8;  // batched ring launches: any Simple s
 constexpr int kGroupedSimpleUnrollMax = 4;  // rings cut into several workgroups: Simple slot at most
                                            // 4 KiB (the 8 KiB kernel holds no cross-workgroup edge
                                            // code, which would make it spill)
-constexpr int kGroupedRingWavesPerCU = 24;  // single-call rings cut into workgroups: their
-                                           // wavefronts per CU at most
+constexpr int kGroupedWavesPerCU = 24;     // single-call rings and trees cut into workgroups:
+                                          // their wavefronts per CU at most
 constexpr int kTreeSimpleUnrollMax = 4;   // the tree's Simple slot is at most 4 KiB (three slot
                                           // arrays live per lane: 8 KiB would spill)
 constexpr int kTreeEdges = 3;             // a tree node's FIFOs: from d0, from d1, from its parent

@@ -2,7 +2,8 @@
 checked on the plan: rings of fewer than 8 ranks spread a short chunk over
 up to 8 wavefronts per CU, a tree whose lanes the FIFOs cap keeps its
 largest slot, and a ring cut into workgroups keeps at most 24 of its
-wavefronts on a CU, its inside FIFOs in LDS and a slot that fits its chunk.
+wavefronts on a CU (a tree too), its inside FIFOs in LDS and a slot that
+fits its chunk.
 Bit for bit against the oracle on every rank."""
 import pytest
 import torch
@@ -70,6 +71,16 @@ def test_ring_cut_into_workgroups_plan(B, gu, cus, n, nbytes):
     assert -(-wg // cus) * gs <= 24, plan                     # ring wavefronts per CU
     chunk = nbytes // plan["nChannels"] // n                  # one loop: a rank's share of a channel
     assert chunk <= slot and (slot == 1024 or slot // 2 < chunk), plan
+
+
+@pytest.mark.parametrize("n,nbytes,nch", [(40, 128 << 10, 4), (52, 128 << 10, 4), (72, 4 * MiB, 16)])
+def test_tree_cut_into_workgroups_waves_per_cu(B, gu, cus, n, nbytes, nch):
+    # 40 and 52 ranks once ran two 13-14-member workgroups on a CU (1.5x the
+    # time of the plan checked here)
+    plan, _, _ = gu.parity_case(n, nbytes // 4, "float32", "sum", "simple", nch, algo="tree", seed=n + 3)
+    gs, wg = plan["ranksPerGroup"], plan["workgroups"]
+    assert 1 < gs <= 16, plan
+    assert -(-wg // cus) * gs <= 24, plan
 
 
 def test_small_ring_ragged_and_16bit(B, gu):
