@@ -90,7 +90,8 @@ def parse():
                     help="summarize rocprofv3 CSV output directories into markdown + profiles/traffic.json")
     ap.add_argument("--profile-label", default="", help="workload key for --summarize-profiles")
     ap.add_argument("--batch", type=int, default=0,
-                    help="time T AllReduces of --count elements issued one by one and as one group")
+                    help="time T AllReduces of --count elements issued one by one, as one group, and "
+                         "captured into a HIP graph and replayed")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="time a plain elementwise copy (torch.neg) of this many bytes instead")
     return ap.parse_args()
@@ -561,8 +562,9 @@ def bench_halves(args, B, gen, torch, np):
 def bench_batch(args, B, gen, torch, np):
     """T AllReduces of `count` fp32 elements per rank on N ranks, each with its
     own buffers: issued one by one, then between arGroupStart / arGroupEnd
-    (aggregated into batched launches).  Reports microseconds per AllReduce
-    for both (events around the whole set, mean over --steps repetitions)."""
+    (aggregated into batched launches), then the T single calls captured once
+    into a HIP graph and replayed.  Reports microseconds per AllReduce for
+    each (events around the whole set, mean over --steps repetitions)."""
     N, T, count = args.nranks, args.batch, args.count
     xs = gen.make_inputs(N, count, "float32", seed=args.seed)
     sends = [[torch.from_numpy(x).cuda() for x in xs] for _ in range(T)]
@@ -600,12 +602,34 @@ def bench_batch(args, B, gen, torch, np):
         if comm.async_error() != B.arSuccess:
             raise SystemExit("batch run failed")
         res[mode] = a.elapsed_time(b) * 1e3 / (args.steps * T)
+    # the T single calls recorded once (one kernel node each) and replayed
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(T):
+            if L.arAllReduce(comm.handle, sp[i], rp[i], count, B.arFloat32, B.arSum, sh) != B.arSuccess:
+                raise SystemExit("arAllReduce under capture failed")
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    if comm.async_error() != B.arSuccess:
+        raise SystemExit("graph replay failed")
+    res["graph"] = a.elapsed_time(b) * 1e3 / (args.steps * T)
+    del g
     plan = comm.group_plan(0)
     single = comm.plan(count, "float32")
     comm.close()
     S = count * 4
     print(json.dumps({"batch": T, "nranks": N, "bytes_per_rank": S, "us_per_allreduce_single": round(res["single"], 3),
                       "us_per_allreduce_group": round(res["group"], 3),
+                      "us_per_allreduce_graph": round(res["graph"], 3),
                       "speedup": round(res["single"] / res["group"], 3),
                       "single_plan": {"algo": B.ALGO_NAMES[single["algo"]], "proto": B.PROTO_NAMES[single["proto"]],
                                       "nch": single["nChannels"]},

@@ -123,7 +123,13 @@ arResult_t arInit(arComm_t* comm, int nranks, int nChannels, arProto_t proto, ar
  * The call only enqueues: one kernel launch on `stream`, or a device copy
  * when nranks == 1 [B ch.6 §三, the one-rank path].  The caller synchronises
  * the stream before reading results [B ch.1 §1.3].  Buffers must stay valid
- * until the work completes.  Element pointers need only element alignment;
+ * until the work completes.  Graph capture: once the comm has made one call
+ * of the same plan, a call records that launch and nothing else (no
+ * allocation, memset, copy or synchronisation), so calls may be captured on
+ * `stream` into a HIP graph and replayed, each replay reducing whatever the
+ * captured buffers then hold; rings and trees cut into workgroups carry
+ * their edge counters from replay to replay.  Group calls (arGroupEnd) stage
+ * their task tables through pinned host memory and are not for capture.  Element pointers need only element alignment;
  * forcing LL128 needs 128-byte aligned buffers, otherwise arInvalidUsage
  * [B ch.2 §2.4, LL128 alignment]; arProtoAuto never picks LL128 then.
  * A Simple ring of at most 16 ranks runs each (channel, lane) in one
