@@ -465,6 +465,21 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   }
   const bool tree = al == arAlgoTree;
   const int N = c->nranks;
+  // A batched launch of rings cut into workgroups runs its tasks side by
+  // side only while all their grids are resident together, so it takes at
+  // most the channels (a power of two) for which every task's grid of one
+  // lane per channel fits two workgroups per CU in the largest groups; with
+  // more, the tasks run in rounds, each round a whole ring's chain of steps
+  // (16 AllReduces of 256 KiB per rank, fp32: 24 ranks on 64 channels
+  // 31.0 us per AllReduce, on 16 9.2 us; 72 ranks on 16 channels 119 us, on
+  // 4 44 us).
+  if (batch && nTasks > 1 && !tree && N > kMaxMembersPerGroup) {
+    const int64_t groups = (N + kMaxMembersPerGroup - 1) / kMaxMembersPerGroup;
+    const int64_t fit = (int64_t)c->numCUs * 2 / (groups * nTasks);
+    int ch = 1;
+    while ((int64_t)ch * 2 <= fit) ch *= 2;
+    if (nch > ch) nch = ch;
+  }
   const uint64_t A = 16 / (uint64_t)esz;
   // FIFOs per (rank, lane): one for the ring, one per incoming edge for the tree
   const int edges = tree ? kTreeEdges : 1;

@@ -88,6 +88,19 @@ def test_group_cooperative_24_ranks(B, gu, algo):
     assert plans[0]["ranksPerGroup"] <= 16 and [p["tasksInLaunch"] for p in plans] == [2, 2, 2, 2]
 
 
+@pytest.mark.parametrize("n,most", [(24, 16), (72, 4)])
+def test_group_of_rings_cut_into_workgroups_fits_one_round(B, gu, n, most):
+    # 16 AllReduces side by side: the channels of a batched launch of rings
+    # past 16 ranks are cut so every task's grid is resident at once (on 64
+    # channels the tasks had run in rounds: 24 ranks 31.0 us per AllReduce,
+    # on 16 channels 9.2 us)
+    with B.Comm(n, 64, "simple", "ring") as comm:
+        plans = run_group(B, gu, comm, [(16384 + 8 * i, "float32", "sum", False, i) for i in range(16)],
+                          "16 x 64 KiB")
+    assert {p["tasksInLaunch"] for p in plans} == {16}
+    assert max(p["nChannels"] for p in plans) <= most, plans[0]
+
+
 def test_group_in_place_and_halves(B, gu, orc):
     from ring_allreduce_reduction_amd import inputs as gen
     n = 8
