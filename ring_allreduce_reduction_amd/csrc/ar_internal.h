@@ -19,6 +19,8 @@ constexpr int kMaxWorkers = 32768;        // (rank, lane) wavefronts a comm prov
 constexpr int kDefaultSlots[3] = {8, 8, 2};
 constexpr int kMaxSlots = 8;              // FIFO depth provisioned per worker
 constexpr int kLdsFifoSlots = 3;          // depth of FIFOs kept in LDS
+constexpr int kGroupedSlotsMax = 4;       // rings cut into workgroups: FIFO depth at most, where it
+                                          // fits LDS (at most kMaxSlots)
 
 // One ring member is one wavefront.  Per FIFO slot ("step") a wavefront moves
 // `unroll` pieces per lane:

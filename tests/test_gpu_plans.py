@@ -83,6 +83,31 @@ def test_tree_cut_into_workgroups_waves_per_cu(B, gu, cus, n, nbytes, nch):
     assert -(-wg // cus) * gs <= 24, plan
 
 
+def test_deeper_fifos_provisioned_on_first_call_of_a_nonblocking_stream(B, gu):
+    # A ring cut into workgroups takes depth-4 FIFOs where they fit LDS; its
+    # first call provisions the device FIFOs of its edges between workgroups
+    # at that depth.  The clear of the new FIFOs must be complete before the
+    # kernel runs on a stream that does not wait for the null stream (a run
+    # that raced it once ran a later call into the wait bound).
+    from ring_allreduce_reduction_amd import inputs as gen
+    n, count = 72, 1 << 18
+    xs = gen.make_inputs(n, count, "float32", seed=5)
+    sends = [gu.to_device(x, "float32") for x in xs]
+    recvs = [torch.empty_like(t) for t in sends]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with B.Comm(n, 64, "simple", "ring") as comm:
+        plan = comm.plan(count, "float32")
+        assert plan["nSlots"] == 4 and plan["ldsFifoBytes"] == plan["ranksPerGroup"] * 4 * plan["stepBytes"], plan
+        for _ in range(64):
+            B.arAllReduce(comm.handle, sends, recvs, stream=s)
+        torch.cuda.synchronize()
+        assert comm.async_error() == B.arSuccess
+        want = gu.expected(xs, "float32", "sum", plan)
+        for r in range(n):
+            gu.assert_bits_equal(gu.to_host_raw(recvs[r], "float32"), want, "float32", "rank %d" % r)
+
+
 def test_small_ring_ragged_and_16bit(B, gu):
     # the spread plan on a count no slot divides, and on both 16-bit types
     gu.parity_case(2, (4 * MiB) // 4 + 12345, "float32", "sum", "simple", 64, seed=5)
