@@ -870,6 +870,29 @@ arResult_t makePlan(arComm* c, int func, uint64_t count, int dtype, int op, bool
   // the lane count stays, so a lane's share spans more, smaller slots.
   if (treeLdsOk && placed && nGroups > 1) {
     treeLds(groupSize);   // as the co-residency checks above counted it
+    // Deeper FIFOs, as for the ring below, where the FIFOs stay where they
+    // are (in LDS if they fit there at depth 2, else in device memory) and
+    // the grid stays co-resident: the tree moves a batch of nSlots columns
+    // up and down at a time, so a deeper FIFO keeps more bytes in flight
+    // (72 ranks x 4 MiB, 16 channels x 3 lanes of 4 KiB in 15-member groups:
+    // depth 2 562 us, 4 448 us; 68 x 2 MiB 0.76x; 24 x 4 KiB 0.94x; 32 x
+    // 256 KiB at depth 4 would leave LDS for device FIFOs, 1.28x, so keeps
+    // depth 2).
+    if (!c->slotsForced) {
+      const int d0 = plan->nSlots;
+      const bool lds0 = plan->ldsFifo;
+      for (int d = kGroupedSlotsMax; d > d0; --d) {
+        plan->nSlots = d;
+        treeLds(groupSize);
+        if (plan->ldsFifo == lds0) {
+          int pc = 0;
+          if (ringKernelOccupancy(*plan, func, dtype, op, batch, &pc) != hipSuccess) return arHipError;
+          if ((int64_t)pc * c->numCUs >= (int64_t)plan->grid) break;
+        }
+        plan->nSlots = d0;
+        treeLds(groupSize);
+      }
+    }
     return arSuccess;
   }
   if (ldsGrouped && nGroups > 1) {

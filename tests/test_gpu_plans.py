@@ -81,6 +81,10 @@ def test_tree_cut_into_workgroups_waves_per_cu(B, gu, cus, n, nbytes, nch):
     gs, wg = plan["ranksPerGroup"], plan["workgroups"]
     assert 1 < gs <= 16, plan
     assert -(-wg // cus) * gs <= 24, plan
+    if plan["ldsFifoBytes"] == 0:                               # device FIFOs: taken at depth 4
+        assert plan["nSlots"] == 4, plan
+    else:                                                       # LDS FIFOs: as deep as still fits
+        assert plan["ldsFifoBytes"] == 2 * gs * plan["nSlots"] * plan["stepBytes"] <= 160 * 1024, plan
 
 
 def test_deeper_fifos_provisioned_on_first_call_of_a_nonblocking_stream(B, gu):
